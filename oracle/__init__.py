@@ -1,0 +1,178 @@
+"""fp64 CPU oracle for the GMA forward pass (TEST INFRASTRUCTURE ONLY).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The HIP library never does, and the
+oracle imports nothing from it.
+
+The numerical work is in ``gma_oracle.c`` (plain C, double precision, straight
+loops).  This module builds it with gcc, marshals numpy arrays, and adds the
+projection step of the full layer (Eq. 4 of "Gaussian Mixture Attention:
+Linear-Time Sequence Mixing via Probabilistic Latent Routing", Section
+"Projections"), for which ``numpy.matmul`` in float64 serves as the library
+matrix product.
+
+Pins (see tests/test_oracle.py): responsibilities against scikit-learn's
+diagonal-covariance GaussianMixture posterior; outputs against a brute-force
+materialised affinity built from scikit-learn's responsibilities; closed
+forms (K=1 mean and running mean, two-component logistic posterior,
+well-separated clusters, identical components); invariants (row sums, causal
+future-perturbation, last causal row equals the bidirectional row).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gma_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_gma_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (IEEE double, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall",
+                               "-o", tmp, _SRC, "-lm", "-lpthread"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _bind(path: str):
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    i64, i32 = ctypes.c_int64, ctypes.c_int
+    lib.gmao_forward.argtypes = [P, P, P, P, P, P, i64, i64, i64, i32, i32, i32,
+                                 ctypes.c_double, i32, P, i64, P, P, P, P, P, i32]
+    lib.gmao_forward.restype = ctypes.c_int
+    lib.gmao_resp.argtypes = [P, i64, i64, i64, i32, P, P, P, i32, P, P, P]
+    lib.gmao_resp.restype = ctypes.c_int
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        _lib = _bind(_LIB_PATH)
+    return _lib
+
+
+class using_library:
+    """Context manager: route calls to another build of the oracle source
+    (used by the mutation tests, which compile deliberately broken copies)."""
+
+    def __init__(self, path: str):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self._saved = _load()
+        _lib = _bind(self.path)
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self._saved
+        return False
+
+
+def default_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data
+
+
+def forward(Q, K, V, mu, log_sigma2, log_pi, eps: float, causal: bool,
+            rows: Optional[np.ndarray] = None, want_assign: bool = False,
+            want_latent: bool = False, nthreads: Optional[int] = None) -> dict:
+    """GMA forward (Eqs. 3, 5-7; causal: the prefix form of Eq. 8b).
+
+    Q, K: [B,H,N,d_r]; V: [B,H,N,d_v]; mu, log_sigma2: [H,K,d_r]; log_pi: [H,K]
+    (any additive per-head constant).  ``rows``: optional sorted row indices
+    to produce.  Returns dict(out=[B,H,R,d_v] float64, assign_q, assign_k,
+    vtilde=[B,H,K,d_v], z=[B,H,K]).
+    """
+    lib = _load()
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    mu, ls2, lpi = _f64(mu), _f64(log_sigma2), _f64(log_pi)
+    B, H, N, d_r = Q.shape
+    d_v = V.shape[-1]
+    Kc = mu.shape[1]
+    assert K.shape == Q.shape and V.shape[:3] == (B, H, N)
+    assert mu.shape == (H, Kc, d_r) and ls2.shape == mu.shape and lpi.shape == (H, Kc)
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+    R = N if rows is None else rows.shape[0]
+    out = np.empty((B, H, R, d_v), np.float64)
+    aq = np.empty((B, H, R), np.int32) if want_assign else None
+    ak = np.empty((B, H, N), np.int32) if want_assign else None
+    vt = np.empty((B, H, Kc, d_v), np.float64) if (want_latent and not causal) else None
+    zt = np.empty((B, H, Kc), np.float64) if (want_latent and not causal) else None
+    rc = lib.gmao_forward(_ptr(Q), _ptr(K), _ptr(V), _ptr(mu), _ptr(ls2), _ptr(lpi),
+                          B, H, N, d_r, d_v, Kc, float(eps), int(bool(causal)),
+                          _ptr(rows), 0 if rows is None else R,
+                          _ptr(out), _ptr(aq), _ptr(ak), _ptr(vt), _ptr(zt),
+                          nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("gmao_forward rejected its arguments (code %d)" % rc)
+    return {"out": out, "assign_q": aq, "assign_k": ak, "vtilde": vt, "z": zt}
+
+
+def responsibilities(X, mu, log_sigma2, log_pi) -> dict:
+    """Eq. 3 for X [U,N,d_r] (or [B,H,N,d_r]); unit u uses head u % H.
+
+    Returns gamma [...,N,K], assign [...,N], score [...,N,K] (natural log of
+    prior times density, i.e. the quantity Eq. 16 takes a softmax of).
+    """
+    lib = _load()
+    X = _f64(X)
+    lead = X.shape[:-2]
+    N, d_r = X.shape[-2:]
+    U = int(np.prod(lead)) if lead else 1
+    mu, ls2, lpi = _f64(mu), _f64(log_sigma2), _f64(log_pi)
+    H, Kc = lpi.shape
+    gamma = np.empty(lead + (N, Kc), np.float64)
+    score = np.empty(lead + (N, Kc), np.float64)
+    assign = np.empty(lead + (N,), np.int32)
+    rc = lib.gmao_resp(_ptr(X), U, H, N, d_r, _ptr(mu), _ptr(ls2), _ptr(lpi), Kc,
+                       _ptr(gamma), _ptr(assign), _ptr(score))
+    if rc != 0:
+        raise ValueError("gmao_resp rejected its arguments (code %d)" % rc)
+    return {"gamma": gamma, "assign": assign, "score": score}
+
+
+def project(X, W, H: int) -> np.ndarray:
+    """Eq. 4: X [B,N,d_model] times W [d_model, H*d] in float64, split into heads.
+
+    Head h takes columns [h*d, (h+1)*d).  Returns [B,H,N,d].
+    """
+    X = _f64(X)
+    W = _f64(W)
+    B, N, _ = X.shape
+    d = W.shape[1] // H
+    P = np.matmul(X, W)                       # [B,N,H*d]
+    return np.ascontiguousarray(P.reshape(B, N, H, d).transpose(0, 2, 1, 3))
+
+
+def layer_forward(X, W_Q, W_K, W_V, H: int, mu, log_sigma2, log_pi, eps: float,
+                  causal: bool, rows: Optional[np.ndarray] = None,
+                  want_assign: bool = False, nthreads: Optional[int] = None) -> dict:
+    """Projection (Eq. 4, no bias, no output projection) followed by the GMA forward."""
+    Q = project(X, W_Q, H)
+    K = project(X, W_K, H)
+    V = project(X, W_V, H)
+    return forward(Q, K, V, mu, log_sigma2, log_pi, eps, causal, rows=rows,
+                   want_assign=want_assign, nthreads=nthreads)
