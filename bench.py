@@ -1,0 +1,193 @@
+#!/usr/bin/env python3
+"""Throughput of the GMA forward pass on one MI355X.
+
+One step = one gma_forward call (prologue, latent write, partial reduction and
+fused responsibility + read-out; or the causal scan) over one batch of synthetic
+inputs already resident in HBM.  Default workload: the long-context
+bidirectional case (B1 H32 N32768 d_r64 d_v128 K128, bf16 inputs, skewed
+parameters).  Prints one JSON line.
+
+Roofline: the dominant kernel's algorithmic bytes per launch divided by its
+average duration, measured with hipEvents the library records around each of
+its launches on the launch stream during the timed region, against MI355X's
+8 TB/s HBM peak.  cpu_baseline: the fp64 oracle on a bounded sample of the
+same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GMA fwd tokens·heads/s at N=32K,K=128; % of HBM/MFMA roofline"
+UNIT = "tokens·heads/s"
+HBM_PEAK_GBS = 8000.0
+
+
+def kernel_bytes(name: str, w, s_in: int, s_out: int) -> int:
+    """Algorithmic HBM bytes of one launch of `name` on workload w."""
+    T = w.B * w.H * w.N
+    if name == "gma_write":
+        return T * (w.d_r + w.d_v) * s_in
+    if name == "gma_read":
+        return T * (w.d_r * s_in + w.d_v * s_out)
+    if name == "gma_causal":
+        return T * ((2 * w.d_r + w.d_v) * s_in + w.d_v * s_out)
+    return 0
+
+
+def traffic_from_profile(kernel: str, workload: str, src_hash: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_counters.json" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except ValueError:
+        return None
+    if d.get("source_sha256") != src_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gaussian_mixture_sequence_gma_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
+
+
+def cpu_baseline(w, gen, max_threads: int = 16):
+    import numpy as np
+    import oracle
+    threads = max(1, min(max_threads, os.cpu_count() or 1))
+    heads = min(w.H, 2 * threads)
+    sl = slice(0, heads)
+    if w.d_model > 0:
+        return None
+    t0 = time.perf_counter()
+    oracle.forward(gen["Q"].f32[:1, sl], gen["K"].f32[:1, sl], gen["V"].f32[:1, sl],
+                   gen["mu"][sl], gen["log_sigma2"][sl], gen["log_pi"][sl], w.eps, w.causal,
+                   nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": heads * w.N / dt, "unit": UNIT, "cores": min(threads, heads),
+            "kind": "oracle",
+            "sample": "batch 0, heads 0..%d of %d at full N=%d (%s), fp64, %.1f s"
+                      % (heads - 1, w.H, w.N, "causal" if w.causal else "bidirectional", dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_bidir_bf16")
+    ap.add_argument("--causal", type=int, default=None, help="override the workload's variant")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested; run with --gpus 1)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gaussian_mixture_sequence_gma_amd import api, binding, inputs
+
+    w = inputs.WORKLOADS[args.workload]
+    if args.causal is not None:
+        w = w.with_(causal=bool(args.causal))
+    binding.load()
+    dev = torch.device("cuda:0")
+    gen = inputs.generate(w, 0)
+    s_in = 2 if w.dtype == "bf16" else 4
+    s_out = s_in
+
+    if w.d_model > 0:
+        X = api.host_tensor_to_device(gen["X"], dev)
+        WQ = api.host_tensor_to_device(gen["W_Q"], dev)
+        WK = api.host_tensor_to_device(gen["W_K"], dev)
+        WV = api.host_tensor_to_device(gen["W_V"], dev)
+    else:
+        Q = api.host_tensor_to_device(gen["Q"], dev)
+        K = api.host_tensor_to_device(gen["K"], dev)
+        V = api.host_tensor_to_device(gen["V"], dev)
+    mu = torch.from_numpy(gen["mu"]).to(dev)
+    ls2 = torch.from_numpy(gen["log_sigma2"]).to(dev)
+    lpi = torch.from_numpy(gen["log_pi"]).to(dev)
+    out_dtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    out = torch.empty((w.B, w.H, w.N, w.d_v), dtype=out_dtype, device=dev)
+    dims = binding.make_dims(w.B, w.H, w.N, w.d_r, w.d_v, w.K,
+                             binding.GMA_BF16 if w.dtype == "bf16" else binding.GMA_F32,
+                             w.chunk)
+    if w.d_model > 0:
+        nbytes = binding.gma_layer_workspace_bytes(dims, w.d_model, int(w.causal))
+    else:
+        nbytes = binding.gma_forward_workspace_bytes(dims, int(w.causal))
+    ws = api.alloc_workspace(nbytes, dev)
+
+    def step():
+        if w.d_model > 0:
+            binding.gma_layer_forward(X, WQ, WK, WV, w.d_model, mu, ls2, lpi, w.eps,
+                                      int(w.causal), out, dims, None, None, ws, ws.numel())
+        else:
+            binding.gma_forward(Q, K, V, mu, ls2, lpi, w.eps, int(w.causal), out, dims,
+                                None, None, ws, ws.numel())
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    binding.gma_timing_collect()            # discard anything left over
+    binding.gma_timing_enable(True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    binding.gma_timing_enable(False)
+    ms = ev0.elapsed_time(ev1) / args.steps
+    kt = binding.gma_timing_collect()
+    value = w.tokens_heads / (ms * 1e-3)
+
+    kernels = {name: {"launches": n, "avg_us": 1e3 * tot / max(n, 1)} for name, n, tot in kt}
+    dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
+    dom_bytes = kernel_bytes(dom, w, s_in, s_out)
+    achieved = dom_bytes / (kernels[dom]["avg_us"] * 1e-6) / 1e9 if dom_bytes else None
+    traffic = traffic_from_profile(dom, w.name, kernel_source_hash())
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
+                "traffic": traffic, "alg_bytes_per_launch": dom_bytes}
+    step_bytes = sum(kernel_bytes(k, w, s_in, s_out) for k in kernels)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, gen)
+
+    cfg = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d_r": w.d_r, "d_v": w.d_v,
+           "K": w.K, "causal": bool(w.causal), "inputs": w.dtype, "eps": w.eps,
+           "kernel_avg_us": {k: round(v["avg_us"], 2) for k, v in kernels.items()},
+           "step_hbm_frac": (step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS) if step_bytes else None}
+    if w.d_model:
+        cfg["d_model"] = w.d_model
+    line = {"metric": METRIC, "value": value, "unit": UNIT, "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+            "data": "synthetic (seeded normal routing vectors/values, random mixture parameters)",
+            "config": cfg, "roofline": roofline, "cpu_baseline": cpu}
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

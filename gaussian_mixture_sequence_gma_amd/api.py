@@ -1,0 +1,94 @@
+"""Convenience layer over the C ABI: derives gma_dims from tensor shapes and
+allocates outputs and workspace with torch (device memory plumbing only).
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+
+def torch_dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return B.GMA_BF16
+    if t.dtype == torch.float32:
+        return B.GMA_F32
+    raise TypeError("unsupported dtype %s (bfloat16 or float32)" % t.dtype)
+
+
+def host_tensor_to_device(t, device) -> torch.Tensor:
+    """Upload a generated inputs.Tensor (bf16 bits or float32 values)."""
+    if getattr(t, "bf16_bits", None) is not None:
+        bits = torch.from_numpy(np.ascontiguousarray(t.bf16_bits).view(np.int16))
+        return bits.to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(t.f32)).to(device)
+
+
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, mu: torch.Tensor,
+            log_sigma2: torch.Tensor, log_pi: torch.Tensor, eps: float = 1e-6,
+            causal: bool = False, assign: bool = False, chunk: int = 0,
+            workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+            stream=None):
+    """O (and optionally z^Q, z^K) for Q, K [B,H,N,d_r], V [B,H,N,d_v]."""
+    Bb, H, N, d_r = Q.shape
+    d_v = V.shape[-1]
+    Kc = mu.shape[1]
+    dims = B.make_dims(Bb, H, N, d_r, d_v, Kc, torch_dtype_code(Q), chunk)
+    need = B.gma_forward_workspace_bytes(dims, int(causal))
+    if workspace is None or workspace.numel() < need:
+        workspace = alloc_workspace(need, Q.device)
+    if out is None:
+        out = torch.empty((Bb, H, N, d_v), dtype=V.dtype, device=V.device)
+    aq = ak = None
+    if assign:
+        aq = torch.empty((Bb, H, N), dtype=torch.int32, device=Q.device)
+        ak = torch.empty((Bb, H, N), dtype=torch.int32, device=Q.device)
+    B.gma_forward(Q, K, V, mu, log_sigma2, log_pi, eps, int(causal), out, dims, aq, ak,
+                  workspace, workspace.numel(), stream)
+    return (out, aq, ak) if assign else out
+
+
+def layer_forward(X: torch.Tensor, W_Q: torch.Tensor, W_K: torch.Tensor, W_V: torch.Tensor,
+                  H: int, mu: torch.Tensor, log_sigma2: torch.Tensor, log_pi: torch.Tensor,
+                  eps: float = 1e-6, causal: bool = True, assign: bool = False,
+                  workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                  stream=None):
+    Bb, N, d_model = X.shape
+    d_r = W_Q.shape[1] // H
+    d_v = W_V.shape[1] // H
+    Kc = mu.shape[1]
+    dims = B.make_dims(Bb, H, N, d_r, d_v, Kc, torch_dtype_code(X))
+    need = B.gma_layer_workspace_bytes(dims, d_model, int(causal))
+    if workspace is None or workspace.numel() < need:
+        workspace = alloc_workspace(need, X.device)
+    if out is None:
+        out = torch.empty((Bb, H, N, d_v), dtype=X.dtype, device=X.device)
+    aq = ak = None
+    if assign:
+        aq = torch.empty((Bb, H, N), dtype=torch.int32, device=X.device)
+        ak = torch.empty((Bb, H, N), dtype=torch.int32, device=X.device)
+    B.gma_layer_forward(X, W_Q, W_K, W_V, d_model, mu, log_sigma2, log_pi, eps, int(causal),
+                        out, dims, aq, ak, workspace, workspace.numel(), stream)
+    return (out, aq, ak) if assign else out
+
+
+def responsibilities(X: torch.Tensor, mu: torch.Tensor, log_sigma2: torch.Tensor,
+                     log_pi: torch.Tensor, stream=None):
+    """gamma [B,H,N,K] fp32 and z [B,H,N] int32 for X [B,H,N,d_r]."""
+    Bb, H, N, d_r = X.shape
+    Kc = mu.shape[1]
+    dims = B.make_dims(Bb, H, N, d_r, 16, Kc, torch_dtype_code(X))
+    need = B.gma_forward_workspace_bytes(dims, 0)
+    ws = alloc_workspace(need, X.device)
+    gamma = torch.empty((Bb, H, N, Kc), dtype=torch.float32, device=X.device)
+    assign = torch.empty((Bb, H, N), dtype=torch.int32, device=X.device)
+    B.gma_responsibilities(X, mu, log_sigma2, log_pi, dims, gamma, assign, ws, ws.numel(),
+                           stream)
+    return gamma, assign

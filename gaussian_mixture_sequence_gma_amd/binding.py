@@ -1,0 +1,175 @@
+"""Thin ctypes binding of libgma.so (include/gma.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  Functions carry the C names; tensors are torch
+tensors (device memory for the gma_* calls), or None for optional arguments.
+A nonzero status raises GmaError with the library's message.  There is no
+fallback: if libgma.so is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import List, Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgma.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "gma.h")
+
+GMA_F32, GMA_BF16 = 0, 1
+GMA_OK, GMA_ERR_INVALID_ARG, GMA_ERR_UNSUPPORTED, GMA_ERR_WORKSPACE, GMA_ERR_HIP = range(5)
+
+
+class GmaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s (%s)" % (message, status_name(status)))
+        self.status = status
+
+
+class gma_dims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("d_r", ctypes.c_int32), ("d_v", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("chunk", ctypes.c_int32)]
+
+
+class gma_kernel_time(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int64),
+                ("total_ms", ctypes.c_double)]
+
+
+_lib = None
+
+
+def load():
+    """Load libgma.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libgma.so not found at %s; build it with "
+                           "`python -m gaussian_mixture_sequence_gma_amd.build`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, S = ctypes.c_void_p, ctypes.c_size_t
+    i32, f32 = ctypes.c_int, ctypes.c_float
+    D = ctypes.POINTER(gma_dims)
+    lib.gma_validate.argtypes = [D, f32, i32]
+    lib.gma_forward_workspace_bytes.argtypes = [D, i32, ctypes.POINTER(S)]
+    lib.gma_forward.argtypes = [P, P, P, P, P, P, f32, i32, P, D, P, P, P, S, P]
+    lib.gma_layer_workspace_bytes.argtypes = [D, ctypes.c_int32, i32, ctypes.POINTER(S)]
+    lib.gma_layer_forward.argtypes = [P, P, P, P, ctypes.c_int32, P, P, P, f32, i32, P, D, P, P,
+                                      P, S, P]
+    lib.gma_responsibilities.argtypes = [P, P, P, P, D, P, P, P, S, P]
+    lib.gma_status_string.argtypes = [i32]
+    lib.gma_status_string.restype = ctypes.c_char_p
+    lib.gma_last_error.argtypes = []
+    lib.gma_last_error.restype = ctypes.c_char_p
+    lib.gma_timing_enable.argtypes = [i32]
+    lib.gma_timing_collect.argtypes = [ctypes.POINTER(gma_kernel_time), i32,
+                                       ctypes.POINTER(ctypes.c_int)]
+    for fn in ("gma_validate", "gma_forward_workspace_bytes", "gma_forward",
+               "gma_layer_workspace_bytes", "gma_layer_forward", "gma_responsibilities",
+               "gma_timing_enable", "gma_timing_collect"):
+        getattr(lib, fn).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def declared_functions() -> List[str]:
+    """Names of the functions include/gma.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w ]+?\*?\s*\b(gma_\w+)\s*\(", text, re.M)))
+
+
+def status_name(status: int) -> str:
+    return load().gma_status_string(int(status)).decode()
+
+
+def _check(status: int):
+    if status != GMA_OK:
+        raise GmaError(status, load().gma_last_error().decode())
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_dims(B, H, N, d_r, d_v, K, dtype, chunk=0) -> gma_dims:
+    return gma_dims(int(B), int(H), int(N), int(d_r), int(d_v), int(K), int(dtype), int(chunk))
+
+
+# ---- C entry points ------------------------------------------------------------
+
+def gma_validate(dims: gma_dims, eps: float, causal: int) -> int:
+    return load().gma_validate(ctypes.byref(dims), float(eps), int(causal))
+
+
+def gma_forward_workspace_bytes(dims: gma_dims, causal: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().gma_forward_workspace_bytes(ctypes.byref(dims), int(causal), ctypes.byref(n)))
+    return n.value
+
+
+def gma_forward(Q_X, K_X, V_X, mu, log_sigma2, log_pi, eps, causal, out, dims: gma_dims,
+                assign_q=None, assign_k=None, workspace=None, workspace_bytes=0, stream=None):
+    _check(load().gma_forward(_ptr(Q_X), _ptr(K_X), _ptr(V_X), _ptr(mu), _ptr(log_sigma2),
+                              _ptr(log_pi), float(eps), int(causal), _ptr(out),
+                              ctypes.byref(dims), _ptr(assign_q), _ptr(assign_k),
+                              _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def gma_layer_workspace_bytes(dims: gma_dims, d_model: int, causal: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().gma_layer_workspace_bytes(ctypes.byref(dims), int(d_model), int(causal),
+                                            ctypes.byref(n)))
+    return n.value
+
+
+def gma_layer_forward(X, W_Q, W_K, W_V, d_model, mu, log_sigma2, log_pi, eps, causal, out,
+                      dims: gma_dims, assign_q=None, assign_k=None, workspace=None,
+                      workspace_bytes=0, stream=None):
+    _check(load().gma_layer_forward(_ptr(X), _ptr(W_Q), _ptr(W_K), _ptr(W_V), int(d_model),
+                                    _ptr(mu), _ptr(log_sigma2), _ptr(log_pi), float(eps),
+                                    int(causal), _ptr(out), ctypes.byref(dims), _ptr(assign_q),
+                                    _ptr(assign_k), _ptr(workspace), int(workspace_bytes),
+                                    _stream(stream)))
+
+
+def gma_responsibilities(X_r, mu, log_sigma2, log_pi, dims: gma_dims, gamma=None, assign=None,
+                         workspace=None, workspace_bytes=0, stream=None):
+    _check(load().gma_responsibilities(_ptr(X_r), _ptr(mu), _ptr(log_sigma2), _ptr(log_pi),
+                                       ctypes.byref(dims), _ptr(gamma), _ptr(assign),
+                                       _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def gma_status_string(status: int) -> str:
+    return status_name(status)
+
+
+def gma_last_error() -> str:
+    return load().gma_last_error().decode()
+
+
+def gma_timing_enable(enable: bool):
+    _check(load().gma_timing_enable(1 if enable else 0))
+
+
+def gma_timing_collect(max_entries: int = 32) -> List[Tuple[str, int, float]]:
+    arr = (gma_kernel_time * max_entries)()
+    cnt = ctypes.c_int(0)
+    _check(load().gma_timing_collect(arr, max_entries, ctypes.byref(cnt)))
+    return [(arr[i].name.decode(), int(arr[i].launches), float(arr[i].total_ms))
+            for i in range(min(cnt.value, max_entries))]

@@ -1,0 +1,369 @@
+// C ABI of the GMA library: validation, planning, workspace layout, launch
+// sequencing, status strings and the kernel-timing facility.  See include/gma.h.
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "gma.h"
+#include "gma_internal.h"
+
+namespace gma {
+
+launch_hook_t g_launch_hook = nullptr;
+
+namespace {
+
+thread_local std::string t_err;
+
+int fail(int status, const std::string& msg) {
+  t_err = msg;
+  return status;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool supported_dim(int v) { return v == 16 || v == 32 || v == 64 || v == 128; }
+
+int check_dims(const gma_dims* d, float eps, int causal) {
+  if (!d) return fail(GMA_ERR_INVALID_ARG, "dims is NULL");
+  if (d->B < 1 || d->H < 1 || d->N < 1) return fail(GMA_ERR_INVALID_ARG, "B, H and N must be >= 1");
+  if (d->d_r < 1 || d->d_v < 1 || d->K < 1)
+    return fail(GMA_ERR_INVALID_ARG, "d_r, d_v and K must be >= 1");
+  if (d->dtype != GMA_F32 && d->dtype != GMA_BF16) return fail(GMA_ERR_INVALID_ARG, "unknown dtype");
+  if (d->chunk < 0) return fail(GMA_ERR_INVALID_ARG, "chunk must be >= 0");
+  if (causal != 0 && causal != 1) return fail(GMA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (!(eps >= 0.f) || !isfinite(eps)) return fail(GMA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (!supported_dim(d->d_r)) return fail(GMA_ERR_UNSUPPORTED, "d_r must be 16, 32, 64 or 128");
+  if (!supported_dim(d->d_v)) return fail(GMA_ERR_UNSUPPORTED, "d_v must be 16, 32, 64 or 128");
+  if (d->K > 128) return fail(GMA_ERR_UNSUPPORTED, "K above 128 is not supported");
+  if (d->chunk != 0 && d->chunk != 64) return fail(GMA_ERR_UNSUPPORTED, "chunk must be 0 or 64");
+  const int64_t lim = (int64_t)1 << 40;
+  if (d->B > lim / d->H) return fail(GMA_ERR_UNSUPPORTED, "B*H too large");
+  const int64_t BH = d->B * d->H;
+  if (BH > 65535) return fail(GMA_ERR_UNSUPPORTED, "B*H above 65535 is not supported");
+  if (d->N > lim / (BH * 128)) return fail(GMA_ERR_UNSUPPORTED, "B*H*N*d too large");
+  return GMA_OK;
+}
+
+int make_plan(const gma_dims* d, int causal, bool fp32_compute, Plan& p) {
+  int st = check_dims(d, 0.f, causal);
+  if (st != GMA_OK) return st;
+  p = Plan{};
+  p.bf = !fp32_compute && d->dtype == GMA_BF16;
+  p.out_bf = d->dtype == GMA_BF16;
+  p.B = d->B;
+  p.H = d->H;
+  p.N = d->N;
+  p.BH = d->B * d->H;
+  p.DR = d->d_r;
+  p.DV = d->d_v;
+  p.K = d->K;
+  int ct = (d->K + 15) / 16, ct2 = 1;
+  while (ct2 < ct) ct2 *= 2;
+  p.CT = ct2;
+  switch (p.CT) {
+    case 1: p.CPW = 1; p.NG = 1; break;
+    case 2: p.CPW = 2; p.NG = 1; break;
+    case 4: p.CPW = 2; p.NG = 2; break;
+    default: p.CPW = 2; p.NG = 4; break;
+  }
+  p.Kp = 16 * p.CT;
+  const int cs = p.bf ? 32 : 16;
+  p.DRP = p.DR < cs ? cs : p.DR;
+  p.TG = 4 / p.NG;
+  p.tiles = (p.N + 63) / 64;
+  // About two workgroups per compute unit (256 CUs) for each streaming kernel.
+  int64_t want = (512 + p.BH - 1) / p.BH;
+  if (want < 1) want = 1;
+  if (want > p.tiles) want = p.tiles;
+  p.tiles_per_split = (int)((p.tiles + want - 1) / want);
+  p.S = (int)((p.tiles + p.tiles_per_split - 1) / p.tiles_per_split);
+  // causal spans: a span is the unit one workgroup scans sequentially
+  {
+    int64_t want_c = (1024 + p.BH - 1) / p.BH;
+    if (want_c < 1) want_c = 1;
+    if (want_c > p.tiles) want_c = p.tiles;
+    p.span_tiles = (int)((p.tiles + want_c - 1) / want_c);
+    p.nspan = (int)((p.tiles + p.span_tiles - 1) / p.span_tiles);
+  }
+  p.head_bytes = round256((size_t)8 * p.Kp * p.DRP + (size_t)4 * p.Kp);
+  size_t off = 0;
+  p.off_params = off;
+  off += round256(p.head_bytes * (size_t)p.H);
+  if (!causal) {
+    const size_t PS = (size_t)p.S * p.TG;
+    p.off_partial = off;
+    off += round256((size_t)p.BH * PS * p.Kp * p.DV * 4);
+    p.off_partial_z = off;
+    off += round256((size_t)p.BH * PS * p.Kp * 4);
+    p.off_vt = off;
+    off += round256((size_t)p.BH * p.Kp * p.DV * 4);
+    p.off_z = off;
+    off += round256((size_t)p.BH * p.Kp * 4);
+  } else {
+    const size_t ns = (size_t)p.nspan;
+    p.off_state = off;
+    off += round256((size_t)p.BH * ns * p.Kp * p.DV * 4);
+    p.off_state_z = off;
+    off += round256((size_t)p.BH * ns * p.Kp * 4);
+    p.off_carry = off;
+    off += round256((size_t)p.BH * ns * p.Kp * p.DV * 4);
+    p.off_carry_z = off;
+    off += round256((size_t)p.BH * ns * p.Kp * 4);
+  }
+  p.total = off;
+  return GMA_OK;
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
+
+// ---- timing ----------------------------------------------------------------
+struct Pending {
+  const char* tag;
+  hipEvent_t start, stop;
+};
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<Pending> g_pending;
+Pending g_open{};
+struct Total {
+  std::string name;
+  int64_t launches;
+  double ms;
+};
+std::vector<Total> g_totals;
+
+void timing_hook(const char* tag, hipStream_t s, int begin) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (begin) {
+    g_open.tag = tag;
+    hipEventCreate(&g_open.start);
+    hipEventCreate(&g_open.stop);
+    hipEventRecord(g_open.start, s);
+  } else {
+    hipEventRecord(g_open.stop, s);
+    g_pending.push_back(g_open);
+  }
+}
+
+int finish_launch(hipError_t e, const char* what) {
+  if (e != hipSuccess)
+    return fail(GMA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  if (getenv("GMA_SYNC_DEBUG")) {
+    e = hipDeviceSynchronize();
+    if (e != hipSuccess)
+      return fail(GMA_ERR_HIP, std::string(what) + " (synchronised): " + hipGetErrorString(e));
+  }
+  return GMA_OK;
+}
+
+}  // namespace
+}  // namespace gma
+
+using namespace gma;
+
+extern "C" {
+
+int gma_validate(const gma_dims* d, float eps, int causal) {
+  t_err.clear();
+  return check_dims(d, eps, causal);
+}
+
+int gma_forward_workspace_bytes(const gma_dims* d, int causal, size_t* bytes) {
+  t_err.clear();
+  if (!bytes) return fail(GMA_ERR_INVALID_ARG, "bytes is NULL");
+  Plan p;
+  int st = make_plan(d, causal, false, p);
+  if (st != GMA_OK) return st;
+  *bytes = p.total;
+  return GMA_OK;
+}
+
+static int forward_impl(const Plan& p, const Tensors& t, int causal, hipStream_t s) {
+  hipError_t e = launch_prologue(p, t, s);
+  if (e != hipSuccess) return finish_launch(e, "prologue launch");
+  e = causal ? launch_causal(p, t, s) : launch_bidir(p, t, s);
+  return finish_launch(e, causal ? "causal launch" : "bidirectional launch");
+}
+
+int gma_forward(const void* Q_X, const void* K_X, const void* V_X, const float* mu,
+                const float* log_sigma2, const float* log_pi, float eps, int causal, void* out,
+                const gma_dims* d, int32_t* assign_q, int32_t* assign_k, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  t_err.clear();
+  int st = check_dims(d, eps, causal);
+  if (st != GMA_OK) return st;
+  if (!Q_X || !K_X || !V_X || !mu || !log_sigma2 || !log_pi || !out || !workspace)
+    return fail(GMA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(Q_X) || !aligned16(K_X) || !aligned16(V_X) || !aligned16(out) ||
+      !aligned16(workspace) || !aligned16(mu) || !aligned16(log_sigma2) ||
+      ((uintptr_t)log_pi & 3) || ((uintptr_t)assign_q & 3) || ((uintptr_t)assign_k & 3))
+    return fail(GMA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  Plan p;
+  st = make_plan(d, causal, false, p);
+  if (st != GMA_OK) return st;
+  if (workspace_bytes < p.total) return fail(GMA_ERR_WORKSPACE, "workspace too small");
+  Tensors t;
+  t.q = Q_X;
+  t.k = K_X;
+  t.v = V_X;
+  t.mu = mu;
+  t.ls2 = log_sigma2;
+  t.lpi = log_pi;
+  t.out = out;
+  t.assign_q = assign_q;
+  t.assign_k = assign_k;
+  t.eps = eps;
+  t.ws = static_cast<char*>(workspace);
+  return forward_impl(p, t, causal, static_cast<hipStream_t>(stream));
+}
+
+int gma_layer_workspace_bytes(const gma_dims* d, int32_t d_model, int causal, size_t* bytes) {
+  t_err.clear();
+  if (!bytes) return fail(GMA_ERR_INVALID_ARG, "bytes is NULL");
+  Plan p;
+  int st = make_plan(d, causal, true, p);
+  if (st != GMA_OK) return st;
+  if (d_model < 64 || d_model > 8192 || d_model % 64)
+    return fail(GMA_ERR_UNSUPPORTED, "d_model must be a multiple of 64 in 64..8192");
+  const size_t proj = round256((size_t)p.BH * p.N * (2 * p.DR + p.DV) * 4);
+  *bytes = round256(p.total) + proj;
+  return GMA_OK;
+}
+
+int gma_layer_forward(const void* X, const void* W_Q, const void* W_K, const void* W_V,
+                      int32_t d_model, const float* mu, const float* log_sigma2,
+                      const float* log_pi, float eps, int causal, void* out, const gma_dims* d,
+                      int32_t* assign_q, int32_t* assign_k, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  t_err.clear();
+  int st = check_dims(d, eps, causal);
+  if (st != GMA_OK) return st;
+  if (d->dtype != GMA_BF16) return fail(GMA_ERR_UNSUPPORTED, "the projection layer takes bf16 X and W");
+  if (d_model < 64 || d_model > 8192 || d_model % 64)
+    return fail(GMA_ERR_UNSUPPORTED, "d_model must be a multiple of 64 in 64..8192");
+  if (!X || !W_Q || !W_K || !W_V || !mu || !log_sigma2 || !log_pi || !out || !workspace)
+    return fail(GMA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(X) || !aligned16(W_Q) || !aligned16(W_K) || !aligned16(W_V) || !aligned16(out) ||
+      !aligned16(workspace) || !aligned16(mu) || !aligned16(log_sigma2) ||
+      ((uintptr_t)log_pi & 3) || ((uintptr_t)assign_q & 3) || ((uintptr_t)assign_k & 3))
+    return fail(GMA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  Plan p;
+  st = make_plan(d, causal, true, p);
+  if (st != GMA_OK) return st;
+  const size_t gma_bytes = round256(p.total);
+  const size_t proj = round256((size_t)p.BH * p.N * (2 * p.DR + p.DV) * 4);
+  if (workspace_bytes < gma_bytes + proj) return fail(GMA_ERR_WORKSPACE, "workspace too small");
+  char* ws = static_cast<char*>(workspace);
+  float* q = reinterpret_cast<float*>(ws + gma_bytes);
+  float* k = q + (size_t)p.BH * p.N * p.DR;
+  float* v = k + (size_t)p.BH * p.N * p.DR;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t M = p.B * p.N;
+  hipError_t e = launch_proj(X, W_Q, M, d_model, (int)(p.H * p.DR), (int)p.H, p.DR, p.N, q, s);
+  if (e == hipSuccess) e = launch_proj(X, W_K, M, d_model, (int)(p.H * p.DR), (int)p.H, p.DR, p.N, k, s);
+  if (e == hipSuccess) e = launch_proj(X, W_V, M, d_model, (int)(p.H * p.DV), (int)p.H, p.DV, p.N, v, s);
+  st = finish_launch(e, "projection launch");
+  if (st != GMA_OK) return st;
+  Tensors t;
+  t.q = q;
+  t.k = k;
+  t.v = v;
+  t.mu = mu;
+  t.ls2 = log_sigma2;
+  t.lpi = log_pi;
+  t.out = out;
+  t.assign_q = assign_q;
+  t.assign_k = assign_k;
+  t.eps = eps;
+  t.ws = ws;
+  return forward_impl(p, t, causal, s);
+}
+
+int gma_responsibilities(const void* X_r, const float* mu, const float* log_sigma2,
+                         const float* log_pi, const gma_dims* d, float* gamma, int32_t* assign,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  t_err.clear();
+  int st = check_dims(d, 0.f, 0);
+  if (st != GMA_OK) return st;
+  if (!X_r || !mu || !log_sigma2 || !log_pi || !workspace)
+    return fail(GMA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(X_r) || !aligned16(workspace) || !aligned16(mu) || !aligned16(log_sigma2) ||
+      ((uintptr_t)log_pi & 3) || ((uintptr_t)gamma & 3) || ((uintptr_t)assign & 3))
+    return fail(GMA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  Plan p;
+  st = make_plan(d, 0, false, p);
+  if (st != GMA_OK) return st;
+  if (workspace_bytes < p.total) return fail(GMA_ERR_WORKSPACE, "workspace too small");
+  Tensors t;
+  t.q = X_r;
+  t.mu = mu;
+  t.ls2 = log_sigma2;
+  t.lpi = log_pi;
+  t.gamma = gamma;
+  t.assign_q = assign;
+  t.ws = static_cast<char*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_prologue(p, t, s);
+  if (e == hipSuccess) e = launch_resp(p, t, s);
+  return finish_launch(e, "responsibility launch");
+}
+
+const char* gma_status_string(int status) {
+  switch (status) {
+    case GMA_OK: return "GMA_OK";
+    case GMA_ERR_INVALID_ARG: return "GMA_ERR_INVALID_ARG: invalid argument";
+    case GMA_ERR_UNSUPPORTED: return "GMA_ERR_UNSUPPORTED: shape outside the supported set";
+    case GMA_ERR_WORKSPACE: return "GMA_ERR_WORKSPACE: workspace too small";
+    case GMA_ERR_HIP: return "GMA_ERR_HIP: HIP runtime or launch failure";
+    default: return "unknown gma status";
+  }
+}
+
+const char* gma_last_error(void) { return t_err.c_str(); }
+
+int gma_timing_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_timing = enable != 0;
+  g_launch_hook = g_timing ? timing_hook : nullptr;
+  return GMA_OK;
+}
+
+int gma_timing_collect(gma_kernel_time* out, int max, int* count) {
+  t_err.clear();
+  std::vector<Pending> pend;
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    pend.swap(g_pending);
+  }
+  std::vector<Total> totals;
+  for (auto& pe : pend) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(pe.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, pe.start, pe.stop);
+    hipEventDestroy(pe.start);
+    hipEventDestroy(pe.stop);
+    if (e != hipSuccess) return fail(GMA_ERR_HIP, std::string("timing: ") + hipGetErrorString(e));
+    bool found = false;
+    for (auto& tt : totals)
+      if (tt.name == pe.tag) {
+        tt.launches += 1;
+        tt.ms += ms;
+        found = true;
+      }
+    if (!found) totals.push_back(Total{pe.tag, 1, (double)ms});
+  }
+  if (count) *count = (int)totals.size();
+  for (int i = 0; out && i < max && i < (int)totals.size(); ++i) {
+    memset(out[i].name, 0, sizeof(out[i].name));
+    strncpy(out[i].name, totals[i].name.c_str(), sizeof(out[i].name) - 1);
+    out[i].launches = totals[i].launches;
+    out[i].total_ms = totals[i].ms;
+  }
+  return GMA_OK;
+}
+
+}  // extern "C"

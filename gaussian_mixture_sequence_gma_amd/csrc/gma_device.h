@@ -1,0 +1,157 @@
+// Device-side building blocks for the gfx950 GMA kernels.
+//
+// Notation follows "Gaussian Mixture Attention: Linear-Time Sequence Mixing via
+// Probabilistic Latent Routing": K components, routing dimension d_r, value
+// dimension d_v, responsibilities gamma (Eq. 3), latent memory V~ and
+// normaliser Z (Eqs. 5-6), read-out O (Eq. 7).
+//
+// MFMA shapes used (CDNA4 / gfx950):
+//   v_mfma_f32_16x16x32_bf16  A 16x32, B 32x16, D 16x16 fp32
+//   v_mfma_f32_16x16x4_f32    A 16x4,  B 4x16,  D 16x16 fp32
+// Operand registers: lane l holds row/column (l % 16) of A/B and contraction
+// indices g*E .. g*E+E-1 of one "chunk" (g = l / 16, E = 8 bf16 or 4 fp32,
+// i.e. 16 bytes per lane).  A bf16 chunk is one MFMA; an fp32 chunk is four
+// k=4 MFMAs that pair element e of A with element e of B.  Either way a chunk
+// contracts CS = 4*E indices and needs one 16-byte load per operand.
+// D layout: lane l holds column (l % 16), rows 4*(l/16) + i, i = 0..3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+namespace gma {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = 64;        // tokens per workgroup tile (four 16-token MFMA tiles)
+constexpr int kWaves = 4;        // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr double kLog2eD = 1.44269504088896340736;
+
+// Token permutation inside a 64-token tile.  MFMA tile gt (0..3), row r = 4g+i
+// maps to token 32*(gt/2) + 8g + 4*(gt%2) + i.  With it, the four rows a lane
+// holds in D layout are consecutive tokens, and the union over a pair of
+// tiles (2p, 2p+1) gives lane group g the eight consecutive tokens
+// 32p + 8g .. 32p + 8g + 7 -- exactly one bf16 operand chunk when the token
+// index is the contraction index.
+__host__ __device__ constexpr int tile_token(int gt, int r) {
+  return 32 * (gt >> 1) + 8 * (r >> 2) + 4 * (gt & 1) + (r & 3);
+}
+
+template <bool BF> struct Prec;
+template <> struct Prec<true> {        // bf16 storage, split-bf16 MFMA arithmetic
+  using in_t = bf16;
+  using op_t = bf16;
+  using chunk_t = bf16x8;
+  static constexpr int E = 8;
+  static constexpr int CS = 32;
+  static constexpr int NARR = 4;       // A_hi, A_lo, B_hi, B_lo
+};
+template <> struct Prec<false> {       // fp32 storage, fp32 MFMA arithmetic
+  using in_t = float;
+  using op_t = float;
+  using chunk_t = f32x4;
+  static constexpr int E = 4;
+  static constexpr int CS = 16;
+  static constexpr int NARR = 2;       // A, B
+};
+
+__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(f32x4 a, f32x4 b, f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+  return c;
+}
+
+template <class T>
+__device__ __forceinline__ T ld16(const void* p) {
+  return *reinterpret_cast<const T*>(__builtin_assume_aligned(p, 16));
+}
+template <class T>
+__device__ __forceinline__ void st16(void* p, T v) {
+  *reinterpret_cast<T*>(__builtin_assume_aligned(p, 16)) = v;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- cross-lane reductions ------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+// Butterfly over the 16 lanes of a DPP row; every lane receives the result
+// (each step pairs lanes symmetrically, so all lanes compute identical values).
+#define GMA_ROW16(OP, v)            \
+  v = OP(v, dpp<0xB1>(v));          \
+  v = OP(v, dpp<0x4E>(v));          \
+  v = OP(v, dpp<0x141>(v));         \
+  v = OP(v, dpp<0x140>(v));
+
+__device__ __forceinline__ float add_f(float a, float b) { return a + b; }
+__device__ __forceinline__ float max_f(float a, float b) { return fmaxf(a, b); }
+
+__device__ __forceinline__ float row16_max(float v) { GMA_ROW16(max_f, v) return v; }
+__device__ __forceinline__ float row16_sum(float v) { GMA_ROW16(add_f, v) return v; }
+
+// Exchange with lane ^ mask (any mask < 64) through the LDS crossbar.
+__device__ __forceinline__ float xor_lane(float v, int mask) {
+  int src = (int)(threadIdx.x & 63) ^ mask;
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
+}
+__device__ __forceinline__ int xor_lane_i(int v, int mask) {
+  int src = (int)(threadIdx.x & 63) ^ mask;
+  return __builtin_amdgcn_ds_bpermute(src << 2, v);
+}
+// Reductions over the four lane groups g (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float groups_max(float v) {
+  v = fmaxf(v, xor_lane(v, 16));
+  return fmaxf(v, xor_lane(v, 32));
+}
+__device__ __forceinline__ float groups_sum(float v) {
+  v += xor_lane(v, 16);
+  return v + xor_lane(v, 32);
+}
+
+// (value, index) argmax merge, ties to the lower index.
+__device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
+  bool take = (v2 > v) || (v2 == v && i2 < i);
+  v = take ? v2 : v;
+  i = take ? i2 : i;
+}
+__device__ __forceinline__ void row16_argmax(float& v, int& i) {
+  argmax_merge(v, i, dpp<0xB1>(v), dpp_i<0xB1>(i));
+  argmax_merge(v, i, dpp<0x4E>(v), dpp_i<0x4E>(i));
+  argmax_merge(v, i, dpp<0x141>(v), dpp_i<0x141>(i));
+  argmax_merge(v, i, dpp<0x140>(v), dpp_i<0x140>(i));
+}
+__device__ __forceinline__ void groups_argmax(float& v, int& i) {
+  argmax_merge(v, i, xor_lane(v, 16), xor_lane_i(i, 16));
+  argmax_merge(v, i, xor_lane(v, 32), xor_lane_i(i, 32));
+}
+
+// ---- conversions -----------------------------------------------------------
+__device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }   // RNE
+__device__ __forceinline__ float from_bf16(bf16 x) { return (float)x; }
+
+// Split an fp32 value into bf16 hi + lo with hi + lo == x to 16 significant bits
+// (exact when x has at most 16 significant bits, e.g. the square of a bf16).
+__device__ __forceinline__ void split_bf16(float x, bf16& hi, bf16& lo) {
+  hi = (bf16)x;
+  lo = (bf16)(x - (float)hi);
+}
+
+template <class T> __device__ __forceinline__ T load_elem(const T* p) { return *p; }
+
+}  // namespace gma

@@ -1,0 +1,63 @@
+// Host-side plan and launcher declarations shared by the GMA translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gma {
+
+// Everything derived from a problem shape: padded sizes, kernel configuration,
+// split counts and the workspace layout.  Computed identically by the
+// workspace-size query and by the forward call.
+struct Plan {
+  bool bf = false;          // bf16 storage / split-bf16 arithmetic
+  bool out_bf = false;      // output element type
+  int64_t B = 0, H = 0, N = 0, BH = 0;
+  int DR = 0, DV = 0, K = 0;
+  int CT = 0;               // 16-wide component tiles (power of two)
+  int CPW = 0, NG = 0;      // component tiles per wave, component groups per workgroup
+  int Kp = 0;               // padded component count = 16 * CT
+  int DRP = 0;              // padded routing dimension (multiple of the MFMA chunk span)
+  int64_t tiles = 0;        // 64-token tiles per sequence
+  int S = 0;                // workgroups per sequence for the write and read kernels
+  int tiles_per_split = 0;
+  int TG = 0;               // token groups per workgroup (partials per split)
+  // causal
+  int span_tiles = 0;       // 64-token chunks per causal span
+  int nspan = 0;            // spans per sequence
+  // workspace layout (bytes)
+  size_t head_bytes = 0;
+  size_t off_params = 0, off_partial = 0, off_partial_z = 0, off_vt = 0, off_z = 0;
+  size_t off_state = 0, off_state_z = 0, off_carry = 0, off_carry_z = 0;
+  size_t total = 0;
+};
+
+struct Tensors {
+  const void* q = nullptr;
+  const void* k = nullptr;
+  const void* v = nullptr;
+  const float* mu = nullptr;
+  const float* ls2 = nullptr;
+  const float* lpi = nullptr;
+  void* out = nullptr;
+  int32_t* assign_q = nullptr;
+  int32_t* assign_k = nullptr;
+  float* gamma = nullptr;
+  float eps = 0.f;
+  char* ws = nullptr;
+};
+
+// Launch helpers; each returns hipSuccess or the launch error.  `tag` names the
+// kernel for the timing facility.
+typedef void (*launch_hook_t)(const char* tag, hipStream_t s, int begin);
+extern launch_hook_t g_launch_hook;
+
+hipError_t launch_prologue(const Plan& p, const Tensors& t, hipStream_t s);
+hipError_t launch_bidir(const Plan& p, const Tensors& t, hipStream_t s);
+hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s);
+hipError_t launch_resp(const Plan& p, const Tensors& t, hipStream_t s);
+hipError_t launch_proj(const void* X, const void* W, int64_t M, int d_model, int ncols,
+                       int H, int dh, int64_t N, float* out, hipStream_t s);
+
+}  // namespace gma

@@ -1,0 +1,141 @@
+/*
+ * gma.h -- C ABI of the MI355X (gfx950) Gaussian Mixture Attention forward library.
+ *
+ * Method: "Gaussian Mixture Attention: Linear-Time Sequence Mixing via
+ * Probabilistic Latent Routing" (arXiv 2606.18283).  Queries and keys are
+ * mapped to posterior responsibilities over K diagonal-Gaussian components
+ * (Section "Gaussian routing components", Eqs. 2-3, and Eq. 16 which writes
+ * the posterior as a softmax of log-prior plus log-density); keys write values
+ * into a K-slot latent memory V~ = Gamma^K^T V_X with normaliser
+ * Z = Gamma^K^T 1 (Eqs. 5-6); queries read O = Gamma^Q V~ / (Gamma^Q Z + eps)
+ * (Eq. 7 and its footnote).  The causal variant replaces V~ and Z by inclusive
+ * prefix sums over positions j <= i (Section "Causal GMA", Eq. 8b).
+ *
+ * Conventions shared by every entry point:
+ *  - Every tensor pointer is DEVICE memory owned by the caller, contiguous,
+ *    row-major, 16-byte aligned.  The library never allocates, frees, or keeps
+ *    a pointer after a call returns.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream) and never synchronise it.  Argument validation is synchronous and
+ *    happens before any launch; on a nonzero return nothing was launched
+ *    (except GMA_ERR_HIP, which reports a failed launch).
+ *  - Calls that share a workspace must not overlap in time; otherwise calls
+ *    are reentrant.  No exception crosses this interface and the library never
+ *    prints; gma_last_error() holds a message for the calling thread.
+ *  - NaN / Inf inputs are not checked and propagate.
+ */
+#ifndef GMA_H
+#define GMA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GMA_F32 = 0, GMA_BF16 = 1 } gma_dtype;
+
+typedef enum {
+  GMA_OK = 0,
+  GMA_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misalignment, eps < 0 or not finite */
+  GMA_ERR_UNSUPPORTED = 2,   /* valid but outside the supported shape set (see gma_dims) */
+  GMA_ERR_WORKSPACE = 3,     /* workspace_bytes smaller than the *_workspace_bytes figure */
+  GMA_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+} gma_status;
+
+/* Problem shape.  B batches x H heads x N positions.
+ *  d_r  routing dimension of Q_X, K_X and the component means: 16, 32, 64 or 128
+ *  d_v  value dimension of V_X and the output: 16, 32, 64 or 128
+ *  K    number of Gaussian components: 1..128
+ *  dtype storage type of Q_X, K_X, V_X and out (gma_layer_forward: of X, W and out)
+ *  chunk causal scan chunk length: 0 (= 64) or 64; the result does not depend on it */
+typedef struct gma_dims {
+  int64_t B, H, N;
+  int32_t d_r, d_v, K;
+  int32_t dtype;
+  int32_t chunk;
+} gma_dims;
+
+/* Host-only check of a shape, eps and variant; no pointer is examined.
+ * Returns GMA_OK, GMA_ERR_INVALID_ARG or GMA_ERR_UNSUPPORTED. */
+int gma_validate(const gma_dims* d, float eps, int causal);
+
+/* Bytes of device workspace gma_forward needs for this shape and variant
+ * (written to *bytes).  The same workspace also serves gma_responsibilities. */
+int gma_forward_workspace_bytes(const gma_dims* d, int causal, size_t* bytes);
+
+/* GMA forward.
+ *  Q_X, K_X    [B,H,N,d_r] of d->dtype: query and key routing vectors q_i, k_j
+ *  V_X         [B,H,N,d_v] of d->dtype: values
+ *  mu          [H,K,d_r] fp32: component means mu_k (one mixture per head, shared
+ *              by queries and keys and by every batch)
+ *  log_sigma2  [H,K,d_r] fp32: log of the diagonal covariance entries sigma^2_kd
+ *  log_pi      [H,K] fp32: log mixture priors, up to an additive constant per head
+ *              (the posterior does not depend on it; e.g. the prior logits of Eq. 15)
+ *  eps         >= 0, finite: the stabiliser of Eq. 7 (also used by the causal form)
+ *  causal      0: Eq. 7 over all keys; 1: inclusive prefix j <= i
+ *  out         [B,H,N,d_v] of d->dtype: O
+ *  assign_q    optional [B,H,N] int32: z_i = argmax_k gamma^Q_ik (lowest index on ties)
+ *  assign_k    optional [B,H,N] int32: the same for keys
+ *  workspace   device scratch of at least gma_forward_workspace_bytes bytes
+ * Arithmetic: fp32 inputs run fp32 MFMA throughout; bf16 inputs run bf16 MFMA
+ * with hi/lo operand splitting for the Gaussian scores and fp32 accumulation. */
+int gma_forward(const void* Q_X, const void* K_X, const void* V_X,
+                const float* mu, const float* log_sigma2, const float* log_pi,
+                float eps, int causal, void* out, const gma_dims* d,
+                int32_t* assign_q, int32_t* assign_k,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace gma_layer_forward needs. */
+int gma_layer_workspace_bytes(const gma_dims* d, int32_t d_model, int causal, size_t* bytes);
+
+/* Projection layer followed by the GMA forward (Section "Projections", Eq. 4:
+ * Q_X = X W_Q, K_X = X W_K, V_X = X W_V; no bias, no output projection).
+ *  X          [B,N,d_model] of d->dtype (GMA_BF16 only)
+ *  W_Q, W_K   [d_model, H*d_r] of d->dtype; head h uses columns [h*d_r, (h+1)*d_r)
+ *  W_V        [d_model, H*d_v] of d->dtype; head h uses columns [h*d_v, (h+1)*d_v)
+ *  d_model    multiple of 64, 64..8192
+ * The projections are kept in fp32 (written to the workspace) and feed the fp32
+ * GMA path; out is [B,H,N,d_v] of d->dtype.  Other arguments as gma_forward. */
+int gma_layer_forward(const void* X, const void* W_Q, const void* W_K, const void* W_V,
+                      int32_t d_model, const float* mu, const float* log_sigma2,
+                      const float* log_pi, float eps, int causal, void* out,
+                      const gma_dims* d, int32_t* assign_q, int32_t* assign_k,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Responsibilities alone (Eq. 3), for testing and diagnostics.
+ *  X_r    [B,H,N,d_r] of d->dtype; head h's parameters apply to [b,h,:,:]
+ *  gamma  optional [B,H,N,K] fp32
+ *  assign optional [B,H,N] int32 (lowest index on ties)
+ * Uses the same arithmetic as gma_forward; workspace as gma_forward_workspace_bytes. */
+int gma_responsibilities(const void* X_r, const float* mu, const float* log_sigma2,
+                         const float* log_pi, const gma_dims* d, float* gamma,
+                         int32_t* assign, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Static description of a status code. */
+const char* gma_status_string(int status);
+
+/* Message describing the last failure of a call made by this thread ("" if none). */
+const char* gma_last_error(void);
+
+/* Kernel timing (profiling aid).  While enabled, every kernel the library
+ * launches is bracketed by two hipEvents recorded on the launch stream.
+ * gma_timing_collect synchronises those events, accumulates per-kernel totals,
+ * writes up to `max` entries and the number of distinct kernels to *count,
+ * and resets the totals.  Not for use from several threads at once. */
+typedef struct gma_kernel_time {
+  char name[48];
+  int64_t launches;
+  double total_ms;
+} gma_kernel_time;
+
+int gma_timing_enable(int enable);
+int gma_timing_collect(gma_kernel_time* out, int max, int* count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GMA_H */

@@ -1,0 +1,122 @@
+"""C ABI checks that need no GPU: the library loads, exports what include/gma.h
+declares, and rejects bad arguments before any launch."""
+import ctypes
+import math
+
+import pytest
+
+from gaussian_mixture_sequence_gma_amd import binding as B
+
+pytestmark = pytest.mark.skipif(not __import__("os").path.exists(B.LIB_PATH),
+                                reason="libgma.so not built")
+
+
+def test_exports_every_declared_function():
+    lib = B.load()
+    names = B.declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _dims(**kw):
+    base = dict(B=1, H=2, N=100, d_r=64, d_v=64, K=64, dtype=B.GMA_BF16, chunk=0)
+    base.update(kw)
+    return B.make_dims(**base)
+
+
+@pytest.mark.parametrize("kw,eps,causal,status", [
+    ({}, 1e-6, 0, B.GMA_OK),
+    ({}, 0.0, 1, B.GMA_OK),
+    ({"B": 0}, 1e-6, 0, B.GMA_ERR_INVALID_ARG),
+    ({"N": 0}, 1e-6, 0, B.GMA_ERR_INVALID_ARG),
+    ({"K": 0}, 1e-6, 0, B.GMA_ERR_INVALID_ARG),
+    ({"d_r": 0}, 1e-6, 0, B.GMA_ERR_INVALID_ARG),
+    ({"dtype": 7}, 1e-6, 0, B.GMA_ERR_INVALID_ARG),
+    ({"chunk": -1}, 1e-6, 0, B.GMA_ERR_INVALID_ARG),
+    ({}, -1e-6, 0, B.GMA_ERR_INVALID_ARG),
+    ({}, float("nan"), 0, B.GMA_ERR_INVALID_ARG),
+    ({}, float("inf"), 0, B.GMA_ERR_INVALID_ARG),
+    ({}, 1e-6, 2, B.GMA_ERR_INVALID_ARG),
+    ({"d_r": 48}, 1e-6, 0, B.GMA_ERR_UNSUPPORTED),
+    ({"d_v": 256}, 1e-6, 0, B.GMA_ERR_UNSUPPORTED),
+    ({"K": 129}, 1e-6, 0, B.GMA_ERR_UNSUPPORTED),
+    ({"chunk": 32}, 1e-6, 1, B.GMA_ERR_UNSUPPORTED),
+    ({"B": 300, "H": 300}, 1e-6, 0, B.GMA_ERR_UNSUPPORTED),
+])
+def test_validate(kw, eps, causal, status):
+    assert B.gma_validate(_dims(**kw), eps, causal) == status
+    if status != B.GMA_OK:
+        assert B.gma_last_error() != ""
+
+
+def test_workspace_query_and_errors():
+    n0 = B.gma_forward_workspace_bytes(_dims(), 0)
+    n1 = B.gma_forward_workspace_bytes(_dims(N=100000), 0)
+    assert 0 < n0 < n1 and n0 % 256 == 0
+    assert B.gma_forward_workspace_bytes(_dims(), 1) > 0
+    with pytest.raises(B.GmaError) as ei:
+        B.gma_forward_workspace_bytes(_dims(K=200), 0)
+    assert ei.value.status == B.GMA_ERR_UNSUPPORTED
+    assert B.gma_layer_workspace_bytes(_dims(), 1024, 1) > B.gma_forward_workspace_bytes(_dims(), 1)
+    with pytest.raises(B.GmaError):
+        B.gma_layer_workspace_bytes(_dims(), 1000, 1)
+
+
+# Fake, never-dereferenced addresses: every call below must fail validation
+# before any HIP call is made.
+A16 = 1 << 20
+MIS = A16 + 4
+
+
+def _fwd(**over):
+    args = dict(Q_X=A16, K_X=A16, V_X=A16, mu=A16, log_sigma2=A16, log_pi=A16, eps=1e-6,
+                causal=0, out=A16, dims=_dims(), assign_q=None, assign_k=None,
+                workspace=A16, workspace_bytes=0, stream=0)
+    args.update(over)
+    with pytest.raises(B.GmaError) as ei:
+        B.gma_forward(**args)
+    return ei.value.status
+
+
+def test_forward_rejects_before_launch():
+    assert _fwd(Q_X=None) == B.GMA_ERR_INVALID_ARG
+    assert _fwd(out=None) == B.GMA_ERR_INVALID_ARG
+    assert _fwd(workspace=None) == B.GMA_ERR_INVALID_ARG
+    assert _fwd(V_X=MIS) == B.GMA_ERR_INVALID_ARG
+    assert _fwd(eps=-1.0) == B.GMA_ERR_INVALID_ARG
+    assert _fwd(dims=_dims(K=300)) == B.GMA_ERR_UNSUPPORTED
+    assert _fwd(workspace_bytes=16) == B.GMA_ERR_WORKSPACE
+
+
+def test_layer_and_resp_reject_before_launch():
+    d = _dims()
+    with pytest.raises(B.GmaError) as ei:
+        B.gma_layer_forward(A16, A16, A16, A16, 1000, A16, A16, A16, 1e-6, 1, A16, d,
+                            workspace=A16, workspace_bytes=1 << 40, stream=0)
+    assert ei.value.status == B.GMA_ERR_UNSUPPORTED
+    with pytest.raises(B.GmaError) as ei:
+        B.gma_layer_forward(A16, A16, A16, A16, 1024, A16, A16, A16, 1e-6, 1, A16,
+                            _dims(dtype=B.GMA_F32), workspace=A16, workspace_bytes=1 << 40,
+                            stream=0)
+    assert ei.value.status == B.GMA_ERR_UNSUPPORTED
+    with pytest.raises(B.GmaError) as ei:
+        B.gma_layer_forward(A16, A16, A16, A16, 1024, A16, A16, A16, 1e-6, 1, A16, d,
+                            workspace=A16, workspace_bytes=64, stream=0)
+    assert ei.value.status == B.GMA_ERR_WORKSPACE
+    with pytest.raises(B.GmaError) as ei:
+        B.gma_responsibilities(None, A16, A16, A16, d, workspace=A16, workspace_bytes=1 << 40,
+                               stream=0)
+    assert ei.value.status == B.GMA_ERR_INVALID_ARG
+
+
+def test_status_strings():
+    for s in range(5):
+        assert B.gma_status_string(s).startswith("GMA_")
+    assert "unknown" in B.gma_status_string(99)
+
+
+def test_timing_collect_empty():
+    B.gma_timing_enable(True)
+    B.gma_timing_enable(False)
+    assert B.gma_timing_collect() == []

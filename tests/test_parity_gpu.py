@@ -1,0 +1,106 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Sizes span several 64-token tiles, ragged tails, every supported d_r / d_v,
+padded component counts, and the full-size workloads in the exact launch
+configuration bench.py times (the plan is a pure function of the shape).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gaussian_mixture_sequence_gma_amd import api, inputs
+from tests.parity import TOL, run_and_compare, upload
+
+pytestmark = pytest.mark.gpu
+
+W = inputs.WORKLOADS
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gaussian_mixture_sequence_gma_amd import binding
+    binding.load()
+
+
+@pytest.mark.parametrize("name", ["tiny_bidir_f32", "lra_bidir_f32"])
+def test_workload_full_compare(name):
+    run_and_compare(W[name])
+
+
+def test_long_context_bf16_sampled_rows():
+    w = W["long_bidir_bf16"]
+    run_and_compare(w, rows=inputs.sample_rows(w.N, 512, seed=5))
+
+
+def test_lra_shape_in_bf16():
+    run_and_compare(W["lra_bidir_f32"].with_(dtype="bf16", B=2))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [1, 63, 65, 200, 1000])
+def test_ragged_lengths(dtype, N):
+    run_and_compare(W["tiny_bidir_f32"].with_(N=N, dtype=dtype, B=2, H=3))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("K", [1, 3, 8, 16, 17, 33, 64, 100, 128])
+def test_component_counts(dtype, K):
+    run_and_compare(W["tiny_bidir_f32"].with_(K=K, d_r=32, d_v=64, N=300, H=2, dtype=dtype))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d_r,d_v", [(16, 16), (16, 128), (32, 32), (64, 16), (128, 64),
+                                     (128, 128)])
+def test_head_dims(dtype, d_r, d_v):
+    run_and_compare(W["tiny_bidir_f32"].with_(d_r=d_r, d_v=d_v, K=40, N=333, dtype=dtype))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_skewed_parameters(dtype):
+    w = W["long_bidir_bf16"].with_(N=2048, H=4, dtype=dtype)
+    run_and_compare(w)
+
+
+def test_single_component_is_mean():
+    w = W["tiny_bidir_f32"].with_(K=1, N=777, H=2)
+    gen = inputs.generate(w, 3)
+    dev = upload(gen)
+    out = api.forward(dev["Q"], dev["K"], dev["V"], dev["mu"], dev["log_sigma2"],
+                      dev["log_pi"], w.eps, False).cpu().numpy()
+    V = gen["V"].f32.astype(np.float64)
+    expect = V.sum(2, keepdims=True) / (w.N + w.eps)
+    err = np.abs(out - expect).max() / np.abs(expect).max()
+    assert err < 1e-5
+
+
+def test_bitwise_deterministic():
+    w = W["lra_bidir_f32"].with_(dtype="bf16", B=1, H=4, N=4096)
+    gen = inputs.generate(w, 0)
+    dev = upload(gen)
+    outs = []
+    for _ in range(3):
+        o, aq, ak = api.forward(dev["Q"], dev["K"], dev["V"], dev["mu"], dev["log_sigma2"],
+                                dev["log_pi"], w.eps, False, assign=True)
+        outs.append((o.clone(), aq.clone(), ak.clone()))
+    for o, aq, ak in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16))
+        assert torch.equal(aq, outs[0][1]) and torch.equal(ak, outs[0][2])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("K,d_r", [(8, 16), (33, 64), (128, 64), (64, 128)])
+def test_responsibilities_match_oracle(dtype, K, d_r):
+    w = W["tiny_bidir_f32"].with_(K=K, d_r=d_r, N=257, H=2, dtype=dtype)
+    gen = inputs.generate(w, 1)
+    dev = upload(gen)
+    gamma, assign = api.responsibilities(dev["Q"], dev["mu"], dev["log_sigma2"], dev["log_pi"])
+    ref = oracle.responsibilities(gen["Q"].f32, gen["mu"], gen["log_sigma2"], gen["log_pi"])
+    g = gamma.cpu().numpy()
+    atol = 2e-5 if dtype == "f32" else 2e-3
+    assert np.abs(g - ref["gamma"]).max() <= atol
+    np.testing.assert_allclose(g.sum(-1), 1.0, atol=1e-5)
+    from tests.parity import check_assign
+    check_assign(assign.cpu().numpy(), ref["assign"], gen["Q"].f32, gen, dtype, "resp")
