@@ -93,6 +93,9 @@ def main():
     ap.add_argument("--workload", default="long_bidir_bf16")
     ap.add_argument("--causal", type=int, default=None, help="override the workload's variant")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a plain 1 GiB device-to-device copy `steps` times (reference "
+                         "kernel of known traffic for scaling HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -101,6 +104,23 @@ def main():
 
     import torch
     from gaussian_mixture_sequence_gma_amd import api, binding, inputs
+
+    if args.calibrate_copy:
+        nbytes = 1 << 30
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / args.steps
+        print(json.dumps({"calibrate_copy_bytes_read": nbytes, "bytes_written": nbytes,
+                          "ms_per_copy": ms, "GBps_read_plus_write": 2 * nbytes / ms / 1e6}))
+        return
 
     w = inputs.WORKLOADS[args.workload]
     if args.causal is not None:

@@ -8,7 +8,9 @@
 //    A = -w/2, B = mu*w, c = log pi - 1/2 sum_d (mu^2 w + log sigma^2),
 //    w = exp(-log sigma^2); the -(d_r/2) log 2pi term is dropped because the
 //    posterior is a softmax over k.  A, B and c carry a factor log2(e) so the
-//    exponentials are exp2.  Both contractions run on MFMA.
+//    exponentials are exp2.  Both contractions run on MFMA.  The fp32 path
+//    contracts A with (x^2 - 1) and adds c + sum_d A_kd afterwards: the same
+//    value in exact arithmetic, with a far smaller fp32 accumulator.
 //  - gamma_ik = exp(s_ik - m_i) / sum_l exp(s_il - m_i) with m_i = max_k s_ik.
 //  - Write (Eqs. 5-6): V~ = Gamma^K^T V_X, Z = Gamma^K^T 1, split over N with
 //    deterministic partial sums.
@@ -34,45 +36,52 @@ namespace gma {
 template <bool BF>
 __global__ void __launch_bounds__(256) gma_prologue_kernel(
     const float* __restrict__ mu, const float* __restrict__ ls2, const float* __restrict__ lpi,
-    int K, int Kp, int DR, int DRP, char* __restrict__ params, size_t head_bytes) {
-  const int h = blockIdx.x;
-  char* base = params + (size_t)h * head_bytes;
-  const float* muh = mu + (size_t)h * K * DR;
-  const float* lh = ls2 + (size_t)h * K * DR;
+    int H, int K, int Kp, int DR, int DRP, char* __restrict__ params, size_t head_bytes) {
   const int n = Kp * DRP;
-  for (int idx = threadIdx.x; idx < n; idx += blockDim.x) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  // one thread per (head, component, routing column): A and B
+  if (gid < (int64_t)H * n) {
+    const int h = (int)(gid / n), idx = (int)(gid - (int64_t)h * n);
     const int k = idx / DRP, d = idx - k * DRP;
+    char* base = params + (size_t)h * head_bytes;
     double a = 0.0, b = 0.0;
     if (k < K && d < DR) {
-      const double w = exp(-(double)lh[k * DR + d]);
+      const size_t off = ((size_t)h * K + k) * DR + d;
+      const double w = (double)expf(-ls2[off]);
       a = -0.5 * w * kLog2eD;
-      b = (double)muh[k * DR + d] * w * kLog2eD;
+      b = (double)mu[off] * w * kLog2eD;
     }
     if constexpr (BF) {
       bf16* Ahi = reinterpret_cast<bf16*>(base);
-      bf16* Alo = Ahi + n;
-      bf16* Bhi = Alo + n;
-      bf16* Blo = Bhi + n;
       const bf16 ah = to_bf16((float)a), bh = to_bf16((float)b);
       Ahi[idx] = ah;
-      Alo[idx] = to_bf16((float)(a - (double)from_bf16(ah)));
-      Bhi[idx] = bh;
-      Blo[idx] = to_bf16((float)(b - (double)from_bf16(bh)));
+      Ahi[n + idx] = to_bf16((float)(a - (double)from_bf16(ah)));
+      Ahi[2 * n + idx] = bh;
+      Ahi[3 * n + idx] = to_bf16((float)(b - (double)from_bf16(bh)));
     } else {
       float* A = reinterpret_cast<float*>(base);
       A[idx] = (float)a;
       A[n + idx] = (float)b;
     }
   }
-  float* c = reinterpret_cast<float*>(base + (size_t)8 * n);
-  for (int k = threadIdx.x; k < Kp; k += blockDim.x) {
+  // one thread per (head, component): c.  fp32 path: the kernels contract A
+  // with (x^2 - 1) instead of x^2 (keeping the fp32 accumulator near zero for
+  // unit-scale routing vectors) and add c' = c + sum_d A_kd once at the end;
+  // bf16 path: c seeds the accumulator.
+  if (gid < (int64_t)H * Kp) {
+    const int h = (int)(gid / Kp), k = (int)(gid - (int64_t)h * Kp);
+    float* c = reinterpret_cast<float*>(params + (size_t)h * head_bytes + (size_t)8 * n);
     if (k < K) {
-      double acc = 0.0;
+      double acc = 0.0, asum = 0.0;
+      const size_t off = ((size_t)h * K + k) * DR;
       for (int d = 0; d < DR; ++d) {
-        const double m = muh[k * DR + d], l = lh[k * DR + d];
-        acc += m * m * exp(-l) + l;
+        const double m = mu[off + d], l = ls2[off + d];
+        const double w = (double)expf(-ls2[off + d]);
+        acc += m * m * w + l;
+        asum += -0.5 * w;
       }
-      c[k] = (float)(kLog2eD * ((double)lpi[(size_t)h * K + k] - 0.5 * acc));
+      const double ck = (double)lpi[(size_t)h * K + k] - 0.5 * acc + (BF ? 0.0 : asum);
+      c[k] = (float)(kLog2eD * ck);
     } else {
       c[k] = -INFINITY;
     }
@@ -149,7 +158,7 @@ __device__ __forceinline__ void load_w(const char* pbase, int ctile0,
   }
 }
 
-// Stage routing features of one tile: bf16 -> (x^2 hi, x^2 lo, x); fp32 -> (x^2, x).
+// Stage routing features of one tile: bf16 -> (x^2 hi, x^2 lo, x); fp32 -> (x^2 - 1, x).
 template <class C>
 __device__ __forceinline__ void stage_features(const typename C::in_t* __restrict__ xg,
                                                int nvalid, typename C::op_t* F) {
@@ -179,7 +188,7 @@ __device__ __forceinline__ void stage_features(const typename C::in_t* __restric
       st16(f + kTile * C::FLD, lo);
       st16(f + 2 * kTile * C::FLD, x);
     } else {
-      st16(f, x * x);
+      st16(f, x * x - 1.f);
       st16(f + kTile * C::FLD, x);
     }
   }
@@ -206,7 +215,8 @@ __device__ __forceinline__ void stage_vt(const typename C::in_t* __restrict__ vg
 }
 
 // Score tiles.  TRANS = false: D[token][component] (features are the A operand);
-// TRANS = true: D[component][token].  Accumulators arrive initialised with c.
+// TRANS = true: D[component][token].  Accumulators arrive initialised with c
+// (bf16 path) or zero (fp32 path, whose c' is added by finish_scores).
 template <class C, bool TRANS>
 __device__ __forceinline__ void score_tiles(const typename C::op_t* F, int gt0,
                                             const typename C::chunk_t (&W)[C::CPW][C::NKS][C::NARR],
@@ -257,6 +267,17 @@ __device__ __forceinline__ void score_tiles(const typename C::op_t* F, int gt0,
       }
     }
   }
+}
+
+// fp32 path: scores = accumulated (x^2 - 1, x) contraction + c'.
+template <class C>
+__device__ __forceinline__ f32x4 score_seed(f32x4 cvals) {
+  if constexpr (C::kBF) return cvals;
+  else return f32x4{0.f, 0.f, 0.f, 0.f};
+}
+template <class C>
+__device__ __forceinline__ void finish_scores(f32x4& s, f32x4 cvals) {
+  if constexpr (!C::kBF) s += cvals;
 }
 
 // ============================================================================
@@ -317,8 +338,12 @@ __global__ void __launch_bounds__(kThreads) gma_write_kernel(BidirArgs a) {
 #pragma unroll
     for (int tt = 0; tt < C::TTW; ++tt)
 #pragma unroll
-      for (int ct = 0; ct < C::CPW; ++ct) S[tt][ct] = f32x4{cv[ct], cv[ct], cv[ct], cv[ct]};
+      for (int ct = 0; ct < C::CPW; ++ct) S[tt][ct] = score_seed<C>(f32x4{cv[ct], cv[ct], cv[ct], cv[ct]});
     score_tiles<C, false>(F, gt0, W, S);
+#pragma unroll
+    for (int tt = 0; tt < C::TTW; ++tt)
+#pragma unroll
+      for (int ct = 0; ct < C::CPW; ++ct) finish_scores<C>(S[tt][ct], f32x4{cv[ct], cv[ct], cv[ct], cv[ct]});
 
     // per-token statistics over this wave's components (lanes of a DPP row hold
     // the 16 components of a tile; rows 4g+i are tokens)
@@ -599,8 +624,12 @@ __global__ void __launch_bounds__(kThreads) gma_read_kernel(BidirArgs a) {
 #pragma unroll
     for (int tt = 0; tt < C::TTW; ++tt)
 #pragma unroll
-      for (int ct = 0; ct < C::CPW; ++ct) S[tt][ct] = cv4[ct];
+      for (int ct = 0; ct < C::CPW; ++ct) S[tt][ct] = score_seed<C>(cv4[ct]);
     score_tiles<C, true>(F, gt0, W, S);
+#pragma unroll
+    for (int tt = 0; tt < C::TTW; ++tt)
+#pragma unroll
+      for (int ct = 0; ct < C::CPW; ++ct) finish_scores<C>(S[tt][ct], cv4[ct]);
 
     // lane (c, g) holds token tile_token(gt, c) and components 16*ctile + 4g + i
     float m[C::TTW], l[C::TTW], dn[C::TTW];
@@ -842,12 +871,14 @@ static hipError_t run_resp(const Plan& p, const Tensors& t, hipStream_t s) {
 
 hipError_t launch_prologue(const Plan& p, const Tensors& t, hipStream_t s) {
   if (g_launch_hook) g_launch_hook("gma_prologue", s, 1);
+  const int64_t nthreads = p.H * (int64_t)p.Kp * p.DRP;
+  const dim3 grid((unsigned)((nthreads + 255) / 256));
   if (p.bf)
-    hipLaunchKernelGGL(gma_prologue_kernel<true>, dim3((unsigned)p.H), dim3(256), 0, s, t.mu, t.ls2,
-                       t.lpi, p.K, p.Kp, p.DR, p.DRP, t.ws + p.off_params, p.head_bytes);
+    hipLaunchKernelGGL(gma_prologue_kernel<true>, grid, dim3(256), 0, s, t.mu, t.ls2, t.lpi,
+                       (int)p.H, p.K, p.Kp, p.DR, p.DRP, t.ws + p.off_params, p.head_bytes);
   else
-    hipLaunchKernelGGL(gma_prologue_kernel<false>, dim3((unsigned)p.H), dim3(256), 0, s, t.mu,
-                       t.ls2, t.lpi, p.K, p.Kp, p.DR, p.DRP, t.ws + p.off_params, p.head_bytes);
+    hipLaunchKernelGGL(gma_prologue_kernel<false>, grid, dim3(256), 0, s, t.mu, t.ls2, t.lpi,
+                       (int)p.H, p.K, p.Kp, p.DR, p.DRP, t.ws + p.off_params, p.head_bytes);
   if (g_launch_hook) g_launch_hook("gma_prologue", s, 0);
   return hipGetLastError();
 }
