@@ -9,6 +9,7 @@
 
 #include "gma.h"
 #include "gma_internal.h"
+#include "gma_tiles.h"
 
 namespace gma {
 
@@ -70,10 +71,18 @@ int make_plan(const gma_dims* d, int causal, bool fp32_compute, Plan& p) {
     case 4: p.CPW = 2; p.NG = 2; break;
     default: p.CPW = 2; p.NG = 4; break;
   }
+  if (causal) {
+    // the scan kernel needs four component groups: K padded to at least 64
+    if (p.CT < 4) p.CT = 4;
+    p.CPW = p.CT / 4;
+    p.NG = 4;
+  }
   p.Kp = 16 * p.CT;
   const int cs = p.bf ? 32 : 16;
   p.DRP = p.DR < cs ? cs : p.DR;
   p.TG = 4 / p.NG;
+  if (causal && causal_lds_bytes(p.bf, p.DR, p.DV, p.Kp) > kMaxLds)
+    return fail(GMA_ERR_UNSUPPORTED, "causal fp32 path: this d_r, d_v, K combination exceeds LDS");
   p.tiles = (p.N + 63) / 64;
   // About two workgroups per compute unit (256 CUs) for each streaming kernel.
   int64_t want = (512 + p.BH - 1) / p.BH;

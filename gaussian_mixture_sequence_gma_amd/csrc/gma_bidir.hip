@@ -22,8 +22,7 @@
 // its A/B coefficients held in VGPRs for the whole kernel) and token group
 // w / NG (NG of the four 16-token MFMA tiles).  Per-token max / sum over
 // components is finished across the NG waves through LDS.
-#include "gma_device.h"
-#include "gma_internal.h"
+#include "gma_tiles.h"
 
 namespace gma {
 
@@ -85,446 +84,6 @@ __global__ void __launch_bounds__(256) gma_prologue_kernel(
     } else {
       c[k] = -INFINITY;
     }
-  }
-}
-
-// ============================================================================
-// Compile-time configuration of the tiled kernels.
-// ============================================================================
-template <bool BF, int CPW_, int NG_, int DR_, int DV_>
-struct Cfg {
-  using P = Prec<BF>;
-  using in_t = typename P::in_t;
-  using op_t = typename P::op_t;
-  using chunk_t = typename P::chunk_t;
-  static constexpr bool kBF = BF;
-  static constexpr int CPW = CPW_, NG = NG_, DR = DR_, DV = DV_;
-  static constexpr int E = P::E, CS = P::CS, NARR = P::NARR;
-  static constexpr int DRP = DR < CS ? CS : DR;
-  static constexpr int NKS = DRP / CS;             // feature chunk steps
-  static constexpr int TG = kWaves / NG;           // token groups
-  static constexpr int TTW = 4 / TG;               // 16-token tiles per wave
-  static constexpr int Kp = 16 * CPW * NG;
-  static constexpr int KpO = (Kp + CS - 1) / CS * CS;  // component extent of the read contraction
-  static constexpr int KSO = KpO / CS;
-  static constexpr int DVT = DV / 16;
-  static constexpr int NF = BF ? 3 : 2;            // staged feature arrays
-  static constexpr int PADE = 16 / sizeof(op_t);
-  static constexpr int FLD = DRP + PADE;           // feature row stride (elements)
-  static constexpr int VLD = kTile + 16 / sizeof(in_t);
-  static constexpr int GLD = KpO + PADE;
-  // read-out work split among the NG waves of a token group
-  static constexpr int DPW = DVT >= NG ? DVT / NG : 1;
-  static constexpr int TPW = DVT >= NG ? TTW : TTW * DVT / NG;
-};
-
-struct BidirArgs {
-  const void* x;          // K_X (write) or Q_X (read / resp), [BH][N][DR]
-  const void* v;          // V_X [BH][N][DV] (write)
-  void* out;              // O [BH][N][DV] (read)
-  const char* params;     // prologue output
-  size_t head_bytes;
-  float* partial;         // [BH][S*TG][Kp][DV]
-  float* partial_z;       // [BH][S*TG][Kp]
-  const float* vt;        // [BH][Kp][DV]
-  const float* z;         // [BH][Kp]
-  int32_t* assign;        // [BH][N] or null
-  float* gamma;           // resp: [BH][N][K] or null
-  int64_t N;
-  int H;
-  int K;
-  int S;
-  int tiles_per_split;
-  float eps;
-  int out_bf;
-};
-
-template <class C>
-__device__ __forceinline__ void load_w(const char* pbase, int ctile0,
-                                       typename C::chunk_t (&W)[C::CPW][C::NKS][C::NARR]) {
-  using op_t = typename C::op_t;
-  using chunk_t = typename C::chunk_t;
-  const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-  const int n = C::Kp * C::DRP;
-  const op_t* arr = reinterpret_cast<const op_t*>(pbase);
-#pragma unroll
-  for (int ct = 0; ct < C::CPW; ++ct) {
-    const int comp = (ctile0 + ct) * 16 + r;
-#pragma unroll
-    for (int s = 0; s < C::NKS; ++s)
-#pragma unroll
-      for (int a = 0; a < C::NARR; ++a)
-        W[ct][s][a] = ld16<chunk_t>(arr + (size_t)a * n + comp * C::DRP + s * C::CS + g * C::E);
-  }
-}
-
-// Stage routing features of one tile: bf16 -> (x^2 hi, x^2 lo, x); fp32 -> (x^2 - 1, x).
-template <class C>
-__device__ __forceinline__ void stage_features(const typename C::in_t* __restrict__ xg,
-                                               int nvalid, typename C::op_t* F) {
-  using chunk_t = typename C::chunk_t;
-  constexpr int CPR = C::DR / C::E;     // 16-byte chunks per token row
-  for (int i = threadIdx.x; i < kTile * CPR; i += kThreads) {
-    const int t = i / CPR, part = i - t * CPR;
-    chunk_t x;
-    if (t < nvalid) {
-      x = ld16<chunk_t>(xg + (size_t)t * C::DR + part * C::E);
-    } else {
-#pragma unroll
-      for (int e = 0; e < C::E; ++e) x[e] = 0;
-    }
-    typename C::op_t* f = F + t * C::FLD + part * C::E;
-    if constexpr (C::kBF) {
-      bf16x8 hi, lo;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float xf = from_bf16(x[e]);
-        bf16 h, l;
-        split_bf16(xf * xf, h, l);
-        hi[e] = h;
-        lo[e] = l;
-      }
-      st16(f, hi);
-      st16(f + kTile * C::FLD, lo);
-      st16(f + 2 * kTile * C::FLD, x);
-    } else {
-      st16(f, x * x - 1.f);
-      st16(f + kTile * C::FLD, x);
-    }
-  }
-}
-
-// Stage V transposed: Vt[d][token].
-template <class C>
-__device__ __forceinline__ void stage_vt(const typename C::in_t* __restrict__ vg, int nvalid,
-                                         typename C::in_t* Vt) {
-  using chunk_t = typename C::chunk_t;
-  constexpr int CPR = C::DV / C::E;
-  for (int i = threadIdx.x; i < kTile * CPR; i += kThreads) {
-    const int t = i / CPR, part = i - t * CPR;
-    chunk_t v;
-    if (t < nvalid) {
-      v = ld16<chunk_t>(vg + (size_t)t * C::DV + part * C::E);
-    } else {
-#pragma unroll
-      for (int e = 0; e < C::E; ++e) v[e] = 0;
-    }
-#pragma unroll
-    for (int e = 0; e < C::E; ++e) Vt[(part * C::E + e) * C::VLD + t] = v[e];
-  }
-}
-
-// Score tiles.  TRANS = false: D[token][component] (features are the A operand);
-// TRANS = true: D[component][token].  Accumulators arrive initialised with c
-// (bf16 path) or zero (fp32 path, whose c' is added by finish_scores).
-template <class C, bool TRANS>
-__device__ __forceinline__ void score_tiles(const typename C::op_t* F, int gt0,
-                                            const typename C::chunk_t (&W)[C::CPW][C::NKS][C::NARR],
-                                            f32x4 (&S)[C::TTW][C::CPW]) {
-  using chunk_t = typename C::chunk_t;
-  const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int s = 0; s < C::NKS; ++s) {
-#pragma unroll
-    for (int tt = 0; tt < C::TTW; ++tt) {
-      const int tok = tile_token(gt0 + tt, r);
-      const typename C::op_t* f = F + tok * C::FLD + s * C::CS + g * C::E;
-      const chunk_t f0 = ld16<chunk_t>(f);
-      const chunk_t f1 = ld16<chunk_t>(f + kTile * C::FLD);
-      if constexpr (C::kBF) {
-        const chunk_t f2 = ld16<chunk_t>(f + 2 * kTile * C::FLD);
-#pragma unroll
-        for (int ct = 0; ct < C::CPW; ++ct) {
-          f32x4 acc = S[tt][ct];
-          if constexpr (!TRANS) {
-            acc = mma(f0, W[ct][s][0], acc);   // x^2_hi * A_hi
-            acc = mma(f1, W[ct][s][0], acc);   // x^2_lo * A_hi
-            acc = mma(f0, W[ct][s][1], acc);   // x^2_hi * A_lo
-            acc = mma(f2, W[ct][s][2], acc);   // x * B_hi
-            acc = mma(f2, W[ct][s][3], acc);   // x * B_lo
-          } else {
-            acc = mma(W[ct][s][0], f0, acc);
-            acc = mma(W[ct][s][0], f1, acc);
-            acc = mma(W[ct][s][1], f0, acc);
-            acc = mma(W[ct][s][2], f2, acc);
-            acc = mma(W[ct][s][3], f2, acc);
-          }
-          S[tt][ct] = acc;
-        }
-      } else {
-#pragma unroll
-        for (int ct = 0; ct < C::CPW; ++ct) {
-          f32x4 acc = S[tt][ct];
-          if constexpr (!TRANS) {
-            acc = mma(f0, W[ct][s][0], acc);   // x^2 * A
-            acc = mma(f1, W[ct][s][1], acc);   // x * B
-          } else {
-            acc = mma(W[ct][s][0], f0, acc);
-            acc = mma(W[ct][s][1], f1, acc);
-          }
-          S[tt][ct] = acc;
-        }
-      }
-    }
-  }
-}
-
-// fp32 path: scores = accumulated (x^2 - 1, x) contraction + c'.
-template <class C>
-__device__ __forceinline__ f32x4 score_seed(f32x4 cvals) {
-  if constexpr (C::kBF) return cvals;
-  else return f32x4{0.f, 0.f, 0.f, 0.f};
-}
-template <class C>
-__device__ __forceinline__ void finish_scores(f32x4& s, f32x4 cvals) {
-  if constexpr (!C::kBF) s += cvals;
-}
-
-// ============================================================================
-// Latent write: grid (S, B*H).  Each workgroup covers tiles_per_split tiles of
-// one sequence and writes TG partial (V~, Z) blocks.
-// ============================================================================
-template <class C>
-__global__ void __launch_bounds__(kThreads) gma_write_kernel(BidirArgs a) {
-  using in_t = typename C::in_t;
-  using op_t = typename C::op_t;
-  using chunk_t = typename C::chunk_t;
-  __shared__ __attribute__((aligned(16))) op_t F[C::NF * kTile * C::FLD];
-  __shared__ __attribute__((aligned(16))) in_t Vt[C::DV * C::VLD];
-  __shared__ __attribute__((aligned(16))) f32x4 stats[C::NG * kTile];
-  __shared__ __attribute__((aligned(16))) float fac[C::NG * kTile];
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c = lane & 15, g = lane >> 4;
-  const int cgi = wave % C::NG, tg = wave / C::NG;
-  const int gt0 = tg * C::TTW;
-  const int64_t bh = blockIdx.y;
-  const int h = (int)(bh % a.H);
-  const int split = blockIdx.x;
-  const int64_t t_begin = (int64_t)split * a.tiles_per_split * kTile;
-  const int64_t t_end = min(a.N, t_begin + (int64_t)a.tiles_per_split * kTile);
-  const bool want_assign = a.assign != nullptr;
-
-  for (int i = threadIdx.x; i < C::NF * kTile * C::FLD; i += kThreads) F[i] = (op_t)0;
-
-  const char* pbase = a.params + (size_t)h * a.head_bytes;
-  chunk_t W[C::CPW][C::NKS][C::NARR];
-  load_w<C>(pbase, cgi * C::CPW, W);
-  const float* cvec = reinterpret_cast<const float*>(pbase + (size_t)8 * C::Kp * C::DRP);
-  float cv[C::CPW];
-#pragma unroll
-  for (int ct = 0; ct < C::CPW; ++ct) cv[ct] = cvec[(cgi * C::CPW + ct) * 16 + c];
-
-  f32x4 vacc[C::CPW][C::DVT];
-  float zacc[C::CPW];
-#pragma unroll
-  for (int ct = 0; ct < C::CPW; ++ct) {
-    zacc[ct] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < C::DVT; ++dt) vacc[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  const in_t* xs = reinterpret_cast<const in_t*>(a.x) + (size_t)bh * a.N * C::DR;
-  const in_t* vs = reinterpret_cast<const in_t*>(a.v) + (size_t)bh * a.N * C::DV;
-
-  for (int64_t tile0 = t_begin; tile0 < t_end; tile0 += kTile) {
-    const int nvalid = (int)min((int64_t)kTile, t_end - tile0);
-    __syncthreads();
-    stage_features<C>(xs + (size_t)tile0 * C::DR, nvalid, F);
-    stage_vt<C>(vs + (size_t)tile0 * C::DV, nvalid, Vt);
-    __syncthreads();
-
-    f32x4 S[C::TTW][C::CPW];
-#pragma unroll
-    for (int tt = 0; tt < C::TTW; ++tt)
-#pragma unroll
-      for (int ct = 0; ct < C::CPW; ++ct) S[tt][ct] = score_seed<C>(f32x4{cv[ct], cv[ct], cv[ct], cv[ct]});
-    score_tiles<C, false>(F, gt0, W, S);
-#pragma unroll
-    for (int tt = 0; tt < C::TTW; ++tt)
-#pragma unroll
-      for (int ct = 0; ct < C::CPW; ++ct) finish_scores<C>(S[tt][ct], f32x4{cv[ct], cv[ct], cv[ct], cv[ct]});
-
-    // per-token statistics over this wave's components (lanes of a DPP row hold
-    // the 16 components of a tile; rows 4g+i are tokens)
-    float m[C::TTW][4], l[C::TTW][4];
-    int am[C::TTW][4];
-#pragma unroll
-    for (int tt = 0; tt < C::TTW; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = S[tt][0][i];
-#pragma unroll
-        for (int ct = 1; ct < C::CPW; ++ct) v = fmaxf(v, S[tt][ct][i]);
-        m[tt][i] = row16_max(v);
-        am[tt][i] = 0;
-      }
-    if (want_assign) {
-#pragma unroll
-      for (int tt = 0; tt < C::TTW; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = S[tt][0][i];
-          int idx = (cgi * C::CPW) * 16 + c;
-#pragma unroll
-          for (int ct = 1; ct < C::CPW; ++ct)
-            argmax_merge(v, idx, S[tt][ct][i], (cgi * C::CPW + ct) * 16 + c);
-          row16_argmax(v, idx);
-          am[tt][i] = idx;
-        }
-    }
-#pragma unroll
-    for (int tt = 0; tt < C::TTW; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float mu_ = m[tt][i] == -INFINITY ? 0.f : m[tt][i];
-        float sum = 0.f;
-#pragma unroll
-        for (int ct = 0; ct < C::CPW; ++ct) {
-          const float e = exp2_fast(S[tt][ct][i] - mu_);
-          S[tt][ct][i] = e;
-          sum += e;
-        }
-        l[tt][i] = row16_sum(sum);
-      }
-
-    float f[C::TTW][4];
-    if constexpr (C::NG > 1) {
-      {
-        const int tts = c >> 2, is = c & 3;
-        float sm = 0.f, sl = 0.f;
-        int sa = 0;
-#pragma unroll
-        for (int tt = 0; tt < C::TTW; ++tt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (tt == tts && i == is) { sm = m[tt][i]; sl = l[tt][i]; sa = am[tt][i]; }
-        if (tts < C::TTW)
-          stats[cgi * kTile + tile_token(gt0 + tts, 4 * g + is)] =
-              f32x4{sm, sl, __int_as_float(sa), 0.f};
-      }
-      __syncthreads();
-      if (threadIdx.x < kTile) {
-        const int t = threadIdx.x;
-        f32x4 st[C::NG];
-        float M = -INFINITY;
-#pragma unroll
-        for (int q = 0; q < C::NG; ++q) {
-          st[q] = stats[q * kTile + t];
-          M = fmaxf(M, st[q][0]);
-        }
-        float L = 0.f, fq[C::NG];
-        int arg = 0;
-        bool found = false;
-#pragma unroll
-        for (int q = 0; q < C::NG; ++q) {
-          fq[q] = st[q][0] == -INFINITY ? 0.f : exp2_fast(st[q][0] - M);
-          L += fq[q] * st[q][1];
-          if (!found && st[q][0] == M) { arg = __float_as_int(st[q][2]); found = true; }
-        }
-        const float invL = 1.f / L;
-#pragma unroll
-        for (int q = 0; q < C::NG; ++q) fac[q * kTile + t] = fq[q] * invL;
-        if (want_assign && t < nvalid) a.assign[(size_t)bh * a.N + tile0 + t] = arg;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int tt = 0; tt < C::TTW; ++tt) {
-        const f32x4 fv = ld16<f32x4>(&fac[cgi * kTile + tile_token(gt0 + tt, 4 * g)]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) f[tt][i] = fv[i];
-      }
-    } else {
-#pragma unroll
-      for (int tt = 0; tt < C::TTW; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) f[tt][i] = 1.f / l[tt][i];
-      if (want_assign && c == 0) {
-#pragma unroll
-        for (int tt = 0; tt < C::TTW; ++tt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int tok = tile_token(gt0 + tt, 4 * g + i);
-            if (tok < nvalid) a.assign[(size_t)bh * a.N + tile0 + tok] = am[tt][i];
-          }
-      }
-    }
-
-    // gamma = e * factor, masked to valid tokens; accumulate Z in fp32
-#pragma unroll
-    for (int tt = 0; tt < C::TTW; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool valid = tile_token(gt0 + tt, 4 * g + i) < nvalid;
-        const float fi = valid ? f[tt][i] : 0.f;
-#pragma unroll
-        for (int ct = 0; ct < C::CPW; ++ct) {
-          const float gm = S[tt][ct][i] * fi;
-          S[tt][ct][i] = gm;
-          zacc[ct] += gm;
-        }
-      }
-
-    // V~ += Gamma^T V over this wave's tokens
-    if constexpr (C::kBF) {
-      constexpr int NP = C::TTW >= 2 ? C::TTW / 2 : 1;
-#pragma unroll
-      for (int pp = 0; pp < NP; ++pp) {
-        const int gta = gt0 + 2 * pp;               // first tile of the pair (or the only one)
-        const int P = gta >> 1;
-        bf16x8 A[C::CPW];
-#pragma unroll
-        for (int ct = 0; ct < C::CPW; ++ct) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) A[ct][e] = (bf16)0.f;
-          if constexpr (C::TTW >= 2) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              A[ct][i] = to_bf16(S[2 * pp][ct][i]);
-              A[ct][4 + i] = to_bf16(S[2 * pp + 1][ct][i]);
-            }
-          } else {
-            const int hsel = gt0 & 1;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) A[ct][4 * hsel + i] = to_bf16(S[0][ct][i]);
-          }
-        }
-#pragma unroll
-        for (int dt = 0; dt < C::DVT; ++dt) {
-          const bf16x8 Bv = ld16<bf16x8>(&Vt[(dt * 16 + c) * C::VLD + 32 * P + 8 * g]);
-#pragma unroll
-          for (int ct = 0; ct < C::CPW; ++ct) vacc[ct][dt] = mma(A[ct], Bv, vacc[ct][dt]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int tt = 0; tt < C::TTW; ++tt) {
-        const int gt = gt0 + tt;
-        const int base = 32 * (gt >> 1) + 8 * g + 4 * (gt & 1);
-#pragma unroll
-        for (int dt = 0; dt < C::DVT; ++dt) {
-          const f32x4 Bv = ld16<f32x4>(&Vt[(dt * 16 + c) * C::VLD + base]);
-#pragma unroll
-          for (int ct = 0; ct < C::CPW; ++ct) vacc[ct][dt] = mma(S[tt][ct], Bv, vacc[ct][dt]);
-        }
-      }
-    }
-  }
-
-  // partial (V~, Z) for this (split, token group)
-  const int PS = a.S * C::TG;
-  const size_t pslot = (size_t)bh * PS + (size_t)split * C::TG + tg;
-  float* pv = a.partial + pslot * C::Kp * C::DV;
-  float* pz = a.partial_z + pslot * C::Kp;
-#pragma unroll
-  for (int ct = 0; ct < C::CPW; ++ct) {
-    const int comp0 = (cgi * C::CPW + ct) * 16;
-#pragma unroll
-    for (int dt = 0; dt < C::DVT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pv[(comp0 + 4 * g + i) * C::DV + dt * 16 + c] = vacc[ct][dt][i];
-    const float zt = groups_sum(zacc[ct]);
-    if (g == 0) pz[comp0 + c] = zt;
   }
 }
 

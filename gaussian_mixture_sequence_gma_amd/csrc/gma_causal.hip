@@ -1,7 +1,543 @@
-// Causal GMA forward (chunked prefix scan) -- not yet implemented.
-#include "gma_device.h"
-#include "gma_internal.h"
+// Causal GMA forward on gfx950: a chunked prefix scan.
+//
+// Paper: "Gaussian Mixture Attention: Linear-Time Sequence Mixing via
+// Probabilistic Latent Routing", Section "Causal GMA" (Eq. 8b and its
+// footnote): the memories become inclusive prefix sums
+//   V~^(i)_k = sum_{j<=i} gamma^K_jk v_j,  Z^(i)_k = sum_{j<=i} gamma^K_jk,
+//   O_i = gamma^Q_i V~^(i) / (gamma^Q_i Z^(i) + eps),
+// which the paper computes as cumulative sums along the sequence.
+//
+// Three launches per call:
+//  1. span totals: the latent-write kernel run with one split per span writes
+//     sum_{j in span} gamma^K_j (x) v_j and sum gamma^K_j for every span;
+//  2. an exclusive scan over spans gives each span its carried-in state;
+//  3. the scan kernel walks its span in 64-token chunks.  For chunk c with
+//     carried state (S, z) it computes
+//        num_i = gamma^Q_i S + sum_{j in c, j<=i} (gamma^Q_i . gamma^K_j) v_j
+//        den_i = gamma^Q_i z + sum_{j in c, j<=i} (gamma^Q_i . gamma^K_j) + eps
+//     on MFMA (the masked intra-chunk affinity never leaves the CU), then
+//     S += Gamma^K_c^T V_c, z += Gamma^K_c^T 1 in registers.
+// The scan kernel uses four component groups (K padded to >= 64) so that all
+// four waves see every token of a chunk and the running state is split over
+// the waves by component.
+#include "gma_tiles.h"
 
 namespace gma {
-hipError_t launch_causal(const Plan&, const Tensors&, hipStream_t) { return hipErrorNotSupported; }
+
+struct CausalArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  const char* params;
+  size_t head_bytes;
+  const float* carry;     // [BH][nspan][Kp][DV] exclusive prefix state
+  const float* carry_z;   // [BH][nspan][Kp]
+  int32_t* assign_q;
+  int32_t* assign_k;
+  int64_t N;
+  int H;
+  int nspan;
+  int span_tiles;
+  float eps;
+  int out_bf;
+};
+
+// Exclusive prefix over spans, fixed order: carry[s] = sum_{s' < s} state[s'].
+__global__ void __launch_bounds__(256) gma_span_scan_kernel(const float* __restrict__ state,
+                                                            const float* __restrict__ state_z,
+                                                            int nspan, int Kp, int DV,
+                                                            float* __restrict__ carry,
+                                                            float* __restrict__ carry_z) {
+  const int64_t bh = blockIdx.y;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const int nv = Kp * DV;
+  if (idx < nv) {
+    const size_t base = (size_t)bh * nspan * nv + idx;
+    float acc = 0.f;
+    for (int s = 0; s < nspan; ++s) {
+      carry[base + (size_t)s * nv] = acc;
+      acc += state[base + (size_t)s * nv];
+    }
+  } else if (idx < nv + Kp) {
+    const size_t base = (size_t)bh * nspan * Kp + (idx - nv);
+    float acc = 0.f;
+    for (int s = 0; s < nspan; ++s) {
+      carry_z[base + (size_t)s * Kp] = acc;
+      acc += state_z[base + (size_t)s * Kp];
+    }
+  }
+}
+
+template <class C>
+__global__ void __launch_bounds__(kThreads) gma_causal_kernel(CausalArgs a) {
+  static_assert(C::NG == 4 && C::TG == 1 && C::TTW == 4, "causal scan needs four component groups");
+  using in_t = typename C::in_t;
+  using op_t = typename C::op_t;
+  using chunk_t = typename C::chunk_t;
+  constexpr int FE = C::NF * kTile * C::FLD;
+  // features (dead once the scores exist) share storage with Gamma^Q, Gamma^K, S
+  __shared__ __attribute__((aligned(16))) op_t U[causal_union_elems(C::NF, C::FLD, C::DV, C::GLD)];
+  __shared__ __attribute__((aligned(16))) in_t Vt[C::DV * C::VLD];
+  op_t* const QF = U;
+  op_t* const KF = U + FE;
+  op_t* const GQ = U;
+  op_t* const GK = U + kTile * C::GLD;
+  op_t* const ST = U + 2 * kTile * C::GLD;
+  __shared__ __attribute__((aligned(16))) float zs[C::Kp];
+  __shared__ __attribute__((aligned(16))) f32x4 statsK[4 * kTile];
+  __shared__ __attribute__((aligned(16))) f32x4 statsQ[4 * kTile];
+  __shared__ __attribute__((aligned(16))) float facK[4 * kTile];
+  __shared__ __attribute__((aligned(16))) float facQ[4 * kTile];
+  __shared__ __attribute__((aligned(16))) float qden[kTile];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int64_t bh = blockIdx.y;
+  const int h = (int)(bh % a.H);
+  const int span = blockIdx.x;
+  const int64_t t_begin = (int64_t)span * a.span_tiles * kTile;
+  const int64_t t_end = a.N < t_begin + (int64_t)a.span_tiles * kTile
+                            ? a.N : t_begin + (int64_t)a.span_tiles * kTile;
+
+
+  const char* pbase = a.params + (size_t)h * a.head_bytes;
+  chunk_t W[C::CPW][C::NKS][C::NARR];
+  load_w<C>(pbase, w * C::CPW, W);
+  const float* cvec = reinterpret_cast<const float*>(pbase + (size_t)8 * C::Kp * C::DRP);
+  float cv[C::CPW];
+  f32x4 cv4[C::CPW];
+#pragma unroll
+  for (int ct = 0; ct < C::CPW; ++ct) {
+    cv[ct] = cvec[(w * C::CPW + ct) * 16 + c];
+    cv4[ct] = ld16<f32x4>(cvec + (w * C::CPW + ct) * 16 + 4 * g);
+  }
+
+  // running state: S (D layout, lane column d, rows components) and z (per component c)
+  const size_t sslot = (size_t)bh * a.nspan + span;
+  f32x4 vacc[C::CPW][C::DVT];
+  float zst[C::CPW];
+#pragma unroll
+  for (int ct = 0; ct < C::CPW; ++ct) {
+    const int comp0 = (w * C::CPW + ct) * 16;
+#pragma unroll
+    for (int dt = 0; dt < C::DVT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        vacc[ct][dt][i] = a.carry[(sslot * C::Kp + comp0 + 4 * g + i) * C::DV + dt * 16 + c];
+    zst[ct] = a.carry_z[sslot * C::Kp + comp0 + c];
+    if (g == 0) zs[comp0 + c] = zst[ct];
+  }
+
+  const in_t* qs = reinterpret_cast<const in_t*>(a.q) + (size_t)bh * a.N * C::DR;
+  const in_t* ks = reinterpret_cast<const in_t*>(a.k) + (size_t)bh * a.N * C::DR;
+  const in_t* vs = reinterpret_cast<const in_t*>(a.v) + (size_t)bh * a.N * C::DV;
+  const bool want_aq = a.assign_q != nullptr, want_ak = a.assign_k != nullptr;
+
+  for (int64_t tile0 = t_begin; tile0 < t_end; tile0 += kTile) {
+    const int nvalid = (int)((t_end - tile0) < kTile ? (t_end - tile0) : kTile);
+    __syncthreads();
+    stage_features<C>(qs + (size_t)tile0 * C::DR, nvalid, QF);
+    stage_features<C>(ks + (size_t)tile0 * C::DR, nvalid, KF);
+    stage_vt<C>(vs + (size_t)tile0 * C::DV, nvalid, Vt);
+    __syncthreads();
+
+    // ---- key responsibilities, D[token][component] --------------------------
+    f32x4 SK[4][C::CPW];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int ct = 0; ct < C::CPW; ++ct)
+        SK[tt][ct] = score_seed<C>(f32x4{cv[ct], cv[ct], cv[ct], cv[ct]});
+    score_tiles<C, false>(KF, 0, W, SK);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int ct = 0; ct < C::CPW; ++ct)
+        finish_scores<C>(SK[tt][ct], f32x4{cv[ct], cv[ct], cv[ct], cv[ct]});
+    float mk[4][4], lk[4][4];
+    int ak[4][4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = SK[tt][0][i];
+        int idx = (w * C::CPW) * 16 + c;
+#pragma unroll
+        for (int ct = 1; ct < C::CPW; ++ct) argmax_merge(v, idx, SK[tt][ct][i], (w * C::CPW + ct) * 16 + c);
+        if (want_ak) {
+          float vv = v;
+          row16_argmax(vv, idx);
+        }
+        mk[tt][i] = row16_max(v);
+        ak[tt][i] = idx;
+        const float mu_ = mk[tt][i] == -INFINITY ? 0.f : mk[tt][i];
+        float sum = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < C::CPW; ++ct) {
+          const float e = exp2_fast(SK[tt][ct][i] - mu_);
+          SK[tt][ct][i] = e;
+          sum += e;
+        }
+        lk[tt][i] = row16_sum(sum);
+      }
+    {
+      const int tts = c >> 2, is = c & 3;
+      float sm = 0.f, sl = 0.f;
+      int sa = 0;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (tt == tts && i == is) { sm = mk[tt][i]; sl = lk[tt][i]; sa = ak[tt][i]; }
+      statsK[w * kTile + tile_token(tts, 4 * g + is)] = f32x4{sm, sl, __int_as_float(sa), 0.f};
+    }
+
+    // ---- query responsibilities, D[component][token] ------------------------
+    f32x4 SQ[4][C::CPW];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int ct = 0; ct < C::CPW; ++ct) SQ[tt][ct] = score_seed<C>(cv4[ct]);
+    score_tiles<C, true>(QF, 0, W, SQ);
+    f32x4 z4[C::CPW];
+#pragma unroll
+    for (int ct = 0; ct < C::CPW; ++ct) z4[ct] = ld16<f32x4>(&zs[(w * C::CPW + ct) * 16 + 4 * g]);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+      for (int ct = 0; ct < C::CPW; ++ct) finish_scores<C>(SQ[tt][ct], cv4[ct]);
+      float v = SQ[tt][0][0];
+      int bi = (w * C::CPW) * 16 + 4 * g;
+#pragma unroll
+      for (int ct = 0; ct < C::CPW; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) argmax_merge(v, bi, SQ[tt][ct][i], (w * C::CPW + ct) * 16 + 4 * g + i);
+      if (want_aq) {
+        float vv = v;
+        groups_argmax(vv, bi);
+      }
+      const float m = groups_max(v);
+      const float mu_ = m == -INFINITY ? 0.f : m;
+      float sum = 0.f, den = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < C::CPW; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = exp2_fast(SQ[tt][ct][i] - mu_);
+          SQ[tt][ct][i] = e;
+          sum += e;
+          den += e * z4[ct][i];
+        }
+      sum = groups_sum(sum);
+      den = groups_sum(den);
+      if (g == 0) statsQ[w * kTile + tile_token(tt, c)] = f32x4{m, sum, den, __int_as_float(bi)};
+    }
+    __syncthreads();
+
+    // ---- combine the four component groups ---------------------------------
+    if (threadIdx.x < 2 * kTile) {
+      const bool isq = threadIdx.x >= kTile;
+      const int t = threadIdx.x & (kTile - 1);
+      const f32x4* st = isq ? statsQ : statsK;
+      f32x4 s4[4];
+      float M = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        s4[q] = st[q * kTile + t];
+        M = fmaxf(M, s4[q][0]);
+      }
+      float L = 0.f, D = 0.f, fq[4];
+      int arg = 0;
+      bool found = false;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        fq[q] = s4[q][0] == -INFINITY ? 0.f : exp2_fast(s4[q][0] - M);
+        L += fq[q] * s4[q][1];
+        D += fq[q] * s4[q][2];
+        const int aq_ = __float_as_int(isq ? s4[q][3] : s4[q][2]);
+        if (!found && s4[q][0] == M) { arg = aq_; found = true; }
+      }
+      const float invL = 1.f / L;
+      float* fac = isq ? facQ : facK;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) fac[q * kTile + t] = fq[q] * invL;
+      if (isq) qden[t] = D * invL;
+      if (t < nvalid) {
+        if (isq && want_aq) a.assign_q[(size_t)bh * a.N + tile0 + t] = arg;
+        if (!isq && want_ak) a.assign_k[(size_t)bh * a.N + tile0 + t] = arg;
+      }
+    }
+    __syncthreads();
+
+    // ---- normalised responsibilities to LDS; carried state to LDS -----------
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const f32x4 fk = ld16<f32x4>(&facK[w * kTile + tile_token(tt, 4 * g)]);
+      const float fqv = facQ[w * kTile + tile_token(tt, c)];
+      const int qtok = tile_token(tt, c);
+#pragma unroll
+      for (int ct = 0; ct < C::CPW; ++ct) {
+        const int comp0 = (w * C::CPW + ct) * 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ktok = tile_token(tt, 4 * g + i);
+          const float gk = ktok < nvalid ? SK[tt][ct][i] * fk[i] : 0.f;
+          SK[tt][ct][i] = gk;
+          GK[ktok * C::GLD + comp0 + c] = (op_t)gk;
+          SQ[tt][ct][i] *= fqv;
+        }
+        op_t* dst = &GQ[qtok * C::GLD + comp0 + 4 * g];
+        if constexpr (C::kBF) {
+          bf16x4 v4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v4[i] = to_bf16(SQ[tt][ct][i]);
+          *reinterpret_cast<bf16x4*>(dst) = v4;
+        } else {
+          st16(dst, SQ[tt][ct]);
+        }
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < C::CPW; ++ct) {
+      const int comp0 = (w * C::CPW + ct) * 16;
+#pragma unroll
+      for (int dt = 0; dt < C::DVT; ++dt) {
+        op_t* dst = &ST[(dt * 16 + c) * C::GLD + comp0 + 4 * g];
+        if constexpr (C::kBF) {
+          bf16x4 v4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v4[i] = to_bf16(vacc[ct][dt][i]);
+          *reinterpret_cast<bf16x4*>(dst) = v4;
+        } else {
+          st16(dst, vacc[ct][dt]);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- outputs: wave w owns query tile w ----------------------------------
+    {
+      const int gt = w;
+      const int Pi = gt >> 1;
+      const int itok_c = tile_token(gt, c);
+      f32x4 acc[C::DVT];
+#pragma unroll
+      for (int dt = 0; dt < C::DVT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // carried memory: Gamma^Q_c S
+#pragma unroll
+      for (int s = 0; s < C::KSO; ++s) {
+        const chunk_t A = ld16<chunk_t>(&GQ[itok_c * C::GLD + s * C::CS + g * C::E]);
+#pragma unroll
+        for (int dt = 0; dt < C::DVT; ++dt) {
+          const chunk_t Bs = ld16<chunk_t>(&ST[(dt * 16 + c) * C::GLD + s * C::CS + g * C::E]);
+          acc[dt] = mma(A, Bs, acc[dt]);
+        }
+      }
+      // intra-chunk: P^T = Gamma^K Gamma^Q^T (rows key tokens, columns query tokens), masked j <= i
+      float rowsum = 0.f;
+      for (int p = 0; p <= Pi; ++p) {
+        f32x4 PT[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int jt = 2 * p + hh;
+          f32x4 pt = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < C::KSO; ++s) {
+            const chunk_t Ak = ld16<chunk_t>(&GK[tile_token(jt, c) * C::GLD + s * C::CS + g * C::E]);
+            const chunk_t Bq = ld16<chunk_t>(&GQ[itok_c * C::GLD + s * C::CS + g * C::E]);
+            pt = mma(Ak, Bq, pt);
+          }
+          if (p == Pi) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (tile_token(jt, 4 * g + i) > itok_c) pt[i] = 0.f;
+          }
+          rowsum += pt[0] + pt[1] + pt[2] + pt[3];
+          PT[hh] = pt;
+        }
+        if constexpr (C::kBF) {
+          bf16x8 Ap;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            Ap[i] = to_bf16(PT[0][i]);
+            Ap[4 + i] = to_bf16(PT[1][i]);
+          }
+#pragma unroll
+          for (int dt = 0; dt < C::DVT; ++dt) {
+            const bf16x8 Bv = ld16<bf16x8>(&Vt[(dt * 16 + c) * C::VLD + 32 * p + 8 * g]);
+            acc[dt] = mma(Ap, Bv, acc[dt]);
+          }
+        } else {
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int dt = 0; dt < C::DVT; ++dt) {
+              const f32x4 Bv = ld16<f32x4>(&Vt[(dt * 16 + c) * C::VLD + 32 * p + 8 * g + 4 * hh]);
+              acc[dt] = mma(PT[hh], Bv, acc[dt]);
+            }
+        }
+      }
+      rowsum = groups_sum(rowsum);   // per query token tile_token(gt, c)
+      const f32x4 qd = ld16<f32x4>(&qden[tile_token(gt, 4 * g)]);
+      float rinv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // row 4g+i of the accumulator is query token tile_token(gt, 4g+i), whose
+        // intra-chunk row sum sits in lane column 4g+i
+        const float rs = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * g + i) << 2, __float_as_int(rowsum)));
+        rinv[i] = 1.f / (qd[i] + rs + a.eps);
+      }
+#pragma unroll
+      for (int dt = 0; dt < C::DVT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = tile_token(gt, 4 * g + i);
+          if (tok < nvalid) {
+            const float o = acc[dt][i] * rinv[i];
+            const size_t off = ((size_t)bh * a.N + tile0 + tok) * C::DV + dt * 16 + c;
+            if (a.out_bf) reinterpret_cast<bf16*>(a.out)[off] = to_bf16(o);
+            else reinterpret_cast<float*>(a.out)[off] = o;
+          }
+        }
+    }
+
+    // ---- state update: S += Gamma^K_c^T V_c, z += Gamma^K_c^T 1 ----------------
+#pragma unroll
+    for (int ct = 0; ct < C::CPW; ++ct) {
+      float zp = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) zp += SK[tt][ct][i];
+      zst[ct] += groups_sum(zp);
+    }
+    if constexpr (C::kBF) {
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        bf16x8 A[C::CPW];
+#pragma unroll
+        for (int ct = 0; ct < C::CPW; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            A[ct][i] = to_bf16(SK[2 * pp][ct][i]);
+            A[ct][4 + i] = to_bf16(SK[2 * pp + 1][ct][i]);
+          }
+#pragma unroll
+        for (int dt = 0; dt < C::DVT; ++dt) {
+          const bf16x8 Bv = ld16<bf16x8>(&Vt[(dt * 16 + c) * C::VLD + 32 * pp + 8 * g]);
+#pragma unroll
+          for (int ct = 0; ct < C::CPW; ++ct) vacc[ct][dt] = mma(A[ct], Bv, vacc[ct][dt]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int base = 32 * (tt >> 1) + 8 * g + 4 * (tt & 1);
+#pragma unroll
+        for (int dt = 0; dt < C::DVT; ++dt) {
+          const f32x4 Bv = ld16<f32x4>(&Vt[(dt * 16 + c) * C::VLD + base]);
+#pragma unroll
+          for (int ct = 0; ct < C::CPW; ++ct) vacc[ct][dt] = mma(SK[tt][ct], Bv, vacc[ct][dt]);
+        }
+      }
+    }
+    // zs is read again only after the next chunk's first barrier
+#pragma unroll
+    for (int ct = 0; ct < C::CPW; ++ct)
+      if (g == 0) zs[(w * C::CPW + ct) * 16 + c] = zst[ct];
+  }
+}
+
+template <class C>
+static hipError_t run_causal(const Plan& p, const Tensors& t, hipStream_t s) {
+  if constexpr (causal_lds_bytes(C::kBF, C::DR, C::DV, C::Kp) > kMaxLds) {
+    return hipErrorNotSupported;     // rejected earlier by validation
+  } else {
+  // 1. span totals through the latent-write kernel (one split per span)
+  BidirArgs wa{};
+  wa.x = t.k;
+  wa.v = t.v;
+  wa.params = t.ws + p.off_params;
+  wa.head_bytes = p.head_bytes;
+  wa.partial = reinterpret_cast<float*>(t.ws + p.off_state);
+  wa.partial_z = reinterpret_cast<float*>(t.ws + p.off_state_z);
+  wa.N = p.N;
+  wa.H = (int)p.H;
+  wa.K = p.K;
+  wa.S = p.nspan;
+  wa.tiles_per_split = p.span_tiles;
+  wa.assign = nullptr;
+  const dim3 grid(p.nspan, (unsigned)p.BH);
+  if (g_launch_hook) g_launch_hook("gma_span_state", s, 1);
+  hipLaunchKernelGGL(gma_write_kernel<C>, grid, dim3(kThreads), 0, s, wa);
+  if (g_launch_hook) g_launch_hook("gma_span_state", s, 0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  // 2. exclusive scan over spans
+  const int nred = C::Kp * C::DV + C::Kp;
+  if (g_launch_hook) g_launch_hook("gma_span_scan", s, 1);
+  hipLaunchKernelGGL(gma_span_scan_kernel, dim3((nred + 255) / 256, (unsigned)p.BH), dim3(256), 0,
+                     s, wa.partial, wa.partial_z, p.nspan, C::Kp, C::DV,
+                     reinterpret_cast<float*>(t.ws + p.off_carry),
+                     reinterpret_cast<float*>(t.ws + p.off_carry_z));
+  if (g_launch_hook) g_launch_hook("gma_span_scan", s, 0);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  // 3. chunked scan
+  CausalArgs ca{};
+  ca.q = t.q;
+  ca.k = t.k;
+  ca.v = t.v;
+  ca.out = t.out;
+  ca.params = t.ws + p.off_params;
+  ca.head_bytes = p.head_bytes;
+  ca.carry = reinterpret_cast<const float*>(t.ws + p.off_carry);
+  ca.carry_z = reinterpret_cast<const float*>(t.ws + p.off_carry_z);
+  ca.assign_q = t.assign_q;
+  ca.assign_k = t.assign_k;
+  ca.N = p.N;
+  ca.H = (int)p.H;
+  ca.nspan = p.nspan;
+  ca.span_tiles = p.span_tiles;
+  ca.eps = t.eps;
+  ca.out_bf = p.out_bf ? 1 : 0;
+  if (g_launch_hook) g_launch_hook("gma_causal", s, 1);
+  hipLaunchKernelGGL(gma_causal_kernel<C>, grid, dim3(kThreads), 0, s, ca);
+  if (g_launch_hook) g_launch_hook("gma_causal", s, 0);
+  return hipGetLastError();
+  }
+}
+
+#define GMA_CDV_CASES(BF, CPW, DR)                                          \
+  switch (p.DV) {                                                           \
+    case 16: return run_causal<Cfg<BF, CPW, 4, DR, 16>>(p, t, s);           \
+    case 32: return run_causal<Cfg<BF, CPW, 4, DR, 32>>(p, t, s);           \
+    case 64: return run_causal<Cfg<BF, CPW, 4, DR, 64>>(p, t, s);           \
+    case 128: return run_causal<Cfg<BF, CPW, 4, DR, 128>>(p, t, s);         \
+  }                                                                         \
+  break;
+#define GMA_CDR_CASES(BF, CPW)                                              \
+  switch (p.DR) {                                                           \
+    case 16: GMA_CDV_CASES(BF, CPW, 16)                                     \
+    case 32: GMA_CDV_CASES(BF, CPW, 32)                                     \
+    case 64: GMA_CDV_CASES(BF, CPW, 64)                                     \
+    case 128: GMA_CDV_CASES(BF, CPW, 128)                                   \
+  }                                                                         \
+  break;
+
+hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s) {
+  if (p.NG != 4) return hipErrorInvalidValue;
+  if (p.bf) {
+    if (p.CPW == 1) { switch (0) { default: GMA_CDR_CASES(true, 1) } }
+    else { switch (0) { default: GMA_CDR_CASES(true, 2) } }
+  } else {
+    if (p.CPW == 1) { switch (0) { default: GMA_CDR_CASES(false, 1) } }
+    else { switch (0) { default: GMA_CDR_CASES(false, 2) } }
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace gma

@@ -62,33 +62,42 @@ def check_assign(gpu: np.ndarray, ref: np.ndarray, X: np.ndarray, gen: dict, dty
     return len(bad)
 
 
-def run_and_compare(w: inputs.Workload, seed: int = 0, rows=None, check_assignments=True):
-    """Run gma_forward on workload w and compare with the oracle.
+def run_and_compare(w: inputs.Workload, seed: int = 0, rows=None, check_assignments=True,
+                    heads=None):
+    """Run gma_forward on workload w (whole batch, as bench.py launches it) and
+    compare with the oracle.
 
     rows: None compares every output row; otherwise a sorted array of row
-    indices compared for every (b, h).  Returns (row-wise error, excused ties).
+    indices compared for every (b, h).  heads: None compares every (b, h);
+    otherwise only batch 0, heads [0, heads) (units are independent, so the
+    oracle runs on that subset).  Returns (row-wise error, excused ties).
     """
     gen = inputs.generate(w, seed)
     dev = upload(gen)
     out, aq, ak = api.forward(dev["Q"], dev["K"], dev["V"], dev["mu"], dev["log_sigma2"],
                               dev["log_pi"], w.eps, w.causal, assign=check_assignments)
     torch.cuda.synchronize()
-    ref = oracle.forward(gen["Q"].f32, gen["K"].f32, gen["V"].f32, gen["mu"],
-                         gen["log_sigma2"], gen["log_pi"], w.eps, w.causal, rows=rows,
-                         want_assign=check_assignments)
-    o = out.float().cpu().numpy()
+    bsl = slice(None) if heads is None else slice(0, 1)
+    hsl = slice(None) if heads is None else slice(0, heads)
+    Q, K, V = gen["Q"].f32[bsl, hsl], gen["K"].f32[bsl, hsl], gen["V"].f32[bsl, hsl]
+    sub = dict(gen)
+    sub["mu"], sub["log_sigma2"], sub["log_pi"] = (gen["mu"][hsl], gen["log_sigma2"][hsl],
+                                                   gen["log_pi"][hsl])
+    ref = oracle.forward(Q, K, V, sub["mu"], sub["log_sigma2"], sub["log_pi"], w.eps, w.causal,
+                         rows=rows, want_assign=check_assignments)
+    o = out.float().cpu().numpy()[bsl, hsl]
     if rows is not None:
         o = o[:, :, rows]
     err = rowwise_rel_err(o, ref["out"])
     ties = 0
     if check_assignments:
-        gq = aq.cpu().numpy()
-        gk = ak.cpu().numpy()
-        Xq = gen["Q"].f32
+        gq = aq.cpu().numpy()[bsl, hsl]
+        gk = ak.cpu().numpy()[bsl, hsl]
+        Xq = Q
         if rows is not None:
             gq, Xq = gq[:, :, rows], Xq[:, :, rows]
-        ties += check_assign(gq, ref["assign_q"], Xq, gen, w.dtype, w.name + " assign_q")
-        ties += check_assign(gk, ref["assign_k"], gen["K"].f32, gen, w.dtype, w.name + " assign_k")
+        ties += check_assign(gq, ref["assign_q"], Xq, sub, w.dtype, w.name + " assign_q")
+        ties += check_assign(gk, ref["assign_k"], K, sub, w.dtype, w.name + " assign_k")
     print("[parity] %s N=%d K=%d d_r=%d d_v=%d %s causal=%d: row-wise err %.3e, ties %d"
           % (w.name, w.N, w.K, w.d_r, w.d_v, w.dtype, int(w.causal), err, ties), flush=True)
     assert np.all(np.isfinite(o)), "non-finite GPU output"
