@@ -29,7 +29,7 @@ struct Cfg {
   static constexpr int KpO = (Kp + CS - 1) / CS * CS;  // component extent of the read contraction
   static constexpr int KSO = KpO / CS;
   static constexpr int DVT = DV / 16;
-  static constexpr int NF = BF ? 3 : 2;            // staged feature arrays
+  static constexpr int NF = BF ? 3 : 1;            // staged feature arrays (fp32: x only)
   static constexpr int PADE = 16 / sizeof(op_t);
   static constexpr int FLD = DRP + PADE;           // feature row stride (elements)
   static constexpr int VLD = kTile + 16 / sizeof(in_t);
@@ -47,7 +47,7 @@ __host__ __device__ constexpr int causal_union_elems(int NF, int FLD, int DV, in
 }
 __host__ __device__ constexpr int causal_lds_bytes(bool bf, int DR, int DV, int Kp) {
   // mirrors Cfg: element sizes, strides and padding
-  return causal_union_elems(bf ? 3 : 2, (DR < (bf ? 32 : 16) ? (bf ? 32 : 16) : DR) + (bf ? 8 : 4),
+  return causal_union_elems(bf ? 3 : 1, (DR < (bf ? 32 : 16) ? (bf ? 32 : 16) : DR) + (bf ? 8 : 4),
                             DV, Kp + (bf ? 8 : 4)) * (bf ? 2 : 4) +
          DV * (kTile + (bf ? 8 : 4)) * (bf ? 2 : 4) +       // Vt
          Kp * 4 + 2 * 4 * kTile * 16 + 2 * 4 * kTile * 4 + kTile * 4;
@@ -94,7 +94,8 @@ __device__ __forceinline__ void load_w(const char* pbase, int ctile0,
   }
 }
 
-// Stage routing features of one tile: bf16 -> (x^2 hi, x^2 lo, x); fp32 -> (x^2 - 1, x).
+// Stage routing features of one tile: bf16 -> (x^2 hi, x^2 lo, x); fp32 -> x (the
+// score loop forms x^2 - 1 in registers).
 template <class C>
 __device__ __forceinline__ void stage_features(const typename C::in_t* __restrict__ xg,
                                                int nvalid, typename C::op_t* F) {
@@ -124,8 +125,7 @@ __device__ __forceinline__ void stage_features(const typename C::in_t* __restric
       st16(f + kTile * C::FLD, lo);
       st16(f + 2 * kTile * C::FLD, x);
     } else {
-      st16(f, x * x - 1.f);
-      st16(f + kTile * C::FLD, x);
+      st16(f, x);
     }
   }
 }
@@ -165,9 +165,9 @@ __device__ __forceinline__ void score_tiles(const typename C::op_t* F, int gt0,
     for (int tt = 0; tt < C::TTW; ++tt) {
       const int tok = tile_token(gt0 + tt, r);
       const typename C::op_t* f = F + tok * C::FLD + s * C::CS + g * C::E;
-      const chunk_t f0 = ld16<chunk_t>(f);
-      const chunk_t f1 = ld16<chunk_t>(f + kTile * C::FLD);
       if constexpr (C::kBF) {
+        const chunk_t f0 = ld16<chunk_t>(f);
+        const chunk_t f1 = ld16<chunk_t>(f + kTile * C::FLD);
         const chunk_t f2 = ld16<chunk_t>(f + 2 * kTile * C::FLD);
 #pragma unroll
         for (int ct = 0; ct < C::CPW; ++ct) {
@@ -188,6 +188,8 @@ __device__ __forceinline__ void score_tiles(const typename C::op_t* F, int gt0,
           S[tt][ct] = acc;
         }
       } else {
+        const chunk_t f1 = ld16<chunk_t>(f);     // x
+        const chunk_t f0 = f1 * f1 - 1.f;        // x^2 - 1
 #pragma unroll
         for (int ct = 0; ct < C::CPW; ++ct) {
           f32x4 acc = S[tt][ct];

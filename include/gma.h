@@ -47,7 +47,8 @@ typedef enum {
 /* Problem shape.  B batches x H heads x N positions.
  *  d_r  routing dimension of Q_X, K_X and the component means: 16, 32, 64 or 128
  *  d_v  value dimension of V_X and the output: 16, 32, 64 or 128
- *  K    number of Gaussian components: 1..128
+ *  K    number of Gaussian components: 1..128 (fp32 causal: K > 64 with d_v = 128
+ *       exceeds the scan kernel's LDS budget and returns GMA_ERR_UNSUPPORTED)
  *  dtype storage type of Q_X, K_X, V_X and out (gma_layer_forward: of X, W and out)
  *  chunk causal scan chunk length: 0 (= 64) or 64; the result does not depend on it */
 typedef struct gma_dims {
