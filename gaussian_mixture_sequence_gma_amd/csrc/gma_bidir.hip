@@ -36,20 +36,29 @@ template <bool BF>
 __global__ void __launch_bounds__(256) gma_prologue_kernel(
     const float* __restrict__ mu, const float* __restrict__ ls2, const float* __restrict__ lpi,
     int H, int K, int Kp, int DR, int DRP, char* __restrict__ params, size_t head_bytes) {
+  // one wave per (head, component) row; lanes stride the routing columns
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= H * Kp) return;
+  const int h = row / Kp, k = row - h * Kp;
   const int n = Kp * DRP;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  // one thread per (head, component, routing column): A and B
-  if (gid < (int64_t)H * n) {
-    const int h = (int)(gid / n), idx = (int)(gid - (int64_t)h * n);
-    const int k = idx / DRP, d = idx - k * DRP;
-    char* base = params + (size_t)h * head_bytes;
+  char* base = params + (size_t)h * head_bytes;
+  // fp32 path: the kernels contract A with (x^2 - 1) instead of x^2 (keeping the
+  // fp32 accumulator near zero for unit-scale routing vectors) and add
+  // c' = c + sum_d A_kd once at the end; bf16 path: c seeds the accumulator.
+  double acc = 0.0, asum = 0.0;
+  for (int d = lane; d < DRP; d += 64) {
     double a = 0.0, b = 0.0;
     if (k < K && d < DR) {
       const size_t off = ((size_t)h * K + k) * DR + d;
+      const double l = ls2[off], m = mu[off];
       const double w = (double)expf(-ls2[off]);
       a = -0.5 * w * kLog2eD;
-      b = (double)mu[off] * w * kLog2eD;
+      b = m * w * kLog2eD;
+      acc += m * m * w + l;
+      asum += -0.5 * w;
     }
+    const int idx = k * DRP + d;
     if constexpr (BF) {
       bf16* Ahi = reinterpret_cast<bf16*>(base);
       const bf16 ah = to_bf16((float)a), bh = to_bf16((float)b);
@@ -63,22 +72,14 @@ __global__ void __launch_bounds__(256) gma_prologue_kernel(
       A[n + idx] = (float)b;
     }
   }
-  // one thread per (head, component): c.  fp32 path: the kernels contract A
-  // with (x^2 - 1) instead of x^2 (keeping the fp32 accumulator near zero for
-  // unit-scale routing vectors) and add c' = c + sum_d A_kd once at the end;
-  // bf16 path: c seeds the accumulator.
-  if (gid < (int64_t)H * Kp) {
-    const int h = (int)(gid / Kp), k = (int)(gid - (int64_t)h * Kp);
-    float* c = reinterpret_cast<float*>(params + (size_t)h * head_bytes + (size_t)8 * n);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    acc += __shfl_xor(acc, off);
+    asum += __shfl_xor(asum, off);
+  }
+  if (lane == 0) {
+    float* c = reinterpret_cast<float*>(base + (size_t)8 * n);
     if (k < K) {
-      double acc = 0.0, asum = 0.0;
-      const size_t off = ((size_t)h * K + k) * DR;
-      for (int d = 0; d < DR; ++d) {
-        const double m = mu[off + d], l = ls2[off + d];
-        const double w = (double)expf(-ls2[off + d]);
-        acc += m * m * w + l;
-        asum += -0.5 * w;
-      }
       const double ck = (double)lpi[(size_t)h * K + k] - 0.5 * acc + (BF ? 0.0 : asum);
       c[k] = (float)(kLog2eD * ck);
     } else {
@@ -115,7 +116,7 @@ __global__ void __launch_bounds__(256) gma_reduce_kernel(const float* __restrict
 // (MODE 1: gamma and assignment written to HBM, for testing).
 // ============================================================================
 template <class C, int MODE>
-__global__ void __launch_bounds__(kThreads) gma_read_kernel(BidirArgs a) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C::kWPERead))) gma_read_kernel(BidirArgs a) {
   using in_t = typename C::in_t;
   using op_t = typename C::op_t;
   using chunk_t = typename C::chunk_t;
@@ -172,12 +173,16 @@ __global__ void __launch_bounds__(kThreads) gma_read_kernel(BidirArgs a) {
   }
 
   const in_t* xs = reinterpret_cast<const in_t*>(a.x) + (size_t)bh * a.N * C::DR;
+  FeatureTile<C> xreg;
+  if (t_begin < t_end) xreg.load(xs, t_begin, (int)min((int64_t)kTile, t_end - t_begin));
 
   for (int64_t tile0 = t_begin; tile0 < t_end; tile0 += kTile) {
     const int nvalid = (int)min((int64_t)kTile, t_end - tile0);
-    __syncthreads();
-    stage_features<C>(xs + (size_t)tile0 * C::DR, nvalid, F);
-    __syncthreads();
+    lds_barrier();
+    xreg.store(F);
+    lds_barrier();
+    if (tile0 + kTile < t_end)
+      xreg.load(xs, tile0 + kTile, (int)min((int64_t)kTile, t_end - tile0 - kTile));
 
     f32x4 S[C::TTW][C::CPW];
 #pragma unroll
@@ -236,7 +241,7 @@ __global__ void __launch_bounds__(kThreads) gma_read_kernel(BidirArgs a) {
           stats[cgi * kTile + tile_token(gt0 + tt, c)] =
               f32x4{m[tt], l[tt], dn[tt], __int_as_float(am[tt])};
       }
-      __syncthreads();
+      lds_barrier();
       if (threadIdx.x < kTile) {
         const int t = threadIdx.x;
         f32x4 st[C::NG];
@@ -267,7 +272,7 @@ __global__ void __launch_bounds__(kThreads) gma_read_kernel(BidirArgs a) {
         }
         if (want_assign && t < nvalid) a.assign[(size_t)bh * a.N + tile0 + t] = arg;
       }
-      __syncthreads();
+      lds_barrier();
 #pragma unroll
       for (int tt = 0; tt < C::TTW; ++tt) f[tt] = fac[cgi * kTile + tile_token(gt0 + tt, c)];
     } else {
@@ -320,7 +325,7 @@ __global__ void __launch_bounds__(kThreads) gma_read_kernel(BidirArgs a) {
           }
         }
       }
-      __syncthreads();
+      lds_barrier();
 
       // O = diag(rinv) Gamma' V~ for this wave's (token tile, d tile) share
 #pragma unroll
@@ -383,12 +388,13 @@ static hipError_t run_bidir(const Plan& p, const Tensors& t, hipStream_t s) {
   a.v = t.v;
   a.assign = t.assign_k;
   if (g_launch_hook) g_launch_hook("gma_write", s, 1);
-  hipLaunchKernelGGL(gma_write_kernel<C>, grid, dim3(kThreads), 0, s, a);
+  if constexpr (C::kBF) hipLaunchKernelGGL(gma_write_bf16_kernel<C>, grid, dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL(gma_write_kernel<C>, grid, dim3(kThreads), 0, s, a);
   if (g_launch_hook) g_launch_hook("gma_write", s, 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  const int PS = p.S * C::TG;
+  const int PS = C::kBF ? p.S : p.S * C::TG;    // partial slots per sequence
   const int nred = C::Kp * C::DV + C::Kp;
   if (g_launch_hook) g_launch_hook("gma_reduce", s, 1);
   hipLaunchKernelGGL(gma_reduce_kernel, dim3((nred + 255) / 256, (unsigned)p.BH), dim3(256), 0, s,
@@ -430,8 +436,8 @@ static hipError_t run_resp(const Plan& p, const Tensors& t, hipStream_t s) {
 
 hipError_t launch_prologue(const Plan& p, const Tensors& t, hipStream_t s) {
   if (g_launch_hook) g_launch_hook("gma_prologue", s, 1);
-  const int64_t nthreads = p.H * (int64_t)p.Kp * p.DRP;
-  const dim3 grid((unsigned)((nthreads + 255) / 256));
+  const int64_t rows = p.H * (int64_t)p.Kp;          // one wave per (head, component)
+  const dim3 grid((unsigned)((rows + 3) / 4));
   if (p.bf)
     hipLaunchKernelGGL(gma_prologue_kernel<true>, grid, dim3(256), 0, s, t.mu, t.ls2, t.lpi,
                        (int)p.H, p.K, p.Kp, p.DR, p.DRP, t.ws + p.off_params, p.head_bytes);

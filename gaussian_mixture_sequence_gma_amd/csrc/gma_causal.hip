@@ -470,7 +470,8 @@ static hipError_t run_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   wa.assign = nullptr;
   const dim3 grid(p.nspan, (unsigned)p.BH);
   if (g_launch_hook) g_launch_hook("gma_span_state", s, 1);
-  hipLaunchKernelGGL(gma_write_kernel<C>, grid, dim3(kThreads), 0, s, wa);
+  if constexpr (C::kBF) hipLaunchKernelGGL(gma_write_bf16_kernel<C>, grid, dim3(kThreads), 0, s, wa);
+  else hipLaunchKernelGGL(gma_write_kernel<C>, grid, dim3(kThreads), 0, s, wa);
   if (g_launch_hook) g_launch_hook("gma_span_state", s, 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

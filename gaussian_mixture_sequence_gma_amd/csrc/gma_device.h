@@ -154,4 +154,63 @@ __device__ __forceinline__ void split_bf16(float x, bf16& hi, bf16& lo) {
 
 template <class T> __device__ __forceinline__ T load_elem(const T* p) { return *p; }
 
+// Workgroup barrier that orders LDS only: outstanding global loads (prefetch of
+// the next tile) stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// ds_read_b64_tr_b16: within each 16-lane group, source lane s = a + 4m
+// supplies an 8-byte block; destination lane 4a + e receives element e of the
+// blocks of source lanes a, a+4, a+8, a+12 (in that order).
+typedef short short4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ short4_t lds_read_tr16(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4_t*)(p));
+}
+
+// MFMA operand chunk from a row-major LDS matrix M[token][col] (bf16, row
+// stride ld elements, multiple of 4): lane (l % 16, g) receives the eight
+// tokens tok0 + 8g .. tok0 + 8g + 7 of column col0 + (l % 16), i.e. the
+// contraction runs over tokens.  Two transpose reads.
+__device__ __forceinline__ bf16x8 tr_chunk(const bf16* M, int ld, int tok0, int col0) {
+  const int lane = threadIdx.x & 63, s = lane & 15, g = lane >> 4;
+  const bf16* p = M + (tok0 + 8 * g + (s >> 2)) * ld + col0 + 4 * (s & 3);
+  const short4_t lo = lds_read_tr16(p);
+  const short4_t hi = lds_read_tr16(p + 4 * ld);
+  typedef short short8_t __attribute__((ext_vector_type(8)));
+  const short8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Swizzled row-major tile: ROWCH 16-byte chunks per row, logical chunk j of
+// row r stored at physical chunk j ^ swz(r), swz(r) = 2r mod ROWCH (even, so
+// the two 8-byte halves a transpose read touches stay together and the four
+// rows of one read land on distinct banks).  Unpadded, so a wave can fill it
+// with 1 KB direct global-to-LDS loads.
+template <int ROWCH>
+__device__ __forceinline__ int swz_elem(int row, int col) {
+  constexpr int mask = ROWCH >= 2 ? ROWCH - 2 : 0;
+  return row * ROWCH * 8 + ((((col >> 3) ^ ((2 * row) & mask))) << 3) + (col & 7);
+}
+template <int ROWCH>
+__device__ __forceinline__ bf16x8 tr_chunk_swz(const bf16* M, int tok0, int col0) {
+  const int lane = threadIdx.x & 63, s = lane & 15, g = lane >> 4;
+  const int row = tok0 + 8 * g + (s >> 2), col = col0 + 4 * (s & 3);
+  const short4_t lo = lds_read_tr16(M + swz_elem<ROWCH>(row, col));
+  const short4_t hi = lds_read_tr16(M + swz_elem<ROWCH>(row + 4, col));
+  typedef short short8_t __attribute__((ext_vector_type(8)));
+  const short8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at
+// lds_base + 16*l (lds_base must be the same for the whole wave).
+__device__ __forceinline__ void global_to_lds16(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
+}
+__device__ __forceinline__ void wait_global_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 }  // namespace gma

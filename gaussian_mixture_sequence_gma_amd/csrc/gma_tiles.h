@@ -34,9 +34,14 @@ struct Cfg {
   static constexpr int FLD = DRP + PADE;           // feature row stride (elements)
   static constexpr int VLD = kTile + 16 / sizeof(in_t);
   static constexpr int GLD = KpO + PADE;
+  // occupancy request (waves per SIMD) for the streaming kernels; set by
+  // WavesPerEU below from register-budget measurements
   // read-out work split among the NG waves of a token group
   static constexpr int DPW = DVT >= NG ? DVT / NG : 1;
   static constexpr int TPW = DVT >= NG ? TTW : TTW * DVT / NG;
+  // 2 waves/SIMD where the compiler fits the kernel in 256 VGPRs without spills
+  static constexpr int kWPEWrite = ((DV == 128 || DR == 128) && NG >= 2) ? 1 : 2;
+  static constexpr int kWPERead = (DR == 128 || (!BF && NG == 4 && DV == 128)) ? 1 : 2;
 };
 
 // LDS bytes of the causal scan kernel: the staged features of Q and K share
@@ -149,6 +154,62 @@ __device__ __forceinline__ void stage_vt(const typename C::in_t* __restrict__ vg
     for (int e = 0; e < C::E; ++e) Vt[(part * C::E + e) * C::VLD + t] = v[e];
   }
 }
+
+// Routing vectors of one 64-token tile held in registers (prefetched while the
+// previous tile is processed), then expanded into the staged feature arrays.
+template <class C>
+struct FeatureTile {
+  using chunk_t = typename C::chunk_t;
+  static constexpr int CPR = C::DR / C::E;            // 16-byte chunks per token row
+  static constexpr int CH = kTile * CPR;
+  static constexpr int NC = (CH + kThreads - 1) / kThreads;
+  chunk_t r[NC];
+
+  __device__ __forceinline__ void load(const typename C::in_t* __restrict__ xs, int64_t tile0,
+                                       int nvalid) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const int i = threadIdx.x + j * kThreads;
+      const int t = i / CPR, part = i - t * CPR;
+      if (i < CH && t < nvalid) r[j] = ld16<chunk_t>(xs + (size_t)(tile0 + t) * C::DR + part * C::E);
+      else r[j] = chunk_t{};
+    }
+  }
+  // bf16 -> (x^2 hi, x^2 lo, x); fp32 -> x.  Also zeroes routing columns beyond d_r.
+  __device__ __forceinline__ void store(typename C::op_t* F) const {
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const int i = threadIdx.x + j * kThreads;
+      if (i < CH) {
+        const int t = i / CPR, part = i - t * CPR;
+        typename C::op_t* f = F + t * C::FLD + part * C::E;
+        if constexpr (C::kBF) {
+          bf16x8 hi, lo;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float xf = from_bf16(r[j][e]);
+            bf16 hh, ll;
+            split_bf16(xf * xf, hh, ll);
+            hi[e] = hh;
+            lo[e] = ll;
+          }
+          st16(f, hi);
+          st16(f + kTile * C::FLD, lo);
+          st16(f + 2 * kTile * C::FLD, r[j]);
+        } else {
+          st16(f, r[j]);
+        }
+      }
+    }
+    if constexpr (C::DR < C::DRP) {
+      constexpr int PADCH = (C::DRP - C::DR) / C::E;
+      for (int i = threadIdx.x; i < C::NF * kTile * PADCH; i += kThreads) {
+        const int row = i / PADCH, pc = i - row * PADCH;
+        st16(F + row * C::FLD + C::DR + pc * C::E, chunk_t{});
+      }
+    }
+  }
+};
 
 // Score tiles.  TRANS = false: D[token][component] (features are the A operand);
 // TRANS = true: D[component][token].  Accumulators arrive initialised with c
@@ -466,5 +527,262 @@ __global__ void __launch_bounds__(kThreads) gma_write_kernel(BidirArgs a) {
   }
 }
 
+
+// ============================================================================
+// Latent write, bf16 inputs.  Scores are computed in the D[component][token]
+// layout (per-token statistics stay inside a lane plus two cross-group steps),
+// Gamma^K goes to LDS row-major [token][component] and both operands of
+// V~ += Gamma^T V are read with transpose reads, so V is staged with plain
+// 16-byte row copies.  Wave w accumulates its own (component, d_v) output tiles
+// over all 64 tokens of each tile; the next tile's K and V are prefetched into
+// registers while the current one is processed.  One partial per workgroup.
+// ============================================================================
+template <class C>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C::kWPEWrite))) gma_write_bf16_kernel(BidirArgs a) {
+  static_assert(C::kBF, "bf16 kernel");
+  constexpr int CT = C::CPW * C::NG;
+  constexpr int CTW = CT >= 4 ? CT / 4 : 1;                  // output component tiles per wave
+  constexpr int DW = CT >= 4 ? C::DVT : (C::DVT * CT + 3) / 4; // output d tiles per wave
+  constexpr int GRLD = C::Kp + 16;                            // Gamma row stride (bf16)
+  constexpr int VROWCH = C::DV / 8;                           // 16-byte chunks per V row
+  constexpr int FE = 3 * kTile * C::FLD;
+  constexpr int UE = FE > kTile * GRLD ? FE : kTile * GRLD;
+  constexpr int VCH = kTile * VROWCH;                         // 16-byte chunks of a V tile
+  static_assert(VCH % 64 == 0, "V tile fills whole wave loads");
+  constexpr int VROUNDS = VCH / 64;                           // wave-wide 1 KB loads per tile
+  // staged features (dead after the scores) share storage with Gamma
+  __shared__ __attribute__((aligned(16))) bf16 U[UE];
+  __shared__ __attribute__((aligned(16))) bf16 Vr[2][kTile * C::DV];   // double buffer, swizzled
+  __shared__ __attribute__((aligned(16))) f32x4 stats[C::NG * kTile];
+  __shared__ __attribute__((aligned(16))) float fac[C::NG * kTile];
+  __shared__ __attribute__((aligned(16))) float zred[C::TG * C::Kp];
+  bf16* const F = U;
+  bf16* const G = U;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int cgi = wave % C::NG, tg = wave / C::NG;
+  const int gt0 = tg * C::TTW;
+  const int64_t bh = blockIdx.y;
+  const int h = (int)(bh % a.H);
+  const int split = blockIdx.x;
+  const int64_t t_begin = (int64_t)split * a.tiles_per_split * kTile;
+  const int64_t t_end = a.N < t_begin + (int64_t)a.tiles_per_split * kTile
+                            ? a.N : t_begin + (int64_t)a.tiles_per_split * kTile;
+  const bool want_assign = a.assign != nullptr;
+
+  const char* pbase = a.params + (size_t)h * a.head_bytes;
+  bf16x8 W[C::CPW][C::NKS][4];
+  load_w<C>(pbase, cgi * C::CPW, W);
+  const float* cvec = reinterpret_cast<const float*>(pbase + (size_t)8 * C::Kp * C::DRP);
+  __shared__ __attribute__((aligned(16))) float cl[C::Kp];   // score seeds, re-read per tile
+  for (int k = threadIdx.x; k < C::Kp; k += kThreads) cl[k] = cvec[k];
+
+  // output tiles of this wave
+  const int oct0 = CT >= 4 ? wave * CTW : wave % CT;
+  f32x4 vacc[CTW][DW];
+#pragma unroll
+  for (int i = 0; i < CTW; ++i)
+#pragma unroll
+    for (int j = 0; j < DW; ++j) vacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float zl[C::CPW][4];
+#pragma unroll
+  for (int ct = 0; ct < C::CPW; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) zl[ct][i] = 0.f;
+
+  const bf16* xs = reinterpret_cast<const bf16*>(a.x) + (size_t)bh * a.N * C::DR;
+  const bf16* vs = reinterpret_cast<const bf16*>(a.v) + (size_t)bh * a.N * C::DV;
+  FeatureTile<C> kreg;
+  // V tile -> Vr[buf] by direct loads; rows past the valid range repeat the last
+  // valid row (their responsibilities are zero, and the loads stay in bounds)
+  auto load_v = [&](int64_t tile0, int buf) {
+    const int nv = (int)(t_end - tile0 < kTile ? t_end - tile0 : kTile);
+#pragma unroll
+    for (int j = 0; j < VROUNDS; j += kWaves) {
+      const int round = j + wave;
+      if (round < VROUNDS) {
+        const int P = round * 64 + lane;                      // physical chunk
+        const int r = P / VROWCH, pc = P - r * VROWCH;
+        const int lc = pc ^ ((2 * r) & (VROWCH >= 2 ? VROWCH - 2 : 0));
+        const int rr = r < nv ? r : nv - 1;
+        global_to_lds16(vs + (size_t)(tile0 + rr) * C::DV + lc * 8, &Vr[buf][round * 64 * 8]);
+      }
+    }
+  };
+  if (t_begin < t_end) {
+    kreg.load(xs, t_begin, (int)(t_end - t_begin < kTile ? t_end - t_begin : kTile));
+    load_v(t_begin, 0);
+  }
+  int buf = 0;
+
+  for (int64_t tile0 = t_begin; tile0 < t_end; tile0 += kTile) {
+    const int nvalid = (int)(t_end - tile0 < kTile ? t_end - tile0 : kTile);
+    lds_barrier();
+    // ---- stage features (x^2 hi, x^2 lo, x; pad columns re-zeroed since Gamma
+    // overlays them); this tile's V rows were loaded into Vr[buf] directly --------
+    kreg.store(F);
+    wait_global_loads();
+    lds_barrier();
+    if (tile0 + kTile < t_end) {
+      const int64_t nt = tile0 + kTile;
+      kreg.load(xs, nt, (int)(t_end - nt < kTile ? t_end - nt : kTile));
+      load_v(nt, buf ^ 1);
+    }
+
+    // ---- scores D[component][token] and per-token statistics --------------------
+    f32x4 S[C::TTW][C::CPW];
+#pragma unroll
+    for (int tt = 0; tt < C::TTW; ++tt)
+#pragma unroll
+      for (int ct = 0; ct < C::CPW; ++ct) S[tt][ct] = ld16<f32x4>(&cl[(cgi * C::CPW + ct) * 16 + 4 * g]);
+    score_tiles<C, true>(F, gt0, W, S);
+    float m[C::TTW], l[C::TTW];
+    int am[C::TTW];
+#pragma unroll
+    for (int tt = 0; tt < C::TTW; ++tt) {
+      float v = S[tt][0][0];
+#pragma unroll
+      for (int ct = 0; ct < C::CPW; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v = fmaxf(v, S[tt][ct][i]);
+      m[tt] = groups_max(v);
+      am[tt] = 0;
+      if (want_assign) {
+        float bv = S[tt][0][0];
+        int bi = (cgi * C::CPW) * 16 + 4 * g;
+#pragma unroll
+        for (int ct = 0; ct < C::CPW; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            argmax_merge(bv, bi, S[tt][ct][i], (cgi * C::CPW + ct) * 16 + 4 * g + i);
+        groups_argmax(bv, bi);
+        am[tt] = bi;
+      }
+      const float mu_ = m[tt] == -INFINITY ? 0.f : m[tt];
+      float sum = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < C::CPW; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = exp2_fast(S[tt][ct][i] - mu_);
+          S[tt][ct][i] = e;
+          sum += e;
+        }
+      l[tt] = groups_sum(sum);
+    }
+    float f[C::TTW];
+    if constexpr (C::NG > 1) {
+      if (g == 0) {
+#pragma unroll
+        for (int tt = 0; tt < C::TTW; ++tt)
+          stats[cgi * kTile + tile_token(gt0 + tt, c)] = f32x4{m[tt], l[tt], 0.f, __int_as_float(am[tt])};
+      }
+      lds_barrier();
+      if (threadIdx.x < kTile) {
+        const int t = threadIdx.x;
+        f32x4 st[C::NG];
+        float M = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < C::NG; ++q) {
+          st[q] = stats[q * kTile + t];
+          M = fmaxf(M, st[q][0]);
+        }
+        float L = 0.f, fq[C::NG];
+        int arg = 0;
+        bool found = false;
+#pragma unroll
+        for (int q = 0; q < C::NG; ++q) {
+          fq[q] = st[q][0] == -INFINITY ? 0.f : exp2_fast(st[q][0] - M);
+          L += fq[q] * st[q][1];
+          if (!found && st[q][0] == M) { arg = __float_as_int(st[q][3]); found = true; }
+        }
+        const float invL = 1.f / L;
+#pragma unroll
+        for (int q = 0; q < C::NG; ++q) fac[q * kTile + t] = fq[q] * invL;
+        if (want_assign && t < nvalid) a.assign[(size_t)bh * a.N + tile0 + t] = arg;
+      }
+      lds_barrier();
+#pragma unroll
+      for (int tt = 0; tt < C::TTW; ++tt) f[tt] = fac[cgi * kTile + tile_token(gt0 + tt, c)];
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < C::TTW; ++tt) {
+        f[tt] = 1.f / l[tt];
+        const int tok = tile_token(gt0 + tt, c);
+        if (want_assign && g == 0 && tok < nvalid) a.assign[(size_t)bh * a.N + tile0 + tok] = am[tt];
+      }
+      lds_barrier();   // every wave is past its feature reads before Gamma overwrites them
+    }
+
+    // ---- Gamma (masked to valid tokens) -> LDS [token][component]; Z partials ----
+#pragma unroll
+    for (int tt = 0; tt < C::TTW; ++tt) {
+      const int tok = tile_token(gt0 + tt, c);
+      const float fi = tok < nvalid ? f[tt] : 0.f;
+#pragma unroll
+      for (int ct = 0; ct < C::CPW; ++ct) {
+        bf16x4 v4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float gm = S[tt][ct][i] * fi;
+          zl[ct][i] += gm;
+          v4[i] = to_bf16(gm);
+        }
+        *reinterpret_cast<bf16x4*>(&G[tok * GRLD + (cgi * C::CPW + ct) * 16 + 4 * g]) = v4;
+      }
+    }
+    lds_barrier();
+
+    // ---- V~ += Gamma^T V over the 64 tokens -----------------------------------
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      bf16x8 A[CTW];
+#pragma unroll
+      for (int i = 0; i < CTW; ++i) A[i] = tr_chunk(G, GRLD, 32 * p, (oct0 + i) * 16);
+#pragma unroll
+      for (int j = 0; j < DW; ++j) {
+        const int dt = CT >= 4 ? j : wave / CT + (4 / CT) * j;
+        if (dt < C::DVT) {
+          const bf16x8 Bv = tr_chunk_swz<VROWCH>(Vr[buf], 32 * p, dt * 16);
+#pragma unroll
+          for (int i = 0; i < CTW; ++i) vacc[i][j] = mma(A[i], Bv, vacc[i][j]);
+        }
+      }
+    }
+    buf ^= 1;
+  }
+
+  // ---- partial (V~, Z) of this workgroup --------------------------------------
+  const size_t pslot = (size_t)bh * a.S + split;
+  float* pv = a.partial + pslot * C::Kp * C::DV;
+  float* pz = a.partial_z + pslot * C::Kp;
+#pragma unroll
+  for (int i = 0; i < CTW; ++i)
+#pragma unroll
+    for (int j = 0; j < DW; ++j) {
+      const int dt = CT >= 4 ? j : wave / CT + (4 / CT) * j;
+      if (dt < C::DVT) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          pv[((oct0 + i) * 16 + 4 * g + r) * C::DV + dt * 16 + c] = vacc[i][j][r];
+      }
+    }
+  // Z: lanes hold per-token partials; sum the 16 lanes of a row, then token groups
+#pragma unroll
+  for (int ct = 0; ct < C::CPW; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float zt = row16_sum(zl[ct][i]);
+      if (c == 0) zred[tg * C::Kp + (cgi * C::CPW + ct) * 16 + 4 * g + i] = zt;
+    }
+  lds_barrier();
+  for (int k = threadIdx.x; k < C::Kp; k += kThreads) {
+    float zt = 0.f;
+#pragma unroll
+    for (int q = 0; q < C::TG; ++q) zt += zred[q * C::Kp + k];
+    pz[k] = zt;
+  }
+}
 
 }  // namespace gma
