@@ -120,8 +120,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C
   using in_t = typename C::in_t;
   using op_t = typename C::op_t;
   using chunk_t = typename C::chunk_t;
-  __shared__ __attribute__((aligned(16))) op_t F[C::NF * kTile * C::FLD];
-  __shared__ __attribute__((aligned(16))) op_t G[MODE == 0 ? kTile * C::GLD : 1];
+  __shared__ __attribute__((aligned(16))) op_t F[C::NF * C::FAS];
+  __shared__ __attribute__((aligned(16))) op_t G[MODE == 0 ? C::GAS : 1];
   __shared__ __attribute__((aligned(16))) f32x4 stats[C::NG * kTile];
   __shared__ __attribute__((aligned(16))) float fac[C::NG * kTile];
   __shared__ __attribute__((aligned(16))) float rinv[kTile];
@@ -137,9 +137,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C
   const int64_t t_end = min(a.N, t_begin + (int64_t)a.tiles_per_split * kTile);
   const bool want_assign = a.assign != nullptr;
 
-  for (int i = threadIdx.x; i < C::NF * kTile * C::FLD; i += kThreads) F[i] = (op_t)0;
+  for (int i = threadIdx.x; i < C::NF * C::FAS; i += kThreads) F[i] = (op_t)0;
   if constexpr (MODE == 0)
-    for (int i = threadIdx.x; i < kTile * C::GLD; i += kThreads) G[i] = (op_t)0;
+    for (int i = threadIdx.x; i < C::GAS; i += kThreads) G[i] = (op_t)0;
 
   const char* pbase = a.params + (size_t)h * a.head_bytes;
   chunk_t W[C::CPW][C::NKS][C::NARR];
@@ -314,7 +314,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C
         const int tok = tile_token(gt0 + tt, c);
 #pragma unroll
         for (int ct = 0; ct < C::CPW; ++ct) {
-          op_t* dst = &G[tok * C::GLD + (cgi * C::CPW + ct) * 16 + 4 * g];
+          op_t* dst = &G[C::grow(tok) + (cgi * C::CPW + ct) * 16 + 4 * g];
           if constexpr (C::kBF) {
             bf16x4 v4;
 #pragma unroll
@@ -327,7 +327,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C
       }
       lds_barrier();
 
-      // O = diag(rinv) Gamma' V~ for this wave's (token tile, d tile) share
+      // O^T = V~^T Gamma'^T for this wave's (token tile, d tile) share: lane column =
+      // token, rows = four consecutive d, so each lane scales by one normaliser and
+      // writes 8 (bf16) or 16 (fp32) contiguous bytes
 #pragma unroll
       for (int jt = 0; jt < C::TPW; ++jt) {
         const int tt = C::DVT >= C::NG ? jt : cgi / C::DVT + (C::NG / C::DVT) * jt;
@@ -338,23 +340,24 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C
         const int rtok = tile_token(gt, c);
 #pragma unroll
         for (int s = 0; s < C::KSO; ++s) {
-          const chunk_t A = ld16<chunk_t>(&G[rtok * C::GLD + s * C::CS + g * C::E]);
+          const chunk_t Bg = ld16<chunk_t>(&G[C::grow(rtok) + s * C::CS + g * C::E]);
 #pragma unroll
-          for (int j = 0; j < C::DPW; ++j) acc[j] = mma(A, Vr[j][s], acc[j]);
+          for (int j = 0; j < C::DPW; ++j) acc[j] = mma(Vr[j][s], Bg, acc[j]);
         }
-        const int tok0 = tile_token(gt, 4 * g);
-        const f32x4 rv = ld16<f32x4>(&rinv[tok0]);
+        const float rv = rinv[rtok];
+        if (rtok < nvalid) {
 #pragma unroll
-        for (int j = 0; j < C::DPW; ++j) {
-          const int dt = C::DVT >= C::NG ? cgi * C::DPW + j : cgi % C::DVT;
+          for (int j = 0; j < C::DPW; ++j) {
+            const int dt = C::DVT >= C::NG ? cgi * C::DPW + j : cgi % C::DVT;
+            const size_t off = ((size_t)bh * a.N + tile0 + rtok) * C::DV + dt * 16 + 4 * g;
+            const f32x4 o = acc[j] * rv;
+            if (a.out_bf) {
+              bf16x4 o4;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int tok = tok0 + i;
-            if (tok < nvalid) {
-              const float o = acc[j][i] * rv[i];
-              const size_t off = ((size_t)bh * a.N + tile0 + tok) * C::DV + dt * 16 + c;
-              if (a.out_bf) reinterpret_cast<bf16*>(a.out)[off] = to_bf16(o);
-              else reinterpret_cast<float*>(a.out)[off] = o;
+              for (int i = 0; i < 4; ++i) o4[i] = to_bf16(o[i]);
+              *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(a.out) + off) = o4;
+            } else {
+              st16(reinterpret_cast<float*>(a.out) + off, o);
             }
           }
         }

@@ -75,15 +75,15 @@ __global__ void __launch_bounds__(kThreads) gma_causal_kernel(CausalArgs a) {
   using in_t = typename C::in_t;
   using op_t = typename C::op_t;
   using chunk_t = typename C::chunk_t;
-  constexpr int FE = C::NF * kTile * C::FLD;
+  constexpr int FE = C::NF * C::FAS;
   // features (dead once the scores exist) share storage with Gamma^Q, Gamma^K, S
-  __shared__ __attribute__((aligned(16))) op_t U[causal_union_elems(C::NF, C::FLD, C::DV, C::GLD)];
+  __shared__ __attribute__((aligned(16))) op_t U[causal_union_elems(C::NF, C::FAS, C::DV, C::GAS, C::GLD)];
   __shared__ __attribute__((aligned(16))) in_t Vt[C::DV * C::VLD];
   op_t* const QF = U;
   op_t* const KF = U + FE;
   op_t* const GQ = U;
-  op_t* const GK = U + kTile * C::GLD;
-  op_t* const ST = U + 2 * kTile * C::GLD;
+  op_t* const GK = U + C::GAS;
+  op_t* const ST = U + 2 * C::GAS;
   __shared__ __attribute__((aligned(16))) float zs[C::Kp];
   __shared__ __attribute__((aligned(16))) f32x4 statsK[4 * kTile];
   __shared__ __attribute__((aligned(16))) f32x4 statsQ[4 * kTile];
@@ -284,10 +284,10 @@ __global__ void __launch_bounds__(kThreads) gma_causal_kernel(CausalArgs a) {
           const int ktok = tile_token(tt, 4 * g + i);
           const float gk = ktok < nvalid ? SK[tt][ct][i] * fk[i] : 0.f;
           SK[tt][ct][i] = gk;
-          GK[ktok * C::GLD + comp0 + c] = (op_t)gk;
+          GK[C::grow(ktok) + comp0 + c] = (op_t)gk;
           SQ[tt][ct][i] *= fqv;
         }
-        op_t* dst = &GQ[qtok * C::GLD + comp0 + 4 * g];
+        op_t* dst = &GQ[C::grow(qtok) + comp0 + 4 * g];
         if constexpr (C::kBF) {
           bf16x4 v4;
 #pragma unroll
@@ -327,7 +327,7 @@ __global__ void __launch_bounds__(kThreads) gma_causal_kernel(CausalArgs a) {
       // carried memory: Gamma^Q_c S
 #pragma unroll
       for (int s = 0; s < C::KSO; ++s) {
-        const chunk_t A = ld16<chunk_t>(&GQ[itok_c * C::GLD + s * C::CS + g * C::E]);
+        const chunk_t A = ld16<chunk_t>(&GQ[C::grow(itok_c) + s * C::CS + g * C::E]);
 #pragma unroll
         for (int dt = 0; dt < C::DVT; ++dt) {
           const chunk_t Bs = ld16<chunk_t>(&ST[(dt * 16 + c) * C::GLD + s * C::CS + g * C::E]);
@@ -344,8 +344,8 @@ __global__ void __launch_bounds__(kThreads) gma_causal_kernel(CausalArgs a) {
           f32x4 pt = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < C::KSO; ++s) {
-            const chunk_t Ak = ld16<chunk_t>(&GK[tile_token(jt, c) * C::GLD + s * C::CS + g * C::E]);
-            const chunk_t Bq = ld16<chunk_t>(&GQ[itok_c * C::GLD + s * C::CS + g * C::E]);
+            const chunk_t Ak = ld16<chunk_t>(&GK[C::grow(tile_token(jt, c)) + s * C::CS + g * C::E]);
+            const chunk_t Bq = ld16<chunk_t>(&GQ[C::grow(itok_c) + s * C::CS + g * C::E]);
             pt = mma(Ak, Bq, pt);
           }
           if (p == Pi) {

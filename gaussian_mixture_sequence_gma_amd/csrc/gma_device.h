@@ -185,6 +185,23 @@ __device__ __forceinline__ bf16x8 tr_chunk(const bf16* M, int ld, int tok0, int 
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Row offset of token row r in a row-major [token][column] bf16 tile read by
+// tr_chunk_g: a bank skew of 16 B for bit 3 and 8 B for bit 4 of r keeps both
+// the 8-byte stores of 16 rows tile_token(gt, 0..15) and the transpose reads
+// of 4 consecutive rows conflict-free (row stride ld must be 16 mod 32 elements).
+__device__ __forceinline__ int gtr_row(int r, int ld) {
+  return r * ld + 8 * ((r >> 3) & 1) + 4 * ((r >> 4) & 1);
+}
+__device__ __forceinline__ bf16x8 tr_chunk_g(const bf16* M, int ld, int tok0, int col0) {
+  const int lane = threadIdx.x & 63, s = lane & 15, g = lane >> 4;
+  const int row = tok0 + 8 * g + (s >> 2), col = col0 + 4 * (s & 3);
+  const short4_t lo = lds_read_tr16(M + gtr_row(row, ld) + col);
+  const short4_t hi = lds_read_tr16(M + gtr_row(row + 4, ld) + col);
+  typedef short short8_t __attribute__((ext_vector_type(8)));
+  const short8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // Swizzled row-major tile: ROWCH 16-byte chunks per row, logical chunk j of
 // row r stored at physical chunk j ^ swz(r), swz(r) = 2r mod ROWCH (even, so
 // the two 8-byte halves a transpose read touches stay together and the four

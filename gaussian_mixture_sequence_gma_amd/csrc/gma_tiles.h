@@ -32,8 +32,17 @@ struct Cfg {
   static constexpr int NF = BF ? 3 : 1;            // staged feature arrays (fp32: x only)
   static constexpr int PADE = 16 / sizeof(op_t);
   static constexpr int FLD = DRP + PADE;           // feature row stride (elements)
+  // Each block of 16 token rows is shifted by a further 64 bytes: the 16 rows one
+  // MFMA operand read touches (tokens r and r+16 of a 32-token pair, see
+  // tile_token) then fall on 16 distinct 4-bank groups for every d_r.  Same for
+  // the Gamma' rows below.
+  static constexpr int SKEW = 64 / (int)sizeof(op_t);
+  static constexpr int FAS = kTile * FLD + 3 * SKEW;   // stride between feature arrays
+  __host__ __device__ static constexpr int frow(int r) { return r * FLD + SKEW * (r >> 4); }
   static constexpr int VLD = kTile + 16 / sizeof(in_t);
   static constexpr int GLD = KpO + PADE;
+  static constexpr int GAS = kTile * GLD + 3 * SKEW;   // Gamma' [token][component] array size
+  __host__ __device__ static constexpr int grow(int r) { return r * GLD + SKEW * (r >> 4); }
   // occupancy request (waves per SIMD) for the streaming kernels; set by
   // WavesPerEU below from register-budget measurements
   // read-out work split among the NG waves of a token group
@@ -46,14 +55,16 @@ struct Cfg {
 
 // LDS bytes of the causal scan kernel: the staged features of Q and K share
 // storage with Gamma^Q, Gamma^K and the carried state (live at different times).
-__host__ __device__ constexpr int causal_union_elems(int NF, int FLD, int DV, int GLD) {
-  return 2 * NF * kTile * FLD > (2 * kTile + DV) * GLD ? 2 * NF * kTile * FLD
-                                                        : (2 * kTile + DV) * GLD;
+__host__ __device__ constexpr int causal_union_elems(int NF, int FAS, int DV, int GAS, int GLD) {
+  return 2 * NF * FAS > 2 * GAS + DV * GLD ? 2 * NF * FAS : 2 * GAS + DV * GLD;
 }
 __host__ __device__ constexpr int causal_lds_bytes(bool bf, int DR, int DV, int Kp) {
-  // mirrors Cfg: element sizes, strides and padding
-  return causal_union_elems(bf ? 3 : 1, (DR < (bf ? 32 : 16) ? (bf ? 32 : 16) : DR) + (bf ? 8 : 4),
-                            DV, Kp + (bf ? 8 : 4)) * (bf ? 2 : 4) +
+  // mirrors Cfg: element sizes, strides, padding and skews
+  return causal_union_elems(bf ? 3 : 1,
+                            kTile * ((DR < (bf ? 32 : 16) ? (bf ? 32 : 16) : DR) + (bf ? 8 : 4)) +
+                                3 * (bf ? 32 : 16),
+                            DV, kTile * (Kp + (bf ? 8 : 4)) + 3 * (bf ? 32 : 16), Kp + (bf ? 8 : 4)) *
+             (bf ? 2 : 4) +
          DV * (kTile + (bf ? 8 : 4)) * (bf ? 2 : 4) +       // Vt
          Kp * 4 + 2 * 4 * kTile * 16 + 2 * 4 * kTile * 4 + kTile * 4;
 }
@@ -115,7 +126,7 @@ __device__ __forceinline__ void stage_features(const typename C::in_t* __restric
 #pragma unroll
       for (int e = 0; e < C::E; ++e) x[e] = 0;
     }
-    typename C::op_t* f = F + t * C::FLD + part * C::E;
+    typename C::op_t* f = F + C::frow(t) + part * C::E;
     if constexpr (C::kBF) {
       bf16x8 hi, lo;
 #pragma unroll
@@ -127,8 +138,8 @@ __device__ __forceinline__ void stage_features(const typename C::in_t* __restric
         lo[e] = l;
       }
       st16(f, hi);
-      st16(f + kTile * C::FLD, lo);
-      st16(f + 2 * kTile * C::FLD, x);
+      st16(f + C::FAS, lo);
+      st16(f + 2 * C::FAS, x);
     } else {
       st16(f, x);
     }
@@ -182,7 +193,7 @@ struct FeatureTile {
       const int i = threadIdx.x + j * kThreads;
       if (i < CH) {
         const int t = i / CPR, part = i - t * CPR;
-        typename C::op_t* f = F + t * C::FLD + part * C::E;
+        typename C::op_t* f = F + C::frow(t) + part * C::E;
         if constexpr (C::kBF) {
           bf16x8 hi, lo;
 #pragma unroll
@@ -194,8 +205,8 @@ struct FeatureTile {
             lo[e] = ll;
           }
           st16(f, hi);
-          st16(f + kTile * C::FLD, lo);
-          st16(f + 2 * kTile * C::FLD, r[j]);
+          st16(f + C::FAS, lo);
+          st16(f + 2 * C::FAS, r[j]);
         } else {
           st16(f, r[j]);
         }
@@ -205,7 +216,8 @@ struct FeatureTile {
       constexpr int PADCH = (C::DRP - C::DR) / C::E;
       for (int i = threadIdx.x; i < C::NF * kTile * PADCH; i += kThreads) {
         const int row = i / PADCH, pc = i - row * PADCH;
-        st16(F + row * C::FLD + C::DR + pc * C::E, chunk_t{});
+        const int arr = row / kTile, t = row - arr * kTile;
+        st16(F + arr * C::FAS + C::frow(t) + C::DR + pc * C::E, chunk_t{});
       }
     }
   }
@@ -225,11 +237,11 @@ __device__ __forceinline__ void score_tiles(const typename C::op_t* F, int gt0,
 #pragma unroll
     for (int tt = 0; tt < C::TTW; ++tt) {
       const int tok = tile_token(gt0 + tt, r);
-      const typename C::op_t* f = F + tok * C::FLD + s * C::CS + g * C::E;
+      const typename C::op_t* f = F + C::frow(tok) + s * C::CS + g * C::E;
       if constexpr (C::kBF) {
         const chunk_t f0 = ld16<chunk_t>(f);
-        const chunk_t f1 = ld16<chunk_t>(f + kTile * C::FLD);
-        const chunk_t f2 = ld16<chunk_t>(f + 2 * kTile * C::FLD);
+        const chunk_t f1 = ld16<chunk_t>(f + C::FAS);
+        const chunk_t f2 = ld16<chunk_t>(f + 2 * C::FAS);
 #pragma unroll
         for (int ct = 0; ct < C::CPW; ++ct) {
           f32x4 acc = S[tt][ct];
@@ -288,7 +300,7 @@ __global__ void __launch_bounds__(kThreads) gma_write_kernel(BidirArgs a) {
   using in_t = typename C::in_t;
   using op_t = typename C::op_t;
   using chunk_t = typename C::chunk_t;
-  __shared__ __attribute__((aligned(16))) op_t F[C::NF * kTile * C::FLD];
+  __shared__ __attribute__((aligned(16))) op_t F[C::NF * C::FAS];
   __shared__ __attribute__((aligned(16))) in_t Vt[C::DV * C::VLD];
   __shared__ __attribute__((aligned(16))) f32x4 stats[C::NG * kTile];
   __shared__ __attribute__((aligned(16))) float fac[C::NG * kTile];
@@ -304,7 +316,7 @@ __global__ void __launch_bounds__(kThreads) gma_write_kernel(BidirArgs a) {
   const int64_t t_end = min(a.N, t_begin + (int64_t)a.tiles_per_split * kTile);
   const bool want_assign = a.assign != nullptr;
 
-  for (int i = threadIdx.x; i < C::NF * kTile * C::FLD; i += kThreads) F[i] = (op_t)0;
+  for (int i = threadIdx.x; i < C::NF * C::FAS; i += kThreads) F[i] = (op_t)0;
 
   const char* pbase = a.params + (size_t)h * a.head_bytes;
   chunk_t W[C::CPW][C::NKS][C::NARR];
@@ -545,8 +557,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C
   constexpr int DW = CT >= 4 ? C::DVT : (C::DVT * CT + 3) / 4; // output d tiles per wave
   constexpr int GRLD = C::Kp + 16;                            // Gamma row stride (bf16)
   constexpr int VROWCH = C::DV / 8;                           // 16-byte chunks per V row
-  constexpr int FE = 3 * kTile * C::FLD;
-  constexpr int UE = FE > kTile * GRLD ? FE : kTile * GRLD;
+  constexpr int FE = 3 * C::FAS;
+  constexpr int GE = kTile * GRLD + 12;
+  constexpr int UE = FE > GE ? FE : GE;
   constexpr int VCH = kTile * VROWCH;                         // 16-byte chunks of a V tile
   static_assert(VCH % 64 == 0, "V tile fills whole wave loads");
   constexpr int VROUNDS = VCH / 64;                           // wave-wide 1 KB loads per tile
@@ -729,7 +742,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C
           zl[ct][i] += gm;
           v4[i] = to_bf16(gm);
         }
-        *reinterpret_cast<bf16x4*>(&G[tok * GRLD + (cgi * C::CPW + ct) * 16 + 4 * g]) = v4;
+        *reinterpret_cast<bf16x4*>(&G[gtr_row(tok, GRLD) + (cgi * C::CPW + ct) * 16 + 4 * g]) = v4;
       }
     }
     lds_barrier();
@@ -739,7 +752,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C
     for (int p = 0; p < 2; ++p) {
       bf16x8 A[CTW];
 #pragma unroll
-      for (int i = 0; i < CTW; ++i) A[i] = tr_chunk(G, GRLD, 32 * p, (oct0 + i) * 16);
+      for (int i = 0; i < CTW; ++i) A[i] = tr_chunk_g(G, GRLD, 32 * p, (oct0 + i) * 16);
 #pragma unroll
       for (int j = 0; j < DW; ++j) {
         const int dt = CT >= 4 ? j : wave / CT + (4 / CT) * j;
