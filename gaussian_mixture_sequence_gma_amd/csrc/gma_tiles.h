@@ -49,7 +49,7 @@ struct Cfg {
   static constexpr int DPW = DVT >= NG ? DVT / NG : 1;
   static constexpr int TPW = DVT >= NG ? TTW : TTW * DVT / NG;
   // 2 waves/SIMD where the compiler fits the kernel in 256 VGPRs without spills
-  static constexpr int kWPEWrite = ((DV == 128 || DR == 128) && NG >= 2) ? 1 : 2;
+  static constexpr int kWPEWrite = (NG == 4 || ((DV == 128 || DR == 128) && NG >= 2)) ? 1 : 2;
   static constexpr int kWPERead = (DR == 128 || (!BF && NG == 4 && DV == 128)) ? 1 : 2;
 };
 
@@ -541,127 +541,212 @@ __global__ void __launch_bounds__(kThreads) gma_write_kernel(BidirArgs a) {
 
 
 // ============================================================================
-// Latent write, bf16 inputs.  Scores are computed in the D[component][token]
-// layout (per-token statistics stay inside a lane plus two cross-group steps),
-// Gamma^K goes to LDS row-major [token][component] and both operands of
-// V~ += Gamma^T V are read with transpose reads, so V is staged with plain
-// 16-byte row copies.  Wave w accumulates its own (component, d_v) output tiles
-// over all 64 tokens of each tile; the next tile's K and V are prefetched into
-// registers while the current one is processed.  One partial per workgroup.
+// Latent write, bf16 inputs, software-pipelined over 64-token tiles.
+//
+// Scores use the D[component][token] layout (per-token statistics stay inside
+// a lane plus two cross-group steps).  Gamma^K goes to LDS row-major
+// [token][component] and both operands of V~ += Gamma^T V (and Z += Gamma^T 1,
+// also on MFMA) are read with transpose reads; V tiles are copied HBM -> LDS by
+// direct loads into a swizzled double buffer.  Iteration k runs the statistics,
+// Gamma and latent-write MMA of tile k while the score MFMAs of tile k+1 are
+// issued in the same basic blocks, so MFMA work overlaps the VALU / LDS phases
+// and the barriers.  Wave w accumulates its own (component, d_v) output tiles
+// over all tokens of the split; one partial per workgroup.
 // ============================================================================
+template <class C, int TT0, int TT1>
+__device__ __forceinline__ void score_range_T(const bf16* const (&fb)[C::TTW],
+                                              const bf16x8 (&W)[C::CPW][C::NKS][4],
+                                              f32x4 (&S)[C::TTW][C::CPW]) {
+  // all feature reads of the range first, then the MFMAs ordered so that
+  // consecutive instructions update independent accumulators
+  constexpr int NT = TT1 - TT0;
+  if constexpr (NT > 0) {
+    bf16x8 f[C::NKS][NT][3];
+#pragma unroll
+    for (int s = 0; s < C::NKS; ++s)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const bf16* fp = fb[TT0 + t] + s * C::CS;
+        f[s][t][0] = ld16<bf16x8>(fp);
+        f[s][t][1] = ld16<bf16x8>(fp + C::FAS);
+        f[s][t][2] = ld16<bf16x8>(fp + 2 * C::FAS);
+      }
+    constexpr int WI[5] = {0, 0, 1, 2, 3};   // A_hi, A_hi, A_lo, B_hi, B_lo
+    constexpr int FI[5] = {0, 1, 0, 2, 2};   // x^2_hi, x^2_lo, x^2_hi, x, x
+#pragma unroll
+    for (int s = 0; s < C::NKS; ++s)
+#pragma unroll
+      for (int q = 0; q < 5; ++q)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int ct = 0; ct < C::CPW; ++ct)
+            S[TT0 + t][ct] = mma(W[ct][s][WI[q]], f[s][t][FI[q]], S[TT0 + t][ct]);
+  }
+}
+
 template <class C>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C::kWPEWrite))) gma_write_bf16_kernel(BidirArgs a) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C::kWPEWrite)))
+gma_write_bf16_kernel(BidirArgs a) {
   static_assert(C::kBF, "bf16 kernel");
+  constexpr int TTW = C::TTW;
   constexpr int CT = C::CPW * C::NG;
-  constexpr int CTW = CT >= 4 ? CT / 4 : 1;                  // output component tiles per wave
-  constexpr int DW = CT >= 4 ? C::DVT : (C::DVT * CT + 3) / 4; // output d tiles per wave
-  constexpr int GRLD = C::Kp + 16;                            // Gamma row stride (bf16)
-  constexpr int VROWCH = C::DV / 8;                           // 16-byte chunks per V row
-  constexpr int FE = 3 * C::FAS;
-  constexpr int GE = kTile * GRLD + 12;
-  constexpr int UE = FE > GE ? FE : GE;
-  constexpr int VCH = kTile * VROWCH;                         // 16-byte chunks of a V tile
-  static_assert(VCH % 64 == 0, "V tile fills whole wave loads");
-  constexpr int VROUNDS = VCH / 64;                           // wave-wide 1 KB loads per tile
-  // staged features (dead after the scores) share storage with Gamma
-  __shared__ __attribute__((aligned(16))) bf16 U[UE];
-  __shared__ __attribute__((aligned(16))) bf16 Vr[2][kTile * C::DV];   // double buffer, swizzled
+  constexpr int CTW = CT >= 4 ? CT / 4 : 1;                    // output component tiles per wave
+  constexpr int DW = CT >= 4 ? C::DVT : (C::DVT * CT + 3) / 4;  // output d tiles per wave
+  constexpr int GRLD = C::Kp + 16;                              // Gamma row stride (16 mod 32)
+  constexpr int VROWCH = C::DV / 8;                             // 16-byte chunks per V row
+  constexpr int VROUNDS = kTile * VROWCH / 64;                  // 1 KB wave loads per V tile
+  constexpr int VRPW = (VROUNDS + kWaves - 1) / kWaves;
+  constexpr int P1 = (TTW + 1) / 2;                             // next-tile score split over phases
+  constexpr int P2 = P1 + (TTW - P1 + 1) / 2;
+  __shared__ __attribute__((aligned(16))) bf16 F[3 * C::FAS];
+  __shared__ __attribute__((aligned(16))) bf16 G[kTile * GRLD + 16];
+  __shared__ __attribute__((aligned(16))) bf16 Vr[2][kTile * C::DV];
   __shared__ __attribute__((aligned(16))) f32x4 stats[C::NG * kTile];
   __shared__ __attribute__((aligned(16))) float fac[C::NG * kTile];
-  __shared__ __attribute__((aligned(16))) float zred[C::TG * C::Kp];
-  bf16* const F = U;
-  bf16* const G = U;
+  __shared__ __attribute__((aligned(16))) float cl[C::Kp];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int cgi = wave % C::NG, tg = wave / C::NG;
-  const int gt0 = tg * C::TTW;
+  const int gt0 = tg * TTW;
   const int64_t bh = blockIdx.y;
   const int h = (int)(bh % a.H);
-  const int split = blockIdx.x;
-  const int64_t t_begin = (int64_t)split * a.tiles_per_split * kTile;
+  const int64_t t_begin = (int64_t)blockIdx.x * a.tiles_per_split * kTile;
   const int64_t t_end = a.N < t_begin + (int64_t)a.tiles_per_split * kTile
                             ? a.N : t_begin + (int64_t)a.tiles_per_split * kTile;
+  const int ntiles = t_end > t_begin ? (int)((t_end - t_begin + kTile - 1) / kTile) : 0;
   const bool want_assign = a.assign != nullptr;
+  const bool wave_valid = cgi * C::CPW * 16 < a.K;   // some real component in this group
 
   const char* pbase = a.params + (size_t)h * a.head_bytes;
   bf16x8 W[C::CPW][C::NKS][4];
   load_w<C>(pbase, cgi * C::CPW, W);
-  const float* cvec = reinterpret_cast<const float*>(pbase + (size_t)8 * C::Kp * C::DRP);
-  __shared__ __attribute__((aligned(16))) float cl[C::Kp];   // score seeds, re-read per tile
-  for (int k = threadIdx.x; k < C::Kp; k += kThreads) cl[k] = cvec[k];
+  {
+    const float* cvec = reinterpret_cast<const float*>(pbase + (size_t)8 * C::Kp * C::DRP);
+    for (int k = threadIdx.x; k < C::Kp; k += kThreads) cl[k] = cvec[k];
+  }
 
-  // output tiles of this wave
+  // lane-constant LDS offsets
+  const bf16* fb[TTW];
+  int gw[TTW];
+#pragma unroll
+  for (int tt = 0; tt < TTW; ++tt) {
+    const int tok = tile_token(gt0 + tt, c);
+    fb[tt] = F + C::frow(tok) + g * 8;
+    gw[tt] = gtr_row(tok, GRLD) + cgi * C::CPW * 16 + 4 * g;
+  }
+  const int s4 = lane & 15, a4 = s4 & 3, m4 = s4 >> 2;
+  const int g_lo = gtr_row(8 * g + m4, GRLD) + 4 * a4;         // rows +4 share the skew
+  const int v_lo = (8 * g + m4) * C::DV + 4 * a4;
+  const int h_lo = (8 * g + m4) & (VROWCH / 2 - 1);
+  const int h_hi = (8 * g + m4 + 4) & (VROWCH / 2 - 1);
   const int oct0 = CT >= 4 ? wave * CTW : wave % CT;
-  f32x4 vacc[CTW][DW];
+  // this wave's direct-load slots of a V tile (row, chunk within the swizzled tile)
+  int vrow[VRPW], voff[VRPW];
 #pragma unroll
-  for (int i = 0; i < CTW; ++i)
-#pragma unroll
-    for (int j = 0; j < DW; ++j) vacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float zl[C::CPW][4];
-#pragma unroll
-  for (int ct = 0; ct < C::CPW; ++ct)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) zl[ct][i] = 0.f;
-
+  for (int j = 0; j < VRPW; ++j) {
+    const int round = wave * VRPW + j;
+    const int P = round * 64 + lane;
+    const int r = P / VROWCH, pc = P - r * VROWCH;
+    vrow[j] = r;
+    voff[j] = (pc ^ (r & (VROWCH / 2 - 1)) * 2) * 8;
+  }
   const bf16* xs = reinterpret_cast<const bf16*>(a.x) + (size_t)bh * a.N * C::DR;
   const bf16* vs = reinterpret_cast<const bf16*>(a.v) + (size_t)bh * a.N * C::DV;
-  FeatureTile<C> kreg;
-  // V tile -> Vr[buf] by direct loads; rows past the valid range repeat the last
-  // valid row (their responsibilities are zero, and the loads stay in bounds)
-  auto load_v = [&](int64_t tile0, int buf) {
-    const int nv = (int)(t_end - tile0 < kTile ? t_end - tile0 : kTile);
+  auto tile_start = [&](int k) { return t_begin + (int64_t)k * kTile; };
+  auto tile_valid = [&](int k) {
+    const int64_t r = t_end - tile_start(k);
+    return (int)(r < kTile ? r : kTile);
+  };
+  auto load_v = [&](int k, int buf) {
+    const int64_t t0 = tile_start(k);
+    const int nv = tile_valid(k);
 #pragma unroll
-    for (int j = 0; j < VROUNDS; j += kWaves) {
-      const int round = j + wave;
+    for (int j = 0; j < VRPW; ++j) {
+      const int round = wave * VRPW + j;
       if (round < VROUNDS) {
-        const int P = round * 64 + lane;                      // physical chunk
-        const int r = P / VROWCH, pc = P - r * VROWCH;
-        const int lc = pc ^ ((2 * r) & (VROWCH >= 2 ? VROWCH - 2 : 0));
-        const int rr = r < nv ? r : nv - 1;
-        global_to_lds16(vs + (size_t)(tile0 + rr) * C::DV + lc * 8, &Vr[buf][round * 64 * 8]);
+        const int rr = vrow[j] < nv ? vrow[j] : nv - 1;     // tail rows repeat a valid row
+        global_to_lds16(vs + (size_t)(t0 + rr) * C::DV + voff[j], &Vr[buf][round * 512]);
       }
     }
   };
-  if (t_begin < t_end) {
-    kreg.load(xs, t_begin, (int)(t_end - t_begin < kTile ? t_end - t_begin : kTile));
-    load_v(t_begin, 0);
+
+  f32x4 vacc[CTW][DW], vz[CTW];
+#pragma unroll
+  for (int i = 0; i < CTW; ++i) {
+    vz[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < DW; ++j) vacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  int buf = 0;
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (bf16)1.0f;
 
-  for (int64_t tile0 = t_begin; tile0 < t_end; tile0 += kTile) {
-    const int nvalid = (int)(t_end - tile0 < kTile ? t_end - tile0 : kTile);
-    lds_barrier();
-    // ---- stage features (x^2 hi, x^2 lo, x; pad columns re-zeroed since Gamma
-    // overlays them); this tile's V rows were loaded into Vr[buf] directly --------
+  f32x4 S[TTW][C::CPW], Sn[TTW][C::CPW];
+  auto seed = [&](f32x4 (&X)[TTW][C::CPW]) {
+#pragma unroll
+    for (int tt = 0; tt < TTW; ++tt)
+#pragma unroll
+      for (int ct = 0; ct < C::CPW; ++ct) X[tt][ct] = ld16<f32x4>(&cl[(cgi * C::CPW + ct) * 16 + 4 * g]);
+  };
+
+  FeatureTile<C> kreg;
+  if (ntiles > 0) {
+    kreg.load(xs, tile_start(0), tile_valid(0));
+    load_v(0, 0);
+    lds_barrier();                       // cl visible
     kreg.store(F);
-    wait_global_loads();
     lds_barrier();
-    if (tile0 + kTile < t_end) {
-      const int64_t nt = tile0 + kTile;
-      kreg.load(xs, nt, (int)(t_end - nt < kTile ? t_end - nt : kTile));
-      load_v(nt, buf ^ 1);
-    }
+    seed(S);
+    score_range_T<C, 0, TTW>(fb, W, S);
+    if (ntiles > 1) kreg.load(xs, tile_start(1), tile_valid(1));
+    lds_barrier();                       // every wave done with the features of tile 0
+    if (ntiles > 1) kreg.store(F);
+    if (ntiles > 2) kreg.load(xs, tile_start(2), tile_valid(2));
+    lds_barrier();
+  }
 
-    // ---- scores D[component][token] and per-token statistics --------------------
-    f32x4 S[C::TTW][C::CPW];
+  for (int k = 0; k < ntiles; ++k) {
+    const bool has_next = k + 1 < ntiles;
+    const int64_t tile0 = tile_start(k);
+    const int nvalid = tile_valid(k);
+    const int buf = k & 1;
+
+    // ---- phase 1: next-tile scores (part) || statistics of tile k ----------------
+    // (branch-free so the scheduler can interleave the two streams; the scores of
+    // a tile past the end are computed from stale features and never used)
+    seed(Sn);
+    score_range_T<C, 0, P1>(fb, W, Sn);
+    float m[TTW], l[TTW];
 #pragma unroll
-    for (int tt = 0; tt < C::TTW; ++tt)
-#pragma unroll
-      for (int ct = 0; ct < C::CPW; ++ct) S[tt][ct] = ld16<f32x4>(&cl[(cgi * C::CPW + ct) * 16 + 4 * g]);
-    score_tiles<C, true>(F, gt0, W, S);
-    float m[C::TTW], l[C::TTW];
-    int am[C::TTW];
-#pragma unroll
-    for (int tt = 0; tt < C::TTW; ++tt) {
+    for (int tt = 0; tt < TTW; ++tt) {
       float v = S[tt][0][0];
 #pragma unroll
       for (int ct = 0; ct < C::CPW; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i) v = fmaxf(v, S[tt][ct][i]);
-      m[tt] = groups_max(v);
-      am[tt] = 0;
-      if (want_assign) {
+      v = groups_max(v);
+      m[tt] = wave_valid ? v : -INFINITY;
+      const float mref = wave_valid ? v : 0.f;      // all-padding group: every e is 0
+      float sum = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < C::CPW; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = exp2_fast(S[tt][ct][i] - mref);
+          S[tt][ct][i] = e;
+          sum += e;
+        }
+      l[tt] = groups_sum(sum);
+    }
+    int am[TTW];
+#pragma unroll
+    for (int tt = 0; tt < TTW; ++tt) am[tt] = 0;
+    if (want_assign) {
+      // exp2 is monotone, so the largest e is the largest score (ties: lowest index)
+#pragma unroll
+      for (int tt = 0; tt < TTW; ++tt) {
         float bv = S[tt][0][0];
         int bi = (cgi * C::CPW) * 16 + 4 * g;
 #pragma unroll
@@ -672,106 +757,107 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C
         groups_argmax(bv, bi);
         am[tt] = bi;
       }
-      const float mu_ = m[tt] == -INFINITY ? 0.f : m[tt];
-      float sum = 0.f;
-#pragma unroll
-      for (int ct = 0; ct < C::CPW; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = exp2_fast(S[tt][ct][i] - mu_);
-          S[tt][ct][i] = e;
-          sum += e;
-        }
-      l[tt] = groups_sum(sum);
     }
-    float f[C::TTW];
-    if constexpr (C::NG > 1) {
-      if (g == 0) {
+    if (C::NG > 1 && g == 0) {
 #pragma unroll
-        for (int tt = 0; tt < C::TTW; ++tt)
-          stats[cgi * kTile + tile_token(gt0 + tt, c)] = f32x4{m[tt], l[tt], 0.f, __int_as_float(am[tt])};
+      for (int tt = 0; tt < TTW; ++tt)
+        stats[cgi * kTile + tile_token(gt0 + tt, c)] = f32x4{m[tt], l[tt], 0.f, __int_as_float(am[tt])};
+    }
+    lds_barrier();
+
+    // ---- phase 2: next-tile scores (part) || combine the component groups -------
+    score_range_T<C, P1, P2>(fb, W, Sn);
+    if (C::NG > 1 && threadIdx.x < kTile) {
+      const int t = threadIdx.x;
+      f32x4 st[C::NG];
+      float M = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < C::NG; ++q) {
+        st[q] = stats[q * kTile + t];
+        M = fmaxf(M, st[q][0]);
       }
-      lds_barrier();
-      if (threadIdx.x < kTile) {
-        const int t = threadIdx.x;
-        f32x4 st[C::NG];
-        float M = -INFINITY;
+      float L = 0.f, fq[C::NG];
+      int arg = 0;
+      bool found = false;
 #pragma unroll
-        for (int q = 0; q < C::NG; ++q) {
-          st[q] = stats[q * kTile + t];
-          M = fmaxf(M, st[q][0]);
-        }
-        float L = 0.f, fq[C::NG];
-        int arg = 0;
-        bool found = false;
-#pragma unroll
-        for (int q = 0; q < C::NG; ++q) {
-          fq[q] = st[q][0] == -INFINITY ? 0.f : exp2_fast(st[q][0] - M);
-          L += fq[q] * st[q][1];
-          if (!found && st[q][0] == M) { arg = __float_as_int(st[q][3]); found = true; }
-        }
-        const float invL = 1.f / L;
-#pragma unroll
-        for (int q = 0; q < C::NG; ++q) fac[q * kTile + t] = fq[q] * invL;
-        if (want_assign && t < nvalid) a.assign[(size_t)bh * a.N + tile0 + t] = arg;
+      for (int q = 0; q < C::NG; ++q) {
+        fq[q] = st[q][0] == -INFINITY ? 0.f : exp2_fast(st[q][0] - M);
+        L += fq[q] * st[q][1];
+        if (!found && st[q][0] == M) { arg = __float_as_int(st[q][3]); found = true; }
       }
-      lds_barrier();
+      const float invL = 1.f / L;
 #pragma unroll
-      for (int tt = 0; tt < C::TTW; ++tt) f[tt] = fac[cgi * kTile + tile_token(gt0 + tt, c)];
-    } else {
+      for (int q = 0; q < C::NG; ++q) fac[q * kTile + t] = fq[q] * invL;
+      if (want_assign && t < nvalid) a.assign[(size_t)bh * a.N + tile0 + t] = arg;
+    }
+    lds_barrier();
+
+    // ---- phase 3: next-tile scores (rest) || Gamma (masked) -> LDS ----------------
+    score_range_T<C, P2, TTW>(fb, W, Sn);
 #pragma unroll
-      for (int tt = 0; tt < C::TTW; ++tt) {
-        f[tt] = 1.f / l[tt];
-        const int tok = tile_token(gt0 + tt, c);
+    for (int tt = 0; tt < TTW; ++tt) {
+      const int tok = tile_token(gt0 + tt, c);
+      float fi;
+      if constexpr (C::NG > 1) fi = fac[cgi * kTile + tok];
+      else {
+        fi = 1.f / l[tt];
         if (want_assign && g == 0 && tok < nvalid) a.assign[(size_t)bh * a.N + tile0 + tok] = am[tt];
       }
-      lds_barrier();   // every wave is past its feature reads before Gamma overwrites them
-    }
-
-    // ---- Gamma (masked to valid tokens) -> LDS [token][component]; Z partials ----
-#pragma unroll
-    for (int tt = 0; tt < C::TTW; ++tt) {
-      const int tok = tile_token(gt0 + tt, c);
-      const float fi = tok < nvalid ? f[tt] : 0.f;
+      fi = tok < nvalid ? fi : 0.f;
 #pragma unroll
       for (int ct = 0; ct < C::CPW; ++ct) {
         bf16x4 v4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float gm = S[tt][ct][i] * fi;
-          zl[ct][i] += gm;
-          v4[i] = to_bf16(gm);
-        }
-        *reinterpret_cast<bf16x4*>(&G[gtr_row(tok, GRLD) + (cgi * C::CPW + ct) * 16 + 4 * g]) = v4;
+        for (int i = 0; i < 4; ++i) v4[i] = to_bf16(S[tt][ct][i] * fi);
+        *reinterpret_cast<bf16x4*>(&G[gw[tt] + ct * 16]) = v4;
       }
     }
+    wait_global_loads();                 // V(k) and the routing vectors of tile k+2
     lds_barrier();
 
-    // ---- V~ += Gamma^T V over the 64 tokens -----------------------------------
+    // ---- phase 4: V~ += Gamma^T V, Z += Gamma^T 1 || stage tile k+2, fetch ahead ---
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       bf16x8 A[CTW];
 #pragma unroll
-      for (int i = 0; i < CTW; ++i) A[i] = tr_chunk_g(G, GRLD, 32 * p, (oct0 + i) * 16);
+      for (int i = 0; i < CTW; ++i) {
+        const bf16* gp = G + g_lo + 32 * p * GRLD + (oct0 + i) * 16;
+        const short4_t lo = lds_read_tr16(gp);
+        const short4_t hi = lds_read_tr16(gp + 4 * GRLD);
+        typedef short short8_t __attribute__((ext_vector_type(8)));
+        A[i] = __builtin_bit_cast(bf16x8, short8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        vz[i] = mma(A[i], ones, vz[i]);
+      }
 #pragma unroll
       for (int j = 0; j < DW; ++j) {
         const int dt = CT >= 4 ? j : wave / CT + (4 / CT) * j;
         if (dt < C::DVT) {
-          const bf16x8 Bv = tr_chunk_swz<VROWCH>(Vr[buf], 32 * p, dt * 16);
+          const bf16* vp = Vr[buf] + 32 * p * C::DV;
+          const short4_t lo = lds_read_tr16(vp + v_lo + 16 * (dt ^ h_lo));
+          const short4_t hi = lds_read_tr16(vp + v_lo + 4 * C::DV + 16 * (dt ^ h_hi));
+          typedef short short8_t __attribute__((ext_vector_type(8)));
+          const bf16x8 Bv = __builtin_bit_cast(bf16x8, short8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 #pragma unroll
           for (int i = 0; i < CTW; ++i) vacc[i][j] = mma(A[i], Bv, vacc[i][j]);
         }
       }
     }
-    buf ^= 1;
+    if (k + 2 < ntiles) kreg.store(F);
+    if (k + 3 < ntiles) kreg.load(xs, tile_start(k + 3), tile_valid(k + 3));
+    if (has_next) load_v(k + 1, buf ^ 1);
+#pragma unroll
+    for (int tt = 0; tt < TTW; ++tt)
+#pragma unroll
+      for (int ct = 0; ct < C::CPW; ++ct) S[tt][ct] = Sn[tt][ct];
+    lds_barrier();
   }
 
-  // ---- partial (V~, Z) of this workgroup --------------------------------------
-  const size_t pslot = (size_t)bh * a.S + split;
+  // ---- partial (V~, Z) of this workgroup ------------------------------------------
+  const size_t pslot = (size_t)bh * a.S + blockIdx.x;
   float* pv = a.partial + pslot * C::Kp * C::DV;
   float* pz = a.partial_z + pslot * C::Kp;
 #pragma unroll
-  for (int i = 0; i < CTW; ++i)
+  for (int i = 0; i < CTW; ++i) {
 #pragma unroll
     for (int j = 0; j < DW; ++j) {
       const int dt = CT >= 4 ? j : wave / CT + (4 / CT) * j;
@@ -781,20 +867,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C
           pv[((oct0 + i) * 16 + 4 * g + r) * C::DV + dt * 16 + c] = vacc[i][j][r];
       }
     }
-  // Z: lanes hold per-token partials; sum the 16 lanes of a row, then token groups
+    // every column of Gamma^T 1 holds Z; waves sharing a component tile write once
+    if (c == 0 && (CT >= 4 || wave / CT == 0)) {
 #pragma unroll
-  for (int ct = 0; ct < C::CPW; ++ct)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float zt = row16_sum(zl[ct][i]);
-      if (c == 0) zred[tg * C::Kp + (cgi * C::CPW + ct) * 16 + 4 * g + i] = zt;
+      for (int r = 0; r < 4; ++r) pz[(oct0 + i) * 16 + 4 * g + r] = vz[i][r];
     }
-  lds_barrier();
-  for (int k = threadIdx.x; k < C::Kp; k += kThreads) {
-    float zt = 0.f;
-#pragma unroll
-    for (int q = 0; q < C::TG; ++q) zt += zred[q * C::Kp + k];
-    pz[k] = zt;
   }
 }
 
