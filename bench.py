@@ -7,10 +7,11 @@ inputs already resident in HBM.  Default workload: the long-context
 bidirectional case (B1 H32 N32768 d_r64 d_v128 K128, bf16 inputs, skewed
 parameters).  Prints one JSON line.
 
-Roofline: the dominant kernel's algorithmic bytes per launch divided by its
-average duration, measured with hipEvents the library records around each of
-its launches on the launch stream during the timed region, against MI355X's
-8 TB/s HBM peak.  cpu_baseline: the fp64 oracle on a bounded sample of the
+Roofline: the dominant kernel's algorithmic bytes (flops, for the MFMA-bound
+projection GEMM of the layer workload) per launch divided by its average
+duration, measured with hipEvents the library records around each of its
+launches on the launch stream during the timed region, against MI355X's 8 TB/s
+HBM peak (2.5 PFLOP/s dense bf16 MFMA).  cpu_baseline: the fp64 oracle on a bounded sample of the
 same workload on this host's cores.
 """
 from __future__ import annotations
@@ -30,9 +31,24 @@ UNIT = "tokens·heads/s"
 HBM_PEAK_GBS = 8000.0
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def kernel_flops(name: str, w) -> int:
+    """Algorithmic flops of one launch of an MFMA-bound kernel (0 for others):
+    the three projections X W_Q, X W_K, X W_V of the layer workload."""
+    if name == "gma_proj":
+        return 2 * w.B * w.N * w.d_model * w.H * (2 * w.d_r + w.d_v)
+    return 0
+
+
 def kernel_bytes(name: str, w, s_in: int, s_out: int) -> int:
-    """Algorithmic HBM bytes of one launch of `name` on workload w."""
+    """Algorithmic HBM bytes of one launch of `name` on workload w (s_in: element
+    size of the routing vectors and values the GMA kernels read)."""
     T = w.B * w.H * w.N
+    if name == "gma_proj":
+        return 2 * (w.B * w.N * w.d_model + w.d_model * w.H * (2 * w.d_r + w.d_v)) + \
+            4 * T * (2 * w.d_r + w.d_v)
     if name == "gma_write":
         return T * (w.d_r + w.d_v) * s_in
     if name == "gma_read":
@@ -66,23 +82,49 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def cpu_baseline(w, gen, max_threads: int = 16):
-    import numpy as np
+def cpu_baseline(w, gen, max_threads: int = 16, min_seconds: float = 10.0,
+                 max_seconds: float = 30.0):
+    """The fp64 oracle on this host: groups of 2*threads heads at full N (projection
+    included for the layer workload), taken in order over (batch, head) and
+    cycling, until min_seconds have passed (a group started later than
+    max_seconds - last group's time is skipped)."""
     import oracle
     threads = max(1, min(max_threads, os.cpu_count() or 1))
-    heads = min(w.H, 2 * threads)
-    sl = slice(0, heads)
-    if w.d_model > 0:
-        return None
+    per = min(w.H, 2 * threads)
+    groups = [(b, h0) for b in range(w.B) for h0 in range(0, w.H, per)]
+    done = 0
     t0 = time.perf_counter()
-    oracle.forward(gen["Q"].f32[:1, sl], gen["K"].f32[:1, sl], gen["V"].f32[:1, sl],
-                   gen["mu"][sl], gen["log_sigma2"][sl], gen["log_pi"][sl], w.eps, w.causal,
-                   nthreads=threads)
+    last = 0.0
+    gi = 0
+    while True:
+        b, h0 = groups[gi % len(groups)]
+        h1 = min(w.H, h0 + per)
+        sl = slice(h0, h1)
+        bs = slice(b, b + 1)
+        t1 = time.perf_counter()
+        if w.d_model > 0:
+            oracle.layer_forward(gen["X"].f32[bs], gen["W_Q"].f32[:, h0 * w.d_r:h1 * w.d_r],
+                                 gen["W_K"].f32[:, h0 * w.d_r:h1 * w.d_r],
+                                 gen["W_V"].f32[:, h0 * w.d_v:h1 * w.d_v], h1 - h0,
+                                 gen["mu"][sl], gen["log_sigma2"][sl], gen["log_pi"][sl],
+                                 w.eps, w.causal, nthreads=threads)
+        else:
+            oracle.forward(gen["Q"].f32[bs, sl], gen["K"].f32[bs, sl], gen["V"].f32[bs, sl],
+                           gen["mu"][sl], gen["log_sigma2"][sl], gen["log_pi"][sl], w.eps,
+                           w.causal, nthreads=threads)
+        last = time.perf_counter() - t1
+        done += (h1 - h0) * w.N
+        gi += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or el + last > max_seconds:
+            break
     dt = time.perf_counter() - t0
-    return {"value": heads * w.N / dt, "unit": UNIT, "cores": min(threads, heads),
+    what = "projection + GMA" if w.d_model > 0 else "GMA"
+    return {"value": done / dt, "unit": UNIT, "cores": min(threads, per),
             "kind": "oracle",
-            "sample": "batch 0, heads 0..%d of %d at full N=%d (%s), fp64, %.1f s"
-                      % (heads - 1, w.H, w.N, "causal" if w.causal else "bidirectional", dt)}
+            "sample": "%d groups of up to %d heads at full N=%d (%s %s, fp64), %d token-heads "
+                      "of %d, %.1f s" % (gi, per, w.N, "causal" if w.causal else "bidirectional",
+                                         what, done, w.tokens_heads, dt)}
 
 
 def main():
@@ -128,8 +170,8 @@ def main():
     binding.load()
     dev = torch.device("cuda:0")
     gen = inputs.generate(w, 0)
-    s_in = 2 if w.dtype == "bf16" else 4
-    s_out = s_in
+    s_out = 2 if w.dtype == "bf16" else 4
+    s_in = 4 if w.d_model > 0 else s_out      # the layer's GMA kernels read fp32 projections
 
     if w.d_model > 0:
         X = api.host_tensor_to_device(gen["X"], dev)
@@ -184,11 +226,20 @@ def main():
     kernels = {name: {"launches": n, "avg_us": 1e3 * tot / max(n, 1)} for name, n, tot in kt}
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
     dom_bytes = kernel_bytes(dom, w, s_in, s_out)
-    achieved = dom_bytes / (kernels[dom]["avg_us"] * 1e-6) / 1e9 if dom_bytes else None
+    dom_flops = kernel_flops(dom, w)
     traffic = traffic_from_profile(dom, w.name, kernel_source_hash())
-    roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
-                "traffic": traffic, "alg_bytes_per_launch": dom_bytes}
+    t_dom = kernels[dom]["avg_us"] * 1e-6
+    if dom_flops:
+        achieved = dom_flops / t_dom / 1e12
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved,
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic,
+                    "alg_flops_per_launch": dom_flops, "alg_bytes_per_launch": dom_bytes}
+    else:
+        achieved = dom_bytes / t_dom / 1e9 if dom_bytes else None
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
+                    "traffic": traffic, "alg_bytes_per_launch": dom_bytes}
     step_bytes = sum(kernel_bytes(k, w, s_in, s_out) for k in kernels)
 
     cpu = None

@@ -271,10 +271,9 @@ int gma_layer_forward(const void* X, const void* W_Q, const void* W_K, const voi
   float* k = q + (size_t)p.BH * p.N * p.DR;
   float* v = k + (size_t)p.BH * p.N * p.DR;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t M = p.B * p.N;
-  hipError_t e = launch_proj(X, W_Q, M, d_model, (int)(p.H * p.DR), (int)p.H, p.DR, p.N, q, s);
-  if (e == hipSuccess) e = launch_proj(X, W_K, M, d_model, (int)(p.H * p.DR), (int)p.H, p.DR, p.N, k, s);
-  if (e == hipSuccess) e = launch_proj(X, W_V, M, d_model, (int)(p.H * p.DV), (int)p.H, p.DV, p.N, v, s);
+  const void* const W[3] = {W_Q, W_K, W_V};
+  float* const P[3] = {q, k, v};
+  hipError_t e = launch_proj(X, W, P, p.B, p.N, (int)p.H, d_model, p.DR, p.DV, s);
   st = finish_launch(e, "projection launch");
   if (st != GMA_OK) return st;
   Tensors t;

@@ -57,7 +57,8 @@ hipError_t launch_prologue(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_bidir(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_resp(const Plan& p, const Tensors& t, hipStream_t s);
-hipError_t launch_proj(const void* X, const void* W, int64_t M, int d_model, int ncols,
-                       int H, int dh, int64_t N, float* out, hipStream_t s);
+// Q_X, K_X, V_X = X W_Q, X W_K, X W_V (W[0..2]) into fp32 head-major out[0..2].
+hipError_t launch_proj(const void* X, const void* const W[3], float* const out[3], int64_t B,
+                       int64_t N, int H, int d_model, int d_r, int d_v, hipStream_t s);
 
 }  // namespace gma

@@ -97,8 +97,12 @@ int gma_layer_workspace_bytes(const gma_dims* d, int32_t d_model, int causal, si
  *  W_Q, W_K   [d_model, H*d_r] of d->dtype; head h uses columns [h*d_r, (h+1)*d_r)
  *  W_V        [d_model, H*d_v] of d->dtype; head h uses columns [h*d_v, (h+1)*d_v)
  *  d_model    multiple of 64, 64..8192
- * The projections are kept in fp32 (written to the workspace) and feed the fp32
- * GMA path; out is [B,H,N,d_v] of d->dtype.  Other arguments as gma_forward. */
+ * The projections are accumulated and kept in fp32 (bf16 x bf16 products are
+ * exact in fp32) and feed the fp32 GMA path; out is [B,H,N,d_v] of d->dtype.
+ * They stay in the workspace after the call, as Q_X, K_X, V_X one after the
+ * other in [B,H,N,d] fp32, starting P bytes before the end of the
+ * gma_layer_workspace_bytes figure, P = 4*B*H*N*(2*d_r + d_v) rounded up to a
+ * multiple of 256.  Other arguments as gma_forward. */
 int gma_layer_forward(const void* X, const void* W_Q, const void* W_K, const void* W_V,
                       int32_t d_model, const float* mu, const float* log_sigma2,
                       const float* log_pi, float eps, int causal, void* out,

@@ -1,0 +1,99 @@
+"""GPU parity of the projection layer (Eq. 4 followed by the GMA forward)
+against the fp64 oracle: X W in float64 (numpy matmul), then the plain
+definition of the forward.
+
+The projections themselves are checked where gma_layer_forward leaves them
+(the tail of its workspace, fp32 [B,H,N,d] for Q_X, K_X, V_X).  Their bound:
+bf16 x bf16 products are exact in fp32 and d_model of them are summed in fp32,
+so the error of an element is at most about d_model * 2^-24 * sum_k |x_k w_k|;
+with N(0,1) X and N(0, 1/d_model) W that is far below 1e-5 of the row norm.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gaussian_mixture_sequence_gma_amd import api, binding, inputs
+from tests.parity import TOL, check_assign, rowwise_rel_err, upload
+
+pytestmark = pytest.mark.gpu
+
+W = inputs.WORKLOADS
+PROJ_TOL = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load()
+
+
+def _run(w, seed=0, rows=None, check_proj=True):
+    gen = inputs.generate(w, seed)
+    dev = upload(gen)
+    dims = binding.make_dims(w.B, w.H, w.N, w.d_r, w.d_v, w.K, binding.GMA_BF16)
+    need = binding.gma_layer_workspace_bytes(dims, w.d_model, int(w.causal))
+    ws = api.alloc_workspace(need, "cuda")
+    out, aq, ak = api.layer_forward(dev["X"], dev["W_Q"], dev["W_K"], dev["W_V"], w.H,
+                                    dev["mu"], dev["log_sigma2"], dev["log_pi"], w.eps,
+                                    w.causal, assign=True, workspace=ws)
+    torch.cuda.synchronize()
+    X = gen["X"].f32
+    P = [oracle.project(X, gen[k].f32, w.H) for k in ("W_Q", "W_K", "W_V")]
+    if check_proj:
+        sizes = [w.B * w.H * w.N * d for d in (w.d_r, w.d_r, w.d_v)]
+        pbytes = 4 * sum(sizes)
+        start = need - ((pbytes + 255) // 256) * 256
+        flat = ws[start:start + pbytes].view(torch.float32).cpu().numpy()
+        off = 0
+        for name, ref, n in zip("QKV", P, sizes):
+            got = flat[off:off + n].reshape(ref.shape)
+            off += n
+            err = rowwise_rel_err(got, ref)
+            print("[layer] %s projection row-wise err %.3e" % (name, err), flush=True)
+            assert err <= PROJ_TOL, "%s projection error %.3e" % (name, err)
+    ref = oracle.forward(P[0], P[1], P[2], gen["mu"], gen["log_sigma2"], gen["log_pi"], w.eps,
+                         w.causal, rows=rows, want_assign=True)
+    o = out.float().cpu().numpy()
+    gq, gk = aq.cpu().numpy(), ak.cpu().numpy()
+    Q = P[0]
+    if rows is not None:
+        o, gq, Q = o[:, :, rows], gq[:, :, rows], Q[:, :, rows]
+    err = rowwise_rel_err(o, ref["out"])
+    ties = check_assign(gq, ref["assign_q"], Q, gen, "f32", w.name + " assign_q")
+    ties += check_assign(gk, ref["assign_k"], P[1], gen, "f32", w.name + " assign_k")
+    print("[layer] %s B=%d H=%d N=%d d_model=%d d_r=%d d_v=%d K=%d causal=%d: err %.3e ties %d"
+          % (w.name, w.B, w.H, w.N, w.d_model, w.d_r, w.d_v, w.K, int(w.causal), err, ties),
+          flush=True)
+    assert np.all(np.isfinite(o))
+    assert err <= TOL["bf16"], "layer output error %.3e" % err
+    return err
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_layer_small(causal):
+    w = W["layer_causal_bf16"].with_(B=2, H=4, N=300, d_model=128, causal=causal)
+    _run(w)
+
+
+@pytest.mark.parametrize("d_model", [64, 192, 1024])
+@pytest.mark.parametrize("N", [1, 127, 129, 700])
+def test_layer_ragged(d_model, N):
+    # H*d of 48 and 96 leave a partly filled 128-feature tile; B*N not a
+    # multiple of the 128-token tile, and tiles straddle the batch boundary.
+    w = W["layer_causal_bf16"].with_(B=3, H=3, N=N, d_r=16, d_v=32, K=7,
+                                     d_model=d_model)
+    _run(w)
+
+
+@pytest.mark.parametrize("d_r,d_v", [(16, 128), (128, 16), (32, 64), (128, 128)])
+def test_layer_head_dims(d_r, d_v):
+    w = W["layer_causal_bf16"].with_(B=1, H=5, N=257, d_r=d_r, d_v=d_v, K=20, d_model=256)
+    _run(w)
+
+
+def test_layer_full_size_sampled_rows():
+    # the full layer shape in the launch configuration bench.py times
+    w = W["layer_causal_bf16"]
+    _run(w, rows=inputs.sample_rows(w.N, 256, seed=3))
