@@ -114,14 +114,43 @@ __device__ __forceinline__ int xor_lane_i(int v, int mask) {
   int src = (int)(threadIdx.x & 63) ^ mask;
   return __builtin_amdgcn_ds_bpermute(src << 2, v);
 }
+// Exchanges between the four lane groups g (16-lane rows) without the LDS
+// crossbar: v_permlane16_swap with both operands = v returns, in every lane,
+// the pair {v of the even row, v of the odd row} of its row pair (lanes l and
+// l ^ 16); v_permlane32_swap does the same for the two halves (l and l ^ 32).
+// Either order of the pair gives bitwise the same max / sum in both lanes.
+__device__ __forceinline__ void pair_xor16(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pair_xor32(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pair_xor16_i(int v, int& a, int& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+  a = (int)r[0];
+  b = (int)r[1];
+}
+__device__ __forceinline__ void pair_xor32_i(int v, int& a, int& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+  a = (int)r[0];
+  b = (int)r[1];
+}
 // Reductions over the four lane groups g (lanes l, l^16, l^32, l^48).
 __device__ __forceinline__ float groups_max(float v) {
-  v = fmaxf(v, xor_lane(v, 16));
-  return fmaxf(v, xor_lane(v, 32));
+  float a, b;
+  pair_xor16(v, a, b);
+  pair_xor32(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
 }
 __device__ __forceinline__ float groups_sum(float v) {
-  v += xor_lane(v, 16);
-  return v + xor_lane(v, 32);
+  float a, b;
+  pair_xor16(v, a, b);
+  pair_xor32(a + b, a, b);
+  return a + b;
 }
 
 // (value, index) argmax merge, ties to the lower index.
@@ -137,8 +166,14 @@ __device__ __forceinline__ void row16_argmax(float& v, int& i) {
   argmax_merge(v, i, dpp<0x140>(v), dpp_i<0x140>(i));
 }
 __device__ __forceinline__ void groups_argmax(float& v, int& i) {
-  argmax_merge(v, i, xor_lane(v, 16), xor_lane_i(i, 16));
-  argmax_merge(v, i, xor_lane(v, 32), xor_lane_i(i, 32));
+  float a, b;
+  int ia, ib;
+  pair_xor16(v, a, b);
+  pair_xor16_i(i, ia, ib);
+  argmax_merge(a, ia, b, ib);
+  pair_xor32(a, v, b);
+  pair_xor32_i(ia, i, ib);
+  argmax_merge(v, i, b, ib);
 }
 
 // ---- conversions -----------------------------------------------------------
