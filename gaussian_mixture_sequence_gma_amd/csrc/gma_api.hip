@@ -98,7 +98,9 @@ int make_plan(const gma_dims* d, int causal, bool fp32_compute, Plan& p) {
     p.span_tiles = (int)((p.tiles + want_c - 1) / want_c);
     p.nspan = (int)((p.tiles + p.span_tiles - 1) / p.span_tiles);
   }
-  p.head_bytes = round256((size_t)8 * p.Kp * p.DRP + (size_t)4 * p.Kp);
+  // per head: the coefficient arrays and c, then (bf16) the same values in
+  // MFMA-operand order for the token-owner read-out
+  p.head_bytes = 2 * round256((size_t)8 * p.Kp * p.DRP + (size_t)4 * p.Kp);
   size_t off = 0;
   p.off_params = off;
   off += round256(p.head_bytes * (size_t)p.H);
@@ -112,6 +114,10 @@ int make_plan(const gma_dims* d, int causal, bool fp32_compute, Plan& p) {
     off += round256((size_t)p.BH * p.Kp * p.DV * 4);
     p.off_z = off;
     off += round256((size_t)p.BH * p.Kp * 4);
+    // V~^T and (Z_hi, Z_lo, 1) as bf16 MFMA operands: (d_v/16 + 1) blocks x K_pad/32
+    // steps x 1 KB per sequence
+    p.off_vtab = off;
+    off += round256((size_t)p.BH * (p.DV / 16 + 1) * ((p.Kp + 31) / 32) * 1024);
   } else {
     const size_t ns = (size_t)p.nspan;
     p.off_state = off;

@@ -26,6 +26,17 @@
 
 namespace gma {
 
+// Row r of the t-th 16-row MFMA tile of a 32-row pair block: 32 (t / 2) +
+// 8 (r / 4) + 4 (t % 2) + r % 4.  With it, lane group g (rows 4g .. 4g+3 of a
+// D tile) of tiles 2p and 2p + 1 together holds the eight consecutive indices
+// 32p + 8g .. 32p + 8g + 7.
+__host__ __device__ constexpr int pair_row(int t, int r) {
+  return 32 * (t >> 1) + 8 * (r >> 2) + 4 * (t & 1) + (r & 3);
+}
+// Inverse: index i -> (tile, row).
+__host__ __device__ constexpr int pair_tile(int i) { return 2 * (i >> 5) + ((i & 7) >> 2); }
+__host__ __device__ constexpr int pair_rowof(int i) { return 4 * ((i & 31) >> 3) + (i & 3); }
+
 // ============================================================================
 // Parameter prologue: per head, A, B (bf16 hi/lo pairs or fp32) and c.
 // Layout per head: NARR arrays [Kp][DRP] (A_hi, A_lo, B_hi, B_lo or A, B)
@@ -62,10 +73,18 @@ __global__ void __launch_bounds__(256) gma_prologue_kernel(
     if constexpr (BF) {
       bf16* Ahi = reinterpret_cast<bf16*>(base);
       const bf16 ah = to_bf16((float)a), bh = to_bf16((float)b);
-      Ahi[idx] = ah;
-      Ahi[n + idx] = to_bf16((float)(a - (double)from_bf16(ah)));
-      Ahi[2 * n + idx] = bh;
-      Ahi[3 * n + idx] = to_bf16((float)(b - (double)from_bf16(bh)));
+      const bf16 v4[4] = {ah, to_bf16((float)(a - (double)from_bf16(ah))), bh,
+                          to_bf16((float)(b - (double)from_bf16(bh)))};
+#pragma unroll
+      for (int ar = 0; ar < 4; ++ar) Ahi[ar * n + idx] = v4[ar];
+      if (Kp % 32 == 0) {
+        // operand order: chunk (tile, routing step, array), lane (row, d group), element
+        bf16* T = reinterpret_cast<bf16*>(base + head_bytes / 2);
+        const int ct = pair_tile(k), r = pair_rowof(k), st = d >> 5, gg = (d & 31) >> 3;
+#pragma unroll
+        for (int ar = 0; ar < 4; ++ar)
+          T[((((ct * (DRP / 32) + st) * 4 + ar) * 64) + r + 16 * gg) * 8 + (d & 7)] = v4[ar];
+      }
     } else {
       float* A = reinterpret_cast<float*>(base);
       A[idx] = (float)a;
@@ -79,35 +98,59 @@ __global__ void __launch_bounds__(256) gma_prologue_kernel(
   }
   if (lane == 0) {
     float* c = reinterpret_cast<float*>(base + (size_t)8 * n);
+    float cv = -INFINITY;
     if (k < K) {
       const double ck = (double)lpi[(size_t)h * K + k] - 0.5 * acc + (BF ? 0.0 : asum);
-      c[k] = (float)(kLog2eD * ck);
-    } else {
-      c[k] = -INFINITY;
+      cv = (float)(kLog2eD * ck);
+    }
+    c[k] = cv;
+    if (BF && Kp % 32 == 0) {
+      float* cp = reinterpret_cast<float*>(base + head_bytes / 2 + (size_t)8 * n);
+      cp[pair_tile(k) * 16 + pair_rowof(k)] = cv;
     }
   }
 }
 
 // Sum the partials of each sequence in a fixed order: V~ [BH][Kp][DV], Z [BH][Kp].
+// With vtab (bf16 path, K_pad a multiple of 32) the sums are also written as
+// the read-out's MFMA operand table: block dt (d tile, paired rows as in
+// pair_row when d_v >= 32), step p (32 components), lane (row, component
+// group), element; block d_v/16 holds rows Z_hi, Z_lo, 1 and zeros.
 __global__ void __launch_bounds__(256) gma_reduce_kernel(const float* __restrict__ partial,
                                                          const float* __restrict__ partial_z,
                                                          int PS, int Kp, int DV,
                                                          float* __restrict__ vt,
-                                                         float* __restrict__ z) {
+                                                         float* __restrict__ z,
+                                                         bf16* __restrict__ vtab) {
   const int64_t bh = blockIdx.y;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   const int nv = Kp * DV;
+  const int DVT = DV / 16, KS = Kp / 32;
+  bf16* vb = vtab ? vtab + (size_t)bh * (DVT + 1) * KS * 512 : nullptr;
   if (idx < nv) {
     const float* p = partial + (size_t)bh * PS * nv + idx;
     float s = 0.f;
     for (int q = 0; q < PS; ++q) s += p[(size_t)q * nv];
     vt[(size_t)bh * nv + idx] = s;
+    if (vb) {
+      const int k = idx / DV, d = idx - k * DV;
+      const int t = DVT >= 2 ? pair_tile(d) : 0, r = DVT >= 2 ? pair_rowof(d) : d;
+      vb[((t * KS + (k >> 5)) * 64 + r + 16 * ((k & 31) >> 3)) * 8 + (k & 7)] = to_bf16(s);
+    }
   } else if (idx < nv + Kp) {
     const int k = idx - nv;
     const float* p = partial_z + (size_t)bh * PS * Kp + k;
     float s = 0.f;
     for (int q = 0; q < PS; ++q) s += p[(size_t)q * Kp];
     z[(size_t)bh * Kp + k] = s;
+    if (vb) {
+      const bf16 zh = to_bf16(s);
+      const bf16 zl = to_bf16(s - from_bf16(zh));
+      bf16* col = vb + ((DVT * KS + (k >> 5)) * 64 + 16 * ((k & 31) >> 3)) * 8 + (k & 7);
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        col[r * 8] = r == 0 ? zh : (r == 1 ? zl : (r == 2 ? (bf16)1.0f : (bf16)0.0f));
+    }
   }
 }
 
@@ -124,7 +167,6 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C
   __shared__ __attribute__((aligned(16))) op_t G[MODE == 0 ? C::GAS : 1];
   __shared__ __attribute__((aligned(16))) f32x4 stats[C::NG * kTile];
   __shared__ __attribute__((aligned(16))) float fac[C::NG * kTile];
-  __shared__ __attribute__((aligned(16))) float rinv[kTile];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -173,23 +215,39 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C
   }
 
   const in_t* xs = reinterpret_cast<const in_t*>(a.x) + (size_t)bh * a.N * C::DR;
+  const op_t* fb[C::TTW];
+#pragma unroll
+  for (int tt = 0; tt < C::TTW; ++tt) fb[tt] = F + C::frow(tile_token(gt0 + tt, c)) + g * C::E;
   FeatureTile<C> xreg;
-  if (t_begin < t_end) xreg.load(xs, t_begin, (int)min((int64_t)kTile, t_end - t_begin));
-
-  for (int64_t tile0 = t_begin; tile0 < t_end; tile0 += kTile) {
-    const int nvalid = (int)min((int64_t)kTile, t_end - tile0);
-    lds_barrier();
+  auto tile_n = [&](int64_t t0) { return (int)min((int64_t)kTile, t_end - t0); };
+  if (t_begin < t_end) {
+    xreg.load(xs, t_begin, tile_n(t_begin));
+    lds_barrier();                         // F zero-fill done before the first stage
     xreg.store(F);
+    if (t_begin + kTile < t_end) xreg.load(xs, t_begin + kTile, tile_n(t_begin + kTile));
     lds_barrier();
-    if (tile0 + kTile < t_end)
-      xreg.load(xs, tile0 + kTile, (int)min((int64_t)kTile, t_end - tile0 - kTile));
+  }
+
+  // Per tile three barriers: B1 after the per-group statistics (every wave is
+  // also done reading F), B2 after the combine and the staging of the next
+  // tile's features, B3 after Gamma' is in LDS.
+  for (int64_t tile0 = t_begin; tile0 < t_end; tile0 += kTile) {
+    const int nvalid = tile_n(tile0);
+    const bool has_next = tile0 + kTile < t_end;
 
     f32x4 S[C::TTW][C::CPW];
 #pragma unroll
     for (int tt = 0; tt < C::TTW; ++tt)
 #pragma unroll
       for (int ct = 0; ct < C::CPW; ++ct) S[tt][ct] = score_seed<C>(cv4[ct]);
-    score_tiles<C, true>(F, gt0, W, S);
+    if constexpr (C::kBF) {
+      // MFMA order with independent accumulators back to back, half a tile of
+      // feature operands in flight at a time
+      score_range_T<C, 0, C::TTW / 2>(fb, W, S);
+      score_range_T<C, C::TTW / 2, C::TTW>(fb, W, S);
+    } else {
+      score_tiles<C, true>(F, gt0, W, S);
+    }
 #pragma unroll
     for (int tt = 0; tt < C::TTW; ++tt)
 #pragma unroll
@@ -227,64 +285,64 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C
           const float e = exp2_fast(S[tt][ct][i] - mu_);
           S[tt][ct][i] = e;
           sum += e;
-          den += e * z4[ct][i];
+          if constexpr (MODE == 0) den += e * z4[ct][i];
         }
       l[tt] = groups_sum(sum);
-      dn[tt] = groups_sum(den);
+      dn[tt] = MODE == 0 ? groups_sum(den) : 0.f;
     }
+    if (C::NG > 1 && g == 0) {
+#pragma unroll
+      for (int tt = 0; tt < C::TTW; ++tt)
+        stats[cgi * kTile + tile_token(gt0 + tt, c)] =
+            f32x4{m[tt], l[tt], dn[tt], __int_as_float(am[tt])};
+    }
+    lds_barrier();                                                    // B1
+
+    if constexpr (C::NG > 1) {
+      // Combine the NG groups of every token: thread (token, q) with the NG
+      // threads of a token adjacent, reduced with in-quad DPP exchanges.  The
+      // factor for group q folds in the normaliser: fq / (D + eps L) for the
+      // read-out, fq / L for the responsibilities.
+      if (threadIdx.x < kTile * C::NG) {
+        const int t = threadIdx.x / C::NG, q = threadIdx.x % C::NG;
+        const f32x4 st = stats[q * kTile + t];
+        float M = st[0];
+        M = fmaxf(M, dpp<0xB1>(M));
+        if constexpr (C::NG == 4) M = fmaxf(M, dpp<0x4E>(M));
+        const float fq = st[0] == -INFINITY ? 0.f : exp2_fast(st[0] - M);
+        float L = fq * st[1], D = fq * st[2];
+        L += dpp<0xB1>(L);
+        D += dpp<0xB1>(D);
+        if constexpr (C::NG == 4) {
+          L += dpp<0x4E>(L);
+          D += dpp<0x4E>(D);
+        }
+        fac[q * kTile + t] = MODE == 0 ? fq / (D + a.eps * L) : fq / L;
+        if (want_assign) {
+          // groups cover increasing component ranges: the smallest index among
+          // the groups attaining the maximum is the lowest-index argmax
+          int key = st[0] == M ? __float_as_int(st[3]) : 0x7fffffff;
+          key = min(key, dpp_i<0xB1>(key));
+          if constexpr (C::NG == 4) key = min(key, dpp_i<0x4E>(key));
+          if (q == 0 && t < nvalid) a.assign[(size_t)bh * a.N + tile0 + t] = key;
+        }
+      }
+    }
+    if (has_next) {
+      xreg.store(F);
+      if (tile0 + 2 * kTile < t_end) xreg.load(xs, tile0 + 2 * kTile, tile_n(tile0 + 2 * kTile));
+    }
+    lds_barrier();                                                    // B2
 
     float f[C::TTW];
     if constexpr (C::NG > 1) {
-      if (g == 0) {
-#pragma unroll
-        for (int tt = 0; tt < C::TTW; ++tt)
-          stats[cgi * kTile + tile_token(gt0 + tt, c)] =
-              f32x4{m[tt], l[tt], dn[tt], __int_as_float(am[tt])};
-      }
-      lds_barrier();
-      if (threadIdx.x < kTile) {
-        const int t = threadIdx.x;
-        f32x4 st[C::NG];
-        float M = -INFINITY;
-#pragma unroll
-        for (int q = 0; q < C::NG; ++q) {
-          st[q] = stats[q * kTile + t];
-          M = fmaxf(M, st[q][0]);
-        }
-        float L = 0.f, D = 0.f, fq[C::NG];
-        int arg = 0;
-        bool found = false;
-#pragma unroll
-        for (int q = 0; q < C::NG; ++q) {
-          fq[q] = st[q][0] == -INFINITY ? 0.f : exp2_fast(st[q][0] - M);
-          L += fq[q] * st[q][1];
-          D += fq[q] * st[q][2];
-          if (!found && st[q][0] == M) { arg = __float_as_int(st[q][3]); found = true; }
-        }
-        if constexpr (MODE == 0) {
-#pragma unroll
-          for (int q = 0; q < C::NG; ++q) fac[q * kTile + t] = fq[q];
-          rinv[t] = 1.f / (D + a.eps * L);
-        } else {
-          const float invL = 1.f / L;
-#pragma unroll
-          for (int q = 0; q < C::NG; ++q) fac[q * kTile + t] = fq[q] * invL;
-        }
-        if (want_assign && t < nvalid) a.assign[(size_t)bh * a.N + tile0 + t] = arg;
-      }
-      lds_barrier();
 #pragma unroll
       for (int tt = 0; tt < C::TTW; ++tt) f[tt] = fac[cgi * kTile + tile_token(gt0 + tt, c)];
     } else {
 #pragma unroll
       for (int tt = 0; tt < C::TTW; ++tt) {
         const int tok = tile_token(gt0 + tt, c);
-        if constexpr (MODE == 0) {
-          f[tt] = 1.f;
-          if (g == 0) rinv[tok] = 1.f / (dn[tt] + a.eps * l[tt]);
-        } else {
-          f[tt] = 1.f / l[tt];
-        }
+        f[tt] = MODE == 0 ? 1.f / (dn[tt] + a.eps * l[tt]) : 1.f / l[tt];
         if (want_assign && g == 0 && tok < nvalid) a.assign[(size_t)bh * a.N + tile0 + tok] = am[tt];
       }
     }
@@ -306,9 +364,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C
           }
         }
       }
-      continue;
     } else {
-      // Gamma' (unnormalised responsibilities relative to the tile maximum) -> LDS [token][component]
+      // Gamma'' = responsibilities already divided by the read-out denominator,
+      // -> LDS [token][component]
 #pragma unroll
       for (int tt = 0; tt < C::TTW; ++tt) {
         const int tok = tile_token(gt0 + tt, c);
@@ -325,11 +383,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C
           }
         }
       }
-      lds_barrier();
+      lds_barrier();                                                  // B3
 
-      // O^T = V~^T Gamma'^T for this wave's (token tile, d tile) share: lane column =
-      // token, rows = four consecutive d, so each lane scales by one normaliser and
-      // writes 8 (bf16) or 16 (fp32) contiguous bytes
+      // O^T = V~^T Gamma''^T for this wave's (token tile, d tile) share: lane
+      // column = token, rows = four consecutive d, written as 8 (bf16) or 16
+      // (fp32) contiguous bytes
 #pragma unroll
       for (int jt = 0; jt < C::TPW; ++jt) {
         const int tt = C::DVT >= C::NG ? jt : cgi / C::DVT + (C::NG / C::DVT) * jt;
@@ -344,23 +402,247 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C
 #pragma unroll
           for (int j = 0; j < C::DPW; ++j) acc[j] = mma(Vr[j][s], Bg, acc[j]);
         }
-        const float rv = rinv[rtok];
         if (rtok < nvalid) {
 #pragma unroll
           for (int j = 0; j < C::DPW; ++j) {
             const int dt = C::DVT >= C::NG ? cgi * C::DPW + j : cgi % C::DVT;
             const size_t off = ((size_t)bh * a.N + tile0 + rtok) * C::DV + dt * 16 + 4 * g;
-            const f32x4 o = acc[j] * rv;
             if (a.out_bf) {
               bf16x4 o4;
 #pragma unroll
-              for (int i = 0; i < 4; ++i) o4[i] = to_bf16(o[i]);
+              for (int i = 0; i < 4; ++i) o4[i] = to_bf16(acc[j][i]);
               *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(a.out) + off) = o4;
             } else {
-              st16(reinterpret_cast<float*>(a.out) + off, o);
+              st16(reinterpret_cast<float*>(a.out) + off, acc[j]);
             }
           }
         }
+      }
+    }
+  }
+}
+
+// ============================================================================
+// Read-out, bf16 inputs, token-owner form.  Every wave owns 32 queries at a
+// time and all K_pad components, so the per-query softmax and the read-out
+// normaliser stay inside the wave: the main loop has no barrier and no LDS
+// write.  The workgroup (8 waves) keeps two read-only tables in LDS:
+//   coef  -- the score coefficients (A_hi, A_lo, B_hi, B_lo) as ready-made MFMA
+//            A operands, component rows in the order pi below;
+//   vtab  -- V~^T as MFMA A operands (bf16) plus one extra 16-row block holding
+//            Z_hi, Z_lo and ones, so the same MFMAs that form Gamma V~ also form
+//            the denominator sum_k e_k Z_k and the mass sum_k e_k.
+// Scores use D[component][query].  Component row r of score tile ct is
+// pi(ct, r) = 32 (ct / 2) + 8 (r / 4) + 4 (ct % 2) + r % 4, which puts the
+// eight consecutive components 32p + 8g .. 32p + 8g + 7 of tiles 2p, 2p+1 in
+// lane group g: exactly the B operand chunk of O^T = V~^T Gamma^T for
+// contraction step p, so e = exp2(s - m) feeds the read-out straight from
+// registers.  Likewise output row r of d tile dt is d = sigma(dt, r) (same
+// pairing), so a lane holds eight consecutive outputs of one query: one
+// 16-byte store per pair of d tiles.
+// ============================================================================
+template <class C>
+struct Read2 {
+  static constexpr int KP = C::Kp;                       // a multiple of 32 (a pair of tiles)
+  static constexpr int CT = KP / 16;
+  static constexpr int KS = KP / 32;
+  static constexpr int NKS = C::DRP / 32;
+  static constexpr int DVT = C::DV / 16;
+  static constexpr int OT = DVT + 1;                     // + (Z_hi, Z_lo, 1) block
+  static constexpr int COEF = CT * NKS * 4;              // 1 KB operand chunks
+  static constexpr int VCH = OT * KS;
+  static constexpr int LDS = (COEF + VCH) * 1024 + KP * 4;
+  static constexpr bool kOK = C::kBF && C::Kp % 32 == 0 && C::DRP <= 64 && LDS <= 150 * 1024;
+};
+
+template <class C>
+__global__ void __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+gma_read2_kernel(BidirArgs a) {
+  using R = Read2<C>;
+  constexpr int NW = 8;
+  __shared__ __attribute__((aligned(16))) bf16x8 coef[R::COEF * 64];
+  __shared__ __attribute__((aligned(16))) bf16x8 vtab[R::VCH * 64];
+  __shared__ __attribute__((aligned(16))) float cperm[R::KP];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int64_t bh = blockIdx.y;
+  const int h = (int)(bh % a.H);
+  const bool want_assign = a.assign != nullptr;
+
+  // ---- tables: contiguous copies of what the prologue and the reduction wrote ----
+  {
+    const char* tb = a.params + (size_t)h * a.head_bytes + a.head_bytes / 2;
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(tb);
+    for (int idx = threadIdx.x; idx < R::COEF * 64; idx += NW * 64) coef[idx] = src[idx];
+    const float* cp = reinterpret_cast<const float*>(tb + (size_t)8 * C::Kp * C::DRP);
+    for (int j = threadIdx.x; j < R::KP; j += NW * 64) cperm[j] = cp[j];
+    const bf16x8* vsrc = a.vtab + (size_t)bh * R::VCH * 64;
+    for (int idx = threadIdx.x; idx < R::VCH * 64; idx += NW * 64) vtab[idx] = vsrc[idx];
+  }
+  __syncthreads();
+
+  // ---- queries: groups of 32, wave w takes groups w, w + 8, ... of this split ----
+  const int64_t G32 = (a.N + 31) / 32;
+  const int64_t gpw = (G32 + gridDim.x - 1) / gridDim.x;
+  const int64_t gb = (int64_t)blockIdx.x * gpw;
+  const int64_t ge = gb + gpw < G32 ? gb + gpw : G32;
+  const bf16* xs = reinterpret_cast<const bf16*>(a.x) + (size_t)bh * a.N * C::DR;
+  bf16* out = reinterpret_cast<bf16*>(a.out) + (size_t)bh * a.N * C::DV;
+
+  // lane (c, g) of query tile tt holds query tok0 + 16 tt + c, routing columns
+  // 32 s + 8 g .. + 7
+  bf16x8 xr[2][R::NKS];
+  auto load_x = [&](int64_t grp) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int64_t tok = grp * 32 + 16 * tt + c;
+#pragma unroll
+      for (int s = 0; s < R::NKS; ++s) {
+        const int col = 32 * s + 8 * g;
+        if (tok < a.N && col < C::DR) xr[tt][s] = ld16<bf16x8>(xs + (size_t)tok * C::DR + col);
+        else xr[tt][s] = bf16x8{};
+      }
+    }
+  };
+  int64_t grp = gb + wave;
+  if (grp < ge) load_x(grp);
+  for (; grp < ge; grp += NW) {
+    // the tables are loop-invariant: keep the compiler from hoisting all of
+    // their reads (far more registers than a wave has) out of the loop
+    asm volatile("" ::: "memory");
+    // features (x^2 hi, x^2 lo, x) of both query tiles
+    bf16x8 f[2][R::NKS][3];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int s = 0; s < R::NKS; ++s) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float xf = from_bf16(xr[tt][s][e]);
+          bf16 hh, ll;
+          split_bf16(xf * xf, hh, ll);
+          f[tt][s][0][e] = hh;
+          f[tt][s][1][e] = ll;
+        }
+        f[tt][s][2] = xr[tt][s];
+      }
+
+    // scores, two component tiles at a time (four independent accumulators)
+    f32x4 S[2][R::CT];
+#pragma unroll
+    for (int ct = 0; ct < R::CT; ++ct) {
+      const f32x4 cs = *reinterpret_cast<const f32x4*>(&cperm[ct * 16 + 4 * g]);
+      S[0][ct] = cs;
+      S[1][ct] = cs;
+    }
+    constexpr int WI[5] = {0, 0, 1, 2, 3};   // A_hi, A_hi, A_lo, B_hi, B_lo
+    constexpr int FI[5] = {0, 1, 0, 2, 2};   // x^2_hi, x^2_lo, x^2_hi, x, x
+    // steps j = (tile pair, routing chunk); the operands of step j + 1 are read
+    // from LDS while the 20 MFMAs of step j run
+    constexpr int NSTEP = R::CT / 2 * R::NKS;
+    auto load_w = [&](int j, bf16x8 (&w)[2][4]) {
+      const int cp = 2 * (j / R::NKS), s = j % R::NKS;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int ar = 0; ar < 4; ++ar) w[u][ar] = coef[(((cp + u) * R::NKS + s) * 4 + ar) * 64 + lane];
+    };
+    bf16x8 wbuf[2][2][4];
+    load_w(0, wbuf[0]);
+#pragma unroll
+    for (int j = 0; j < NSTEP; ++j) {
+      if (j + 1 < NSTEP) load_w(j + 1, wbuf[(j + 1) & 1]);
+      const int cp = 2 * (j / R::NKS), s = j % R::NKS;
+#pragma unroll
+      for (int q = 0; q < 5; ++q)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            S[tt][cp + u] = mma(wbuf[j & 1][u][WI[q]], f[tt][s][FI[q]], S[tt][cp + u]);
+    }
+    if (grp + NW < ge) load_x(grp + NW);
+
+    // per query: max over components (in-lane, then across the four lane
+    // groups), e = exp2(s - m) packed as the read-out operand
+    bf16x8 E[2][R::KS];
+    int am[2] = {0, 0};
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      float v = S[tt][0][0];
+#pragma unroll
+      for (int ct = 0; ct < R::CT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v = fmaxf(v, S[tt][ct][i]);
+      const float m = groups_max(v);
+      if (want_assign) {
+        float bv = S[tt][0][0];
+        int bi = pair_row(0, 4 * g);
+#pragma unroll
+        for (int ct = 0; ct < R::CT; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) argmax_merge(bv, bi, S[tt][ct][i], pair_row(ct, 4 * g + i));
+        groups_argmax(bv, bi);
+        am[tt] = bi;
+      }
+#pragma unroll
+      for (int p = 0; p < R::KS; ++p)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          E[tt][p][i] = to_bf16(exp2_fast(S[tt][2 * p][i] - m));
+          E[tt][p][4 + i] = to_bf16(exp2_fast(S[tt][2 * p + 1][i] - m));
+        }
+    }
+
+    // O^T (and the denominator block) = V~^T E^T
+    f32x4 O[2][R::OT];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int dt = 0; dt < R::OT; ++dt) O[tt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int NV = R::OT * R::KS;
+    bf16x8 vb[4];
+#pragma unroll
+    for (int j = 0; j < 3 && j < NV; ++j) vb[j] = vtab[j * 64 + lane];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      if (j + 3 < NV) vb[(j + 3) & 3] = vtab[(j + 3) * 64 + lane];
+      const int dt = j / R::KS, p = j % R::KS;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) O[tt][dt] = mma(vb[j & 3], E[tt][p], O[tt][dt]);
+    }
+
+    // O_i = num_i / (D_i + eps L_i); rows 0..2 of the last block (lane group 0)
+    // hold Z_hi . e, Z_lo . e and sum e
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const f32x4 dz = O[tt][R::DVT];
+      float r = 1.f / (dz[0] + dz[1] + a.eps * dz[2]);
+      float r0, r1;
+      pair_xor16(r, r0, r1);
+      pair_xor32(r0, r, r1);          // every lane: the value of lane group 0
+      const int64_t tok = grp * 32 + 16 * tt + c;
+      if (tok < a.N) {
+        bf16* orow = out + (size_t)tok * C::DV;
+        if constexpr (R::DVT >= 2) {
+#pragma unroll
+          for (int qd = 0; qd < R::DVT / 2; ++qd) {
+            bf16x8 o8;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              o8[i] = to_bf16(O[tt][2 * qd][i] * r);
+              o8[4 + i] = to_bf16(O[tt][2 * qd + 1][i] * r);
+            }
+            st16(orow + 32 * qd + 8 * g, o8);
+          }
+        } else {
+          bf16x4 o4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o4[i] = to_bf16(O[tt][0][i] * r);
+          *reinterpret_cast<bf16x4*>(orow + 4 * g) = o4;
+        }
+        if (want_assign && g == 0) a.assign[(size_t)bh * a.N + tok] = am[tt];
       }
     }
   }
@@ -378,6 +660,7 @@ static hipError_t run_bidir(const Plan& p, const Tensors& t, hipStream_t s) {
   a.partial_z = reinterpret_cast<float*>(t.ws + p.off_partial_z);
   a.vt = reinterpret_cast<const float*>(t.ws + p.off_vt);
   a.z = reinterpret_cast<const float*>(t.ws + p.off_z);
+  a.vtab = reinterpret_cast<const bf16x8*>(t.ws + p.off_vtab);
   a.N = p.N;
   a.H = (int)p.H;
   a.K = p.K;
@@ -403,7 +686,8 @@ static hipError_t run_bidir(const Plan& p, const Tensors& t, hipStream_t s) {
   hipLaunchKernelGGL(gma_reduce_kernel, dim3((nred + 255) / 256, (unsigned)p.BH), dim3(256), 0, s,
                      a.partial, a.partial_z, PS, C::Kp, C::DV,
                      reinterpret_cast<float*>(t.ws + p.off_vt),
-                     reinterpret_cast<float*>(t.ws + p.off_z));
+                     reinterpret_cast<float*>(t.ws + p.off_z),
+                     Read2<C>::kOK ? reinterpret_cast<bf16*>(t.ws + p.off_vtab) : nullptr);
   if (g_launch_hook) g_launch_hook("gma_reduce", s, 0);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -413,7 +697,17 @@ static hipError_t run_bidir(const Plan& p, const Tensors& t, hipStream_t s) {
   a.out = t.out;
   a.assign = t.assign_q;
   if (g_launch_hook) g_launch_hook("gma_read", s, 1);
-  hipLaunchKernelGGL((gma_read_kernel<C, 0>), grid, dim3(kThreads), 0, s, a);
+  if constexpr (Read2<C>::kOK) {
+    // about one workgroup per compute unit, at least eight 32-query groups each
+    const int64_t g32 = (p.N + 31) / 32;
+    int64_t s2 = (256 + p.BH - 1) / p.BH;
+    const int64_t cap = (g32 + 7) / 8;
+    if (s2 > cap) s2 = cap;
+    if (s2 < 1) s2 = 1;
+    hipLaunchKernelGGL(gma_read2_kernel<C>, dim3((unsigned)s2, (unsigned)p.BH), dim3(512), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((gma_read_kernel<C, 0>), grid, dim3(kThreads), 0, s, a);
+  }
   if (g_launch_hook) g_launch_hook("gma_read", s, 0);
   return hipGetLastError();
 }

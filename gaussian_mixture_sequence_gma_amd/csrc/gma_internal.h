@@ -28,7 +28,7 @@ struct Plan {
   int nspan = 0;            // spans per sequence
   // workspace layout (bytes)
   size_t head_bytes = 0;
-  size_t off_params = 0, off_partial = 0, off_partial_z = 0, off_vt = 0, off_z = 0;
+  size_t off_params = 0, off_partial = 0, off_partial_z = 0, off_vt = 0, off_z = 0, off_vtab = 0;
   size_t off_state = 0, off_state_z = 0, off_carry = 0, off_carry_z = 0;
   size_t total = 0;
 };

@@ -79,6 +79,7 @@ struct BidirArgs {
   float* partial;         // [BH][S*TG][Kp][DV]
   float* partial_z;       // [BH][S*TG][Kp]
   const float* vt;        // [BH][Kp][DV]
+  const bf16x8* vtab;     // [BH][(DV/16 + 1) * Kp/32 * 64] read-out operand table
   const float* z;         // [BH][Kp]
   int32_t* assign;        // [BH][N] or null
   float* gamma;           // resp: [BH][N][K] or null
