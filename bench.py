@@ -130,8 +130,8 @@ def cpu_baseline(w, gen, max_threads: int = 16, min_seconds: float = 10.0,
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="long_bidir_bf16")
     ap.add_argument("--causal", type=int, default=None, help="override the workload's variant")
     ap.add_argument("--no-cpu-baseline", action="store_true")

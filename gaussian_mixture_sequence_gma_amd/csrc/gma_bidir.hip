@@ -317,7 +317,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C
           L += dpp<0x4E>(L);
           D += dpp<0x4E>(D);
         }
-        fac[q * kTile + t] = MODE == 0 ? fq / (D + a.eps * L) : fq / L;
+        fac[q * kTile + t] = MODE == 0 ? fq * fast_rcp(D + a.eps * L) : fq * fast_rcp(L);
         if (want_assign) {
           // groups cover increasing component ranges: the smallest index among
           // the groups attaining the maximum is the lowest-index argmax
@@ -342,7 +342,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C
 #pragma unroll
       for (int tt = 0; tt < C::TTW; ++tt) {
         const int tok = tile_token(gt0 + tt, c);
-        f[tt] = MODE == 0 ? 1.f / (dn[tt] + a.eps * l[tt]) : 1.f / l[tt];
+        f[tt] = MODE == 0 ? fast_rcp(dn[tt] + a.eps * l[tt]) : fast_rcp(l[tt]);
         if (want_assign && g == 0 && tok < nvalid) a.assign[(size_t)bh * a.N + tile0 + tok] = am[tt];
       }
     }
@@ -553,6 +553,8 @@ gma_read2_kernel(BidirArgs a) {
 #pragma unroll
     for (int j = 0; j < NSTEP; ++j) {
       if (j + 1 < NSTEP) load_w(j + 1, wbuf[(j + 1) & 1]);
+      // keep the prefetch one full step ahead of its use
+      __builtin_amdgcn_sched_barrier(0);
       const int cp = 2 * (j / R::NKS), s = j % R::NKS;
 #pragma unroll
       for (int q = 0; q < 5; ++q)
@@ -561,6 +563,7 @@ gma_read2_kernel(BidirArgs a) {
 #pragma unroll
           for (int u = 0; u < 2; ++u)
             S[tt][cp + u] = mma(wbuf[j & 1][u][WI[q]], f[tt][s][FI[q]], S[tt][cp + u]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (grp + NW < ge) load_x(grp + NW);
 
@@ -601,16 +604,20 @@ gma_read2_kernel(BidirArgs a) {
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int dt = 0; dt < R::OT; ++dt) O[tt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // contraction step p outermost: consecutive MFMAs update different blocks
     constexpr int NV = R::OT * R::KS;
+    auto vidx = [&](int j) { return ((j % R::OT) * R::KS + j / R::OT) * 64 + lane; };
     bf16x8 vb[4];
 #pragma unroll
-    for (int j = 0; j < 3 && j < NV; ++j) vb[j] = vtab[j * 64 + lane];
+    for (int j = 0; j < 3 && j < NV; ++j) vb[j] = vtab[vidx(j)];
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      if (j + 3 < NV) vb[(j + 3) & 3] = vtab[(j + 3) * 64 + lane];
-      const int dt = j / R::KS, p = j % R::KS;
+      if (j + 3 < NV) vb[(j + 3) & 3] = vtab[vidx(j + 3)];
+      __builtin_amdgcn_sched_barrier(0);
+      const int dt = j % R::OT, p = j / R::OT;
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) O[tt][dt] = mma(vb[j & 3], E[tt][p], O[tt][dt]);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // O_i = num_i / (D_i + eps L_i); rows 0..2 of the last block (lane group 0)
@@ -618,7 +625,7 @@ gma_read2_kernel(BidirArgs a) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const f32x4 dz = O[tt][R::DVT];
-      float r = 1.f / (dz[0] + dz[1] + a.eps * dz[2]);
+      float r = fast_rcp(dz[0] + dz[1] + a.eps * dz[2]);
       float r0, r1;
       pair_xor16(r, r0, r1);
       pair_xor32(r0, r, r1);          // every lane: the value of lane group 0
@@ -649,6 +656,521 @@ gma_read2_kernel(BidirArgs a) {
 }
 
 // ============================================================================
+// Latent write, bf16 inputs, token-owner form.  Every wave owns 32 keys at a
+// time and all K_pad components, and accumulates its own V~ (K_pad x d_v, in
+// the accumulation registers) and Z over all its keys, so the main loop has no
+// barrier and no exchange between waves: the per-key softmax stays inside the
+// wave.  The workgroup shares the score-coefficient table of the read-out
+// (same LDS layout); each wave stages its own V tiles (32 keys, swizzled rows)
+// by direct global -> LDS copies, double-buffered.
+// Scores use D[key][component] with key rows in tile_token order, so lane
+// group g of the two key tiles holds keys 8g .. 8g + 7: the normalised
+// responsibilities are the A operand of V~ += Gamma^T V straight from
+// registers.  The four waves' partial V~ and Z are added in LDS at the end, in
+// a fixed order.
+// ============================================================================
+template <class C>
+struct Write2 {
+  static constexpr int KP = C::Kp;
+  static constexpr int CT = KP / 16;
+  static constexpr int NKS = C::DRP / 32;
+  static constexpr int DVT = C::DV / 16;
+  static constexpr int ROWCH = C::DV / 8;                 // 16-byte chunks per V row
+  static constexpr int VT = 32 * C::DV;                   // bf16 elements of one V tile
+  static constexpr int NDMA = VT * 2 / 1024;               // 1 KB wave copies per V tile
+  static constexpr int COEF = CT * NKS * 4;
+  static constexpr int LOOP_LDS = COEF * 1024 + KP * 4 + 4 * 2 * VT * 2;
+  static constexpr int RED_LDS = 2 * (KP * C::DV + 4 * KP) * 4;   // two partial slots
+  static constexpr int LDS = LOOP_LDS > RED_LDS ? LOOP_LDS : RED_LDS;
+  static constexpr bool kOK = C::kBF && KP % 32 == 0 && C::DRP <= 64 && C::DV >= 32 &&
+                              LDS <= 160 * 1024 && CT * DVT * 4 <= 256;
+};
+
+template <class C>
+__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gma_write2_kernel(BidirArgs a) {
+  using R = Write2<C>;
+  constexpr int NW = 4;
+  __shared__ __attribute__((aligned(16))) char lds[R::LDS];
+  bf16x8* coef = reinterpret_cast<bf16x8*>(lds);
+  float* cperm = reinterpret_cast<float*>(lds + R::COEF * 1024);
+  bf16* vbuf = reinterpret_cast<bf16*>(lds + R::COEF * 1024 + R::KP * 4);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int64_t bh = blockIdx.y;
+  const int h = (int)(bh % a.H);
+  const bool want_assign = a.assign != nullptr;
+
+  {
+    const char* tb = a.params + (size_t)h * a.head_bytes + a.head_bytes / 2;
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(tb);
+    for (int idx = threadIdx.x; idx < R::COEF * 64; idx += NW * 64) coef[idx] = src[idx];
+    const float* cp = reinterpret_cast<const float*>(tb + (size_t)8 * C::Kp * C::DRP);
+    for (int j = threadIdx.x; j < R::KP; j += NW * 64) cperm[j] = cp[j];
+  }
+  __syncthreads();
+
+  const int64_t G32 = (a.N + 31) / 32;
+  const int64_t gpw = (G32 + gridDim.x - 1) / gridDim.x;
+  const int64_t gb = (int64_t)blockIdx.x * gpw;
+  const int64_t ge = gb + gpw < G32 ? gb + gpw : G32;
+  const bf16* xs = reinterpret_cast<const bf16*>(a.x) + (size_t)bh * a.N * C::DR;
+  const bf16* vs = reinterpret_cast<const bf16*>(a.v) + (size_t)bh * a.N * C::DV;
+  bf16* myv = vbuf + wave * 2 * R::VT;
+
+  // key row r of key tile tt is key 8 (r / 4) + 4 tt + r % 4 of the group.  The
+  // loads are unconditional (clamped address, value zeroed afterwards) so that
+  // every group issues the same number of memory operations: the wait for the
+  // V copies below counts them.
+  bf16x8 xr[2][R::NKS];
+  auto load_x = [&](int64_t grp) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int64_t tok = grp * 32 + tile_token(tt, c);
+#pragma unroll
+      for (int s = 0; s < R::NKS; ++s) {
+        const int col = 32 * s + 8 * g;
+        const bool ok = tok < a.N && col < C::DR;
+        const bf16x8 v = ld16<bf16x8>(xs + (size_t)(ok ? tok : 0) * C::DR + (ok ? col : 0));
+        xr[tt][s] = ok ? v : bf16x8{};
+      }
+    }
+  };
+  // V tile of a group -> buffer b: lane l of copy j fills row j * 1024 / (2 d_v) +
+  // l / ROWCH, physical chunk l % ROWCH (swizzled as swz_elem<ROWCH>)
+  auto load_v = [&](int64_t grp, int b) {
+    constexpr int RPK = 512 / C::DV;      // rows per 1 KB copy
+#pragma unroll
+    for (int j = 0; j < R::NDMA; ++j) {
+      const int row = j * RPK + lane / R::ROWCH, pc = lane % R::ROWCH;
+      const int lc = R::ROWCH >= 2 ? (pc ^ ((2 * row) & (R::ROWCH - 2))) : pc;
+      int64_t tok = grp * 32 + row;
+      if (tok >= a.N) tok = a.N - 1;                       // rows past the end get Gamma = 0
+      global_to_lds16(vs + (size_t)tok * C::DV + lc * 8, myv + b * R::VT + j * 512);
+    }
+  };
+
+  f32x4 acc[R::CT][R::DVT];
+#pragma unroll
+  for (int ct = 0; ct < R::CT; ++ct)
+#pragma unroll
+    for (int dt = 0; dt < R::DVT; ++dt) acc[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float zacc[R::CT];
+#pragma unroll
+  for (int ct = 0; ct < R::CT; ++ct) zacc[ct] = 0.f;
+
+  int64_t grp = gb + wave;
+  int buf = 0;
+  if (grp < ge) {
+    load_x(grp);
+    load_v(grp, 0);
+  }
+  for (; grp < ge; grp += NW, buf ^= 1) {
+    asm volatile("" ::: "memory");      // keep the table reads inside the loop
+    bf16x8 f[2][R::NKS][3];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int s = 0; s < R::NKS; ++s) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float xf = from_bf16(xr[tt][s][e]);
+          bf16 hh, ll;
+          split_bf16(xf * xf, hh, ll);
+          f[tt][s][0][e] = hh;
+          f[tt][s][1][e] = ll;
+        }
+        f[tt][s][2] = xr[tt][s];
+      }
+    const bool more = grp + NW < ge;
+    if (more) load_v(grp + NW, buf ^ 1);
+
+    f32x4 S[2][R::CT];
+#pragma unroll
+    for (int ct = 0; ct < R::CT; ++ct) {
+      const float cv = cperm[ct * 16 + c];
+      S[0][ct] = f32x4{cv, cv, cv, cv};
+      S[1][ct] = S[0][ct];
+    }
+    constexpr int WI[5] = {0, 0, 1, 2, 3};
+    constexpr int FI[5] = {0, 1, 0, 2, 2};
+    constexpr int NSTEP = R::CT / 2 * R::NKS;
+    auto load_w = [&](int j, bf16x8 (&w)[2][4]) {
+      const int cp = 2 * (j / R::NKS), s = j % R::NKS;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int ar = 0; ar < 4; ++ar) w[u][ar] = coef[(((cp + u) * R::NKS + s) * 4 + ar) * 64 + lane];
+    };
+    bf16x8 wbuf[2][2][4];
+    load_w(0, wbuf[0]);
+#pragma unroll
+    for (int j = 0; j < NSTEP; ++j) {
+      if (j + 1 < NSTEP) load_w(j + 1, wbuf[(j + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      const int cp = 2 * (j / R::NKS), s = j % R::NKS;
+#pragma unroll
+      for (int q = 0; q < 5; ++q)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            S[tt][cp + u] = mma(f[tt][s][FI[q]], wbuf[j & 1][u][WI[q]], S[tt][cp + u]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (more) load_x(grp + NW);
+
+    // per key (row 4g + i of key tile tt): softmax over the CT columns of this
+    // lane and the 16 lanes of its row
+    bf16x8 A[R::CT];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float m = S[tt][0][i];
+#pragma unroll
+        for (int ct = 1; ct < R::CT; ++ct) m = fmaxf(m, S[tt][ct][i]);
+        m = row16_max(m);
+        float l = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < R::CT; ++ct) {
+          const float e = exp2_fast(S[tt][ct][i] - m);
+          S[tt][ct][i] = e;
+          l += e;
+        }
+        l = row16_sum(l);
+        const int64_t tok = grp * 32 + 8 * g + 4 * tt + i;
+        const float inv = tok < a.N ? fast_rcp(l) : 0.f;
+#pragma unroll
+        for (int ct = 0; ct < R::CT; ++ct) {
+          const float gm = S[tt][ct][i] * inv;
+          zacc[ct] += gm;
+          A[ct][4 * tt + i] = to_bf16(gm);
+        }
+      }
+    if (want_assign) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // the largest responsibility is the largest score (ties: lowest index)
+          float bv = S[tt][0][i];
+          int bi = pair_row(0, c);
+#pragma unroll
+          for (int ct = 1; ct < R::CT; ++ct) argmax_merge(bv, bi, S[tt][ct][i], pair_row(ct, c));
+          row16_argmax(bv, bi);
+          const int64_t tok = grp * 32 + 8 * g + 4 * tt + i;
+          if (c == 0 && tok < a.N) a.assign[(size_t)bh * a.N + tok] = bi;
+        }
+    }
+
+    // V(grp) has arrived once at most the copies and loads of the next group
+    // (issued after it) are outstanding
+    if (more) {
+      if constexpr (R::NDMA + 2 * R::NKS == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+      else if constexpr (R::NDMA + 2 * R::NKS == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else if constexpr (R::NDMA + 2 * R::NKS == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+      else if constexpr (R::NDMA + 2 * R::NKS == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+      else if constexpr (R::NDMA + 2 * R::NKS == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else wait_global_loads();
+    } else {
+      wait_global_loads();
+    }
+    const bf16* vt = myv + buf * R::VT;
+#pragma unroll
+    for (int dt = 0; dt < R::DVT; ++dt) {
+      const bf16x8 vb = tr_chunk_swz<R::ROWCH>(vt, 0, dt * 16);
+#pragma unroll
+      for (int ct = 0; ct < R::CT; ++ct) acc[ct][dt] = mma(A[ct], vb, acc[ct][dt]);
+    }
+  }
+
+  // ---- the four waves' partials, added in LDS in a fixed order --------------------
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(lds);
+  constexpr int NV = R::CT * R::DVT * 4;
+  auto put = [&](int slot) {
+    float* r = red + slot * (NV + R::CT) * 64;
+#pragma unroll
+    for (int ct = 0; ct < R::CT; ++ct) {
+#pragma unroll
+      for (int dt = 0; dt < R::DVT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[((ct * R::DVT + dt) * 4 + i) * 64 + lane] = acc[ct][dt][i];
+      r[(NV + ct) * 64 + lane] = zacc[ct];
+    }
+  };
+  auto add = [&](int slot) {
+    const float* r = red + slot * (NV + R::CT) * 64;
+#pragma unroll
+    for (int ct = 0; ct < R::CT; ++ct) {
+#pragma unroll
+      for (int dt = 0; dt < R::DVT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[ct][dt][i] += r[((ct * R::DVT + dt) * 4 + i) * 64 + lane];
+      zacc[ct] += r[(NV + ct) * 64 + lane];
+    }
+  };
+  if (wave >= 2) put(wave - 2);
+  __syncthreads();
+  if (wave < 2) add(wave);
+  __syncthreads();
+  if (wave == 1) put(0);
+  __syncthreads();
+  if (wave == 0) {
+    add(0);
+    const size_t pslot = (size_t)bh * gridDim.x + blockIdx.x;
+    float* pv = a.partial + pslot * C::Kp * C::DV;
+    float* pz = a.partial_z + pslot * C::Kp;
+#pragma unroll
+    for (int ct = 0; ct < R::CT; ++ct) {
+#pragma unroll
+      for (int dt = 0; dt < R::DVT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pv[pair_row(ct, 4 * g + i) * C::DV + dt * 16 + c] = acc[ct][dt][i];
+      // lanes of one column c hold different keys: sum the four groups
+      const float zt = groups_sum(zacc[ct]);
+      if (g == 0) pz[pair_row(ct, c)] = zt;
+    }
+  }
+}
+
+// ============================================================================
+// Latent write, bf16 inputs, component-owner form with responsibilities kept
+// in registers.  Wave (cgi, tg) holds the coefficients of component group cgi
+// (CPW tiles) and scores the tokens of its token group in the layout
+// D[token][component], rows in tile_token order: lane group g of key tiles 2P,
+// 2P + 1 then holds keys 32P + 8g .. 32P + 8g + 7 of one component, which is
+// the A operand of V~ += Gamma^T V with no transpose.  Per-token statistics
+// over the wave's components (16-lane row reductions) are combined across the
+// NG groups through LDS by all threads; V tiles are copied HBM -> LDS directly
+// into a double buffer.  Two barriers per 64-token tile; small enough in
+// registers and LDS for two workgroups per compute unit.
+// ============================================================================
+template <class C>
+struct Write3 {
+  static constexpr int VROWCH = C::DV / 8;
+  static constexpr int VROUNDS = kTile * VROWCH / 64;           // 1 KB wave copies per V tile
+  static constexpr int VRPW = (VROUNDS + kWaves - 1) / kWaves;
+  static constexpr bool kOK = C::kBF && C::NG >= 2 && C::TTW % 2 == 0 && C::DV >= 32;
+};
+
+template <class C>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+gma_write3_kernel(BidirArgs a) {
+  using R = Write3<C>;
+  constexpr int TTW = C::TTW, CPW = C::CPW, NG = C::NG;
+  __shared__ __attribute__((aligned(16))) bf16 F[3 * C::FAS];
+  __shared__ __attribute__((aligned(16))) bf16 Vr[2][kTile * C::DV];
+  __shared__ __attribute__((aligned(16))) f32x4 stats[NG * kTile];
+  __shared__ __attribute__((aligned(16))) float fac[NG * kTile];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int cgi = wave % NG, tg = wave / NG;
+  const int gt0 = tg * TTW;
+  const int64_t bh = blockIdx.y;
+  const int h = (int)(bh % a.H);
+  const int64_t t_begin = (int64_t)blockIdx.x * a.tiles_per_split * kTile;
+  const int64_t t_end = a.N < t_begin + (int64_t)a.tiles_per_split * kTile
+                            ? a.N : t_begin + (int64_t)a.tiles_per_split * kTile;
+  const int ntiles = t_end > t_begin ? (int)((t_end - t_begin + kTile - 1) / kTile) : 0;
+  const bool want_assign = a.assign != nullptr;
+
+  const char* pbase = a.params + (size_t)h * a.head_bytes;
+  bf16x8 W[CPW][C::NKS][4];
+  load_w<C>(pbase, cgi * CPW, W);
+  float cv[CPW];
+  {
+    const float* cvec = reinterpret_cast<const float*>(pbase + (size_t)8 * C::Kp * C::DRP);
+#pragma unroll
+    for (int ct = 0; ct < CPW; ++ct) cv[ct] = cvec[(cgi * CPW + ct) * 16 + c];
+  }
+  const bf16* fb[TTW];
+#pragma unroll
+  for (int tt = 0; tt < TTW; ++tt) fb[tt] = F + C::frow(tile_token(gt0 + tt, c)) + g * 8;
+
+  const bf16* xs = reinterpret_cast<const bf16*>(a.x) + (size_t)bh * a.N * C::DR;
+  const bf16* vs = reinterpret_cast<const bf16*>(a.v) + (size_t)bh * a.N * C::DV;
+  auto tile_start = [&](int k) { return t_begin + (int64_t)k * kTile; };
+  auto tile_valid = [&](int k) {
+    const int64_t r = t_end - tile_start(k);
+    return (int)(r < kTile ? r : kTile);
+  };
+  auto load_v = [&](int k, int buf) {
+    const int64_t t0 = tile_start(k);
+    const int nv = tile_valid(k);
+#pragma unroll
+    for (int j = 0; j < R::VRPW; ++j) {
+      const int round = wave * R::VRPW + j;
+      if (round < R::VROUNDS) {
+        const int P = round * 64 + lane;
+        const int r = P / R::VROWCH, pc = P - r * R::VROWCH;
+        const int lc = pc ^ ((2 * r) & (R::VROWCH - 2));
+        const int rr = r < nv ? r : nv - 1;                 // tail rows repeat a valid row
+        global_to_lds16(vs + (size_t)(t0 + rr) * C::DV + lc * 8, &Vr[buf][round * 512]);
+      }
+    }
+  };
+
+  f32x4 vacc[CPW][C::DVT], vz[CPW];
+#pragma unroll
+  for (int ct = 0; ct < CPW; ++ct) {
+    vz[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int dt = 0; dt < C::DVT; ++dt) vacc[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (bf16)1.0f;
+
+  FeatureTile<C> kreg;
+  if (ntiles > 0) {
+    kreg.load(xs, tile_start(0), tile_valid(0));
+    load_v(0, 0);
+    kreg.store(F);
+    if (ntiles > 1) kreg.load(xs, tile_start(1), tile_valid(1));
+    lds_barrier();
+  }
+
+  for (int k = 0; k < ntiles; ++k) {
+    const int64_t tile0 = tile_start(k);
+    const int nvalid = tile_valid(k);
+    const int buf = k & 1;
+
+    // scores D[token][component], independent accumulators back to back
+    f32x4 S[TTW][CPW];
+#pragma unroll
+    for (int tt = 0; tt < TTW; ++tt)
+#pragma unroll
+      for (int ct = 0; ct < CPW; ++ct) S[tt][ct] = f32x4{cv[ct], cv[ct], cv[ct], cv[ct]};
+    {
+      constexpr int WI[5] = {0, 0, 1, 2, 3};
+      constexpr int FI[5] = {0, 1, 0, 2, 2};
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        constexpr int NT = TTW / 2;
+        bf16x8 f[C::NKS][NT][3];
+#pragma unroll
+        for (int s = 0; s < C::NKS; ++s)
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const bf16* fp = fb[h2 * NT + t] + s * C::CS;
+            f[s][t][0] = ld16<bf16x8>(fp);
+            f[s][t][1] = ld16<bf16x8>(fp + C::FAS);
+            f[s][t][2] = ld16<bf16x8>(fp + 2 * C::FAS);
+          }
+#pragma unroll
+        for (int s = 0; s < C::NKS; ++s)
+#pragma unroll
+          for (int q = 0; q < 5; ++q)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+              for (int ct = 0; ct < CPW; ++ct)
+                S[h2 * NT + t][ct] = mma(f[s][t][FI[q]], W[ct][s][WI[q]], S[h2 * NT + t][ct]);
+      }
+    }
+
+    // per token (row 4g + i of tile tt): max and sum over this wave's components
+#pragma unroll
+    for (int tt = 0; tt < TTW; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float m = S[tt][0][i];
+#pragma unroll
+        for (int ct = 1; ct < CPW; ++ct) m = fmaxf(m, S[tt][ct][i]);
+        m = row16_max(m);
+        int am = 0;
+        if (want_assign) {
+          float bv = S[tt][0][i];
+          am = (cgi * CPW) * 16 + c;
+#pragma unroll
+          for (int ct = 1; ct < CPW; ++ct) argmax_merge(bv, am, S[tt][ct][i], (cgi * CPW + ct) * 16 + c);
+          row16_argmax(bv, am);
+        }
+        const float mref = m == -INFINITY ? 0.f : m;      // all-padding group: every e is 0
+        float l = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < CPW; ++ct) {
+          const float e = exp2_fast(S[tt][ct][i] - mref);
+          S[tt][ct][i] = e;
+          l += e;
+        }
+        l = row16_sum(l);
+        if (c == 0) stats[cgi * kTile + tile_token(gt0 + tt, 4 * g + i)] = f32x4{m, l, 0.f, __int_as_float(am)};
+      }
+    lds_barrier();                                                    // B1
+
+    // combine the NG groups of every token (thread (token, q), quad exchanges)
+    if (threadIdx.x < kTile * NG) {
+      const int t = threadIdx.x / NG, q = threadIdx.x % NG;
+      const f32x4 st = stats[q * kTile + t];
+      float M = st[0];
+      M = fmaxf(M, dpp<0xB1>(M));
+      if constexpr (NG == 4) M = fmaxf(M, dpp<0x4E>(M));
+      const float fq = st[0] == -INFINITY ? 0.f : exp2_fast(st[0] - M);
+      float L = fq * st[1];
+      L += dpp<0xB1>(L);
+      if constexpr (NG == 4) L += dpp<0x4E>(L);
+      fac[q * kTile + t] = t < nvalid ? fq * fast_rcp(L) : 0.f;
+      if (want_assign) {
+        int key = st[0] == M ? __float_as_int(st[3]) : 0x7fffffff;
+        key = min(key, dpp_i<0xB1>(key));
+        if constexpr (NG == 4) key = min(key, dpp_i<0x4E>(key));
+        if (q == 0 && t < nvalid) a.assign[(size_t)bh * a.N + tile0 + t] = key;
+      }
+    }
+    if (k + 1 < ntiles) kreg.store(F);
+    wait_global_loads();                 // this wave's copies of V(k)
+    if (k + 1 < ntiles) load_v(k + 1, buf ^ 1);
+    if (k + 2 < ntiles) kreg.load(xs, tile_start(k + 2), tile_valid(k + 2));
+    lds_barrier();                                                    // B2
+
+    // Gamma = e * fac (bf16) as the A operand of V~ += Gamma^T V
+    bf16x8 A[CPW][TTW / 2];
+#pragma unroll
+    for (int tt = 0; tt < TTW; ++tt) {
+      const f32x4 f4 = *reinterpret_cast<const f32x4*>(&fac[cgi * kTile + tile_token(gt0 + tt, 4 * g)]);
+#pragma unroll
+      for (int ct = 0; ct < CPW; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) A[ct][tt >> 1][4 * (tt & 1) + i] = to_bf16(S[tt][ct][i] * f4[i]);
+    }
+#pragma unroll
+    for (int P = 0; P < TTW / 2; ++P) {
+      const int tok0 = 32 * ((gt0 >> 1) + P);
+#pragma unroll
+      for (int ct = 0; ct < CPW; ++ct) vz[ct] = mma(A[ct][P], ones, vz[ct]);
+#pragma unroll
+      for (int dt = 0; dt < C::DVT; ++dt) {
+        const bf16x8 Bv = tr_chunk_swz<R::VROWCH>(Vr[buf], tok0, dt * 16);
+#pragma unroll
+        for (int ct = 0; ct < CPW; ++ct) vacc[ct][dt] = mma(A[ct][P], Bv, vacc[ct][dt]);
+      }
+    }
+  }
+
+  // partial (V~, Z) of this (split, token group)
+  const size_t pslot = ((size_t)bh * a.S + blockIdx.x) * C::TG + tg;
+  float* pv = a.partial + pslot * C::Kp * C::DV;
+  float* pz = a.partial_z + pslot * C::Kp;
+#pragma unroll
+  for (int ct = 0; ct < CPW; ++ct) {
+    const int comp0 = (cgi * CPW + ct) * 16;
+#pragma unroll
+    for (int dt = 0; dt < C::DVT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pv[(comp0 + 4 * g + i) * C::DV + dt * 16 + c] = vacc[ct][dt][i];
+    if (c == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pz[comp0 + 4 * g + i] = vz[ct][i];
+    }
+  }
+}
+
+// ============================================================================
 // Host-side dispatch.
 // ============================================================================
 template <class C>
@@ -673,14 +1195,32 @@ static hipError_t run_bidir(const Plan& p, const Tensors& t, hipStream_t s) {
   a.x = t.k;
   a.v = t.v;
   a.assign = t.assign_k;
+  // token-owner write: about one workgroup per compute unit, each at least four
+  // 32-key groups; its splits replace the plan's (the partial buffer holds
+  // S * TG >= this many slots per sequence)
+  int PS = C::kBF ? p.S : p.S * C::TG;          // partial slots per sequence
   if (g_launch_hook) g_launch_hook("gma_write", s, 1);
-  if constexpr (C::kBF) hipLaunchKernelGGL(gma_write_bf16_kernel<C>, grid, dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL(gma_write_kernel<C>, grid, dim3(kThreads), 0, s, a);
+  if constexpr (Write2<C>::kOK) {
+    const int64_t g32 = (p.N + 31) / 32;
+    int64_t s2 = (256 + p.BH - 1) / p.BH;
+    const int64_t cap = (g32 + 3) / 4;
+    if (s2 > cap) s2 = cap;
+    if (s2 > PS) s2 = PS;
+    if (s2 < 1) s2 = 1;
+    PS = (int)s2;
+    hipLaunchKernelGGL(gma_write2_kernel<C>, dim3((unsigned)s2, (unsigned)p.BH), dim3(256), 0, s, a);
+  } else if constexpr (Write3<C>::kOK) {
+    PS = p.S * C::TG;
+    hipLaunchKernelGGL(gma_write3_kernel<C>, grid, dim3(kThreads), 0, s, a);
+  } else if constexpr (C::kBF) {
+    hipLaunchKernelGGL(gma_write_bf16_kernel<C>, grid, dim3(kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(gma_write_kernel<C>, grid, dim3(kThreads), 0, s, a);
+  }
   if (g_launch_hook) g_launch_hook("gma_write", s, 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  const int PS = C::kBF ? p.S : p.S * C::TG;    // partial slots per sequence
   const int nred = C::Kp * C::DV + C::Kp;
   if (g_launch_hook) g_launch_hook("gma_reduce", s, 1);
   hipLaunchKernelGGL(gma_reduce_kernel, dim3((nred + 255) / 256, (unsigned)p.BH), dim3(256), 0, s,

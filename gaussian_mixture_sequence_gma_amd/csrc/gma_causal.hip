@@ -258,7 +258,7 @@ __global__ void __launch_bounds__(kThreads) gma_causal_kernel(CausalArgs a) {
         const int aq_ = __float_as_int(isq ? s4[q][3] : s4[q][2]);
         if (!found && s4[q][0] == M) { arg = aq_; found = true; }
       }
-      const float invL = 1.f / L;
+      const float invL = fast_rcp(L);
       float* fac = isq ? facQ : facK;
 #pragma unroll
       for (int q = 0; q < 4; ++q) fac[q * kTile + t] = fq[q] * invL;
@@ -386,7 +386,7 @@ __global__ void __launch_bounds__(kThreads) gma_causal_kernel(CausalArgs a) {
         // row 4g+i of the accumulator is query token tile_token(gt, 4g+i), whose
         // intra-chunk row sum sits in lane column 4g+i
         const float rs = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * g + i) << 2, __float_as_int(rowsum)));
-        rinv[i] = 1.f / (qd[i] + rs + a.eps);
+        rinv[i] = fast_rcp(qd[i] + rs + a.eps);
       }
 #pragma unroll
       for (int dt = 0; dt < C::DVT; ++dt)

@@ -81,15 +81,21 @@ __device__ __forceinline__ void st16(void* p, T v) {
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+// Hardware reciprocal (v_rcp_f32, about 1 ulp); the normalisers it inverts are
+// positive sums well inside the normal range.
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // ---- cross-lane reductions ------------------------------------------------
+// (The patterns used -- quad permutes and row mirrors -- read valid lanes
+// only, so bound_ctrl is immaterial; with it set the compiler can fold the
+// move into the consuming ALU instruction.)
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int v) {
-  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
 }
 // Butterfly over the 16 lanes of a DPP row; every lane receives the result
 // (each step pairs lanes symmetrically, so all lanes compute identical values).

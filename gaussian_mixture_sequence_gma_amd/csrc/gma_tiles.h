@@ -434,7 +434,7 @@ __global__ void __launch_bounds__(kThreads) gma_write_kernel(BidirArgs a) {
           L += fq[q] * st[q][1];
           if (!found && st[q][0] == M) { arg = __float_as_int(st[q][2]); found = true; }
         }
-        const float invL = 1.f / L;
+        const float invL = fast_rcp(L);
 #pragma unroll
         for (int q = 0; q < C::NG; ++q) fac[q * kTile + t] = fq[q] * invL;
         if (want_assign && t < nvalid) a.assign[(size_t)bh * a.N + tile0 + t] = arg;
@@ -450,7 +450,7 @@ __global__ void __launch_bounds__(kThreads) gma_write_kernel(BidirArgs a) {
 #pragma unroll
       for (int tt = 0; tt < C::TTW; ++tt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) f[tt][i] = 1.f / l[tt][i];
+        for (int i = 0; i < 4; ++i) f[tt][i] = fast_rcp(l[tt][i]);
       if (want_assign && c == 0) {
 #pragma unroll
         for (int tt = 0; tt < C::TTW; ++tt)
@@ -786,7 +786,7 @@ gma_write_bf16_kernel(BidirArgs a) {
         L += fq[q] * st[q][1];
         if (!found && st[q][0] == M) { arg = __float_as_int(st[q][3]); found = true; }
       }
-      const float invL = 1.f / L;
+      const float invL = fast_rcp(L);
 #pragma unroll
       for (int q = 0; q < C::NG; ++q) fac[q * kTile + t] = fq[q] * invL;
       if (want_assign && t < nvalid) a.assign[(size_t)bh * a.N + tile0 + t] = arg;
@@ -801,7 +801,7 @@ gma_write_bf16_kernel(BidirArgs a) {
       float fi;
       if constexpr (C::NG > 1) fi = fac[cgi * kTile + tok];
       else {
-        fi = 1.f / l[tt];
+        fi = fast_rcp(l[tt]);
         if (want_assign && g == 0 && tok < nvalid) a.assign[(size_t)bh * a.N + tile0 + tok] = am[tt];
       }
       fi = tok < nvalid ? fi : 0.f;
