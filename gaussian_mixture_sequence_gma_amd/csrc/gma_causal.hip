@@ -20,7 +20,7 @@
 // The scan kernel uses four component groups (K padded to >= 64) so that all
 // four waves see every token of a chunk and the running state is split over
 // the waves by component.
-#include "gma_tiles.h"
+#include "gma_owner.h"
 
 namespace gma {
 
@@ -449,6 +449,390 @@ __global__ void __launch_bounds__(kThreads) gma_causal_kernel(CausalArgs a) {
   }
 }
 
+// ============================================================================
+// Causal scan, bf16 inputs, token-owner form.  Wave w owns tokens 16w .. 16w+15
+// of every 64-token chunk, as queries and as keys, with all K_pad components:
+// both score tiles (D[component][token], rows in the pair_row order) share each
+// coefficient operand read from LDS, and the softmaxes stay inside the wave.
+// Per chunk the wave writes its normalised Gamma^K rows to LDS; after one
+// barrier it forms, for its 16 queries,
+//   num = e^Q S + sum_{j <= i in chunk} (e^Q . Gamma^K_j) v_j,
+//   den = e^Q z + sum_{j <= i} (e^Q . Gamma^K_j) + eps * sum_k e^Q_k
+// (e^Q = exp2(s - max), unnormalised: the ratio is the same), all on MFMA: the
+// carried state S, z is an LDS operand table (S^T in bf16 with rows Z_hi, Z_lo
+// and ones appended, as the bidirectional read-out uses V~), and the intra-
+// chunk affinity P = Gamma^K e^Q^T feeds V^T P straight from registers.  After
+// a second barrier each wave adds Gamma^K_c^T V_c to its quarter of S (fp32
+// registers) and rewrites its part of the table.
+// ============================================================================
+template <class C>
+struct Causal2 {
+  static constexpr int KP = C::Kp;
+  static constexpr int CT = KP / 16;
+  static constexpr int KS = KP / 32;
+  static constexpr int NKS = C::DRP / 32;
+  static constexpr int DVT = C::DV / 16;
+  static constexpr int OT = DVT + 1;
+  static constexpr int CTW = CT / 4;                       // state component tiles per wave
+  static constexpr int COEF = CT * NKS * 4;
+  static constexpr int GLD = KP % 128 == 64 ? KP + 8 : KP + 16;   // Gamma^K row stride
+  static constexpr int VROWCH = C::DV / 8;
+  static constexpr int VROUNDS = kTile * VROWCH / 64;      // 1 KB wave copies per V tile
+  static constexpr int VRPW = (VROUNDS + kWaves - 1) / kWaves;
+  static constexpr int STCH = OT * KS;
+  static constexpr int lds_bytes(int nb) {
+    return COEF * 1024 + KP * 4 + nb * kTile * GLD * 2 + nb * kTile * C::DV * 2 + STCH * 1024;
+  }
+  // Gamma^K and V tiles double-buffered when they fit (two barriers per chunk),
+  // else single-buffered with a third barrier after the state update
+  static constexpr int NB = lds_bytes(2) <= 160 * 1024 ? 2 : 1;
+  static constexpr bool kOK = C::kBF && KP % 64 == 0 && C::DRP <= 64 && C::DV >= 32 &&
+                              lds_bytes(NB) <= 160 * 1024;
+};
+
+template <class C>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+gma_causal2_kernel(CausalArgs a) {
+  using R = Causal2<C>;
+  __shared__ __attribute__((aligned(16))) bf16x8 coef[R::COEF * 64];
+  __shared__ __attribute__((aligned(16))) float cperm[R::KP];
+  __shared__ __attribute__((aligned(16))) bf16 G[R::NB][kTile * R::GLD];
+  __shared__ __attribute__((aligned(16))) bf16 Vb[R::NB][kTile * C::DV];
+  __shared__ __attribute__((aligned(16))) bf16 ST[R::STCH * 512];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int64_t bh = blockIdx.y;
+  const int h = (int)(bh % a.H);
+  const int span = blockIdx.x;
+  const int64_t t_begin = (int64_t)span * a.span_tiles * kTile;
+  const int64_t t_end = a.N < t_begin + (int64_t)a.span_tiles * kTile
+                            ? a.N : t_begin + (int64_t)a.span_tiles * kTile;
+  const int nchunks = t_end > t_begin ? (int)((t_end - t_begin + kTile - 1) / kTile) : 0;
+  const bool want_aq = a.assign_q != nullptr, want_ak = a.assign_k != nullptr;
+
+  // ---- tables, carried state -------------------------------------------------
+  {
+    const char* tb = a.params + (size_t)h * a.head_bytes + a.head_bytes / 2;
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(tb);
+    for (int idx = threadIdx.x; idx < R::COEF * 64; idx += kThreads) coef[idx] = src[idx];
+    const float* cp = reinterpret_cast<const float*>(tb + (size_t)8 * C::Kp * C::DRP);
+    for (int j = threadIdx.x; j < R::KP; j += kThreads) cperm[j] = cp[j];
+    // the (Z_hi, Z_lo, 1) block: the ones row and the zero rows are constant
+    // (rows 0 and 1 belong to write_st, which runs concurrently)
+    for (int idx = threadIdx.x; idx < R::KS * 64; idx += kThreads) {
+      const int r = idx & 15;
+      if (r < 2) continue;
+      bf16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (bf16)(r == 2 ? 1.0f : 0.0f);
+      reinterpret_cast<bf16x8*>(ST)[R::DVT * R::KS * 64 + idx] = v;
+    }
+  }
+  const size_t sslot = (size_t)bh * a.nspan + span;
+  f32x4 sacc[R::CTW][R::DVT], zacc[R::CTW];
+#pragma unroll
+  for (int j = 0; j < R::CTW; ++j) {
+    const int comp0 = (w * R::CTW + j) * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) zacc[j][i] = a.carry_z[sslot * C::Kp + comp0 + 4 * g + i];
+#pragma unroll
+    for (int dt = 0; dt < R::DVT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sacc[j][dt][i] = a.carry[(sslot * C::Kp + comp0 + 4 * g + i) * C::DV + dt * 16 + c];
+  }
+  // this wave's rows of the state table: S^T (d rows in pair_row order) and Z
+  auto write_st = [&]() {
+#pragma unroll
+    for (int j = 0; j < R::CTW; ++j) {
+      const int comp0 = (w * R::CTW + j) * 16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int comp = comp0 + 4 * g + i;
+        const int p = comp >> 5, gg = (comp & 31) >> 3, e = comp & 7;
+#pragma unroll
+        for (int dt = 0; dt < R::DVT; ++dt) {
+          const int d = dt * 16 + c;
+          ST[((pair_tile(d) * R::KS + p) * 64 + pair_rowof(d) + 16 * gg) * 8 + e] = to_bf16(sacc[j][dt][i]);
+        }
+        if (c < 2) {
+          const float zz = zacc[j][i];
+          const float zh = from_bf16(to_bf16(zz));
+          ST[((R::DVT * R::KS + p) * 64 + c + 16 * gg) * 8 + e] = to_bf16(c == 0 ? zz : zz - zh);
+        }
+      }
+    }
+  };
+  write_st();
+
+  const bf16* qs = reinterpret_cast<const bf16*>(a.q) + (size_t)bh * a.N * C::DR;
+  const bf16* ks = reinterpret_cast<const bf16*>(a.k) + (size_t)bh * a.N * C::DR;
+  const bf16* vs = reinterpret_cast<const bf16*>(a.v) + (size_t)bh * a.N * C::DV;
+  bf16x8 xq[R::NKS], xk[R::NKS];
+  auto load_x = [&](int k) {
+    const int64_t tok = t_begin + (int64_t)k * kTile + 16 * w + c;
+#pragma unroll
+    for (int s = 0; s < R::NKS; ++s) {
+      const int col = 32 * s + 8 * g;
+      const bool ok = tok < t_end && col < C::DR;
+      const size_t off = (size_t)(ok ? tok : t_begin) * C::DR + (ok ? col : 0);
+      const bf16x8 q = ld16<bf16x8>(qs + off), kk = ld16<bf16x8>(ks + off);
+      xq[s] = ok ? q : bf16x8{};
+      xk[s] = ok ? kk : bf16x8{};
+    }
+  };
+  auto load_v = [&](int k, int buf) {
+    const int64_t t0 = t_begin + (int64_t)k * kTile;
+    const int64_t rem = t_end - t0;
+    const int nv = (int)(rem < kTile ? rem : kTile);
+#pragma unroll
+    for (int j = 0; j < R::VRPW; ++j) {
+      const int round = w * R::VRPW + j;
+      if (round < R::VROUNDS) {
+        const int P = round * 64 + lane;
+        const int r = P / R::VROWCH, pc = P - r * R::VROWCH;
+        const int lc = pc ^ ((2 * r) & (R::VROWCH - 2));
+        const int rr = r < nv ? r : nv - 1;
+        global_to_lds16(vs + (size_t)(t0 + rr) * C::DV + lc * 8, &Vb[buf][round * 512]);
+      }
+    }
+  };
+  bf16x8 ones, ones_r3;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    ones[e] = (bf16)1.0f;
+    ones_r3[e] = (bf16)(c == 3 ? 1.0f : 0.0f);          // A operand: row 3 = 1
+  }
+  if (nchunks > 0) {
+    load_x(0);
+    load_v(0, 0);
+  }
+  __syncthreads();                       // coefficient table and seeds visible to every wave
+
+  for (int k = 0; k < nchunks; ++k) {
+    const int buf = R::NB == 2 ? (k & 1) : 0;
+    const int64_t tile0 = t_begin + (int64_t)k * kTile;
+    const int64_t rem = t_end - tile0;
+    const int nvalid = (int)(rem < kTile ? rem : kTile);
+    asm volatile("" ::: "memory");
+    // features of this wave's 16 queries and 16 keys
+    bf16x8 fq[R::NKS][3], fk[R::NKS][3];
+#pragma unroll
+    for (int s = 0; s < R::NKS; ++s) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bf16 hh, ll;
+        const float q = from_bf16(xq[s][e]);
+        split_bf16(q * q, hh, ll);
+        fq[s][0][e] = hh;
+        fq[s][1][e] = ll;
+        const float kf = from_bf16(xk[s][e]);
+        split_bf16(kf * kf, hh, ll);
+        fk[s][0][e] = hh;
+        fk[s][1][e] = ll;
+      }
+      fq[s][2] = xq[s];
+      fk[s][2] = xk[s];
+    }
+    // scores: each coefficient operand serves the query and the key tile
+    f32x4 SQ[R::CT], SK[R::CT];
+#pragma unroll
+    for (int ct = 0; ct < R::CT; ++ct) {
+      const f32x4 cs = *reinterpret_cast<const f32x4*>(&cperm[ct * 16 + 4 * g]);
+      SQ[ct] = cs;
+      SK[ct] = cs;
+    }
+    {
+      constexpr int WI[5] = {0, 0, 1, 2, 3};
+      constexpr int FI[5] = {0, 1, 0, 2, 2};
+      constexpr int NSTEP = R::CT / 2 * R::NKS;
+      auto load_w = [&](int j, bf16x8 (&wv)[2][4]) {
+        const int cp = 2 * (j / R::NKS), s = j % R::NKS;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int ar = 0; ar < 4; ++ar) wv[u][ar] = coef[(((cp + u) * R::NKS + s) * 4 + ar) * 64 + lane];
+      };
+      bf16x8 wbuf[2][2][4];
+      load_w(0, wbuf[0]);
+#pragma unroll
+      for (int j = 0; j < NSTEP; ++j) {
+        if (j + 1 < NSTEP) load_w(j + 1, wbuf[(j + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        const int cp = 2 * (j / R::NKS), s = j % R::NKS;
+#pragma unroll
+        for (int q = 0; q < 5; ++q)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            SQ[cp + u] = mma(wbuf[j & 1][u][WI[q]], fq[s][FI[q]], SQ[cp + u]);
+            SK[cp + u] = mma(wbuf[j & 1][u][WI[q]], fk[s][FI[q]], SK[cp + u]);
+          }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // queries: e = exp2(s - max), packed as the B operand of the contractions
+    // over components; keys: normalised responsibilities -> G
+    const int qi = 16 * w + c;                      // this lane's query (and key) in the chunk
+    bf16x8 Eq[R::KS];
+    {
+      float v = SQ[0][0];
+#pragma unroll
+      for (int ct = 0; ct < R::CT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v = fmaxf(v, SQ[ct][i]);
+      const float m = groups_max(v);
+#pragma unroll
+      for (int p = 0; p < R::KS; ++p)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          Eq[p][i] = to_bf16(exp2_fast(SQ[2 * p][i] - m));
+          Eq[p][4 + i] = to_bf16(exp2_fast(SQ[2 * p + 1][i] - m));
+        }
+      if (want_aq) {
+        float bv = SQ[0][0];
+        int bi = pair_row(0, 4 * g);
+#pragma unroll
+        for (int ct = 0; ct < R::CT; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) argmax_merge(bv, bi, SQ[ct][i], pair_row(ct, 4 * g + i));
+        groups_argmax(bv, bi);
+        if (g == 0 && qi < nvalid) a.assign_q[(size_t)bh * a.N + tile0 + qi] = bi;
+      }
+    }
+    {
+      float v = SK[0][0];
+#pragma unroll
+      for (int ct = 0; ct < R::CT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v = fmaxf(v, SK[ct][i]);
+      const float m = groups_max(v);
+      float l = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < R::CT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = exp2_fast(SK[ct][i] - m);
+          SK[ct][i] = e;
+          l += e;
+        }
+      l = groups_sum(l);
+      const float inv = qi < nvalid ? fast_rcp(l) : 0.f;
+      bf16* grow_ = &G[buf][qi * R::GLD + 8 * g];
+#pragma unroll
+      for (int p = 0; p < R::KS; ++p) {
+        bf16x8 v8;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v8[i] = to_bf16(SK[2 * p][i] * inv);
+          v8[4 + i] = to_bf16(SK[2 * p + 1][i] * inv);
+        }
+        st16(grow_ + 32 * p, v8);
+      }
+      if (want_ak) {
+        float bv = SK[0][0];
+        int bi = pair_row(0, 4 * g);
+#pragma unroll
+        for (int ct = 0; ct < R::CT; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) argmax_merge(bv, bi, SK[ct][i], pair_row(ct, 4 * g + i));
+        groups_argmax(bv, bi);
+        if (g == 0 && qi < nvalid) a.assign_k[(size_t)bh * a.N + tile0 + qi] = bi;
+      }
+    }
+    wait_global_loads();                 // V(k) and this wave's loads
+    lds_barrier();                                                    // B1
+    if (k + 1 < nchunks) {
+      if constexpr (R::NB == 2) load_v(k + 1, buf ^ 1);
+      load_x(k + 1);
+    }
+
+    // ---- outputs of this wave's 16 queries ------------------------------------
+    f32x4 acc[R::OT];
+#pragma unroll
+    for (int dt = 0; dt < R::OT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < R::KS; ++p)
+#pragma unroll
+      for (int dt = 0; dt < R::OT; ++dt)
+        acc[dt] = mma(reinterpret_cast<const bf16x8*>(ST)[(dt * R::KS + p) * 64 + lane], Eq[p], acc[dt]);
+    // intra-chunk: key pairs (32 keys; rows of key tile jt in tile_token order,
+    // so a pair covers keys 32pp .. 32pp + 31) up to the one holding this wave's
+    // queries, which is masked to keys <= query
+    for (int pp = 0; pp <= (w >> 1); ++pp) {
+      f32x4 P[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int jt = 2 * pp + b;
+        P[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const bf16* gr = &G[buf][tile_token(jt, c) * R::GLD + 8 * g];
+#pragma unroll
+        for (int p = 0; p < R::KS; ++p) P[b] = mma(ld16<bf16x8>(gr + 32 * p), Eq[p], P[b]);
+        if (pp == (w >> 1)) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (tile_token(jt, 4 * g + i) > qi) P[b][i] = 0.f;
+        }
+      }
+      bf16x8 Pc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        Pc[i] = to_bf16(P[0][i]);
+        Pc[4 + i] = to_bf16(P[1][i]);
+      }
+      // V^T chunk with rows in pair_row order: source lane s reads block
+      // pair_row(dt, 4 (s % 4))
+      const int a4 = lane & 3;
+#pragma unroll
+      for (int dt = 0; dt < R::DVT; ++dt) {
+        const bf16x8 Av = tr_chunk_swz_blk<R::VROWCH>(Vb[buf], 32 * pp, pair_row(dt, 4 * a4));
+        acc[dt] = mma(Av, Pc, acc[dt]);
+      }
+      acc[R::DVT] = mma(ones_r3, Pc, acc[R::DVT]);
+    }
+    {
+      const f32x4 dz = acc[R::DVT];
+      float r = fast_rcp(dz[0] + dz[1] + dz[3] + a.eps * dz[2]);
+      float r0, r1;
+      pair_xor16(r, r0, r1);
+      pair_xor32(r0, r, r1);
+      if (qi < nvalid) {
+        bf16* orow = reinterpret_cast<bf16*>(a.out) + ((size_t)bh * a.N + tile0 + qi) * C::DV;
+#pragma unroll
+        for (int qd = 0; qd < R::DVT / 2; ++qd) {
+          bf16x8 o8;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            o8[i] = to_bf16(acc[2 * qd][i] * r);
+            o8[4 + i] = to_bf16(acc[2 * qd + 1][i] * r);
+          }
+          st16(orow + 32 * qd + 8 * g, o8);
+        }
+      }
+    }
+    lds_barrier();                                                    // B2
+
+    // ---- state update on this wave's components: S += Gamma^K^T V, z += Gamma^K^T 1
+#pragma unroll
+    for (int P2 = 0; P2 < 2; ++P2) {
+#pragma unroll
+      for (int j = 0; j < R::CTW; ++j) {
+        const bf16x8 Ag = tr_chunk(G[buf], R::GLD, 32 * P2, (w * R::CTW + j) * 16);
+        zacc[j] = mma(Ag, ones, zacc[j]);
+#pragma unroll
+        for (int dt = 0; dt < R::DVT; ++dt)
+          sacc[j][dt] = mma(Ag, tr_chunk_swz<R::VROWCH>(Vb[buf], 32 * P2, dt * 16), sacc[j][dt]);
+      }
+    }
+    write_st();
+    if constexpr (R::NB == 1) {
+      lds_barrier();                                                  // B3: G, V free
+      if (k + 1 < nchunks) load_v(k + 1, 0);
+    }
+  }
+}
+
 template <class C>
 static hipError_t run_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   if constexpr (causal_lds_bytes(C::kBF, C::DR, C::DV, C::Kp) > kMaxLds) {
@@ -470,8 +854,17 @@ static hipError_t run_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   wa.assign = nullptr;
   const dim3 grid(p.nspan, (unsigned)p.BH);
   if (g_launch_hook) g_launch_hook("gma_span_state", s, 1);
-  if constexpr (C::kBF) hipLaunchKernelGGL(gma_write_bf16_kernel<C>, grid, dim3(kThreads), 0, s, wa);
-  else hipLaunchKernelGGL(gma_write_kernel<C>, grid, dim3(kThreads), 0, s, wa);
+  // the token-owner write pays a per-workgroup set-up: use it for long spans
+  // (at least eight 32-token steps per wave), one split per span
+  if (Write2<C>::kOK && p.span_tiles >= 16) {
+    wa.gpw = 2 * p.span_tiles;
+    if constexpr (Write2<C>::kOK)
+      hipLaunchKernelGGL(gma_write2_kernel<C>, grid, dim3(256), 0, s, wa);
+  } else if constexpr (C::kBF) {
+    hipLaunchKernelGGL(gma_write_bf16_kernel<C>, grid, dim3(kThreads), 0, s, wa);
+  } else {
+    hipLaunchKernelGGL(gma_write_kernel<C>, grid, dim3(kThreads), 0, s, wa);
+  }
   if (g_launch_hook) g_launch_hook("gma_span_state", s, 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -506,7 +899,8 @@ static hipError_t run_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   ca.eps = t.eps;
   ca.out_bf = p.out_bf ? 1 : 0;
   if (g_launch_hook) g_launch_hook("gma_causal", s, 1);
-  hipLaunchKernelGGL(gma_causal_kernel<C>, grid, dim3(kThreads), 0, s, ca);
+  if constexpr (Causal2<C>::kOK) hipLaunchKernelGGL(gma_causal2_kernel<C>, grid, dim3(kThreads), 0, s, ca);
+  else hipLaunchKernelGGL(gma_causal_kernel<C>, grid, dim3(kThreads), 0, s, ca);
   if (g_launch_hook) g_launch_hook("gma_causal", s, 0);
   return hipGetLastError();
   }

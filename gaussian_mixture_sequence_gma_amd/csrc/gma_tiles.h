@@ -88,6 +88,7 @@ struct BidirArgs {
   int K;
   int S;
   int tiles_per_split;
+  int gpw;                // token-owner write: 32-token groups per split (0: derived)
   float eps;
   int out_bf;
 };

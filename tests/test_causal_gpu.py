@@ -26,6 +26,16 @@ def test_lm_causal_bf16_full():
     run_and_compare(W["lm_causal_bf16"])
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_causal_several_chunks_per_span(dtype, seed):
+    # B*H = 48 at N = 2048 gives spans of two 64-token chunks: the carried state
+    # entering a span and the in-span update both matter (and the kernel's
+    # start-of-span set-up runs concurrently with other waves' first chunk)
+    w = W["lm_causal_bf16"].with_(N=2048, dtype=dtype)
+    run_and_compare(w, seed=seed, heads=3)
+
+
 def test_long_context_causal_bf16_heads_subset():
     w = W["long_bidir_bf16"].with_(causal=True)
     run_and_compare(w, rows=inputs.sample_rows(w.N, 512, seed=7), heads=4)
