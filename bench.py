@@ -42,19 +42,21 @@ def kernel_flops(name: str, w) -> int:
     return 0
 
 
-def kernel_bytes(name: str, w, s_in: int, s_out: int) -> int:
-    """Algorithmic HBM bytes of one launch of `name` on workload w (s_in: element
-    size of the routing vectors and values the GMA kernels read)."""
+def kernel_bytes(name: str, w, s_r: int, s_v: int, s_out: int) -> int:
+    """Algorithmic HBM bytes of one launch of `name` on workload w: s_r, s_v are
+    the bytes per element of the routing vectors and values the GMA kernels
+    read (a split routing vector is a bf16 pair, 4 bytes), s_out of O.  The
+    layer's projection writes Q_X, K_X, V_X in the form the GMA kernels read."""
     T = w.B * w.H * w.N
     if name == "gma_proj":
         return 2 * (w.B * w.N * w.d_model + w.d_model * w.H * (2 * w.d_r + w.d_v)) + \
-            4 * T * (2 * w.d_r + w.d_v)
-    if name == "gma_write":
-        return T * (w.d_r + w.d_v) * s_in
+            T * (2 * w.d_r * s_r + w.d_v * s_v)
+    if name in ("gma_write", "gma_span_state"):
+        return T * (w.d_r * s_r + w.d_v * s_v)
     if name == "gma_read":
-        return T * (w.d_r * s_in + w.d_v * s_out)
+        return T * (w.d_r * s_r + w.d_v * s_out)
     if name == "gma_causal":
-        return T * ((2 * w.d_r + w.d_v) * s_in + w.d_v * s_out)
+        return T * (2 * w.d_r * s_r + w.d_v * s_v + w.d_v * s_out)
     return 0
 
 
@@ -171,7 +173,7 @@ def main():
     dev = torch.device("cuda:0")
     gen = inputs.generate(w, 0)
     s_out = 2 if w.dtype == "bf16" else 4
-    s_in = 4 if w.d_model > 0 else s_out      # the layer's GMA kernels read fp32 projections
+    s_r = s_v = s_out
 
     if w.d_model > 0:
         X = api.host_tensor_to_device(gen["X"], dev)
@@ -192,6 +194,10 @@ def main():
                              w.chunk)
     if w.d_model > 0:
         nbytes = binding.gma_layer_workspace_bytes(dims, w.d_model, int(w.causal))
+        # the projections reach the GMA kernels as bf16 pairs (Q_X, K_X) and
+        # bf16 (V_X), or all in fp32
+        fmt, _ = binding.gma_layer_projection_layout(dims, w.d_model, int(w.causal))
+        s_r, s_v = (4, 2) if fmt == binding.GMA_PROJ_SPLIT_BF16 else (4, 4)
     else:
         nbytes = binding.gma_forward_workspace_bytes(dims, int(w.causal))
     ws = api.alloc_workspace(nbytes, dev)
@@ -225,7 +231,7 @@ def main():
 
     kernels = {name: {"launches": n, "avg_us": 1e3 * tot / max(n, 1)} for name, n, tot in kt}
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
-    dom_bytes = kernel_bytes(dom, w, s_in, s_out)
+    dom_bytes = kernel_bytes(dom, w, s_r, s_v, s_out)
     dom_flops = kernel_flops(dom, w)
     traffic = traffic_from_profile(dom, w.name, kernel_source_hash())
     t_dom = kernels[dom]["avg_us"] * 1e-6
@@ -240,7 +246,7 @@ def main():
         roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
                     "traffic": traffic, "alg_bytes_per_launch": dom_bytes}
-    step_bytes = sum(kernel_bytes(k, w, s_in, s_out) for k in kernels)
+    step_bytes = sum(kernel_bytes(k, w, s_r, s_v, s_out) for k in kernels)
 
     cpu = None
     if not args.no_cpu_baseline:

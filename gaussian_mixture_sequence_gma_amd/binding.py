@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libgma.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "gma.h")
 
 GMA_F32, GMA_BF16 = 0, 1
+GMA_PROJ_F32, GMA_PROJ_SPLIT_BF16 = 0, 1
 GMA_OK, GMA_ERR_INVALID_ARG, GMA_ERR_UNSUPPORTED, GMA_ERR_WORKSPACE, GMA_ERR_HIP = range(5)
 
 
@@ -59,6 +60,9 @@ def load():
     lib.gma_layer_workspace_bytes.argtypes = [D, ctypes.c_int32, i32, ctypes.POINTER(S)]
     lib.gma_layer_forward.argtypes = [P, P, P, P, ctypes.c_int32, P, P, P, f32, i32, P, D, P, P,
                                       P, S, P]
+    lib.gma_layer_projection_layout.argtypes = [D, ctypes.c_int32, i32,
+                                                ctypes.POINTER(ctypes.c_int32),
+                                                ctypes.POINTER(S * 5)]
     lib.gma_responsibilities.argtypes = [P, P, P, P, D, P, P, P, S, P]
     lib.gma_status_string.argtypes = [i32]
     lib.gma_status_string.restype = ctypes.c_char_p
@@ -68,7 +72,8 @@ def load():
     lib.gma_timing_collect.argtypes = [ctypes.POINTER(gma_kernel_time), i32,
                                        ctypes.POINTER(ctypes.c_int)]
     for fn in ("gma_validate", "gma_forward_workspace_bytes", "gma_forward",
-               "gma_layer_workspace_bytes", "gma_layer_forward", "gma_responsibilities",
+               "gma_layer_workspace_bytes", "gma_layer_forward", "gma_layer_projection_layout",
+               "gma_responsibilities",
                "gma_timing_enable", "gma_timing_collect"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -146,6 +151,15 @@ def gma_layer_forward(X, W_Q, W_K, W_V, d_model, mu, log_sigma2, log_pi, eps, ca
                                     int(causal), _ptr(out), ctypes.byref(dims), _ptr(assign_q),
                                     _ptr(assign_k), _ptr(workspace), int(workspace_bytes),
                                     _stream(stream)))
+
+
+def gma_layer_projection_layout(dims: gma_dims, d_model: int, causal: int):
+    """(format, offsets): a GMA_PROJ_* code and the five byte offsets."""
+    fmt = ctypes.c_int32(0)
+    offs = (ctypes.c_size_t * 5)()
+    _check(load().gma_layer_projection_layout(ctypes.byref(dims), int(d_model), int(causal),
+                                              ctypes.byref(fmt), ctypes.byref(offs)))
+    return fmt.value, list(offs)
 
 
 def gma_responsibilities(X_r, mu, log_sigma2, log_pi, dims: gma_dims, gamma=None, assign=None,

@@ -236,16 +236,74 @@ int gma_forward(const void* Q_X, const void* K_X, const void* V_X, const float* 
   return forward_impl(p, t, causal, static_cast<hipStream_t>(stream));
 }
 
+// The layer's plan and where its projections sit.  Where the bf16 kernels
+// take split routing vectors for this shape, the projection epilogue writes
+// Q_X and K_X as bf16 pairs (16 significant bits) and V_X in bf16, and the
+// bf16 GMA kernels run on them; otherwise the projections stay fp32 and feed
+// the fp32 GMA path.
+struct LayerPlan {
+  Plan p;
+  int split = 0;
+  size_t gma_bytes = 0;
+  size_t off[5] = {0, 0, 0, 0, 0};   // from the start of the workspace
+  size_t total = 0;
+};
+
+static int layer_plan(const gma_dims* d, int32_t d_model, int causal, LayerPlan& L) {
+  if (d->dtype != GMA_BF16) return fail(GMA_ERR_UNSUPPORTED, "the projection layer takes bf16 X and W");
+  if (d_model < 64 || d_model > 8192 || d_model % 64)
+    return fail(GMA_ERR_UNSUPPORTED, "d_model must be a multiple of 64 in 64..8192");
+  int st = make_plan(d, causal, false, L.p);
+  L.split = st == GMA_OK && (causal ? causal_split_ok(L.p) : bidir_split_ok(L.p));
+  if (!L.split) {
+    st = make_plan(d, causal, true, L.p);
+    if (st != GMA_OK) return st;
+  }
+  t_err.clear();
+  const Plan& p = L.p;
+  L.gma_bytes = round256(p.total);
+  size_t off = L.gma_bytes;
+  const size_t nr = (size_t)p.BH * p.N * p.DR, nv = (size_t)p.BH * p.N * p.DV;
+  if (L.split) {
+    for (int m = 0; m < 4; ++m) {
+      L.off[m] = off;
+      off += round256(2 * nr);
+    }
+    L.off[4] = off;
+    off += round256(2 * nv);
+  } else {
+    L.off[0] = off;
+    L.off[1] = off + 4 * nr;
+    L.off[2] = off + 8 * nr;
+    off += round256(4 * (2 * nr + nv));
+  }
+  L.total = off;
+  return GMA_OK;
+}
+
 int gma_layer_workspace_bytes(const gma_dims* d, int32_t d_model, int causal, size_t* bytes) {
   t_err.clear();
   if (!bytes) return fail(GMA_ERR_INVALID_ARG, "bytes is NULL");
-  Plan p;
-  int st = make_plan(d, causal, true, p);
+  int st = check_dims(d, 0.f, causal);
   if (st != GMA_OK) return st;
-  if (d_model < 64 || d_model > 8192 || d_model % 64)
-    return fail(GMA_ERR_UNSUPPORTED, "d_model must be a multiple of 64 in 64..8192");
-  const size_t proj = round256((size_t)p.BH * p.N * (2 * p.DR + p.DV) * 4);
-  *bytes = round256(p.total) + proj;
+  LayerPlan L;
+  st = layer_plan(d, d_model, causal, L);
+  if (st != GMA_OK) return st;
+  *bytes = L.total;
+  return GMA_OK;
+}
+
+int gma_layer_projection_layout(const gma_dims* d, int32_t d_model, int causal, int32_t* format,
+                                size_t offsets[5]) {
+  t_err.clear();
+  if (!format || !offsets) return fail(GMA_ERR_INVALID_ARG, "format or offsets is NULL");
+  int st = check_dims(d, 0.f, causal);
+  if (st != GMA_OK) return st;
+  LayerPlan L;
+  st = layer_plan(d, d_model, causal, L);
+  if (st != GMA_OK) return st;
+  *format = L.split ? GMA_PROJ_SPLIT_BF16 : GMA_PROJ_F32;
+  for (int m = 0; m < 5; ++m) offsets[m] = L.off[m];
   return GMA_OK;
 }
 
@@ -257,35 +315,40 @@ int gma_layer_forward(const void* X, const void* W_Q, const void* W_K, const voi
   t_err.clear();
   int st = check_dims(d, eps, causal);
   if (st != GMA_OK) return st;
-  if (d->dtype != GMA_BF16) return fail(GMA_ERR_UNSUPPORTED, "the projection layer takes bf16 X and W");
-  if (d_model < 64 || d_model > 8192 || d_model % 64)
-    return fail(GMA_ERR_UNSUPPORTED, "d_model must be a multiple of 64 in 64..8192");
   if (!X || !W_Q || !W_K || !W_V || !mu || !log_sigma2 || !log_pi || !out || !workspace)
     return fail(GMA_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned16(X) || !aligned16(W_Q) || !aligned16(W_K) || !aligned16(W_V) || !aligned16(out) ||
       !aligned16(workspace) || !aligned16(mu) || !aligned16(log_sigma2) ||
       ((uintptr_t)log_pi & 3) || ((uintptr_t)assign_q & 3) || ((uintptr_t)assign_k & 3))
     return fail(GMA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
-  Plan p;
-  st = make_plan(d, causal, true, p);
+  LayerPlan L;
+  st = layer_plan(d, d_model, causal, L);
   if (st != GMA_OK) return st;
-  const size_t gma_bytes = round256(p.total);
-  const size_t proj = round256((size_t)p.BH * p.N * (2 * p.DR + p.DV) * 4);
-  if (workspace_bytes < gma_bytes + proj) return fail(GMA_ERR_WORKSPACE, "workspace too small");
+  const Plan& p = L.p;
+  if (workspace_bytes < L.total) return fail(GMA_ERR_WORKSPACE, "workspace too small");
   char* ws = static_cast<char*>(workspace);
-  float* q = reinterpret_cast<float*>(ws + gma_bytes);
-  float* k = q + (size_t)p.BH * p.N * p.DR;
-  float* v = k + (size_t)p.BH * p.N * p.DR;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const void* const W[3] = {W_Q, W_K, W_V};
-  float* const P[3] = {q, k, v};
-  hipError_t e = launch_proj(X, W, P, p.B, p.N, (int)p.H, d_model, p.DR, p.DV, s);
+  void* P[3];
+  void* lo[2] = {nullptr, nullptr};
+  if (L.split) {
+    P[0] = ws + L.off[0];
+    lo[0] = ws + L.off[1];
+    P[1] = ws + L.off[2];
+    lo[1] = ws + L.off[3];
+    P[2] = ws + L.off[4];
+  } else {
+    for (int m = 0; m < 3; ++m) P[m] = ws + L.off[m];
+  }
+  hipError_t e = launch_proj(X, W, P, lo, L.split, p.B, p.N, (int)p.H, d_model, p.DR, p.DV, s);
   st = finish_launch(e, "projection launch");
   if (st != GMA_OK) return st;
   Tensors t;
-  t.q = q;
-  t.k = k;
-  t.v = v;
+  t.q = P[0];
+  t.k = P[1];
+  t.v = P[2];
+  t.q_lo = lo[0];
+  t.k_lo = lo[1];
   t.mu = mu;
   t.ls2 = log_sigma2;
   t.lpi = log_pi;

@@ -444,7 +444,7 @@ struct Read2 {
   static constexpr bool kOK = C::kBF && C::Kp % 32 == 0 && C::DRP <= 64 && LDS <= 150 * 1024;
 };
 
-template <class C>
+template <class C, bool XS>
 __global__ void __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gma_read2_kernel(BidirArgs a) {
   using R = Read2<C>;
@@ -481,7 +481,8 @@ gma_read2_kernel(BidirArgs a) {
 
   // lane (c, g) of query tile tt holds query tok0 + 16 tt + c, routing columns
   // 32 s + 8 g .. + 7
-  bf16x8 xr[2][R::NKS];
+  const bf16* xls = XS ? reinterpret_cast<const bf16*>(a.x_lo) + (size_t)bh * a.N * C::DR : xs;
+  bf16x8 xr[2][R::NKS], xl[2][R::NKS];
   auto load_x = [&](int64_t grp) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -489,8 +490,13 @@ gma_read2_kernel(BidirArgs a) {
 #pragma unroll
       for (int s = 0; s < R::NKS; ++s) {
         const int col = 32 * s + 8 * g;
-        if (tok < a.N && col < C::DR) xr[tt][s] = ld16<bf16x8>(xs + (size_t)tok * C::DR + col);
-        else xr[tt][s] = bf16x8{};
+        if (tok < a.N && col < C::DR) {
+          xr[tt][s] = ld16<bf16x8>(xs + (size_t)tok * C::DR + col);
+          if constexpr (XS) xl[tt][s] = ld16<bf16x8>(xls + (size_t)tok * C::DR + col);
+        } else {
+          xr[tt][s] = bf16x8{};
+          if constexpr (XS) xl[tt][s] = bf16x8{};
+        }
       }
     }
   };
@@ -500,22 +506,12 @@ gma_read2_kernel(BidirArgs a) {
     // the tables are loop-invariant: keep the compiler from hoisting all of
     // their reads (far more registers than a wave has) out of the loop
     asm volatile("" ::: "memory");
-    // features (x^2 hi, x^2 lo, x) of both query tiles
-    bf16x8 f[2][R::NKS][3];
+    // features of both query tiles
+    bf16x8 f[2][R::NKS][NFX<XS>];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int s = 0; s < R::NKS; ++s) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float xf = from_bf16(xr[tt][s][e]);
-          bf16 hh, ll;
-          split_bf16(xf * xf, hh, ll);
-          f[tt][s][0][e] = hh;
-          f[tt][s][1][e] = ll;
-        }
-        f[tt][s][2] = xr[tt][s];
-      }
+      for (int s = 0; s < R::NKS; ++s) make_features<XS>(xr[tt][s], xl[tt][s], f[tt][s]);
 
     // scores, two component tiles at a time (four independent accumulators)
     f32x4 S[2][R::CT];
@@ -525,8 +521,6 @@ gma_read2_kernel(BidirArgs a) {
       S[0][ct] = cs;
       S[1][ct] = cs;
     }
-    constexpr int WI[5] = {0, 0, 1, 2, 3};   // A_hi, A_hi, A_lo, B_hi, B_lo
-    constexpr int FI[5] = {0, 1, 0, 2, 2};   // x^2_hi, x^2_lo, x^2_hi, x, x
     // steps j = (tile pair, routing chunk); the operands of step j + 1 are read
     // from LDS while the 20 MFMAs of step j run
     constexpr int NSTEP = R::CT / 2 * R::NKS;
@@ -546,12 +540,12 @@ gma_read2_kernel(BidirArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       const int cp = 2 * (j / R::NKS), s = j % R::NKS;
 #pragma unroll
-      for (int q = 0; q < 5; ++q)
+      for (int q = 0; q < NQX<XS>; ++q)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int u = 0; u < 2; ++u)
-            S[tt][cp + u] = mma(wbuf[j & 1][u][WI[q]], f[tt][s][FI[q]], S[tt][cp + u]);
+            S[tt][cp + u] = mma(wbuf[j & 1][u][kWI[q]], f[tt][s][kFI[q]], S[tt][cp + u]);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (grp + NW < ge) load_x(grp + NW);
@@ -900,13 +894,17 @@ static hipError_t run_bidir(const Plan& p, const Tensors& t, hipStream_t s) {
   a.out_bf = p.out_bf ? 1 : 0;
   const dim3 grid(p.S, (unsigned)p.BH);
 
+  const bool split = t.k_lo != nullptr;
   a.x = t.k;
+  a.x_lo = t.k_lo;
   a.v = t.v;
   a.assign = t.assign_k;
   // token-owner write: about one workgroup per compute unit, each at least four
   // 32-key groups; its splits replace the plan's (the partial buffer holds
-  // S * TG >= this many slots per sequence)
+  // S * TG >= this many slots per sequence).  Split routing vectors (the
+  // layer's projections) run only on the token-owner kernels.
   int PS = C::kBF ? p.S : p.S * C::TG;          // partial slots per sequence
+  if (split && !(Write2<C>::kOK && Read2<C>::kOK)) return hipErrorNotSupported;
   if (g_launch_hook) g_launch_hook("gma_write", s, 1);
   if constexpr (Write2<C>::kOK) {
     const int64_t g32 = (p.N + 31) / 32;
@@ -916,7 +914,9 @@ static hipError_t run_bidir(const Plan& p, const Tensors& t, hipStream_t s) {
     if (s2 > PS) s2 = PS;
     if (s2 < 1) s2 = 1;
     PS = (int)s2;
-    hipLaunchKernelGGL(gma_write2_kernel<C>, dim3((unsigned)s2, (unsigned)p.BH), dim3(256), 0, s, a);
+    const dim3 g2((unsigned)s2, (unsigned)p.BH);
+    if (split) hipLaunchKernelGGL((gma_write2_kernel<C, true>), g2, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((gma_write2_kernel<C, false>), g2, dim3(256), 0, s, a);
   } else if constexpr (Write3<C>::kOK) {
     PS = p.S * C::TG;
     hipLaunchKernelGGL(gma_write3_kernel<C>, grid, dim3(kThreads), 0, s, a);
@@ -941,6 +941,7 @@ static hipError_t run_bidir(const Plan& p, const Tensors& t, hipStream_t s) {
   if (e != hipSuccess) return e;
 
   a.x = t.q;
+  a.x_lo = t.q_lo;
   a.v = nullptr;
   a.out = t.out;
   a.assign = t.assign_q;
@@ -952,7 +953,10 @@ static hipError_t run_bidir(const Plan& p, const Tensors& t, hipStream_t s) {
     const int64_t cap = (g32 + 7) / 8;
     if (s2 > cap) s2 = cap;
     if (s2 < 1) s2 = 1;
-    hipLaunchKernelGGL(gma_read2_kernel<C>, dim3((unsigned)s2, (unsigned)p.BH), dim3(512), 0, s, a);
+    if (split)
+      hipLaunchKernelGGL((gma_read2_kernel<C, true>), dim3((unsigned)s2, (unsigned)p.BH), dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((gma_read2_kernel<C, false>), dim3((unsigned)s2, (unsigned)p.BH), dim3(512), 0, s, a);
   } else {
     hipLaunchKernelGGL((gma_read_kernel<C, 0>), grid, dim3(kThreads), 0, s, a);
   }
@@ -1018,6 +1022,20 @@ hipError_t launch_prologue(const Plan& p, const Tensors& t, hipStream_t s) {
     case 8: GMA_DR_CASES(FN, BF, 2, 4)                                      \
   }                                                                         \
   break;
+
+template <class C>
+static hipError_t split_query(const Plan&, const Tensors&, hipStream_t) {
+  return Read2<C>::kOK && Write2<C>::kOK ? hipSuccess : hipErrorNotSupported;
+}
+
+static hipError_t split_query_all(const Plan& p, const Tensors& t, hipStream_t s) {
+  switch (0) { default: GMA_GROUP_CASES(split_query, true) }
+  return hipErrorNotSupported;
+}
+
+bool bidir_split_ok(const Plan& p) {
+  return p.bf && split_query_all(p, Tensors{}, nullptr) == hipSuccess;
+}
 
 hipError_t launch_bidir(const Plan& p, const Tensors& t, hipStream_t s) {
   if (p.bf) {

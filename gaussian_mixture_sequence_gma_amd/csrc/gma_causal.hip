@@ -41,6 +41,8 @@ struct CausalArgs {
   int span_tiles;
   float eps;
   int out_bf;
+  const void* q_lo;       // split routing vectors: low bf16 parts, or null
+  const void* k_lo;
 };
 
 // Exclusive prefix over spans, fixed order: carry[s] = sum_{s' < s} state[s'].
@@ -490,7 +492,7 @@ struct Causal2 {
                               lds_bytes(NB) <= 160 * 1024;
 };
 
-template <class C>
+template <class C, bool XS>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 gma_causal2_kernel(CausalArgs a) {
   using R = Causal2<C>;
@@ -569,7 +571,9 @@ gma_causal2_kernel(CausalArgs a) {
   const bf16* qs = reinterpret_cast<const bf16*>(a.q) + (size_t)bh * a.N * C::DR;
   const bf16* ks = reinterpret_cast<const bf16*>(a.k) + (size_t)bh * a.N * C::DR;
   const bf16* vs = reinterpret_cast<const bf16*>(a.v) + (size_t)bh * a.N * C::DV;
-  bf16x8 xq[R::NKS], xk[R::NKS];
+  const bf16* qls = XS ? reinterpret_cast<const bf16*>(a.q_lo) + (size_t)bh * a.N * C::DR : qs;
+  const bf16* kls = XS ? reinterpret_cast<const bf16*>(a.k_lo) + (size_t)bh * a.N * C::DR : ks;
+  bf16x8 xq[R::NKS], xk[R::NKS], xql[R::NKS], xkl[R::NKS];
   auto load_x = [&](int k) {
     const int64_t tok = t_begin + (int64_t)k * kTile + 16 * w + c;
 #pragma unroll
@@ -580,6 +584,11 @@ gma_causal2_kernel(CausalArgs a) {
       const bf16x8 q = ld16<bf16x8>(qs + off), kk = ld16<bf16x8>(ks + off);
       xq[s] = ok ? q : bf16x8{};
       xk[s] = ok ? kk : bf16x8{};
+      if constexpr (XS) {
+        const bf16x8 ql = ld16<bf16x8>(qls + off), kl = ld16<bf16x8>(kls + off);
+        xql[s] = ok ? ql : bf16x8{};
+        xkl[s] = ok ? kl : bf16x8{};
+      }
     }
   };
   auto load_v = [&](int k, int buf) {
@@ -617,23 +626,11 @@ gma_causal2_kernel(CausalArgs a) {
     const int nvalid = (int)(rem < kTile ? rem : kTile);
     asm volatile("" ::: "memory");
     // features of this wave's 16 queries and 16 keys
-    bf16x8 fq[R::NKS][3], fk[R::NKS][3];
+    bf16x8 fq[R::NKS][NFX<XS>], fk[R::NKS][NFX<XS>];
 #pragma unroll
     for (int s = 0; s < R::NKS; ++s) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        bf16 hh, ll;
-        const float q = from_bf16(xq[s][e]);
-        split_bf16(q * q, hh, ll);
-        fq[s][0][e] = hh;
-        fq[s][1][e] = ll;
-        const float kf = from_bf16(xk[s][e]);
-        split_bf16(kf * kf, hh, ll);
-        fk[s][0][e] = hh;
-        fk[s][1][e] = ll;
-      }
-      fq[s][2] = xq[s];
-      fk[s][2] = xk[s];
+      make_features<XS>(xq[s], xql[s], fq[s]);
+      make_features<XS>(xk[s], xkl[s], fk[s]);
     }
     // scores: each coefficient operand serves the query and the key tile
     f32x4 SQ[R::CT], SK[R::CT];
@@ -644,8 +641,6 @@ gma_causal2_kernel(CausalArgs a) {
       SK[ct] = cs;
     }
     {
-      constexpr int WI[5] = {0, 0, 1, 2, 3};
-      constexpr int FI[5] = {0, 1, 0, 2, 2};
       constexpr int NSTEP = R::CT / 2 * R::NKS;
       auto load_w = [&](int j, bf16x8 (&wv)[2][4]) {
         const int cp = 2 * (j / R::NKS), s = j % R::NKS;
@@ -662,11 +657,11 @@ gma_causal2_kernel(CausalArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         const int cp = 2 * (j / R::NKS), s = j % R::NKS;
 #pragma unroll
-        for (int q = 0; q < 5; ++q)
+        for (int q = 0; q < NQX<XS>; ++q)
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            SQ[cp + u] = mma(wbuf[j & 1][u][WI[q]], fq[s][FI[q]], SQ[cp + u]);
-            SK[cp + u] = mma(wbuf[j & 1][u][WI[q]], fk[s][FI[q]], SK[cp + u]);
+            SQ[cp + u] = mma(wbuf[j & 1][u][kWI[q]], fq[s][kFI[q]], SQ[cp + u]);
+            SK[cp + u] = mma(wbuf[j & 1][u][kWI[q]], fk[s][kFI[q]], SK[cp + u]);
           }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -840,7 +835,10 @@ static hipError_t run_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   } else {
   // 1. span totals through the latent-write kernel (one split per span)
   BidirArgs wa{};
+  const bool split = t.k_lo != nullptr;
+  if (split && !(Causal2<C>::kOK && Write2<C>::kOK)) return hipErrorNotSupported;
   wa.x = t.k;
+  wa.x_lo = t.k_lo;
   wa.v = t.v;
   wa.params = t.ws + p.off_params;
   wa.head_bytes = p.head_bytes;
@@ -856,10 +854,12 @@ static hipError_t run_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   if (g_launch_hook) g_launch_hook("gma_span_state", s, 1);
   // the token-owner write pays a per-workgroup set-up: use it for long spans
   // (at least eight 32-token steps per wave), one split per span
-  if (Write2<C>::kOK && p.span_tiles >= 16) {
+  if (Write2<C>::kOK && (split || p.span_tiles >= 16)) {
     wa.gpw = 2 * p.span_tiles;
-    if constexpr (Write2<C>::kOK)
-      hipLaunchKernelGGL(gma_write2_kernel<C>, grid, dim3(256), 0, s, wa);
+    if constexpr (Write2<C>::kOK) {
+      if (split) hipLaunchKernelGGL((gma_write2_kernel<C, true>), grid, dim3(256), 0, s, wa);
+      else hipLaunchKernelGGL((gma_write2_kernel<C, false>), grid, dim3(256), 0, s, wa);
+    }
   } else if constexpr (C::kBF) {
     hipLaunchKernelGGL(gma_write_bf16_kernel<C>, grid, dim3(kThreads), 0, s, wa);
   } else {
@@ -898,9 +898,15 @@ static hipError_t run_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   ca.span_tiles = p.span_tiles;
   ca.eps = t.eps;
   ca.out_bf = p.out_bf ? 1 : 0;
+  ca.q_lo = t.q_lo;
+  ca.k_lo = t.k_lo;
   if (g_launch_hook) g_launch_hook("gma_causal", s, 1);
-  if constexpr (Causal2<C>::kOK) hipLaunchKernelGGL(gma_causal2_kernel<C>, grid, dim3(kThreads), 0, s, ca);
-  else hipLaunchKernelGGL(gma_causal_kernel<C>, grid, dim3(kThreads), 0, s, ca);
+  if constexpr (Causal2<C>::kOK) {
+    if (split) hipLaunchKernelGGL((gma_causal2_kernel<C, true>), grid, dim3(kThreads), 0, s, ca);
+    else hipLaunchKernelGGL((gma_causal2_kernel<C, false>), grid, dim3(kThreads), 0, s, ca);
+  } else {
+    hipLaunchKernelGGL(gma_causal_kernel<C>, grid, dim3(kThreads), 0, s, ca);
+  }
   if (g_launch_hook) g_launch_hook("gma_causal", s, 0);
   return hipGetLastError();
   }
@@ -922,6 +928,33 @@ static hipError_t run_causal(const Plan& p, const Tensors& t, hipStream_t s) {
     case 128: GMA_CDV_CASES(BF, CPW, 128)                                   \
   }                                                                         \
   break;
+
+template <class C>
+static hipError_t causal_split_query(const Plan&, const Tensors&, hipStream_t) {
+  return Causal2<C>::kOK && Write2<C>::kOK ? hipSuccess : hipErrorNotSupported;
+}
+#define GMA_CSDV_CASES(CPW, DR)                                             \
+  switch (p.DV) {                                                           \
+    case 16: return causal_split_query<Cfg<true, CPW, 4, DR, 16>>(p, t, s); \
+    case 32: return causal_split_query<Cfg<true, CPW, 4, DR, 32>>(p, t, s); \
+    case 64: return causal_split_query<Cfg<true, CPW, 4, DR, 64>>(p, t, s); \
+    case 128: return causal_split_query<Cfg<true, CPW, 4, DR, 128>>(p, t, s); \
+  }                                                                         \
+  break;
+static hipError_t causal_split_query_all(const Plan& p, const Tensors& t, hipStream_t s) {
+  if (p.NG != 4) return hipErrorNotSupported;
+  switch (p.DR) {
+    case 16: if (p.CPW == 1) { GMA_CSDV_CASES(1, 16) } else { GMA_CSDV_CASES(2, 16) } break;
+    case 32: if (p.CPW == 1) { GMA_CSDV_CASES(1, 32) } else { GMA_CSDV_CASES(2, 32) } break;
+    case 64: if (p.CPW == 1) { GMA_CSDV_CASES(1, 64) } else { GMA_CSDV_CASES(2, 64) } break;
+    case 128: if (p.CPW == 1) { GMA_CSDV_CASES(1, 128) } else { GMA_CSDV_CASES(2, 128) } break;
+  }
+  return hipErrorNotSupported;
+}
+
+bool causal_split_ok(const Plan& p) {
+  return p.bf && causal_split_query_all(p, Tensors{}, nullptr) == hipSuccess;
+}
 
 hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   if (p.NG != 4) return hipErrorInvalidValue;

@@ -195,6 +195,14 @@ __device__ __forceinline__ void split_bf16(float x, bf16& hi, bf16& lo) {
 
 template <class T> __device__ __forceinline__ T load_elem(const T* p) { return *p; }
 
+// Wait until at most N vector memory operations of this wave are outstanding
+// (they complete in issue order, so everything issued before the last N has).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt takes 0..63");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Workgroup barrier that orders LDS only: outstanding global loads (prefetch of
 // the next tile) stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {

@@ -46,6 +46,10 @@ struct Tensors {
   float* gamma = nullptr;
   float eps = 0.f;
   char* ws = nullptr;
+  // routing vectors given as bf16 pairs (value = q + q_lo): the layer's
+  // projections on the bf16 kernels
+  const void* q_lo = nullptr;
+  const void* k_lo = nullptr;
 };
 
 // Launch helpers; each returns hipSuccess or the launch error.  `tag` names the
@@ -54,11 +58,17 @@ typedef void (*launch_hook_t)(const char* tag, hipStream_t s, int begin);
 extern launch_hook_t g_launch_hook;
 
 hipError_t launch_prologue(const Plan& p, const Tensors& t, hipStream_t s);
+// Whether the bf16 kernels take split routing vectors (q_lo / k_lo) for this shape.
+bool bidir_split_ok(const Plan& p);
+bool causal_split_ok(const Plan& p);
 hipError_t launch_bidir(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_resp(const Plan& p, const Tensors& t, hipStream_t s);
 // Q_X, K_X, V_X = X W_Q, X W_K, X W_V (W[0..2]) into fp32 head-major out[0..2].
-hipError_t launch_proj(const void* X, const void* const W[3], float* const out[3], int64_t B,
-                       int64_t N, int H, int d_model, int d_r, int d_v, hipStream_t s);
+// split = 0: out[0..2] are fp32.  split = 1: Q_X and K_X as bf16 pairs (out[m],
+// lo[m]: value = out + lo, 16 significant bits), V_X as bf16 in out[2].
+hipError_t launch_proj(const void* X, const void* const W[3], void* const out[3],
+                       void* const lo[2], int split, int64_t B, int64_t N, int H, int d_model,
+                       int d_r, int d_v, hipStream_t s);
 
 }  // namespace gma

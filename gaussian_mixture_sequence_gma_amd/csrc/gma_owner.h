@@ -19,6 +19,30 @@ __host__ __device__ constexpr int pair_row(int t, int r) {
 __host__ __device__ constexpr int pair_tile(int i) { return 2 * (i >> 5) + ((i & 7) >> 2); }
 __host__ __device__ constexpr int pair_rowof(int i) { return 4 * ((i & 31) >> 3) + (i & 3); }
 
+// Score operands of one 8-wide routing chunk.  bf16 routing vectors x (exact
+// squares): features (x^2 hi, x^2 lo, x) and five products x^2_hi A_hi,
+// x^2_lo A_hi, x^2_hi A_lo, x B_hi, x B_lo.  Split routing vectors x = xh + xl
+// (two bf16 parts, 16 significant bits): x^2 is formed in fp32 and split, the
+// features gain xl and a sixth product xl B_hi (xl B_lo is below 2^-16 of x B).
+template <bool XS> constexpr int NFX = XS ? 4 : 3;
+template <bool XS> constexpr int NQX = XS ? 6 : 5;
+constexpr int kWI[6] = {0, 0, 1, 2, 3, 2};   // A_hi, A_hi, A_lo, B_hi, B_lo, B_hi
+constexpr int kFI[6] = {0, 1, 0, 2, 2, 3};   // x^2_hi, x^2_lo, x^2_hi, x, x, x_lo
+template <bool XS>
+__device__ __forceinline__ void make_features(const bf16x8& xh, const bf16x8& xl,
+                                              bf16x8 (&f)[NFX<XS>]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = XS ? from_bf16(xh[e]) + from_bf16(xl[e]) : from_bf16(xh[e]);
+    bf16 hh, ll;
+    split_bf16(x * x, hh, ll);
+    f[0][e] = hh;
+    f[1][e] = ll;
+  }
+  f[2] = xh;
+  if constexpr (XS) f[3] = xl;
+}
+
 // Like tr_chunk_swz, but source lane s reads the 4-column block blk (a multiple
 // of 4) chosen by the caller for s % 4: destination lane 4a + e then receives
 // column blk(a) + e of the eight rows tok0 + 8g .. tok0 + 8g + 7.
@@ -64,7 +88,7 @@ struct Write2 {
                               LDS <= 160 * 1024 && CT * DVT * 4 <= 256;
 };
 
-template <class C>
+template <class C, bool XS>
 __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gma_write2_kernel(BidirArgs a) {
   using R = Write2<C>;
@@ -101,7 +125,8 @@ gma_write2_kernel(BidirArgs a) {
   // loads are unconditional (clamped address, value zeroed afterwards) so that
   // every group issues the same number of memory operations: the wait for the
   // V copies below counts them.
-  bf16x8 xr[2][R::NKS];
+  const bf16* xls = XS ? reinterpret_cast<const bf16*>(a.x_lo) + (size_t)bh * a.N * C::DR : xs;
+  bf16x8 xr[2][R::NKS], xl[2][R::NKS];
   auto load_x = [&](int64_t grp) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -110,8 +135,13 @@ gma_write2_kernel(BidirArgs a) {
       for (int s = 0; s < R::NKS; ++s) {
         const int col = 32 * s + 8 * g;
         const bool ok = tok < a.N && col < C::DR;
-        const bf16x8 v = ld16<bf16x8>(xs + (size_t)(ok ? tok : 0) * C::DR + (ok ? col : 0));
+        const size_t off = (size_t)(ok ? tok : 0) * C::DR + (ok ? col : 0);
+        const bf16x8 v = ld16<bf16x8>(xs + off);
         xr[tt][s] = ok ? v : bf16x8{};
+        if constexpr (XS) {
+          const bf16x8 vl = ld16<bf16x8>(xls + off);
+          xl[tt][s] = ok ? vl : bf16x8{};
+        }
       }
     }
   };
@@ -146,21 +176,11 @@ gma_write2_kernel(BidirArgs a) {
   }
   for (; grp < ge; grp += NW, buf ^= 1) {
     asm volatile("" ::: "memory");      // keep the table reads inside the loop
-    bf16x8 f[2][R::NKS][3];
+    bf16x8 f[2][R::NKS][NFX<XS>];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int s = 0; s < R::NKS; ++s) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float xf = from_bf16(xr[tt][s][e]);
-          bf16 hh, ll;
-          split_bf16(xf * xf, hh, ll);
-          f[tt][s][0][e] = hh;
-          f[tt][s][1][e] = ll;
-        }
-        f[tt][s][2] = xr[tt][s];
-      }
+      for (int s = 0; s < R::NKS; ++s) make_features<XS>(xr[tt][s], xl[tt][s], f[tt][s]);
     const bool more = grp + NW < ge;
     if (more) load_v(grp + NW, buf ^ 1);
 
@@ -171,8 +191,6 @@ gma_write2_kernel(BidirArgs a) {
       S[0][ct] = f32x4{cv, cv, cv, cv};
       S[1][ct] = S[0][ct];
     }
-    constexpr int WI[5] = {0, 0, 1, 2, 3};
-    constexpr int FI[5] = {0, 1, 0, 2, 2};
     constexpr int NSTEP = R::CT / 2 * R::NKS;
     auto load_w = [&](int j, bf16x8 (&w)[2][4]) {
       const int cp = 2 * (j / R::NKS), s = j % R::NKS;
@@ -189,12 +207,12 @@ gma_write2_kernel(BidirArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       const int cp = 2 * (j / R::NKS), s = j % R::NKS;
 #pragma unroll
-      for (int q = 0; q < 5; ++q)
+      for (int q = 0; q < NQX<XS>; ++q)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int u = 0; u < 2; ++u)
-            S[tt][cp + u] = mma(f[tt][s][FI[q]], wbuf[j & 1][u][WI[q]], S[tt][cp + u]);
+            S[tt][cp + u] = mma(f[tt][s][kFI[q]], wbuf[j & 1][u][kWI[q]], S[tt][cp + u]);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (more) load_x(grp + NW);
@@ -246,12 +264,7 @@ gma_write2_kernel(BidirArgs a) {
     // V(grp) has arrived once at most the copies and loads of the next group
     // (issued after it) are outstanding
     if (more) {
-      if constexpr (R::NDMA + 2 * R::NKS == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-      else if constexpr (R::NDMA + 2 * R::NKS == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      else if constexpr (R::NDMA + 2 * R::NKS == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-      else if constexpr (R::NDMA + 2 * R::NKS == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-      else if constexpr (R::NDMA + 2 * R::NKS == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-      else wait_global_loads();
+      wait_vmcnt<R::NDMA + (XS ? 4 : 2) * R::NKS>();
     } else {
       wait_global_loads();
     }

@@ -2,11 +2,14 @@
 // "Projections", Eq. 4): Q_X = X W_Q, K_X = X W_K, V_X = X W_V with no bias.
 // X is [B*N, d_model] bf16, each W is [d_model, H*d] bf16, and head h owns
 // columns [h*d, (h+1)*d).  The products are accumulated in fp32 on bf16 MFMA
-// and stored unrounded in fp32, head-major [B,H,N,d], which is the layout the
-// GMA kernels stream.
+// and stored head-major [B,H,N,d], the layout the GMA kernels stream, in one
+// of two forms: unrounded fp32, or (split) the routing vectors Q_X and K_X as
+// bf16 pairs hi + lo carrying 16 significant bits and V_X rounded to bf16 --
+// the operands of the bf16 GMA kernels, at 4 + 4 + 2 bytes per element instead
+// of 12.
 //
-// One launch covers all three matrices.  A workgroup owns 128 output features
-// x 128 tokens and walks d_model in steps of 64; both operand tiles are copied
+// One launch covers all three matrices.  A workgroup owns 32 WF output
+// features x 32 WT tokens (2 x 2 waves) and walks d_model in steps of 64; both operand tiles are copied
 // global -> LDS directly (no register staging) into a double buffer, so the
 // copy of step k+1 runs under the MFMAs of step k.  The product is formed as
 // D^T = W^T X^T: W supplies the MFMA A operand through transpose reads of its
@@ -19,14 +22,14 @@
 namespace gma {
 namespace {
 
-constexpr int kPT = 128;   // tokens per workgroup tile
-constexpr int kPF = 128;   // output features per workgroup tile
 constexpr int kPK = 64;    // d_model step
 
 struct ProjArgs {
   const bf16* X;
   const bf16* W[3];
-  float* out[3];
+  void* out[3];
+  bf16* lo[2];       // split: low halves of Q_X and K_X
+  int split;
   int ncols[3];      // H * d of each matrix (multiple of 16)
   int dh[3];         // d of each matrix
   int ft0[4];        // first feature tile of each matrix; ft0[3] = total feature tiles
@@ -35,14 +38,30 @@ struct ProjArgs {
   int64_t blocks;
 };
 
-// X tile [128 tokens][64 k]: eight 16-byte chunks per row, chunk c of row r at
+// X tile [tokens][64 k]: eight 16-byte chunks per row, chunk c of row r at
 // c ^ xswz(r).  Eight consecutive rows, and the eight even (odd) rows of 16
 // consecutive ones, read the same logical chunk from distinct banks.
 __device__ __forceinline__ int xswz(int r) { return (r ^ (r >> 3)) & 7; }
 
-__global__ void __launch_bounds__(kThreads, 2) gma_proj_kernel(ProjArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 Xs[2][kPT * kPK];
-  __shared__ __attribute__((aligned(16))) bf16 Ws[2][kPK * kPF];
+// Wave tile (16 WF features) x (16 WT tokens); the workgroup is 2 x 2 waves.
+// WF = WT = 8 (128 x 128 per wave, accumulators in the 256 accumulation
+// registers, one wave per SIMD) reads 16 KB of LDS operands per 64 MFMAs,
+// half the LDS traffic per flop of a 64 x 64 wave tile.
+template <int WF, int WT>
+struct ProjTile {
+  static constexpr int BF = 32 * WF;                 // features per workgroup
+  static constexpr int BT = 32 * WT;                 // tokens per workgroup
+  static constexpr int WROWCH = BF / 8;              // 16-byte chunks per W row
+  static constexpr int XSEG = BT / 8;                // 1 KB copies per X tile (8 rows each)
+  static constexpr int WSEG = kPK * BF * 2 / 1024;   // 1 KB copies per W tile
+  static constexpr int WROWS = 64 / WROWCH;          // W rows per copy
+};
+
+template <int WF, int WT>
+__global__ void __launch_bounds__(kThreads, (WF * WT >= 64 ? 1 : 2)) gma_proj_kernel(ProjArgs a) {
+  using T = ProjTile<WF, WT>;
+  __shared__ __attribute__((aligned(16))) bf16 Xs[2][T::BT * kPK];
+  __shared__ __attribute__((aligned(16))) bf16 Ws[2][kPK * T::BF];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int s16 = lane & 15, g = lane >> 4;
@@ -55,27 +74,32 @@ __global__ void __launch_bounds__(kThreads, 2) gma_proj_kernel(ProjArgs a) {
   const int64_t mt = L / ftot;
   const int ft = (int)(L - mt * ftot);
   const int m = ft >= a.ft0[2] ? 2 : (ft >= a.ft0[1] ? 1 : 0);
-  const int f0 = (ft - a.ft0[m]) * kPF;
+  const int f0 = (ft - a.ft0[m]) * T::BF;
   const int ncols = a.ncols[m];
-  const int64_t tok0 = mt * kPT;
+  const int64_t tok0 = mt * T::BT;
   const bf16* __restrict__ X = a.X;
   const bf16* __restrict__ W = a.W[m];
 
-  // Per-lane global sources of the direct copies.  X: wave w fills 1 KB
-  // segments w, w+4, w+8, w+12 (eight rows each); W: the same segments hold
-  // four k-rows each.
-  const bf16* xsrc[4];
-  const bf16* wsrc[4];
+  // Per-lane global sources of the direct copies: wave w fills 1 KB segments
+  // w, w + 4, ... of each tile.
+  constexpr int XPW = T::XSEG / 4, WPW = T::WSEG / 4;
+  const bf16* xsrc[XPW];
+  const bf16* wsrc[WPW];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < XPW; ++j) {
     const int seg = w + 4 * j;
     const int xr = 8 * seg + (lane >> 3);
     int64_t tok = tok0 + xr;
     if (tok >= a.M) tok = a.M - 1;                        // ragged tail: rows never stored
     const int xc = (lane & 7) ^ xswz(xr);
     xsrc[j] = X + tok * a.Dm + xc * 8;
-    const int wr = 4 * seg + (lane >> 4);
-    const int wc = (lane & 15) ^ ((2 * wr) & 14);          // swz_elem<16> layout
+  }
+#pragma unroll
+  for (int j = 0; j < WPW; ++j) {
+    const int seg = w + 4 * j;
+    const int wr = T::WROWS * seg + lane / T::WROWCH;
+    const int pc = lane % T::WROWCH;
+    const int wc = pc ^ ((2 * wr) & (T::WROWCH - 2));     // swz_elem<WROWCH> layout
     int col = f0 + wc * 8;
     if (col >= ncols) col = ncols - 8;                     // ragged features: never stored
     wsrc[j] = W + (int64_t)wr * ncols + col;
@@ -84,18 +108,17 @@ __global__ void __launch_bounds__(kThreads, 2) gma_proj_kernel(ProjArgs a) {
     const int64_t kx = (int64_t)kstep * kPK;
     const int64_t kw = kx * ncols;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      global_to_lds16(xsrc[j] + kx, &Xs[buf][(w + 4 * j) * 512]);
-      global_to_lds16(wsrc[j] + kw, &Ws[buf][(w + 4 * j) * 512]);
-    }
+    for (int j = 0; j < XPW; ++j) global_to_lds16(xsrc[j] + kx, &Xs[buf][(w + 4 * j) * 512]);
+#pragma unroll
+    for (int j = 0; j < WPW; ++j) global_to_lds16(wsrc[j] + kw, &Ws[buf][(w + 4 * j) * 512]);
   };
 
-  const int wf = w & 1, wt = w >> 1;   // wave owns features wf*64.., tokens wt*64..
-  f32x4 acc[4][4];
+  const int wf = w & 1, wt = w >> 1;   // wave owns features wf*16WF.., tokens wt*16WT..
+  f32x4 acc[WF][WT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < WF; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < WT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = a.Dm / kPK;
   stage(0, 0);
@@ -106,19 +129,19 @@ __global__ void __launch_bounds__(kThreads, 2) gma_proj_kernel(ProjArgs a) {
     if (it + 1 < nk) stage(it + 1, buf ^ 1);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 wa[4], xb[4];
+      bf16x8 wa[WF], xb[WT];
 #pragma unroll
-      for (int fm = 0; fm < 4; ++fm)
-        wa[fm] = tr_chunk_swz<16>(Ws[buf], kk * 32, wf * 64 + fm * 16);
+      for (int fm = 0; fm < WF; ++fm)
+        wa[fm] = tr_chunk_swz<T::WROWCH>(Ws[buf], kk * 32, wf * 16 * WF + fm * 16);
 #pragma unroll
-      for (int tn = 0; tn < 4; ++tn) {
-        const int r = wt * 64 + tn * 16 + s16;
+      for (int tn = 0; tn < WT; ++tn) {
+        const int r = wt * 16 * WT + tn * 16 + s16;
         xb[tn] = ld16<bf16x8>(&Xs[buf][r * kPK + (((kk * 4 + g) ^ xswz(r)) << 3)]);
       }
 #pragma unroll
-      for (int fm = 0; fm < 4; ++fm)
+      for (int fm = 0; fm < WF; ++fm)
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn) acc[fm][tn] = mma(wa[fm], xb[tn], acc[fm][tn]);
+        for (int tn = 0; tn < WT; ++tn) acc[fm][tn] = mma(wa[fm], xb[tn], acc[fm][tn]);
     }
     wait_global_loads();
     lds_barrier();
@@ -127,49 +150,81 @@ __global__ void __launch_bounds__(kThreads, 2) gma_proj_kernel(ProjArgs a) {
   // Lane (s16, g) of tile (fm, tn) holds features f..f+3, f = 16 fm + 4 g, of
   // token 16 tn + s16; four consecutive features never straddle a head.
   const int dh = a.dh[m];
-  float* __restrict__ out = a.out[m];
+  void* __restrict__ out = a.out[m];
+  bf16* __restrict__ lo = m < 2 ? a.lo[m] : nullptr;
 #pragma unroll
-  for (int tn = 0; tn < 4; ++tn) {
-    const int64_t t = tok0 + wt * 64 + tn * 16 + s16;
+  for (int tn = 0; tn < WT; ++tn) {
+    const int64_t t = tok0 + wt * 16 * WT + tn * 16 + s16;
     if (t >= a.M) continue;
     const int64_t b = t / a.N, n = t - b * a.N;
 #pragma unroll
-    for (int fm = 0; fm < 4; ++fm) {
-      const int f = f0 + wf * 64 + fm * 16 + 4 * g;
+    for (int fm = 0; fm < WF; ++fm) {
+      const int f = f0 + wf * 16 * WF + fm * 16 + 4 * g;
       if (f >= ncols) continue;
       const int h = f / dh, j = f - h * dh;
-      st16(out + (((b * a.H + h) * a.N + n) * dh + j), acc[fm][tn]);
+      const int64_t e = ((b * a.H + h) * a.N + n) * dh + j;
+      if (!a.split) {
+        st16(static_cast<float*>(out) + e, acc[fm][tn]);
+      } else {
+        bf16x4 hi, lw;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          bf16 h, l;
+          split_bf16(acc[fm][tn][u], h, l);
+          hi[u] = h;
+          lw[u] = l;
+        }
+        *reinterpret_cast<bf16x4*>(static_cast<bf16*>(out) + e) = hi;
+        if (lo) *reinterpret_cast<bf16x4*>(lo + e) = lw;
+      }
     }
   }
 }
 
+template <int WF, int WT>
+hipError_t launch_tiles(ProjArgs& a, hipStream_t s) {
+  using T = ProjTile<WF, WT>;
+  int ft = 0;
+  for (int m = 0; m < 3; ++m) {
+    a.ft0[m] = ft;
+    ft += (a.ncols[m] + T::BF - 1) / T::BF;
+  }
+  a.ft0[3] = ft;
+  const int64_t mtiles = (a.M + T::BT - 1) / T::BT;
+  a.blocks = mtiles * ft;
+  if (a.blocks > 0x7fffffff) return hipErrorInvalidValue;
+  gma_proj_kernel<WF, WT><<<dim3((unsigned)a.blocks), dim3(kThreads), 0, s>>>(a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_proj(const void* X, const void* const W[3], float* const out[3], int64_t B,
-                       int64_t N, int H, int d_model, int d_r, int d_v, hipStream_t s) {
+hipError_t launch_proj(const void* X, const void* const W[3], void* const out[3],
+                       void* const lo[2], int split, int64_t B, int64_t N, int H, int d_model,
+                       int d_r, int d_v, hipStream_t s) {
   ProjArgs a{};
   a.X = static_cast<const bf16*>(X);
+  a.split = split ? 1 : 0;
+  if (a.split) {
+    if (!lo || !lo[0] || !lo[1]) return hipErrorInvalidValue;
+    a.lo[0] = static_cast<bf16*>(lo[0]);
+    a.lo[1] = static_cast<bf16*>(lo[1]);
+  }
   const int d[3] = {d_r, d_r, d_v};
-  int ft = 0;
   for (int m = 0; m < 3; ++m) {
     a.W[m] = static_cast<const bf16*>(W[m]);
     a.out[m] = out[m];
     a.dh[m] = d[m];
     a.ncols[m] = H * d[m];
-    a.ft0[m] = ft;
-    ft += (a.ncols[m] + kPF - 1) / kPF;
   }
-  a.ft0[3] = ft;
   a.M = B * N;
   a.N = N;
   a.H = H;
   a.Dm = d_model;
-  const int64_t mtiles = (a.M + kPT - 1) / kPT;
-  a.blocks = mtiles * ft;
-  if (a.blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (g_launch_hook) g_launch_hook("gma_proj", s, 1);
-  gma_proj_kernel<<<dim3((unsigned)a.blocks), dim3(kThreads), 0, s>>>(a);
-  hipError_t e = hipGetLastError();
+  // large problems: 128 x 128 wave tiles; small ones keep more workgroups
+  const bool big = a.M >= 4096 && a.ncols[0] >= 256 && a.ncols[2] >= 256;
+  hipError_t e = big ? launch_tiles<8, 8>(a, s) : launch_tiles<4, 4>(a, s);
   if (g_launch_hook) g_launch_hook("gma_proj", s, 0);
   return e;
 }

@@ -72,6 +72,7 @@ constexpr int kMaxLds = 160 * 1024;
 
 struct BidirArgs {
   const void* x;          // K_X (write) or Q_X (read / resp), [BH][N][DR]
+  const void* x_lo;       // split routing vectors: low bf16 parts (x = x + x_lo), or null
   const void* v;          // V_X [BH][N][DV] (write)
   void* out;              // O [BH][N][DV] (read)
   const char* params;     // prologue output

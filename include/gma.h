@@ -97,17 +97,33 @@ int gma_layer_workspace_bytes(const gma_dims* d, int32_t d_model, int causal, si
  *  W_Q, W_K   [d_model, H*d_r] of d->dtype; head h uses columns [h*d_r, (h+1)*d_r)
  *  W_V        [d_model, H*d_v] of d->dtype; head h uses columns [h*d_v, (h+1)*d_v)
  *  d_model    multiple of 64, 64..8192
- * The projections are accumulated and kept in fp32 (bf16 x bf16 products are
- * exact in fp32) and feed the fp32 GMA path; out is [B,H,N,d_v] of d->dtype.
- * They stay in the workspace after the call, as Q_X, K_X, V_X one after the
- * other in [B,H,N,d] fp32, starting P bytes before the end of the
- * gma_layer_workspace_bytes figure, P = 4*B*H*N*(2*d_r + d_v) rounded up to a
- * multiple of 256.  Other arguments as gma_forward. */
+ * The projections are accumulated in fp32 (bf16 x bf16 products are exact in
+ * fp32).  Where the bf16 GMA kernels support the shape (see
+ * gma_layer_projection_layout) Q_X and K_X are then kept as bf16 pairs hi + lo
+ * (16 significant bits), V_X is rounded to bf16, and the bf16 GMA path runs on
+ * them; otherwise all three stay fp32 and feed the fp32 GMA path.  out is
+ * [B,H,N,d_v] of d->dtype.  The projections stay in the workspace after the
+ * call, at the offsets gma_layer_projection_layout reports.  Other arguments
+ * as gma_forward. */
 int gma_layer_forward(const void* X, const void* W_Q, const void* W_K, const void* W_V,
                       int32_t d_model, const float* mu, const float* log_sigma2,
                       const float* log_pi, float eps, int causal, void* out,
                       const gma_dims* d, int32_t* assign_q, int32_t* assign_k,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Storage of the projections gma_layer_forward leaves in its workspace. */
+typedef enum {
+  GMA_PROJ_F32 = 0,        /* Q_X, K_X, V_X fp32 [B,H,N,d] at offsets[0..2] */
+  GMA_PROJ_SPLIT_BF16 = 1  /* bf16 [B,H,N,d]: Q_X hi, Q_X lo, K_X hi, K_X lo, V_X at
+                              offsets[0..4]; Q_X = hi + lo */
+} gma_proj_format;
+
+/* Where gma_layer_forward leaves the projections for this shape and variant
+ * (host only): *format is a gma_proj_format and offsets[m] the byte offset of
+ * array m from the start of the workspace (unused entries 0).  offsets holds 5
+ * entries.  Errors as gma_layer_workspace_bytes. */
+int gma_layer_projection_layout(const gma_dims* d, int32_t d_model, int causal,
+                                int32_t* format, size_t offsets[5]);
 
 /* Responsibilities alone (Eq. 3), for testing and diagnostics.
  *  X_r    [B,H,N,d_r] of d->dtype; head h's parameters apply to [b,h,:,:]
