@@ -8,14 +8,15 @@
 // the operands of the bf16 GMA kernels, at 4 + 4 + 2 bytes per element instead
 // of 12.
 //
-// One launch covers all three matrices.  A workgroup owns 32 WF output
-// features x 32 WT tokens (2 x 2 waves) and walks d_model in steps of 64; both operand tiles are copied
+// One launch covers all three matrices.  A workgroup of WAF x WAT waves owns
+// (16 WF WAF) output features x (16 WT WAT) tokens, each wave 16 WF x 16 WT of
+// them, and walks d_model in steps of 64; both operand tiles are copied
 // global -> LDS directly (no register staging) into a double buffer, so the
 // copy of step k+1 runs under the MFMAs of step k.  The product is formed as
 // D^T = W^T X^T: W supplies the MFMA A operand through transpose reads of its
 // row-major [k][feature] tile, X supplies the B operand with plain 16-byte
 // reads of its row-major [token][k] tile, and each accumulator lane then holds
-// four consecutive features of one token, stored as one 16-byte vector.
+// four consecutive features of one token.
 #include "gma_device.h"
 #include "gma_internal.h"
 
@@ -23,6 +24,7 @@ namespace gma {
 namespace {
 
 constexpr int kPK = 64;    // d_model step
+constexpr int kBand = 8;   // token tiles per band of the tile order
 
 struct ProjArgs {
   const bf16* X;
@@ -43,36 +45,47 @@ struct ProjArgs {
 // consecutive ones, read the same logical chunk from distinct banks.
 __device__ __forceinline__ int xswz(int r) { return (r ^ (r >> 3)) & 7; }
 
-// Wave tile (16 WF features) x (16 WT tokens); the workgroup is 2 x 2 waves.
-// WF = WT = 8 (128 x 128 per wave, accumulators in the 256 accumulation
-// registers, one wave per SIMD) reads 16 KB of LDS operands per 64 MFMAs,
-// half the LDS traffic per flop of a 64 x 64 wave tile.
-template <int WF, int WT>
+// Large problems: 256 x 256 workgroup tiles of eight 64 x 128 wave tiles, two
+// waves per SIMD (128 accumulators each, so one wave's MFMAs run while the
+// other waits on LDS); per 64-deep step a wave reads 12 KB of LDS operands for
+// 64 MFMAs.  Small problems: 64 x 64 tiles of four 32 x 32 wave tiles, for
+// more workgroups.
+template <int WF, int WT, int WAF, int WAT>
 struct ProjTile {
-  static constexpr int BF = 32 * WF;                 // features per workgroup
-  static constexpr int BT = 32 * WT;                 // tokens per workgroup
-  static constexpr int WROWCH = BF / 8;              // 16-byte chunks per W row
-  static constexpr int XSEG = BT / 8;                // 1 KB copies per X tile (8 rows each)
-  static constexpr int WSEG = kPK * BF * 2 / 1024;   // 1 KB copies per W tile
-  static constexpr int WROWS = 64 / WROWCH;          // W rows per copy
+  static constexpr int NW = WAF * WAT;                // waves per workgroup
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int BF = 16 * WF * WAF;            // features per workgroup
+  static constexpr int BT = 16 * WT * WAT;            // tokens per workgroup
+  static constexpr int WROWCH = BF / 8;               // 16-byte chunks per W row
+  static constexpr int XSEG = BT / 8;                 // 1 KB copies per X tile (8 rows each)
+  static constexpr int WSEG = kPK * BF * 2 / 1024;    // 1 KB copies per W tile
+  static constexpr int WROWS = 64 / WROWCH;           // W rows per copy
+  static_assert(XSEG % NW == 0 && WSEG % NW == 0, "copies must divide among the waves");
+  static_assert(WROWCH >= 2 && WROWCH <= 64, "W tile row of 32..1024 bytes");
 };
 
-template <int WF, int WT>
-__global__ void __launch_bounds__(kThreads, (WF * WT >= 64 ? 1 : 2)) gma_proj_kernel(ProjArgs a) {
-  using T = ProjTile<WF, WT>;
+template <int WF, int WT, int WAF, int WAT>
+__global__ void __launch_bounds__(64 * WAF * WAT) gma_proj_kernel(ProjArgs a) {
+  using T = ProjTile<WF, WT, WAF, WAT>;
   __shared__ __attribute__((aligned(16))) bf16 Xs[2][T::BT * kPK];
   __shared__ __attribute__((aligned(16))) bf16 Ws[2][kPK * T::BF];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int s16 = lane & 15, g = lane >> 4;
 
-  // Consecutive logical tiles share the X token tile; group them on one XCD
-  // (workgroups are dealt to the eight XCDs round-robin) so X stays in its L2.
+  // Workgroups are dealt to the eight XCDs round-robin; give each XCD a
+  // contiguous run of logical tiles, ordered in bands of kBand token tiles
+  // (feature tile outer, token tile inner), so the workgroups an XCD runs at
+  // once share a few X and W tiles in its L2.
   int64_t L = blockIdx.x;
   if ((a.blocks & 7) == 0) L = (L & 7) * (a.blocks >> 3) + (L >> 3);
   const int ftot = a.ft0[3];
-  const int64_t mt = L / ftot;
-  const int ft = (int)(L - mt * ftot);
+  const int64_t mtiles = a.blocks / ftot;
+  const int64_t band = L / ((int64_t)kBand * ftot);
+  const int64_t bt = (band + 1) * kBand <= mtiles ? kBand : mtiles - band * kBand;
+  const int64_t rb = L - band * kBand * ftot;
+  const int ft = (int)(rb / bt);
+  const int64_t mt = band * kBand + rb % bt;
   const int m = ft >= a.ft0[2] ? 2 : (ft >= a.ft0[1] ? 1 : 0);
   const int f0 = (ft - a.ft0[m]) * T::BF;
   const int ncols = a.ncols[m];
@@ -81,13 +94,13 @@ __global__ void __launch_bounds__(kThreads, (WF * WT >= 64 ? 1 : 2)) gma_proj_ke
   const bf16* __restrict__ W = a.W[m];
 
   // Per-lane global sources of the direct copies: wave w fills 1 KB segments
-  // w, w + 4, ... of each tile.
-  constexpr int XPW = T::XSEG / 4, WPW = T::WSEG / 4;
+  // w, w + NW, ... of each tile.
+  constexpr int XPW = T::XSEG / T::NW, WPW = T::WSEG / T::NW;
   const bf16* xsrc[XPW];
   const bf16* wsrc[WPW];
 #pragma unroll
   for (int j = 0; j < XPW; ++j) {
-    const int seg = w + 4 * j;
+    const int seg = w + T::NW * j;
     const int xr = 8 * seg + (lane >> 3);
     int64_t tok = tok0 + xr;
     if (tok >= a.M) tok = a.M - 1;                        // ragged tail: rows never stored
@@ -96,7 +109,7 @@ __global__ void __launch_bounds__(kThreads, (WF * WT >= 64 ? 1 : 2)) gma_proj_ke
   }
 #pragma unroll
   for (int j = 0; j < WPW; ++j) {
-    const int seg = w + 4 * j;
+    const int seg = w + T::NW * j;
     const int wr = T::WROWS * seg + lane / T::WROWCH;
     const int pc = lane % T::WROWCH;
     const int wc = pc ^ ((2 * wr) & (T::WROWCH - 2));     // swz_elem<WROWCH> layout
@@ -108,12 +121,12 @@ __global__ void __launch_bounds__(kThreads, (WF * WT >= 64 ? 1 : 2)) gma_proj_ke
     const int64_t kx = (int64_t)kstep * kPK;
     const int64_t kw = kx * ncols;
 #pragma unroll
-    for (int j = 0; j < XPW; ++j) global_to_lds16(xsrc[j] + kx, &Xs[buf][(w + 4 * j) * 512]);
+    for (int j = 0; j < XPW; ++j) global_to_lds16(xsrc[j] + kx, &Xs[buf][(w + T::NW * j) * 512]);
 #pragma unroll
-    for (int j = 0; j < WPW; ++j) global_to_lds16(wsrc[j] + kw, &Ws[buf][(w + 4 * j) * 512]);
+    for (int j = 0; j < WPW; ++j) global_to_lds16(wsrc[j] + kw, &Ws[buf][(w + T::NW * j) * 512]);
   };
 
-  const int wf = w & 1, wt = w >> 1;   // wave owns features wf*16WF.., tokens wt*16WT..
+  const int wf = w % WAF, wt = w / WAF;   // wave owns features wf*16WF.., tokens wt*16WT..
   f32x4 acc[WF][WT];
 #pragma unroll
   for (int i = 0; i < WF; ++i)
@@ -169,10 +182,10 @@ __global__ void __launch_bounds__(kThreads, (WF * WT >= 64 ? 1 : 2)) gma_proj_ke
         bf16x4 hi, lw;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          bf16 h, l;
-          split_bf16(acc[fm][tn][u], h, l);
-          hi[u] = h;
-          lw[u] = l;
+          bf16 vh, vl;
+          split_bf16(acc[fm][tn][u], vh, vl);
+          hi[u] = vh;
+          lw[u] = vl;
         }
         *reinterpret_cast<bf16x4*>(static_cast<bf16*>(out) + e) = hi;
         if (lo) *reinterpret_cast<bf16x4*>(lo + e) = lw;
@@ -181,9 +194,9 @@ __global__ void __launch_bounds__(kThreads, (WF * WT >= 64 ? 1 : 2)) gma_proj_ke
   }
 }
 
-template <int WF, int WT>
+template <int WF, int WT, int WAF, int WAT>
 hipError_t launch_tiles(ProjArgs& a, hipStream_t s) {
-  using T = ProjTile<WF, WT>;
+  using T = ProjTile<WF, WT, WAF, WAT>;
   int ft = 0;
   for (int m = 0; m < 3; ++m) {
     a.ft0[m] = ft;
@@ -193,7 +206,7 @@ hipError_t launch_tiles(ProjArgs& a, hipStream_t s) {
   const int64_t mtiles = (a.M + T::BT - 1) / T::BT;
   a.blocks = mtiles * ft;
   if (a.blocks > 0x7fffffff) return hipErrorInvalidValue;
-  gma_proj_kernel<WF, WT><<<dim3((unsigned)a.blocks), dim3(kThreads), 0, s>>>(a);
+  gma_proj_kernel<WF, WT, WAF, WAT><<<dim3((unsigned)a.blocks), dim3(T::THREADS), 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -222,9 +235,9 @@ hipError_t launch_proj(const void* X, const void* const W[3], void* const out[3]
   a.H = H;
   a.Dm = d_model;
   if (g_launch_hook) g_launch_hook("gma_proj", s, 1);
-  // large problems: 128 x 128 wave tiles; small ones keep more workgroups
+  // large problems: 256 x 256 workgroup tiles; small ones keep more workgroups
   const bool big = a.M >= 4096 && a.ncols[0] >= 256 && a.ncols[2] >= 256;
-  hipError_t e = big ? launch_tiles<8, 8>(a, s) : launch_tiles<4, 4>(a, s);
+  hipError_t e = big ? launch_tiles<4, 8, 4, 2>(a, s) : launch_tiles<2, 2, 2, 2>(a, s);
   if (g_launch_hook) g_launch_hook("gma_proj", s, 0);
   return e;
 }
