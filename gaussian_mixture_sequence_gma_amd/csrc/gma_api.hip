@@ -90,9 +90,17 @@ int make_plan(const gma_dims* d, int causal, bool fp32_compute, Plan& p) {
   if (want > p.tiles) want = p.tiles;
   p.tiles_per_split = (int)((p.tiles + want - 1) / want);
   p.S = (int)((p.tiles + p.tiles_per_split - 1) / p.tiles_per_split);
-  // causal spans: a span is the unit one workgroup scans sequentially
+  // causal spans: a span is the unit one workgroup scans sequentially.  The
+  // bf16 scan kernel holds two 4-wave workgroups per compute unit when its LDS
+  // allows (else one): as many spans as fit the chip at once, so every
+  // workgroup scans in the same round; otherwise about four per compute unit.
   {
     int64_t want_c = (1024 + p.BH - 1) / p.BH;
+    const int lds2 = causal2_lds_bytes(p.bf, p.DRP, p.DV, p.Kp);
+    if (lds2 > 0) {
+      const int64_t resident = 256 * (2 * lds2 <= kMaxLds ? 2 : 1);
+      want_c = resident / p.BH;
+    }
     if (want_c < 1) want_c = 1;
     if (want_c > p.tiles) want_c = p.tiles;
     p.span_tiles = (int)((p.tiles + want_c - 1) / want_c);

@@ -490,6 +490,8 @@ struct Causal2 {
   static constexpr int NB = lds_bytes(2) <= 160 * 1024 ? 2 : 1;
   static constexpr bool kOK = C::kBF && KP % 64 == 0 && C::DRP <= 64 && C::DV >= 32 &&
                               lds_bytes(NB) <= 160 * 1024;
+  static_assert(!kOK || causal2_lds_bytes(true, C::DRP, C::DV, KP) == lds_bytes(NB),
+                "span sizing mirrors this LDS budget");
 };
 
 template <class C, bool XS>

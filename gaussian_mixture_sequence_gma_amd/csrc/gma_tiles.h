@@ -70,6 +70,25 @@ __host__ __device__ constexpr int causal_lds_bytes(bool bf, int DR, int DV, int 
 }
 constexpr int kMaxLds = 160 * 1024;
 
+// LDS bytes of the bf16 token-owner scan kernel (gma_causal2_kernel), or 0 where
+// it does not apply: the coefficient operand table and constants, the Gamma^K
+// and V tiles (double-buffered when that fits) and the carried-state operand
+// table.  Mirrors Causal2 in gma_causal.hip.
+__host__ __device__ constexpr int causal2_lds_bytes_nb(int DRP, int DV, int Kp, int nb) {
+  return (Kp / 16) * (DRP / 32) * 4 * 1024 + Kp * 4 +
+         nb * kTile * (Kp % 128 == 64 ? Kp + 8 : Kp + 16) * 2 + nb * kTile * DV * 2 +
+         (DV / 16 + 1) * (Kp / 32) * 1024;
+}
+__host__ __device__ constexpr int causal2_lds_bytes(bool bf, int DRP, int DV, int Kp) {
+  return !(bf && Kp % 64 == 0 && DRP <= 64 && DV >= 32)
+             ? 0
+             : (causal2_lds_bytes_nb(DRP, DV, Kp, 2) <= kMaxLds
+                    ? causal2_lds_bytes_nb(DRP, DV, Kp, 2)
+                    : (causal2_lds_bytes_nb(DRP, DV, Kp, 1) <= kMaxLds
+                           ? causal2_lds_bytes_nb(DRP, DV, Kp, 1)
+                           : 0));
+}
+
 struct BidirArgs {
   const void* x;          // K_X (write) or Q_X (read / resp), [BH][N][DR]
   const void* x_lo;       // split routing vectors: low bf16 parts (x = x + x_lo), or null
