@@ -162,19 +162,31 @@ __global__ void __launch_bounds__(64 * WAF * WAT) gma_proj_kernel(ProjArgs a) {
 
   // Lane (s16, g) of tile (fm, tn) holds features f..f+3, f = 16 fm + 4 g, of
   // token 16 tn + s16; four consecutive features never straddle a head.
-  const int dh = a.dh[m];
+  const int dh = a.dh[m], lgd = __builtin_ctz(dh);     // d is a power of two
   void* __restrict__ out = a.out[m];
   bf16* __restrict__ lo = m < 2 ? a.lo[m] : nullptr;
+  // (batch, position) of the tile's first token, once per workgroup; a tile of
+  // BT tokens crosses at most one batch boundary when N >= BT
+  const int64_t b0 = tok0 / a.N, n0 = tok0 - b0 * a.N;
 #pragma unroll
   for (int tn = 0; tn < WT; ++tn) {
-    const int64_t t = tok0 + wt * 16 * WT + tn * 16 + s16;
-    if (t >= a.M) continue;
-    const int64_t b = t / a.N, n = t - b * a.N;
+    const int r = wt * 16 * WT + tn * 16 + s16;
+    if (tok0 + r >= a.M) continue;
+    int64_t b = b0, n = n0 + r;
+    if (a.N >= T::BT) {
+      if (n >= a.N) {
+        n -= a.N;
+        ++b;
+      }
+    } else {
+      b += n / a.N;
+      n -= (n / a.N) * a.N;
+    }
 #pragma unroll
     for (int fm = 0; fm < WF; ++fm) {
       const int f = f0 + wf * 16 * WF + fm * 16 + 4 * g;
       if (f >= ncols) continue;
-      const int h = f / dh, j = f - h * dh;
+      const int h = f >> lgd, j = f & (dh - 1);
       const int64_t e = ((b * a.H + h) * a.N + n) * dh + j;
       if (!a.split) {
         st16(static_cast<float*>(out) + e, acc[fm][tn]);
@@ -225,6 +237,7 @@ hipError_t launch_proj(const void* X, const void* const W[3], void* const out[3]
   }
   const int d[3] = {d_r, d_r, d_v};
   for (int m = 0; m < 3; ++m) {
+    if (d[m] < 4 || (d[m] & (d[m] - 1))) return hipErrorInvalidValue;   // head dims: powers of two
     a.W[m] = static_cast<const bf16*>(W[m]);
     a.out[m] = out[m];
     a.dh[m] = d[m];
