@@ -899,16 +899,17 @@ static hipError_t run_bidir(const Plan& p, const Tensors& t, hipStream_t s) {
   a.x_lo = t.k_lo;
   a.v = t.v;
   a.assign = t.assign_k;
-  // token-owner write: about one workgroup per compute unit, each at least four
-  // 32-key groups; its splits replace the plan's (the partial buffer holds
-  // S * TG >= this many slots per sequence).  Split routing vectors (the
+  // token-owner write: about one workgroup per compute unit (two where two
+  // waves fit on a SIMD), each at least four 32-key groups; its splits
+  // replace the plan's (the partial buffer holds S * TG >= this many slots per
+  // sequence).  Split routing vectors (the
   // layer's projections) run only on the token-owner kernels.
   int PS = C::kBF ? p.S : p.S * C::TG;          // partial slots per sequence
   if (split && !(Write2<C>::kOK && Read2<C>::kOK)) return hipErrorNotSupported;
   if (g_launch_hook) g_launch_hook("gma_write", s, 1);
   if constexpr (Write2<C>::kOK) {
     const int64_t g32 = (p.N + 31) / 32;
-    int64_t s2 = (256 + p.BH - 1) / p.BH;
+    int64_t s2 = (256 * Write2<C>::WPE + p.BH - 1) / p.BH;
     const int64_t cap = (g32 + 3) / 4;
     if (s2 > cap) s2 = cap;
     if (s2 > PS) s2 = PS;

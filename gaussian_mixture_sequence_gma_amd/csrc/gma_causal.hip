@@ -854,9 +854,10 @@ static hipError_t run_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   wa.assign = nullptr;
   const dim3 grid(p.nspan, (unsigned)p.BH);
   if (g_launch_hook) g_launch_hook("gma_span_state", s, 1);
-  // the token-owner write pays a per-workgroup set-up: use it for long spans
-  // (at least eight 32-token steps per wave), one split per span
-  if (Write2<C>::kOK && (split || p.span_tiles >= 16)) {
+  // the token-owner write pays a per-workgroup set-up (its coefficient table):
+  // use it for spans of at least four 32-token steps per wave, or eight where
+  // it runs one wave per SIMD; one split per span
+  if (Write2<C>::kOK && (split || p.span_tiles >= (Write2<C>::WPE == 2 ? 4 : 16))) {
     wa.gpw = 2 * p.span_tiles;
     if constexpr (Write2<C>::kOK) {
       if (split) hipLaunchKernelGGL((gma_write2_kernel<C, true>), grid, dim3(256), 0, s, wa);

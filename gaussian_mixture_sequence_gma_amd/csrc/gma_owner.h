@@ -86,10 +86,12 @@ struct Write2 {
   static constexpr int LDS = LOOP_LDS > RED_LDS ? LOOP_LDS : RED_LDS;
   static constexpr bool kOK = C::kBF && KP % 32 == 0 && C::DRP <= 64 && C::DV >= 32 &&
                               LDS <= 160 * 1024 && CT * DVT * 4 <= 256;
+  // waves per SIMD: two where V~ takes at most 64 accumulation registers
+  static constexpr int WPE = CT * DVT * 4 <= 64 ? 2 : 1;
 };
 
 template <class C, bool XS>
-__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Write2<C>::WPE, Write2<C>::WPE)))
 gma_write2_kernel(BidirArgs a) {
   using R = Write2<C>;
   constexpr int NW = 4;
