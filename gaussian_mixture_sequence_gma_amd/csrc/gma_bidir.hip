@@ -443,12 +443,17 @@ struct Read2 {
   static constexpr int LDS = (COEF + VCH) * 1024 + KP * 4;
   static constexpr bool kOK = C::kBF && C::Kp % 32 == 0 && C::DRP <= 64 && LDS <= 150 * 1024;
 };
+// Waves per SIMD of the read-out (one workgroup of 4 * WPE waves per compute
+// unit): three where the registers allow (plain routing vectors), two for
+// split ones (their features take more registers).
+template <bool XS> constexpr int kRead2WPE = XS ? 2 : 3;
 
 template <class C, bool XS>
-__global__ void __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(256 * kRead2WPE<XS>, 1)
+__attribute__((amdgpu_waves_per_eu(kRead2WPE<XS>, kRead2WPE<XS>)))
 gma_read2_kernel(BidirArgs a) {
   using R = Read2<C>;
-  constexpr int NW = 8;
+  constexpr int NW = 4 * kRead2WPE<XS>;
   __shared__ __attribute__((aligned(16))) bf16x8 coef[R::COEF * 64];
   __shared__ __attribute__((aligned(16))) bf16x8 vtab[R::VCH * 64];
   __shared__ __attribute__((aligned(16))) float cperm[R::KP];
@@ -506,13 +511,6 @@ gma_read2_kernel(BidirArgs a) {
     // the tables are loop-invariant: keep the compiler from hoisting all of
     // their reads (far more registers than a wave has) out of the loop
     asm volatile("" ::: "memory");
-    // features of both query tiles
-    bf16x8 f[2][R::NKS][NFX<XS>];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int s = 0; s < R::NKS; ++s) make_features<XS>(xr[tt][s], xl[tt][s], f[tt][s]);
-
     // scores, two component tiles at a time (four independent accumulators)
     f32x4 S[2][R::CT];
 #pragma unroll
@@ -521,34 +519,48 @@ gma_read2_kernel(BidirArgs a) {
       S[0][ct] = cs;
       S[1][ct] = cs;
     }
-    // steps j = (tile pair, routing chunk); the operands of step j + 1 are read
-    // from LDS while the 20 MFMAs of step j run
-    constexpr int NSTEP = R::CT / 2 * R::NKS;
+    // steps j = (routing chunk s outer, tile pair inner): the features of one
+    // routing chunk are live at a time.  With three waves per SIMD the other
+    // waves cover the LDS latency of each step's operands; with two, the
+    // operands of step j + 1 are read while the MFMAs of step j run.
+    constexpr int NCP = R::CT / 2;
+    constexpr int NSTEP = NCP * R::NKS;
+    constexpr int NBUF = kRead2WPE<XS> >= 3 ? 1 : 2;
     auto load_w = [&](int j, bf16x8 (&w)[2][4]) {
-      const int cp = 2 * (j / R::NKS), s = j % R::NKS;
+      const int cp = 2 * (j % NCP), s = j / NCP;
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int ar = 0; ar < 4; ++ar) w[u][ar] = coef[(((cp + u) * R::NKS + s) * 4 + ar) * 64 + lane];
     };
-    bf16x8 wbuf[2][2][4];
-    load_w(0, wbuf[0]);
+    bf16x8 wbuf[NBUF][2][4];
+    bf16x8 f[2][NFX<XS>];
+    if constexpr (NBUF == 2) load_w(0, wbuf[0]);
 #pragma unroll
     for (int j = 0; j < NSTEP; ++j) {
-      if (j + 1 < NSTEP) load_w(j + 1, wbuf[(j + 1) & 1]);
-      // keep the prefetch one full step ahead of its use
-      __builtin_amdgcn_sched_barrier(0);
-      const int cp = 2 * (j / R::NKS), s = j % R::NKS;
+      const int cp = 2 * (j % NCP), s = j / NCP;
+      if (j % NCP == 0) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) make_features<XS>(xr[tt][s], xl[tt][s], f[tt]);
+        if (s == R::NKS - 1 && grp + NW < ge) load_x(grp + NW);
+      }
+      if constexpr (NBUF == 2) {
+        if (j + 1 < NSTEP) load_w(j + 1, wbuf[(j + 1) & 1]);
+        // keep the prefetch one full step ahead of its use
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        load_w(j, wbuf[0]);
+      }
+      bf16x8 (&w)[2][4] = wbuf[NBUF == 2 ? (j & 1) : 0];
 #pragma unroll
       for (int q = 0; q < NQX<XS>; ++q)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int u = 0; u < 2; ++u)
-            S[tt][cp + u] = mma(wbuf[j & 1][u][kWI[q]], f[tt][s][kFI[q]], S[tt][cp + u]);
-      __builtin_amdgcn_sched_barrier(0);
+            S[tt][cp + u] = mma(w[u][kWI[q]], f[tt][kFI[q]], S[tt][cp + u]);
+      if constexpr (NBUF == 2) __builtin_amdgcn_sched_barrier(0);
     }
-    if (grp + NW < ge) load_x(grp + NW);
 
     // per query: max over components (in-lane, then across the four lane
     // groups), e = exp2(s - m) packed as the read-out operand
@@ -955,9 +967,11 @@ static hipError_t run_bidir(const Plan& p, const Tensors& t, hipStream_t s) {
     if (s2 > cap) s2 = cap;
     if (s2 < 1) s2 = 1;
     if (split)
-      hipLaunchKernelGGL((gma_read2_kernel<C, true>), dim3((unsigned)s2, (unsigned)p.BH), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((gma_read2_kernel<C, true>), dim3((unsigned)s2, (unsigned)p.BH),
+                         dim3(256 * kRead2WPE<true>), 0, s, a);
     else
-      hipLaunchKernelGGL((gma_read2_kernel<C, false>), dim3((unsigned)s2, (unsigned)p.BH), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((gma_read2_kernel<C, false>), dim3((unsigned)s2, (unsigned)p.BH),
+                         dim3(256 * kRead2WPE<false>), 0, s, a);
   } else {
     hipLaunchKernelGGL((gma_read_kernel<C, 0>), grid, dim3(kThreads), 0, s, a);
   }
