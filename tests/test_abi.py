@@ -120,3 +120,51 @@ def test_timing_collect_empty():
     B.gma_timing_enable(True)
     B.gma_timing_enable(False)
     assert B.gma_timing_collect() == []
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+@pytest.mark.parametrize("kw,fmt", [
+    # bf16 token-owner kernels take split routing vectors: split bf16 projections
+    ({}, B.GMA_PROJ_SPLIT_BF16),
+    ({"K": 32, "N": 16384}, B.GMA_PROJ_SPLIT_BF16),
+    ({"K": 128, "d_v": 128}, B.GMA_PROJ_SPLIT_BF16),
+    # d_r = 128 exceeds the token-owner kernels: fp32 projections, fp32 path
+    ({"d_r": 128}, B.GMA_PROJ_F32),
+])
+def test_layer_projection_layout(kw, fmt, causal):
+    d = _dims(**kw)
+    got, offs = B.gma_layer_projection_layout(d, 256, causal)
+    total = B.gma_layer_workspace_bytes(d, 256, causal)
+    assert got == fmt
+    T = d.B * d.H * d.N
+    if got == B.GMA_PROJ_F32:
+        sizes = [4 * T * d.d_r, 4 * T * d.d_r, 4 * T * d.d_v]
+        used = offs[:3]
+        assert offs[3] == offs[4] == 0
+    else:
+        sizes = [2 * T * d.d_r] * 4 + [2 * T * d.d_v]
+        used = offs
+    # arrays in order, 16-byte aligned, not overlapping, inside the workspace
+    for i, (o, n) in enumerate(zip(used, sizes)):
+        assert o % 16 == 0
+        assert o + n <= total
+        if i + 1 < len(used):
+            assert o + n <= used[i + 1]
+    # the projections fill the tail of the workspace, after the GMA part
+    assert used[0] > 0
+    assert total - (used[-1] + sizes[-1]) < 256
+
+
+def test_layer_projection_layout_errors():
+    fmt, offs = B.gma_layer_projection_layout(_dims(), 256, 0)
+    assert fmt in (B.GMA_PROJ_F32, B.GMA_PROJ_SPLIT_BF16)
+    with pytest.raises(B.GmaError) as ei:
+        B.gma_layer_projection_layout(_dims(), 100, 0)          # d_model not a multiple of 64
+    assert ei.value.status == B.GMA_ERR_UNSUPPORTED
+    with pytest.raises(B.GmaError) as ei:
+        B.gma_layer_projection_layout(_dims(dtype=B.GMA_F32), 256, 0)
+    assert ei.value.status == B.GMA_ERR_UNSUPPORTED
+    lib = B.load()
+    out = (ctypes.c_size_t * 5)()
+    assert lib.gma_layer_projection_layout(ctypes.byref(_dims()), 256, 0, None,
+                                           ctypes.byref(out)) == B.GMA_ERR_INVALID_ARG

@@ -119,3 +119,10 @@ def test_layer_full_size_sampled_rows():
     # the full layer shape in the launch configuration bench.py times
     w = W["layer_causal_bf16"]
     _run(w, rows=inputs.sample_rows(w.N, 256, seed=3))
+
+
+def test_layer_full_size_bidirectional_sampled_rows():
+    # the full layer shape, bidirectional: split projections into the bf16
+    # token-owner write and read-out
+    w = W["layer_causal_bf16"].with_(causal=False)
+    _run(w, rows=inputs.sample_rows(w.N, 256, seed=4))
