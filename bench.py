@@ -65,19 +65,20 @@ def kernel_bytes(name: str, w, s_r: int, s_v: int, s_out: int) -> int:
     return 0
 
 
-def traffic_from_profile(kernel: str, workload: str, src_hash: str):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
+def profile_counters(kernel: str, workload: str, src_hash: str) -> dict:
+    """The committed rocprofv3 counter summary of a kernel on a workload (HBM
+    bytes per launch, MFMA busy fraction), if it was taken on the current
+    kernel source; else {}."""
     path = os.path.join(ROOT, "profiles", "%s_%s_counters.json" % (kernel, workload))
     if not os.path.exists(path):
-        return None
+        return {}
     try:
         d = json.load(open(path))
     except ValueError:
-        return None
+        return {}
     if d.get("source_sha256") != src_hash:
-        return None
-    return d.get("hbm_bytes_per_launch")
+        return {}
+    return d
 
 
 def kernel_source_hash() -> str:
@@ -251,19 +252,22 @@ def main():
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
     dom_bytes = kernel_bytes(dom, w, s_r, s_v, s_out)
     dom_flops = kernel_flops(dom, w)
-    traffic = traffic_from_profile(dom, w.name, kernel_source_hash())
+    prof = profile_counters(dom, w.name, kernel_source_hash())
+    traffic = prof.get("hbm_bytes_per_launch")
     t_dom = kernels[dom]["avg_us"] * 1e-6
     if dom_flops:
         achieved = dom_flops / t_dom / 1e12
         roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved,
                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic,
+                    "mfma_busy": prof.get("mfma_busy"),
                     "alg_flops_per_launch": dom_flops, "alg_bytes_per_launch": dom_bytes}
     else:
         achieved = dom_bytes / t_dom / 1e9 if dom_bytes else None
         roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
-                    "traffic": traffic, "alg_bytes_per_launch": dom_bytes}
+                    "traffic": traffic, "mfma_busy": prof.get("mfma_busy"),
+                    "alg_bytes_per_launch": dom_bytes}
     step_bytes = sum(kernel_bytes(k, w, s_r, s_v, s_out) for k in kernels)
 
     cpu = None
