@@ -546,25 +546,31 @@ gma_causal2_kernel(CausalArgs a) {
       for (int i = 0; i < 4; ++i)
         sacc[j][dt][i] = a.carry[(sslot * C::Kp + comp0 + 4 * g + i) * C::DV + dt * 16 + c];
   }
-  // this wave's rows of the state table: S^T (d rows in pair_row order) and Z
+  // this wave's rows of the state table: S^T (d rows in pair_row order) and Z.
+  // A lane's four components 4g .. 4g+3 of a tile are four consecutive
+  // elements of one 16-byte operand chunk: one 8-byte store per (tile, d).
   auto write_st = [&]() {
 #pragma unroll
     for (int j = 0; j < R::CTW; ++j) {
-      const int comp0 = (w * R::CTW + j) * 16;
+      const int comp = (w * R::CTW + j) * 16 + 4 * g;
+      const int p = comp >> 5, gg = (comp & 31) >> 3, e = comp & 7;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int comp = comp0 + 4 * g + i;
-        const int p = comp >> 5, gg = (comp & 31) >> 3, e = comp & 7;
+      for (int dt = 0; dt < R::DVT; ++dt) {
+        const int d = dt * 16 + c;
+        bf16x4 v;
 #pragma unroll
-        for (int dt = 0; dt < R::DVT; ++dt) {
-          const int d = dt * 16 + c;
-          ST[((pair_tile(d) * R::KS + p) * 64 + pair_rowof(d) + 16 * gg) * 8 + e] = to_bf16(sacc[j][dt][i]);
-        }
-        if (c < 2) {
+        for (int i = 0; i < 4; ++i) v[i] = to_bf16(sacc[j][dt][i]);
+        *reinterpret_cast<bf16x4*>(&ST[((pair_tile(d) * R::KS + p) * 64 + pair_rowof(d) + 16 * gg) * 8 + e]) = v;
+      }
+      if (c < 2) {
+        bf16x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
           const float zz = zacc[j][i];
           const float zh = from_bf16(to_bf16(zz));
-          ST[((R::DVT * R::KS + p) * 64 + c + 16 * gg) * 8 + e] = to_bf16(c == 0 ? zz : zz - zh);
+          v[i] = to_bf16(c == 0 ? zz : zz - zh);
         }
+        *reinterpret_cast<bf16x4*>(&ST[((R::DVT * R::KS + p) * 64 + c + 16 * gg) * 8 + e]) = v;
       }
     }
   };
