@@ -581,8 +581,14 @@ gma_causal2_kernel(CausalArgs a) {
   const bf16* vs = reinterpret_cast<const bf16*>(a.v) + (size_t)bh * a.N * C::DV;
   const bf16* qls = XS ? reinterpret_cast<const bf16*>(a.q_lo) + (size_t)bh * a.N * C::DR : qs;
   const bf16* kls = XS ? reinterpret_cast<const bf16*>(a.k_lo) + (size_t)bh * a.N * C::DR : ks;
-  bf16x8 xq[R::NKS], xk[R::NKS], xql[R::NKS], xkl[R::NKS];
-  auto load_x = [&](int k) {
+  // routing vectors of a chunk; plain ones are loaded two chunks ahead (two
+  // register buffers, chunks alternating between them), split ones one chunk
+  // ahead (their registers would not fit twice)
+  constexpr bool XPF = !XS;
+  bf16x8 xqA[R::NKS], xkA[R::NKS], xqlA[R::NKS], xklA[R::NKS];
+  bf16x8 xqB[R::NKS], xkB[R::NKS], xqlB[R::NKS], xklB[R::NKS];
+  auto load_x = [&](int k, bf16x8 (&xq)[R::NKS], bf16x8 (&xk)[R::NKS], bf16x8 (&xql)[R::NKS],
+                    bf16x8 (&xkl)[R::NKS]) {
     const int64_t tok = t_begin + (int64_t)k * kTile + 16 * w + c;
 #pragma unroll
     for (int s = 0; s < R::NKS; ++s) {
@@ -622,12 +628,17 @@ gma_causal2_kernel(CausalArgs a) {
     ones_r3[e] = (bf16)(c == 3 ? 1.0f : 0.0f);          // A operand: row 3 = 1
   }
   if (nchunks > 0) {
-    load_x(0);
+    load_x(0, xqA, xkA, xqlA, xklA);
     load_v(0, 0);
   }
+  if (XPF && nchunks > 1) load_x(1, xqB, xkB, xqlB, xklB);
   __syncthreads();                       // coefficient table and seeds visible to every wave
 
-  for (int k = 0; k < nchunks; ++k) {
+  // one chunk; xq .. xkl hold its routing vectors and afterwards receive those
+  // of chunk k + XD
+  constexpr int XD = XPF ? 2 : 1;
+  auto chunk = [&](int k, bf16x8 (&xq)[R::NKS], bf16x8 (&xk)[R::NKS], bf16x8 (&xql)[R::NKS],
+                   bf16x8 (&xkl)[R::NKS]) {
     const int buf = R::NB == 2 ? (k & 1) : 0;
     const int64_t tile0 = t_begin + (int64_t)k * kTile;
     const int64_t rem = t_end - tile0;
@@ -746,10 +757,10 @@ gma_causal2_kernel(CausalArgs a) {
     }
     wait_global_loads();                 // V(k) and this wave's loads
     lds_barrier();                                                    // B1
-    if (k + 1 < nchunks) {
-      if constexpr (R::NB == 2) load_v(k + 1, buf ^ 1);
-      load_x(k + 1);
+    if constexpr (R::NB == 2) {
+      if (k + 1 < nchunks) load_v(k + 1, buf ^ 1);
     }
+    if (k + XD < nchunks) load_x(k + XD, xq, xk, xql, xkl);
 
     // ---- outputs of this wave's 16 queries ------------------------------------
     f32x4 acc[R::OT];
@@ -833,6 +844,14 @@ gma_causal2_kernel(CausalArgs a) {
       lds_barrier();                                                  // B3: G, V free
       if (k + 1 < nchunks) load_v(k + 1, 0);
     }
+  };
+  if constexpr (XPF) {
+    for (int k = 0; k < nchunks; k += 2) {
+      chunk(k, xqA, xkA, xqlA, xklA);
+      if (k + 1 < nchunks) chunk(k + 1, xqB, xkB, xqlB, xklB);
+    }
+  } else {
+    for (int k = 0; k < nchunks; ++k) chunk(k, xqA, xkA, xqlA, xklA);
   }
 }
 
