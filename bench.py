@@ -11,7 +11,9 @@ Timing: W untimed warm-up steps, then K steps timed with events on the stream
 (ms_per_step and value), then the same K steps again with a hipEvent pair the
 library records around each of its launches on the launch stream (per-kernel
 durations; the events add a few microseconds between launches, so that pass's
-step time is reported apart).
+step time is reported apart).  Unless --no-flush, a 512 MiB fill runs between
+steps, outside the timed events, so that no workload is served from the 256 MB
+Infinity Cache.
 
 Roofline: the dominant kernel's algorithmic bytes (flops, for the MFMA-bound
 projection GEMM of the layer workload) per launch divided by its average
@@ -143,6 +145,8 @@ def main():
     ap.add_argument("--workload", default="long_bidir_bf16")
     ap.add_argument("--causal", type=int, default=None, help="override the workload's variant")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", dest="flush", action="store_false",
+                    help="do not evict the Infinity Cache between timed steps")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device-to-device copy `steps` times (reference "
                          "kernel of known traffic for scaling HBM byte counters) and exit")
@@ -216,36 +220,58 @@ def main():
             binding.gma_forward(Q, K, V, mu, ls2, lpi, w.eps, int(w.causal), out, dims,
                                 None, None, ws, ws.numel())
 
+    # Between timed steps a 512 MiB fill evicts the 256 MB Infinity Cache (and
+    # L2), so a workload whose tensors would fit there is still read from HBM;
+    # each step is then timed by its own event pair, the fill outside it.
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.flush else None
+
+    def flush():
+        if flush_buf is not None:
+            flush_buf.fill_(1)
+
     for _ in range(args.warmup):
+        flush()
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+
+    def timed(k):
+        """Mean ms per step over k steps (event pairs on the launch stream)."""
+        if flush_buf is None:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(k):
+                step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / k
+        pairs = []
+        torch.cuda.synchronize()
+        for _ in range(k):
+            flush()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in pairs) / k
+
     # timed region 1: K steps as a user runs them -> ms_per_step and value
     binding.gma_timing_enable(False)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms = timed(args.steps)
     value = w.tokens_heads / (ms * 1e-3)
     # timed region 2: the same K steps with a hipEvent pair around every launch
     # (recorded by the library on the launch stream) -> per-kernel durations;
     # the events themselves add a few microseconds between launches, so this
-    # region's wall time is reported separately
+    # region's step time is reported separately
     binding.gma_timing_collect()            # discard anything left over
     binding.gma_timing_enable(True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
+    ms_instrumented = timed(args.steps)
     binding.gma_timing_enable(False)
-    ms_instrumented = ev0.elapsed_time(ev1) / args.steps
     kt = binding.gma_timing_collect()
 
     kernels = {name: {"launches": n, "avg_us": 1e3 * tot / max(n, 1)} for name, n, tot in kt}
@@ -279,6 +305,7 @@ def main():
            "kernel_avg_us": {k: round(v["avg_us"], 2) for k, v in kernels.items()},
            "kernel_timing": "second pass of the K steps with a hipEvent pair around each launch "
                             "(%.4f ms/step in that pass)" % ms_instrumented,
+           "cache_flush": "512 MiB fill between timed steps" if args.flush else None,
            "step_hbm_frac": (step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS) if step_bytes else None}
     if w.d_model:
         cfg["d_model"] = w.d_model
