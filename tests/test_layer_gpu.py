@@ -126,3 +126,12 @@ def test_layer_full_size_bidirectional_sampled_rows():
     # token-owner write and read-out
     w = W["layer_causal_bf16"].with_(causal=False)
     _run(w, rows=inputs.sample_rows(w.N, 256, seed=4))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_layer_large_mixture(causal):
+    # K = 128 and d_v = 128 on split projections: the split variants of the
+    # one-wave-per-SIMD write, the read-out and the scan at their largest tables
+    w = W["layer_causal_bf16"].with_(B=1, H=3, N=333, d_r=64, d_v=128, K=128, d_model=256,
+                                     causal=causal)
+    _run(w)
