@@ -193,28 +193,26 @@ gma_write2_kernel(BidirArgs a) {
       S[0][ct] = f32x4{cv, cv, cv, cv};
       S[1][ct] = S[0][ct];
     }
-    constexpr int NSTEP = R::CT / 2 * R::NKS;
-    auto load_w = [&](int j, bf16x8 (&w)[2][4]) {
-      const int cp = 2 * (j / R::NKS), s = j % R::NKS;
+    // half-steps h = (component tile, routing chunk): the four operands of
+    // half-step h + 1 are read from LDS while the MFMAs of h run
+    constexpr int NH = R::CT * R::NKS;
+    auto load_w = [&](int hs, bf16x8 (&w)[4]) {
+      const int ct = hs / R::NKS, s = hs % R::NKS;
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int ar = 0; ar < 4; ++ar) w[u][ar] = coef[(((cp + u) * R::NKS + s) * 4 + ar) * 64 + lane];
+      for (int ar = 0; ar < 4; ++ar) w[ar] = coef[((ct * R::NKS + s) * 4 + ar) * 64 + lane];
     };
-    bf16x8 wbuf[2][2][4];
+    bf16x8 wbuf[2][4];
     load_w(0, wbuf[0]);
 #pragma unroll
-    for (int j = 0; j < NSTEP; ++j) {
-      if (j + 1 < NSTEP) load_w(j + 1, wbuf[(j + 1) & 1]);
+    for (int hs = 0; hs < NH; ++hs) {
+      if (hs + 1 < NH) load_w(hs + 1, wbuf[(hs + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
-      const int cp = 2 * (j / R::NKS), s = j % R::NKS;
+      const int ct = hs / R::NKS, s = hs % R::NKS;
 #pragma unroll
       for (int q = 0; q < NQX<XS>; ++q)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
-            S[tt][cp + u] = mma(f[tt][s][kFI[q]], wbuf[j & 1][u][kWI[q]], S[tt][cp + u]);
+          S[tt][ct] = mma(f[tt][s][kFI[q]], wbuf[hs & 1][kWI[q]], S[tt][ct]);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (more) load_x(grp + NW);
