@@ -581,10 +581,8 @@ gma_causal2_kernel(CausalArgs a) {
   const bf16* vs = reinterpret_cast<const bf16*>(a.v) + (size_t)bh * a.N * C::DV;
   const bf16* qls = XS ? reinterpret_cast<const bf16*>(a.q_lo) + (size_t)bh * a.N * C::DR : qs;
   const bf16* kls = XS ? reinterpret_cast<const bf16*>(a.k_lo) + (size_t)bh * a.N * C::DR : ks;
-  // routing vectors of a chunk; plain ones are loaded two chunks ahead (two
-  // register buffers, chunks alternating between them), split ones one chunk
-  // ahead (their registers would not fit twice)
-  constexpr bool XPF = !XS;
+  // routing vectors of a chunk, loaded two chunks ahead: two register
+  // buffers, chunks alternating between them
   bf16x8 xqA[R::NKS], xkA[R::NKS], xqlA[R::NKS], xklA[R::NKS];
   bf16x8 xqB[R::NKS], xkB[R::NKS], xqlB[R::NKS], xklB[R::NKS];
   auto load_x = [&](int k, bf16x8 (&xq)[R::NKS], bf16x8 (&xk)[R::NKS], bf16x8 (&xql)[R::NKS],
@@ -631,12 +629,11 @@ gma_causal2_kernel(CausalArgs a) {
     load_x(0, xqA, xkA, xqlA, xklA);
     load_v(0, 0);
   }
-  if (XPF && nchunks > 1) load_x(1, xqB, xkB, xqlB, xklB);
+  if (nchunks > 1) load_x(1, xqB, xkB, xqlB, xklB);
   __syncthreads();                       // coefficient table and seeds visible to every wave
 
   // one chunk; xq .. xkl hold its routing vectors and afterwards receive those
-  // of chunk k + XD
-  constexpr int XD = XPF ? 2 : 1;
+  // of chunk k + 2
   auto chunk = [&](int k, bf16x8 (&xq)[R::NKS], bf16x8 (&xk)[R::NKS], bf16x8 (&xql)[R::NKS],
                    bf16x8 (&xkl)[R::NKS]) {
     const int buf = R::NB == 2 ? (k & 1) : 0;
@@ -660,28 +657,26 @@ gma_causal2_kernel(CausalArgs a) {
       SK[ct] = cs;
     }
     {
-      constexpr int NSTEP = R::CT / 2 * R::NKS;
-      auto load_w = [&](int j, bf16x8 (&wv)[2][4]) {
-        const int cp = 2 * (j / R::NKS), s = j % R::NKS;
+      // half-steps h = (component tile, routing chunk): the four operands of
+      // half-step h + 1 are read from LDS while the MFMAs of h run
+      constexpr int NH = R::CT * R::NKS;
+      auto load_w = [&](int hs, bf16x8 (&wv)[4]) {
+        const int ct = hs / R::NKS, s = hs % R::NKS;
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int ar = 0; ar < 4; ++ar) wv[u][ar] = coef[(((cp + u) * R::NKS + s) * 4 + ar) * 64 + lane];
+        for (int ar = 0; ar < 4; ++ar) wv[ar] = coef[((ct * R::NKS + s) * 4 + ar) * 64 + lane];
       };
-      bf16x8 wbuf[2][2][4];
+      bf16x8 wbuf[2][4];
       load_w(0, wbuf[0]);
 #pragma unroll
-      for (int j = 0; j < NSTEP; ++j) {
-        if (j + 1 < NSTEP) load_w(j + 1, wbuf[(j + 1) & 1]);
+      for (int hs = 0; hs < NH; ++hs) {
+        if (hs + 1 < NH) load_w(hs + 1, wbuf[(hs + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
-        const int cp = 2 * (j / R::NKS), s = j % R::NKS;
+        const int ct = hs / R::NKS, s = hs % R::NKS;
 #pragma unroll
-        for (int q = 0; q < NQX<XS>; ++q)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            SQ[cp + u] = mma(wbuf[j & 1][u][kWI[q]], fq[s][kFI[q]], SQ[cp + u]);
-            SK[cp + u] = mma(wbuf[j & 1][u][kWI[q]], fk[s][kFI[q]], SK[cp + u]);
-          }
+        for (int q = 0; q < NQX<XS>; ++q) {
+          SQ[ct] = mma(wbuf[hs & 1][kWI[q]], fq[s][kFI[q]], SQ[ct]);
+          SK[ct] = mma(wbuf[hs & 1][kWI[q]], fk[s][kFI[q]], SK[ct]);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -760,7 +755,7 @@ gma_causal2_kernel(CausalArgs a) {
     if constexpr (R::NB == 2) {
       if (k + 1 < nchunks) load_v(k + 1, buf ^ 1);
     }
-    if (k + XD < nchunks) load_x(k + XD, xq, xk, xql, xkl);
+    if (k + 2 < nchunks) load_x(k + 2, xq, xk, xql, xkl);
 
     // ---- outputs of this wave's 16 queries ------------------------------------
     f32x4 acc[R::OT];
@@ -845,13 +840,9 @@ gma_causal2_kernel(CausalArgs a) {
       if (k + 1 < nchunks) load_v(k + 1, 0);
     }
   };
-  if constexpr (XPF) {
-    for (int k = 0; k < nchunks; k += 2) {
-      chunk(k, xqA, xkA, xqlA, xklA);
-      if (k + 1 < nchunks) chunk(k + 1, xqB, xkB, xqlB, xklB);
-    }
-  } else {
-    for (int k = 0; k < nchunks; ++k) chunk(k, xqA, xkA, xqlA, xklA);
+  for (int k = 0; k < nchunks; k += 2) {
+    chunk(k, xqA, xkA, xqlA, xklA);
+    if (k + 1 < nchunks) chunk(k + 1, xqB, xkB, xqlB, xklB);
   }
 }
 
