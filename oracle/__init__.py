@@ -154,6 +154,31 @@ def responsibilities(X, mu, log_sigma2, log_pi) -> dict:
     return {"gamma": gamma, "assign": assign, "score": score}
 
 
+def decode_step(S, z, q, k, v, mu, log_sigma2, log_pi, eps: float) -> dict:
+    """One token of the causal form from a carried prefix state ("Causal GMA":
+    the prefix memories V~^(i), Z^(i) and Eq. 8b, prefix j <= i inclusive).
+
+    The state of a prefix is V~ = sum_j gamma^K_j (outer) v_j and Z = sum_j
+    gamma^K_j over its tokens.  Appending token i adds its own key term, then
+    its query reads the updated state:
+      S' = S + gamma^K(k_i) (outer) v_i,  z' = z + gamma^K(k_i),
+      o_i = gamma^Q(q_i) . S' / (gamma^Q(q_i) . z' + eps).
+    S [B,H,K,d_v], z [B,H,K], q, k [B,H,d_r], v [B,H,d_v]; the responsibilities
+    are the C oracle's (Eq. 3).  Returns dict(S, z, out [B,H,d_v], assign_q,
+    assign_k), all float64 (assignments int32).
+    """
+    S, z, v = _f64(S), _f64(z), _f64(v)
+    rq = responsibilities(_f64(q)[:, :, None, :], mu, log_sigma2, log_pi)
+    rk = responsibilities(_f64(k)[:, :, None, :], mu, log_sigma2, log_pi)
+    gq, gk = rq["gamma"][:, :, 0], rk["gamma"][:, :, 0]          # [B,H,K]
+    S2 = S + gk[:, :, :, None] * v[:, :, None, :]
+    z2 = z + gk
+    num = np.einsum("bhk,bhkd->bhd", gq, S2)
+    den = np.einsum("bhk,bhk->bh", gq, z2) + eps
+    return {"S": S2, "z": z2, "out": num / den[:, :, None],
+            "assign_q": rq["assign"][:, :, 0], "assign_k": rk["assign"][:, :, 0]}
+
+
 def project(X, W, H: int) -> np.ndarray:
     """Eq. 4: X [B,N,d_model] times W [d_model, H*d] in float64, split into heads.
 
