@@ -64,6 +64,11 @@ def kernel_bytes(name: str, w, s_r: int, s_v: int, s_out: int) -> int:
         return T * (w.d_r * s_r + w.d_v * s_out)
     if name == "gma_causal":
         return T * (2 * w.d_r * s_r + w.d_v * s_v + w.d_v * s_out)
+    if name == "gma_decode":
+        # the fp32 state (S, z) read and written, the token's q, k, v and o,
+        # and each head's mixture parameters once
+        return w.B * w.H * (8 * w.K * (w.d_v + 1) + 2 * w.d_r * s_r + w.d_v * (s_v + s_out)) + \
+            w.H * w.K * (2 * w.d_r + 1) * 4
     return 0
 
 
@@ -100,6 +105,8 @@ def cpu_baseline(w, gen, max_threads: int = 16, min_seconds: float = 10.0,
     max_seconds - last group's time is skipped)."""
     import oracle
     threads = max(1, min(max_threads, os.cpu_count() or 1))
+    if w.state_len > 0:
+        return cpu_baseline_decode(w, gen, min_seconds, max_seconds)
     per = min(w.H, 2 * threads)
     groups = [(b, h0) for b in range(w.B) for h0 in range(0, w.H, per)]
     done = 0
@@ -135,6 +142,31 @@ def cpu_baseline(w, gen, max_threads: int = 16, min_seconds: float = 10.0,
             "sample": "%d groups of up to %d heads at full N=%d (%s %s, fp64), %d token-heads "
                       "of %d, %.1f s" % (gi, per, w.N, "causal" if w.causal else "bidirectional",
                                          what, done, w.tokens_heads, dt)}
+
+
+def cpu_baseline_decode(w, gen, min_seconds: float, max_seconds: float):
+    """The oracle's decode step over the whole batch (the carried state
+    advancing from call to call), repeated until min_seconds have passed."""
+    import oracle
+    S, z = gen["S"], gen["z"]
+    q, k, v = gen["Q"].f32[:, :, 0], gen["K"].f32[:, :, 0], gen["V"].f32[:, :, 0]
+    calls = 0
+    t0 = time.perf_counter()
+    last = 0.0
+    while True:
+        t1 = time.perf_counter()
+        r = oracle.decode_step(S, z, q, k, v, gen["mu"], gen["log_sigma2"], gen["log_pi"], w.eps)
+        S, z = r["S"], r["z"]
+        last = time.perf_counter() - t1
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or el + last > max_seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": calls * w.tokens_heads / dt, "unit": UNIT, "cores": 1, "kind": "oracle",
+            "sample": "%d decode steps over the whole batch (%d sequences x heads, fp64, "
+                      "numpy on one thread for the state update), %.1f s"
+                      % (calls, w.B * w.H, dt)}
 
 
 def main():
@@ -185,6 +217,7 @@ def main():
     s_out = 2 if w.dtype == "bf16" else 4
     s_r = s_v = s_out
 
+    decode = w.state_len > 0
     if w.d_model > 0:
         X = api.host_tensor_to_device(gen["X"], dev)
         WQ = api.host_tensor_to_device(gen["W_Q"], dev)
@@ -208,12 +241,19 @@ def main():
         # bf16 (V_X), or all in fp32
         fmt, _ = binding.gma_layer_projection_layout(dims, w.d_model, int(w.causal))
         s_r, s_v = (4, 2) if fmt == binding.GMA_PROJ_SPLIT_BF16 else (4, 4)
+    elif decode:
+        nbytes = 0
+        # the carried state, advanced in place by every step
+        S_state = torch.from_numpy(gen["S"]).to(dev)
+        z_state = torch.from_numpy(gen["z"]).to(dev)
     else:
         nbytes = binding.gma_forward_workspace_bytes(dims, int(w.causal))
     ws = api.alloc_workspace(nbytes, dev)
 
     def step():
-        if w.d_model > 0:
+        if decode:
+            binding.gma_decode_step(Q, K, V, mu, ls2, lpi, w.eps, S_state, z_state, out, dims)
+        elif w.d_model > 0:
             binding.gma_layer_forward(X, WQ, WK, WV, w.d_model, mu, ls2, lpi, w.eps,
                                       int(w.causal), out, dims, None, None, ws, ws.numel())
         else:
@@ -309,6 +349,9 @@ def main():
            "step_hbm_frac": (step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS) if step_bytes else None}
     if w.d_model:
         cfg["d_model"] = w.d_model
+    if decode:
+        cfg["step"] = "one decode token per sequence against a carried fp32 state"
+        cfg["state_len"] = w.state_len
     line = {"metric": METRIC, "value": value, "unit": UNIT, "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,

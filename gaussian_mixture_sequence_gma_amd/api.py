@@ -92,3 +92,39 @@ def responsibilities(X: torch.Tensor, mu: torch.Tensor, log_sigma2: torch.Tensor
     B.gma_responsibilities(X, mu, log_sigma2, log_pi, dims, gamma, assign, ws, ws.numel(),
                            stream)
     return gamma, assign
+
+
+def prefix_state(K: torch.Tensor, V: torch.Tensor, mu: torch.Tensor, log_sigma2: torch.Tensor,
+                 log_pi: torch.Tensor, assign: bool = False, stream=None):
+    """Carried causal state (S [B,H,K,d_v], z [B,H,K], fp32) after the keys and
+    values K [B,H,N,d_r], V [B,H,N,d_v]; optionally the key assignments."""
+    Bb, H, N, d_r = K.shape
+    d_v = V.shape[-1]
+    Kc = mu.shape[1]
+    dims = B.make_dims(Bb, H, N, d_r, d_v, Kc, torch_dtype_code(K))
+    ws = alloc_workspace(B.gma_forward_workspace_bytes(dims, 0), K.device)
+    S = torch.empty((Bb, H, Kc, d_v), dtype=torch.float32, device=K.device)
+    z = torch.empty((Bb, H, Kc), dtype=torch.float32, device=K.device)
+    ak = torch.empty((Bb, H, N), dtype=torch.int32, device=K.device) if assign else None
+    B.gma_prefix_state(K, V, mu, log_sigma2, log_pi, S, z, dims, ak, ws, ws.numel(), stream)
+    return (S, z, ak) if assign else (S, z)
+
+
+def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mu: torch.Tensor,
+                log_sigma2: torch.Tensor, log_pi: torch.Tensor, S: torch.Tensor,
+                z: torch.Tensor, eps: float = 1e-6, assign: bool = False,
+                out: Optional[torch.Tensor] = None, stream=None):
+    """One token per sequence, q, k [B,H,1,d_r], v [B,H,1,d_v]: returns o
+    [B,H,1,d_v] and updates S, z in place (optionally z^Q, z^K [B,H])."""
+    Bb, H, _, d_r = q.shape
+    d_v = v.shape[-1]
+    Kc = mu.shape[1]
+    dims = B.make_dims(Bb, H, 1, d_r, d_v, Kc, torch_dtype_code(q))
+    if out is None:
+        out = torch.empty((Bb, H, 1, d_v), dtype=v.dtype, device=v.device)
+    aq = ak = None
+    if assign:
+        aq = torch.empty((Bb, H), dtype=torch.int32, device=q.device)
+        ak = torch.empty((Bb, H), dtype=torch.int32, device=q.device)
+    B.gma_decode_step(q, k, v, mu, log_sigma2, log_pi, eps, S, z, out, dims, aq, ak, stream)
+    return (out, aq, ak) if assign else out

@@ -64,6 +64,8 @@ def load():
                                                 ctypes.POINTER(ctypes.c_int32),
                                                 ctypes.POINTER(S * 5)]
     lib.gma_responsibilities.argtypes = [P, P, P, P, D, P, P, P, S, P]
+    lib.gma_prefix_state.argtypes = [P, P, P, P, P, P, P, D, P, P, S, P]
+    lib.gma_decode_step.argtypes = [P, P, P, P, P, P, f32, P, P, P, D, P, P, P]
     lib.gma_status_string.argtypes = [i32]
     lib.gma_status_string.restype = ctypes.c_char_p
     lib.gma_last_error.argtypes = []
@@ -73,7 +75,7 @@ def load():
                                        ctypes.POINTER(ctypes.c_int)]
     for fn in ("gma_validate", "gma_forward_workspace_bytes", "gma_forward",
                "gma_layer_workspace_bytes", "gma_layer_forward", "gma_layer_projection_layout",
-               "gma_responsibilities",
+               "gma_responsibilities", "gma_prefix_state", "gma_decode_step",
                "gma_timing_enable", "gma_timing_collect"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -167,6 +169,22 @@ def gma_responsibilities(X_r, mu, log_sigma2, log_pi, dims: gma_dims, gamma=None
     _check(load().gma_responsibilities(_ptr(X_r), _ptr(mu), _ptr(log_sigma2), _ptr(log_pi),
                                        ctypes.byref(dims), _ptr(gamma), _ptr(assign),
                                        _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def gma_prefix_state(K_X, V_X, mu, log_sigma2, log_pi, state_v, state_z, dims: gma_dims,
+                     assign_k=None, workspace=None, workspace_bytes=0, stream=None):
+    _check(load().gma_prefix_state(_ptr(K_X), _ptr(V_X), _ptr(mu), _ptr(log_sigma2),
+                                   _ptr(log_pi), _ptr(state_v), _ptr(state_z),
+                                   ctypes.byref(dims), _ptr(assign_k), _ptr(workspace),
+                                   int(workspace_bytes), _stream(stream)))
+
+
+def gma_decode_step(q, k, v, mu, log_sigma2, log_pi, eps, state_v, state_z, out,
+                    dims: gma_dims, assign_q=None, assign_k=None, stream=None):
+    _check(load().gma_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(mu), _ptr(log_sigma2),
+                                  _ptr(log_pi), float(eps), _ptr(state_v), _ptr(state_z),
+                                  _ptr(out), ctypes.byref(dims), _ptr(assign_q),
+                                  _ptr(assign_k), _stream(stream)))
 
 
 def gma_status_string(status: int) -> str:

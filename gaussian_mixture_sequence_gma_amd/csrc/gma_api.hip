@@ -397,6 +397,76 @@ int gma_responsibilities(const void* X_r, const float* mu, const float* log_sigm
   return finish_launch(e, "responsibility launch");
 }
 
+int gma_prefix_state(const void* K_X, const void* V_X, const float* mu, const float* log_sigma2,
+                     const float* log_pi, float* state_v, float* state_z, const gma_dims* d,
+                     int32_t* assign_k, void* workspace, size_t workspace_bytes, void* stream) {
+  t_err.clear();
+  int st = check_dims(d, 0.f, 0);
+  if (st != GMA_OK) return st;
+  if (!K_X || !V_X || !mu || !log_sigma2 || !log_pi || !state_v || !state_z || !workspace)
+    return fail(GMA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(K_X) || !aligned16(V_X) || !aligned16(workspace) || !aligned16(mu) ||
+      !aligned16(log_sigma2) || !aligned16(state_v) || ((uintptr_t)log_pi & 3) ||
+      ((uintptr_t)state_z & 3) || ((uintptr_t)assign_k & 3))
+    return fail(GMA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  Plan p;
+  st = make_plan(d, 0, false, p);
+  if (st != GMA_OK) return st;
+  if (workspace_bytes < p.total) return fail(GMA_ERR_WORKSPACE, "workspace too small");
+  Tensors t;
+  t.k = K_X;
+  t.v = V_X;
+  t.mu = mu;
+  t.ls2 = log_sigma2;
+  t.lpi = log_pi;
+  t.assign_k = assign_k;
+  t.state_v = state_v;
+  t.state_z = state_z;
+  t.ws = static_cast<char*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_prologue(p, t, s);
+  if (e == hipSuccess) e = launch_bidir(p, t, s);
+  return finish_launch(e, "prefix state launch");
+}
+
+int gma_decode_step(const void* q, const void* k, const void* v, const float* mu,
+                    const float* log_sigma2, const float* log_pi, float eps, float* state_v,
+                    float* state_z, void* out, const gma_dims* d, int32_t* assign_q,
+                    int32_t* assign_k, void* stream) {
+  t_err.clear();
+  int st = check_dims(d, eps, 1);
+  if (st != GMA_OK) return st;
+  if (d->N != 1) return fail(GMA_ERR_INVALID_ARG, "a decode step takes N = 1 token per sequence");
+  if (!q || !k || !v || !mu || !log_sigma2 || !log_pi || !state_v || !state_z || !out)
+    return fail(GMA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(mu) ||
+      !aligned16(log_sigma2) || !aligned16(state_v) || ((uintptr_t)log_pi & 3) ||
+      ((uintptr_t)state_z & 3) || ((uintptr_t)assign_q & 3) || ((uintptr_t)assign_k & 3))
+    return fail(GMA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  Plan p;
+  p.out_bf = d->dtype == GMA_BF16;
+  p.B = d->B;
+  p.H = d->H;
+  p.N = 1;
+  p.BH = d->B * d->H;
+  p.DR = d->d_r;
+  p.DV = d->d_v;
+  p.K = d->K;
+  Tensors t;
+  t.q = q;
+  t.k = k;
+  t.v = v;
+  t.mu = mu;
+  t.ls2 = log_sigma2;
+  t.lpi = log_pi;
+  t.out = out;
+  t.assign_q = assign_q;
+  t.assign_k = assign_k;
+  t.eps = eps;
+  return finish_launch(launch_decode(p, t, state_v, state_z, static_cast<hipStream_t>(stream)),
+                       "decode launch");
+}
+
 const char* gma_status_string(int status) {
   switch (status) {
     case GMA_OK: return "GMA_OK";

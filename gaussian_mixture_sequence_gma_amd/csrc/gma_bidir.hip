@@ -101,6 +101,8 @@ __global__ void __launch_bounds__(256) gma_prologue_kernel(
 }
 
 // Sum the partials of each sequence in a fixed order: V~ [BH][Kp][DV], Z [BH][Kp].
+// With st_v / st_z the first K rows are also written unpadded, [BH][K][DV] and
+// [BH][K]: the carried state of a prefix for the decode step.
 // With vtab (bf16 path, K_pad a multiple of 32) the sums are also written as
 // the read-out's MFMA operand table: block dt (d tile, paired rows as in
 // pair_row when d_v >= 32), step p (32 components), lane (row, component
@@ -110,7 +112,9 @@ __global__ void __launch_bounds__(256) gma_reduce_kernel(const float* __restrict
                                                          int PS, int Kp, int DV,
                                                          float* __restrict__ vt,
                                                          float* __restrict__ z,
-                                                         bf16* __restrict__ vtab) {
+                                                         bf16* __restrict__ vtab,
+                                                         float* __restrict__ st_v,
+                                                         float* __restrict__ st_z, int K) {
   const int64_t bh = blockIdx.y;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   const int nv = Kp * DV;
@@ -121,8 +125,9 @@ __global__ void __launch_bounds__(256) gma_reduce_kernel(const float* __restrict
     float s = 0.f;
     for (int q = 0; q < PS; ++q) s += p[(size_t)q * nv];
     vt[(size_t)bh * nv + idx] = s;
+    const int k = idx / DV, d = idx - k * DV;
+    if (st_v && k < K) st_v[((size_t)bh * K + k) * DV + d] = s;
     if (vb) {
-      const int k = idx / DV, d = idx - k * DV;
       const int t = DVT >= 2 ? pair_tile(d) : 0, r = DVT >= 2 ? pair_rowof(d) : d;
       vb[((t * KS + (k >> 5)) * 64 + r + 16 * ((k & 31) >> 3)) * 8 + (k & 7)] = to_bf16(s);
     }
@@ -132,6 +137,7 @@ __global__ void __launch_bounds__(256) gma_reduce_kernel(const float* __restrict
     float s = 0.f;
     for (int q = 0; q < PS; ++q) s += p[(size_t)q * Kp];
     z[(size_t)bh * Kp + k] = s;
+    if (st_z && k < K) st_z[(size_t)bh * K + k] = s;
     if (vb) {
       const bf16 zh = to_bf16(s);
       const bf16 zl = to_bf16(s - from_bf16(zh));
@@ -948,10 +954,13 @@ static hipError_t run_bidir(const Plan& p, const Tensors& t, hipStream_t s) {
                      a.partial, a.partial_z, PS, C::Kp, C::DV,
                      reinterpret_cast<float*>(t.ws + p.off_vt),
                      reinterpret_cast<float*>(t.ws + p.off_z),
-                     Read2<C>::kOK ? reinterpret_cast<bf16*>(t.ws + p.off_vtab) : nullptr);
+                     Read2<C>::kOK && !t.state_v ? reinterpret_cast<bf16*>(t.ws + p.off_vtab)
+                                                 : nullptr,
+                     t.state_v, t.state_z, p.K);
   if (g_launch_hook) g_launch_hook("gma_reduce", s, 0);
   e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // a prefix state stops here: V~ and Z are the state after the last key
+  if (e != hipSuccess || t.state_v) return e;
 
   a.x = t.q;
   a.x_lo = t.q_lo;

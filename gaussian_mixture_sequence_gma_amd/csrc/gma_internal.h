@@ -50,6 +50,10 @@ struct Tensors {
   // projections on the bf16 kernels
   const void* q_lo = nullptr;
   const void* k_lo = nullptr;
+  // bidirectional launch that stops after the latent write: V~ [BH,K,d_v] and
+  // Z [BH,K] of all the keys, unpadded (the carried state of a prefix)
+  float* state_v = nullptr;
+  float* state_z = nullptr;
 };
 
 // Launch helpers; each returns hipSuccess or the launch error.  `tag` names the
@@ -64,6 +68,10 @@ bool causal_split_ok(const Plan& p);
 hipError_t launch_bidir(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_resp(const Plan& p, const Tensors& t, hipStream_t s);
+// One causal decode step (N = 1 per sequence) against the carried state
+// state_v [BH,K,d_v], state_z [BH,K] (fp32, updated in place).
+hipError_t launch_decode(const Plan& p, const Tensors& t, float* state_v, float* state_z,
+                         hipStream_t s);
 // Q_X, K_X, V_X = X W_Q, X W_K, X W_V (W[0..2]) into fp32 head-major out[0..2].
 // split = 0: out[0..2] are fp32.  split = 1: Q_X and K_X as bf16 pairs (out[m],
 // lo[m]: value = out + lo, 16 significant bits), V_X as bf16 in out[2].

@@ -17,6 +17,10 @@ Workloads (names describe the shape; all use numpy ``default_rng(seed)``):
   prior logits ~ N(0, 2)
 * ``layer_causal_bf16``   X[2,16384,1024] bf16, W_Q/W_K/W_V [1024, 16*64] with
   entries ~ N(0, 1/1024) rounded to bf16, H16 d_r64 d_v64 K32, causal
+* ``decode_bf16``         one causal decode step for a serving batch: B64 H32,
+  one new token per sequence (N1), d_r64 d_v128 K128 bf16, the long-context
+  parameter distributions, and a carried state standing for a 4096-token
+  prefix (see ``make_state``)
 
 ``N(0, a)`` denotes variance ``a``.  Routing vectors and values are standard
 normal, the stand-in for learned projections (no dataset or trained weights
@@ -58,6 +62,7 @@ class Workload:
     chunk: int = 64
     d_model: int = 0      # > 0: projection-layer workload (X and W are drawn)
     w_var: float = 0.0
+    state_len: int = 0    # > 0: decode-step workload (a carried state is drawn)
 
     @property
     def tokens_heads(self) -> int:
@@ -77,6 +82,8 @@ WORKLOADS: Dict[str, Workload] = {
                  mu_var=1.5, ls2_lo=-1.5, ls2_hi=0.5, logit_var=2.0),
         Workload("layer_causal_bf16", 2, 16, 16384, 64, 64, 32, "bf16", True,
                  d_model=1024, w_var=1.0 / 1024.0),
+        Workload("decode_bf16", 64, 32, 1, 64, 128, 128, "bf16", True,
+                 mu_var=1.5, ls2_lo=-1.5, ls2_hi=0.5, logit_var=2.0, state_len=4096),
     ]
 }
 
@@ -129,13 +136,26 @@ def make_params(rng: np.random.Generator, w: Workload):
     return mu, ls2, alpha
 
 
+def make_state(rng: np.random.Generator, B: int, H: int, K: int, d_v: int, length: int):
+    """A carried causal state standing for a prefix of ``length`` tokens, float32:
+    the per-component counts z [B,H,K] split ``length`` by a flat Dirichlet
+    draw, and S [B,H,K,d_v] has entries ~ N(0, z) (a sum of z standard normal
+    values).  Draw order: the Dirichlet weights, then the normals."""
+    wts = rng.dirichlet(np.ones(K), size=(B, H))
+    z = (length * wts).astype(np.float32)
+    S = rng.standard_normal(size=(B, H, K, d_v), dtype=np.float32)
+    S *= np.sqrt(z)[..., None]
+    return np.ascontiguousarray(S), np.ascontiguousarray(z)
+
+
 def generate(w: Workload, seed: int = 0) -> Dict[str, object]:
     """Draw one batch of inputs for workload ``w``.
 
     Returns a dict with Tensor entries ``Q``, ``K``, ``V`` ([B,H,N,d]) or, for
     a projection-layer workload, ``X`` ([B,N,d_model]), ``W_Q``, ``W_K``
     ([d_model, H*d_r]), ``W_V`` ([d_model, H*d_v]); and float32 arrays ``mu``,
-    ``log_sigma2``, ``log_pi``.
+    ``log_sigma2``, ``log_pi``; for a decode-step workload also the carried
+    state ``S`` [B,H,K,d_v] and ``z`` [B,H,K] (float32, drawn last).
     """
     rng = np.random.default_rng(seed)
     out: Dict[str, object] = {"workload": w, "seed": seed}
@@ -150,6 +170,8 @@ def generate(w: Workload, seed: int = 0) -> Dict[str, object]:
         out["V"] = _store(_normal(rng, (w.B, w.H, w.N, w.d_v), 1.0), w.dtype)
     mu, ls2, alpha = make_params(rng, w)
     out["mu"], out["log_sigma2"], out["log_pi"] = mu, ls2, alpha
+    if w.state_len > 0:
+        out["S"], out["z"] = make_state(rng, w.B, w.H, w.K, w.d_v, w.state_len)
     return out
 
 

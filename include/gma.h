@@ -135,6 +135,43 @@ int gma_responsibilities(const void* X_r, const float* mu, const float* log_sigm
                          int32_t* assign, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/* Carried state of a causal prefix ("Causal GMA": the prefix memories of
+ * Eq. 8b at the last position, i.e. Eqs. 5-6 over all N keys given):
+ *  K_X        [B,H,N,d_r] of d->dtype: key routing vectors of the prefix
+ *  V_X        [B,H,N,d_v] of d->dtype: its values
+ *  mu, log_sigma2, log_pi  as gma_forward
+ *  state_v    [B,H,K,d_v] fp32 (16-byte aligned): written, S = Gamma^K^T V_X
+ *  state_z    [B,H,K] fp32: written, z = Gamma^K^T 1
+ *  assign_k   optional [B,H,N] int32: key assignments (lowest index on ties)
+ *  workspace  at least gma_forward_workspace_bytes(d, 0) bytes
+ * The same kernels as the bidirectional write step of gma_forward (same
+ * arithmetic); the pair (state_v, state_z) is what gma_decode_step carries. */
+int gma_prefix_state(const void* K_X, const void* V_X, const float* mu,
+                     const float* log_sigma2, const float* log_pi, float* state_v,
+                     float* state_z, const gma_dims* d, int32_t* assign_k,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* One causal decode step ("Causal GMA", Eq. 8b at a new position i): with the
+ * carried state S = sum_{j<i} gamma^K_j v_j^T and z = sum_{j<i} gamma^K_j,
+ *   S' = S + gamma^K(k_i) v_i^T,  z' = z + gamma^K(k_i),
+ *   o_i = gamma^Q(q_i)^T S' / (gamma^Q(q_i)^T z' + eps),
+ * and S', z' overwrite S, z.  d->N must be 1 (else GMA_ERR_INVALID_ARG);
+ * d->chunk is ignored.
+ *  q, k       [B,H,1,d_r] of d->dtype: the new token's query and key routing vectors
+ *  v          [B,H,1,d_v] of d->dtype: its value
+ *  mu, log_sigma2, log_pi, eps  as gma_forward
+ *  state_v    [B,H,K,d_v] fp32 (16-byte aligned): S in, S' out
+ *  state_z    [B,H,K] fp32: z in, z' out (all zeros for an empty prefix)
+ *  out        [B,H,1,d_v] of d->dtype: o_i
+ *  assign_q, assign_k  optional [B,H] int32: argmax of gamma^Q, gamma^K
+ * No workspace.  Responsibilities use the direct form of the diagonal
+ * log-density in fp32; the state stays fp32.  Starting from zeros and stepping
+ * through a sequence gives gma_forward's causal output row by row. */
+int gma_decode_step(const void* q, const void* k, const void* v, const float* mu,
+                    const float* log_sigma2, const float* log_pi, float eps,
+                    float* state_v, float* state_z, void* out, const gma_dims* d,
+                    int32_t* assign_q, int32_t* assign_k, void* stream);
+
 /* Static description of a status code. */
 const char* gma_status_string(int status);
 

@@ -168,3 +168,50 @@ def test_layer_projection_layout_errors():
     out = (ctypes.c_size_t * 5)()
     assert lib.gma_layer_projection_layout(ctypes.byref(_dims()), 256, 0, None,
                                            ctypes.byref(out)) == B.GMA_ERR_INVALID_ARG
+
+
+def _decode(**over):
+    args = dict(q=A16, k=A16, v=A16, mu=A16, log_sigma2=A16, log_pi=A16, eps=1e-6,
+                state_v=A16, state_z=A16, out=A16, dims=_dims(N=1), assign_q=None,
+                assign_k=None, stream=0)
+    args.update(over)
+    with pytest.raises(B.GmaError) as ei:
+        B.gma_decode_step(**args)
+    return ei.value.status
+
+
+def test_decode_step_rejects_before_launch():
+    assert _decode(dims=_dims(N=2)) == B.GMA_ERR_INVALID_ARG      # one token per sequence
+    assert _decode(q=None) == B.GMA_ERR_INVALID_ARG
+    assert _decode(state_v=None) == B.GMA_ERR_INVALID_ARG
+    assert _decode(state_z=None) == B.GMA_ERR_INVALID_ARG
+    assert _decode(out=None) == B.GMA_ERR_INVALID_ARG
+    assert _decode(state_v=A16 + 4) == B.GMA_ERR_INVALID_ARG     # 16-byte aligned
+    assert _decode(assign_k=A16 + 2) == B.GMA_ERR_INVALID_ARG
+    assert _decode(eps=float("nan")) == B.GMA_ERR_INVALID_ARG
+    assert _decode(dims=_dims(N=1, K=129)) == B.GMA_ERR_UNSUPPORTED
+    assert _decode(dims=_dims(N=1, d_v=48)) == B.GMA_ERR_UNSUPPORTED
+    assert "N = 1" in (lambda: (_decode(dims=_dims(N=3)), B.gma_last_error())[1])()
+
+
+def _prefix(**over):
+    args = dict(K_X=A16, V_X=A16, mu=A16, log_sigma2=A16, log_pi=A16, state_v=A16,
+                state_z=A16, dims=_dims(), assign_k=None, workspace=A16,
+                workspace_bytes=1 << 40, stream=0)
+    args.update(over)
+    with pytest.raises(B.GmaError) as ei:
+        B.gma_prefix_state(**args)
+    return ei.value.status
+
+
+def test_prefix_state_rejects_before_launch():
+    assert _prefix(K_X=None) == B.GMA_ERR_INVALID_ARG
+    assert _prefix(state_z=None) == B.GMA_ERR_INVALID_ARG
+    assert _prefix(workspace=None) == B.GMA_ERR_INVALID_ARG
+    assert _prefix(state_v=A16 + 8) == B.GMA_ERR_INVALID_ARG
+    assert _prefix(dims=_dims(K=0)) == B.GMA_ERR_INVALID_ARG
+    assert _prefix(dims=_dims(d_r=8)) == B.GMA_ERR_UNSUPPORTED
+    assert _prefix(workspace_bytes=32) == B.GMA_ERR_WORKSPACE
+    # the forward's bidirectional workspace is enough
+    n = B.gma_forward_workspace_bytes(_dims(), 0)
+    assert _prefix(workspace_bytes=n - 1) == B.GMA_ERR_WORKSPACE
