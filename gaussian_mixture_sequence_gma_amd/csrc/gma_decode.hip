@@ -96,7 +96,31 @@ __global__ void __launch_bounds__(256) gma_decode_kernel(DecodeArgs a) {
   const int h = (int)(bh % a.H);
   const int K = a.K;
 
-  // 1. this thread's state rows r0 + p * SR, columns col .. col + 3.  Rows
+  // 1. the token's routing vectors (16 dims per lane) and the component
+  //    parameters of the first score passes are requested first, so that the
+  //    scores wait only for them and not for the state behind them
+  const int sl = (lane % L) * 16;
+  float xq[16], xk[16];
+  load16(static_cast<const T*>(a.q) + (size_t)bh * DR + sl, xq);
+  load16(static_cast<const T*>(a.k) + (size_t)bh * DR + sl, xk);
+  const float* mu = a.mu + (size_t)h * K * DR;
+  const float* ls = a.ls2 + (size_t)h * K * DR;
+  constexpr int PC = 4 * CW;                 // components per score pass
+  constexpr int NPRE = PC >= 128 ? 1 : 2;    // passes whose parameters are preloaded
+  f32x4 pm[NPRE][4], pv[NPRE][4];
+  auto load_pass = [&](int c0, f32x4 (&m)[4], f32x4 (&l)[4]) {
+    // rows past K re-read row K - 1; their scores are not stored
+    const int c = min(c0 + wave * CW + lane / L, K - 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m[i] = ld16<f32x4>(mu + (size_t)c * DR + sl + 4 * i);
+      l[i] = ld16<f32x4>(ls + (size_t)c * DR + sl + 4 * i);
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < NPRE; ++j) load_pass(j * PC, pm[j], pv[j]);
+
+  // 2. this thread's state rows r0 + p * SR, columns col .. col + 3.  Rows
   //    past K re-read row K - 1 (no branch around the loads) and are neither
   //    stored nor counted.
   const int col = (t % C4) * 4, r0 = t / C4;
@@ -112,31 +136,20 @@ __global__ void __launch_bounds__(256) gma_decode_kernel(DecodeArgs a) {
   }
   const f32x4 vv = load4(static_cast<const T*>(a.v) + (size_t)bh * DV + col);
 
-  // 2. scores s_c(x) = log pi_c - (1/2) sum_d [(x_d - mu_cd)^2 / sigma^2_cd + log sigma^2_cd]
+  // 3. scores s_c(x) = log pi_c - (1/2) sum_d [(x_d - mu_cd)^2 / sigma^2_cd + log sigma^2_cd]
   //    (the 2 pi term is common to all components and cancels in the posterior)
-  const int sl = (lane % L) * 16;
-  float xq[16], xk[16];
-  load16(static_cast<const T*>(a.q) + (size_t)bh * DR + sl, xq);
-  load16(static_cast<const T*>(a.k) + (size_t)bh * DR + sl, xk);
-  const float* mu = a.mu + (size_t)h * K * DR;
-  const float* ls = a.ls2 + (size_t)h * K * DR;
-#pragma unroll 1
-  for (int c0 = 0; c0 < K; c0 += 4 * CW) {
+  auto score_pass = [&](int c0, const f32x4 (&m)[4], const f32x4 (&l)[4]) {
     const int c = c0 + wave * CW + lane / L;
     float pq = 0.f, pk = 0.f, pl = 0.f;
-    if (c < K) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 m = ld16<f32x4>(mu + (size_t)c * DR + sl + 4 * i);
-        const f32x4 l = ld16<f32x4>(ls + (size_t)c * DR + sl + 4 * i);
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float prec = expf(-l[e]);
-          const float dq = xq[4 * i + e] - m[e], dk = xk[4 * i + e] - m[e];
-          pq += dq * dq * prec;
-          pk += dk * dk * prec;
-          pl += l[e];
-        }
+      for (int e = 0; e < 4; ++e) {
+        const float prec = expf(-l[i][e]);
+        const float dq = xq[4 * i + e] - m[i][e], dk = xk[4 * i + e] - m[i][e];
+        pq += dq * dq * prec;
+        pk += dk * dk * prec;
+        pl += l[i][e];
       }
     }
 #pragma unroll
@@ -150,6 +163,15 @@ __global__ void __launch_bounds__(256) gma_decode_kernel(DecodeArgs a) {
       s_sc[0][c] = lp - 0.5f * (pq + pl);
       s_sc[1][c] = lp - 0.5f * (pk + pl);
     }
+  };
+#pragma unroll
+  for (int j = 0; j < NPRE; ++j)
+    if (j * PC < K) score_pass(j * PC, pm[j], pv[j]);
+#pragma unroll 1
+  for (int c0 = NPRE * PC; c0 < K; c0 += PC) {
+    f32x4 m[4], l[4];
+    load_pass(c0, m, l);
+    score_pass(c0, m, l);
   }
   __syncthreads();
 
