@@ -11,6 +11,10 @@ Linear-Time Sequence Mixing via Probabilistic Latent Routing", Section
 "Projections"), for which ``numpy.matmul`` in float64 serves as the library
 matrix product.
 
+``reparameterize`` (Eqs. 14-15) is plain numpy; its pins are in
+tests/test_oracle_reparam.py (scipy's softplus and log_softmax, closed
+values, the simplex and shift invariance).
+
 Pins (see tests/test_oracle.py): responsibilities against scikit-learn's
 diagonal-covariance GaussianMixture posterior; outputs against a brute-force
 materialised affinity built from scikit-learn's responsibilities; closed
@@ -177,6 +181,27 @@ def decode_step(S, z, q, k, v, mu, log_sigma2, log_pi, eps: float) -> dict:
     den = np.einsum("bhk,bhk->bh", gq, z2) + eps
     return {"S": S2, "z": z2, "out": num / den[:, :, None],
             "assign_q": rq["assign"][:, :, 0], "assign_k": rk["assign"][:, :, 0]}
+
+
+def reparameterize(omega, alpha, eps_sigma: float) -> dict:
+    """Constrained mixture parameters from the unconstrained ones (the
+    reparameterisations used for training: Eq. 14, sigma^2 = log(1 + exp(omega)) +
+    eps_sigma per component and routing dimension; Eq. 15, pi = softmax over
+    the components of the logits alpha).
+
+    omega [H,K,d_r], alpha [H,K].  Returns dict(log_sigma2 [H,K,d_r],
+    log_pi [H,K]) in float64, the arrays the forward takes.  log(1 + exp(w))
+    is evaluated as max(w, 0) + log1p(exp(-|w|)) (the same number, without
+    overflow for large w); log pi_k = alpha_k - log sum_l exp(alpha_l), with
+    the largest logit subtracted inside the exponentials.
+    """
+    w = _f64(omega)
+    a = _f64(alpha)
+    sp = np.maximum(w, 0.0) + np.log1p(np.exp(-np.abs(w)))
+    log_sigma2 = np.log(sp + float(eps_sigma))
+    m = a.max(axis=-1, keepdims=True)
+    lse = m + np.log(np.exp(a - m).sum(axis=-1, keepdims=True))
+    return {"log_sigma2": log_sigma2, "log_pi": a - lse}
 
 
 def project(X, W, H: int) -> np.ndarray:
