@@ -176,6 +176,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="long_bidir_bf16")
     ap.add_argument("--causal", type=int, default=None, help="override the workload's variant")
+    ap.add_argument("--reparam", action="store_true",
+                    help="each step first derives log sigma^2 and log pi on the device from "
+                         "unconstrained parameters (gma_reparameterize; the workload's log "
+                         "sigma^2 and log pi arrays stand in for omega and alpha)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", dest="flush", action="store_false",
                     help="do not evict the Infinity Cache between timed steps")
@@ -250,7 +254,13 @@ def main():
         nbytes = binding.gma_forward_workspace_bytes(dims, int(w.causal))
     ws = api.alloc_workspace(nbytes, dev)
 
+    if args.reparam:
+        omega, alpha = ls2, lpi
+        ls2, lpi = torch.empty_like(omega), torch.empty_like(alpha)
+
     def step():
+        if args.reparam:
+            binding.gma_reparameterize(omega, alpha, 1e-4, w.H, w.K, w.d_r, ls2, lpi)
         if decode:
             binding.gma_decode_step(Q, K, V, mu, ls2, lpi, w.eps, S_state, z_state, out, dims)
         elif w.d_model > 0:
@@ -349,6 +359,8 @@ def main():
            "step_hbm_frac": (step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS) if step_bytes else None}
     if w.d_model:
         cfg["d_model"] = w.d_model
+    if args.reparam:
+        cfg["reparam"] = "gma_reparameterize (Eqs. 14-15, eps_sigma 1e-4) at the start of each step"
     if decode:
         cfg["step"] = "one decode token per sequence against a carried fp32 state"
         cfg["state_len"] = w.state_len

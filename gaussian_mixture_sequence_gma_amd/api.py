@@ -128,3 +128,13 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mu: torch.Ten
         ak = torch.empty((Bb, H), dtype=torch.int32, device=q.device)
     B.gma_decode_step(q, k, v, mu, log_sigma2, log_pi, eps, S, z, out, dims, aq, ak, stream)
     return (out, aq, ak) if assign else out
+
+
+def reparameterize(omega: torch.Tensor, alpha: torch.Tensor, eps_sigma: float = 1e-4,
+                   stream=None):
+    """(log_sigma2 [H,K,d_r], log_pi [H,K]) from omega [H,K,d_r] and alpha [H,K]."""
+    H, Kc, d_r = omega.shape
+    ls2 = torch.empty_like(omega)
+    lpi = torch.empty_like(alpha)
+    B.gma_reparameterize(omega, alpha, eps_sigma, H, Kc, d_r, ls2, lpi, stream)
+    return ls2, lpi

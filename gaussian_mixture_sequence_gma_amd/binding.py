@@ -66,6 +66,8 @@ def load():
     lib.gma_responsibilities.argtypes = [P, P, P, P, D, P, P, P, S, P]
     lib.gma_prefix_state.argtypes = [P, P, P, P, P, P, P, D, P, P, S, P]
     lib.gma_decode_step.argtypes = [P, P, P, P, P, P, f32, P, P, P, D, P, P, P]
+    lib.gma_reparameterize.argtypes = [P, P, f32, ctypes.c_int64, ctypes.c_int32,
+                                       ctypes.c_int32, P, P, P]
     lib.gma_status_string.argtypes = [i32]
     lib.gma_status_string.restype = ctypes.c_char_p
     lib.gma_last_error.argtypes = []
@@ -75,7 +77,7 @@ def load():
                                        ctypes.POINTER(ctypes.c_int)]
     for fn in ("gma_validate", "gma_forward_workspace_bytes", "gma_forward",
                "gma_layer_workspace_bytes", "gma_layer_forward", "gma_layer_projection_layout",
-               "gma_responsibilities", "gma_prefix_state", "gma_decode_step",
+               "gma_responsibilities", "gma_prefix_state", "gma_decode_step", "gma_reparameterize",
                "gma_timing_enable", "gma_timing_collect"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -185,6 +187,11 @@ def gma_decode_step(q, k, v, mu, log_sigma2, log_pi, eps, state_v, state_z, out,
                                   _ptr(log_pi), float(eps), _ptr(state_v), _ptr(state_z),
                                   _ptr(out), ctypes.byref(dims), _ptr(assign_q),
                                   _ptr(assign_k), _stream(stream)))
+
+
+def gma_reparameterize(omega, alpha, eps_sigma, H, K, d_r, log_sigma2, log_pi, stream=None):
+    _check(load().gma_reparameterize(_ptr(omega), _ptr(alpha), float(eps_sigma), int(H), int(K),
+                                     int(d_r), _ptr(log_sigma2), _ptr(log_pi), _stream(stream)))
 
 
 def gma_status_string(status: int) -> str:

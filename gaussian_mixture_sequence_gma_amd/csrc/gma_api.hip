@@ -467,6 +467,24 @@ int gma_decode_step(const void* q, const void* k, const void* v, const float* mu
                        "decode launch");
 }
 
+int gma_reparameterize(const float* omega, const float* alpha, float eps_sigma, int64_t H,
+                       int32_t K, int32_t d_r, float* log_sigma2, float* log_pi, void* stream) {
+  t_err.clear();
+  if (!omega || !alpha || !log_sigma2 || !log_pi)
+    return fail(GMA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (((uintptr_t)omega & 3) || ((uintptr_t)alpha & 3) || ((uintptr_t)log_sigma2 & 3) ||
+      ((uintptr_t)log_pi & 3))
+    return fail(GMA_ERR_INVALID_ARG, "tensor pointers must be 4-byte aligned");
+  if (H < 1 || K < 1 || d_r < 1) return fail(GMA_ERR_INVALID_ARG, "H, K and d_r must be >= 1");
+  if (!(eps_sigma > 0.f) || !isfinite(eps_sigma))
+    return fail(GMA_ERR_INVALID_ARG, "eps_sigma must be finite and > 0");
+  if (H > 65535 || (int64_t)K * d_r > ((int64_t)1 << 24) || H * K * (int64_t)d_r > ((int64_t)1 << 30))
+    return fail(GMA_ERR_UNSUPPORTED, "parameter arrays too large");
+  return finish_launch(launch_reparam(omega, alpha, eps_sigma, H, K, d_r, log_sigma2, log_pi,
+                                      static_cast<hipStream_t>(stream)),
+                       "reparameterisation launch");
+}
+
 const char* gma_status_string(int status) {
   switch (status) {
     case GMA_OK: return "GMA_OK";

@@ -72,6 +72,10 @@ hipError_t launch_resp(const Plan& p, const Tensors& t, hipStream_t s);
 // state_v [BH,K,d_v], state_z [BH,K] (fp32, updated in place).
 hipError_t launch_decode(const Plan& p, const Tensors& t, float* state_v, float* state_z,
                          hipStream_t s);
+// log sigma^2 = log(softplus(omega) + eps_sigma) over [H,K,d_r] and
+// log pi = alpha - logsumexp(alpha) over [H,K].
+hipError_t launch_reparam(const float* omega, const float* alpha, float eps_sigma, int64_t H,
+                          int K, int d_r, float* log_sigma2, float* log_pi, hipStream_t s);
 // Q_X, K_X, V_X = X W_Q, X W_K, X W_V (W[0..2]) into fp32 head-major out[0..2].
 // split = 0: out[0..2] are fp32.  split = 1: Q_X and K_X as bf16 pairs (out[m],
 // lo[m]: value = out + lo, 16 significant bits), V_X as bf16 in out[2].

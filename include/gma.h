@@ -172,6 +172,22 @@ int gma_decode_step(const void* q, const void* k, const void* v, const float* mu
                     float* state_v, float* state_z, void* out, const gma_dims* d,
                     int32_t* assign_q, int32_t* assign_k, void* stream);
 
+/* Constrained mixture parameters from the unconstrained ones the optimiser
+ * updates (the reparameterisations used for training, Eqs. 14-15):
+ *   log_sigma2[h,k,j] = log(log(1 + exp(omega[h,k,j])) + eps_sigma)
+ *   log_pi[h,k]       = alpha[h,k] - log sum_l exp(alpha[h,l])
+ *  omega      [H,K,d_r] fp32: covariance parameters
+ *  alpha      [H,K] fp32: mixture-prior logits
+ *  eps_sigma  > 0, finite: the variance floor of Eq. 14
+ *  log_sigma2 [H,K,d_r] fp32, log_pi [H,K] fp32: written; the arrays gma_forward,
+ *             gma_layer_forward and gma_decode_step take
+ * fp32 arithmetic; log(1 + exp(w)) is evaluated as max(w,0) + log1p(exp(-|w|)).
+ * Pointers need 4-byte alignment here; H <= 65535, K * d_r <= 2^24 and
+ * H * K * d_r <= 2^30 (else GMA_ERR_UNSUPPORTED).  Any H, K, d_r >= 1 is accepted. */
+int gma_reparameterize(const float* omega, const float* alpha, float eps_sigma, int64_t H,
+                       int32_t K, int32_t d_r, float* log_sigma2, float* log_pi,
+                       void* stream);
+
 /* Static description of a status code. */
 const char* gma_status_string(int status);
 

@@ -215,3 +215,21 @@ def test_prefix_state_rejects_before_launch():
     # the forward's bidirectional workspace is enough
     n = B.gma_forward_workspace_bytes(_dims(), 0)
     assert _prefix(workspace_bytes=n - 1) == B.GMA_ERR_WORKSPACE
+
+
+def test_reparameterize_rejects_before_launch():
+    def st(**over):
+        args = dict(omega=A16, alpha=A16, eps_sigma=1e-4, H=2, K=8, d_r=16, log_sigma2=A16,
+                    log_pi=A16, stream=0)
+        args.update(over)
+        with pytest.raises(B.GmaError) as ei:
+            B.gma_reparameterize(**args)
+        return ei.value.status
+    assert st(omega=None) == B.GMA_ERR_INVALID_ARG
+    assert st(log_pi=None) == B.GMA_ERR_INVALID_ARG
+    assert st(alpha=A16 + 2) == B.GMA_ERR_INVALID_ARG
+    assert st(eps_sigma=0.0) == B.GMA_ERR_INVALID_ARG
+    assert st(eps_sigma=float("inf")) == B.GMA_ERR_INVALID_ARG
+    assert st(K=0) == B.GMA_ERR_INVALID_ARG
+    assert st(H=70000) == B.GMA_ERR_UNSUPPORTED
+    assert st(H=65535, K=4096, d_r=4096) == B.GMA_ERR_UNSUPPORTED

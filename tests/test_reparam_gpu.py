@@ -1,0 +1,60 @@
+"""GPU parity of gma_reparameterize (Eqs. 14-15 of "Gaussian Mixture
+Attention: Linear-Time Sequence Mixing via Probabilistic Latent Routing")
+against oracle.reparameterize, alone and feeding the forward.
+
+Tolerance: fp32 elementwise functions, |err| <= 2e-6 + 1e-6 |ref| on
+log sigma^2 and 1e-5 + 1e-6 |ref| on log pi (a log-sum-exp of up to 128
+fp32 terms)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gaussian_mixture_sequence_gma_amd import api, inputs
+from tests.parity import TOL, rowwise_rel_err, upload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("H,K,d_r,scale,eps_sigma", [
+    (1, 1, 16, 1.0, 1e-4),
+    (3, 7, 5, 3.0, 1e-3),          # sizes off any vector width
+    (32, 128, 64, 4.0, 1e-4),      # the long-context parameter shape
+    (2, 100, 128, 30.0, 1e-2),     # large |omega|: softplus saturates both ways
+])
+def test_reparameterize_matches_oracle(H, K, d_r, scale, eps_sigma):
+    rng = np.random.default_rng(H * 1000 + K)
+    om = rng.normal(0, scale, (H, K, d_r)).astype(np.float32)
+    al = rng.normal(0, scale, (H, K)).astype(np.float32)
+    om.flat[:4] = [0.0, 88.0, -88.0, 1e-3][:min(4, om.size)]
+    ls2, lpi = api.reparameterize(torch.from_numpy(om).cuda(), torch.from_numpy(al).cuda(),
+                                  eps_sigma)
+    torch.cuda.synchronize()
+    ref = oracle.reparameterize(om, al, eps_sigma)
+    g_ls2, g_lpi = ls2.cpu().numpy().astype(np.float64), lpi.cpu().numpy().astype(np.float64)
+    e1 = np.abs(g_ls2 - ref["log_sigma2"]) - 1e-6 * np.abs(ref["log_sigma2"])
+    e2 = np.abs(g_lpi - ref["log_pi"]) - 1e-6 * np.abs(ref["log_pi"])
+    print("reparam %s: ls2 %.2e  lpi %.2e" % ((H, K, d_r), e1.max(), e2.max()))
+    assert e1.max() <= 2e-6
+    assert e2.max() <= 1e-5
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_reparameterized_forward_matches_oracle(causal):
+    """Device reparameterisation feeding gma_forward equals the oracle forward
+    on the oracle's reparameterised parameters."""
+    w = inputs.Workload("reparam_fwd", 2, 4, 700, 64, 64, 64, "f32", causal)
+    gen = inputs.generate(w, 9)
+    rng = np.random.default_rng(10)
+    om = rng.normal(0, 1.0, (w.H, w.K, w.d_r)).astype(np.float32)
+    al = rng.normal(0, 1.0, (w.H, w.K)).astype(np.float32)
+    dev = upload(gen)
+    ls2, lpi = api.reparameterize(torch.from_numpy(om).cuda(), torch.from_numpy(al).cuda(), 1e-4)
+    out = api.forward(dev["Q"], dev["K"], dev["V"], dev["mu"], ls2, lpi, w.eps, causal)
+    torch.cuda.synchronize()
+    r = oracle.reparameterize(om, al, 1e-4)
+    ref = oracle.forward(gen["Q"].f32, gen["K"].f32, gen["V"].f32, gen["mu"], r["log_sigma2"],
+                         r["log_pi"], w.eps, causal)["out"]
+    e = rowwise_rel_err(out.cpu().numpy(), ref)
+    print("reparam + forward causal=%d: %.2e" % (causal, e))
+    assert e <= TOL["f32"]
