@@ -11,6 +11,8 @@ Linear-Time Sequence Mixing via Probabilistic Latent Routing", Section
 "Projections"), for which ``numpy.matmul`` in float64 serves as the library
 matrix product.
 
+``usage_stats`` (component-usage diagnostics) is plain numpy over the C
+responsibilities; its pins are in tests/test_oracle_usage.py.
 ``reparameterize`` (Eqs. 14-15) is plain numpy; its pins are in
 tests/test_oracle_reparam.py (scipy's softplus and log_softmax, closed
 values, the simplex and shift invariance).
@@ -181,6 +183,43 @@ def decode_step(S, z, q, k, v, mu, log_sigma2, log_pi, eps: float) -> dict:
     den = np.einsum("bhk,bhk->bh", gq, z2) + eps
     return {"S": S2, "z": z2, "out": num / den[:, :, None],
             "assign_q": rq["assign"][:, :, 0], "assign_k": rk["assign"][:, :, 0]}
+
+
+def usage_stats(X, mu, log_sigma2, log_pi, util_threshold: float) -> dict:
+    """Component-usage diagnostics of the responsibilities of X [B,H,N,d_r]
+    (the marginal use of the components and the hard assignments
+    z_i = argmax_k gamma_ik, monitored for under-use and collapse), per head
+    over the T = B*N tokens of that head:
+
+      counts[h,k]      #{i : z_i = k}
+      mean_gamma[h,k]  (1/T) sum_i gamma_ik
+      utilization[h,k] (1/T) #{i : gamma_ik > util_threshold}
+      token_entropy[h] (1/T) sum_i -sum_k gamma_ik ln gamma_ik   (0 ln 0 = 0)
+      usage_entropy[h] -sum_k p_k ln p_k / ln K, p_k = counts[h,k] / T (0 if K = 1)
+      used[h]          #{k : counts[h,k] > 0}
+
+    The responsibilities and assignments are the C oracle's (Eq. 3).
+    """
+    r = responsibilities(X, mu, log_sigma2, log_pi)
+    g, z = r["gamma"], r["assign"]
+    B, H, N, K = g.shape
+    T = B * N
+    counts = np.zeros((H, K), np.int64)
+    for h in range(H):
+        for b in range(B):
+            for k in range(K):
+                counts[h, k] += int(np.count_nonzero(z[b, h] == k))
+    mean_gamma = g.sum(axis=(0, 2)) / T
+    utilization = (g > util_threshold).sum(axis=(0, 2)) / T
+    glng = np.where(g > 0, g * np.log(np.where(g > 0, g, 1.0)), 0.0)
+    token_entropy = -glng.sum(axis=(0, 2, 3)) / T
+    p = counts / T
+    plnp = np.where(p > 0, p * np.log(np.where(p > 0, p, 1.0)), 0.0)
+    usage_entropy = -plnp.sum(-1) / np.log(K) if K > 1 else np.zeros(H)
+    used = (counts > 0).sum(-1)
+    return {"counts": counts, "mean_gamma": mean_gamma, "utilization": utilization,
+            "token_entropy": token_entropy, "usage_entropy": usage_entropy, "used": used,
+            "gamma": g, "assign": z}
 
 
 def reparameterize(omega, alpha, eps_sigma: float) -> dict:
