@@ -64,6 +64,8 @@ def kernel_bytes(name: str, w, s_r: int, s_v: int, s_out: int) -> int:
         return T * (w.d_r * s_r + w.d_v * s_out)
     if name == "gma_causal":
         return T * (2 * w.d_r * s_r + w.d_v * s_v + w.d_v * s_out)
+    if name == "gma_usage":
+        return T * w.d_r * s_r
     if name == "gma_decode":
         # the fp32 state (S, z) read and written, the token's q, k, v and o,
         # and each head's mixture parameters once
@@ -180,6 +182,9 @@ def main():
                     help="each step first derives log sigma^2 and log pi on the device from "
                          "unconstrained parameters (gma_reparameterize; the workload's log "
                          "sigma^2 and log pi arrays stand in for omega and alpha)")
+    ap.add_argument("--usage-stats", action="store_true",
+                    help="time gma_usage_stats (component-usage diagnostics) over the "
+                         "workload's queries instead of the forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", dest="flush", action="store_false",
                     help="do not evict the Infinity Cache between timed steps")
@@ -258,7 +263,19 @@ def main():
         omega, alpha = ls2, lpi
         ls2, lpi = torch.empty_like(omega), torch.empty_like(alpha)
 
+    if args.usage_stats:
+        if decode or w.d_model > 0:
+            sys.exit("--usage-stats takes a workload with routing vectors (not decode or layer)")
+        ws = api.alloc_workspace(binding.gma_usage_workspace_bytes(dims), dev)
+        u_counts = torch.empty((w.H, w.K), dtype=torch.int32, device=dev)
+        u_f = torch.empty((3, w.H, w.K), dtype=torch.float32, device=dev)
+        u_hs = torch.empty((w.H, 3), dtype=torch.float32, device=dev)
+
     def step():
+        if args.usage_stats:
+            binding.gma_usage_stats(Q, mu, ls2, lpi, dims, 0.1, u_counts, u_f[0], u_f[1], u_hs,
+                                    ws, ws.numel())
+            return
         if args.reparam:
             binding.gma_reparameterize(omega, alpha, 1e-4, w.H, w.K, w.d_r, ls2, lpi)
         if decode:
@@ -347,7 +364,7 @@ def main():
     step_bytes = sum(kernel_bytes(k, w, s_r, s_v, s_out) for k in kernels)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.usage_stats:
         cpu = cpu_baseline(w, gen)
 
     cfg = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d_r": w.d_r, "d_v": w.d_v,
@@ -359,6 +376,8 @@ def main():
            "step_hbm_frac": (step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS) if step_bytes else None}
     if w.d_model:
         cfg["d_model"] = w.d_model
+    if args.usage_stats:
+        cfg["step"] = "gma_usage_stats over the queries (threshold 0.1) in place of the forward"
     if args.reparam:
         cfg["reparam"] = "gma_reparameterize (Eqs. 14-15, eps_sigma 1e-4) at the start of each step"
     if decode:

@@ -138,3 +138,22 @@ def reparameterize(omega: torch.Tensor, alpha: torch.Tensor, eps_sigma: float = 
     lpi = torch.empty_like(alpha)
     B.gma_reparameterize(omega, alpha, eps_sigma, H, Kc, d_r, ls2, lpi, stream)
     return ls2, lpi
+
+
+def usage_stats(X: torch.Tensor, mu: torch.Tensor, log_sigma2: torch.Tensor,
+                log_pi: torch.Tensor, util_threshold: float = 0.1, stream=None):
+    """Per-head component-usage diagnostics of the responsibilities of X
+    [B,H,N,d_r]: dict(counts [H,K] int32, mean_gamma, utilization [H,K],
+    token_entropy, usage_entropy, used [H])."""
+    Bb, H, N, d_r = X.shape
+    Kc = mu.shape[1]
+    dims = B.make_dims(Bb, H, N, d_r, 16, Kc, torch_dtype_code(X))
+    ws = alloc_workspace(B.gma_usage_workspace_bytes(dims), X.device)
+    counts = torch.empty((H, Kc), dtype=torch.int32, device=X.device)
+    mg = torch.empty((H, Kc), dtype=torch.float32, device=X.device)
+    ut = torch.empty((H, Kc), dtype=torch.float32, device=X.device)
+    hs = torch.empty((H, 3), dtype=torch.float32, device=X.device)
+    B.gma_usage_stats(X, mu, log_sigma2, log_pi, dims, util_threshold, counts, mg, ut, hs, ws,
+                      ws.numel(), stream)
+    return {"counts": counts, "mean_gamma": mg, "utilization": ut, "token_entropy": hs[:, 0],
+            "usage_entropy": hs[:, 1], "used": hs[:, 2]}

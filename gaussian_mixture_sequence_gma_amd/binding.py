@@ -68,6 +68,8 @@ def load():
     lib.gma_decode_step.argtypes = [P, P, P, P, P, P, f32, P, P, P, D, P, P, P]
     lib.gma_reparameterize.argtypes = [P, P, f32, ctypes.c_int64, ctypes.c_int32,
                                        ctypes.c_int32, P, P, P]
+    lib.gma_usage_workspace_bytes.argtypes = [D, ctypes.POINTER(S)]
+    lib.gma_usage_stats.argtypes = [P, P, P, P, D, f32, P, P, P, P, P, S, P]
     lib.gma_status_string.argtypes = [i32]
     lib.gma_status_string.restype = ctypes.c_char_p
     lib.gma_last_error.argtypes = []
@@ -78,6 +80,7 @@ def load():
     for fn in ("gma_validate", "gma_forward_workspace_bytes", "gma_forward",
                "gma_layer_workspace_bytes", "gma_layer_forward", "gma_layer_projection_layout",
                "gma_responsibilities", "gma_prefix_state", "gma_decode_step", "gma_reparameterize",
+               "gma_usage_workspace_bytes", "gma_usage_stats",
                "gma_timing_enable", "gma_timing_collect"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -187,6 +190,21 @@ def gma_decode_step(q, k, v, mu, log_sigma2, log_pi, eps, state_v, state_z, out,
                                   _ptr(log_pi), float(eps), _ptr(state_v), _ptr(state_z),
                                   _ptr(out), ctypes.byref(dims), _ptr(assign_q),
                                   _ptr(assign_k), _stream(stream)))
+
+
+def gma_usage_workspace_bytes(dims: gma_dims) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().gma_usage_workspace_bytes(ctypes.byref(dims), ctypes.byref(n)))
+    return n.value
+
+
+def gma_usage_stats(X_r, mu, log_sigma2, log_pi, dims: gma_dims, util_threshold, counts=None,
+                    mean_gamma=None, utilization=None, head_stats=None, workspace=None,
+                    workspace_bytes=0, stream=None):
+    _check(load().gma_usage_stats(_ptr(X_r), _ptr(mu), _ptr(log_sigma2), _ptr(log_pi),
+                                  ctypes.byref(dims), float(util_threshold), _ptr(counts),
+                                  _ptr(mean_gamma), _ptr(utilization), _ptr(head_stats),
+                                  _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
 def gma_reparameterize(omega, alpha, eps_sigma, H, K, d_r, log_sigma2, log_pi, stream=None):

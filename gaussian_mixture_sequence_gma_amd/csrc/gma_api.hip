@@ -397,6 +397,57 @@ int gma_responsibilities(const void* X_r, const float* mu, const float* log_sigm
   return finish_launch(e, "responsibility launch");
 }
 
+// Usage statistics: the bidirectional plan's parameter tables, then the
+// per-workgroup partials of the statistics kernel.
+static size_t usage_diag_offset(const Plan& p) { return round256(p.total); }
+static size_t usage_total(const Plan& p) {
+  return usage_diag_offset(p) + round256((size_t)p.BH * p.S * (3 * p.Kp + 4) * 4);
+}
+
+int gma_usage_workspace_bytes(const gma_dims* d, size_t* bytes) {
+  t_err.clear();
+  if (!bytes) return fail(GMA_ERR_INVALID_ARG, "bytes is NULL");
+  Plan p;
+  int st = make_plan(d, 0, false, p);
+  if (st != GMA_OK) return st;
+  *bytes = usage_total(p);
+  return GMA_OK;
+}
+
+int gma_usage_stats(const void* X_r, const float* mu, const float* log_sigma2,
+                    const float* log_pi, const gma_dims* d, float util_threshold,
+                    int32_t* counts, float* mean_gamma, float* utilization, float* head_stats,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  t_err.clear();
+  int st = check_dims(d, 0.f, 0);
+  if (st != GMA_OK) return st;
+  if (!X_r || !mu || !log_sigma2 || !log_pi || !workspace)
+    return fail(GMA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(X_r) || !aligned16(workspace) || !aligned16(mu) || !aligned16(log_sigma2) ||
+      ((uintptr_t)log_pi & 3) || ((uintptr_t)counts & 3) || ((uintptr_t)mean_gamma & 3) ||
+      ((uintptr_t)utilization & 3) || ((uintptr_t)head_stats & 3))
+    return fail(GMA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (!isfinite(util_threshold)) return fail(GMA_ERR_INVALID_ARG, "util_threshold must be finite");
+  Plan p;
+  st = make_plan(d, 0, false, p);
+  if (st != GMA_OK) return st;
+  if (d->B * d->N >= ((int64_t)1 << 31))
+    return fail(GMA_ERR_UNSUPPORTED, "B*N must be below 2^31 for the int32 counts");
+  if (workspace_bytes < usage_total(p)) return fail(GMA_ERR_WORKSPACE, "workspace too small");
+  Tensors t;
+  t.q = X_r;
+  t.mu = mu;
+  t.ls2 = log_sigma2;
+  t.lpi = log_pi;
+  t.ws = static_cast<char*>(workspace);
+  t.diag = reinterpret_cast<float*>(t.ws + usage_diag_offset(p));
+  t.thr = util_threshold;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_prologue(p, t, s);
+  if (e == hipSuccess) e = launch_usage(p, t, counts, mean_gamma, utilization, head_stats, s);
+  return finish_launch(e, "usage statistics launch");
+}
+
 int gma_prefix_state(const void* K_X, const void* V_X, const float* mu, const float* log_sigma2,
                      const float* log_pi, float* state_v, float* state_z, const gma_dims* d,
                      int32_t* assign_k, void* workspace, size_t workspace_bytes, void* stream) {

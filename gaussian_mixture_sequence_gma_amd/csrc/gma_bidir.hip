@@ -151,7 +151,11 @@ __global__ void __launch_bounds__(256) gma_reduce_kernel(const float* __restrict
 
 // ============================================================================
 // Fused query responsibilities + read-out (MODE 0), or responsibilities only
-// (MODE 1: gamma and assignment written to HBM, for testing).
+// (MODE 1: gamma and assignment written to HBM, for testing), or usage
+// statistics of the responsibilities (MODE 2: per workgroup, for each
+// component the sum of gamma, the number of tokens with gamma above a.thr and
+// the number of tokens assigned to it, and the sum of gamma ln gamma over all
+// tokens and components, written to a.diag; nothing per token).
 // ============================================================================
 template <class C, int MODE>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C::kWPERead))) gma_read_kernel(BidirArgs a) {
@@ -162,6 +166,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C
   __shared__ __attribute__((aligned(16))) op_t G[MODE == 0 ? C::GAS : 1];
   __shared__ __attribute__((aligned(16))) f32x4 stats[C::NG * kTile];
   __shared__ __attribute__((aligned(16))) float fac[C::NG * kTile];
+  // usage statistics: per token group the gamma sums and threshold counts of
+  // every component, then the four waves' gamma ln gamma sums; assignments
+  __shared__ float dred[MODE == 2 ? 2 * C::TG * C::Kp + kWaves : 1];
+  __shared__ int hist[MODE == 2 ? C::Kp : 1];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -172,7 +180,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C
   const int split = blockIdx.x;
   const int64_t t_begin = (int64_t)split * a.tiles_per_split * kTile;
   const int64_t t_end = min(a.N, t_begin + (int64_t)a.tiles_per_split * kTile);
-  const bool want_assign = a.assign != nullptr;
+  const bool want_assign = a.assign != nullptr || MODE == 2;
+  float dsum[C::CPW][4], dcnt[C::CPW][4], dent = 0.f;
+#pragma unroll
+  for (int ct = 0; ct < C::CPW; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dsum[ct][i] = dcnt[ct][i] = 0.f;
+  if constexpr (MODE == 2)
+    for (int i = threadIdx.x; i < C::Kp; i += kThreads) hist[i] = 0;
 
   for (int i = threadIdx.x; i < C::NF * C::FAS; i += kThreads) F[i] = (op_t)0;
   if constexpr (MODE == 0)
@@ -319,7 +334,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C
           int key = st[0] == M ? __float_as_int(st[3]) : 0x7fffffff;
           key = min(key, dpp_i<0xB1>(key));
           if constexpr (C::NG == 4) key = min(key, dpp_i<0x4E>(key));
-          if (q == 0 && t < nvalid) a.assign[(size_t)bh * a.N + tile0 + t] = key;
+          if (q == 0 && t < nvalid) {
+            if constexpr (MODE == 2) {
+              if ((unsigned)key < (unsigned)C::Kp) atomicAdd(&hist[key], 1);
+            } else {
+              a.assign[(size_t)bh * a.N + tile0 + t] = key;
+            }
+          }
         }
       }
     }
@@ -338,11 +359,32 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C
       for (int tt = 0; tt < C::TTW; ++tt) {
         const int tok = tile_token(gt0 + tt, c);
         f[tt] = MODE == 0 ? fast_rcp(dn[tt] + a.eps * l[tt]) : fast_rcp(l[tt]);
-        if (want_assign && g == 0 && tok < nvalid) a.assign[(size_t)bh * a.N + tile0 + tok] = am[tt];
+        if (want_assign && g == 0 && tok < nvalid) {
+          if constexpr (MODE == 2) {
+            if ((unsigned)am[tt] < (unsigned)C::Kp) atomicAdd(&hist[am[tt]], 1);
+          } else {
+            a.assign[(size_t)bh * a.N + tile0 + tok] = am[tt];
+          }
+        }
       }
     }
 
-    if constexpr (MODE == 1) {
+    if constexpr (MODE == 2) {
+#pragma unroll
+      for (int tt = 0; tt < C::TTW; ++tt) {
+        if (tile_token(gt0 + tt, c) < nvalid) {
+#pragma unroll
+          for (int ct = 0; ct < C::CPW; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float gm = S[tt][ct][i] * f[tt];      // exactly 0 for padded components
+              dsum[ct][i] += gm;
+              dcnt[ct][i] += gm > a.thr ? 1.f : 0.f;
+              dent += gm > 0.f ? gm * __logf(gm) : 0.f;
+            }
+        }
+      }
+    } else if constexpr (MODE == 1) {
       if (a.gamma != nullptr) {
 #pragma unroll
         for (int tt = 0; tt < C::TTW; ++tt) {
@@ -413,6 +455,43 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C
           }
         }
       }
+    }
+  }
+
+  if constexpr (MODE == 2) {
+    // over the 16 token columns of a lane row (DPP), then over the token
+    // groups in a fixed order; counts are exact in fp32 (< 2^24 per workgroup)
+#pragma unroll
+    for (int ct = 0; ct < C::CPW; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float s1 = row16_sum(dsum[ct][i]), s2 = row16_sum(dcnt[ct][i]);
+        const int comp = (cgi * C::CPW + ct) * 16 + 4 * g + i;
+        if (c == 0) {
+          dred[(2 * tg) * C::Kp + comp] = s1;
+          dred[(2 * tg + 1) * C::Kp + comp] = s2;
+        }
+      }
+    const float e = groups_sum(row16_sum(dent));
+    if (lane == 0) dred[2 * C::TG * C::Kp + wave] = e;
+    lds_barrier();
+    float* out = a.diag + ((size_t)bh * gridDim.x + split) * (3 * C::Kp + 4);
+    for (int k = threadIdx.x; k < C::Kp; k += kThreads) {
+      float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+      for (int q = 0; q < C::TG; ++q) {
+        s1 += dred[(2 * q) * C::Kp + k];
+        s2 += dred[(2 * q + 1) * C::Kp + k];
+      }
+      out[k] = s1;
+      out[C::Kp + k] = s2;
+      out[2 * C::Kp + k] = (float)hist[k];
+    }
+    if (threadIdx.x == 0) {
+      float e4 = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) e4 += dred[2 * C::TG * C::Kp + w];
+      out[3 * C::Kp] = e4;
     }
   }
 }
@@ -1007,6 +1086,77 @@ static hipError_t run_resp(const Plan& p, const Tensors& t, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <class C>
+static hipError_t run_usage(const Plan& p, const Tensors& t, hipStream_t s) {
+  BidirArgs a{};
+  a.params = t.ws + p.off_params;
+  a.head_bytes = p.head_bytes;
+  a.N = p.N;
+  a.H = (int)p.H;
+  a.K = p.K;
+  a.S = p.S;
+  a.tiles_per_split = p.tiles_per_split;
+  a.x = t.q;
+  a.diag = t.diag;
+  a.thr = t.thr;
+  if (g_launch_hook) g_launch_hook("gma_usage", s, 1);
+  hipLaunchKernelGGL((gma_read_kernel<C, 2>), dim3(p.S, (unsigned)p.BH), dim3(kThreads), 0, s, a);
+  if (g_launch_hook) g_launch_hook("gma_usage", s, 0);
+  return hipGetLastError();
+}
+
+// Per head: the usage statistics summed over batches and workgroups in a
+// fixed order (counts exact), then the per-head figures.  One workgroup per head.
+__global__ void __launch_bounds__(256) gma_usage_reduce_kernel(
+    const float* __restrict__ diag, int64_t B, int H, int S, int Kp, int K, int64_t ntok,
+    int32_t* __restrict__ counts, float* __restrict__ mean_gamma, float* __restrict__ util,
+    float* __restrict__ head_stats) {
+  __shared__ double r_ent[256];
+  __shared__ int r_used[256];
+  const int h = blockIdx.x, t = threadIdx.x;
+  const int W = 3 * Kp + 4;
+  const double inv = 1.0 / (double)ntok;
+  double ue = 0.0;
+  int used = 0;
+  for (int k = t; k < K; k += 256) {
+    double gs = 0.0;
+    int64_t n = 0, hc = 0;
+    for (int64_t b = 0; b < B; ++b)
+      for (int sp = 0; sp < S; ++sp) {
+        const float* base = diag + ((size_t)(b * H + h) * S + sp) * W;
+        gs += base[k];
+        n += (int64_t)base[Kp + k];
+        hc += (int64_t)base[2 * Kp + k];
+      }
+    if (counts) counts[(size_t)h * K + k] = (int32_t)hc;
+    if (mean_gamma) mean_gamma[(size_t)h * K + k] = (float)(gs * inv);
+    if (util) util[(size_t)h * K + k] = (float)((double)n * inv);
+    if (hc > 0) {
+      const double pk = (double)hc * inv;
+      ue -= pk * log(pk);
+      ++used;
+    }
+  }
+  r_ent[t] = ue;
+  r_used[t] = used;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (t < w) {
+      r_ent[t] += r_ent[t + w];
+      r_used[t] += r_used[t + w];
+    }
+    __syncthreads();
+  }
+  if (t == 0 && head_stats) {
+    double te = 0.0;
+    for (int64_t b = 0; b < B; ++b)
+      for (int sp = 0; sp < S; ++sp) te += diag[((size_t)(b * H + h) * S + sp) * W + 3 * Kp];
+    head_stats[(size_t)h * 3 + 0] = (float)(-te * inv);
+    head_stats[(size_t)h * 3 + 1] = K > 1 ? (float)(r_ent[0] / log((double)K)) : 0.f;
+    head_stats[(size_t)h * 3 + 2] = (float)r_used[0];
+  }
+}
+
 hipError_t launch_prologue(const Plan& p, const Tensors& t, hipStream_t s) {
   if (g_launch_hook) g_launch_hook("gma_prologue", s, 1);
   const int64_t rows = p.H * (int64_t)p.Kp;          // one wave per (head, component)
@@ -1087,6 +1237,39 @@ hipError_t launch_bidir(const Plan& p, const Tensors& t, hipStream_t s) {
     case 8: GMA_RESP_DR_CASES(BF, 2, 4)                                     \
   }                                                                         \
   break;
+
+#define GMA_USAGE_DR_CASES(BF, CPW, NG)                                     \
+  switch (p.DR) {                                                           \
+    case 16: e = run_usage<Cfg<BF, CPW, NG, 16, 16>>(p, t, s); break;       \
+    case 32: e = run_usage<Cfg<BF, CPW, NG, 32, 16>>(p, t, s); break;       \
+    case 64: e = run_usage<Cfg<BF, CPW, NG, 64, 16>>(p, t, s); break;       \
+    case 128: e = run_usage<Cfg<BF, CPW, NG, 128, 16>>(p, t, s); break;     \
+  }                                                                         \
+  break;
+#define GMA_USAGE_CASES(BF)                                                 \
+  switch (p.CT) {                                                           \
+    case 1: GMA_USAGE_DR_CASES(BF, 1, 1)                                    \
+    case 2: GMA_USAGE_DR_CASES(BF, 2, 1)                                    \
+    case 4: GMA_USAGE_DR_CASES(BF, 2, 2)                                    \
+    case 8: GMA_USAGE_DR_CASES(BF, 2, 4)                                    \
+  }                                                                         \
+  break;
+
+hipError_t launch_usage(const Plan& p, const Tensors& t, int32_t* counts, float* mean_gamma,
+                        float* util, float* head_stats, hipStream_t s) {
+  hipError_t e = hipErrorInvalidValue;
+  if (p.bf) {
+    switch (0) { default: GMA_USAGE_CASES(true) }
+  } else {
+    switch (0) { default: GMA_USAGE_CASES(false) }
+  }
+  if (e != hipSuccess) return e;
+  if (g_launch_hook) g_launch_hook("gma_usage_reduce", s, 1);
+  hipLaunchKernelGGL(gma_usage_reduce_kernel, dim3((unsigned)p.H), dim3(256), 0, s, t.diag, p.B,
+                     (int)p.H, p.S, p.Kp, p.K, p.B * p.N, counts, mean_gamma, util, head_stats);
+  if (g_launch_hook) g_launch_hook("gma_usage_reduce", s, 0);
+  return hipGetLastError();
+}
 
 hipError_t launch_resp(const Plan& p, const Tensors& t, hipStream_t s) {
   if (p.bf) {

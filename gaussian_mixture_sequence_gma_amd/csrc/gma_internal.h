@@ -54,6 +54,9 @@ struct Tensors {
   // Z [BH,K] of all the keys, unpadded (the carried state of a prefix)
   float* state_v = nullptr;
   float* state_z = nullptr;
+  // usage statistics: per-workgroup partials and the utilisation threshold
+  float* diag = nullptr;
+  float thr = 0.f;
 };
 
 // Launch helpers; each returns hipSuccess or the launch error.  `tag` names the
@@ -68,6 +71,10 @@ bool causal_split_ok(const Plan& p);
 hipError_t launch_bidir(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_resp(const Plan& p, const Tensors& t, hipStream_t s);
+// Usage statistics of the responsibilities of t.q (per head, over batches and
+// tokens); t.diag holds B*H*S*(3 K_pad + 4) floats of partials.
+hipError_t launch_usage(const Plan& p, const Tensors& t, int32_t* counts, float* mean_gamma,
+                        float* util, float* head_stats, hipStream_t s);
 // One causal decode step (N = 1 per sequence) against the carried state
 // state_v [BH,K,d_v], state_z [BH,K] (fp32, updated in place).
 hipError_t launch_decode(const Plan& p, const Tensors& t, float* state_v, float* state_z,

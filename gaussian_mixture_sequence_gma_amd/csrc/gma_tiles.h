@@ -103,6 +103,8 @@ struct BidirArgs {
   const float* z;         // [BH][Kp]
   int32_t* assign;        // [BH][N] or null
   float* gamma;           // resp: [BH][N][K] or null
+  float* diag;            // usage statistics: [BH][S][3 Kp + 4] per-workgroup partials
+  float thr;              // usage statistics: responsibility threshold of the utilisation
   int64_t N;
   int H;
   int K;

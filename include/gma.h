@@ -135,6 +135,34 @@ int gma_responsibilities(const void* X_r, const float* mu, const float* log_sigm
                          int32_t* assign, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/* Bytes of device workspace gma_usage_stats needs for this shape. */
+int gma_usage_workspace_bytes(const gma_dims* d, size_t* bytes);
+
+/* Component-usage diagnostics of the responsibilities (Eq. 3) of routing
+ * vectors X_r, per head over all batches and positions -- the marginal use of
+ * the mixture components and the hard assignments z_i = argmax_k gamma_ik that
+ * the paper proposes to monitor for under-use and collapse.  With
+ * T = B * N tokens per head:
+ *  X_r         [B,H,N,d_r] of d->dtype (queries or keys); d->d_v is not used
+ *              but must be a supported value
+ *  util_threshold  finite; e.g. 0.1
+ *  counts      optional [H,K] int32: tokens i with z_i = k (lowest index on ties)
+ *  mean_gamma  optional [H,K] fp32: (1/T) sum_i gamma_ik
+ *  utilization optional [H,K] fp32: (1/T) #{i : gamma_ik > util_threshold}
+ *  head_stats  optional [H,3] fp32: mean token entropy (1/T) sum_i
+ *              -sum_k gamma_ik ln gamma_ik (nats); usage entropy
+ *              -sum_k p_k ln p_k / ln K with p_k = counts_k / T (0 when K = 1);
+ *              the number of components with counts_k > 0
+ *  workspace   at least gma_usage_workspace_bytes bytes
+ * The responsibilities are those of gma_responsibilities (same arithmetic);
+ * the statistics are reduced on the device, none per token reaches memory.
+ * B*N must be below 2^31 (else GMA_ERR_UNSUPPORTED). */
+int gma_usage_stats(const void* X_r, const float* mu, const float* log_sigma2,
+                    const float* log_pi, const gma_dims* d, float util_threshold,
+                    int32_t* counts, float* mean_gamma, float* utilization,
+                    float* head_stats, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
 /* Carried state of a causal prefix ("Causal GMA": the prefix memories of
  * Eq. 8b at the last position, i.e. Eqs. 5-6 over all N keys given):
  *  K_X        [B,H,N,d_r] of d->dtype: key routing vectors of the prefix
