@@ -11,6 +11,9 @@ Linear-Time Sequence Mixing via Probabilistic Latent Routing", Section
 "Projections"), for which ``numpy.matmul`` in float64 serves as the library
 matrix product.
 
+``backward`` (gradients of the bidirectional forward) is plain numpy over the
+C responsibilities; its pins are in tests/test_oracle_backward.py (central
+finite differences of the C forward, invariants, closed cases).
 ``usage_stats`` (component-usage diagnostics) is plain numpy over the C
 responsibilities; its pins are in tests/test_oracle_usage.py.
 ``reparameterize`` (Eqs. 14-15) is plain numpy; its pins are in
@@ -183,6 +186,61 @@ def decode_step(S, z, q, k, v, mu, log_sigma2, log_pi, eps: float) -> dict:
     den = np.einsum("bhk,bhk->bh", gq, z2) + eps
     return {"S": S2, "z": z2, "out": num / den[:, :, None],
             "assign_q": rq["assign"][:, :, 0], "assign_k": rk["assign"][:, :, 0]}
+
+
+def backward(Q, K, V, mu, log_sigma2, log_pi, eps: float, dO) -> dict:
+    """Gradients of a scalar loss through the bidirectional forward, given
+    dL/dO ("Gradient structure": the score gradient of Eq. 18 and its
+    footnote, chained to the score's arguments by the chain rule of Eq. 17).
+
+    Forward, per unit: gamma = softmax_k(s) (Eq. 3), V~ = Gk^T V, Z = Gk^T 1
+    (Eqs. 5-6), n_i = Gq_i V~, d_i = Gq_i . Z + eps, o_i = n_i / d_i (Eq. 7).
+    Backward, in that order:
+      a_i = dO_i / d_i,  b_i = -(dO_i . o_i) / d_i
+      dGq_ik = a_i . V~_k + b_i Z_k
+      dV~_k = sum_i Gq_ik a_i,  dZ_k = sum_i Gq_ik b_i
+      dV_j = sum_k Gk_jk dV~_k,  dGk_jk = v_j . dV~_k + dZ_k
+      ds_ik = gamma_ik (dG_ik - sum_l gamma_il dG_il)                 (Eq. 18)
+    and with s_ik = log pi_k - (1/2) sum_d [(x_id - mu_kd)^2 w_kd + log sigma^2_kd],
+    w = exp(-log sigma^2):
+      dx_id = -sum_k ds_ik (x_id - mu_kd) w_kd
+      dmu_kd = sum_i ds_ik (x_id - mu_kd) w_kd
+      dlog sigma^2_kd = sum_i ds_ik ((x_id - mu_kd)^2 w_kd - 1) / 2
+      dlog pi_k = sum_i ds_ik
+    where the parameter sums run over queries and keys of every batch.
+    Shapes as forward; dO [B,H,N,d_v].  Returns float64 dQ, dK, dV, dmu,
+    dlog_sigma2, dlog_pi.
+    """
+    Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
+    mu, ls2, lpi = _f64(mu), _f64(log_sigma2), _f64(log_pi)
+    Gq = responsibilities(Q, mu, ls2, lpi)["gamma"]                 # [B,H,N,K]
+    Gk = responsibilities(K, mu, ls2, lpi)["gamma"]
+    Vt = np.einsum("bhnk,bhnd->bhkd", Gk, V)
+    Z = Gk.sum(axis=2)                                             # [B,H,K]
+    den = np.einsum("bhnk,bhk->bhn", Gq, Z) + eps
+    O = np.einsum("bhnk,bhkd->bhnd", Gq, Vt) / den[..., None]
+    a = dO / den[..., None]
+    bb = -(dO * O).sum(-1) / den
+    dGq = np.einsum("bhnd,bhkd->bhnk", a, Vt) + bb[..., None] * Z[:, :, None, :]
+    dVt = np.einsum("bhnk,bhnd->bhkd", Gq, a)
+    dZ = np.einsum("bhnk,bhn->bhk", Gq, bb)
+    dV = np.einsum("bhnk,bhkd->bhnd", Gk, dVt)
+    dGk = np.einsum("bhnd,bhkd->bhnk", V, dVt) + dZ[:, :, None, :]
+    w = np.exp(-ls2)                                               # [H,K,d_r]
+    out = {"dV": dV}
+    dmu = np.zeros_like(mu)
+    dls2 = np.zeros_like(ls2)
+    dlpi = np.zeros_like(lpi)
+    for name, X, G, dG in (("dQ", Q, Gq, dGq), ("dK", K, Gk, dGk)):
+        ds = G * (dG - (G * dG).sum(-1, keepdims=True))            # Eq. 18
+        diff = X[:, :, :, None, :] - mu[None, :, None, :, :]       # [B,H,N,K,d_r]
+        out[name] = -np.einsum("bhnk,bhnkd,hkd->bhnd", ds, diff, w)
+        dmu += np.einsum("bhnk,bhnkd,hkd->hkd", ds, diff, w)
+        dls2 += 0.5 * (np.einsum("bhnk,bhnkd,hkd->hkd", ds, diff ** 2, w)
+                       - ds.sum(axis=(0, 2))[:, :, None])
+        dlpi += ds.sum(axis=(0, 2))
+    out.update(dmu=dmu, dlog_sigma2=dls2, dlog_pi=dlpi)
+    return out
 
 
 def usage_stats(X, mu, log_sigma2, log_pi, util_threshold: float) -> dict:
