@@ -185,6 +185,9 @@ def main():
     ap.add_argument("--usage-stats", action="store_true",
                     help="time gma_usage_stats (component-usage diagnostics) over the "
                          "workload's queries instead of the forward")
+    ap.add_argument("--backward", action="store_true",
+                    help="time gma_backward (gradients of the bidirectional forward, dL/dO "
+                         "standard normal) instead of the forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", dest="flush", action="store_false",
                     help="do not evict the Infinity Cache between timed steps")
@@ -271,7 +274,19 @@ def main():
         u_f = torch.empty((3, w.H, w.K), dtype=torch.float32, device=dev)
         u_hs = torch.empty((w.H, 3), dtype=torch.float32, device=dev)
 
+    if args.backward:
+        if decode or w.d_model > 0 or w.causal:
+            sys.exit("--backward takes a bidirectional workload with routing vectors")
+        ws = api.alloc_workspace(binding.gma_backward_workspace_bytes(dims, 0), dev)
+        dO = torch.randn((w.B, w.H, w.N, w.d_v), device=dev).to(out_dtype)
+        grads = [torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V),
+                 torch.empty_like(mu), torch.empty_like(ls2), torch.empty_like(lpi)]
+
     def step():
+        if args.backward:
+            binding.gma_backward(Q, K, V, mu, ls2, lpi, w.eps, 0, dO, dims, *grads, ws,
+                                 ws.numel())
+            return
         if args.usage_stats:
             binding.gma_usage_stats(Q, mu, ls2, lpi, dims, 0.1, u_counts, u_f[0], u_f[1], u_hs,
                                     ws, ws.numel())
@@ -364,7 +379,7 @@ def main():
     step_bytes = sum(kernel_bytes(k, w, s_r, s_v, s_out) for k in kernels)
 
     cpu = None
-    if not args.no_cpu_baseline and not args.usage_stats:
+    if not args.no_cpu_baseline and not args.usage_stats and not args.backward:
         cpu = cpu_baseline(w, gen)
 
     cfg = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d_r": w.d_r, "d_v": w.d_v,
@@ -378,6 +393,8 @@ def main():
         cfg["d_model"] = w.d_model
     if args.usage_stats:
         cfg["step"] = "gma_usage_stats over the queries (threshold 0.1) in place of the forward"
+    if args.backward:
+        cfg["step"] = "gma_backward (all gradients, forward recomputed) in place of the forward"
     if args.reparam:
         cfg["reparam"] = "gma_reparameterize (Eqs. 14-15, eps_sigma 1e-4) at the start of each step"
     if decode:

@@ -68,6 +68,8 @@ def load():
     lib.gma_decode_step.argtypes = [P, P, P, P, P, P, f32, P, P, P, D, P, P, P]
     lib.gma_reparameterize.argtypes = [P, P, f32, ctypes.c_int64, ctypes.c_int32,
                                        ctypes.c_int32, P, P, P]
+    lib.gma_backward_workspace_bytes.argtypes = [D, i32, ctypes.POINTER(S)]
+    lib.gma_backward.argtypes = [P, P, P, P, P, P, f32, i32, P, D, P, P, P, P, P, P, P, S, P]
     lib.gma_usage_workspace_bytes.argtypes = [D, ctypes.POINTER(S)]
     lib.gma_usage_stats.argtypes = [P, P, P, P, D, f32, P, P, P, P, P, S, P]
     lib.gma_status_string.argtypes = [i32]
@@ -81,6 +83,7 @@ def load():
                "gma_layer_workspace_bytes", "gma_layer_forward", "gma_layer_projection_layout",
                "gma_responsibilities", "gma_prefix_state", "gma_decode_step", "gma_reparameterize",
                "gma_usage_workspace_bytes", "gma_usage_stats",
+               "gma_backward_workspace_bytes", "gma_backward",
                "gma_timing_enable", "gma_timing_collect"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -190,6 +193,21 @@ def gma_decode_step(q, k, v, mu, log_sigma2, log_pi, eps, state_v, state_z, out,
                                   _ptr(log_pi), float(eps), _ptr(state_v), _ptr(state_z),
                                   _ptr(out), ctypes.byref(dims), _ptr(assign_q),
                                   _ptr(assign_k), _stream(stream)))
+
+
+def gma_backward_workspace_bytes(dims: gma_dims, causal: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().gma_backward_workspace_bytes(ctypes.byref(dims), int(causal), ctypes.byref(n)))
+    return n.value
+
+
+def gma_backward(Q_X, K_X, V_X, mu, log_sigma2, log_pi, eps, causal, dO, dims: gma_dims, dQ, dK,
+                 dV, dmu, dlog_sigma2, dlog_pi, workspace=None, workspace_bytes=0, stream=None):
+    _check(load().gma_backward(_ptr(Q_X), _ptr(K_X), _ptr(V_X), _ptr(mu), _ptr(log_sigma2),
+                               _ptr(log_pi), float(eps), int(causal), _ptr(dO),
+                               ctypes.byref(dims), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dmu),
+                               _ptr(dlog_sigma2), _ptr(dlog_pi), _ptr(workspace),
+                               int(workspace_bytes), _stream(stream)))
 
 
 def gma_usage_workspace_bytes(dims: gma_dims) -> int:

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgma.so")
 OBJDIR = os.path.join(PKG, "_build")
 SOURCES = ["gma_api.hip", "gma_bidir.hip", "gma_causal.hip", "gma_proj.hip", "gma_decode.hip",
-           "gma_params.hip"]
+           "gma_params.hip", "gma_backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

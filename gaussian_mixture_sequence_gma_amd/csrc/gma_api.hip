@@ -448,6 +448,69 @@ int gma_usage_stats(const void* X_r, const float* mu, const float* log_sigma2,
   return finish_launch(e, "usage statistics launch");
 }
 
+static int backward_plan(const gma_dims* d, int causal, Plan& p) {
+  if (causal) return fail(GMA_ERR_UNSUPPORTED, "the causal backward is not available");
+  int st = make_plan(d, 0, false, p);
+  if (st != GMA_OK) return st;
+  if (d->N > (int64_t)65535 * 64)
+    return fail(GMA_ERR_UNSUPPORTED, "the backward takes N up to 65535 * 64");
+  return GMA_OK;
+}
+
+int gma_backward_workspace_bytes(const gma_dims* d, int causal, size_t* bytes) {
+  t_err.clear();
+  if (!bytes) return fail(GMA_ERR_INVALID_ARG, "bytes is NULL");
+  int st = check_dims(d, 0.f, causal);
+  if (st != GMA_OK) return st;
+  Plan p;
+  st = backward_plan(d, causal, p);
+  if (st != GMA_OK) return st;
+  *bytes = backward_workspace_bytes(p);
+  return GMA_OK;
+}
+
+int gma_backward(const void* Q_X, const void* K_X, const void* V_X, const float* mu,
+                 const float* log_sigma2, const float* log_pi, float eps, int causal,
+                 const void* dO, const gma_dims* d, void* dQ, void* dK, void* dV, float* dmu,
+                 float* dlog_sigma2, float* dlog_pi, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  t_err.clear();
+  int st = check_dims(d, eps, causal);
+  if (st != GMA_OK) return st;
+  if (!Q_X || !K_X || !V_X || !mu || !log_sigma2 || !log_pi || !dO || !dQ || !dK || !dV ||
+      !dmu || !dlog_sigma2 || !dlog_pi || !workspace)
+    return fail(GMA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(Q_X) || !aligned16(K_X) || !aligned16(V_X) || !aligned16(dO) ||
+      !aligned16(dQ) || !aligned16(dK) || !aligned16(dV) || !aligned16(workspace) ||
+      !aligned16(mu) || !aligned16(log_sigma2) || ((uintptr_t)log_pi & 3) ||
+      ((uintptr_t)dmu & 3) || ((uintptr_t)dlog_sigma2 & 3) || ((uintptr_t)dlog_pi & 3))
+    return fail(GMA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  Plan p;
+  st = backward_plan(d, causal, p);
+  if (st != GMA_OK) return st;
+  if (workspace_bytes < backward_workspace_bytes(p))
+    return fail(GMA_ERR_WORKSPACE, "workspace too small");
+  Tensors t;
+  t.q = Q_X;
+  t.k = K_X;
+  t.v = V_X;
+  t.mu = mu;
+  t.ls2 = log_sigma2;
+  t.lpi = log_pi;
+  t.eps = eps;
+  t.ws = static_cast<char*>(workspace);
+  BwdTensors g;
+  g.dO = dO;
+  g.dQ = dQ;
+  g.dK = dK;
+  g.dV = dV;
+  g.dmu = dmu;
+  g.dls2 = dlog_sigma2;
+  g.dlpi = dlog_pi;
+  return finish_launch(launch_backward(p, t, g, static_cast<hipStream_t>(stream)),
+                       "backward launch");
+}
+
 int gma_prefix_state(const void* K_X, const void* V_X, const float* mu, const float* log_sigma2,
                      const float* log_pi, float* state_v, float* state_z, const gma_dims* d,
                      int32_t* assign_k, void* workspace, size_t workspace_bytes, void* stream) {

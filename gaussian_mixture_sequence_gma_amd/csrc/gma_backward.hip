@@ -1,0 +1,469 @@
+// Backward of the bidirectional forward ("Gaussian Mixture Attention:
+// Linear-Time Sequence Mixing via Probabilistic Latent Routing", "Gradient
+// structure": the score gradient of Eq. 18, chained to Q_X, K_X, V_X and the
+// mixture parameters).
+//
+// Per unit u = (b, h), with Gq, Gk the [N,K] responsibilities (Eq. 3):
+//   [V~ | Z]   = Gk^T [V | 1]                    (Eqs. 5-6)
+//   [n | d-e]  = Gq [V~ | Z],  o = n / d          (Eq. 7)
+//   [a | b]    = [dO / d | -(dO . o) / d]
+//   dGq        = [a | b] [V~ | Z]^T               (= a . V~_k + b Z_k)
+//   [dV~ | dZ] = Gq^T [a | b]
+//   dV         = Gk dV~,   dGk = [V | 1] [dV~ | dZ]^T
+//   dS         = G (dG - rowsum(G dG))            (Eq. 18, queries and keys)
+//   [P1 | P2]  = dS [w | mu w],  w = exp(-log sigma^2):  dX = -X P1 + P2
+//   [R1|R2|r0] = dS^T [X | X^2 | 1],  summed over batches and over Q and K:
+//     dmu = w (R1 - mu r0),  dlog sigma^2 = w (R2 - 2 mu R1 + mu^2 r0) / 2 - r0 / 2,
+//     dlog pi = r0.
+// Appending a column of ones to the right operand turns every normaliser and
+// every rank-one term into part of a product, so the whole pass is a chain of
+// batched fp32 products (MFMA 16x16x4 f32, split over the token dimension
+// where the product contracts it) and row-wise elementwise kernels.  The
+// responsibilities come from the forward's responsibility kernel.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "gma_device.h"
+#include "gma_internal.h"
+
+namespace gma {
+
+namespace {
+
+// ---- batched fp32 product C[u] = op(A[u]) op(B[u]) --------------------------
+struct GemmArgs {
+  const float* A;
+  const float* B;
+  float* C;          // result, or the split partials [U][ksplit][M][N]
+  int M, N, K;
+  int lda, ldb, ldc;
+  int64_t sA, sB, sC;
+  int bmod;          // > 0: B of unit u is B + (u % bmod) * sB
+  int ksplit;
+};
+
+constexpr int kGT = 64;                 // output tile
+constexpr int kGK = 16;                 // contraction step
+constexpr int kGLD = kGK + 4;           // LDS row stride (floats), 16-byte rows
+
+// Row-major A is M x K (TA: stored K x M), B is K x N (TB: stored N x K).
+// Four waves, each a 32 x 32 quarter of the 64 x 64 tile as 2 x 2 MFMA tiles;
+// LDS holds A and B^T tiles as [row][k] so a lane reads its four contraction
+// values as one 16-byte load.  Loads are bounds-checked element by element
+// (any M, N, K and leading dimension).
+template <bool TA, bool TB>
+__global__ void __launch_bounds__(256) gma_bgemm_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) float As[kGT * kGLD];
+  __shared__ __attribute__((aligned(16))) float Bs[kGT * kGLD];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int r = lane & 15, gq = lane >> 4;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int n0 = blockIdx.x * kGT, m0 = blockIdx.y * kGT;
+  const int u = blockIdx.z / g.ksplit, ks = blockIdx.z % g.ksplit;
+  const int kchunk = ((g.K + g.ksplit - 1) / g.ksplit + kGK - 1) / kGK * kGK;
+  const int kb = ks * kchunk, ke = min(g.K, kb + kchunk);
+  const float* A = g.A + (size_t)u * g.sA;
+  const float* B = g.B + (size_t)(g.bmod > 0 ? u % g.bmod : u) * g.sB;
+
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int k0 = kb; k0 < ke; k0 += kGK) {
+    // stage A as [m][k] and B as [n][k]
+    if (!TA) {
+      const int m = t >> 2, k4 = (t & 3) * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int gm = m0 + m, gk = k0 + k4 + e;
+        As[m * kGLD + k4 + e] = (gm < g.M && gk < ke) ? A[(size_t)gm * g.lda + gk] : 0.f;
+      }
+    } else {
+      const int k = t >> 4, m4 = (t & 15) * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int gm = m0 + m4 + e, gk = k0 + k;
+        As[(m4 + e) * kGLD + k] = (gm < g.M && gk < ke) ? A[(size_t)gk * g.lda + gm] : 0.f;
+      }
+    }
+    if (TB) {
+      const int n = t >> 2, k4 = (t & 3) * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int gn = n0 + n, gk = k0 + k4 + e;
+        Bs[n * kGLD + k4 + e] = (gn < g.N && gk < ke) ? B[(size_t)gn * g.ldb + gk] : 0.f;
+      }
+    } else {
+      const int k = t >> 4, n4 = (t & 15) * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int gn = n0 + n4 + e, gk = k0 + k;
+        Bs[(n4 + e) * kGLD + k] = (gn < g.N && gk < ke) ? B[(size_t)gk * g.ldb + gn] : 0.f;
+      }
+    }
+    __syncthreads();
+    f32x4 a[2], b[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) a[i] = ld16<f32x4>(&As[(32 * wr + 16 * i + r) * kGLD + 4 * gq]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b[j] = ld16<f32x4>(&Bs[(32 * wc + 16 * j + r) * kGLD + 4 * gq]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mma(a[i], b[j], acc[i][j]);
+    __syncthreads();
+  }
+
+  // D layout: lane (r, gq) holds rows 4 gq + e, column r of each 16 x 16 tile
+  float* C;
+  int ldc;
+  if (g.ksplit > 1) {
+    C = g.C + ((size_t)u * g.ksplit + ks) * g.M * g.N;
+    ldc = g.N;
+  } else {
+    C = g.C + (size_t)u * g.sC;
+    ldc = g.ldc;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + 32 * wr + 16 * i + 4 * gq + e, n = n0 + 32 * wc + 16 * j + r;
+        if (m < g.M && n < g.N) C[(size_t)m * ldc + n] = acc[i][j][e];
+      }
+}
+
+// C[u][m][n] = sum over the splits, in split order.
+__global__ void __launch_bounds__(256) gma_split_sum_kernel(const float* __restrict__ part,
+                                                            int ksplit, int M, int N,
+                                                            float* __restrict__ C, int ldc,
+                                                            int64_t sC) {
+  const int u = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= M * N) return;
+  const float* p = part + (size_t)u * ksplit * M * N + i;
+  float s = 0.f;
+  for (int k = 0; k < ksplit; ++k) s += p[(size_t)k * M * N];
+  C[(size_t)u * sC + (size_t)(i / N) * ldc + i % N] = s;
+}
+
+template <class T>
+__device__ __forceinline__ float ldx(const void* p, size_t i) {
+  return (float)static_cast<const T*>(p)[i];
+}
+template <class T>
+__device__ __forceinline__ void stx(void* p, size_t i, float v) {
+  static_cast<T*>(p)[i] = (T)v;
+}
+
+// Per token: X3 = [x | x^2 | 1] for a routing vector, and (values) V1 = [v | 1].
+template <class T>
+__global__ void __launch_bounds__(256) gma_bwd_prep_kernel(const void* __restrict__ x, int d,
+                                                           int squares, int64_t rows,
+                                                           float* __restrict__ out) {
+  const int W = squares ? 2 * d + 1 : d + 1;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * W) return;
+  const int64_t row = i / W;
+  const int c = (int)(i - row * W);
+  float v;
+  if (c < d) {
+    v = ldx<T>(x, (size_t)row * d + c);
+  } else if (squares && c < 2 * d) {
+    const float xv = ldx<T>(x, (size_t)row * d + c - d);
+    v = xv * xv;
+  } else {
+    v = 1.f;
+  }
+  out[i] = v;
+}
+
+// Per head: WW = [w | mu w], w = exp(-log sigma^2), as [K][2 d_r].
+__global__ void __launch_bounds__(256) gma_bwd_params_kernel(const float* __restrict__ mu,
+                                                             const float* __restrict__ ls2,
+                                                             int64_t n, int d,
+                                                             float* __restrict__ ww) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int64_t row = i / d;
+  const int c = (int)(i - row * d);
+  const float w = expf(-ls2[i]);
+  ww[row * 2 * d + c] = w;
+  ww[row * 2 * d + d + c] = mu[i] * w;
+}
+
+// One wave per token: from [n | d - eps] and dO, [a | b] in place.
+template <class T>
+__global__ void __launch_bounds__(256) gma_bwd_ab_kernel(float* __restrict__ nd,
+                                                         const void* __restrict__ dO, int dv,
+                                                         float eps, int64_t rows) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  float* r = nd + (size_t)row * (dv + 1);
+  const float den = r[dv] + eps;
+  float dot = 0.f;
+  for (int c = lane; c < dv; c += 64) dot += ldx<T>(dO, (size_t)row * dv + c) * r[c];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) dot += xor_lane(dot, o);
+  const float inv = 1.f / den;
+  for (int c = lane; c < dv; c += 64) r[c] = ldx<T>(dO, (size_t)row * dv + c) * inv;
+  if (lane == 0) r[dv] = -dot * inv * inv;     // o = n / d: (dO . n) / d^2
+}
+
+// One wave per token: dS = G (dG - sum_l G_l dG_l), in place on dG.
+__global__ void __launch_bounds__(256) gma_bwd_softmax_kernel(const float* __restrict__ G,
+                                                              float* __restrict__ dG, int K,
+                                                              int64_t rows) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float* gr = G + (size_t)row * K;
+  float* dr = dG + (size_t)row * K;
+  float s = 0.f;
+  for (int k = lane; k < K; k += 64) s += gr[k] * dr[k];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += xor_lane(s, o);
+  for (int k = lane; k < K; k += 64) dr[k] = gr[k] * (dr[k] - s);
+}
+
+// dX = -x P1 + P2 from X3 = [x | x^2 | 1] and P = [P1 | P2].
+template <class T>
+__global__ void __launch_bounds__(256) gma_bwd_dx_kernel(const float* __restrict__ x3,
+                                                         const float* __restrict__ P, int d,
+                                                         int64_t rows, void* __restrict__ dx) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * d) return;
+  const int64_t row = i / d;
+  const int c = (int)(i - row * d);
+  const float* p = P + (size_t)row * 2 * d;
+  stx<T>(dx, i, -x3[(size_t)row * (2 * d + 1) + c] * p[c] + p[d + c]);
+}
+
+template <class T>
+__global__ void __launch_bounds__(256) gma_bwd_store_kernel(const float* __restrict__ src,
+                                                            int64_t n, void* __restrict__ dst) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) stx<T>(dst, i, src[i]);
+}
+
+// Per head: sum R = [R1 | R2 | r0] over batches and over queries and keys,
+// then the parameter gradients.
+__global__ void __launch_bounds__(256) gma_bwd_param_grad_kernel(
+    const float* __restrict__ Rq, const float* __restrict__ Rk, int64_t B, int H, int K, int d,
+    const float* __restrict__ mu, const float* __restrict__ ls2, float* __restrict__ dmu,
+    float* __restrict__ dls2, float* __restrict__ dlpi) {
+  const int h = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= K * d) return;
+  const int k = i / d, c = i - k * d;
+  const int W = 2 * d + 1;
+  double r1 = 0.0, r2 = 0.0, r0 = 0.0;
+  for (int src = 0; src < 2; ++src) {
+    const float* R = src ? Rk : Rq;
+    for (int64_t b = 0; b < B; ++b) {
+      const float* row = R + ((size_t)(b * H + h) * K + k) * W;
+      r1 += row[c];
+      r2 += row[d + c];
+      r0 += row[2 * d];
+    }
+  }
+  const size_t pi = (size_t)h * K * d + i;
+  const double m = mu[pi], w = exp(-(double)ls2[pi]);
+  dmu[pi] = (float)(w * (r1 - m * r0));
+  dls2[pi] = (float)(0.5 * w * (r2 - 2.0 * m * r1 + m * m * r0) - 0.5 * r0);
+  if (c == 0) dlpi[(size_t)h * K + k] = (float)r0;
+}
+
+}  // namespace
+
+// ---- host ------------------------------------------------------------------
+namespace {
+
+size_t r256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct BwdLayout {
+  size_t x3q, x3k, v1, nd, gq, gk, dgq, dgk, p, dv, vtz, dvtz, rq, rk, ww, part, total;
+  int ks_tok;        // split of the token contractions
+};
+
+BwdLayout bwd_layout(const Plan& p) {
+  BwdLayout L{};
+  const size_t U = (size_t)p.BH, N = (size_t)p.N, K = (size_t)p.K;
+  const size_t dr = p.DR, dv = p.DV;
+  // token contractions: M, N <= 2 d_r + 1 <= 257, so at most 25 output tiles
+  // per unit; split the tokens so that about 1024 workgroups run
+  int ks = (int)((1024 + U - 1) / U);
+  const int maxk = (int)((p.N + 255) / 256);      // at least 256 tokens per split
+  if (ks > maxk) ks = maxk;
+  if (ks > 32) ks = 32;
+  if ((int64_t)ks * p.BH > 65535) ks = (int)(65535 / p.BH);
+  if (ks < 1) ks = 1;
+  L.ks_tok = ks;
+  size_t off = r256(p.total);
+  auto take = [&](size_t bytes) { const size_t o = off; off += r256(bytes); return o; };
+  L.x3q = take(U * N * (2 * dr + 1) * 4);
+  L.x3k = take(U * N * (2 * dr + 1) * 4);
+  L.v1 = take(U * N * (dv + 1) * 4);
+  L.nd = take(U * N * (dv + 1) * 4);
+  L.gq = take(U * N * K * 4);
+  L.gk = take(U * N * K * 4);
+  L.dgq = take(U * N * K * 4);
+  L.dgk = take(U * N * K * 4);
+  L.p = take(U * N * 2 * dr * 4);
+  L.dv = take(U * N * dv * 4);
+  L.vtz = take(U * K * (dv + 1) * 4);
+  L.dvtz = take(U * K * (dv + 1) * 4);
+  L.rq = take(U * K * (2 * dr + 1) * 4);
+  L.rk = take(U * K * (2 * dr + 1) * 4);
+  L.ww = take((size_t)p.H * K * 2 * dr * 4);
+  const size_t wmax = (2 * dr + 1) > (dv + 1) ? (2 * dr + 1) : (dv + 1);
+  L.part = take(U * (size_t)ks * K * wmax * 4);
+  L.total = off;
+  return L;
+}
+
+hipError_t gemm(bool ta, bool tb, const float* A, int lda, int64_t sA, const float* B, int ldb,
+                int64_t sB, int bmod, float* C, int ldc, int64_t sC, int M, int N, int K,
+                int64_t U, int ksplit, float* part, hipStream_t s) {
+  GemmArgs g{A, B, ksplit > 1 ? part : C, M, N, K, lda, ldb, ldc, sA, sB, sC, bmod, ksplit};
+  const dim3 grid((unsigned)((N + kGT - 1) / kGT), (unsigned)((M + kGT - 1) / kGT),
+                  (unsigned)(U * ksplit));
+  if (!ta && !tb) hipLaunchKernelGGL((gma_bgemm_kernel<false, false>), grid, dim3(256), 0, s, g);
+  else if (!ta && tb) hipLaunchKernelGGL((gma_bgemm_kernel<false, true>), grid, dim3(256), 0, s, g);
+  else if (ta && !tb) hipLaunchKernelGGL((gma_bgemm_kernel<true, false>), grid, dim3(256), 0, s, g);
+  else hipLaunchKernelGGL((gma_bgemm_kernel<true, true>), grid, dim3(256), 0, s, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ksplit <= 1) return e;
+  hipLaunchKernelGGL(gma_split_sum_kernel, dim3((unsigned)((M * N + 255) / 256), (unsigned)U),
+                     dim3(256), 0, s, part, ksplit, M, N, C, ldc, sC);
+  return hipGetLastError();
+}
+
+unsigned blocks(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+template <class T>
+hipError_t run_backward(const Plan& p, const Tensors& t, const BwdTensors& gt, hipStream_t s) {
+  const BwdLayout L = bwd_layout(p);
+  char* ws = t.ws;
+  float* x3q = reinterpret_cast<float*>(ws + L.x3q);
+  float* x3k = reinterpret_cast<float*>(ws + L.x3k);
+  float* v1 = reinterpret_cast<float*>(ws + L.v1);
+  float* nd = reinterpret_cast<float*>(ws + L.nd);
+  float* Gq = reinterpret_cast<float*>(ws + L.gq);
+  float* Gk = reinterpret_cast<float*>(ws + L.gk);
+  float* dGq = reinterpret_cast<float*>(ws + L.dgq);
+  float* dGk = reinterpret_cast<float*>(ws + L.dgk);
+  float* P = reinterpret_cast<float*>(ws + L.p);
+  float* dvf = reinterpret_cast<float*>(ws + L.dv);
+  float* vtz = reinterpret_cast<float*>(ws + L.vtz);
+  float* dvtz = reinterpret_cast<float*>(ws + L.dvtz);
+  float* Rq = reinterpret_cast<float*>(ws + L.rq);
+  float* Rk = reinterpret_cast<float*>(ws + L.rk);
+  float* WW = reinterpret_cast<float*>(ws + L.ww);
+  float* part = reinterpret_cast<float*>(ws + L.part);
+  const int64_t U = p.BH, N = p.N, rows = U * N;
+  const int K = p.K, dr = p.DR, dv = p.DV, ks = L.ks_tok;
+  const int w3 = 2 * dr + 1, w1 = dv + 1;
+  hipError_t e;
+#define GMA_CHECK(x) do { e = (x); if (e != hipSuccess) return e; } while (0)
+  // responsibilities of queries and keys
+  Tensors tr = t;
+  tr.assign_q = nullptr;
+  tr.q = t.q;
+  tr.gamma = Gq;
+  GMA_CHECK(launch_resp(p, tr, s));
+  tr.q = t.k;
+  tr.gamma = Gk;
+  GMA_CHECK(launch_resp(p, tr, s));
+  if (g_launch_hook) g_launch_hook("gma_bwd_prep", s, 1);
+  hipLaunchKernelGGL(gma_bwd_prep_kernel<T>, dim3(blocks(rows * w3, 256)), dim3(256), 0, s, t.q,
+                     dr, 1, rows, x3q);
+  hipLaunchKernelGGL(gma_bwd_prep_kernel<T>, dim3(blocks(rows * w3, 256)), dim3(256), 0, s, t.k,
+                     dr, 1, rows, x3k);
+  hipLaunchKernelGGL(gma_bwd_prep_kernel<T>, dim3(blocks(rows * w1, 256)), dim3(256), 0, s, t.v,
+                     dv, 0, rows, v1);
+  hipLaunchKernelGGL(gma_bwd_params_kernel, dim3(blocks(p.H * K * dr, 256)), dim3(256), 0, s,
+                     t.mu, t.ls2, p.H * K * (int64_t)dr, dr, WW);
+  GMA_CHECK(hipGetLastError());
+  if (g_launch_hook) g_launch_hook("gma_bwd_prep", s, 0);
+
+  if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 1);
+  // [V~ | Z] = Gk^T [V | 1]
+  GMA_CHECK(gemm(true, false, Gk, K, N * K, v1, w1, N * w1, 0, vtz, w1, (int64_t)K * w1, K, w1,
+                 (int)N, U, ks, part, s));
+  // [n | d - eps] = Gq [V~ | Z]
+  GMA_CHECK(gemm(false, false, Gq, K, N * K, vtz, w1, (int64_t)K * w1, 0, nd, w1, N * w1,
+                 (int)N, w1, K, U, 1, part, s));
+  if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 0);
+  if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 1);
+  hipLaunchKernelGGL(gma_bwd_ab_kernel<T>, dim3(blocks(rows, 4)), dim3(256), 0, s, nd, gt.dO, dv,
+                     t.eps, rows);
+  GMA_CHECK(hipGetLastError());
+  if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 0);
+  if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 1);
+  // dGq = [a | b] [V~ | Z]^T
+  GMA_CHECK(gemm(false, true, nd, w1, N * w1, vtz, w1, (int64_t)K * w1, 0, dGq, K, N * K, (int)N,
+                 K, w1, U, 1, part, s));
+  // [dV~ | dZ] = Gq^T [a | b]
+  GMA_CHECK(gemm(true, false, Gq, K, N * K, nd, w1, N * w1, 0, dvtz, w1, (int64_t)K * w1, K, w1,
+                 (int)N, U, ks, part, s));
+  // dV = Gk dV~
+  GMA_CHECK(gemm(false, false, Gk, K, N * K, dvtz, w1, (int64_t)K * w1, 0, dvf, dv, N * dv,
+                 (int)N, dv, K, U, 1, part, s));
+  // dGk = [V | 1] [dV~ | dZ]^T
+  GMA_CHECK(gemm(false, true, v1, w1, N * w1, dvtz, w1, (int64_t)K * w1, 0, dGk, K, N * K, (int)N,
+                 K, w1, U, 1, part, s));
+  if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 0);
+  if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 1);
+  hipLaunchKernelGGL(gma_bwd_softmax_kernel, dim3(blocks(rows, 4)), dim3(256), 0, s, Gq, dGq, K,
+                     rows);
+  hipLaunchKernelGGL(gma_bwd_softmax_kernel, dim3(blocks(rows, 4)), dim3(256), 0, s, Gk, dGk, K,
+                     rows);
+  hipLaunchKernelGGL(gma_bwd_store_kernel<T>, dim3(blocks(rows * dv, 256)), dim3(256), 0, s, dvf,
+                     rows * dv, gt.dV);
+  GMA_CHECK(hipGetLastError());
+  if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 0);
+
+  for (int side = 0; side < 2; ++side) {
+    float* dS = side ? dGk : dGq;
+    float* x3 = side ? x3k : x3q;
+    if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 1);
+    // [P1 | P2] = dS [w | mu w] (the head's table)
+    GMA_CHECK(gemm(false, false, dS, K, N * K, WW, 2 * dr, (int64_t)K * 2 * dr, (int)p.H, P,
+                   2 * dr, N * 2 * dr, (int)N, 2 * dr, K, U, 1, part, s));
+    // [R1 | R2 | r0] = dS^T [x | x^2 | 1]
+    GMA_CHECK(gemm(true, false, dS, K, N * K, x3, w3, N * w3, 0, side ? Rk : Rq, w3,
+                   (int64_t)K * w3, K, w3, (int)N, U, ks, part, s));
+    if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 0);
+    if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 1);
+    hipLaunchKernelGGL(gma_bwd_dx_kernel<T>, dim3(blocks(rows * dr, 256)), dim3(256), 0, s, x3,
+                       P, dr, rows, side ? gt.dK : gt.dQ);
+    GMA_CHECK(hipGetLastError());
+    if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 0);
+  }
+  if (g_launch_hook) g_launch_hook("gma_bwd_params", s, 1);
+  hipLaunchKernelGGL(gma_bwd_param_grad_kernel, dim3(blocks((int64_t)K * dr, 256), (unsigned)p.H),
+                     dim3(256), 0, s, Rq, Rk, p.B, (int)p.H, K, dr, t.mu, t.ls2, gt.dmu,
+                     gt.dls2, gt.dlpi);
+  if (g_launch_hook) g_launch_hook("gma_bwd_params", s, 0);
+#undef GMA_CHECK
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(const Plan& p) { return bwd_layout(p).total; }
+
+hipError_t launch_backward(const Plan& p, const Tensors& t, const BwdTensors& gt,
+                           hipStream_t s) {
+  const hipError_t e = launch_prologue(p, t, s);
+  if (e != hipSuccess) return e;
+  return p.out_bf ? run_backward<bf16>(p, t, gt, s) : run_backward<float>(p, t, gt, s);
+}
+
+}  // namespace gma

@@ -79,6 +79,19 @@ hipError_t launch_usage(const Plan& p, const Tensors& t, int32_t* counts, float*
 // state_v [BH,K,d_v], state_z [BH,K] (fp32, updated in place).
 hipError_t launch_decode(const Plan& p, const Tensors& t, float* state_v, float* state_z,
                          hipStream_t s);
+// Backward of the bidirectional forward: dO in, gradients out (dQ, dK, dV of
+// the input dtype; parameter gradients fp32, written).
+struct BwdTensors {
+  const void* dO = nullptr;
+  void* dQ = nullptr;
+  void* dK = nullptr;
+  void* dV = nullptr;
+  float* dmu = nullptr;
+  float* dls2 = nullptr;
+  float* dlpi = nullptr;
+};
+size_t backward_workspace_bytes(const Plan& p);
+hipError_t launch_backward(const Plan& p, const Tensors& t, const BwdTensors& gt, hipStream_t s);
 // log sigma^2 = log(softplus(omega) + eps_sigma) over [H,K,d_r] and
 // log pi = alpha - logsumexp(alpha) over [H,K].
 hipError_t launch_reparam(const float* omega, const float* alpha, float eps_sigma, int64_t H,

@@ -135,6 +135,35 @@ int gma_responsibilities(const void* X_r, const float* mu, const float* log_sigm
                          int32_t* assign, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/* Bytes of device workspace gma_backward needs (causal must be 0). */
+int gma_backward_workspace_bytes(const gma_dims* d, int causal, size_t* bytes);
+
+/* Gradients of a scalar loss L through the bidirectional forward, given
+ * dL/dO ("Gradient structure": the score gradient of Eq. 18, gamma times the
+ * upstream gradient minus its gamma-weighted mean, chained through the
+ * Gaussian score of Eqs. 2-3 and 16 to the routing vectors and the
+ * parameters, and through Eqs. 5-7 to the values).
+ *  Q_X, K_X, V_X, mu, log_sigma2, log_pi, eps  as gma_forward (causal must
+ *             be 0: the causal backward returns GMA_ERR_UNSUPPORTED)
+ *  dO         [B,H,N,d_v] of d->dtype: dL/dO
+ *  dQ, dK     [B,H,N,d_r] of d->dtype: written
+ *  dV         [B,H,N,d_v] of d->dtype: written
+ *  dmu, dlog_sigma2  [H,K,d_r] fp32; dlog_pi [H,K] fp32: written (not
+ *             accumulated), summed over batches and over queries and keys
+ *  workspace  at least gma_backward_workspace_bytes bytes (it holds the
+ *             responsibilities, their gradients and fp32 copies of the inputs:
+ *             about 4 (2(2 d_r + 1) + 2(d_v + 1) + 4K + 2 d_r + d_v) bytes per
+ *             token-head)
+ * The forward quantities are recomputed; the output O is not an input.
+ * fp32 arithmetic (products on fp32 MFMA); for bf16 inputs the
+ * responsibilities are those of the bf16 forward.  N is limited to
+ * 65535 * 64 (else GMA_ERR_UNSUPPORTED). */
+int gma_backward(const void* Q_X, const void* K_X, const void* V_X, const float* mu,
+                 const float* log_sigma2, const float* log_pi, float eps, int causal,
+                 const void* dO, const gma_dims* d, void* dQ, void* dK, void* dV,
+                 float* dmu, float* dlog_sigma2, float* dlog_pi, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace gma_usage_stats needs for this shape. */
 int gma_usage_workspace_bytes(const gma_dims* d, size_t* bytes);
 

@@ -233,3 +233,26 @@ def test_reparameterize_rejects_before_launch():
     assert st(K=0) == B.GMA_ERR_INVALID_ARG
     assert st(H=70000) == B.GMA_ERR_UNSUPPORTED
     assert st(H=65535, K=4096, d_r=4096) == B.GMA_ERR_UNSUPPORTED
+
+
+def test_backward_rejects_before_launch():
+    def st(**over):
+        args = dict(Q_X=A16, K_X=A16, V_X=A16, mu=A16, log_sigma2=A16, log_pi=A16, eps=1e-6,
+                    causal=0, dO=A16, dims=_dims(), dQ=A16, dK=A16, dV=A16, dmu=A16,
+                    dlog_sigma2=A16, dlog_pi=A16, workspace=A16, workspace_bytes=1 << 50,
+                    stream=0)
+        args.update(over)
+        with pytest.raises(B.GmaError) as ei:
+            B.gma_backward(**args)
+        return ei.value.status
+    assert st(causal=1) == B.GMA_ERR_UNSUPPORTED
+    assert st(dO=None) == B.GMA_ERR_INVALID_ARG
+    assert st(dmu=None) == B.GMA_ERR_INVALID_ARG
+    assert st(dQ=MIS) == B.GMA_ERR_INVALID_ARG
+    assert st(workspace_bytes=1024) == B.GMA_ERR_WORKSPACE
+    assert st(dims=_dims(N=65535 * 64 + 1)) == B.GMA_ERR_UNSUPPORTED
+    n = B.gma_backward_workspace_bytes(_dims(), 0)
+    assert n > B.gma_forward_workspace_bytes(_dims(), 0)
+    assert st(workspace_bytes=n - 1) == B.GMA_ERR_WORKSPACE
+    with pytest.raises(B.GmaError):
+        B.gma_backward_workspace_bytes(_dims(), 1)

@@ -1,0 +1,64 @@
+"""GPU parity of gma_backward (gradients of the bidirectional forward, "Gradient
+structure" of "Gaussian Mixture Attention: Linear-Time Sequence Mixing via
+Probabilistic Latent Routing", Eq. 18) against oracle.backward.
+
+Metric: per gradient tensor, the normwise relative error ||g - r||_F / ||r||_F
+(elements of dS are differences of nearly equal terms, so an element-wise
+bound is meaningless).  Bound: 1e-4 for fp32 inputs (fp32 arithmetic on fp32
+MFMA); 2e-2 for bf16 inputs (responsibilities of the bf16 forward, bf16
+storage of dQ, dK, dV).  With K = 1 no gradient reaches the routing side and
+those tensors must be (near) zero.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gaussian_mixture_sequence_gma_amd import api, inputs
+from tests.parity import upload
+
+pytestmark = pytest.mark.gpu
+
+BWD_TOL = {"f32": 1e-4, "bf16": 2e-2}
+NAMES = ("dQ", "dK", "dV", "dmu", "dlog_sigma2", "dlog_pi")
+
+
+def _case(B, H, N, d_r, d_v, K, dtype, skew, seed=31):
+    kw = dict(mu_var=1.5, ls2_lo=-1.5, ls2_hi=0.5, logit_var=2.0) if skew else {}
+    w = inputs.Workload("bwd", B, H, N, d_r, d_v, K, dtype, False, **kw)
+    gen = inputs.generate(w, seed)
+    rng = np.random.default_rng(seed + 1)
+    dO = inputs._store(rng.standard_normal((B, H, N, d_v), dtype=np.float32), dtype)
+    dev = upload(gen)
+    dOd = api.host_tensor_to_device(dO, "cuda")
+    g = api.backward(dev["Q"], dev["K"], dev["V"], dev["mu"], dev["log_sigma2"], dev["log_pi"],
+                     dOd, w.eps)
+    torch.cuda.synchronize()
+    ref = oracle.backward(gen["Q"].f32, gen["K"].f32, gen["V"].f32, gen["mu"],
+                          gen["log_sigma2"], gen["log_pi"], w.eps, dO.f32)
+    return {k: g[k].float().cpu().numpy().astype(np.float64) for k in NAMES}, ref
+
+
+@pytest.mark.parametrize("B,H,N,d_r,d_v,K,dtype,skew", [
+    (2, 2, 300, 32, 64, 40, "f32", False),
+    (1, 3, 513, 64, 128, 128, "f32", True),
+    (2, 2, 100, 128, 16, 7, "f32", False),
+    (2, 2, 1000, 64, 64, 64, "bf16", False),
+    (1, 2, 200, 128, 32, 100, "bf16", False),
+    (1, 2, 4096, 64, 128, 128, "bf16", True),     # the long-context head shape
+])
+def test_backward_matches_oracle(B, H, N, d_r, d_v, K, dtype, skew):
+    got, ref = _case(B, H, N, d_r, d_v, K, dtype, skew)
+    errs = {k: np.linalg.norm(got[k] - ref[k]) / np.linalg.norm(ref[k]) for k in NAMES}
+    print("backward %s: %s" % ((B, H, N, d_r, d_v, K, dtype),
+                               "  ".join("%s %.2e" % kv for kv in errs.items())))
+    for k in NAMES:
+        assert errs[k] <= BWD_TOL[dtype], k
+
+
+def test_backward_single_component():
+    got, ref = _case(1, 2, 77, 16, 16, 1, "f32", False)
+    scale = np.abs(ref["dV"]).max()
+    for k in ("dQ", "dK", "dmu", "dlog_sigma2", "dlog_pi"):
+        assert np.abs(got[k]).max() <= 1e-5 * max(scale, 1.0), k
+    assert np.linalg.norm(got["dV"] - ref["dV"]) / np.linalg.norm(ref["dV"]) <= 1e-5
