@@ -64,6 +64,10 @@ def kernel_bytes(name: str, w, s_r: int, s_v: int, s_out: int) -> int:
         return T * (w.d_r * s_r + w.d_v * s_out)
     if name == "gma_causal":
         return T * (2 * w.d_r * s_r + w.d_v * s_v + w.d_v * s_out)
+    if name == "gma_backward":
+        # the whole backward: Q_X, K_X, V_X and dO read, dQ, dK, dV written
+        # (the responsibilities and their gradients are intermediates)
+        return T * (4 * w.d_r + 3 * w.d_v) * s_out + w.H * w.K * (4 * w.d_r + 1) * 4
     if name == "gma_usage":
         return T * w.d_r * s_r
     if name == "gma_decode":
@@ -358,6 +362,11 @@ def main():
 
     kernels = {name: {"launches": n, "avg_us": 1e3 * tot / max(n, 1)} for name, n, tot in kt}
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
+    if args.backward:
+        # the backward is a chain of passes over fp32 intermediates: its
+        # roofline is taken for the whole step against its algorithmic bytes
+        kernels["gma_backward"] = {"launches": args.steps, "avg_us": 1e3 * ms}
+        dom = "gma_backward"
     dom_bytes = kernel_bytes(dom, w, s_r, s_v, s_out)
     dom_flops = kernel_flops(dom, w)
     prof = profile_counters(dom, w.name, kernel_source_hash())

@@ -40,17 +40,22 @@ struct GemmArgs {
   int64_t sA, sB, sC;
   int bmod;          // > 0: B of unit u is B + (u % bmod) * sB
   int ksplit;
+  int vec;           // bit 0: A rows 16-byte aligned; bit 1: B rows
 };
 
 constexpr int kGT = 64;                 // output tile
-constexpr int kGK = 16;                 // contraction step
+constexpr int kGK = 16;                 // contraction step (a multiple of 16)
+constexpr int kGQ = kGK / 16;           // four-element groups per thread and operand
 constexpr int kGLD = kGK + 4;           // LDS row stride (floats), 16-byte rows
 
 // Row-major A is M x K (TA: stored K x M), B is K x N (TB: stored N x K).
 // Four waves, each a 32 x 32 quarter of the 64 x 64 tile as 2 x 2 MFMA tiles;
 // LDS holds A and B^T tiles as [row][k] so a lane reads its four contraction
-// values as one 16-byte load.  Loads are bounds-checked element by element
-// (any M, N, K and leading dimension).
+// values as one 16-byte load.  Each thread moves kGQ x 4 consecutive elements of
+// a row of A and of B per step: 16-byte loads where the operand allows it
+// (g.vec bit 0 for A, bit 1 for B: leading dimension, unit stride and base
+// 16-byte aligned) and the four are in bounds, else four checked loads; the
+// next step's elements are loaded while the current step multiplies.
 template <bool TA, bool TB>
 __global__ void __launch_bounds__(256) gma_bgemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) float As[kGT * kGLD];
@@ -64,6 +69,43 @@ __global__ void __launch_bounds__(256) gma_bgemm_kernel(GemmArgs g) {
   const int kb = ks * kchunk, ke = min(g.K, kb + kchunk);
   const float* A = g.A + (size_t)u * g.sA;
   const float* B = g.B + (size_t)(g.bmod > 0 ? u % g.bmod : u) * g.sB;
+  const bool va = g.vec & 1, vb = (g.vec >> 1) & 1;
+
+  // this thread's kGQ x 4 elements: along k (A: row m; B^T: row n) or along m / n
+  constexpr int TPK = 16 / kGQ;                 // threads per k row of a transposed operand
+  const int ar = TA ? t / TPK : t >> 2, ac = TA ? (t % TPK) * 4 * kGQ : (t & 3) * 4 * kGQ;
+  const int br = TB ? t >> 2 : t / TPK, bc = TB ? (t & 3) * 4 * kGQ : (t % TPK) * 4 * kGQ;
+  float ra[4 * kGQ], rb[4 * kGQ];
+  // four consecutive elements of a row: p[0..3], valid while idx + e < lim
+  auto quad = [](bool vec, const float* p, bool row_ok, int idx, int lim, float* dst) {
+    if (vec && row_ok && idx + 3 < lim) {
+      const f32x4 v = ld16<f32x4>(p);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[e] = v[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[e] = (row_ok && idx + e < lim) ? p[e] : 0.f;
+    }
+  };
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int h = 0; h < kGQ; ++h) {
+      if (!TA) {                                 // A[m][k], m = m0 + ar, k = k0 + ac + 4h + e
+        const int gm = m0 + ar, gk = k0 + ac + 4 * h;
+        quad(va, A + (size_t)gm * g.lda + gk, gm < g.M, gk, ke, ra + 4 * h);
+      } else {                                   // A[k][m], k = k0 + ar, m = m0 + ac + 4h + e
+        const int gk = k0 + ar, gm = m0 + ac + 4 * h;
+        quad(va, A + (size_t)gk * g.lda + gm, gk < ke, gm, g.M, ra + 4 * h);
+      }
+      if (TB) {                                  // B[n][k], n = n0 + br, k = k0 + bc + 4h + e
+        const int gn = n0 + br, gk = k0 + bc + 4 * h;
+        quad(vb, B + (size_t)gn * g.ldb + gk, gn < g.N, gk, ke, rb + 4 * h);
+      } else {                                   // B[k][n], k = k0 + br, n = n0 + bc + 4h + e
+        const int gk = k0 + br, gn = n0 + bc + 4 * h;
+        quad(vb, B + (size_t)gk * g.ldb + gn, gk < ke, gn, g.N, rb + 4 * h);
+      }
+    }
+  };
 
   f32x4 acc[2][2];
 #pragma unroll
@@ -71,48 +113,40 @@ __global__ void __launch_bounds__(256) gma_bgemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  if (kb < ke) load(kb);
   for (int k0 = kb; k0 < ke; k0 += kGK) {
     // stage A as [m][k] and B as [n][k]
-    if (!TA) {
-      const int m = t >> 2, k4 = (t & 3) * 4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int gm = m0 + m, gk = k0 + k4 + e;
-        As[m * kGLD + k4 + e] = (gm < g.M && gk < ke) ? A[(size_t)gm * g.lda + gk] : 0.f;
+    for (int h = 0; h < kGQ; ++h) {
+      if (!TA) {
+        st16(&As[ar * kGLD + ac + 4 * h], f32x4{ra[4 * h], ra[4 * h + 1], ra[4 * h + 2], ra[4 * h + 3]});
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) As[(ac + 4 * h + e) * kGLD + ar] = ra[4 * h + e];
       }
-    } else {
-      const int k = t >> 4, m4 = (t & 15) * 4;
+      if (TB) {
+        st16(&Bs[br * kGLD + bc + 4 * h], f32x4{rb[4 * h], rb[4 * h + 1], rb[4 * h + 2], rb[4 * h + 3]});
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int gm = m0 + m4 + e, gk = k0 + k;
-        As[(m4 + e) * kGLD + k] = (gm < g.M && gk < ke) ? A[(size_t)gk * g.lda + gm] : 0.f;
-      }
-    }
-    if (TB) {
-      const int n = t >> 2, k4 = (t & 3) * 4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int gn = n0 + n, gk = k0 + k4 + e;
-        Bs[n * kGLD + k4 + e] = (gn < g.N && gk < ke) ? B[(size_t)gn * g.ldb + gk] : 0.f;
-      }
-    } else {
-      const int k = t >> 4, n4 = (t & 15) * 4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int gn = n0 + n4 + e, gk = k0 + k;
-        Bs[(n4 + e) * kGLD + k] = (gn < g.N && gk < ke) ? B[(size_t)gk * g.ldb + gn] : 0.f;
+        for (int e = 0; e < 4; ++e) Bs[(bc + 4 * h + e) * kGLD + br] = rb[4 * h + e];
       }
     }
     __syncthreads();
-    f32x4 a[2], b[2];
+    if (k0 + kGK < ke) load(k0 + kGK);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) a[i] = ld16<f32x4>(&As[(32 * wr + 16 * i + r) * kGLD + 4 * gq]);
+    for (int kk = 0; kk < kGK / 16; ++kk) {
+      f32x4 a[2], b[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) b[j] = ld16<f32x4>(&Bs[(32 * wc + 16 * j + r) * kGLD + 4 * gq]);
+      for (int i = 0; i < 2; ++i)
+        a[i] = ld16<f32x4>(&As[(32 * wr + 16 * i + r) * kGLD + 16 * kk + 4 * gq]);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 2; ++j)
+        b[j] = ld16<f32x4>(&Bs[(32 * wc + 16 * j + r) * kGLD + 16 * kk + 4 * gq]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mma(a[i], b[j], acc[i][j]);
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mma(a[i], b[j], acc[i][j]);
+    }
     __syncthreads();
   }
 
@@ -160,26 +194,30 @@ __device__ __forceinline__ void stx(void* p, size_t i, float v) {
   static_cast<T*>(p)[i] = (T)v;
 }
 
-// Per token: X3 = [x | x^2 | 1] for a routing vector, and (values) V1 = [v | 1].
+// Per token: X3 = [x | x^2 | 1] for a routing vector, and (values) V1 = [v | 1],
+// rows of stride ld (the padding columns are never read).  128 threads per
+// row, two rows at a time per workgroup, striding over the rows.
 template <class T>
 __global__ void __launch_bounds__(256) gma_bwd_prep_kernel(const void* __restrict__ x, int d,
-                                                           int squares, int64_t rows,
+                                                           int squares, int64_t rows, int ld,
                                                            float* __restrict__ out) {
   const int W = squares ? 2 * d + 1 : d + 1;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= rows * W) return;
-  const int64_t row = i / W;
-  const int c = (int)(i - row * W);
-  float v;
-  if (c < d) {
-    v = ldx<T>(x, (size_t)row * d + c);
-  } else if (squares && c < 2 * d) {
-    const float xv = ldx<T>(x, (size_t)row * d + c - d);
-    v = xv * xv;
-  } else {
-    v = 1.f;
+  for (int64_t row = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7); row < rows;
+       row += (int64_t)gridDim.x * 2) {
+    float* o = out + (size_t)row * ld;
+    for (int c = threadIdx.x & 127; c < W; c += 128) {
+      float v;
+      if (c < d) {
+        v = ldx<T>(x, (size_t)row * d + c);
+      } else if (squares && c < 2 * d) {
+        const float xv = ldx<T>(x, (size_t)row * d + c - d);
+        v = xv * xv;
+      } else {
+        v = 1.f;
+      }
+      o[c] = v;
+    }
   }
-  out[i] = v;
 }
 
 // Per head: WW = [w | mu w], w = exp(-log sigma^2), as [K][2 d_r].
@@ -200,11 +238,11 @@ __global__ void __launch_bounds__(256) gma_bwd_params_kernel(const float* __rest
 template <class T>
 __global__ void __launch_bounds__(256) gma_bwd_ab_kernel(float* __restrict__ nd,
                                                          const void* __restrict__ dO, int dv,
-                                                         float eps, int64_t rows) {
+                                                         int ld, float eps, int64_t rows) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  float* r = nd + (size_t)row * (dv + 1);
+  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows;
+       row += (int64_t)gridDim.x * 4) {
+  float* r = nd + (size_t)row * ld;
   const float den = r[dv] + eps;
   float dot = 0.f;
   for (int c = lane; c < dv; c += 64) dot += ldx<T>(dO, (size_t)row * dv + c) * r[c];
@@ -213,6 +251,7 @@ __global__ void __launch_bounds__(256) gma_bwd_ab_kernel(float* __restrict__ nd,
   const float inv = 1.f / den;
   for (int c = lane; c < dv; c += 64) r[c] = ldx<T>(dO, (size_t)row * dv + c) * inv;
   if (lane == 0) r[dv] = -dot * inv * inv;     // o = n / d: (dO . n) / d^2
+  }
 }
 
 // One wave per token: dS = G (dG - sum_l G_l dG_l), in place on dG.
@@ -220,8 +259,8 @@ __global__ void __launch_bounds__(256) gma_bwd_softmax_kernel(const float* __res
                                                               float* __restrict__ dG, int K,
                                                               int64_t rows) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows;
+       row += (int64_t)gridDim.x * 4) {
   const float* gr = G + (size_t)row * K;
   float* dr = dG + (size_t)row * K;
   float s = 0.f;
@@ -229,39 +268,41 @@ __global__ void __launch_bounds__(256) gma_bwd_softmax_kernel(const float* __res
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) s += xor_lane(s, o);
   for (int k = lane; k < K; k += 64) dr[k] = gr[k] * (dr[k] - s);
+  }
 }
 
 // dX = -x P1 + P2 from X3 = [x | x^2 | 1] and P = [P1 | P2].
 template <class T>
-__global__ void __launch_bounds__(256) gma_bwd_dx_kernel(const float* __restrict__ x3,
+__global__ void __launch_bounds__(256) gma_bwd_dx_kernel(const float* __restrict__ x3, int ld,
                                                          const float* __restrict__ P, int d,
                                                          int64_t rows, void* __restrict__ dx) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= rows * d) return;
-  const int64_t row = i / d;
-  const int c = (int)(i - row * d);
-  const float* p = P + (size_t)row * 2 * d;
-  stx<T>(dx, i, -x3[(size_t)row * (2 * d + 1) + c] * p[c] + p[d + c]);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < rows * d;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t row = i / d;
+    const int c = (int)(i - row * d);
+    const float* p = P + (size_t)row * 2 * d;
+    stx<T>(dx, i, -x3[(size_t)row * ld + c] * p[c] + p[d + c]);
+  }
 }
 
 template <class T>
 __global__ void __launch_bounds__(256) gma_bwd_store_kernel(const float* __restrict__ src,
                                                             int64_t n, void* __restrict__ dst) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) stx<T>(dst, i, src[i]);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    stx<T>(dst, i, src[i]);
 }
 
 // Per head: sum R = [R1 | R2 | r0] over batches and over queries and keys,
 // then the parameter gradients.
 __global__ void __launch_bounds__(256) gma_bwd_param_grad_kernel(
     const float* __restrict__ Rq, const float* __restrict__ Rk, int64_t B, int H, int K, int d,
+    int W,
     const float* __restrict__ mu, const float* __restrict__ ls2, float* __restrict__ dmu,
     float* __restrict__ dls2, float* __restrict__ dlpi) {
   const int h = blockIdx.y;
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= K * d) return;
   const int k = i / d, c = i - k * d;
-  const int W = 2 * d + 1;
   double r1 = 0.0, r2 = 0.0, r0 = 0.0;
   for (int src = 0; src < 2; ++src) {
     const float* R = src ? Rk : Rq;
@@ -306,20 +347,21 @@ BwdLayout bwd_layout(const Plan& p) {
   L.ks_tok = ks;
   size_t off = r256(p.total);
   auto take = [&](size_t bytes) { const size_t o = off; off += r256(bytes); return o; };
-  L.x3q = take(U * N * (2 * dr + 1) * 4);
-  L.x3k = take(U * N * (2 * dr + 1) * 4);
-  L.v1 = take(U * N * (dv + 1) * 4);
-  L.nd = take(U * N * (dv + 1) * 4);
+  const size_t w3p = 2 * dr + 4, w1p = dv + 4;      // padded row strides
+  L.x3q = take(U * N * w3p * 4);
+  L.x3k = take(U * N * w3p * 4);
+  L.v1 = take(U * N * w1p * 4);
+  L.nd = take(U * N * w1p * 4);
   L.gq = take(U * N * K * 4);
   L.gk = take(U * N * K * 4);
   L.dgq = take(U * N * K * 4);
   L.dgk = take(U * N * K * 4);
   L.p = take(U * N * 2 * dr * 4);
   L.dv = take(U * N * dv * 4);
-  L.vtz = take(U * K * (dv + 1) * 4);
-  L.dvtz = take(U * K * (dv + 1) * 4);
-  L.rq = take(U * K * (2 * dr + 1) * 4);
-  L.rk = take(U * K * (2 * dr + 1) * 4);
+  L.vtz = take(U * K * w1p * 4);
+  L.dvtz = take(U * K * w1p * 4);
+  L.rq = take(U * K * w3p * 4);
+  L.rk = take(U * K * w3p * 4);
   L.ww = take((size_t)p.H * K * 2 * dr * 4);
   const size_t wmax = (2 * dr + 1) > (dv + 1) ? (2 * dr + 1) : (dv + 1);
   L.part = take(U * (size_t)ks * K * wmax * 4);
@@ -330,7 +372,9 @@ BwdLayout bwd_layout(const Plan& p) {
 hipError_t gemm(bool ta, bool tb, const float* A, int lda, int64_t sA, const float* B, int ldb,
                 int64_t sB, int bmod, float* C, int ldc, int64_t sC, int M, int N, int K,
                 int64_t U, int ksplit, float* part, hipStream_t s) {
-  GemmArgs g{A, B, ksplit > 1 ? part : C, M, N, K, lda, ldb, ldc, sA, sB, sC, bmod, ksplit};
+  const int vec = ((lda % 4 == 0 && sA % 4 == 0 && ((uintptr_t)A & 15) == 0) ? 1 : 0) |
+                  ((ldb % 4 == 0 && sB % 4 == 0 && ((uintptr_t)B & 15) == 0) ? 2 : 0);
+  GemmArgs g{A, B, ksplit > 1 ? part : C, M, N, K, lda, ldb, ldc, sA, sB, sC, bmod, ksplit, vec};
   const dim3 grid((unsigned)((N + kGT - 1) / kGT), (unsigned)((M + kGT - 1) / kGT),
                   (unsigned)(U * ksplit));
   if (!ta && !tb) hipLaunchKernelGGL((gma_bgemm_kernel<false, false>), grid, dim3(256), 0, s, g);
@@ -345,6 +389,11 @@ hipError_t gemm(bool ta, bool tb, const float* A, int lda, int64_t sA, const flo
 }
 
 unsigned blocks(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+// striding kernels: at most eight workgroups per compute unit
+unsigned sblocks(int64_t n, int per) {
+  const int64_t b = (n + per - 1) / per;
+  return (unsigned)(b < 2048 ? b : 2048);
+}
 
 template <class T>
 hipError_t run_backward(const Plan& p, const Tensors& t, const BwdTensors& gt, hipStream_t s) {
@@ -368,7 +417,8 @@ hipError_t run_backward(const Plan& p, const Tensors& t, const BwdTensors& gt, h
   float* part = reinterpret_cast<float*>(ws + L.part);
   const int64_t U = p.BH, N = p.N, rows = U * N;
   const int K = p.K, dr = p.DR, dv = p.DV, ks = L.ks_tok;
-  const int w3 = 2 * dr + 1, w1 = dv + 1;
+  const int w3 = 2 * dr + 1, w1 = dv + 1;           // logical widths
+  const int l3 = 2 * dr + 4, l1 = dv + 4;           // row strides (multiples of 4)
   hipError_t e;
 #define GMA_CHECK(x) do { e = (x); if (e != hipSuccess) return e; } while (0)
   // responsibilities of queries and keys
@@ -381,12 +431,12 @@ hipError_t run_backward(const Plan& p, const Tensors& t, const BwdTensors& gt, h
   tr.gamma = Gk;
   GMA_CHECK(launch_resp(p, tr, s));
   if (g_launch_hook) g_launch_hook("gma_bwd_prep", s, 1);
-  hipLaunchKernelGGL(gma_bwd_prep_kernel<T>, dim3(blocks(rows * w3, 256)), dim3(256), 0, s, t.q,
-                     dr, 1, rows, x3q);
-  hipLaunchKernelGGL(gma_bwd_prep_kernel<T>, dim3(blocks(rows * w3, 256)), dim3(256), 0, s, t.k,
-                     dr, 1, rows, x3k);
-  hipLaunchKernelGGL(gma_bwd_prep_kernel<T>, dim3(blocks(rows * w1, 256)), dim3(256), 0, s, t.v,
-                     dv, 0, rows, v1);
+  hipLaunchKernelGGL(gma_bwd_prep_kernel<T>, dim3(sblocks(rows, 2)), dim3(256), 0, s, t.q, dr, 1,
+                     rows, l3, x3q);
+  hipLaunchKernelGGL(gma_bwd_prep_kernel<T>, dim3(sblocks(rows, 2)), dim3(256), 0, s, t.k, dr, 1,
+                     rows, l3, x3k);
+  hipLaunchKernelGGL(gma_bwd_prep_kernel<T>, dim3(sblocks(rows, 2)), dim3(256), 0, s, t.v, dv, 0,
+                     rows, l1, v1);
   hipLaunchKernelGGL(gma_bwd_params_kernel, dim3(blocks(p.H * K * dr, 256)), dim3(256), 0, s,
                      t.mu, t.ls2, p.H * K * (int64_t)dr, dr, WW);
   GMA_CHECK(hipGetLastError());
@@ -394,37 +444,37 @@ hipError_t run_backward(const Plan& p, const Tensors& t, const BwdTensors& gt, h
 
   if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 1);
   // [V~ | Z] = Gk^T [V | 1]
-  GMA_CHECK(gemm(true, false, Gk, K, N * K, v1, w1, N * w1, 0, vtz, w1, (int64_t)K * w1, K, w1,
+  GMA_CHECK(gemm(true, false, Gk, K, N * K, v1, l1, N * l1, 0, vtz, l1, (int64_t)K * l1, K, w1,
                  (int)N, U, ks, part, s));
   // [n | d - eps] = Gq [V~ | Z]
-  GMA_CHECK(gemm(false, false, Gq, K, N * K, vtz, w1, (int64_t)K * w1, 0, nd, w1, N * w1,
+  GMA_CHECK(gemm(false, false, Gq, K, N * K, vtz, l1, (int64_t)K * l1, 0, nd, l1, N * l1,
                  (int)N, w1, K, U, 1, part, s));
   if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 0);
   if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 1);
-  hipLaunchKernelGGL(gma_bwd_ab_kernel<T>, dim3(blocks(rows, 4)), dim3(256), 0, s, nd, gt.dO, dv,
-                     t.eps, rows);
+  hipLaunchKernelGGL(gma_bwd_ab_kernel<T>, dim3(sblocks(rows, 4)), dim3(256), 0, s, nd, gt.dO, dv,
+                     l1, t.eps, rows);
   GMA_CHECK(hipGetLastError());
   if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 0);
   if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 1);
   // dGq = [a | b] [V~ | Z]^T
-  GMA_CHECK(gemm(false, true, nd, w1, N * w1, vtz, w1, (int64_t)K * w1, 0, dGq, K, N * K, (int)N,
+  GMA_CHECK(gemm(false, true, nd, l1, N * l1, vtz, l1, (int64_t)K * l1, 0, dGq, K, N * K, (int)N,
                  K, w1, U, 1, part, s));
   // [dV~ | dZ] = Gq^T [a | b]
-  GMA_CHECK(gemm(true, false, Gq, K, N * K, nd, w1, N * w1, 0, dvtz, w1, (int64_t)K * w1, K, w1,
+  GMA_CHECK(gemm(true, false, Gq, K, N * K, nd, l1, N * l1, 0, dvtz, l1, (int64_t)K * l1, K, w1,
                  (int)N, U, ks, part, s));
   // dV = Gk dV~
-  GMA_CHECK(gemm(false, false, Gk, K, N * K, dvtz, w1, (int64_t)K * w1, 0, dvf, dv, N * dv,
+  GMA_CHECK(gemm(false, false, Gk, K, N * K, dvtz, l1, (int64_t)K * l1, 0, dvf, dv, N * dv,
                  (int)N, dv, K, U, 1, part, s));
   // dGk = [V | 1] [dV~ | dZ]^T
-  GMA_CHECK(gemm(false, true, v1, w1, N * w1, dvtz, w1, (int64_t)K * w1, 0, dGk, K, N * K, (int)N,
+  GMA_CHECK(gemm(false, true, v1, l1, N * l1, dvtz, l1, (int64_t)K * l1, 0, dGk, K, N * K, (int)N,
                  K, w1, U, 1, part, s));
   if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 0);
   if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 1);
-  hipLaunchKernelGGL(gma_bwd_softmax_kernel, dim3(blocks(rows, 4)), dim3(256), 0, s, Gq, dGq, K,
+  hipLaunchKernelGGL(gma_bwd_softmax_kernel, dim3(sblocks(rows, 4)), dim3(256), 0, s, Gq, dGq, K,
                      rows);
-  hipLaunchKernelGGL(gma_bwd_softmax_kernel, dim3(blocks(rows, 4)), dim3(256), 0, s, Gk, dGk, K,
+  hipLaunchKernelGGL(gma_bwd_softmax_kernel, dim3(sblocks(rows, 4)), dim3(256), 0, s, Gk, dGk, K,
                      rows);
-  hipLaunchKernelGGL(gma_bwd_store_kernel<T>, dim3(blocks(rows * dv, 256)), dim3(256), 0, s, dvf,
+  hipLaunchKernelGGL(gma_bwd_store_kernel<T>, dim3(sblocks(rows * dv, 256)), dim3(256), 0, s, dvf,
                      rows * dv, gt.dV);
   GMA_CHECK(hipGetLastError());
   if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 0);
@@ -437,18 +487,18 @@ hipError_t run_backward(const Plan& p, const Tensors& t, const BwdTensors& gt, h
     GMA_CHECK(gemm(false, false, dS, K, N * K, WW, 2 * dr, (int64_t)K * 2 * dr, (int)p.H, P,
                    2 * dr, N * 2 * dr, (int)N, 2 * dr, K, U, 1, part, s));
     // [R1 | R2 | r0] = dS^T [x | x^2 | 1]
-    GMA_CHECK(gemm(true, false, dS, K, N * K, x3, w3, N * w3, 0, side ? Rk : Rq, w3,
-                   (int64_t)K * w3, K, w3, (int)N, U, ks, part, s));
+    GMA_CHECK(gemm(true, false, dS, K, N * K, x3, l3, N * l3, 0, side ? Rk : Rq, l3,
+                   (int64_t)K * l3, K, w3, (int)N, U, ks, part, s));
     if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 0);
     if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 1);
-    hipLaunchKernelGGL(gma_bwd_dx_kernel<T>, dim3(blocks(rows * dr, 256)), dim3(256), 0, s, x3,
-                       P, dr, rows, side ? gt.dK : gt.dQ);
+    hipLaunchKernelGGL(gma_bwd_dx_kernel<T>, dim3(sblocks(rows * dr, 256)), dim3(256), 0, s, x3,
+                       l3, P, dr, rows, side ? gt.dK : gt.dQ);
     GMA_CHECK(hipGetLastError());
     if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 0);
   }
   if (g_launch_hook) g_launch_hook("gma_bwd_params", s, 1);
   hipLaunchKernelGGL(gma_bwd_param_grad_kernel, dim3(blocks((int64_t)K * dr, 256), (unsigned)p.H),
-                     dim3(256), 0, s, Rq, Rk, p.B, (int)p.H, K, dr, t.mu, t.ls2, gt.dmu,
+                     dim3(256), 0, s, Rq, Rk, p.B, (int)p.H, K, dr, l3, t.mu, t.ls2, gt.dmu,
                      gt.dls2, gt.dlpi);
   if (g_launch_hook) g_launch_hook("gma_bwd_params", s, 0);
 #undef GMA_CHECK
