@@ -188,7 +188,7 @@ def decode_step(S, z, q, k, v, mu, log_sigma2, log_pi, eps: float) -> dict:
             "assign_q": rq["assign"][:, :, 0], "assign_k": rk["assign"][:, :, 0]}
 
 
-def backward(Q, K, V, mu, log_sigma2, log_pi, eps: float, dO) -> dict:
+def backward(Q, K, V, mu, log_sigma2, log_pi, eps: float, dO, causal: bool = False) -> dict:
     """Gradients of a scalar loss through the bidirectional forward, given
     dL/dO ("Gradient structure": the score gradient of Eq. 18 and its
     footnote, chained to the score's arguments by the chain rule of Eq. 17).
@@ -208,6 +208,11 @@ def backward(Q, K, V, mu, log_sigma2, log_pi, eps: float, dO) -> dict:
       dlog sigma^2_kd = sum_i ds_ik ((x_id - mu_kd)^2 w_kd - 1) / 2
       dlog pi_k = sum_i ds_ik
     where the parameter sums run over queries and keys of every batch.
+    Causal ("Causal GMA", Eq. 8b): V~ and Z become the inclusive prefix sums
+    S_i, z_i over j <= i, so dGq_ik = a_i . S_i,k + b_i z_i,k, and a key j
+    receives the suffix sums over the queries i >= j:
+    dV_j = sum_k Gk_jk sum_{i>=j} Gq_ik a_i,
+    dGk_jk = v_j . sum_{i>=j} Gq_ik a_i + sum_{i>=j} Gq_ik b_i.
     Shapes as forward; dO [B,H,N,d_v].  Returns float64 dQ, dK, dV, dmu,
     dlog_sigma2, dlog_pi.
     """
@@ -215,17 +220,33 @@ def backward(Q, K, V, mu, log_sigma2, log_pi, eps: float, dO) -> dict:
     mu, ls2, lpi = _f64(mu), _f64(log_sigma2), _f64(log_pi)
     Gq = responsibilities(Q, mu, ls2, lpi)["gamma"]                 # [B,H,N,K]
     Gk = responsibilities(K, mu, ls2, lpi)["gamma"]
-    Vt = np.einsum("bhnk,bhnd->bhkd", Gk, V)
-    Z = Gk.sum(axis=2)                                             # [B,H,K]
-    den = np.einsum("bhnk,bhk->bhn", Gq, Z) + eps
-    O = np.einsum("bhnk,bhkd->bhnd", Gq, Vt) / den[..., None]
-    a = dO / den[..., None]
-    bb = -(dO * O).sum(-1) / den
-    dGq = np.einsum("bhnd,bhkd->bhnk", a, Vt) + bb[..., None] * Z[:, :, None, :]
-    dVt = np.einsum("bhnk,bhnd->bhkd", Gq, a)
-    dZ = np.einsum("bhnk,bhn->bhk", Gq, bb)
-    dV = np.einsum("bhnk,bhkd->bhnd", Gk, dVt)
-    dGk = np.einsum("bhnd,bhkd->bhnk", V, dVt) + dZ[:, :, None, :]
+    if not causal:
+        Vt = np.einsum("bhnk,bhnd->bhkd", Gk, V)
+        Z = Gk.sum(axis=2)                                         # [B,H,K]
+        den = np.einsum("bhnk,bhk->bhn", Gq, Z) + eps
+        O = np.einsum("bhnk,bhkd->bhnd", Gq, Vt) / den[..., None]
+        a = dO / den[..., None]
+        bb = -(dO * O).sum(-1) / den
+        dGq = np.einsum("bhnd,bhkd->bhnk", a, Vt) + bb[..., None] * Z[:, :, None, :]
+        dVt = np.einsum("bhnk,bhnd->bhkd", Gq, a)
+        dZ = np.einsum("bhnk,bhn->bhk", Gq, bb)
+        dV = np.einsum("bhnk,bhkd->bhnd", Gk, dVt)
+        dGk = np.einsum("bhnd,bhkd->bhnk", V, dVt) + dZ[:, :, None, :]
+    else:
+        # prefix states per position (inclusive), [B,H,N,K,d_v] and [B,H,N,K]
+        S = np.cumsum(Gk[..., :, None] * V[..., None, :], axis=2)
+        z = np.cumsum(Gk, axis=2)
+        den = np.einsum("bhnk,bhnk->bhn", Gq, z) + eps
+        O = np.einsum("bhnk,bhnkd->bhnd", Gq, S) / den[..., None]
+        a = dO / den[..., None]
+        bb = -(dO * O).sum(-1) / den
+        dGq = np.einsum("bhnd,bhnkd->bhnk", a, S) + bb[..., None] * z
+        # suffix sums over the queries i >= j
+        T = Gq[..., :, None] * a[..., None, :]                     # [B,H,N,K,d_v]
+        G = np.flip(np.cumsum(np.flip(T, axis=2), axis=2), axis=2)
+        Hs = np.flip(np.cumsum(np.flip(Gq * bb[..., None], axis=2), axis=2), axis=2)
+        dV = np.einsum("bhnk,bhnkd->bhnd", Gk, G)
+        dGk = np.einsum("bhnd,bhnkd->bhnk", V, G) + Hs
     w = np.exp(-ls2)                                               # [H,K,d_r]
     out = {"dV": dV}
     dmu = np.zeros_like(mu)
