@@ -279,17 +279,17 @@ def main():
         u_hs = torch.empty((w.H, 3), dtype=torch.float32, device=dev)
 
     if args.backward:
-        if decode or w.d_model > 0 or w.causal:
-            sys.exit("--backward takes a bidirectional workload with routing vectors")
-        ws = api.alloc_workspace(binding.gma_backward_workspace_bytes(dims, 0), dev)
+        if decode or w.d_model > 0:
+            sys.exit("--backward takes a workload with routing vectors (not decode or layer)")
+        ws = api.alloc_workspace(binding.gma_backward_workspace_bytes(dims, int(w.causal)), dev)
         dO = torch.randn((w.B, w.H, w.N, w.d_v), device=dev).to(out_dtype)
         grads = [torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V),
                  torch.empty_like(mu), torch.empty_like(ls2), torch.empty_like(lpi)]
 
     def step():
         if args.backward:
-            binding.gma_backward(Q, K, V, mu, ls2, lpi, w.eps, 0, dO, dims, *grads, ws,
-                                 ws.numel())
+            binding.gma_backward(Q, K, V, mu, ls2, lpi, w.eps, int(w.causal), dO, dims, *grads,
+                                 ws, ws.numel())
             return
         if args.usage_stats:
             binding.gma_usage_stats(Q, mu, ls2, lpi, dims, 0.1, u_counts, u_f[0], u_f[1], u_hs,

@@ -161,19 +161,21 @@ def usage_stats(X: torch.Tensor, mu: torch.Tensor, log_sigma2: torch.Tensor,
 
 def backward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, mu: torch.Tensor,
              log_sigma2: torch.Tensor, log_pi: torch.Tensor, dO: torch.Tensor,
-             eps: float = 1e-6, workspace: Optional[torch.Tensor] = None, stream=None):
-    """Gradients of the bidirectional forward given dO: dict(dQ, dK, dV in the
-    input dtype; dmu, dlog_sigma2, dlog_pi fp32)."""
+             eps: float = 1e-6, causal: bool = False, workspace: Optional[torch.Tensor] = None,
+             stream=None):
+    """Gradients of the forward given dO: dict(dQ, dK, dV in the input dtype;
+    dmu, dlog_sigma2, dlog_pi fp32)."""
     Bb, H, N, d_r = Q.shape
     d_v = V.shape[-1]
     Kc = mu.shape[1]
     dims = B.make_dims(Bb, H, N, d_r, d_v, Kc, torch_dtype_code(Q))
-    need = B.gma_backward_workspace_bytes(dims, 0)
+    need = B.gma_backward_workspace_bytes(dims, int(causal))
     if workspace is None or workspace.numel() < need:
         workspace = alloc_workspace(need, Q.device)
     g = {"dQ": torch.empty_like(Q), "dK": torch.empty_like(K), "dV": torch.empty_like(V),
          "dmu": torch.empty_like(mu), "dlog_sigma2": torch.empty_like(log_sigma2),
          "dlog_pi": torch.empty_like(log_pi)}
-    B.gma_backward(Q, K, V, mu, log_sigma2, log_pi, eps, 0, dO, dims, g["dQ"], g["dK"], g["dV"],
-                   g["dmu"], g["dlog_sigma2"], g["dlog_pi"], workspace, workspace.numel(), stream)
+    B.gma_backward(Q, K, V, mu, log_sigma2, log_pi, eps, int(causal), dO, dims, g["dQ"], g["dK"],
+                   g["dV"], g["dmu"], g["dlog_sigma2"], g["dlog_pi"], workspace,
+                   workspace.numel(), stream)
     return g

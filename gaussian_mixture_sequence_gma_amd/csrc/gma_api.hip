@@ -448,12 +448,17 @@ int gma_usage_stats(const void* X_r, const float* mu, const float* log_sigma2,
   return finish_launch(e, "usage statistics launch");
 }
 
+// The backward's plan: the bidirectional plan at N, or (causal) at N rounded
+// up to the 64-token chunk.
 static int backward_plan(const gma_dims* d, int causal, Plan& p) {
-  if (causal) return fail(GMA_ERR_UNSUPPORTED, "the causal backward is not available");
-  int st = make_plan(d, 0, false, p);
+  gma_dims dp = *d;
+  if (causal) dp.N = (d->N + 63) / 64 * 64;
+  int st = make_plan(&dp, 0, false, p);
   if (st != GMA_OK) return st;
-  if (d->N > (int64_t)65535 * 64)
+  if (dp.N > (int64_t)65535 * 64)
     return fail(GMA_ERR_UNSUPPORTED, "the backward takes N up to 65535 * 64");
+  if (causal && p.BH * (dp.N / 64) > 65535)
+    return fail(GMA_ERR_UNSUPPORTED, "the causal backward takes B*H*ceil(N/64) up to 65535");
   return GMA_OK;
 }
 
@@ -465,7 +470,7 @@ int gma_backward_workspace_bytes(const gma_dims* d, int causal, size_t* bytes) {
   Plan p;
   st = backward_plan(d, causal, p);
   if (st != GMA_OK) return st;
-  *bytes = backward_workspace_bytes(p);
+  *bytes = backward_workspace_bytes(p, causal != 0, d->N);
   return GMA_OK;
 }
 
@@ -488,7 +493,7 @@ int gma_backward(const void* Q_X, const void* K_X, const void* V_X, const float*
   Plan p;
   st = backward_plan(d, causal, p);
   if (st != GMA_OK) return st;
-  if (workspace_bytes < backward_workspace_bytes(p))
+  if (workspace_bytes < backward_workspace_bytes(p, causal != 0, d->N))
     return fail(GMA_ERR_WORKSPACE, "workspace too small");
   Tensors t;
   t.q = Q_X;
@@ -507,7 +512,8 @@ int gma_backward(const void* Q_X, const void* K_X, const void* V_X, const float*
   g.dmu = dmu;
   g.dls2 = dlog_sigma2;
   g.dlpi = dlog_pi;
-  return finish_launch(launch_backward(p, t, g, static_cast<hipStream_t>(stream)),
+  return finish_launch(launch_backward(p, t, g, causal != 0, d->N,
+                                       static_cast<hipStream_t>(stream)),
                        "backward launch");
 }
 

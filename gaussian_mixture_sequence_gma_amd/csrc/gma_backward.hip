@@ -20,6 +20,12 @@
 // batched fp32 products (MFMA 16x16x4 f32, split over the token dimension
 // where the product contracts it) and row-wise elementwise kernels.  The
 // responsibilities come from the forward's responsibility kernel.
+//
+// Causal ("Causal GMA", Eq. 8b): the same chain per 64-token chunk, with the
+// prefix states of the earlier chunks ([V~ | Z] totals per chunk, exclusive
+// prefix) for the queries, the suffix states of the later chunks for the keys
+// (Gq_c^T [a | b]_c, exclusive suffix), and inside a chunk the masked 64 x 64
+// products Gq_c Gk_c^T and [a | b]_c [V | 1]_c^T.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -41,6 +47,7 @@ struct GemmArgs {
   int bmod;          // > 0: B of unit u is B + (u % bmod) * sB
   int ksplit;
   int vec;           // bit 0: A rows 16-byte aligned; bit 1: B rows
+  int accum;         // add to C instead of overwriting it (ksplit == 1 only)
 };
 
 constexpr int kGT = 64;                 // output tile
@@ -167,7 +174,10 @@ __global__ void __launch_bounds__(256) gma_bgemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = m0 + 32 * wr + 16 * i + 4 * gq + e, n = n0 + 32 * wc + 16 * j + r;
-        if (m < g.M && n < g.N) C[(size_t)m * ldc + n] = acc[i][j][e];
+        if (m < g.M && n < g.N) {
+          float* c = C + (size_t)m * ldc + n;
+          *c = g.accum ? *c + acc[i][j][e] : acc[i][j][e];
+        }
       }
 }
 
@@ -272,24 +282,77 @@ __global__ void __launch_bounds__(256) gma_bwd_softmax_kernel(const float* __res
 }
 
 // dX = -x P1 + P2 from X3 = [x | x^2 | 1] and P = [P1 | P2].
+// Rows are padded to Np per unit (Np = N without padding); row r of unit u
+// goes to row u * N + r of the caller's tensor when r < N.
 template <class T>
 __global__ void __launch_bounds__(256) gma_bwd_dx_kernel(const float* __restrict__ x3, int ld,
                                                          const float* __restrict__ P, int d,
-                                                         int64_t rows, void* __restrict__ dx) {
+                                                         int64_t rows, int64_t Np, int64_t N,
+                                                         void* __restrict__ dx) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < rows * d;
        i += (int64_t)gridDim.x * 256) {
     const int64_t row = i / d;
     const int c = (int)(i - row * d);
+    const int64_t u = row / Np, r = row - u * Np;
+    if (r >= N) continue;
     const float* p = P + (size_t)row * 2 * d;
-    stx<T>(dx, i, -x3[(size_t)row * ld + c] * p[c] + p[d + c]);
+    stx<T>(dx, (size_t)(u * N + r) * d + c, -x3[(size_t)row * ld + c] * p[c] + p[d + c]);
   }
 }
 
 template <class T>
-__global__ void __launch_bounds__(256) gma_bwd_store_kernel(const float* __restrict__ src,
-                                                            int64_t n, void* __restrict__ dst) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    stx<T>(dst, i, src[i]);
+__global__ void __launch_bounds__(256) gma_bwd_store_kernel(const float* __restrict__ src, int d,
+                                                            int64_t rows, int64_t Np, int64_t N,
+                                                            void* __restrict__ dst) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < rows * d;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t row = i / d;
+    const int c = (int)(i - row * d);
+    const int64_t u = row / Np, r = row - u * Np;
+    if (r < N) stx<T>(dst, (size_t)(u * N + r) * d + c, src[i]);
+  }
+}
+
+// [U][N][d] -> [U][Np][d], rows N..Np-1 zero.
+template <class T>
+__global__ void __launch_bounds__(256) gma_bwd_pad_kernel(const void* __restrict__ src, int d,
+                                                          int64_t U, int64_t Np, int64_t N,
+                                                          void* __restrict__ dst) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < U * Np * d;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t row = i / d;
+    const int c = (int)(i - row * d);
+    const int64_t u = row / Np, r = row - u * Np;
+    static_cast<T*>(dst)[i] =
+        r < N ? static_cast<const T*>(src)[(size_t)(u * N + r) * d + c] : (T)0.f;
+  }
+}
+
+// Exclusive scan over the nc chunk records of each unit (reverse: over the
+// later chunks), in place; records of n floats.
+__global__ void __launch_bounds__(256) gma_bwd_chunk_scan_kernel(float* __restrict__ x, int nc,
+                                                                 int n, int reverse) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  float* base = x + (size_t)blockIdx.y * nc * n + e;
+  float run = 0.f;
+  for (int i = 0; i < nc; ++i) {
+    const int c = reverse ? nc - 1 - i : i;
+    const float v = base[(size_t)c * n];
+    base[(size_t)c * n] = run;
+    run += v;
+  }
+}
+
+// Chunk-local masks on [Z][64][64]: lower keeps column <= row (key j <= query
+// i), upper keeps column >= row (query i >= key j).
+__global__ void __launch_bounds__(256) gma_bwd_mask_kernel(float* __restrict__ m, int64_t n,
+                                                           int upper) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * 256) {
+    const int r = (int)((i >> 6) & 63), c = (int)(i & 63);
+    if (upper ? c < r : c > r) m[i] = 0.f;
+  }
 }
 
 // Per head: sum R = [R1 | R2 | r0] over batches and over queries and keys,
@@ -326,55 +389,69 @@ __global__ void __launch_bounds__(256) gma_bwd_param_grad_kernel(
 namespace {
 
 size_t r256(size_t x) { return (x + 255) & ~(size_t)255; }
+constexpr int kChunk = 64;                  // causal chunk (one product tile)
 
+// The backward runs on rows padded to Np per unit: Np = N (bidirectional) or
+// N rounded up to the chunk (causal; zero rows at the end of a sequence affect
+// no earlier position, and their dO is zero).  pp is the plan at Np.
 struct BwdLayout {
-  size_t x3q, x3k, v1, nd, gq, gk, dgq, dgk, p, dv, vtz, dvtz, rq, rk, ww, part, total;
+  int64_t Np = 0, nc = 0;
+  size_t pads, x3q, x3k, v1, nd, gq, gk, dgq, dgk, p, dv, vtz, dvtz, rq, rk, ww, part;
+  size_t pc, qc, total;
   int ks_tok;        // split of the token contractions
 };
 
-BwdLayout bwd_layout(const Plan& p) {
+BwdLayout bwd_layout(const Plan& pp, bool causal, int64_t N) {
   BwdLayout L{};
-  const size_t U = (size_t)p.BH, N = (size_t)p.N, K = (size_t)p.K;
-  const size_t dr = p.DR, dv = p.DV;
-  // token contractions: M, N <= 2 d_r + 1 <= 257, so at most 25 output tiles
-  // per unit; split the tokens so that about 1024 workgroups run
+  L.Np = pp.N;
+  L.nc = causal ? pp.N / kChunk : 0;
+  const size_t U = (size_t)pp.BH, Np = (size_t)pp.N, K = (size_t)pp.K;
+  const size_t dr = pp.DR, dv = pp.DV, es = pp.bf ? 2 : 4;
   int ks = (int)((1024 + U - 1) / U);
-  const int maxk = (int)((p.N + 255) / 256);      // at least 256 tokens per split
+  const int maxk = (int)((pp.N + 255) / 256);      // at least 256 tokens per split
   if (ks > maxk) ks = maxk;
   if (ks > 32) ks = 32;
-  if ((int64_t)ks * p.BH > 65535) ks = (int)(65535 / p.BH);
+  if ((int64_t)ks * pp.BH > 65535) ks = (int)(65535 / pp.BH);
   if (ks < 1) ks = 1;
   L.ks_tok = ks;
-  size_t off = r256(p.total);
+  size_t off = r256(pp.total);
   auto take = [&](size_t bytes) { const size_t o = off; off += r256(bytes); return o; };
   const size_t w3p = 2 * dr + 4, w1p = dv + 4;      // padded row strides
-  L.x3q = take(U * N * w3p * 4);
-  L.x3k = take(U * N * w3p * 4);
-  L.v1 = take(U * N * w1p * 4);
-  L.nd = take(U * N * w1p * 4);
-  L.gq = take(U * N * K * 4);
-  L.gk = take(U * N * K * 4);
-  L.dgq = take(U * N * K * 4);
-  L.dgk = take(U * N * K * 4);
-  L.p = take(U * N * 2 * dr * 4);
-  L.dv = take(U * N * dv * 4);
-  L.vtz = take(U * K * w1p * 4);
-  L.dvtz = take(U * K * w1p * 4);
+  // causal: padded copies of Q_X, K_X, V_X, dO in the input type
+  L.pads = take(causal && (int64_t)Np != N ? U * Np * (2 * dr + 2 * dv) * es : 0);
+  L.x3q = take(U * Np * w3p * 4);
+  L.x3k = take(U * Np * w3p * 4);
+  L.v1 = take(U * Np * w1p * 4);
+  L.nd = take(U * Np * w1p * 4);
+  L.gq = take(U * Np * K * 4);
+  L.gk = take(U * Np * K * 4);
+  L.dgq = take(U * Np * K * 4);
+  L.dgk = take(U * Np * K * 4);
+  L.p = take(U * Np * 2 * dr * 4);
+  L.dv = take(U * Np * dv * 4);
+  // [V~ | Z] and [dV~ | dZ] per unit, or per chunk (causal: the carried prefix
+  // and suffix states)
+  const size_t recs = causal ? U * (size_t)L.nc : U;
+  L.vtz = take(recs * K * w1p * 4);
+  L.dvtz = take(recs * K * w1p * 4);
   L.rq = take(U * K * w3p * 4);
   L.rk = take(U * K * w3p * 4);
-  L.ww = take((size_t)p.H * K * 2 * dr * 4);
+  L.ww = take((size_t)pp.H * K * 2 * dr * 4);
   const size_t wmax = (2 * dr + 1) > (dv + 1) ? (2 * dr + 1) : (dv + 1);
   L.part = take(U * (size_t)ks * K * wmax * 4);
+  L.pc = take(causal ? recs * kChunk * kChunk * 4 : 0);
+  L.qc = take(causal ? recs * kChunk * kChunk * 4 : 0);
   L.total = off;
   return L;
 }
 
 hipError_t gemm(bool ta, bool tb, const float* A, int lda, int64_t sA, const float* B, int ldb,
                 int64_t sB, int bmod, float* C, int ldc, int64_t sC, int M, int N, int K,
-                int64_t U, int ksplit, float* part, hipStream_t s) {
+                int64_t U, int ksplit, float* part, hipStream_t s, bool accum = false) {
   const int vec = ((lda % 4 == 0 && sA % 4 == 0 && ((uintptr_t)A & 15) == 0) ? 1 : 0) |
                   ((ldb % 4 == 0 && sB % 4 == 0 && ((uintptr_t)B & 15) == 0) ? 2 : 0);
-  GemmArgs g{A, B, ksplit > 1 ? part : C, M, N, K, lda, ldb, ldc, sA, sB, sC, bmod, ksplit, vec};
+  GemmArgs g{A, B, ksplit > 1 ? part : C, M, N, K, lda, ldb, ldc, sA, sB, sC, bmod, ksplit, vec,
+             accum ? 1 : 0};
   const dim3 grid((unsigned)((N + kGT - 1) / kGT), (unsigned)((M + kGT - 1) / kGT),
                   (unsigned)(U * ksplit));
   if (!ta && !tb) hipLaunchKernelGGL((gma_bgemm_kernel<false, false>), grid, dim3(256), 0, s, g);
@@ -396,8 +473,10 @@ unsigned sblocks(int64_t n, int per) {
 }
 
 template <class T>
-hipError_t run_backward(const Plan& p, const Tensors& t, const BwdTensors& gt, hipStream_t s) {
-  const BwdLayout L = bwd_layout(p);
+hipError_t run_backward(const Plan& pp, const Tensors& t0, const BwdTensors& gt, bool causal,
+                        int64_t N0, hipStream_t s) {
+  const BwdLayout L = bwd_layout(pp, causal, N0);
+  Tensors t = t0;
   char* ws = t.ws;
   float* x3q = reinterpret_cast<float*>(ws + L.x3q);
   float* x3k = reinterpret_cast<float*>(ws + L.x3k);
@@ -415,21 +494,46 @@ hipError_t run_backward(const Plan& p, const Tensors& t, const BwdTensors& gt, h
   float* Rk = reinterpret_cast<float*>(ws + L.rk);
   float* WW = reinterpret_cast<float*>(ws + L.ww);
   float* part = reinterpret_cast<float*>(ws + L.part);
-  const int64_t U = p.BH, N = p.N, rows = U * N;
-  const int K = p.K, dr = p.DR, dv = p.DV, ks = L.ks_tok;
+  float* pc = reinterpret_cast<float*>(ws + L.pc);
+  float* qc = reinterpret_cast<float*>(ws + L.qc);
+  const int64_t U = pp.BH, Np = L.Np, rows = U * Np;
+  const int K = pp.K, dr = pp.DR, dv = pp.DV, ks = L.ks_tok;
   const int w3 = 2 * dr + 1, w1 = dv + 1;           // logical widths
   const int l3 = 2 * dr + 4, l1 = dv + 4;           // row strides (multiples of 4)
+  const void* dO = gt.dO;
   hipError_t e;
 #define GMA_CHECK(x) do { e = (x); if (e != hipSuccess) return e; } while (0)
+  if (L.pads && Np != N0) {
+    // causal with a ragged last chunk: zero-padded copies of the inputs
+    T* pq = reinterpret_cast<T*>(ws + L.pads);
+    T* pk = pq + (size_t)rows * dr;
+    T* pv = pk + (size_t)rows * dr;
+    T* pd = pv + (size_t)rows * dv;
+    if (g_launch_hook) g_launch_hook("gma_bwd_prep", s, 1);
+    hipLaunchKernelGGL(gma_bwd_pad_kernel<T>, dim3(sblocks(rows * dr, 256)), dim3(256), 0, s, t.q,
+                       dr, U, Np, N0, (void*)pq);
+    hipLaunchKernelGGL(gma_bwd_pad_kernel<T>, dim3(sblocks(rows * dr, 256)), dim3(256), 0, s, t.k,
+                       dr, U, Np, N0, (void*)pk);
+    hipLaunchKernelGGL(gma_bwd_pad_kernel<T>, dim3(sblocks(rows * dv, 256)), dim3(256), 0, s, t.v,
+                       dv, U, Np, N0, (void*)pv);
+    hipLaunchKernelGGL(gma_bwd_pad_kernel<T>, dim3(sblocks(rows * dv, 256)), dim3(256), 0, s, dO,
+                       dv, U, Np, N0, (void*)pd);
+    GMA_CHECK(hipGetLastError());
+    if (g_launch_hook) g_launch_hook("gma_bwd_prep", s, 0);
+    t.q = pq;
+    t.k = pk;
+    t.v = pv;
+    dO = pd;
+  }
   // responsibilities of queries and keys
   Tensors tr = t;
   tr.assign_q = nullptr;
   tr.q = t.q;
   tr.gamma = Gq;
-  GMA_CHECK(launch_resp(p, tr, s));
+  GMA_CHECK(launch_resp(pp, tr, s));
   tr.q = t.k;
   tr.gamma = Gk;
-  GMA_CHECK(launch_resp(p, tr, s));
+  GMA_CHECK(launch_resp(pp, tr, s));
   if (g_launch_hook) g_launch_hook("gma_bwd_prep", s, 1);
   hipLaunchKernelGGL(gma_bwd_prep_kernel<T>, dim3(sblocks(rows, 2)), dim3(256), 0, s, t.q, dr, 1,
                      rows, l3, x3q);
@@ -437,37 +541,95 @@ hipError_t run_backward(const Plan& p, const Tensors& t, const BwdTensors& gt, h
                      rows, l3, x3k);
   hipLaunchKernelGGL(gma_bwd_prep_kernel<T>, dim3(sblocks(rows, 2)), dim3(256), 0, s, t.v, dv, 0,
                      rows, l1, v1);
-  hipLaunchKernelGGL(gma_bwd_params_kernel, dim3(blocks(p.H * K * dr, 256)), dim3(256), 0, s,
-                     t.mu, t.ls2, p.H * K * (int64_t)dr, dr, WW);
+  hipLaunchKernelGGL(gma_bwd_params_kernel, dim3(blocks(pp.H * K * dr, 256)), dim3(256), 0, s,
+                     t.mu, t.ls2, pp.H * K * (int64_t)dr, dr, WW);
   GMA_CHECK(hipGetLastError());
   if (g_launch_hook) g_launch_hook("gma_bwd_prep", s, 0);
 
-  if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 1);
-  // [V~ | Z] = Gk^T [V | 1]
-  GMA_CHECK(gemm(true, false, Gk, K, N * K, v1, l1, N * l1, 0, vtz, l1, (int64_t)K * l1, K, w1,
-                 (int)N, U, ks, part, s));
-  // [n | d - eps] = Gq [V~ | Z]
-  GMA_CHECK(gemm(false, false, Gq, K, N * K, vtz, l1, (int64_t)K * l1, 0, nd, l1, N * l1,
-                 (int)N, w1, K, U, 1, part, s));
-  if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 0);
+  const int64_t Z = causal ? U * L.nc : U;      // product batch: units, or chunks
+  const int C = kChunk;
+  if (!causal) {
+    if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 1);
+    // [V~ | Z] = Gk^T [V | 1]
+    GMA_CHECK(gemm(true, false, Gk, K, Np * K, v1, l1, Np * l1, 0, vtz, l1, (int64_t)K * l1, K,
+                   w1, (int)Np, U, ks, part, s));
+    // [n | d - eps] = Gq [V~ | Z]
+    GMA_CHECK(gemm(false, false, Gq, K, Np * K, vtz, l1, (int64_t)K * l1, 0, nd, l1, Np * l1,
+                   (int)Np, w1, K, U, 1, part, s));
+    if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 0);
+  } else {
+    if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 1);
+    // per chunk: [V~ | Z] totals, then their exclusive prefix over chunks
+    GMA_CHECK(gemm(true, false, Gk, K, (int64_t)C * K, v1, l1, (int64_t)C * l1, 0, vtz, l1,
+                   (int64_t)K * l1, K, w1, C, Z, 1, part, s));
+    hipLaunchKernelGGL(gma_bwd_chunk_scan_kernel, dim3(blocks((int64_t)K * l1, 256), (unsigned)U),
+                       dim3(256), 0, s, vtz, (int)L.nc, K * l1, 0);
+    GMA_CHECK(hipGetLastError());
+    // in-chunk affinity Gq_c Gk_c^T, keys j <= query i
+    GMA_CHECK(gemm(false, true, Gq, K, (int64_t)C * K, Gk, K, (int64_t)C * K, 0, pc, C,
+                   (int64_t)C * C, C, C, K, Z, 1, part, s));
+    hipLaunchKernelGGL(gma_bwd_mask_kernel, dim3(sblocks(Z * C * C, 256)), dim3(256), 0, s, pc,
+                       Z * C * C, 0);
+    GMA_CHECK(hipGetLastError());
+    // [n | d - eps] = Gq_c [V~ | Z]_prefix + mask(Gq_c Gk_c^T) [V | 1]_c
+    GMA_CHECK(gemm(false, false, Gq, K, (int64_t)C * K, vtz, l1, (int64_t)K * l1, 0, nd, l1,
+                   (int64_t)C * l1, C, w1, K, Z, 1, part, s));
+    GMA_CHECK(gemm(false, false, pc, C, (int64_t)C * C, v1, l1, (int64_t)C * l1, 0, nd, l1,
+                   (int64_t)C * l1, C, w1, C, Z, 1, part, s, true));
+    if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 0);
+  }
   if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 1);
-  hipLaunchKernelGGL(gma_bwd_ab_kernel<T>, dim3(sblocks(rows, 4)), dim3(256), 0, s, nd, gt.dO, dv,
+  hipLaunchKernelGGL(gma_bwd_ab_kernel<T>, dim3(sblocks(rows, 4)), dim3(256), 0, s, nd, dO, dv,
                      l1, t.eps, rows);
   GMA_CHECK(hipGetLastError());
   if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 0);
   if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 1);
-  // dGq = [a | b] [V~ | Z]^T
-  GMA_CHECK(gemm(false, true, nd, l1, N * l1, vtz, l1, (int64_t)K * l1, 0, dGq, K, N * K, (int)N,
-                 K, w1, U, 1, part, s));
-  // [dV~ | dZ] = Gq^T [a | b]
-  GMA_CHECK(gemm(true, false, Gq, K, N * K, nd, l1, N * l1, 0, dvtz, l1, (int64_t)K * l1, K, w1,
-                 (int)N, U, ks, part, s));
-  // dV = Gk dV~
-  GMA_CHECK(gemm(false, false, Gk, K, N * K, dvtz, l1, (int64_t)K * l1, 0, dvf, dv, N * dv,
-                 (int)N, dv, K, U, 1, part, s));
-  // dGk = [V | 1] [dV~ | dZ]^T
-  GMA_CHECK(gemm(false, true, v1, l1, N * l1, dvtz, l1, (int64_t)K * l1, 0, dGk, K, N * K, (int)N,
-                 K, w1, U, 1, part, s));
+  if (!causal) {
+    // dGq = [a | b] [V~ | Z]^T
+    GMA_CHECK(gemm(false, true, nd, l1, Np * l1, vtz, l1, (int64_t)K * l1, 0, dGq, K, Np * K,
+                   (int)Np, K, w1, U, 1, part, s));
+    // [dV~ | dZ] = Gq^T [a | b]
+    GMA_CHECK(gemm(true, false, Gq, K, Np * K, nd, l1, Np * l1, 0, dvtz, l1, (int64_t)K * l1, K,
+                   w1, (int)Np, U, ks, part, s));
+    // dV = Gk dV~
+    GMA_CHECK(gemm(false, false, Gk, K, Np * K, dvtz, l1, (int64_t)K * l1, 0, dvf, dv, Np * dv,
+                   (int)Np, dv, K, U, 1, part, s));
+    // dGk = [V | 1] [dV~ | dZ]^T
+    GMA_CHECK(gemm(false, true, v1, l1, Np * l1, dvtz, l1, (int64_t)K * l1, 0, dGk, K, Np * K,
+                   (int)Np, K, w1, U, 1, part, s));
+  } else {
+    // dGq_c = [a | b]_c [V~ | Z]_prefix^T + mask([a | b]_c [V | 1]_c^T) Gk_c
+    GMA_CHECK(gemm(false, true, nd, l1, (int64_t)C * l1, vtz, l1, (int64_t)K * l1, 0, dGq, K,
+                   (int64_t)C * K, C, K, w1, Z, 1, part, s));
+    GMA_CHECK(gemm(false, true, nd, l1, (int64_t)C * l1, v1, l1, (int64_t)C * l1, 0, qc, C,
+                   (int64_t)C * C, C, C, w1, Z, 1, part, s));
+    hipLaunchKernelGGL(gma_bwd_mask_kernel, dim3(sblocks(Z * C * C, 256)), dim3(256), 0, s, qc,
+                       Z * C * C, 0);
+    GMA_CHECK(hipGetLastError());
+    GMA_CHECK(gemm(false, false, qc, C, (int64_t)C * C, Gk, K, (int64_t)C * K, 0, dGq, K,
+                   (int64_t)C * K, C, K, C, Z, 1, part, s, true));
+    // per chunk: Gq_c^T [a | b]_c, then the exclusive suffix over later chunks
+    GMA_CHECK(gemm(true, false, Gq, K, (int64_t)C * K, nd, l1, (int64_t)C * l1, 0, dvtz, l1,
+                   (int64_t)K * l1, K, w1, C, Z, 1, part, s));
+    hipLaunchKernelGGL(gma_bwd_chunk_scan_kernel, dim3(blocks((int64_t)K * l1, 256), (unsigned)U),
+                       dim3(256), 0, s, dvtz, (int)L.nc, K * l1, 1);
+    GMA_CHECK(hipGetLastError());
+    // dGk_c = [V | 1]_c [dV~ | dZ]_suffix^T + mask([V | 1]_c [a | b]_c^T) Gq_c
+    GMA_CHECK(gemm(false, true, v1, l1, (int64_t)C * l1, dvtz, l1, (int64_t)K * l1, 0, dGk, K,
+                   (int64_t)C * K, C, K, w1, Z, 1, part, s));
+    GMA_CHECK(gemm(false, true, v1, l1, (int64_t)C * l1, nd, l1, (int64_t)C * l1, 0, qc, C,
+                   (int64_t)C * C, C, C, w1, Z, 1, part, s));
+    hipLaunchKernelGGL(gma_bwd_mask_kernel, dim3(sblocks(Z * C * C, 256)), dim3(256), 0, s, qc,
+                       Z * C * C, 1);
+    GMA_CHECK(hipGetLastError());
+    GMA_CHECK(gemm(false, false, qc, C, (int64_t)C * C, Gq, K, (int64_t)C * K, 0, dGk, K,
+                   (int64_t)C * K, C, K, C, Z, 1, part, s, true));
+    // dV_c = Gk_c dV~_suffix + mask(Gq_c Gk_c^T)^T a_c
+    GMA_CHECK(gemm(false, false, Gk, K, (int64_t)C * K, dvtz, l1, (int64_t)K * l1, 0, dvf, dv,
+                   (int64_t)C * dv, C, dv, K, Z, 1, part, s));
+    GMA_CHECK(gemm(true, false, pc, C, (int64_t)C * C, nd, l1, (int64_t)C * l1, 0, dvf, dv,
+                   (int64_t)C * dv, C, dv, C, Z, 1, part, s, true));
+  }
   if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 0);
   if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 1);
   hipLaunchKernelGGL(gma_bwd_softmax_kernel, dim3(sblocks(rows, 4)), dim3(256), 0, s, Gq, dGq, K,
@@ -475,7 +637,7 @@ hipError_t run_backward(const Plan& p, const Tensors& t, const BwdTensors& gt, h
   hipLaunchKernelGGL(gma_bwd_softmax_kernel, dim3(sblocks(rows, 4)), dim3(256), 0, s, Gk, dGk, K,
                      rows);
   hipLaunchKernelGGL(gma_bwd_store_kernel<T>, dim3(sblocks(rows * dv, 256)), dim3(256), 0, s, dvf,
-                     rows * dv, gt.dV);
+                     dv, rows, Np, N0, gt.dV);
   GMA_CHECK(hipGetLastError());
   if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 0);
 
@@ -484,21 +646,21 @@ hipError_t run_backward(const Plan& p, const Tensors& t, const BwdTensors& gt, h
     float* x3 = side ? x3k : x3q;
     if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 1);
     // [P1 | P2] = dS [w | mu w] (the head's table)
-    GMA_CHECK(gemm(false, false, dS, K, N * K, WW, 2 * dr, (int64_t)K * 2 * dr, (int)p.H, P,
-                   2 * dr, N * 2 * dr, (int)N, 2 * dr, K, U, 1, part, s));
+    GMA_CHECK(gemm(false, false, dS, K, Np * K, WW, 2 * dr, (int64_t)K * 2 * dr, (int)pp.H, P,
+                   2 * dr, Np * 2 * dr, (int)Np, 2 * dr, K, U, 1, part, s));
     // [R1 | R2 | r0] = dS^T [x | x^2 | 1]
-    GMA_CHECK(gemm(true, false, dS, K, N * K, x3, l3, N * l3, 0, side ? Rk : Rq, l3,
-                   (int64_t)K * l3, K, w3, (int)N, U, ks, part, s));
+    GMA_CHECK(gemm(true, false, dS, K, Np * K, x3, l3, Np * l3, 0, side ? Rk : Rq, l3,
+                   (int64_t)K * l3, K, w3, (int)Np, U, ks, part, s));
     if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 0);
     if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 1);
     hipLaunchKernelGGL(gma_bwd_dx_kernel<T>, dim3(sblocks(rows * dr, 256)), dim3(256), 0, s, x3,
-                       l3, P, dr, rows, side ? gt.dK : gt.dQ);
+                       l3, P, dr, rows, Np, N0, side ? gt.dK : gt.dQ);
     GMA_CHECK(hipGetLastError());
     if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 0);
   }
   if (g_launch_hook) g_launch_hook("gma_bwd_params", s, 1);
-  hipLaunchKernelGGL(gma_bwd_param_grad_kernel, dim3(blocks((int64_t)K * dr, 256), (unsigned)p.H),
-                     dim3(256), 0, s, Rq, Rk, p.B, (int)p.H, K, dr, l3, t.mu, t.ls2, gt.dmu,
+  hipLaunchKernelGGL(gma_bwd_param_grad_kernel, dim3(blocks((int64_t)K * dr, 256), (unsigned)pp.H),
+                     dim3(256), 0, s, Rq, Rk, pp.B, (int)pp.H, K, dr, l3, t.mu, t.ls2, gt.dmu,
                      gt.dls2, gt.dlpi);
   if (g_launch_hook) g_launch_hook("gma_bwd_params", s, 0);
 #undef GMA_CHECK
@@ -507,13 +669,16 @@ hipError_t run_backward(const Plan& p, const Tensors& t, const BwdTensors& gt, h
 
 }  // namespace
 
-size_t backward_workspace_bytes(const Plan& p) { return bwd_layout(p).total; }
+size_t backward_workspace_bytes(const Plan& pp, bool causal, int64_t N) {
+  return bwd_layout(pp, causal, N).total;
+}
 
-hipError_t launch_backward(const Plan& p, const Tensors& t, const BwdTensors& gt,
-                           hipStream_t s) {
-  const hipError_t e = launch_prologue(p, t, s);
+hipError_t launch_backward(const Plan& pp, const Tensors& t, const BwdTensors& gt, bool causal,
+                           int64_t N, hipStream_t s) {
+  const hipError_t e = launch_prologue(pp, t, s);
   if (e != hipSuccess) return e;
-  return p.out_bf ? run_backward<bf16>(p, t, gt, s) : run_backward<float>(p, t, gt, s);
+  return pp.out_bf ? run_backward<bf16>(pp, t, gt, causal, N, s)
+                   : run_backward<float>(pp, t, gt, causal, N, s);
 }
 
 }  // namespace gma

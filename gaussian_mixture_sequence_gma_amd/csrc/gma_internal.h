@@ -79,7 +79,7 @@ hipError_t launch_usage(const Plan& p, const Tensors& t, int32_t* counts, float*
 // state_v [BH,K,d_v], state_z [BH,K] (fp32, updated in place).
 hipError_t launch_decode(const Plan& p, const Tensors& t, float* state_v, float* state_z,
                          hipStream_t s);
-// Backward of the bidirectional forward: dO in, gradients out (dQ, dK, dV of
+// Backward of the forward (bidirectional or causal): dO in, gradients out (dQ, dK, dV of
 // the input dtype; parameter gradients fp32, written).
 struct BwdTensors {
   const void* dO = nullptr;
@@ -90,8 +90,11 @@ struct BwdTensors {
   float* dls2 = nullptr;
   float* dlpi = nullptr;
 };
-size_t backward_workspace_bytes(const Plan& p);
-hipError_t launch_backward(const Plan& p, const Tensors& t, const BwdTensors& gt, hipStream_t s);
+// pp: the plan at the padded length (N rounded up to 64 when causal); N: the
+// caller's sequence length.
+size_t backward_workspace_bytes(const Plan& pp, bool causal, int64_t N);
+hipError_t launch_backward(const Plan& pp, const Tensors& t, const BwdTensors& gt, bool causal,
+                           int64_t N, hipStream_t s);
 // log sigma^2 = log(softplus(omega) + eps_sigma) over [H,K,d_r] and
 // log pi = alpha - logsumexp(alpha) over [H,K].
 hipError_t launch_reparam(const float* omega, const float* alpha, float eps_sigma, int64_t H,

@@ -135,16 +135,15 @@ int gma_responsibilities(const void* X_r, const float* mu, const float* log_sigm
                          int32_t* assign, void* workspace, size_t workspace_bytes,
                          void* stream);
 
-/* Bytes of device workspace gma_backward needs (causal must be 0). */
+/* Bytes of device workspace gma_backward needs for this shape and variant. */
 int gma_backward_workspace_bytes(const gma_dims* d, int causal, size_t* bytes);
 
-/* Gradients of a scalar loss L through the bidirectional forward, given
- * dL/dO ("Gradient structure": the score gradient of Eq. 18, gamma times the
- * upstream gradient minus its gamma-weighted mean, chained through the
- * Gaussian score of Eqs. 2-3 and 16 to the routing vectors and the
- * parameters, and through Eqs. 5-7 to the values).
- *  Q_X, K_X, V_X, mu, log_sigma2, log_pi, eps  as gma_forward (causal must
- *             be 0: the causal backward returns GMA_ERR_UNSUPPORTED)
+/* Gradients of a scalar loss L through the forward, given dL/dO ("Gradient
+ * structure": the score gradient of Eq. 18, gamma times the upstream
+ * gradient minus its gamma-weighted mean, chained through the Gaussian score
+ * of Eqs. 2-3 and 16 to the routing vectors and the parameters, and through
+ * Eqs. 5-7, or the prefix form of Eq. 8b when causal, to the values).
+ *  Q_X, K_X, V_X, mu, log_sigma2, log_pi, eps, causal  as gma_forward
  *  dO         [B,H,N,d_v] of d->dtype: dL/dO
  *  dQ, dK     [B,H,N,d_r] of d->dtype: written
  *  dV         [B,H,N,d_v] of d->dtype: written
@@ -157,7 +156,9 @@ int gma_backward_workspace_bytes(const gma_dims* d, int causal, size_t* bytes);
  * The forward quantities are recomputed; the output O is not an input.
  * fp32 arithmetic (products on fp32 MFMA); for bf16 inputs the
  * responsibilities are those of the bf16 forward.  N is limited to
- * 65535 * 64 (else GMA_ERR_UNSUPPORTED). */
+ * 65535 * 64, and when causal B*H*ceil(N/64) to 65535 (else
+ * GMA_ERR_UNSUPPORTED); the causal workspace also holds per-64-token-chunk
+ * states and 64 x 64 chunk products. */
 int gma_backward(const void* Q_X, const void* K_X, const void* V_X, const float* mu,
                  const float* log_sigma2, const float* log_pi, float eps, int causal,
                  const void* dO, const gma_dims* d, void* dQ, void* dK, void* dV,
