@@ -53,20 +53,24 @@ struct GemmArgs {
 constexpr int kGT = 64;                 // output tile
 constexpr int kGK = 16;                 // contraction step (a multiple of 16)
 constexpr int kGQ = kGK / 16;           // four-element groups per thread and operand
-constexpr int kGLD = kGK + 4;           // LDS row stride (floats), 16-byte rows
+constexpr int kGLD = kGK + 4;           // LDS row stride of [row][k] tiles (floats)
+constexpr int kTLD = kGT + 4;           // LDS row stride of [k][row] tiles (floats)
+constexpr int kLDS = kGT * kGLD > kGK * kTLD ? kGT * kGLD : kGK * kTLD;
 
 // Row-major A is M x K (TA: stored K x M), B is K x N (TB: stored N x K).
-// Four waves, each a 32 x 32 quarter of the 64 x 64 tile as 2 x 2 MFMA tiles;
-// LDS holds A and B^T tiles as [row][k] so a lane reads its four contraction
-// values as one 16-byte load.  Each thread moves kGQ x 4 consecutive elements of
+// Four waves, each a 32 x 32 quarter of the 64 x 64 tile as 2 x 2 MFMA tiles.
+// An operand whose rows run along k is kept as [row][k] in LDS and a lane
+// reads its four contraction values as one 16-byte load; a transposed operand
+// (rows along m or n) is kept as it arrives, [k][row], and read as four
+// conflict-free 4-byte loads.  Each thread moves kGQ x 4 consecutive elements of
 // a row of A and of B per step: 16-byte loads where the operand allows it
 // (g.vec bit 0 for A, bit 1 for B: leading dimension, unit stride and base
 // 16-byte aligned) and the four are in bounds, else four checked loads; the
 // next step's elements are loaded while the current step multiplies.
 template <bool TA, bool TB>
 __global__ void __launch_bounds__(256) gma_bgemm_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) float As[kGT * kGLD];
-  __shared__ __attribute__((aligned(16))) float Bs[kGT * kGLD];
+  __shared__ __attribute__((aligned(16))) float As[kLDS];
+  __shared__ __attribute__((aligned(16))) float Bs[kLDS];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int r = lane & 15, gq = lane >> 4;
   const int wr = wave >> 1, wc = wave & 1;
@@ -122,33 +126,43 @@ __global__ void __launch_bounds__(256) gma_bgemm_kernel(GemmArgs g) {
 
   if (kb < ke) load(kb);
   for (int k0 = kb; k0 < ke; k0 += kGK) {
-    // stage A as [m][k] and B as [n][k]
+    // stage each operand as its rows arrive: A as [m][k] (or, transposed, as
+    // [k][m]) and B as [n][k] (or [k][n]); always 16-byte stores
 #pragma unroll
     for (int h = 0; h < kGQ; ++h) {
-      if (!TA) {
-        st16(&As[ar * kGLD + ac + 4 * h], f32x4{ra[4 * h], ra[4 * h + 1], ra[4 * h + 2], ra[4 * h + 3]});
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) As[(ac + 4 * h + e) * kGLD + ar] = ra[4 * h + e];
-      }
-      if (TB) {
-        st16(&Bs[br * kGLD + bc + 4 * h], f32x4{rb[4 * h], rb[4 * h + 1], rb[4 * h + 2], rb[4 * h + 3]});
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Bs[(bc + 4 * h + e) * kGLD + br] = rb[4 * h + e];
-      }
+      const f32x4 va4 = f32x4{ra[4 * h], ra[4 * h + 1], ra[4 * h + 2], ra[4 * h + 3]};
+      const f32x4 vb4 = f32x4{rb[4 * h], rb[4 * h + 1], rb[4 * h + 2], rb[4 * h + 3]};
+      if (!TA) st16(&As[ar * kGLD + ac + 4 * h], va4);
+      else st16(&As[ar * kTLD + ac + 4 * h], va4);
+      if (TB) st16(&Bs[br * kGLD + bc + 4 * h], vb4);
+      else st16(&Bs[br * kTLD + bc + 4 * h], vb4);
     }
     __syncthreads();
     if (k0 + kGK < ke) load(k0 + kGK);
 #pragma unroll
     for (int kk = 0; kk < kGK / 16; ++kk) {
+      // lane (r, gq) takes contraction indices 16 kk + 4 gq + e of row r
       f32x4 a[2], b[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = ld16<f32x4>(&As[(32 * wr + 16 * i + r) * kGLD + 16 * kk + 4 * gq]);
+      for (int i = 0; i < 2; ++i) {
+        const int m = 32 * wr + 16 * i + r;
+        if (!TA) {
+          a[i] = ld16<f32x4>(&As[m * kGLD + 16 * kk + 4 * gq]);
+        } else {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = ld16<f32x4>(&Bs[(32 * wc + 16 * j + r) * kGLD + 16 * kk + 4 * gq]);
+          for (int e = 0; e < 4; ++e) a[i][e] = As[(16 * kk + 4 * gq + e) * kTLD + m];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = 32 * wc + 16 * j + r;
+        if (TB) {
+          b[j] = ld16<f32x4>(&Bs[n * kGLD + 16 * kk + 4 * gq]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) b[j][e] = Bs[(16 * kk + 4 * gq + e) * kTLD + n];
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
