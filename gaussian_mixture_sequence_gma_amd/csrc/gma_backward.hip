@@ -219,28 +219,27 @@ __device__ __forceinline__ void stx(void* p, size_t i, float v) {
 }
 
 // Per token: X3 = [x | x^2 | 1] for a routing vector, and (values) V1 = [v | 1],
-// rows of stride ld (the padding columns are never read).  128 threads per
-// row, two rows at a time per workgroup, striding over the rows.
+// rows of stride ld (= width + 3; the pad columns after the ones are zero).
+// d / 4 threads per row, four elements each, 16-byte stores.
+__device__ __forceinline__ f32x4 load4x(const bf16* p) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(__builtin_assume_aligned(p, 8));
+  return f32x4{from_bf16(v[0]), from_bf16(v[1]), from_bf16(v[2]), from_bf16(v[3])};
+}
+__device__ __forceinline__ f32x4 load4x(const float* p) { return ld16<f32x4>(p); }
+
 template <class T>
 __global__ void __launch_bounds__(256) gma_bwd_prep_kernel(const void* __restrict__ x, int d,
                                                            int squares, int64_t rows, int ld,
                                                            float* __restrict__ out) {
-  const int W = squares ? 2 * d + 1 : d + 1;
-  for (int64_t row = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7); row < rows;
-       row += (int64_t)gridDim.x * 2) {
+  const int tpr = d / 4, rpb = 256 / tpr;
+  const int j = threadIdx.x % tpr;
+  for (int64_t row = (int64_t)blockIdx.x * rpb + threadIdx.x / tpr; row < rows;
+       row += (int64_t)gridDim.x * rpb) {
+    const f32x4 v = load4x(static_cast<const T*>(x) + (size_t)row * d + 4 * j);
     float* o = out + (size_t)row * ld;
-    for (int c = threadIdx.x & 127; c < W; c += 128) {
-      float v;
-      if (c < d) {
-        v = ldx<T>(x, (size_t)row * d + c);
-      } else if (squares && c < 2 * d) {
-        const float xv = ldx<T>(x, (size_t)row * d + c - d);
-        v = xv * xv;
-      } else {
-        v = 1.f;
-      }
-      o[c] = v;
-    }
+    st16(o + 4 * j, v);
+    if (squares) st16(o + d + 4 * j, v * v);
+    if (j == 0) st16(o + (squares ? 2 * d : d), f32x4{1.f, 0.f, 0.f, 0.f});
   }
 }
 
@@ -549,12 +548,12 @@ hipError_t run_backward(const Plan& pp, const Tensors& t0, const BwdTensors& gt,
   tr.gamma = Gk;
   GMA_CHECK(launch_resp(pp, tr, s));
   if (g_launch_hook) g_launch_hook("gma_bwd_prep", s, 1);
-  hipLaunchKernelGGL(gma_bwd_prep_kernel<T>, dim3(sblocks(rows, 2)), dim3(256), 0, s, t.q, dr, 1,
-                     rows, l3, x3q);
-  hipLaunchKernelGGL(gma_bwd_prep_kernel<T>, dim3(sblocks(rows, 2)), dim3(256), 0, s, t.k, dr, 1,
-                     rows, l3, x3k);
-  hipLaunchKernelGGL(gma_bwd_prep_kernel<T>, dim3(sblocks(rows, 2)), dim3(256), 0, s, t.v, dv, 0,
-                     rows, l1, v1);
+  hipLaunchKernelGGL(gma_bwd_prep_kernel<T>, dim3(sblocks(rows, 1024 / dr)), dim3(256), 0, s, t.q,
+                     dr, 1, rows, l3, x3q);
+  hipLaunchKernelGGL(gma_bwd_prep_kernel<T>, dim3(sblocks(rows, 1024 / dr)), dim3(256), 0, s, t.k,
+                     dr, 1, rows, l3, x3k);
+  hipLaunchKernelGGL(gma_bwd_prep_kernel<T>, dim3(sblocks(rows, 1024 / dv)), dim3(256), 0, s, t.v,
+                     dv, 0, rows, l1, v1);
   hipLaunchKernelGGL(gma_bwd_params_kernel, dim3(blocks(pp.H * K * dr, 256)), dim3(256), 0, s,
                      t.mu, t.ls2, pp.H * K * (int64_t)dr, dr, WW);
   GMA_CHECK(hipGetLastError());
