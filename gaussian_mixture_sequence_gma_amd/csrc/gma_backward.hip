@@ -296,20 +296,30 @@ __global__ void __launch_bounds__(256) gma_bwd_softmax_kernel(const float* __res
 
 // dX = -x P1 + P2 from X3 = [x | x^2 | 1] and P = [P1 | P2].
 // Rows are padded to Np per unit (Np = N without padding); row r of unit u
-// goes to row u * N + r of the caller's tensor when r < N.
+// goes to row u * N + r of the caller's tensor when r < N.  Four consecutive
+// elements per thread.
+template <class T>
+__device__ __forceinline__ void store4x(void* p, size_t i, f32x4 v) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) stx<T>(p, i + e, v[e]);
+}
+
 template <class T>
 __global__ void __launch_bounds__(256) gma_bwd_dx_kernel(const float* __restrict__ x3, int ld,
                                                          const float* __restrict__ P, int d,
                                                          int64_t rows, int64_t Np, int64_t N,
                                                          void* __restrict__ dx) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < rows * d;
+  const int q = d / 4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < rows * q;
        i += (int64_t)gridDim.x * 256) {
-    const int64_t row = i / d;
-    const int c = (int)(i - row * d);
+    const int64_t row = i / q;
+    const int c = 4 * (int)(i - row * q);
     const int64_t u = row / Np, r = row - u * Np;
     if (r >= N) continue;
     const float* p = P + (size_t)row * 2 * d;
-    stx<T>(dx, (size_t)(u * N + r) * d + c, -x3[(size_t)row * ld + c] * p[c] + p[d + c]);
+    const f32x4 xv = ld16<f32x4>(x3 + (size_t)row * ld + c);
+    const f32x4 p1 = ld16<f32x4>(p + c), p2 = ld16<f32x4>(p + d + c);
+    store4x<T>(dx, (size_t)(u * N + r) * d + c, p2 - xv * p1);
   }
 }
 
@@ -317,12 +327,13 @@ template <class T>
 __global__ void __launch_bounds__(256) gma_bwd_store_kernel(const float* __restrict__ src, int d,
                                                             int64_t rows, int64_t Np, int64_t N,
                                                             void* __restrict__ dst) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < rows * d;
+  const int q = d / 4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < rows * q;
        i += (int64_t)gridDim.x * 256) {
-    const int64_t row = i / d;
-    const int c = (int)(i - row * d);
+    const int64_t row = i / q;
+    const int c = 4 * (int)(i - row * q);
     const int64_t u = row / Np, r = row - u * Np;
-    if (r < N) stx<T>(dst, (size_t)(u * N + r) * d + c, src[i]);
+    if (r < N) store4x<T>(dst, (size_t)(u * N + r) * d + c, ld16<f32x4>(src + (size_t)row * d + c));
   }
 }
 
@@ -649,8 +660,8 @@ hipError_t run_backward(const Plan& pp, const Tensors& t0, const BwdTensors& gt,
                      rows);
   hipLaunchKernelGGL(gma_bwd_softmax_kernel, dim3(sblocks(rows, 4)), dim3(256), 0, s, Gk, dGk, K,
                      rows);
-  hipLaunchKernelGGL(gma_bwd_store_kernel<T>, dim3(sblocks(rows * dv, 256)), dim3(256), 0, s, dvf,
-                     dv, rows, Np, N0, gt.dV);
+  hipLaunchKernelGGL(gma_bwd_store_kernel<T>, dim3(sblocks(rows * dv / 4, 256)), dim3(256), 0, s,
+                     dvf, dv, rows, Np, N0, gt.dV);
   GMA_CHECK(hipGetLastError());
   if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 0);
 
@@ -666,8 +677,8 @@ hipError_t run_backward(const Plan& pp, const Tensors& t0, const BwdTensors& gt,
                    (int64_t)K * l3, K, w3, (int)Np, U, ks, part, s));
     if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 0);
     if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 1);
-    hipLaunchKernelGGL(gma_bwd_dx_kernel<T>, dim3(sblocks(rows * dr, 256)), dim3(256), 0, s, x3,
-                       l3, P, dr, rows, Np, N0, side ? gt.dK : gt.dQ);
+    hipLaunchKernelGGL(gma_bwd_dx_kernel<T>, dim3(sblocks(rows * dr / 4, 256)), dim3(256), 0, s,
+                       x3, l3, P, dr, rows, Np, N0, side ? gt.dK : gt.dQ);
     GMA_CHECK(hipGetLastError());
     if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 0);
   }
