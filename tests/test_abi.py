@@ -257,3 +257,26 @@ def test_backward_rejects_before_launch():
     assert st(workspace_bytes=n - 1) == B.GMA_ERR_WORKSPACE
     assert B.gma_backward_workspace_bytes(_dims(N=100), 1) > B.gma_backward_workspace_bytes(
         _dims(N=100), 0)
+
+
+def test_usage_stats_rejects_before_launch():
+    def st(**over):
+        args = dict(X_r=A16, mu=A16, log_sigma2=A16, log_pi=A16, dims=_dims(),
+                    util_threshold=0.1, counts=None, mean_gamma=None, utilization=None,
+                    head_stats=None, workspace=A16, workspace_bytes=1 << 40, stream=0)
+        args.update(over)
+        with pytest.raises(B.GmaError) as ei:
+            B.gma_usage_stats(**args)
+        return ei.value.status
+    assert st(X_r=None) == B.GMA_ERR_INVALID_ARG
+    assert st(workspace=None) == B.GMA_ERR_INVALID_ARG
+    assert st(X_r=MIS) == B.GMA_ERR_INVALID_ARG
+    assert st(counts=A16 + 2) == B.GMA_ERR_INVALID_ARG
+    assert st(util_threshold=float("nan")) == B.GMA_ERR_INVALID_ARG
+    assert st(dims=_dims(K=0)) == B.GMA_ERR_INVALID_ARG
+    assert st(dims=_dims(d_r=24)) == B.GMA_ERR_UNSUPPORTED
+    assert st(dims=_dims(B=65535, H=1, N=32769)) == B.GMA_ERR_UNSUPPORTED       # B*N >= 2^31
+    assert "2^31" in B.gma_last_error()
+    n = B.gma_usage_workspace_bytes(_dims())
+    assert n >= B.gma_forward_workspace_bytes(_dims(), 0)
+    assert st(workspace_bytes=n - 1) == B.GMA_ERR_WORKSPACE
