@@ -1086,8 +1086,200 @@ static hipError_t run_resp(const Plan& p, const Tensors& t, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ============================================================================
+// Usage statistics, token-owner form (bf16 routing vectors, K_pad a multiple of
+// 32, d_r <= 64): the latent write's key loop without the values.  Every wave
+// owns 32 tokens at a time and all components: scores on MFMA from the
+// coefficient table in LDS, the per-token softmax inside the wave, and per
+// lane, for the components of its column, the sums of gamma and of gamma >
+// thr, per token sum_k gamma ln gamma from the softmax's own sums, and an LDS
+// histogram of the assignments.  With
+// no V~ in the accumulation registers it runs two waves per SIMD.  One record
+// of 3 K_pad + 4 floats per workgroup, as the component-owner statistics pass.
+// ============================================================================
 template <class C>
-static hipError_t run_usage(const Plan& p, const Tensors& t, hipStream_t s) {
+struct Usage2 {
+  static constexpr int KP = C::Kp;
+  static constexpr int CT = KP / 16;
+  static constexpr int NKS = C::DRP / 32;
+  static constexpr int COEF = CT * NKS * 4;
+  static constexpr int LDS = COEF * 1024 + KP * 4 + KP * 4 + 4 * (3 * KP + 1) * 4;
+  static constexpr bool kOK = C::kBF && KP % 32 == 0 && C::DRP <= 64 && LDS <= 80 * 1024;
+};
+
+template <class C>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+gma_usage2_kernel(BidirArgs a) {
+  using R = Usage2<C>;
+  constexpr int NW = 4;
+  __shared__ __attribute__((aligned(16))) char lds[R::LDS];
+  bf16x8* coef = reinterpret_cast<bf16x8*>(lds);
+  float* cperm = reinterpret_cast<float*>(lds + R::COEF * 1024);
+  int* hist = reinterpret_cast<int*>(lds + R::COEF * 1024 + R::KP * 4);
+  float* red = reinterpret_cast<float*>(lds + R::COEF * 1024 + 2 * R::KP * 4);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int64_t bh = blockIdx.y;
+  const int h = (int)(bh % a.H);
+  {
+    const char* tb = a.params + (size_t)h * a.head_bytes + a.head_bytes / 2;
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(tb);
+    for (int idx = threadIdx.x; idx < R::COEF * 64; idx += NW * 64) coef[idx] = src[idx];
+    const float* cp = reinterpret_cast<const float*>(tb + (size_t)8 * C::Kp * C::DRP);
+    for (int j = threadIdx.x; j < R::KP; j += NW * 64) {
+      cperm[j] = cp[j];
+      hist[j] = 0;
+    }
+  }
+  __syncthreads();
+
+  const int64_t G32 = (a.N + 31) / 32;
+  const int64_t gpw = (G32 + gridDim.x - 1) / gridDim.x;
+  const int64_t gb = (int64_t)blockIdx.x * gpw;
+  const int64_t ge = gb + gpw < G32 ? gb + gpw : G32;
+  const bf16* xs = reinterpret_cast<const bf16*>(a.x) + (size_t)bh * a.N * C::DR;
+
+  bf16x8 xr[2][R::NKS];
+  auto load_x = [&](int64_t grp) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int64_t tok = grp * 32 + tile_token(tt, c);
+#pragma unroll
+      for (int s = 0; s < R::NKS; ++s) {
+        const int col = 32 * s + 8 * g;
+        const bool ok = tok < a.N && col < C::DR;
+        const bf16x8 v = ld16<bf16x8>(xs + (size_t)(ok ? tok : 0) * C::DR + (ok ? col : 0));
+        xr[tt][s] = ok ? v : bf16x8{};
+      }
+    }
+  };
+
+  float gsum[R::CT], gcnt[R::CT], gent = 0.f;
+#pragma unroll
+  for (int ct = 0; ct < R::CT; ++ct) gsum[ct] = gcnt[ct] = 0.f;
+
+  int64_t grp = gb + wave;
+  if (grp < ge) load_x(grp);
+  for (; grp < ge; grp += NW) {
+    bf16x8 f[2][R::NKS][NFX<false>];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int s = 0; s < R::NKS; ++s) make_features<false>(xr[tt][s], xr[tt][s], f[tt][s]);
+    if (grp + NW < ge) load_x(grp + NW);
+
+    f32x4 S[2][R::CT];
+#pragma unroll
+    for (int ct = 0; ct < R::CT; ++ct) {
+      const float cv = cperm[ct * 16 + c];
+      S[0][ct] = f32x4{cv, cv, cv, cv};
+      S[1][ct] = S[0][ct];
+    }
+    // steps hs = (component tile, routing chunk): the four coefficient operands
+    // of step hs + 1 are read from LDS while the MFMAs of step hs run
+    constexpr int NH = R::CT * R::NKS;
+    bf16x8 wbuf[2][4];
+#pragma unroll
+    for (int ar = 0; ar < 4; ++ar) wbuf[0][ar] = coef[ar * 64 + lane];
+#pragma unroll
+    for (int hs = 0; hs < NH; ++hs) {
+      if (hs + 1 < NH) {
+#pragma unroll
+        for (int ar = 0; ar < 4; ++ar) wbuf[(hs + 1) & 1][ar] = coef[((hs + 1) * 4 + ar) * 64 + lane];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const int ct = hs / R::NKS, s = hs % R::NKS;
+#pragma unroll
+      for (int q = 0; q < NQX<false>; ++q)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+          S[tt][ct] = mma(f[tt][s][kFI[q]], wbuf[hs & 1][kWI[q]], S[tt][ct]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // per token (row 4g + i of key tile tt): softmax over the CT columns of
+    // this lane and the 16 lanes of its row; lane column c of tile ct is
+    // component pair_row(ct, c)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t tok = grp * 32 + 8 * g + 4 * tt + i;
+        const bool valid = tok < a.N;
+        // the row maximum, then the lowest component index attaining it (in a
+        // lane the component index grows with the tile)
+        float m = S[tt][0][i];
+#pragma unroll
+        for (int ct = 1; ct < R::CT; ++ct) m = fmaxf(m, S[tt][ct][i]);
+        m = row16_max(m);
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int ct = R::CT - 1; ct >= 0; --ct) bi = S[tt][ct][i] == m ? pair_row(ct, c) : bi;
+        bi = min(bi, dpp_i<0xB1>(bi));
+        bi = min(bi, dpp_i<0x4E>(bi));
+        bi = min(bi, dpp_i<0x141>(bi));
+        bi = min(bi, dpp_i<0x140>(bi));
+        // scores are in log2 units: with t = s - m, gamma = 2^t / l and
+        // sum_k gamma ln gamma = ln 2 * sum_k 2^t t / l - ln l, one log per token
+        float l = 0.f, et = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < R::CT; ++ct) {
+          const float tk = S[tt][ct][i] - m;
+          const float e = exp2_fast(tk);
+          S[tt][ct][i] = e;
+          l += e;
+          et += e > 0.f ? e * tk : 0.f;
+        }
+        l = row16_sum(l);
+        et = row16_sum(et);
+        const float inv = valid ? fast_rcp(l) : 0.f;
+        if (valid && c == 0) gent += 0.69314718f * et * inv - __logf(l);
+#pragma unroll
+        for (int ct = 0; ct < R::CT; ++ct) {
+          const float gm = S[tt][ct][i] * inv;
+          gsum[ct] += gm;
+          gcnt[ct] += (valid && gm > a.thr) ? 1.f : 0.f;
+        }
+        if (valid && c == 0 && (unsigned)bi < (unsigned)R::KP) atomicAdd(&hist[bi], 1);
+      }
+  }
+
+  // lanes of one column c hold different tokens: sum the four lane groups,
+  // then the four waves in order
+#pragma unroll
+  for (int ct = 0; ct < R::CT; ++ct) {
+    const float s1 = groups_sum(gsum[ct]), s2 = groups_sum(gcnt[ct]);
+    if (g == 0) {
+      red[(wave * 3 + 0) * R::KP + pair_row(ct, c)] = s1;
+      red[(wave * 3 + 1) * R::KP + pair_row(ct, c)] = s2;
+    }
+  }
+  const float e = groups_sum(row16_sum(gent));
+  if (lane == 0) red[NW * 3 * R::KP + wave] = e;
+  __syncthreads();
+  float* out = a.diag + ((size_t)bh * gridDim.x + blockIdx.x) * (3 * C::Kp + 4);
+  for (int k = threadIdx.x; k < R::KP; k += NW * 64) {
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      s1 += red[(w * 3 + 0) * R::KP + k];
+      s2 += red[(w * 3 + 1) * R::KP + k];
+    }
+    out[k] = s1;
+    out[C::Kp + k] = s2;
+    out[2 * C::Kp + k] = (float)hist[k];
+  }
+  if (threadIdx.x == 0) {
+    float e4 = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) e4 += red[NW * 3 * R::KP + w];
+    out[3 * C::Kp] = e4;
+  }
+}
+
+template <class C>
+static hipError_t run_usage(const Plan& p, const Tensors& t, int& splits, hipStream_t s) {
   BidirArgs a{};
   a.params = t.ws + p.off_params;
   a.head_bytes = p.head_bytes;
@@ -1100,7 +1292,23 @@ static hipError_t run_usage(const Plan& p, const Tensors& t, hipStream_t s) {
   a.diag = t.diag;
   a.thr = t.thr;
   if (g_launch_hook) g_launch_hook("gma_usage", s, 1);
-  hipLaunchKernelGGL((gma_read_kernel<C, 2>), dim3(p.S, (unsigned)p.BH), dim3(kThreads), 0, s, a);
+  if constexpr (Usage2<C>::kOK) {
+    // about two workgroups per compute unit, at least four 32-token groups each,
+    // no more than the partial records the workspace holds (p.S per sequence)
+    const int64_t g32 = (p.N + 31) / 32;
+    int64_t s2 = (512 + p.BH - 1) / p.BH;
+    const int64_t cap = (g32 + 3) / 4;
+    if (s2 > cap) s2 = cap;
+    if (s2 > p.S) s2 = p.S;
+    if (s2 < 1) s2 = 1;
+    splits = (int)s2;
+    hipLaunchKernelGGL(gma_usage2_kernel<C>, dim3((unsigned)s2, (unsigned)p.BH), dim3(256), 0, s,
+                       a);
+  } else {
+    splits = p.S;
+    hipLaunchKernelGGL((gma_read_kernel<C, 2>), dim3(p.S, (unsigned)p.BH), dim3(kThreads), 0, s,
+                       a);
+  }
   if (g_launch_hook) g_launch_hook("gma_usage", s, 0);
   return hipGetLastError();
 }
@@ -1240,10 +1448,10 @@ hipError_t launch_bidir(const Plan& p, const Tensors& t, hipStream_t s) {
 
 #define GMA_USAGE_DR_CASES(BF, CPW, NG)                                     \
   switch (p.DR) {                                                           \
-    case 16: e = run_usage<Cfg<BF, CPW, NG, 16, 16>>(p, t, s); break;       \
-    case 32: e = run_usage<Cfg<BF, CPW, NG, 32, 16>>(p, t, s); break;       \
-    case 64: e = run_usage<Cfg<BF, CPW, NG, 64, 16>>(p, t, s); break;       \
-    case 128: e = run_usage<Cfg<BF, CPW, NG, 128, 16>>(p, t, s); break;     \
+    case 16: e = run_usage<Cfg<BF, CPW, NG, 16, 16>>(p, t, splits, s); break;   \
+    case 32: e = run_usage<Cfg<BF, CPW, NG, 32, 16>>(p, t, splits, s); break;   \
+    case 64: e = run_usage<Cfg<BF, CPW, NG, 64, 16>>(p, t, splits, s); break;   \
+    case 128: e = run_usage<Cfg<BF, CPW, NG, 128, 16>>(p, t, splits, s); break; \
   }                                                                         \
   break;
 #define GMA_USAGE_CASES(BF)                                                 \
@@ -1258,6 +1466,7 @@ hipError_t launch_bidir(const Plan& p, const Tensors& t, hipStream_t s) {
 hipError_t launch_usage(const Plan& p, const Tensors& t, int32_t* counts, float* mean_gamma,
                         float* util, float* head_stats, hipStream_t s) {
   hipError_t e = hipErrorInvalidValue;
+  int splits = p.S;
   if (p.bf) {
     switch (0) { default: GMA_USAGE_CASES(true) }
   } else {
@@ -1266,7 +1475,7 @@ hipError_t launch_usage(const Plan& p, const Tensors& t, int32_t* counts, float*
   if (e != hipSuccess) return e;
   if (g_launch_hook) g_launch_hook("gma_usage_reduce", s, 1);
   hipLaunchKernelGGL(gma_usage_reduce_kernel, dim3((unsigned)p.H), dim3(256), 0, s, t.diag, p.B,
-                     (int)p.H, p.S, p.Kp, p.K, p.B * p.N, counts, mean_gamma, util, head_stats);
+                     (int)p.H, splits, p.Kp, p.K, p.B * p.N, counts, mean_gamma, util, head_stats);
   if (g_launch_hook) g_launch_hook("gma_usage_reduce", s, 0);
   return hipGetLastError();
 }
