@@ -195,6 +195,139 @@ __global__ void __launch_bounds__(256) gma_bgemm_kernel(GemmArgs g) {
       }
 }
 
+// The same product for 64 < N <= 16 TN (the augmented widths d + 1 and K):
+// one workgroup covers every column of 64 rows, so the left operand is read
+// once rather than once per 64 columns.  Four waves of 16 rows x 16 TN columns
+// (TN MFMA tiles each); staging and operand reads as in gma_bgemm_kernel.
+template <bool TA, bool TB, int TN>
+__global__ void __launch_bounds__(256) gma_bgemm_wide_kernel(GemmArgs g) {
+  constexpr int BN = 16 * TN;
+  constexpr int BLD = BN + 4;                       // [k][n] row stride
+  constexpr int BQ = BN * kGK / 4;                  // four-element groups of the B tile
+  constexpr int QPT = (BQ + 255) / 256;             // per thread
+  __shared__ __attribute__((aligned(16))) float As[kLDS];
+  __shared__ __attribute__((aligned(16))) float Bs[(BN * kGLD > kGK * BLD) ? BN * kGLD : kGK * BLD];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int r = lane & 15, gq = lane >> 4;
+  const int m0 = blockIdx.y * kGT;
+  const int u = blockIdx.z / g.ksplit, ks = blockIdx.z % g.ksplit;
+  const int kchunk = ((g.K + g.ksplit - 1) / g.ksplit + kGK - 1) / kGK * kGK;
+  const int kb = ks * kchunk, ke = min(g.K, kb + kchunk);
+  const float* A = g.A + (size_t)u * g.sA;
+  const float* B = g.B + (size_t)(g.bmod > 0 ? u % g.bmod : u) * g.sB;
+  const bool va = g.vec & 1, vb = (g.vec >> 1) & 1;
+
+  constexpr int TPK = 16 / kGQ;
+  const int ar = TA ? t / TPK : t >> 2, ac = TA ? (t % TPK) * 4 * kGQ : (t & 3) * 4 * kGQ;
+  float ra[4 * kGQ], rb[4 * QPT];
+  auto quad = [](bool vec, const float* p, bool row_ok, int idx, int lim, float* dst) {
+    if (vec && row_ok && idx + 3 < lim) {
+      const f32x4 v = ld16<f32x4>(p);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[e] = v[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[e] = (row_ok && idx + e < lim) ? p[e] : 0.f;
+    }
+  };
+  // B group q: TB -> row n = q / (kGK / 4), k = 4 (q % (kGK / 4));
+  //            else -> k = q / (BN / 4), n = 4 (q % (BN / 4))
+  auto bq_row = [](int q) { return TB ? q / (kGK / 4) : q / (BN / 4); };
+  auto bq_col = [](int q) { return TB ? 4 * (q % (kGK / 4)) : 4 * (q % (BN / 4)); };
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int h = 0; h < kGQ; ++h) {
+      if (!TA) {
+        const int gm = m0 + ar, gk = k0 + ac + 4 * h;
+        quad(va, A + (size_t)gm * g.lda + gk, gm < g.M, gk, ke, ra + 4 * h);
+      } else {
+        const int gk = k0 + ar, gm = m0 + ac + 4 * h;
+        quad(va, A + (size_t)gk * g.lda + gm, gk < ke, gm, g.M, ra + 4 * h);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+      const int q = t + 256 * j;
+      if (q >= BQ) break;
+      if (TB) {
+        const int gn = bq_row(q), gk = k0 + bq_col(q);
+        quad(vb, B + (size_t)gn * g.ldb + gk, gn < g.N, gk, ke, rb + 4 * j);
+      } else {
+        const int gk = k0 + bq_row(q), gn = bq_col(q);
+        quad(vb, B + (size_t)gk * g.ldb + gn, gk < ke, gn, g.N, rb + 4 * j);
+      }
+    }
+  };
+
+  f32x4 acc[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (kb < ke) load(kb);
+  for (int k0 = kb; k0 < ke; k0 += kGK) {
+#pragma unroll
+    for (int h = 0; h < kGQ; ++h) {
+      const f32x4 va4 = f32x4{ra[4 * h], ra[4 * h + 1], ra[4 * h + 2], ra[4 * h + 3]};
+      if (!TA) st16(&As[ar * kGLD + ac + 4 * h], va4);
+      else st16(&As[ar * kTLD + ac + 4 * h], va4);
+    }
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+      const int q = t + 256 * j;
+      if (q >= BQ) break;
+      const f32x4 vb4 = f32x4{rb[4 * j], rb[4 * j + 1], rb[4 * j + 2], rb[4 * j + 3]};
+      if (TB) st16(&Bs[bq_row(q) * kGLD + bq_col(q)], vb4);
+      else st16(&Bs[bq_row(q) * BLD + bq_col(q)], vb4);
+    }
+    __syncthreads();
+    if (k0 + kGK < ke) load(k0 + kGK);
+#pragma unroll
+    for (int kk = 0; kk < kGK / 16; ++kk) {
+      f32x4 a;
+      const int m = 16 * wave + r;
+      if (!TA) {
+        a = ld16<f32x4>(&As[m * kGLD + 16 * kk + 4 * gq]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] = As[(16 * kk + 4 * gq + e) * kTLD + m];
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = 16 * j + r;
+        f32x4 b;
+        if (TB) {
+          b = ld16<f32x4>(&Bs[n * kGLD + 16 * kk + 4 * gq]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) b[e] = Bs[(16 * kk + 4 * gq + e) * BLD + n];
+        }
+        acc[j] = mma(a, b, acc[j]);
+      }
+    }
+    __syncthreads();
+  }
+
+  float* C;
+  int ldc;
+  if (g.ksplit > 1) {
+    C = g.C + ((size_t)u * g.ksplit + ks) * g.M * g.N;
+    ldc = g.N;
+  } else {
+    C = g.C + (size_t)u * g.sC;
+    ldc = g.ldc;
+  }
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = m0 + 16 * wave + 4 * gq + e, n = 16 * j + r;
+      if (m < g.M && n < g.N) {
+        float* c = C + (size_t)m * ldc + n;
+        *c = g.accum ? *c + acc[j][e] : acc[j][e];
+      }
+    }
+}
+
 // C[u][m][n] = sum over the splits, in split order.
 __global__ void __launch_bounds__(256) gma_split_sum_kernel(const float* __restrict__ part,
                                                             int ksplit, int M, int N,
@@ -469,6 +602,13 @@ BwdLayout bwd_layout(const Plan& pp, bool causal, int64_t N) {
   return L;
 }
 
+template <bool TA, bool TB>
+void launch_gemm_kernel(bool wide9, bool wide, dim3 grid, const GemmArgs& g, hipStream_t s) {
+  if (!wide) hipLaunchKernelGGL((gma_bgemm_kernel<TA, TB>), grid, dim3(256), 0, s, g);
+  else if (!wide9) hipLaunchKernelGGL((gma_bgemm_wide_kernel<TA, TB, 8>), grid, dim3(256), 0, s, g);
+  else hipLaunchKernelGGL((gma_bgemm_wide_kernel<TA, TB, 9>), grid, dim3(256), 0, s, g);
+}
+
 hipError_t gemm(bool ta, bool tb, const float* A, int lda, int64_t sA, const float* B, int ldb,
                 int64_t sB, int bmod, float* C, int ldc, int64_t sC, int M, int N, int K,
                 int64_t U, int ksplit, float* part, hipStream_t s, bool accum = false) {
@@ -476,12 +616,14 @@ hipError_t gemm(bool ta, bool tb, const float* A, int lda, int64_t sA, const flo
                   ((ldb % 4 == 0 && sB % 4 == 0 && ((uintptr_t)B & 15) == 0) ? 2 : 0);
   GemmArgs g{A, B, ksplit > 1 ? part : C, M, N, K, lda, ldb, ldc, sA, sB, sC, bmod, ksplit, vec,
              accum ? 1 : 0};
-  const dim3 grid((unsigned)((N + kGT - 1) / kGT), (unsigned)((M + kGT - 1) / kGT),
+  // 64 < N <= 144: one column tile of 128 (8 MFMA tiles per wave) or 144 (9)
+  const bool wide = N > kGT && N <= 144, wide9 = N > 128;
+  const dim3 grid(wide ? 1u : (unsigned)((N + kGT - 1) / kGT), (unsigned)((M + kGT - 1) / kGT),
                   (unsigned)(U * ksplit));
-  if (!ta && !tb) hipLaunchKernelGGL((gma_bgemm_kernel<false, false>), grid, dim3(256), 0, s, g);
-  else if (!ta && tb) hipLaunchKernelGGL((gma_bgemm_kernel<false, true>), grid, dim3(256), 0, s, g);
-  else if (ta && !tb) hipLaunchKernelGGL((gma_bgemm_kernel<true, false>), grid, dim3(256), 0, s, g);
-  else hipLaunchKernelGGL((gma_bgemm_kernel<true, true>), grid, dim3(256), 0, s, g);
+  if (!ta && !tb) launch_gemm_kernel<false, false>(wide9, wide, grid, g, s);
+  else if (!ta && tb) launch_gemm_kernel<false, true>(wide9, wide, grid, g, s);
+  else if (ta && !tb) launch_gemm_kernel<true, false>(wide9, wide, grid, g, s);
+  else launch_gemm_kernel<true, true>(wide9, wide, grid, g, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ksplit <= 1) return e;
   hipLaunchKernelGGL(gma_split_sum_kernel, dim3((unsigned)((M * N + 255) / 256), (unsigned)U),
