@@ -402,8 +402,7 @@ __global__ void __launch_bounds__(256) gma_bwd_ab_kernel(float* __restrict__ nd,
   const float den = r[dv] + eps;
   float dot = 0.f;
   for (int c = lane; c < dv; c += 64) dot += ldx<T>(dO, (size_t)row * dv + c) * r[c];
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) dot += xor_lane(dot, o);
+  dot = groups_sum(row16_sum(dot));
   const float inv = 1.f / den;
   for (int c = lane; c < dv; c += 64) r[c] = ldx<T>(dO, (size_t)row * dv + c) * inv;
   if (lane == 0) r[dv] = -dot * inv * inv;     // o = n / d: (dO . n) / d^2
@@ -421,8 +420,7 @@ __global__ void __launch_bounds__(256) gma_bwd_softmax_kernel(const float* __res
   float* dr = dG + (size_t)row * K;
   float s = 0.f;
   for (int k = lane; k < K; k += 64) s += gr[k] * dr[k];
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) s += xor_lane(s, o);
+  s = groups_sum(row16_sum(s));
   for (int k = lane; k < K; k += 64) dr[k] = gr[k] * (dr[k] - s);
   }
 }
