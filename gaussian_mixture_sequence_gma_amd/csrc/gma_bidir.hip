@@ -1068,6 +1068,9 @@ static hipError_t run_bidir(const Plan& p, const Tensors& t, hipStream_t s) {
 }
 
 template <class C>
+static void launch_resp_kernel(const Plan& p, const BidirArgs& a, hipStream_t s);
+
+template <class C>
 static hipError_t run_resp(const Plan& p, const Tensors& t, hipStream_t s) {
   BidirArgs a{};
   a.params = t.ws + p.off_params;
@@ -1081,7 +1084,7 @@ static hipError_t run_resp(const Plan& p, const Tensors& t, hipStream_t s) {
   a.assign = t.assign_q;
   a.gamma = t.gamma;
   if (g_launch_hook) g_launch_hook("gma_resp", s, 1);
-  hipLaunchKernelGGL((gma_read_kernel<C, 1>), dim3(p.S, (unsigned)p.BH), dim3(kThreads), 0, s, a);
+  launch_resp_kernel<C>(p, a, s);
   if (g_launch_hook) g_launch_hook("gma_resp", s, 0);
   return hipGetLastError();
 }
@@ -1096,6 +1099,8 @@ static hipError_t run_resp(const Plan& p, const Tensors& t, hipStream_t s) {
 // histogram of the assignments.  With
 // no V~ in the accumulation registers it runs two waves per SIMD.  One record
 // of 3 K_pad + 4 floats per workgroup, as the component-owner statistics pass.
+// MODE 1 writes the responsibilities and assignments instead (a.gamma
+// [BH][N][K], a.assign [BH][N], either may be null), with no statistics.
 // ============================================================================
 template <class C>
 struct Usage2 {
@@ -1107,7 +1112,7 @@ struct Usage2 {
   static constexpr bool kOK = C::kBF && KP % 32 == 0 && C::DRP <= 64 && LDS <= 80 * 1024;
 };
 
-template <class C>
+template <class C, int MODE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 gma_usage2_kernel(BidirArgs a) {
   using R = Usage2<C>;
@@ -1214,12 +1219,14 @@ gma_usage2_kernel(BidirArgs a) {
         for (int ct = 1; ct < R::CT; ++ct) m = fmaxf(m, S[tt][ct][i]);
         m = row16_max(m);
         int bi = 0x7fffffff;
+        if (MODE == 0 || a.assign != nullptr) {
 #pragma unroll
-        for (int ct = R::CT - 1; ct >= 0; --ct) bi = S[tt][ct][i] == m ? pair_row(ct, c) : bi;
-        bi = min(bi, dpp_i<0xB1>(bi));
-        bi = min(bi, dpp_i<0x4E>(bi));
-        bi = min(bi, dpp_i<0x141>(bi));
-        bi = min(bi, dpp_i<0x140>(bi));
+          for (int ct = R::CT - 1; ct >= 0; --ct) bi = S[tt][ct][i] == m ? pair_row(ct, c) : bi;
+          bi = min(bi, dpp_i<0xB1>(bi));
+          bi = min(bi, dpp_i<0x4E>(bi));
+          bi = min(bi, dpp_i<0x141>(bi));
+          bi = min(bi, dpp_i<0x140>(bi));
+        }
         // scores are in log2 units: with t = s - m, gamma = 2^t / l and
         // sum_k gamma ln gamma = ln 2 * sum_k 2^t t / l - ln l, one log per token
         float l = 0.f, et = 0.f;
@@ -1232,18 +1239,31 @@ gma_usage2_kernel(BidirArgs a) {
           et += e > 0.f ? e * tk : 0.f;
         }
         l = row16_sum(l);
-        et = row16_sum(et);
         const float inv = valid ? fast_rcp(l) : 0.f;
-        if (valid && c == 0) gent += 0.69314718f * et * inv - __logf(l);
+        if constexpr (MODE == 0) {
+          et = row16_sum(et);
+          if (valid && c == 0) gent += 0.69314718f * et * inv - __logf(l);
 #pragma unroll
-        for (int ct = 0; ct < R::CT; ++ct) {
-          const float gm = S[tt][ct][i] * inv;
-          gsum[ct] += gm;
-          gcnt[ct] += (valid && gm > a.thr) ? 1.f : 0.f;
+          for (int ct = 0; ct < R::CT; ++ct) {
+            const float gm = S[tt][ct][i] * inv;
+            gsum[ct] += gm;
+            gcnt[ct] += (valid && gm > a.thr) ? 1.f : 0.f;
+          }
+          if (valid && c == 0 && (unsigned)bi < (unsigned)R::KP) atomicAdd(&hist[bi], 1);
+        } else {
+          if (valid && a.gamma != nullptr) {
+            float* gr = a.gamma + ((size_t)bh * a.N + tok) * a.K;
+#pragma unroll
+            for (int ct = 0; ct < R::CT; ++ct) {
+              const int comp = pair_row(ct, c);
+              if (comp < a.K) gr[comp] = S[tt][ct][i] * inv;
+            }
+          }
+          if (valid && c == 0 && a.assign != nullptr) a.assign[(size_t)bh * a.N + tok] = bi;
         }
-        if (valid && c == 0 && (unsigned)bi < (unsigned)R::KP) atomicAdd(&hist[bi], 1);
       }
   }
+  if constexpr (MODE == 1) return;
 
   // lanes of one column c hold different tokens: sum the four lane groups,
   // then the four waves in order
@@ -1278,6 +1298,24 @@ gma_usage2_kernel(BidirArgs a) {
   }
 }
 
+// Responsibilities and assignments of a.x: the token-owner kernel where it
+// applies (about two workgroups per compute unit, at least four 32-token groups
+// each), else the component-owner kernel.
+template <class C>
+static void launch_resp_kernel(const Plan& p, const BidirArgs& a, hipStream_t s) {
+  if constexpr (Usage2<C>::kOK) {
+    const int64_t g32 = (p.N + 31) / 32;
+    int64_t s2 = (512 + p.BH - 1) / p.BH;
+    const int64_t cap = (g32 + 3) / 4;
+    if (s2 > cap) s2 = cap;
+    if (s2 < 1) s2 = 1;
+    hipLaunchKernelGGL((gma_usage2_kernel<C, 1>), dim3((unsigned)s2, (unsigned)p.BH), dim3(256), 0,
+                       s, a);
+  } else {
+    hipLaunchKernelGGL((gma_read_kernel<C, 1>), dim3(p.S, (unsigned)p.BH), dim3(kThreads), 0, s, a);
+  }
+}
+
 template <class C>
 static hipError_t run_usage(const Plan& p, const Tensors& t, int& splits, hipStream_t s) {
   BidirArgs a{};
@@ -1302,8 +1340,8 @@ static hipError_t run_usage(const Plan& p, const Tensors& t, int& splits, hipStr
     if (s2 > p.S) s2 = p.S;
     if (s2 < 1) s2 = 1;
     splits = (int)s2;
-    hipLaunchKernelGGL(gma_usage2_kernel<C>, dim3((unsigned)s2, (unsigned)p.BH), dim3(256), 0, s,
-                       a);
+    hipLaunchKernelGGL((gma_usage2_kernel<C, 0>), dim3((unsigned)s2, (unsigned)p.BH), dim3(256), 0,
+                       s, a);
   } else {
     splits = p.S;
     hipLaunchKernelGGL((gma_read_kernel<C, 2>), dim3(p.S, (unsigned)p.BH), dim3(kThreads), 0, s,
