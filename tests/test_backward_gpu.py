@@ -89,3 +89,47 @@ def test_causal_backward_single_token():
     assert np.linalg.norm(got["dV"] - ref["dV"]) / np.linalg.norm(ref["dV"]) <= 1e-5
     for k in ("dQ", "dK", "dmu", "dlog_sigma2", "dlog_pi"):
         assert np.abs(got[k] - ref[k]).max() <= 1e-5, k
+
+
+@pytest.mark.parametrize("wname", ["long_bidir_bf16", "lm_causal_bf16"])
+def test_backward_full_size_invariants(wname):
+    """The workloads as the benchmark runs them (B1 H32 N32768 K128
+    bidirectional; B4 H12 N8192 K64 causal), checked through properties of the
+    gradient that hold at any size: log pi enters only through a softmax
+    (sum_k dlog_pi = 0 per head); the scores depend on x - mu only (the
+    gradients of a common shift of routing vectors and means cancel); and the
+    value gradients sum to sum_i dO_i (1 - eps / d_i), d_i = gamma^Q_i . Z(_i) +
+    eps, to within the bf16 rounding of dV."""
+    w = inputs.WORKLOADS[wname]
+    gen = inputs.generate(w, 0)
+    dev = upload(gen)
+    torch.manual_seed(0)
+    dOd = torch.randn((w.B, w.H, w.N, w.d_v), device="cuda").to(dev["V"].dtype)
+    g = api.backward(dev["Q"], dev["K"], dev["V"], dev["mu"], dev["log_sigma2"], dev["log_pi"],
+                     dOd, w.eps, w.causal)
+    torch.cuda.synchronize()
+    dlpi = g["dlog_pi"].double()
+    scale = dlpi.abs().sum(-1)
+    assert (dlpi.sum(-1).abs() <= 1e-4 * scale).all()
+    shift = (g["dQ"].double().sum((0, 2)) + g["dK"].double().sum((0, 2)) +
+             g["dmu"].double().sum(1))
+    sscale = g["dQ"].double().abs().sum((0, 2)) + g["dmu"].double().abs().sum(1)
+    err_shift = float((shift.abs() / sscale).max())
+    # dV is stored in bf16: each element carries up to 2^-9 of itself, so the
+    # sum over positions is bounded by 2^-9 sum_j |dV_j| (checked with 2^-8)
+    dV = g["dV"].double()
+    vsum = dV.sum(2)
+    # d_i = gamma^Q_i . Z(_i) + eps from the library's own responsibilities
+    gq, _ = api.responsibilities(dev["Q"], dev["mu"], dev["log_sigma2"], dev["log_pi"])
+    gk, _ = api.responsibilities(dev["K"], dev["mu"], dev["log_sigma2"], dev["log_pi"])
+    gk = gk.double()
+    z = torch.cumsum(gk, dim=2) if w.causal else gk.sum(2, keepdim=True)
+    d = (gq.double() * z).sum(-1) + w.eps
+    del gq, gk, z
+    osum = (dOd.double() * (1.0 - w.eps / d)[..., None]).sum(2)
+    bound = 2.0 ** -8 * dV.abs().sum(2) + 1e-4 * dOd.double().abs().sum(2)
+    err_v = float(((vsum - osum).abs() / bound).max())
+    print("%s: sum dlog_pi %.2e  shift %.2e  sum dV / bound %.2f" % (
+        wname, float((dlpi.sum(-1).abs() / scale).max()), err_shift, err_v))
+    assert err_shift <= 1e-3
+    assert err_v <= 1.0
