@@ -161,3 +161,22 @@ def test_prefill_then_decode_matches_causal_forward(dtype):
     e = rowwise_rel_err(o.float().cpu().numpy(), ref)
     print("prefill + decode %s: %.2e" % (dtype, e))
     assert e <= TOL[dtype]
+
+
+def test_prefix_state_full_size_sampled_heads():
+    """The carried state of the long-context prefix (B1 H32 N32768 d_r64 d_v128
+    K128, bf16) in one launch; heads 0 and 1 against the oracle's latent memory
+    (heads are independent)."""
+    w = inputs.WORKLOADS["long_bidir_bf16"]
+    gen = inputs.generate(w, 0)
+    dev = upload(gen)
+    S, z = api.prefix_state(dev["K"], dev["V"], dev["mu"], dev["log_sigma2"], dev["log_pi"])
+    torch.cuda.synchronize()
+    hs = slice(0, 2)
+    ref = oracle.forward(gen["Q"].f32[:, hs], gen["K"].f32[:, hs], gen["V"].f32[:, hs],
+                         gen["mu"][hs], gen["log_sigma2"][hs], gen["log_pi"][hs], w.eps, False,
+                         want_latent=True)
+    e_S = rowwise_rel_err(S[:, hs].cpu().numpy(), ref["vtilde"])
+    e_z = rowwise_rel_err(z[:, hs].cpu().numpy(), ref["z"])
+    print("prefix full size: S %.2e  z %.2e" % (e_S, e_z))
+    assert e_S <= TOL["bf16"] and e_z <= TOL["bf16"]
