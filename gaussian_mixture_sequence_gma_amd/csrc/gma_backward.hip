@@ -1,7 +1,7 @@
-// Backward of the bidirectional forward ("Gaussian Mixture Attention:
-// Linear-Time Sequence Mixing via Probabilistic Latent Routing", "Gradient
-// structure": the score gradient of Eq. 18, chained to Q_X, K_X, V_X and the
-// mixture parameters).
+// Backward of the forward, bidirectional and causal ("Gaussian Mixture
+// Attention: Linear-Time Sequence Mixing via Probabilistic Latent Routing",
+// "Gradient structure": the score gradient of Eq. 18, chained to Q_X, K_X, V_X
+// and the mixture parameters).
 //
 // Per unit u = (b, h), with Gq, Gk the [N,K] responsibilities (Eq. 3):
 //   [V~ | Z]   = Gk^T [V | 1]                    (Eqs. 5-6)
@@ -18,8 +18,10 @@
 // Appending a column of ones to the right operand turns every normaliser and
 // every rank-one term into part of a product, so the whole pass is a chain of
 // batched fp32 products (MFMA 16x16x4 f32, split over the token dimension
-// where the product contracts it) and row-wise elementwise kernels.  The
-// responsibilities come from the forward's responsibility kernel.
+// where the product contracts it; one column tile per workgroup for widths up
+// to 144) and row-wise kernels.  Rows of the augmented operands are padded to
+// a multiple of four floats.  The responsibilities come from the
+// responsibility kernel of the forward path.
 //
 // Causal ("Causal GMA", Eq. 8b): the same chain per 64-token chunk, with the
 // prefix states of the earlier chunks ([V~ | Z] totals per chunk, exclusive
