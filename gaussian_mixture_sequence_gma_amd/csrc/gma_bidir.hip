@@ -107,6 +107,8 @@ __global__ void __launch_bounds__(256) gma_prologue_kernel(
 // the read-out's MFMA operand table: block dt (d tile, paired rows as in
 // pair_row when d_v >= 32), step p (32 components), lane (row, component
 // group), element; block d_v/16 holds rows Z_hi, Z_lo, 1 and zeros.
+// Thread j < DV * Kp / 8 sums column d = j % DV of the eight components
+// 8 (j / DV) .. + 7 (one 16-byte operand chunk); the next Kp threads sum Z.
 __global__ void __launch_bounds__(256) gma_reduce_kernel(const float* __restrict__ partial,
                                                          const float* __restrict__ partial_z,
                                                          int PS, int Kp, int DV,
@@ -117,22 +119,32 @@ __global__ void __launch_bounds__(256) gma_reduce_kernel(const float* __restrict
                                                          float* __restrict__ st_z, int K) {
   const int64_t bh = blockIdx.y;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  const int nv = Kp * DV;
+  const int nv = Kp * DV, nv8 = nv / 8;
   const int DVT = DV / 16, KS = Kp / 32;
   bf16* vb = vtab ? vtab + (size_t)bh * (DVT + 1) * KS * 512 : nullptr;
-  if (idx < nv) {
-    const float* p = partial + (size_t)bh * PS * nv + idx;
-    float s = 0.f;
-    for (int q = 0; q < PS; ++q) s += p[(size_t)q * nv];
-    vt[(size_t)bh * nv + idx] = s;
-    const int k = idx / DV, d = idx - k * DV;
-    if (st_v && k < K) st_v[((size_t)bh * K + k) * DV + d] = s;
+  if (idx < nv8) {
+    const int d = idx % DV, k0 = 8 * (idx / DV);
+    const float* p = partial + (size_t)bh * PS * nv + (size_t)k0 * DV + d;
+    float sum[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sum[e] = 0.f;
+    for (int q = 0; q < PS; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum[e] += p[(size_t)q * nv + e * DV];
+    bf16x8 pk;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int k = k0 + e;
+      vt[(size_t)bh * nv + (size_t)k * DV + d] = sum[e];
+      if (st_v && k < K) st_v[((size_t)bh * K + k) * DV + d] = sum[e];
+      pk[e] = to_bf16(sum[e]);
+    }
     if (vb) {
       const int t = DVT >= 2 ? pair_tile(d) : 0, r = DVT >= 2 ? pair_rowof(d) : d;
-      vb[((t * KS + (k >> 5)) * 64 + r + 16 * ((k & 31) >> 3)) * 8 + (k & 7)] = to_bf16(s);
+      st16(vb + ((t * KS + (k0 >> 5)) * 64 + r + 16 * ((k0 & 31) >> 3)) * 8, pk);
     }
-  } else if (idx < nv + Kp) {
-    const int k = idx - nv;
+  } else if (idx < nv8 + Kp) {
+    const int k = idx - nv8;
     const float* p = partial_z + (size_t)bh * PS * Kp + k;
     float s = 0.f;
     for (int q = 0; q < PS; ++q) s += p[(size_t)q * Kp];
@@ -1027,7 +1039,7 @@ static hipError_t run_bidir(const Plan& p, const Tensors& t, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  const int nred = C::Kp * C::DV + C::Kp;
+  const int nred = C::Kp * C::DV / 8 + C::Kp;
   if (g_launch_hook) g_launch_hook("gma_reduce", s, 1);
   hipLaunchKernelGGL(gma_reduce_kernel, dim3((nred + 255) / 256, (unsigned)p.BH), dim3(256), 0, s,
                      a.partial, a.partial_z, PS, C::Kp, C::DV,
