@@ -128,7 +128,8 @@ __global__ void __launch_bounds__(256) gma_decode_kernel(DecodeArgs a) {
   f32x4 st[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p)
-    st[p] = ld16<f32x4>(sv + (size_t)min(r0 + p * SR, K - 1) * DV + col);
+    st[p] = __builtin_nontemporal_load(
+        reinterpret_cast<const f32x4*>(sv + (size_t)min(r0 + p * SR, K - 1) * DV + col));
   float z0 = 0.f, z1 = 0.f;
   if (wave == 1) {
     if (lane < K) z0 = a.sz[(size_t)bh * K + lane];
@@ -214,7 +215,7 @@ __global__ void __launch_bounds__(256) gma_decode_kernel(DecodeArgs a) {
       const float gk = s_g[1][r], gq = s_g[0][r];
       const f32x4 s = st[p] + gk * vv;
       if (r < K) {
-        st16(sv + (size_t)r * DV + col, s);
+        __builtin_nontemporal_store(s, reinterpret_cast<f32x4*>(sv + (size_t)r * DV + col));
         num += gq * s;
       }
     }
