@@ -277,6 +277,20 @@ __device__ __forceinline__ bf16x8 tr_chunk_swz(const bf16* M, int tok0, int col0
 __device__ __forceinline__ void global_to_lds16(const void* gsrc, void* lds_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
 }
+// The same for data read once per call (streamed keys and values): the
+// non-temporal cache policy (aux bit 1).
+__device__ __forceinline__ void global_to_lds16_nt(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 2);
+}
+// 16-byte loads and stores of streamed data with the non-temporal policy.
+template <class T>
+__device__ __forceinline__ T ld16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const T*>(__builtin_assume_aligned(p, 16)));
+}
+template <class T>
+__device__ __forceinline__ void st16_nt(void* p, T v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<T*>(__builtin_assume_aligned(p, 16)));
+}
 __device__ __forceinline__ void wait_global_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 }  // namespace gma

@@ -138,10 +138,10 @@ gma_write2_kernel(BidirArgs a) {
         const int col = 32 * s + 8 * g;
         const bool ok = tok < a.N && col < C::DR;
         const size_t off = (size_t)(ok ? tok : 0) * C::DR + (ok ? col : 0);
-        const bf16x8 v = ld16<bf16x8>(xs + off);
+        const bf16x8 v = ld16_nt<bf16x8>(xs + off);
         xr[tt][s] = ok ? v : bf16x8{};
         if constexpr (XS) {
-          const bf16x8 vl = ld16<bf16x8>(xls + off);
+          const bf16x8 vl = ld16_nt<bf16x8>(xls + off);
           xl[tt][s] = ok ? vl : bf16x8{};
         }
       }
@@ -157,7 +157,7 @@ gma_write2_kernel(BidirArgs a) {
       const int lc = R::ROWCH >= 2 ? (pc ^ ((2 * row) & (R::ROWCH - 2))) : pc;
       int64_t tok = grp * 32 + row;
       if (tok >= a.N) tok = a.N - 1;                       // rows past the end get Gamma = 0
-      global_to_lds16(vs + (size_t)tok * C::DV + lc * 8, myv + b * R::VT + j * 512);
+      global_to_lds16_nt(vs + (size_t)tok * C::DV + lc * 8, myv + b * R::VT + j * 512);
     }
   };
 
