@@ -593,11 +593,11 @@ gma_causal2_kernel(CausalArgs a) {
       const int col = 32 * s + 8 * g;
       const bool ok = tok < t_end && col < C::DR;
       const size_t off = (size_t)(ok ? tok : t_begin) * C::DR + (ok ? col : 0);
-      const bf16x8 q = ld16<bf16x8>(qs + off), kk = ld16<bf16x8>(ks + off);
+      const bf16x8 q = ld16_nt<bf16x8>(qs + off), kk = ld16_nt<bf16x8>(ks + off);
       xq[s] = ok ? q : bf16x8{};
       xk[s] = ok ? kk : bf16x8{};
       if constexpr (XS) {
-        const bf16x8 ql = ld16<bf16x8>(qls + off), kl = ld16<bf16x8>(kls + off);
+        const bf16x8 ql = ld16_nt<bf16x8>(qls + off), kl = ld16_nt<bf16x8>(kls + off);
         xql[s] = ok ? ql : bf16x8{};
         xkl[s] = ok ? kl : bf16x8{};
       }
@@ -615,7 +615,7 @@ gma_causal2_kernel(CausalArgs a) {
         const int r = P / R::VROWCH, pc = P - r * R::VROWCH;
         const int lc = pc ^ ((2 * r) & (R::VROWCH - 2));
         const int rr = r < nv ? r : nv - 1;
-        global_to_lds16(vs + (size_t)(t0 + rr) * C::DV + lc * 8, &Vb[buf][round * 512]);
+        global_to_lds16_nt(vs + (size_t)(t0 + rr) * C::DV + lc * 8, &Vb[buf][round * 512]);
       }
     }
   };
