@@ -339,8 +339,18 @@ __global__ void __launch_bounds__(256) gma_split_sum_kernel(const float* __restr
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= M * N) return;
   const float* p = part + (size_t)u * ksplit * M * N + i;
+  const size_t st = (size_t)M * N;
   float s = 0.f;
-  for (int k = 0; k < ksplit; ++k) s += p[(size_t)k * M * N];
+  // eight splits' loads in flight before they are added, in split order
+  int k = 0;
+  for (; k + 8 <= ksplit; k += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = p[(size_t)(k + j) * st];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += v[j];
+  }
+  for (; k < ksplit; ++k) s += p[(size_t)k * st];
   C[(size_t)u * sC + (size_t)(i / N) * ldc + i % N] = s;
 }
 
@@ -493,7 +503,24 @@ __global__ void __launch_bounds__(256) gma_bwd_chunk_scan_kernel(float* __restri
   if (e >= n) return;
   float* base = x + (size_t)blockIdx.y * nc * n + e;
   float run = 0.f;
-  for (int i = 0; i < nc; ++i) {
+  // eight records read before their exclusive sums overwrite them (each
+  // element belongs to this thread alone), summed in scan order
+  int i = 0;
+  for (; i + 8 <= nc; i += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = reverse ? nc - 1 - (i + j) : i + j;
+      v[j] = base[(size_t)c * n];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = reverse ? nc - 1 - (i + j) : i + j;
+      base[(size_t)c * n] = run;
+      run += v[j];
+    }
+  }
+  for (; i < nc; ++i) {
     const int c = reverse ? nc - 1 - i : i;
     const float v = base[(size_t)c * n];
     base[(size_t)c * n] = run;

@@ -128,7 +128,20 @@ __global__ void __launch_bounds__(256) gma_reduce_kernel(const float* __restrict
     float sum[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) sum[e] = 0.f;
-    for (int q = 0; q < PS; ++q)
+    // four partial slots' loads in flight before they are added, in slot order
+    int q = 0;
+    for (; q + 4 <= PS; q += 4) {
+      float v[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[u][e] = p[(size_t)(q + u) * nv + e * DV];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum[e] += v[u][e];
+    }
+    for (; q < PS; ++q)
 #pragma unroll
       for (int e = 0; e < 8; ++e) sum[e] += p[(size_t)q * nv + e * DV];
     bf16x8 pk;
@@ -147,7 +160,15 @@ __global__ void __launch_bounds__(256) gma_reduce_kernel(const float* __restrict
     const int k = idx - nv8;
     const float* p = partial_z + (size_t)bh * PS * Kp + k;
     float s = 0.f;
-    for (int q = 0; q < PS; ++q) s += p[(size_t)q * Kp];
+    int q = 0;
+    for (; q + 8 <= PS; q += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = p[(size_t)(q + u) * Kp];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; q < PS; ++q) s += p[(size_t)q * Kp];
     z[(size_t)bh * Kp + k] = s;
     if (st_z && k < K) st_z[(size_t)bh * K + k] = s;
     if (vb) {
@@ -1379,13 +1400,30 @@ __global__ void __launch_bounds__(256) gma_usage_reduce_kernel(
   for (int k = t; k < K; k += 256) {
     double gs = 0.0;
     int64_t n = 0, hc = 0;
-    for (int64_t b = 0; b < B; ++b)
-      for (int sp = 0; sp < S; ++sp) {
-        const float* base = diag + ((size_t)(b * H + h) * S + sp) * W;
-        gs += base[k];
-        n += (int64_t)base[Kp + k];
-        hc += (int64_t)base[2 * Kp + k];
+    for (int64_t b = 0; b < B; ++b) {
+      const float* row = diag + (size_t)(b * H + h) * S * W + k;
+      // four workgroups' records loaded before they are added, in order
+      int sp = 0;
+      for (; sp + 4 <= S; sp += 4) {
+        float v[4][3];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int c = 0; c < 3; ++c) v[u][c] = row[(size_t)(sp + u) * W + c * Kp];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          gs += v[u][0];
+          n += (int64_t)v[u][1];
+          hc += (int64_t)v[u][2];
+        }
       }
+      for (; sp < S; ++sp) {
+        const float* base = row + (size_t)sp * W;
+        gs += base[0];
+        n += (int64_t)base[Kp];
+        hc += (int64_t)base[2 * Kp];
+      }
+    }
     if (counts) counts[(size_t)h * K + k] = (int32_t)hc;
     if (mean_gamma) mean_gamma[(size_t)h * K + k] = (float)(gs * inv);
     if (util) util[(size_t)h * K + k] = (float)((double)n * inv);

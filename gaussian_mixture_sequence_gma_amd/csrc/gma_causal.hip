@@ -45,6 +45,30 @@ struct CausalArgs {
   const void* k_lo;
 };
 
+// out[s] = sum_{s' < s} in[s'] over n terms at stride st, summed in order.
+// The loads of eight terms are issued before their sums are stored: the trip
+// count is a run-time value, so otherwise every add waits for its own load.
+__device__ __forceinline__ void exclusive_sum_strided(const float* __restrict__ in,
+                                                      float* __restrict__ out, int n,
+                                                      size_t st) {
+  float acc = 0.f;
+  int s = 0;
+  for (; s + 8 <= n; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = in[(size_t)(s + u) * st];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      out[(size_t)(s + u) * st] = acc;
+      acc += v[u];
+    }
+  }
+  for (; s < n; ++s) {
+    out[(size_t)s * st] = acc;
+    acc += in[(size_t)s * st];
+  }
+}
+
 // Exclusive prefix over spans, fixed order: carry[s] = sum_{s' < s} state[s'].
 __global__ void __launch_bounds__(256) gma_span_scan_kernel(const float* __restrict__ state,
                                                             const float* __restrict__ state_z,
@@ -56,18 +80,10 @@ __global__ void __launch_bounds__(256) gma_span_scan_kernel(const float* __restr
   const int nv = Kp * DV;
   if (idx < nv) {
     const size_t base = (size_t)bh * nspan * nv + idx;
-    float acc = 0.f;
-    for (int s = 0; s < nspan; ++s) {
-      carry[base + (size_t)s * nv] = acc;
-      acc += state[base + (size_t)s * nv];
-    }
+    exclusive_sum_strided(state + base, carry + base, nspan, (size_t)nv);
   } else if (idx < nv + Kp) {
     const size_t base = (size_t)bh * nspan * Kp + (idx - nv);
-    float acc = 0.f;
-    for (int s = 0; s < nspan; ++s) {
-      carry_z[base + (size_t)s * Kp] = acc;
-      acc += state_z[base + (size_t)s * Kp];
-    }
+    exclusive_sum_strided(state_z + base, carry_z + base, nspan, (size_t)Kp);
   }
 }
 
