@@ -1391,6 +1391,7 @@ __global__ void __launch_bounds__(256) gma_usage_reduce_kernel(
     int32_t* __restrict__ counts, float* __restrict__ mean_gamma, float* __restrict__ util,
     float* __restrict__ head_stats) {
   __shared__ double r_ent[256];
+  __shared__ double r_tok[256];
   __shared__ int r_used[256];
   const int h = blockIdx.x, t = threadIdx.x;
   const int W = 3 * Kp + 4;
@@ -1433,21 +1434,27 @@ __global__ void __launch_bounds__(256) gma_usage_reduce_kernel(
       ++used;
     }
   }
+  // the workgroups' token-entropy sums: thread t takes records t, t + 256, ...
+  // in order, then the same fixed-order tree as the other two sums
+  double te = 0.0;
+  for (int64_t r = t; r < B * S; r += 256) {
+    const int64_t b = r / S, sp = r - b * S;
+    te += diag[((size_t)(b * H + h) * S + sp) * W + 3 * Kp];
+  }
   r_ent[t] = ue;
   r_used[t] = used;
+  r_tok[t] = te;
   __syncthreads();
   for (int w = 128; w >= 1; w >>= 1) {
     if (t < w) {
       r_ent[t] += r_ent[t + w];
       r_used[t] += r_used[t + w];
+      r_tok[t] += r_tok[t + w];
     }
     __syncthreads();
   }
   if (t == 0 && head_stats) {
-    double te = 0.0;
-    for (int64_t b = 0; b < B; ++b)
-      for (int sp = 0; sp < S; ++sp) te += diag[((size_t)(b * H + h) * S + sp) * W + 3 * Kp];
-    head_stats[(size_t)h * 3 + 0] = (float)(-te * inv);
+    head_stats[(size_t)h * 3 + 0] = (float)(-r_tok[0] * inv);
     head_stats[(size_t)h * 3 + 1] = K > 1 ? (float)(r_ent[0] / log((double)K)) : 0.f;
     head_stats[(size_t)h * 3 + 2] = (float)r_used[0];
   }
