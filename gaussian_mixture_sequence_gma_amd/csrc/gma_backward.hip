@@ -421,6 +421,46 @@ __global__ void __launch_bounds__(256) gma_bwd_ab_kernel(float* __restrict__ nd,
   }
 }
 
+// The same with one 16-lane row per token (four tokens per wave, no loop) for
+// d_v <= 64 M: lane j holds elements 4 j + 64 m as 16-byte vectors.  Every
+// lane reads d - eps before lane 0 overwrites it (the row's lanes run in
+// lockstep and the store follows the read).
+template <class T, int M>
+__global__ void __launch_bounds__(256) gma_bwd_ab16_kernel(float* __restrict__ nd,
+                                                           const void* __restrict__ dO, int dv,
+                                                           int ld, float eps, int64_t rows) {
+  const int j = threadIdx.x & 15;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (row >= rows) return;     // whole 16-lane rows leave together
+  float* r = nd + (size_t)row * ld;
+  const T* o = static_cast<const T*>(dO) + (size_t)row * dv;
+  const float den = r[dv] + eps;
+  f32x4 g[M], n[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int c = 4 * j + 64 * m;
+    if (c < dv) {
+      g[m] = load4x(o + c);
+      n[m] = ld16<f32x4>(r + c);
+    } else {
+      g[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+      n[m] = g[m];
+    }
+  }
+  float dot = 0.f;
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+    dot += g[m][0] * n[m][0] + g[m][1] * n[m][1] + g[m][2] * n[m][2] + g[m][3] * n[m][3];
+  dot = row16_sum(dot);
+  const float inv = 1.f / den;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int c = 4 * j + 64 * m;
+    if (c < dv) st16(r + c, g[m] * inv);
+  }
+  if (j == 0) r[dv] = -dot * inv * inv;
+}
+
 // One wave per token: dS = G (dG - sum_l G_l dG_l), in place on dG.
 __global__ void __launch_bounds__(256) gma_bwd_softmax_kernel(const float* __restrict__ G,
                                                               float* __restrict__ dG, int K,
@@ -434,6 +474,42 @@ __global__ void __launch_bounds__(256) gma_bwd_softmax_kernel(const float* __res
   for (int k = lane; k < K; k += 64) s += gr[k] * dr[k];
   s = groups_sum(row16_sum(s));
   for (int k = lane; k < K; k += 64) dr[k] = gr[k] * (dr[k] - s);
+  }
+}
+
+// The same for K a multiple of 4 (rows 16-byte aligned), K <= 64 M: one
+// 16-lane row per token, four tokens per wave, no loop; lane j holds elements
+// 4 j + 64 m (m < M) as 16-byte vectors, so every load of a token is issued
+// before its sum is formed.
+template <int M>
+__global__ void __launch_bounds__(256) gma_bwd_softmax16_kernel(const float* __restrict__ G,
+                                                                float* __restrict__ dG, int K,
+                                                                int64_t rows) {
+  const int j = threadIdx.x & 15;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (row >= rows) return;     // whole 16-lane rows leave together
+  const float* gr = G + (size_t)row * K;
+  float* dr = dG + (size_t)row * K;
+  f32x4 g[M], d[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int c = 4 * j + 64 * m;
+    if (c < K) {
+      g[m] = ld16<f32x4>(gr + c);
+      d[m] = ld16<f32x4>(dr + c);
+    } else {
+      g[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+      d[m] = g[m];
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int m = 0; m < M; ++m) s += g[m][0] * d[m][0] + g[m][1] * d[m][1] + g[m][2] * d[m][2] + g[m][3] * d[m][3];
+  s = row16_sum(s);
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int c = 4 * j + 64 * m;
+    if (c < K) st16(dr + c, g[m] * (d[m] - s));
   }
 }
 
@@ -665,6 +741,19 @@ unsigned sblocks(int64_t n, int per) {
   return (unsigned)(b < 2048 ? b : 2048);
 }
 
+static void launch_bwd_softmax(const float* G, float* dG, int K, int64_t rows, hipStream_t s) {
+  if (K % 4 == 0 && K <= 128) {
+    const dim3 grid((unsigned)((rows + 15) / 16));
+    if (K <= 64)
+      hipLaunchKernelGGL(gma_bwd_softmax16_kernel<1>, grid, dim3(256), 0, s, G, dG, K, rows);
+    else
+      hipLaunchKernelGGL(gma_bwd_softmax16_kernel<2>, grid, dim3(256), 0, s, G, dG, K, rows);
+    return;
+  }
+  hipLaunchKernelGGL(gma_bwd_softmax_kernel, dim3(sblocks(rows, 4)), dim3(256), 0, s, G, dG, K,
+                     rows);
+}
+
 template <class T>
 hipError_t run_backward(const Plan& pp, const Tensors& t0, const BwdTensors& gt, bool causal,
                         int64_t N0, hipStream_t s) {
@@ -772,8 +861,18 @@ hipError_t run_backward(const Plan& pp, const Tensors& t0, const BwdTensors& gt,
     if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 0);
   }
   if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 1);
-  hipLaunchKernelGGL(gma_bwd_ab_kernel<T>, dim3(sblocks(rows, 4)), dim3(256), 0, s, nd, dO, dv,
-                     l1, t.eps, rows);
+  if (dv % 4 == 0 && dv <= 128) {
+    const dim3 g16((unsigned)((rows + 15) / 16));
+    if (dv <= 64)
+      hipLaunchKernelGGL((gma_bwd_ab16_kernel<T, 1>), g16, dim3(256), 0, s, nd, dO, dv, l1, t.eps,
+                         rows);
+    else
+      hipLaunchKernelGGL((gma_bwd_ab16_kernel<T, 2>), g16, dim3(256), 0, s, nd, dO, dv, l1, t.eps,
+                         rows);
+  } else {
+    hipLaunchKernelGGL(gma_bwd_ab_kernel<T>, dim3(sblocks(rows, 4)), dim3(256), 0, s, nd, dO, dv,
+                       l1, t.eps, rows);
+  }
   GMA_CHECK(hipGetLastError());
   if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 0);
   if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 1);
@@ -825,10 +924,8 @@ hipError_t run_backward(const Plan& pp, const Tensors& t0, const BwdTensors& gt,
   }
   if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 0);
   if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 1);
-  hipLaunchKernelGGL(gma_bwd_softmax_kernel, dim3(sblocks(rows, 4)), dim3(256), 0, s, Gq, dGq, K,
-                     rows);
-  hipLaunchKernelGGL(gma_bwd_softmax_kernel, dim3(sblocks(rows, 4)), dim3(256), 0, s, Gk, dGk, K,
-                     rows);
+  launch_bwd_softmax(Gq, dGq, K, rows, s);
+  launch_bwd_softmax(Gk, dGk, K, rows, s);
   hipLaunchKernelGGL(gma_bwd_store_kernel<T>, dim3(sblocks(rows * dv / 4, 256)), dim3(256), 0, s,
                      dvf, dv, rows, Np, N0, gt.dV);
   GMA_CHECK(hipGetLastError());
