@@ -738,7 +738,7 @@ unsigned blocks(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
 // striding kernels: at most eight workgroups per compute unit
 unsigned sblocks(int64_t n, int per) {
   const int64_t b = (n + per - 1) / per;
-  return (unsigned)(b < 2048 ? b : 2048);
+  return (unsigned)(b < 16384 ? b : 16384);
 }
 
 static void launch_bwd_softmax(const float* G, float* dG, int K, int64_t rows, hipStream_t s) {
