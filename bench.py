@@ -13,7 +13,8 @@ library records around each of its launches on the launch stream (per-kernel
 durations; the events add a few microseconds between launches, so that pass's
 step time is reported apart).  Unless --no-flush, a 512 MiB fill runs between
 steps, outside the timed events, so that no workload is served from the 256 MB
-Infinity Cache.
+Infinity Cache; each step then has its own event pair, and the median and the
+minimum of the K step times are reported beside the mean (config.step_ms_*).
 
 Roofline: the dominant kernel's algorithmic bytes (flops, for the MFMA-bound
 projection GEMM of the layer workload) per launch divided by its average
@@ -27,6 +28,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -322,7 +324,8 @@ def main():
     stream = torch.cuda.current_stream()
 
     def timed(k):
-        """Mean ms per step over k steps (event pairs on the launch stream)."""
+        """Mean ms per step over k steps (event pairs on the launch stream),
+        and the per-step times where each step has its own pair."""
         if flush_buf is None:
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
@@ -332,7 +335,7 @@ def main():
                 step()
             e1.record(stream)
             torch.cuda.synchronize()
-            return e0.elapsed_time(e1) / k
+            return e0.elapsed_time(e1) / k, []
         pairs = []
         torch.cuda.synchronize()
         for _ in range(k):
@@ -344,11 +347,12 @@ def main():
             e1.record(stream)
             pairs.append((e0, e1))
         torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in pairs) / k
+        per = [a.elapsed_time(b) for a, b in pairs]
+        return sum(per) / k, per
 
     # timed region 1: K steps as a user runs them -> ms_per_step and value
     binding.gma_timing_enable(False)
-    ms = timed(args.steps)
+    ms, per_step = timed(args.steps)
     value = w.tokens_heads / (ms * 1e-3)
     # timed region 2: the same K steps with a hipEvent pair around every launch
     # (recorded by the library on the launch stream) -> per-kernel durations;
@@ -356,7 +360,7 @@ def main():
     # region's step time is reported separately
     binding.gma_timing_collect()            # discard anything left over
     binding.gma_timing_enable(True)
-    ms_instrumented = timed(args.steps)
+    ms_instrumented = timed(args.steps)[0]
     binding.gma_timing_enable(False)
     kt = binding.gma_timing_collect()
 
@@ -397,6 +401,8 @@ def main():
            "kernel_timing": "second pass of the K steps with a hipEvent pair around each launch "
                             "(%.4f ms/step in that pass)" % ms_instrumented,
            "cache_flush": "512 MiB fill between timed steps" if args.flush else None,
+           "step_ms_median": statistics.median(per_step) if per_step else None,
+           "step_ms_min": min(per_step) if per_step else None,
            "step_hbm_frac": (step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS) if step_bytes else None}
     if w.d_model:
         cfg["d_model"] = w.d_model
