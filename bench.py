@@ -389,6 +389,8 @@ def main():
                     "unit": "GB/s", "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
                     "traffic": traffic, "mfma_busy": prof.get("mfma_busy"),
                     "alg_bytes_per_launch": dom_bytes}
+    # the counters' HBM bytes over the same measured duration
+    roofline["traffic_gbs"] = traffic / t_dom / 1e9 if traffic else None
     step_bytes = sum(kernel_bytes(k, w, s_r, s_v, s_out) for k in kernels)
 
     cpu = None
