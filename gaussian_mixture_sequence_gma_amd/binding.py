@@ -54,7 +54,7 @@ def load():
     P, S = ctypes.c_void_p, ctypes.c_size_t
     i32, f32 = ctypes.c_int, ctypes.c_float
     D = ctypes.POINTER(gma_dims)
-    lib.gma_validate.argtypes = [D, f32, i32]
+    lib.gma_validate.argtypes = [D, f32, i32, ctypes.POINTER(P), i32, S, S]
     lib.gma_forward_workspace_bytes.argtypes = [D, i32, ctypes.POINTER(S)]
     lib.gma_forward.argtypes = [P, P, P, P, P, P, f32, i32, P, D, P, P, P, S, P]
     lib.gma_layer_workspace_bytes.argtypes = [D, ctypes.c_int32, i32, ctypes.POINTER(S)]
@@ -128,8 +128,13 @@ def make_dims(B, H, N, d_r, d_v, K, dtype, chunk=0) -> gma_dims:
 
 # ---- C entry points ------------------------------------------------------------
 
-def gma_validate(dims: gma_dims, eps: float, causal: int) -> int:
-    return load().gma_validate(ctypes.byref(dims), float(eps), int(causal))
+def gma_validate(dims: gma_dims, eps: float, causal: int, ptrs=(), workspace_bytes: int = 0,
+                 workspace_needed: int = 0) -> int:
+    """Status of gma_validate (no exception): ptrs are tensors, ints or None."""
+    arr = (ctypes.c_void_p * max(len(ptrs), 1))(*[_ptr(x) for x in ptrs])
+    return load().gma_validate(ctypes.byref(dims), float(eps), int(causal),
+                               arr if ptrs else None, len(ptrs), int(workspace_bytes),
+                               int(workspace_needed))
 
 
 def gma_forward_workspace_bytes(dims: gma_dims, causal: int) -> int:

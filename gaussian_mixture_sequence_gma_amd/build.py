@@ -36,12 +36,15 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int | None = None) -> str:
-    """Compile every source and link libgma.so; always rebuilds."""
+def build(jobs: int | None = None, only: list | None = None) -> str:
+    """Compile every source (or, with `only`, just those, reusing the other
+    objects of an earlier build) and link libgma.so."""
     os.makedirs(OBJDIR, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
+    todo = SOURCES if not only else [s for s in SOURCES if s in only]
+    jobs = jobs or min(len(todo), os.cpu_count() or 1)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        list(ex.map(_compile, todo))
+    objs = [os.path.join(OBJDIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -54,6 +57,8 @@ def build(jobs: int | None = None) -> str:
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("-j", "--jobs", type=int, default=None)
+    ap.add_argument("--only", nargs="*", default=None,
+                    help="recompile only these sources (e.g. gma_api.hip)")
     args = ap.parse_args()
-    print(build(args.jobs))
+    print(build(args.jobs, args.only))
     sys.exit(0)

@@ -3,7 +3,6 @@
 #include <math.h>
 #include <string.h>
 
-#include <mutex>
 #include <string>
 #include <vector>
 
@@ -13,7 +12,7 @@
 
 namespace gma {
 
-launch_hook_t g_launch_hook = nullptr;
+thread_local launch_hook_t g_launch_hook = nullptr;
 
 namespace {
 
@@ -28,7 +27,9 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 bool supported_dim(int v) { return v == 16 || v == 32 || v == 64 || v == 128; }
 
-int check_dims(const gma_dims* d, float eps, int causal) {
+// scan: the call runs the causal forward's scan kernels (gma_forward,
+// gma_layer_forward, gma_validate), whose fp32 form has an LDS limit.
+int check_dims(const gma_dims* d, float eps, int causal, bool scan = true) {
   if (!d) return fail(GMA_ERR_INVALID_ARG, "dims is NULL");
   if (d->B < 1 || d->H < 1 || d->N < 1) return fail(GMA_ERR_INVALID_ARG, "B, H and N must be >= 1");
   if (d->d_r < 1 || d->d_v < 1 || d->K < 1)
@@ -46,6 +47,14 @@ int check_dims(const gma_dims* d, float eps, int causal) {
   const int64_t BH = d->B * d->H;
   if (BH > 65535) return fail(GMA_ERR_UNSUPPORTED, "B*H above 65535 is not supported");
   if (d->N > lim / (BH * 128)) return fail(GMA_ERR_UNSUPPORTED, "B*H*N*d too large");
+  if (causal && scan && d->dtype == GMA_F32) {
+    // the fp32 scan kernel keeps its tiles in LDS (K padded to a power-of-two
+    // number of 16-wide tiles, at least four)
+    int ct = (d->K + 15) / 16, ct2 = 4;
+    while (ct2 < ct) ct2 *= 2;
+    if (causal_lds_bytes(false, d->d_r, d->d_v, 16 * ct2) > kMaxLds)
+      return fail(GMA_ERR_UNSUPPORTED, "causal fp32 path: this d_r, d_v, K combination exceeds LDS");
+  }
   return GMA_OK;
 }
 
@@ -144,31 +153,33 @@ int make_plan(const gma_dims* d, int causal, bool fp32_compute, Plan& p) {
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
 
 // ---- timing ----------------------------------------------------------------
+// Per calling thread: each thread that enables timing records and collects
+// only the launches it makes itself.
 struct Pending {
   const char* tag;
   hipEvent_t start, stop;
 };
-std::mutex g_tmu;
-bool g_timing = false;
-std::vector<Pending> g_pending;
-Pending g_open{};
 struct Total {
   std::string name;
   int64_t launches;
   double ms;
 };
-std::vector<Total> g_totals;
+struct TimingState {
+  std::vector<Pending> pending;
+  Pending open{};
+};
+thread_local TimingState t_timing;
 
 void timing_hook(const char* tag, hipStream_t s, int begin) {
-  std::lock_guard<std::mutex> lk(g_tmu);
+  TimingState& ts = t_timing;
   if (begin) {
-    g_open.tag = tag;
-    hipEventCreate(&g_open.start);
-    hipEventCreate(&g_open.stop);
-    hipEventRecord(g_open.start, s);
+    ts.open.tag = tag;
+    hipEventCreate(&ts.open.start);
+    hipEventCreate(&ts.open.stop);
+    hipEventRecord(ts.open.start, s);
   } else {
-    hipEventRecord(g_open.stop, s);
-    g_pending.push_back(g_open);
+    hipEventRecord(ts.open.stop, s);
+    ts.pending.push_back(ts.open);
   }
 }
 
@@ -190,9 +201,20 @@ using namespace gma;
 
 extern "C" {
 
-int gma_validate(const gma_dims* d, float eps, int causal) {
+int gma_validate(const gma_dims* d, float eps, int causal, const void* const* ptrs, int nptrs,
+                 size_t workspace_bytes, size_t workspace_needed) {
   t_err.clear();
-  return check_dims(d, eps, causal);
+  int st = check_dims(d, eps, causal);
+  if (st != GMA_OK) return st;
+  if (nptrs < 0 || (nptrs > 0 && !ptrs))
+    return fail(GMA_ERR_INVALID_ARG, "pointer list is NULL or nptrs is negative");
+  for (int i = 0; i < nptrs; ++i) {
+    if (!ptrs[i]) return fail(GMA_ERR_INVALID_ARG, "pointer " + std::to_string(i) + " is NULL");
+    if (!aligned16(ptrs[i]))
+      return fail(GMA_ERR_INVALID_ARG, "pointer " + std::to_string(i) + " is not 16-byte aligned");
+  }
+  if (workspace_bytes < workspace_needed) return fail(GMA_ERR_WORKSPACE, "workspace too small");
+  return GMA_OK;
 }
 
 int gma_forward_workspace_bytes(const gma_dims* d, int causal, size_t* bytes) {
@@ -465,7 +487,7 @@ static int backward_plan(const gma_dims* d, int causal, Plan& p) {
 int gma_backward_workspace_bytes(const gma_dims* d, int causal, size_t* bytes) {
   t_err.clear();
   if (!bytes) return fail(GMA_ERR_INVALID_ARG, "bytes is NULL");
-  int st = check_dims(d, 0.f, causal);
+  int st = check_dims(d, 0.f, causal, false);
   if (st != GMA_OK) return st;
   Plan p;
   st = backward_plan(d, causal, p);
@@ -480,7 +502,7 @@ int gma_backward(const void* Q_X, const void* K_X, const void* V_X, const float*
                  float* dlog_sigma2, float* dlog_pi, void* workspace, size_t workspace_bytes,
                  void* stream) {
   t_err.clear();
-  int st = check_dims(d, eps, causal);
+  int st = check_dims(d, eps, causal, false);
   if (st != GMA_OK) return st;
   if (!Q_X || !K_X || !V_X || !mu || !log_sigma2 || !log_pi || !dO || !dQ || !dK || !dV ||
       !dmu || !dlog_sigma2 || !dlog_pi || !workspace)
@@ -554,7 +576,11 @@ int gma_decode_step(const void* q, const void* k, const void* v, const float* mu
                     float* state_z, void* out, const gma_dims* d, int32_t* assign_q,
                     int32_t* assign_k, void* stream) {
   t_err.clear();
-  int st = check_dims(d, eps, 1);
+  if (!d) return fail(GMA_ERR_INVALID_ARG, "dims is NULL");
+  gma_dims dd = *d;
+  dd.chunk = 0;           // a decode step has no chunk
+  d = &dd;
+  int st = check_dims(d, eps, 1, false);
   if (st != GMA_OK) return st;
   if (d->N != 1) return fail(GMA_ERR_INVALID_ARG, "a decode step takes N = 1 token per sequence");
   if (!q || !k || !v || !mu || !log_sigma2 || !log_pi || !state_v || !state_z || !out)
@@ -619,19 +645,14 @@ const char* gma_status_string(int status) {
 const char* gma_last_error(void) { return t_err.c_str(); }
 
 int gma_timing_enable(int enable) {
-  std::lock_guard<std::mutex> lk(g_tmu);
-  g_timing = enable != 0;
-  g_launch_hook = g_timing ? timing_hook : nullptr;
+  g_launch_hook = enable ? timing_hook : nullptr;
   return GMA_OK;
 }
 
 int gma_timing_collect(gma_kernel_time* out, int max, int* count) {
   t_err.clear();
   std::vector<Pending> pend;
-  {
-    std::lock_guard<std::mutex> lk(g_tmu);
-    pend.swap(g_pending);
-  }
+  pend.swap(t_timing.pending);
   std::vector<Total> totals;
   for (auto& pe : pend) {
     float ms = 0.f;

@@ -62,7 +62,8 @@ struct Tensors {
 // Launch helpers; each returns hipSuccess or the launch error.  `tag` names the
 // kernel for the timing facility.
 typedef void (*launch_hook_t)(const char* tag, hipStream_t s, int begin);
-extern launch_hook_t g_launch_hook;
+// Per calling thread (set by gma_timing_enable); null when timing is off.
+extern thread_local launch_hook_t g_launch_hook;
 
 hipError_t launch_prologue(const Plan& p, const Tensors& t, hipStream_t s);
 // Whether the bf16 kernels take split routing vectors (q_lo / k_lo) for this shape.

@@ -58,9 +58,15 @@ typedef struct gma_dims {
   int32_t chunk;
 } gma_dims;
 
-/* Host-only check of a shape, eps and variant; no pointer is examined.
- * Returns GMA_OK, GMA_ERR_INVALID_ARG or GMA_ERR_UNSUPPORTED. */
-int gma_validate(const gma_dims* d, float eps, int causal);
+/* Host-only check of a call's arguments, as the entry points make it before any
+ * launch: the shape, eps and variant (the same rules as gma_forward, including
+ * the fp32 causal LDS limit), then each of the nptrs pointers in ptrs (each
+ * must be non-NULL and 16-byte aligned; nptrs may be 0 and ptrs NULL), then
+ * workspace_bytes against workspace_needed (a *_workspace_bytes figure).  No
+ * pointer is dereferenced.  Returns GMA_OK, GMA_ERR_INVALID_ARG,
+ * GMA_ERR_UNSUPPORTED or GMA_ERR_WORKSPACE. */
+int gma_validate(const gma_dims* d, float eps, int causal, const void* const* ptrs, int nptrs,
+                 size_t workspace_bytes, size_t workspace_needed);
 
 /* Bytes of device workspace gma_forward needs for this shape and variant
  * (written to *bytes).  The same workspace also serves gma_responsibilities. */
@@ -252,11 +258,12 @@ const char* gma_status_string(int status);
 /* Message describing the last failure of a call made by this thread ("" if none). */
 const char* gma_last_error(void);
 
-/* Kernel timing (profiling aid).  While enabled, every kernel the library
- * launches is bracketed by two hipEvents recorded on the launch stream.
- * gma_timing_collect synchronises those events, accumulates per-kernel totals,
- * writes up to `max` entries and the number of distinct kernels to *count,
- * and resets the totals.  Not for use from several threads at once. */
+/* Kernel timing (profiling aid), per calling thread.  While a thread has it
+ * enabled, every kernel the library launches from that thread is bracketed by
+ * two hipEvents recorded on the launch stream.  gma_timing_collect synchronises
+ * the calling thread's events, accumulates per-kernel totals, writes up to
+ * `max` entries and the number of distinct kernels to *count, and resets them.
+ * Other threads' calls are neither timed nor affected. */
 typedef struct gma_kernel_time {
   char name[48];
   int64_t launches;

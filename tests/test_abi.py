@@ -50,6 +50,23 @@ def test_validate(kw, eps, causal, status):
         assert B.gma_last_error() != ""
 
 
+def test_validate_pointers_and_workspace():
+    d = _dims()
+    assert B.gma_validate(d, 1e-6, 0, ptrs=(1 << 20, 1 << 21), workspace_bytes=512,
+                          workspace_needed=512) == B.GMA_OK
+    assert B.gma_validate(d, 1e-6, 0, ptrs=(1 << 20, None)) == B.GMA_ERR_INVALID_ARG
+    assert "pointer 1" in B.gma_last_error()
+    assert B.gma_validate(d, 1e-6, 0, ptrs=((1 << 20) + 8,)) == B.GMA_ERR_INVALID_ARG
+    assert B.gma_validate(d, 1e-6, 0, workspace_bytes=100,
+                          workspace_needed=101) == B.GMA_ERR_WORKSPACE
+    # the shape is checked first
+    assert B.gma_validate(_dims(K=0), 1e-6, 0, ptrs=(None,)) == B.GMA_ERR_INVALID_ARG
+    # fp32 causal beyond the scan kernel's LDS budget: rejected by validation itself
+    big = B.make_dims(1, 1, 333, 64, 128, 128, B.GMA_F32)
+    assert B.gma_validate(big, 1e-6, 1) == B.GMA_ERR_UNSUPPORTED
+    assert B.gma_validate(big, 1e-6, 0) == B.GMA_OK
+
+
 def test_workspace_query_and_errors():
     n0 = B.gma_forward_workspace_bytes(_dims(), 0)
     n1 = B.gma_forward_workspace_bytes(_dims(N=100000), 0)
@@ -188,6 +205,10 @@ def test_decode_step_rejects_before_launch():
     assert _decode(out=None) == B.GMA_ERR_INVALID_ARG
     assert _decode(state_v=A16 + 4) == B.GMA_ERR_INVALID_ARG     # 16-byte aligned
     assert _decode(assign_k=A16 + 2) == B.GMA_ERR_INVALID_ARG
+    # the chunk length does not apply to a decode step: with chunk = 32 the
+    # call fails on the NULL output, not on the chunk
+    assert _decode(dims=_dims(N=1, chunk=32), out=None) == B.GMA_ERR_INVALID_ARG
+    assert "NULL" in B.gma_last_error()
     assert _decode(eps=float("nan")) == B.GMA_ERR_INVALID_ARG
     assert _decode(dims=_dims(N=1, K=129)) == B.GMA_ERR_UNSUPPORTED
     assert _decode(dims=_dims(N=1, d_v=48)) == B.GMA_ERR_UNSUPPORTED

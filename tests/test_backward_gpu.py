@@ -2,11 +2,29 @@
 structure" of "Gaussian Mixture Attention: Linear-Time Sequence Mixing via
 Probabilistic Latent Routing", Eq. 18) against oracle.backward.
 
-Metric: per gradient tensor, the normwise relative error ||g - r||_F / ||r||_F
-(elements of dS are differences of nearly equal terms, so an element-wise
-bound is meaningless).  Bound: 1e-4 for fp32 inputs (fp32 arithmetic on fp32
-MFMA); 2e-2 for bf16 inputs (responsibilities of the bf16 forward, bf16
-storage of dQ, dK, dV).  With K = 1 no gradient reaches the routing side and
+Metrics, per gradient tensor:
+  dQ, dK, dV ([B,H,N,d] rows): row-wise relative error, max over rows i of
+    ||g_i - r_i||_inf / max(||r_i||_inf, 1e-2 max_i ||r_i||_inf);
+  dmu, dlog_sigma2, dlog_pi ([H,K,d_r], [H,K]): element-wise relative error,
+    |g - r| / max(|r|, 1e-2 max |r|).
+The floor sits at 1e-2 of the tensor's largest row (element): a routing
+gradient is a difference of nearly equal terms (Eq. 18 subtracts the
+responsibility-weighted mean), so a row whose gradient nearly cancels carries an
+absolute error of the size of its terms, not of its value.  The floor does not
+hide a wrong row: one with error e (absolute) fails as soon as
+e > tol * 1e-2 * max row, i.e. any wrong row above 1e-6 (fp32) or 2e-4 (bf16)
+of the largest one.
+Bounds.  The value gradient dV: 1e-4 for fp32 inputs (fp32 arithmetic on fp32
+MFMA), 2e-2 for bf16 inputs (responsibilities of the bf16 forward, bf16
+storage).  The routing gradients (dQ, dK and the parameter elements) pass
+through the softmax Jacobian of Eq. 18, gamma (dGamma - gamma . dGamma), whose
+cancellation scales the responsibilities' own relative error (about 1e-5 on
+the fp32 path: its score gaps are off by up to 3e-5) by the ratio of the terms
+to the result; the parameter elements are also sums over all 2 B N queries and
+keys of terms of both signs (sum_k dlog_pi_k = 0 exactly).  Their bound is 1e-3
+for fp32 inputs (a ratio of up to 100) and 2e-2 for bf16 inputs.
+The normwise error ||g - r||_F / ||r||_F and the errors at a 1e-3 floor are
+printed beside them.  With K = 1 no gradient reaches the routing side and
 those tensors must be (near) zero.
 """
 import numpy as np
@@ -15,12 +33,40 @@ import torch
 
 import oracle
 from gaussian_mixture_sequence_gma_amd import api, inputs
-from tests.parity import upload
+from tests.parity import elementwise_rel_err, rowwise_rel_err, upload
 
 pytestmark = pytest.mark.gpu
 
-BWD_TOL = {"f32": 1e-4, "bf16": 2e-2}
+BWD_TOL = {"f32": 1e-4, "bf16": 2e-2}          # dV
+ROUTE_TOL = {"f32": 1e-3, "bf16": 2e-2}         # dQ, dK, dmu, dlog_sigma2, dlog_pi
 NAMES = ("dQ", "dK", "dV", "dmu", "dlog_sigma2", "dlog_pi")
+ROWS = ("dQ", "dK", "dV")
+FLOOR = 1e-2
+
+
+def _errors(got, ref, floor=FLOOR):
+    """Row-wise (dQ, dK, dV) or element-wise (parameters) error per gradient tensor."""
+    errs = {}
+    for k in NAMES:
+        if k in ROWS:
+            errs[k] = rowwise_rel_err(got[k], ref[k], floor=floor)
+        else:
+            errs[k] = elementwise_rel_err(got[k], ref[k], floor=floor)
+    return errs
+
+
+def _check(label, got, ref, dtype):
+    errs = _errors(got, ref)
+    fine = _errors(got, ref, 1e-3)
+    norm = {k: float(np.linalg.norm(got[k] - ref[k]) / np.linalg.norm(ref[k])) for k in NAMES}
+    print("%s: %s | floor 1e-3 %s | normwise %s" % (
+        label, "  ".join("%s %.2e" % kv for kv in errs.items()),
+        "  ".join("%.1e" % v for v in fine.values()),
+        "  ".join("%.1e" % v for v in norm.values())), flush=True)
+    for k in NAMES:
+        assert np.all(np.isfinite(got[k])), k
+        tol = BWD_TOL[dtype] if k == "dV" else ROUTE_TOL[dtype]
+        assert errs[k] <= tol, (k, errs[k])
 
 
 def _case(B, H, N, d_r, d_v, K, dtype, skew, seed=31, causal=False):
@@ -49,11 +95,7 @@ def _case(B, H, N, d_r, d_v, K, dtype, skew, seed=31, causal=False):
 ])
 def test_backward_matches_oracle(B, H, N, d_r, d_v, K, dtype, skew):
     got, ref = _case(B, H, N, d_r, d_v, K, dtype, skew)
-    errs = {k: np.linalg.norm(got[k] - ref[k]) / np.linalg.norm(ref[k]) for k in NAMES}
-    print("backward %s: %s" % ((B, H, N, d_r, d_v, K, dtype),
-                               "  ".join("%s %.2e" % kv for kv in errs.items())))
-    for k in NAMES:
-        assert errs[k] <= BWD_TOL[dtype], k
+    _check("backward %s" % ((B, H, N, d_r, d_v, K, dtype),), got, ref, dtype)
 
 
 def test_backward_single_component():
@@ -74,11 +116,7 @@ def test_backward_single_component():
 ])
 def test_causal_backward_matches_oracle(B, H, N, d_r, d_v, K, dtype, skew):
     got, ref = _case(B, H, N, d_r, d_v, K, dtype, skew, causal=True)
-    errs = {k: np.linalg.norm(got[k] - ref[k]) / np.linalg.norm(ref[k]) for k in NAMES}
-    print("causal backward %s: %s" % ((B, H, N, d_r, d_v, K, dtype),
-                                      "  ".join("%s %.2e" % kv for kv in errs.items())))
-    for k in NAMES:
-        assert errs[k] <= BWD_TOL[dtype], k
+    _check("causal backward %s" % ((B, H, N, d_r, d_v, K, dtype),), got, ref, dtype)
 
 
 def test_causal_backward_single_token():
@@ -91,6 +129,30 @@ def test_causal_backward_single_token():
         assert np.abs(got[k] - ref[k]).max() <= 1e-5, k
 
 
+@pytest.mark.parametrize("wname,heads", [("long_bidir_bf16", 1), ("lm_causal_bf16", 2)])
+def test_backward_full_shape_slice(wname, heads):
+    """The benchmark workloads at their full length N, on a slice of units
+    (batch 0, heads [0, heads)): units are independent, and the parameter
+    gradients of the slice are its own sums.  The inputs are the full
+    workload's arrays, sliced; dO is standard normal, stored in the input dtype."""
+    w = inputs.WORKLOADS[wname]
+    gen = inputs.generate(w, 0)
+    hs = slice(0, heads)
+    Q, K, V = (np.ascontiguousarray(gen[k].f32[0:1, hs]) for k in ("Q", "K", "V"))
+    mu, ls2, lpi = (np.ascontiguousarray(gen[k][hs]) for k in ("mu", "log_sigma2", "log_pi"))
+    rng = np.random.default_rng(11)
+    dO = inputs._store(rng.standard_normal((1, heads, w.N, w.d_v), dtype=np.float32), w.dtype)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = {k: torch.from_numpy(a).to("cuda").to(tdt) for k, a in (("Q", Q), ("K", K), ("V", V))}
+    par = {k: torch.from_numpy(a).to("cuda") for k, a in (("mu", mu), ("ls2", ls2), ("lpi", lpi))}
+    g = api.backward(dev["Q"], dev["K"], dev["V"], par["mu"], par["ls2"], par["lpi"],
+                     api.host_tensor_to_device(dO, "cuda"), w.eps, w.causal)
+    torch.cuda.synchronize()
+    got = {k: g[k].float().cpu().numpy().astype(np.float64) for k in NAMES}
+    ref = oracle.backward(Q, K, V, mu, ls2, lpi, w.eps, dO.f32, w.causal)
+    _check("%s slice B1 H%d N%d" % (wname, heads, w.N), got, ref, w.dtype)
+
+
 @pytest.mark.parametrize("wname", ["long_bidir_bf16", "lm_causal_bf16"])
 def test_backward_full_size_invariants(wname):
     """The workloads as the benchmark runs them (B1 H32 N32768 K128
@@ -99,7 +161,8 @@ def test_backward_full_size_invariants(wname):
     (sum_k dlog_pi = 0 per head); the scores depend on x - mu only (the
     gradients of a common shift of routing vectors and means cancel); and the
     value gradients sum to sum_i dO_i (1 - eps / d_i), d_i = gamma^Q_i . Z(_i) +
-    eps, to within the bf16 rounding of dV."""
+    eps (d_i from the oracle's responsibilities), to within the bf16 rounding of
+    dV."""
     w = inputs.WORKLOADS[wname]
     gen = inputs.generate(w, 0)
     dev = upload(gen)
@@ -119,13 +182,18 @@ def test_backward_full_size_invariants(wname):
     # sum over positions is bounded by 2^-9 sum_j |dV_j| (checked with 2^-8)
     dV = g["dV"].double()
     vsum = dV.sum(2)
-    # d_i = gamma^Q_i . Z(_i) + eps from the library's own responsibilities
-    gq, _ = api.responsibilities(dev["Q"], dev["mu"], dev["log_sigma2"], dev["log_pi"])
-    gk, _ = api.responsibilities(dev["K"], dev["mu"], dev["log_sigma2"], dev["log_pi"])
-    gk = gk.double()
-    z = torch.cumsum(gk, dim=2) if w.causal else gk.sum(2, keepdim=True)
-    d = (gq.double() * z).sum(-1) + w.eps
-    del gq, gk, z
+    # d_i = gamma^Q_i . Z(_i) + eps from the oracle's responsibilities (fp64),
+    # one head at a time
+    d = torch.empty((w.B, w.H, w.N), dtype=torch.float64)
+    for b in range(w.B):
+        for h in range(w.H):
+            hs = slice(h, h + 1)
+            par = (gen["mu"][hs], gen["log_sigma2"][hs], gen["log_pi"][hs])
+            gq = oracle.responsibilities(gen["Q"].f32[b, h][None], *par)["gamma"][0]
+            gk = oracle.responsibilities(gen["K"].f32[b, h][None], *par)["gamma"][0]
+            z = np.cumsum(gk, axis=0) if w.causal else gk.sum(0, keepdims=True)
+            d[b, h] = torch.from_numpy((gq * z).sum(-1) + w.eps)
+    d = d.to(dOd.device)
     osum = (dOd.double() * (1.0 - w.eps / d)[..., None]).sum(2)
     bound = 2.0 ** -8 * dV.abs().sum(2) + 1e-4 * dOd.double().abs().sum(2)
     err_v = float(((vsum - osum).abs() / bound).max())

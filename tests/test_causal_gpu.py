@@ -63,8 +63,9 @@ def test_causal_head_dims(dtype, d_r, d_v, K):
     if dtype == "f32" and K > 64 and d_v == 128:
         from gaussian_mixture_sequence_gma_amd import binding as B
         dims = B.make_dims(1, 1, 333, d_r, d_v, K, B.GMA_F32)
-        assert B.gma_validate(dims, 1e-6, 1) == B.GMA_OK      # a valid shape ...
-        with pytest.raises(B.GmaError) as ei:                 # ... outside the fp32 scan's LDS
+        # outside the fp32 scan's LDS: gma_validate and the workspace query agree
+        assert B.gma_validate(dims, 1e-6, 1) == B.GMA_ERR_UNSUPPORTED
+        with pytest.raises(B.GmaError) as ei:
             B.gma_forward_workspace_bytes(dims, 1)
         assert ei.value.status == B.GMA_ERR_UNSUPPORTED
         return

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from gaussian_mixture_sequence_gma_amd import api, inputs
-from tests.parity import TOL, run_and_compare, upload
+from tests.parity import TIE_DELTA, TOL, run_and_compare, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -33,6 +33,12 @@ def test_workload_full_compare(name):
 def test_long_context_bf16_sampled_rows():
     w = W["long_bidir_bf16"]
     run_and_compare(w, rows=inputs.sample_rows(w.N, 512, seed=5))
+
+
+def test_lm_shape_bidirectional_full():
+    """The language-model shape (B4 H12 N8192 d_r64 d_v64 K64, bf16) with the
+    other causal setting, compared in full."""
+    run_and_compare(W["lm_causal_bf16"].with_(causal=False))
 
 
 def test_lra_shape_in_bf16():
@@ -104,3 +110,37 @@ def test_responsibilities_match_oracle(dtype, K, d_r):
     np.testing.assert_allclose(g.sum(-1), 1.0, atol=1e-5)
     from tests.parity import check_assign
     check_assign(assign.cpu().numpy(), ref["assign"], gen["Q"].f32, gen, dtype, "resp")
+
+
+@pytest.mark.parametrize("name,dtype,d_r", [("long_bidir_bf16", "bf16", 64),
+                                            ("lm_causal_bf16", "bf16", 64),
+                                            ("long_bidir_bf16", "bf16", 128),
+                                            ("lra_bidir_f32", "f32", 64)])
+def test_score_gap_error_within_tie_band(name, dtype, d_r):
+    """The argmax tie band (an assignment mismatch is excused when the oracle's
+    own score gap is within TIE_DELTA) must exceed what the kernels' score
+    arithmetic can move a gap by.  The error of the gap between a token's two
+    largest oracle scores is read off the responsibilities: ln gamma_k1 -
+    ln gamma_k2 equals s_k1 - s_k2 (the log-sum-exp cancels).  Measured over
+    tokens whose two largest responsibilities are both above 1e-30, it must
+    stay below half the band."""
+    w = W[name].with_(B=1, H=4, N=4096, d_r=d_r, dtype=dtype, causal=False)
+    gen = inputs.generate(w, 2)
+    dev = upload(gen)
+    gamma, _ = api.responsibilities(dev["Q"], dev["mu"], dev["log_sigma2"], dev["log_pi"])
+    g = gamma.cpu().numpy().astype(np.float64)
+    ref = oracle.responsibilities(gen["Q"].f32, gen["mu"], gen["log_sigma2"], gen["log_pi"])
+    s = ref["score"]
+    top = np.argsort(-s, axis=-1)[..., :2]
+    k1, k2 = top[..., 0:1], top[..., 1:2]
+    g1 = np.take_along_axis(g, k1, -1)[..., 0]
+    g2 = np.take_along_axis(g, k2, -1)[..., 0]
+    ok = (g1 > 1e-30) & (g2 > 1e-30)
+    gap_ref = (np.take_along_axis(s, k1, -1) - np.take_along_axis(s, k2, -1))[..., 0]
+    with np.errstate(divide="ignore"):
+        gap_gpu = np.log(g1) - np.log(g2)
+    err = np.abs(gap_gpu - gap_ref)[ok]
+    print("%s d_r=%d %s: score-gap error max %.2e (p99.9 %.2e) over %d tokens; band %.0e"
+          % (name, d_r, dtype, err.max(), np.quantile(err, 0.999), err.size, TIE_DELTA[dtype]))
+    assert ok.mean() > 0.5
+    assert err.max() <= 0.5 * TIE_DELTA[dtype]
