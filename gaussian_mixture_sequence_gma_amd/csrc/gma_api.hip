@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include <string>
 #include <vector>
 
@@ -264,6 +266,62 @@ int gma_forward(const void* Q_X, const void* K_X, const void* V_X, const float* 
   t.eps = eps;
   t.ws = static_cast<char*>(workspace);
   return forward_impl(p, t, causal, static_cast<hipStream_t>(stream));
+}
+
+// ---- the workspace of gma_forward_noalloc ------------------------------------
+// A file-scope device array: each GPU the library runs on holds its own copy.
+// In host code `scratch` is only a host-side stand-in for the symbol; its
+// device address (per device) comes from hipGetSymbolAddress and is the only
+// form ever passed to a kernel.
+static __device__ __attribute__((aligned(256))) char scratch[GMA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up once per device (with
+// that device current) and kept.
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GMA_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(GMA_ERR_UNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(GMA_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return GMA_OK;
+}
+}  // namespace
+
+int gma_forward_noalloc(const void* Q_X, const void* K_X, const void* V_X, const float* mu,
+                        const float* log_sigma2, const float* log_pi, float eps, int causal,
+                        void* out, const gma_dims* d, int32_t* assign_q, int32_t* assign_k,
+                        void* stream) {
+  t_err.clear();
+  int st = check_dims(d, eps, causal);
+  if (st != GMA_OK) return st;
+  if (!Q_X || !K_X || !V_X || !mu || !log_sigma2 || !log_pi || !out)
+    return fail(GMA_ERR_INVALID_ARG, "a required pointer is NULL");
+  Plan p;
+  st = make_plan(d, causal, false, p);
+  if (st != GMA_OK) return st;
+  if (p.total > GMA_NOALLOC_SCRATCH_BYTES)
+    return fail(GMA_ERR_UNSUPPORTED, "this shape needs " + std::to_string(p.total) +
+                                         " bytes of workspace, above the " +
+                                         std::to_string((size_t)GMA_NOALLOC_SCRATCH_BYTES) +
+                                         " of the static scratch array");
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != GMA_OK) return st;
+  return gma_forward(Q_X, K_X, V_X, mu, log_sigma2, log_pi, eps, causal, out, d, assign_q,
+                     assign_k, ws, GMA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 // The layer's plan and where its projections sit.  Where the bf16 kernels

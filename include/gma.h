@@ -94,6 +94,23 @@ int gma_forward(const void* Q_X, const void* K_X, const void* V_X,
                 int32_t* assign_q, int32_t* assign_k,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* gma_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  It runs the same kernels as gma_forward, with the
+ * workspace taken from a static device array of GMA_NOALLOC_SCRATCH_BYTES
+ * that the library holds on each GPU it runs on until the process ends; the
+ * call allocates nothing.  Shapes whose gma_forward_workspace_bytes exceed
+ * that size return GMA_ERR_UNSUPPORTED before any launch.  Every call on a
+ * GPU shares that GPU's array (no part of it needs to start at zero: each
+ * kernel reads only what an earlier kernel of the same call wrote), so calls
+ * that overlap in time on one GPU (different streams, or threads) race and
+ * must be serialised by the caller.  Arguments and errors as gma_forward. */
+#define GMA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int gma_forward_noalloc(const void* Q_X, const void* K_X, const void* V_X,
+                        const float* mu, const float* log_sigma2, const float* log_pi,
+                        float eps, int causal, void* out, const gma_dims* d,
+                        int32_t* assign_q, int32_t* assign_k, void* stream);
+
 /* Bytes of device workspace gma_layer_forward needs. */
 int gma_layer_workspace_bytes(const gma_dims* d, int32_t d_model, int causal, size_t* bytes);
 
