@@ -22,7 +22,7 @@
 // its A/B coefficients held in VGPRs for the whole kernel) and token group
 // w / NG (NG of the four 16-token MFMA tiles).  Per-token max / sum over
 // components is finished across the NG waves through LDS.
-#include "gma_owner.h"
+#include "gma_team.h"
 
 namespace gma {
 
@@ -1035,9 +1035,23 @@ static hipError_t run_bidir(const Plan& p, const Tensors& t, hipStream_t s) {
   // sequence).  Split routing vectors (the
   // layer's projections) run only on the token-owner kernels.
   int PS = C::kBF ? p.S : p.S * C::TG;          // partial slots per sequence
-  if (split && !(Write2<C>::kOK && Read2<C>::kOK)) return hipErrorNotSupported;
+  if (split && !((WriteTeam<C>::kOK || Write2<C>::kOK) && Read2<C>::kOK))
+    return hipErrorNotSupported;
   if (g_launch_hook) g_launch_hook("gma_write", s, 1);
-  if constexpr (Write2<C>::kOK) {
+  if constexpr (WriteTeam<C>::kOK) {
+    // team write (K_pad 128 or 256): one eight-wave workgroup per compute
+    // unit, each team at least two 32-key groups
+    const int64_t g32 = (p.N + 31) / 32;
+    int64_t s2 = (256 + p.BH - 1) / p.BH;
+    const int64_t cap = (g32 + 2 * WriteTeam<C>::NT - 1) / (2 * WriteTeam<C>::NT);
+    if (s2 > cap) s2 = cap;
+    if (s2 > PS) s2 = PS;
+    if (s2 < 1) s2 = 1;
+    PS = (int)s2;
+    const dim3 g2((unsigned)s2, (unsigned)p.BH);
+    if (split) hipLaunchKernelGGL((gma_write_team_kernel<C, true>), g2, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((gma_write_team_kernel<C, false>), g2, dim3(512), 0, s, a);
+  } else if constexpr (Write2<C>::kOK) {
     const int64_t g32 = (p.N + 31) / 32;
     int64_t s2 = (256 * Write2<C>::WPE + p.BH - 1) / p.BH;
     const int64_t cap = (g32 + 3) / 4;
@@ -1502,7 +1516,8 @@ hipError_t launch_prologue(const Plan& p, const Tensors& t, hipStream_t s) {
 
 template <class C>
 static hipError_t split_query(const Plan&, const Tensors&, hipStream_t) {
-  return Read2<C>::kOK && Write2<C>::kOK ? hipSuccess : hipErrorNotSupported;
+  return Read2<C>::kOK && (WriteTeam<C>::kOK || Write2<C>::kOK) ? hipSuccess
+                                                                 : hipErrorNotSupported;
 }
 
 static hipError_t split_query_all(const Plan& p, const Tensors& t, hipStream_t s) {

@@ -20,7 +20,7 @@
 // The scan kernel uses four component groups (K padded to >= 64) so that all
 // four waves see every token of a chunk and the running state is split over
 // the waves by component.
-#include "gma_owner.h"
+#include "gma_team.h"
 
 namespace gma {
 
@@ -870,7 +870,8 @@ static hipError_t run_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   // 1. span totals through the latent-write kernel (one split per span)
   BidirArgs wa{};
   const bool split = t.k_lo != nullptr;
-  if (split && !(Causal2<C>::kOK && Write2<C>::kOK)) return hipErrorNotSupported;
+  if (split && !(Causal2<C>::kOK && (WriteTeam<C>::kOK || Write2<C>::kOK)))
+    return hipErrorNotSupported;
   wa.x = t.k;
   wa.x_lo = t.k_lo;
   wa.v = t.v;
@@ -889,7 +890,14 @@ static hipError_t run_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   // the token-owner write pays a per-workgroup set-up (its coefficient table):
   // use it for spans of at least four 32-token steps per wave, or eight where
   // it runs one wave per SIMD; one split per span
-  if (Write2<C>::kOK && (split || p.span_tiles >= (Write2<C>::WPE == 2 ? 4 : 16))) {
+  if (WriteTeam<C>::kOK && (split || p.span_tiles >= 4)) {
+    // team write: one split per span; a span is 2 span_tiles 32-key groups
+    wa.gpw = 2 * p.span_tiles;
+    if constexpr (WriteTeam<C>::kOK) {
+      if (split) hipLaunchKernelGGL((gma_write_team_kernel<C, true>), grid, dim3(512), 0, s, wa);
+      else hipLaunchKernelGGL((gma_write_team_kernel<C, false>), grid, dim3(512), 0, s, wa);
+    }
+  } else if (Write2<C>::kOK && (split || p.span_tiles >= (Write2<C>::WPE == 2 ? 4 : 16))) {
     wa.gpw = 2 * p.span_tiles;
     if constexpr (Write2<C>::kOK) {
       if (split) hipLaunchKernelGGL((gma_write2_kernel<C, true>), grid, dim3(256), 0, s, wa);
@@ -966,7 +974,8 @@ static hipError_t run_causal(const Plan& p, const Tensors& t, hipStream_t s) {
 
 template <class C>
 static hipError_t causal_split_query(const Plan&, const Tensors&, hipStream_t) {
-  return Causal2<C>::kOK && Write2<C>::kOK ? hipSuccess : hipErrorNotSupported;
+  return Causal2<C>::kOK && (WriteTeam<C>::kOK || Write2<C>::kOK) ? hipSuccess
+                                                                   : hipErrorNotSupported;
 }
 #define GMA_CSDV_CASES(CPW, DR)                                             \
   switch (p.DV) {                                                           \

@@ -293,4 +293,24 @@ __device__ __forceinline__ void st16_nt(void* p, T v) {
 }
 __device__ __forceinline__ void wait_global_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Raw buffer resource over [base, base + bytes) (bytes < 2^31): a load whose
+// byte offset reaches past the end returns zeros (and a copy to LDS writes
+// zeros), so tails need no clamping.  Offsets are 32-bit per lane, the base and
+// size live in scalar registers.
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+__device__ __forceinline__ buf_rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+// 16-byte load of streamed data (non-temporal policy).
+template <class T>
+__device__ __forceinline__ T buf_ld16_nt(buf_rsrc rs, uint32_t off) {
+  return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 2));
+}
+// 16 bytes per lane straight into LDS: lane l's bytes land at lds_base + 16 l.
+__device__ __forceinline__ void buf_to_lds16_nt(buf_rsrc rs, uint32_t off, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rs, (__attribute__((address_space(3))) void*)(lds_base), 16, off, 0, 0, 2);
+}
+
 }  // namespace gma

@@ -31,16 +31,49 @@ constexpr int kFI[6] = {0, 1, 0, 2, 2, 3};   // x^2_hi, x^2_lo, x^2_hi, x, x, x_
 template <bool XS>
 __device__ __forceinline__ void make_features(const bf16x8& xh, const bf16x8& xl,
                                               bf16x8 (&f)[NFX<XS>]) {
+  if constexpr (!XS) {
+    // Per pair of elements (one 32-bit word): widen both to fp32 (a shift and a
+    // mask), square, round the pair to bf16 in one conversion (x^2 hi), and
+    // take the remainders x^2 - hi with one bf16 dot product each (hi . (-1, 0)
+    // + x^2): exact, since x^2 has at most 16 significant bits and the
+    // remainder at most 8, so its top half is the exact bf16 (x^2 lo).
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const u32x4 p = __builtin_bit_cast(u32x4, xh);
+    // the bf16 pairs (-1, 0) and (0, -1), materialised in registers by a move
+    // the compiler cannot see through: as an inline constant of the dot
+    // product's packed-bf16 operand, -1.0 would be open to reinterpretation
+    unsigned k0, k1;
+    asm("v_mov_b32 %0, 0xbf80" : "=v"(k0));
+    asm("v_mov_b32 %0, 0xbf800000" : "=v"(k1));
+    const bf16x2 m0 = __builtin_bit_cast(bf16x2, k0);   // (-1, 0)
+    const bf16x2 m1 = __builtin_bit_cast(bf16x2, k1);   // (0, -1)
+    u32x4 hi, lo;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float x = XS ? from_bf16(xh[e]) + from_bf16(xl[e]) : from_bf16(xh[e]);
-    bf16 hh, ll;
-    split_bf16(x * x, hh, ll);
-    f[0][e] = hh;
-    f[1][e] = ll;
+    for (int j = 0; j < 4; ++j) {
+      const float a0 = __uint_as_float(p[j] << 16), a1 = __uint_as_float(p[j] & 0xffff0000u);
+      const float q0 = a0 * a0, q1 = a1 * a1;
+      const bf16x2 h = {(bf16)q0, (bf16)q1};      // one v_cvt_pk_bf16_f32 (RNE)
+      const float l0 = __builtin_amdgcn_fdot2_f32_bf16(h, m0, q0, false);
+      const float l1 = __builtin_amdgcn_fdot2_f32_bf16(h, m1, q1, false);
+      hi[j] = __builtin_bit_cast(unsigned, h);
+      lo[j] = __builtin_amdgcn_perm(__float_as_uint(l1), __float_as_uint(l0), 0x07060302u);
+    }
+    f[0] = __builtin_bit_cast(bf16x8, hi);
+    f[1] = __builtin_bit_cast(bf16x8, lo);
+    f[2] = xh;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = from_bf16(xh[e]) + from_bf16(xl[e]);
+      bf16 hh, ll;
+      split_bf16(x * x, hh, ll);
+      f[0][e] = hh;
+      f[1][e] = ll;
+    }
+    f[2] = xh;
+    f[3] = xl;
   }
-  f[2] = xh;
-  if constexpr (XS) f[3] = xl;
 }
 
 // Like tr_chunk_swz, but source lane s reads the 4-column block blk (a multiple
