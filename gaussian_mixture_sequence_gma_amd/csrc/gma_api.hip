@@ -42,21 +42,29 @@ int check_dims(const gma_dims* d, float eps, int causal, bool scan = true) {
   if (!(eps >= 0.f) || !isfinite(eps)) return fail(GMA_ERR_INVALID_ARG, "eps must be finite and >= 0");
   if (!supported_dim(d->d_r)) return fail(GMA_ERR_UNSUPPORTED, "d_r must be 16, 32, 64 or 128");
   if (!supported_dim(d->d_v)) return fail(GMA_ERR_UNSUPPORTED, "d_v must be 16, 32, 64 or 128");
-  if (d->K > 128) return fail(GMA_ERR_UNSUPPORTED, "K above 128 is not supported");
+  if (d->K > 256) return fail(GMA_ERR_UNSUPPORTED, "K above 256 is not supported");
   if (d->chunk != 0 && d->chunk != 64) return fail(GMA_ERR_UNSUPPORTED, "chunk must be 0 or 64");
   const int64_t lim = (int64_t)1 << 40;
   if (d->B > lim / d->H) return fail(GMA_ERR_UNSUPPORTED, "B*H too large");
   const int64_t BH = d->B * d->H;
   if (BH > 65535) return fail(GMA_ERR_UNSUPPORTED, "B*H above 65535 is not supported");
   if (d->N > lim / (BH * 128)) return fail(GMA_ERR_UNSUPPORTED, "B*H*N*d too large");
-  if (causal && scan && d->dtype == GMA_F32) {
-    // the fp32 scan kernel keeps its tiles in LDS (K padded to a power-of-two
-    // number of 16-wide tiles, at least four)
-    int ct = (d->K + 15) / 16, ct2 = 4;
-    while (ct2 < ct) ct2 *= 2;
-    if (causal_lds_bytes(false, d->d_r, d->d_v, 16 * ct2) > kMaxLds)
-      return fail(GMA_ERR_UNSUPPORTED, "causal fp32 path: this d_r, d_v, K combination exceeds LDS");
-  }
+  (void)scan;
+  return GMA_OK;
+}
+
+int make_plan(const gma_dims* d, int causal, bool fp32_compute, Plan& p);
+
+// The bidirectional plan at N rounded up to the 64-token chunk, on which the
+// causal product path runs; its chunk products are batched over B*H*N/64.
+int prod_plan(const gma_dims* d, bool fp32_compute, Plan& pp) {
+  gma_dims dp = *d;
+  dp.N = (d->N + 63) / 64 * 64;
+  int st = make_plan(&dp, 0, fp32_compute, pp);
+  if (st != GMA_OK) return st;
+  if (pp.BH * (dp.N / 64) > 65535)
+    return fail(GMA_ERR_UNSUPPORTED,
+                "causal product path: B*H*ceil(N/64) must be at most 65535 for this K, d_r, d_v");
   return GMA_OK;
 }
 
@@ -80,7 +88,8 @@ int make_plan(const gma_dims* d, int causal, bool fp32_compute, Plan& p) {
     case 1: p.CPW = 1; p.NG = 1; break;
     case 2: p.CPW = 2; p.NG = 1; break;
     case 4: p.CPW = 2; p.NG = 2; break;
-    default: p.CPW = 2; p.NG = 4; break;
+    case 8: p.CPW = 2; p.NG = 4; break;
+    default: p.CPW = 4; p.NG = 4; break;        // 16 tiles: K up to 256
   }
   if (causal) {
     // the scan kernel needs four component groups: K padded to at least 64
@@ -92,8 +101,17 @@ int make_plan(const gma_dims* d, int causal, bool fp32_compute, Plan& p) {
   const int cs = p.bf ? 32 : 16;
   p.DRP = p.DR < cs ? cs : p.DR;
   p.TG = 4 / p.NG;
-  if (causal && causal_lds_bytes(p.bf, p.DR, p.DV, p.Kp) > kMaxLds)
-    return fail(GMA_ERR_UNSUPPORTED, "causal fp32 path: this d_r, d_v, K combination exceeds LDS");
+  if (causal && causal_lds_bytes(p.bf, p.DR, p.DV, p.Kp) > kMaxLds) {
+    // the scan kernel's tiles do not fit in LDS: the causal forward runs as a
+    // chain of products over stored responsibilities, on the bidirectional
+    // plan at the length rounded up to the 64-token chunk
+    Plan pp;
+    int st2 = prod_plan(d, fp32_compute, pp);
+    if (st2 != GMA_OK) return st2;
+    p.prod = true;
+    p.total = prod_forward_workspace_bytes(pp, true, d->N);
+    return GMA_OK;
+  }
   p.tiles = (p.N + 63) / 64;
   // About two workgroups per compute unit (256 CUs) for each streaming kernel.
   int64_t want = (512 + p.BH - 1) / p.BH;
@@ -208,6 +226,9 @@ int gma_validate(const gma_dims* d, float eps, int causal, const void* const* pt
   t_err.clear();
   int st = check_dims(d, eps, causal);
   if (st != GMA_OK) return st;
+  Plan p;
+  st = make_plan(d, causal, false, p);
+  if (st != GMA_OK) return st;
   if (nptrs < 0 || (nptrs > 0 && !ptrs))
     return fail(GMA_ERR_INVALID_ARG, "pointer list is NULL or nptrs is negative");
   for (int i = 0; i < nptrs; ++i) {
@@ -229,7 +250,15 @@ int gma_forward_workspace_bytes(const gma_dims* d, int causal, size_t* bytes) {
   return GMA_OK;
 }
 
-static int forward_impl(const Plan& p, const Tensors& t, int causal, hipStream_t s) {
+static int forward_impl(const Plan& p, const Tensors& t, int causal, hipStream_t s,
+                        const gma_dims* d, bool fp32_compute) {
+  if (p.prod) {
+    Plan pp;
+    int st = prod_plan(d, fp32_compute, pp);
+    if (st != GMA_OK) return st;
+    return finish_launch(launch_prod_forward(pp, t, true, p.N, p.out_bf, s),
+                         "causal product-path launch");
+  }
   hipError_t e = launch_prologue(p, t, s);
   if (e != hipSuccess) return finish_launch(e, "prologue launch");
   e = causal ? launch_causal(p, t, s) : launch_bidir(p, t, s);
@@ -265,7 +294,7 @@ int gma_forward(const void* Q_X, const void* K_X, const void* V_X, const float* 
   t.assign_k = assign_k;
   t.eps = eps;
   t.ws = static_cast<char*>(workspace);
-  return forward_impl(p, t, causal, static_cast<hipStream_t>(stream));
+  return forward_impl(p, t, causal, static_cast<hipStream_t>(stream), d, false);
 }
 
 // ---- the workspace of gma_forward_noalloc ------------------------------------
@@ -342,7 +371,7 @@ static int layer_plan(const gma_dims* d, int32_t d_model, int causal, LayerPlan&
   if (d_model < 64 || d_model > 8192 || d_model % 64)
     return fail(GMA_ERR_UNSUPPORTED, "d_model must be a multiple of 64 in 64..8192");
   int st = make_plan(d, causal, false, L.p);
-  L.split = st == GMA_OK && (causal ? causal_split_ok(L.p) : bidir_split_ok(L.p));
+  L.split = st == GMA_OK && !L.p.prod && (causal ? causal_split_ok(L.p) : bidir_split_ok(L.p));
   if (!L.split) {
     st = make_plan(d, causal, true, L.p);
     if (st != GMA_OK) return st;
@@ -445,7 +474,7 @@ int gma_layer_forward(const void* X, const void* W_Q, const void* W_K, const voi
   t.assign_k = assign_k;
   t.eps = eps;
   t.ws = ws;
-  return forward_impl(p, t, causal, s);
+  return forward_impl(p, t, causal, s, d, !L.split);
 }
 
 int gma_responsibilities(const void* X_r, const float* mu, const float* log_sigma2,

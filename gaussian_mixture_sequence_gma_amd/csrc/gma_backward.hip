@@ -643,6 +643,38 @@ __global__ void __launch_bounds__(256) gma_bwd_param_grad_kernel(
   if (c == 0) dlpi[(size_t)h * K + k] = (float)r0;
 }
 
+// Forward on the product path: O = n / (d + eps) from the [n | d - eps] rows,
+// stored at the unpadded position in the output type.
+template <class T>
+__global__ void __launch_bounds__(256) gma_prod_out_kernel(const float* __restrict__ nd, int dv,
+                                                           int ld, float eps, int64_t rows,
+                                                           int64_t Np, int64_t N,
+                                                           void* __restrict__ out) {
+  const int q = dv / 4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < rows * q;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t row = i / q;
+    const int c = 4 * (int)(i - row * q);
+    const int64_t u = row / Np, r = row - u * Np;
+    if (r < N) {
+      const float* src = nd + (size_t)row * ld;
+      const float inv = 1.f / (src[dv] + eps);
+      store4x<T>(out, (size_t)(u * N + r) * dv + c, ld16<f32x4>(src + c) * inv);
+    }
+  }
+}
+
+// [U][Np] int32 -> [U][N].
+__global__ void __launch_bounds__(256) gma_prod_assign_kernel(const int32_t* __restrict__ src,
+                                                              int64_t U, int64_t Np, int64_t N,
+                                                              int32_t* __restrict__ dst) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < U * N;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t u = i / N, r = i - u * N;
+    dst[i] = src[u * Np + r];
+  }
+}
+
 }  // namespace
 
 // ---- host ------------------------------------------------------------------
@@ -957,6 +989,141 @@ hipError_t run_backward(const Plan& pp, const Tensors& t0, const BwdTensors& gt,
   return hipGetLastError();
 }
 
+// ---- the forward as a chain of products --------------------------------------
+// For shapes whose fused scan kernel does not fit (the causal form at large
+// K x d_v): the responsibilities of queries and keys are stored in fp32 and the
+// forward runs on the same batched products as the backward's first part:
+//   [V~ | Z] = Gk^T [V | 1],  [n | d - eps] = Gq [V~ | Z]      (Eqs. 5-7)
+// or, causal ("Causal GMA", Eq. 8b), per 64-token chunk c:
+//   [n | d - eps]_c = Gq_c [V~ | Z]_prefix(c) + mask(Gq_c Gk_c^T) [V | 1]_c,
+// then O = n / (d + eps).
+struct ProdLayout {
+  int64_t Np = 0, nc = 0;
+  size_t pads, v1, nd, gq, gk, vtz, part, pc, asg, total;
+  int ks_tok;
+};
+
+ProdLayout prod_layout(const Plan& pp, bool causal, int64_t N, size_t in_size) {
+  ProdLayout L{};
+  L.Np = pp.N;
+  L.nc = causal ? pp.N / kChunk : 0;
+  const size_t U = (size_t)pp.BH, Np = (size_t)pp.N, K = (size_t)pp.K;
+  const size_t dr = pp.DR, dv = pp.DV;
+  int ks = (int)((1024 + U - 1) / U);
+  const int maxk = (int)((pp.N + 255) / 256);
+  if (ks > maxk) ks = maxk;
+  if (ks > 32) ks = 32;
+  if ((int64_t)ks * pp.BH > 65535) ks = (int)(65535 / pp.BH);
+  if (ks < 1) ks = 1;
+  L.ks_tok = ks;
+  size_t off = r256(pp.total);
+  auto take = [&](size_t bytes) { const size_t o = off; off += r256(bytes); return o; };
+  const size_t w1p = dv + 4;
+  L.pads = take(causal && (int64_t)Np != N ? U * Np * (2 * dr + dv) * in_size : 0);
+  L.v1 = take(U * Np * w1p * 4);
+  L.nd = take(U * Np * w1p * 4);
+  L.gq = take(U * Np * K * 4);
+  L.gk = take(U * Np * K * 4);
+  const size_t recs = causal ? U * (size_t)L.nc : U;
+  L.vtz = take(recs * K * w1p * 4);
+  L.part = take(causal ? 0 : U * (size_t)ks * K * w1p * 4);
+  L.pc = take(causal ? recs * kChunk * kChunk * 4 : 0);
+  L.asg = take(2 * U * Np * 4);
+  L.total = off;
+  return L;
+}
+
+template <class TI, class TO>
+hipError_t run_prod_forward(const Plan& pp, const Tensors& t0, bool causal, int64_t N0,
+                            hipStream_t s) {
+  const ProdLayout L = prod_layout(pp, causal, N0, sizeof(TI));
+  Tensors t = t0;
+  char* ws = t.ws;
+  float* v1 = reinterpret_cast<float*>(ws + L.v1);
+  float* nd = reinterpret_cast<float*>(ws + L.nd);
+  float* Gq = reinterpret_cast<float*>(ws + L.gq);
+  float* Gk = reinterpret_cast<float*>(ws + L.gk);
+  float* vtz = reinterpret_cast<float*>(ws + L.vtz);
+  float* part = reinterpret_cast<float*>(ws + L.part);
+  float* pc = reinterpret_cast<float*>(ws + L.pc);
+  int32_t* aq = reinterpret_cast<int32_t*>(ws + L.asg);
+  int32_t* ak = aq + (size_t)pp.BH * L.Np;
+  const int64_t U = pp.BH, Np = L.Np, rows = U * Np;
+  const int K = pp.K, dr = pp.DR, dv = pp.DV;
+  const int w1 = dv + 1, l1 = dv + 4;
+  hipError_t e;
+#define GMA_CHECK(x) do { e = (x); if (e != hipSuccess) return e; } while (0)
+  if (g_launch_hook) g_launch_hook("gma_prod_prep", s, 1);
+  if (L.pads && Np != N0) {
+    TI* pq = reinterpret_cast<TI*>(ws + L.pads);
+    TI* pk = pq + (size_t)rows * dr;
+    TI* pv = pk + (size_t)rows * dr;
+    hipLaunchKernelGGL(gma_bwd_pad_kernel<TI>, dim3(sblocks(rows * dr, 256)), dim3(256), 0, s,
+                       t.q, dr, U, Np, N0, (void*)pq);
+    hipLaunchKernelGGL(gma_bwd_pad_kernel<TI>, dim3(sblocks(rows * dr, 256)), dim3(256), 0, s,
+                       t.k, dr, U, Np, N0, (void*)pk);
+    hipLaunchKernelGGL(gma_bwd_pad_kernel<TI>, dim3(sblocks(rows * dv, 256)), dim3(256), 0, s,
+                       t.v, dv, U, Np, N0, (void*)pv);
+    GMA_CHECK(hipGetLastError());
+    t.q = pq;
+    t.k = pk;
+    t.v = pv;
+  }
+  hipLaunchKernelGGL(gma_bwd_prep_kernel<TI>, dim3(sblocks(rows, 1024 / dv)), dim3(256), 0, s,
+                     t.v, dv, 0, rows, l1, v1);
+  GMA_CHECK(hipGetLastError());
+  if (g_launch_hook) g_launch_hook("gma_prod_prep", s, 0);
+  // responsibilities (and assignments) of queries and keys, fp32 [U][Np][K]
+  Tensors tr = t;
+  tr.q = t.q;
+  tr.gamma = Gq;
+  tr.assign_q = t0.assign_q ? aq : nullptr;
+  GMA_CHECK(launch_resp(pp, tr, s));
+  tr.q = t.k;
+  tr.gamma = Gk;
+  tr.assign_q = t0.assign_k ? ak : nullptr;
+  GMA_CHECK(launch_resp(pp, tr, s));
+
+  const int64_t Z = causal ? U * L.nc : U;
+  const int C = kChunk;
+  if (g_launch_hook) g_launch_hook("gma_prod_gemm", s, 1);
+  if (!causal) {
+    GMA_CHECK(gemm(true, false, Gk, K, Np * K, v1, l1, Np * l1, 0, vtz, l1, (int64_t)K * l1, K,
+                   w1, (int)Np, U, L.ks_tok, part, s));
+    GMA_CHECK(gemm(false, false, Gq, K, Np * K, vtz, l1, (int64_t)K * l1, 0, nd, l1, Np * l1,
+                   (int)Np, w1, K, U, 1, part, s));
+  } else {
+    GMA_CHECK(gemm(true, false, Gk, K, (int64_t)C * K, v1, l1, (int64_t)C * l1, 0, vtz, l1,
+                   (int64_t)K * l1, K, w1, C, Z, 1, part, s));
+    hipLaunchKernelGGL(gma_bwd_chunk_scan_kernel, dim3(blocks((int64_t)K * l1, 256), (unsigned)U),
+                       dim3(256), 0, s, vtz, (int)L.nc, K * l1, 0);
+    GMA_CHECK(hipGetLastError());
+    GMA_CHECK(gemm(false, true, Gq, K, (int64_t)C * K, Gk, K, (int64_t)C * K, 0, pc, C,
+                   (int64_t)C * C, C, C, K, Z, 1, part, s));
+    hipLaunchKernelGGL(gma_bwd_mask_kernel, dim3(sblocks(Z * C * C, 256)), dim3(256), 0, s, pc,
+                       Z * C * C, 0);
+    GMA_CHECK(hipGetLastError());
+    GMA_CHECK(gemm(false, false, Gq, K, (int64_t)C * K, vtz, l1, (int64_t)K * l1, 0, nd, l1,
+                   (int64_t)C * l1, C, w1, K, Z, 1, part, s));
+    GMA_CHECK(gemm(false, false, pc, C, (int64_t)C * C, v1, l1, (int64_t)C * l1, 0, nd, l1,
+                   (int64_t)C * l1, C, w1, C, Z, 1, part, s, true));
+  }
+  if (g_launch_hook) g_launch_hook("gma_prod_gemm", s, 0);
+  if (g_launch_hook) g_launch_hook("gma_prod_out", s, 1);
+  hipLaunchKernelGGL(gma_prod_out_kernel<TO>, dim3(sblocks(rows * dv / 4, 256)), dim3(256), 0, s,
+                     nd, dv, l1, t.eps, rows, Np, N0, t0.out);
+  GMA_CHECK(hipGetLastError());
+  if (t0.assign_q)
+    hipLaunchKernelGGL(gma_prod_assign_kernel, dim3(sblocks(U * N0, 256)), dim3(256), 0, s, aq, U,
+                       Np, N0, t0.assign_q);
+  if (t0.assign_k)
+    hipLaunchKernelGGL(gma_prod_assign_kernel, dim3(sblocks(U * N0, 256)), dim3(256), 0, s, ak, U,
+                       Np, N0, t0.assign_k);
+  if (g_launch_hook) g_launch_hook("gma_prod_out", s, 0);
+#undef GMA_CHECK
+  return hipGetLastError();
+}
+
 }  // namespace
 
 size_t backward_workspace_bytes(const Plan& pp, bool causal, int64_t N) {
@@ -969,6 +1136,23 @@ hipError_t launch_backward(const Plan& pp, const Tensors& t, const BwdTensors& g
   if (e != hipSuccess) return e;
   return pp.out_bf ? run_backward<bf16>(pp, t, gt, causal, N, s)
                    : run_backward<float>(pp, t, gt, causal, N, s);
+}
+
+}  // namespace gma
+
+namespace gma {
+
+size_t prod_forward_workspace_bytes(const Plan& pp, bool causal, int64_t N) {
+  return prod_layout(pp, causal, N, pp.bf ? 2 : 4).total;
+}
+
+hipError_t launch_prod_forward(const Plan& pp, const Tensors& t, bool causal, int64_t N,
+                               bool out_bf, hipStream_t s) {
+  const hipError_t e = launch_prologue(pp, t, s);
+  if (e != hipSuccess) return e;
+  if (pp.bf) return run_prod_forward<bf16, bf16>(pp, t, causal, N, s);
+  return out_bf ? run_prod_forward<float, bf16>(pp, t, causal, N, s)
+                : run_prod_forward<float, float>(pp, t, causal, N, s);
 }
 
 }  // namespace gma

@@ -1511,6 +1511,7 @@ hipError_t launch_prologue(const Plan& p, const Tensors& t, hipStream_t s) {
     case 2: GMA_DR_CASES(FN, BF, 2, 1)                                      \
     case 4: GMA_DR_CASES(FN, BF, 2, 2)                                      \
     case 8: GMA_DR_CASES(FN, BF, 2, 4)                                      \
+    case 16: GMA_DR_CASES(FN, BF, 4, 4)                                     \
   }                                                                         \
   break;
 
@@ -1553,6 +1554,7 @@ hipError_t launch_bidir(const Plan& p, const Tensors& t, hipStream_t s) {
     case 2: GMA_RESP_DR_CASES(BF, 2, 1)                                     \
     case 4: GMA_RESP_DR_CASES(BF, 2, 2)                                     \
     case 8: GMA_RESP_DR_CASES(BF, 2, 4)                                     \
+    case 16: GMA_RESP_DR_CASES(BF, 4, 4)                                    \
   }                                                                         \
   break;
 
@@ -1570,6 +1572,7 @@ hipError_t launch_bidir(const Plan& p, const Tensors& t, hipStream_t s) {
     case 2: GMA_USAGE_DR_CASES(BF, 2, 1)                                    \
     case 4: GMA_USAGE_DR_CASES(BF, 2, 2)                                    \
     case 8: GMA_USAGE_DR_CASES(BF, 2, 4)                                    \
+    case 16: GMA_USAGE_DR_CASES(BF, 4, 4)                                   \
   }                                                                         \
   break;
 

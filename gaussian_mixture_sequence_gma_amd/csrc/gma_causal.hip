@@ -988,10 +988,10 @@ static hipError_t causal_split_query(const Plan&, const Tensors&, hipStream_t) {
 static hipError_t causal_split_query_all(const Plan& p, const Tensors& t, hipStream_t s) {
   if (p.NG != 4) return hipErrorNotSupported;
   switch (p.DR) {
-    case 16: if (p.CPW == 1) { GMA_CSDV_CASES(1, 16) } else { GMA_CSDV_CASES(2, 16) } break;
-    case 32: if (p.CPW == 1) { GMA_CSDV_CASES(1, 32) } else { GMA_CSDV_CASES(2, 32) } break;
-    case 64: if (p.CPW == 1) { GMA_CSDV_CASES(1, 64) } else { GMA_CSDV_CASES(2, 64) } break;
-    case 128: if (p.CPW == 1) { GMA_CSDV_CASES(1, 128) } else { GMA_CSDV_CASES(2, 128) } break;
+    case 16: if (p.CPW == 1) { GMA_CSDV_CASES(1, 16) } else if (p.CPW == 2) { GMA_CSDV_CASES(2, 16) } else { GMA_CSDV_CASES(4, 16) } break;
+    case 32: if (p.CPW == 1) { GMA_CSDV_CASES(1, 32) } else if (p.CPW == 2) { GMA_CSDV_CASES(2, 32) } else { GMA_CSDV_CASES(4, 32) } break;
+    case 64: if (p.CPW == 1) { GMA_CSDV_CASES(1, 64) } else if (p.CPW == 2) { GMA_CSDV_CASES(2, 64) } else { GMA_CSDV_CASES(4, 64) } break;
+    case 128: if (p.CPW == 1) { GMA_CSDV_CASES(1, 128) } else if (p.CPW == 2) { GMA_CSDV_CASES(2, 128) } else { GMA_CSDV_CASES(4, 128) } break;
   }
   return hipErrorNotSupported;
 }
@@ -1004,10 +1004,12 @@ hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   if (p.NG != 4) return hipErrorInvalidValue;
   if (p.bf) {
     if (p.CPW == 1) { switch (0) { default: GMA_CDR_CASES(true, 1) } }
-    else { switch (0) { default: GMA_CDR_CASES(true, 2) } }
+    else if (p.CPW == 2) { switch (0) { default: GMA_CDR_CASES(true, 2) } }
+    else { switch (0) { default: GMA_CDR_CASES(true, 4) } }
   } else {
     if (p.CPW == 1) { switch (0) { default: GMA_CDR_CASES(false, 1) } }
-    else { switch (0) { default: GMA_CDR_CASES(false, 2) } }
+    else if (p.CPW == 2) { switch (0) { default: GMA_CDR_CASES(false, 2) } }
+    else { switch (0) { default: GMA_CDR_CASES(false, 4) } }
   }
   return hipErrorInvalidValue;
 }

@@ -76,18 +76,20 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-template <class T, int DR, int DV>
+template <class T, int DR, int DV, int KM>
 __global__ void __launch_bounds__(256) gma_decode_kernel(DecodeArgs a) {
   constexpr int L = DR / 16;                 // lanes per component in the score pass
   constexpr int CW = 64 / L;                 // components per wave per score pass
   constexpr int C4 = DV / 4;                 // four-column groups of a state row
   constexpr int SR = 256 / C4;               // state rows per pass of the workgroup
-  constexpr int NP = (128 + SR - 1) / SR;    // passes at the largest K
+  constexpr int NP = (KM + SR - 1) / SR;     // passes at the largest K (KM: 128 or 256)
+  constexpr int CL = KM / 64;                // components per lane in the posterior
   static_assert(DR % 16 == 0 && DR <= 128 && DV % 16 == 0 && DV <= 128, "shape");
+  static_assert(KM == 128 || KM == 256, "K bound");
 
-  __shared__ float s_sc[2][128];             // scores: queries, keys
-  __shared__ float s_g[2][128];              // responsibilities: queries, keys
-  __shared__ float s_z[128];                 // updated normaliser z'
+  __shared__ float s_sc[2][KM];              // scores: queries, keys
+  __shared__ float s_g[2][KM];               // responsibilities: queries, keys
+  __shared__ float s_z[KM];                  // updated normaliser z'
   __shared__ __attribute__((aligned(16))) float s_red[SR * DV];
   __shared__ float s_den;
 
@@ -130,10 +132,13 @@ __global__ void __launch_bounds__(256) gma_decode_kernel(DecodeArgs a) {
   for (int p = 0; p < NP; ++p)
     st[p] = __builtin_nontemporal_load(
         reinterpret_cast<const f32x4*>(sv + (size_t)min(r0 + p * SR, K - 1) * DV + col));
-  float z0 = 0.f, z1 = 0.f;
+  float zc[CL];
+#pragma unroll
+  for (int j = 0; j < CL; ++j) zc[j] = 0.f;
   if (wave == 1) {
-    if (lane < K) z0 = a.sz[(size_t)bh * K + lane];
-    if (lane + 64 < K) z1 = a.sz[(size_t)bh * K + lane + 64];
+#pragma unroll
+    for (int j = 0; j < CL; ++j)
+      if (lane + 64 * j < K) zc[j] = a.sz[(size_t)bh * K + lane + 64 * j];
   }
   const f32x4 vv = load4(static_cast<const T*>(a.v) + (size_t)bh * DV + col);
 
@@ -177,29 +182,34 @@ __global__ void __launch_bounds__(256) gma_decode_kernel(DecodeArgs a) {
   __syncthreads();
 
   // 3. posteriors (Eq. 3): wave 0 queries, wave 1 keys; lane holds components
-  //    lane and lane + 64.  Hard assignment: argmax, lowest index on ties.
+  //    lane + 64 j, j < KM / 64.  Hard assignment: argmax, lowest index on ties.
   if (wave < 2) {
     const float* sc = s_sc[wave];
-    const bool ok0 = lane < K, ok1 = lane + 64 < K;
-    const float v0 = ok0 ? sc[lane] : -INFINITY;
-    const float v1 = ok1 ? sc[lane + 64] : -INFINITY;
-    float m = v0;
+    float v[CL];
+#pragma unroll
+    for (int j = 0; j < CL; ++j) v[j] = lane + 64 * j < K ? sc[lane + 64 * j] : -INFINITY;
+    float m = v[0];
     int im = lane;
-    argmax_merge(m, im, v1, lane + 64);
+#pragma unroll
+    for (int j = 1; j < CL; ++j) argmax_merge(m, im, v[j], lane + 64 * j);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) argmax_merge(m, im, xor_lane(m, o), xor_lane_i(im, o));
-    const float e0 = ok0 ? expf(v0 - m) : 0.f;
-    const float e1 = ok1 ? expf(v1 - m) : 0.f;
-    const float inv = 1.f / wave_sum(e0 + e1);
-    const float g0 = e0 * inv, g1 = e1 * inv;
-    s_g[wave][lane] = g0;
-    s_g[wave][lane + 64] = g1;
-    if (wave == 1) {
-      const float zn0 = z0 + g0, zn1 = z1 + g1;
-      s_z[lane] = zn0;
-      s_z[lane + 64] = zn1;
-      if (ok0) a.sz[(size_t)bh * K + lane] = zn0;
-      if (ok1) a.sz[(size_t)bh * K + lane + 64] = zn1;
+    float e[CL], esum = 0.f;
+#pragma unroll
+    for (int j = 0; j < CL; ++j) {
+      e[j] = lane + 64 * j < K ? expf(v[j] - m) : 0.f;
+      esum += e[j];
+    }
+    const float inv = 1.f / wave_sum(esum);
+#pragma unroll
+    for (int j = 0; j < CL; ++j) {
+      const float gj = e[j] * inv;
+      s_g[wave][lane + 64 * j] = gj;
+      if (wave == 1) {
+        const float zn = zc[j] + gj;
+        s_z[lane + 64 * j] = zn;
+        if (lane + 64 * j < K) a.sz[(size_t)bh * K + lane + 64 * j] = zn;
+      }
     }
     int32_t* as = wave ? a.assign_k : a.assign_q;
     if (as && lane == 0) as[bh] = im;
@@ -211,7 +221,7 @@ __global__ void __launch_bounds__(256) gma_decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     if (p * SR < K) {
-      const int r = r0 + p * SR;             // < 128: s_g holds zeros past K
+      const int r = r0 + p * SR;             // < KM: s_g holds zeros past K
       const float gk = s_g[1][r], gq = s_g[0][r];
       const f32x4 s = st[p] + gk * vv;
       if (r < K) {
@@ -221,8 +231,10 @@ __global__ void __launch_bounds__(256) gma_decode_kernel(DecodeArgs a) {
     }
   }
   if (wave == 0) {
-    const float d = (lane < K ? s_g[0][lane] * s_z[lane] : 0.f) +
-                    (lane + 64 < K ? s_g[0][lane + 64] * s_z[lane + 64] : 0.f);
+    float d = 0.f;
+#pragma unroll
+    for (int j = 0; j < CL; ++j)
+      d += lane + 64 * j < K ? s_g[0][lane + 64 * j] * s_z[lane + 64 * j] : 0.f;
     const float den = wave_sum(d);
     if (lane == 0) s_den = den + a.eps;
   }
@@ -236,26 +248,26 @@ __global__ void __launch_bounds__(256) gma_decode_kernel(DecodeArgs a) {
   }
 }
 
-template <class T, int DR>
+template <class T, int DR, int KM>
 hipError_t launch_dv(const DecodeArgs& a, int DV, int64_t BH, hipStream_t s) {
   const dim3 grid((unsigned)BH), block(256);
   switch (DV) {
-    case 16: hipLaunchKernelGGL((gma_decode_kernel<T, DR, 16>), grid, block, 0, s, a); break;
-    case 32: hipLaunchKernelGGL((gma_decode_kernel<T, DR, 32>), grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL((gma_decode_kernel<T, DR, 64>), grid, block, 0, s, a); break;
-    case 128: hipLaunchKernelGGL((gma_decode_kernel<T, DR, 128>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((gma_decode_kernel<T, DR, 16, KM>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((gma_decode_kernel<T, DR, 32, KM>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((gma_decode_kernel<T, DR, 64, KM>), grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((gma_decode_kernel<T, DR, 128, KM>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <class T>
+template <class T, int KM>
 hipError_t launch_dr(const DecodeArgs& a, int DR, int DV, int64_t BH, hipStream_t s) {
   switch (DR) {
-    case 16: return launch_dv<T, 16>(a, DV, BH, s);
-    case 32: return launch_dv<T, 32>(a, DV, BH, s);
-    case 64: return launch_dv<T, 64>(a, DV, BH, s);
-    case 128: return launch_dv<T, 128>(a, DV, BH, s);
+    case 16: return launch_dv<T, 16, KM>(a, DV, BH, s);
+    case 32: return launch_dv<T, 32, KM>(a, DV, BH, s);
+    case 64: return launch_dv<T, 64, KM>(a, DV, BH, s);
+    case 128: return launch_dv<T, 128, KM>(a, DV, BH, s);
   }
   return hipErrorInvalidValue;
 }
@@ -280,8 +292,12 @@ hipError_t launch_decode(const Plan& p, const Tensors& t, float* state_v, float*
   a.K = p.K;
   a.eps = t.eps;
   if (g_launch_hook) g_launch_hook("gma_decode", s, 1);
-  const hipError_t e = p.out_bf ? launch_dr<bf16>(a, p.DR, p.DV, p.BH, s)
-                                : launch_dr<float>(a, p.DR, p.DV, p.BH, s);
+  // the component count bounds the LDS arrays and the passes: 128 or 256
+  const bool wide = p.K > 128;
+  const hipError_t e = p.out_bf ? (wide ? launch_dr<bf16, 256>(a, p.DR, p.DV, p.BH, s)
+                                        : launch_dr<bf16, 128>(a, p.DR, p.DV, p.BH, s))
+                                : (wide ? launch_dr<float, 256>(a, p.DR, p.DV, p.BH, s)
+                                        : launch_dr<float, 128>(a, p.DR, p.DV, p.BH, s));
   if (g_launch_hook) g_launch_hook("gma_decode", s, 0);
   return e;
 }

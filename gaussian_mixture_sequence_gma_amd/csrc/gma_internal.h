@@ -26,6 +26,7 @@ struct Plan {
   // causal
   int span_tiles = 0;       // 64-token chunks per causal span
   int nspan = 0;            // spans per sequence
+  bool prod = false;        // causal on the product path (the scan kernel does not fit)
   // workspace layout (bytes)
   size_t head_bytes = 0;
   size_t off_params = 0, off_partial = 0, off_partial_z = 0, off_vt = 0, off_z = 0, off_vtab = 0;
@@ -96,6 +97,13 @@ struct BwdTensors {
 size_t backward_workspace_bytes(const Plan& pp, bool causal, int64_t N);
 hipError_t launch_backward(const Plan& pp, const Tensors& t, const BwdTensors& gt, bool causal,
                            int64_t N, hipStream_t s);
+// The forward as a chain of fp32 products over stored responsibilities, for
+// shapes whose fused scan kernel does not fit.  pp: the bidirectional plan at
+// the padded length (N rounded up to 64 when causal); N: the caller's length;
+// out_bf: the output type (the inputs are of pp's type).
+size_t prod_forward_workspace_bytes(const Plan& pp, bool causal, int64_t N);
+hipError_t launch_prod_forward(const Plan& pp, const Tensors& t, bool causal, int64_t N,
+                               bool out_bf, hipStream_t s);
 // log sigma^2 = log(softplus(omega) + eps_sigma) over [H,K,d_r] and
 // log pi = alpha - logsumexp(alpha) over [H,K].
 hipError_t launch_reparam(const float* omega, const float* alpha, float eps_sigma, int64_t H,

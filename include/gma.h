@@ -47,8 +47,12 @@ typedef enum {
 /* Problem shape.  B batches x H heads x N positions.
  *  d_r  routing dimension of Q_X, K_X and the component means: 16, 32, 64 or 128
  *  d_v  value dimension of V_X and the output: 16, 32, 64 or 128
- *  K    number of Gaussian components: 1..128 (fp32 causal: K > 64 with d_v = 128
- *       exceeds the scan kernel's LDS budget and returns GMA_ERR_UNSUPPORTED)
+ *  K    number of Gaussian components: 1..256.  A causal shape whose scan kernel
+ *       tiles do not fit in LDS (fp32 with K > 64 and d_v = 128 or K > 128;
+ *       bf16 with K > 128 and d_v = 128) runs the causal form as a chain of
+ *       fp32 products over stored responsibilities instead, which needs
+ *       B*H*ceil(N/64) <= 65535 (else GMA_ERR_UNSUPPORTED) and a larger
+ *       workspace; the result is the same to the fp32 rounding level
  *  dtype storage type of Q_X, K_X, V_X and out (gma_layer_forward: of X, W and out)
  *  chunk causal scan chunk length: 0 (= 64) or 64; the result does not depend on it */
 typedef struct gma_dims {
@@ -60,7 +64,7 @@ typedef struct gma_dims {
 
 /* Host-only check of a call's arguments, as the entry points make it before any
  * launch: the shape, eps and variant (the same rules as gma_forward, including
- * the fp32 causal LDS limit), then each of the nptrs pointers in ptrs (each
+ * the product-path batch limit of the causal form), then each of the nptrs pointers in ptrs (each
  * must be non-NULL and 16-byte aligned; nptrs may be 0 and ptrs NULL), then
  * workspace_bytes against workspace_needed (a *_workspace_bytes figure).  No
  * pointer is dereferenced.  Returns GMA_OK, GMA_ERR_INVALID_ARG,

@@ -40,7 +40,8 @@ def _dims(**kw):
     ({}, 1e-6, 2, B.GMA_ERR_INVALID_ARG),
     ({"d_r": 48}, 1e-6, 0, B.GMA_ERR_UNSUPPORTED),
     ({"d_v": 256}, 1e-6, 0, B.GMA_ERR_UNSUPPORTED),
-    ({"K": 129}, 1e-6, 0, B.GMA_ERR_UNSUPPORTED),
+    ({"K": 257}, 1e-6, 0, B.GMA_ERR_UNSUPPORTED),
+    ({"K": 256}, 1e-6, 0, B.GMA_OK),
     ({"chunk": 32}, 1e-6, 1, B.GMA_ERR_UNSUPPORTED),
     ({"B": 300, "H": 300}, 1e-6, 0, B.GMA_ERR_UNSUPPORTED),
 ])
@@ -61,10 +62,14 @@ def test_validate_pointers_and_workspace():
                           workspace_needed=101) == B.GMA_ERR_WORKSPACE
     # the shape is checked first
     assert B.gma_validate(_dims(K=0), 1e-6, 0, ptrs=(None,)) == B.GMA_ERR_INVALID_ARG
-    # fp32 causal beyond the scan kernel's LDS budget: rejected by validation itself
+    # fp32 causal beyond the scan kernel's LDS budget runs on the product path,
+    # whose chunk products are batched over B*H*ceil(N/64) <= 65535
     big = B.make_dims(1, 1, 333, 64, 128, 128, B.GMA_F32)
-    assert B.gma_validate(big, 1e-6, 1) == B.GMA_ERR_UNSUPPORTED
-    assert B.gma_validate(big, 1e-6, 0) == B.GMA_OK
+    assert B.gma_validate(big, 1e-6, 1) == B.GMA_OK
+    long = B.make_dims(1, 2, 64 * 40000, 64, 128, 128, B.GMA_F32)
+    assert B.gma_validate(long, 1e-6, 1) == B.GMA_ERR_UNSUPPORTED
+    assert "65535" in B.gma_last_error()
+    assert B.gma_validate(long, 1e-6, 0) == B.GMA_OK
 
 
 def test_workspace_query_and_errors():
@@ -73,7 +78,7 @@ def test_workspace_query_and_errors():
     assert 0 < n0 < n1 and n0 % 256 == 0
     assert B.gma_forward_workspace_bytes(_dims(), 1) > 0
     with pytest.raises(B.GmaError) as ei:
-        B.gma_forward_workspace_bytes(_dims(K=200), 0)
+        B.gma_forward_workspace_bytes(_dims(K=300), 0)
     assert ei.value.status == B.GMA_ERR_UNSUPPORTED
     assert B.gma_layer_workspace_bytes(_dims(), 1024, 1) > B.gma_forward_workspace_bytes(_dims(), 1)
     with pytest.raises(B.GmaError):
@@ -210,7 +215,7 @@ def test_decode_step_rejects_before_launch():
     assert _decode(dims=_dims(N=1, chunk=32), out=None) == B.GMA_ERR_INVALID_ARG
     assert "NULL" in B.gma_last_error()
     assert _decode(eps=float("nan")) == B.GMA_ERR_INVALID_ARG
-    assert _decode(dims=_dims(N=1, K=129)) == B.GMA_ERR_UNSUPPORTED
+    assert _decode(dims=_dims(N=1, K=257)) == B.GMA_ERR_UNSUPPORTED
     assert _decode(dims=_dims(N=1, d_v=48)) == B.GMA_ERR_UNSUPPORTED
     assert "N = 1" in (lambda: (_decode(dims=_dims(N=3)), B.gma_last_error())[1])()
 

@@ -92,6 +92,8 @@ def _case(B, H, N, d_r, d_v, K, dtype, skew, seed=31, causal=False):
     (2, 2, 1000, 64, 64, 64, "bf16", False),
     (1, 2, 200, 128, 32, 100, "bf16", False),
     (1, 2, 4096, 64, 128, 128, "bf16", True),     # the long-context head shape
+    (1, 2, 500, 64, 64, 256, "bf16", False),      # K = 256
+    (2, 1, 300, 32, 32, 200, "f32", False),
 ])
 def test_backward_matches_oracle(B, H, N, d_r, d_v, K, dtype, skew):
     got, ref = _case(B, H, N, d_r, d_v, K, dtype, skew)

@@ -59,16 +59,9 @@ def test_causal_component_counts(dtype, K):
                                        (128, 64, 40), (64, 128, 128), (128, 128, 64),
                                        (128, 64, 128)])
 def test_causal_head_dims(dtype, d_r, d_v, K):
+    # (fp32 with K > 64 and d_v = 128 exceeds the scan kernel's LDS and runs on
+    # the product path)
     w = W["tiny_bidir_f32"].with_(d_r=d_r, d_v=d_v, K=K, N=333, dtype=dtype, causal=True)
-    if dtype == "f32" and K > 64 and d_v == 128:
-        from gaussian_mixture_sequence_gma_amd import binding as B
-        dims = B.make_dims(1, 1, 333, d_r, d_v, K, B.GMA_F32)
-        # outside the fp32 scan's LDS: gma_validate and the workspace query agree
-        assert B.gma_validate(dims, 1e-6, 1) == B.GMA_ERR_UNSUPPORTED
-        with pytest.raises(B.GmaError) as ei:
-            B.gma_forward_workspace_bytes(dims, 1)
-        assert ei.value.status == B.GMA_ERR_UNSUPPORTED
-        return
     run_and_compare(w)
 
 

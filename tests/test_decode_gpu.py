@@ -52,6 +52,9 @@ def _decode_once(w, seed):
     (2, 4, 64, 128, 128, "bf16", True),      # the long-context head shape
     (4, 2, 16, 64, 65, "bf16", False),       # K one past a wave's 64 components
     (1, 1, 128, 128, 128, "f32", True),
+    (2, 2, 64, 64, 200, "f32", False),       # K above 128: four components per lane
+    (2, 3, 64, 128, 256, "bf16", True),      # the language model's K = 256
+    (1, 2, 32, 32, 129, "bf16", False),
 ])
 def test_decode_step_matches_oracle(B, H, d_r, d_v, K, dtype, skew):
     w = _wl(B, H, d_r, d_v, K, dtype, skew=skew)

@@ -97,7 +97,8 @@ def test_bitwise_deterministic():
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("K,d_r", [(8, 16), (33, 64), (128, 64), (64, 128)])
+@pytest.mark.parametrize("K,d_r", [(8, 16), (33, 64), (128, 64), (64, 128), (256, 64),
+                                   (200, 32)])
 def test_responsibilities_match_oracle(dtype, K, d_r):
     w = W["tiny_bidir_f32"].with_(K=K, d_r=d_r, N=257, H=2, dtype=dtype)
     gen = inputs.generate(w, 1)

@@ -67,6 +67,8 @@ def _check(gen, X, dtype, thr, heads=None):
     (3, 2, 64, 64, 64, "f32", False, 0.0),
     (1, 4, 2000, 64, 128, "bf16", True, 0.1),
     (2, 2, 513, 128, 100, "bf16", False, 0.05),
+    (1, 2, 700, 64, 256, "bf16", True, 0.1),   # K = 256 (the language-model setting)
+    (2, 2, 300, 32, 200, "f32", False, 0.1),
 ])
 def test_usage_stats_matches_oracle(B, H, N, d_r, K, dtype, skew, thr):
     kw = dict(mu_var=1.5, ls2_lo=-1.5, ls2_hi=0.5, logit_var=2.0) if skew else {}
