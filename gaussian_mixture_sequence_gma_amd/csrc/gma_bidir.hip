@@ -1049,8 +1049,13 @@ static hipError_t run_bidir(const Plan& p, const Tensors& t, hipStream_t s) {
     if (s2 < 1) s2 = 1;
     PS = (int)s2;
     const dim3 g2((unsigned)s2, (unsigned)p.BH);
-    if (split) hipLaunchKernelGGL((gma_write_team_kernel<C, true>), g2, dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((gma_write_team_kernel<C, false>), g2, dim3(512), 0, s, a);
+    if (a.assign) {
+      if (split) hipLaunchKernelGGL((gma_write_team_kernel<C, true, true>), g2, dim3(512), 0, s, a);
+      else hipLaunchKernelGGL((gma_write_team_kernel<C, false, true>), g2, dim3(512), 0, s, a);
+    } else {
+      if (split) hipLaunchKernelGGL((gma_write_team_kernel<C, true, false>), g2, dim3(512), 0, s, a);
+      else hipLaunchKernelGGL((gma_write_team_kernel<C, false, false>), g2, dim3(512), 0, s, a);
+    }
   } else if constexpr (Write2<C>::kOK) {
     const int64_t g32 = (p.N + 31) / 32;
     int64_t s2 = (256 * Write2<C>::WPE + p.BH - 1) / p.BH;

@@ -894,8 +894,8 @@ static hipError_t run_causal(const Plan& p, const Tensors& t, hipStream_t s) {
     // team write: one split per span; a span is 2 span_tiles 32-key groups
     wa.gpw = 2 * p.span_tiles;
     if constexpr (WriteTeam<C>::kOK) {
-      if (split) hipLaunchKernelGGL((gma_write_team_kernel<C, true>), grid, dim3(512), 0, s, wa);
-      else hipLaunchKernelGGL((gma_write_team_kernel<C, false>), grid, dim3(512), 0, s, wa);
+      if (split) hipLaunchKernelGGL((gma_write_team_kernel<C, true, false>), grid, dim3(512), 0, s, wa);
+      else hipLaunchKernelGGL((gma_write_team_kernel<C, false, false>), grid, dim3(512), 0, s, wa);
     }
   } else if (Write2<C>::kOK && (split || p.span_tiles >= (Write2<C>::WPE == 2 ? 4 : 16))) {
     wa.gpw = 2 * p.span_tiles;

@@ -47,8 +47,8 @@ struct WriteTeam {
   // V tiles: [team][2 buffers] of VT bf16, their own array
   static constexpr int VSH = NT * 2 * VT;
   // the other LDS: coefficient table, c, exchange records [team][round
-  // parity][wave][32 keys] of (m, l, argmax, 0), factor tables [wave][64],
-  // flags [wave]
+  // parity][wave] of 128 floats (m of the 32 keys, then l, then the argmax,
+  // then unused), factor tables [wave][64], flags [wave]
   static constexpr int OFF_C = COEF * 1024;
   static constexpr int OFF_X = OFF_C + KP * 4;
   static constexpr int OFF_FT = OFF_X + NT * 2 * TS * 32 * 16;
@@ -78,7 +78,8 @@ __device__ __forceinline__ void team_wait(const int* flag, int v) {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <class C, bool XS>
+// AS: key assignments are written (a.assign non-null)
+template <class C, bool XS, bool AS>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gma_write_team_kernel(BidirArgs a) {
   using R = WriteTeam<C>;
@@ -96,7 +97,7 @@ gma_write_team_kernel(BidirArgs a) {
   const int c = lane & 15, g = lane >> 4;
   const int64_t bh = blockIdx.y;
   const int h = (int)(bh % a.H);
-  const bool want_assign = a.assign != nullptr;
+  constexpr bool want_assign = AS;
 
   {
     const char* tb = a.params + (size_t)h * a.head_bytes + a.head_bytes / 2;
@@ -164,9 +165,15 @@ gma_write_team_kernel(BidirArgs a) {
   for (int ct = 0; ct < CTW; ++ct)
 #pragma unroll
     for (int dt = 0; dt < R::DVT; ++dt) acc[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Z accumulates the same bf16 responsibilities as V~ (pairs summed by a bf16
+  // dot product with (1, 1))
   float zacc[CTW];
 #pragma unroll
   for (int ct = 0; ct < CTW; ++ct) zacc[ct] = 0.f;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  unsigned ones_bits;
+  asm("v_mov_b32 %0, 0x3f803f80" : "=v"(ones_bits));
+  const bf16x2 ones2 = __builtin_bit_cast(bf16x2, ones_bits);
 
   // Issue order per round: x(next) after the scores, V(next) after the V~
   // update; so at the top of a round x(this) is followed only by V(this)'s
@@ -209,17 +216,19 @@ gma_write_team_kernel(BidirArgs a) {
 #pragma unroll
         for (int q = 0; q < NQX<XS>; ++q)
 #pragma unroll
-          for (int tt = 0; tt < 2; ++tt) S[tt][ct] = mma(f[tt][kFI[q]], w[kWI[q]], S[tt][ct]);
+          for (int tt = 0; tt < 2; ++tt)
+            S[tt][ct] = mma(f[tt][kFI[q]], w[kWI[q]], S[tt][ct]);
       }
     }
     __builtin_amdgcn_s_setprio(0);
     if (more) load_x(grp + NT);
 
     // ---- per key: local maximum and sum over this wave's components, posted as
-    // the record (m, l, argmax) of key 8 g + 4 tt + i by lane c = 4 tt + i of
-    // each lane group -------------------------------------------------------------
+    // the records m, l, argmax of keys 8 g + 4 tt + i by lane c = 0 of each
+    // lane group ------------------------------------------------------------------
     {
-      float4* rec = xch + (buf * TS + r) * 32 + 8 * g;
+      float mm[8], ll[8];
+      int bb[8];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -248,11 +257,26 @@ gma_write_team_kernel(BidirArgs a) {
           for (int ct = 0; ct < CTW; ++ct) {
             const float e = exp2_fast(S[tt][ct][i] - m);
             S[tt][ct][i] = e;
-            l += e;
+            l = ct == 0 ? e : l + e;
           }
           l = row16_sum(l);
-          if (c == 4 * tt + i) rec[4 * tt + i] = float4{m, l, __int_as_float(bi), 0.f};
+          mm[4 * tt + i] = m;
+          ll[4 * tt + i] = l;
+          bb[4 * tt + i] = bi;
         }
+      if (c == 0) {
+        float4* rec = xch + (buf * TS + r) * 32 + 2 * g;
+        rec[0] = float4{mm[0], mm[1], mm[2], mm[3]};
+        rec[1] = float4{mm[4], mm[5], mm[6], mm[7]};
+        rec[8] = float4{ll[0], ll[1], ll[2], ll[3]};
+        rec[9] = float4{ll[4], ll[5], ll[6], ll[7]};
+        if (want_assign) {
+          rec[16] = float4{__int_as_float(bb[0]), __int_as_float(bb[1]), __int_as_float(bb[2]),
+                           __int_as_float(bb[3])};
+          rec[17] = float4{__int_as_float(bb[4]), __int_as_float(bb[5]), __int_as_float(bb[6]),
+                           __int_as_float(bb[7])};
+        }
+      }
     }
     // this wave's copies of V(grp) have landed once at most the x loads of the
     // next group are outstanding
@@ -271,15 +295,14 @@ gma_write_team_kernel(BidirArgs a) {
     // table and read back by the 16 lanes of each group ---------------------------
     if (c < 8) {
       const int key = 8 * g + c;
-      const float4* rb = xch + buf * TS * 32 + key;
+      const float* rb = reinterpret_cast<const float*>(xch + buf * TS * 32) + key;
       float mw[TS], lw[TS];
       int iw[TS];
 #pragma unroll
       for (int w = 0; w < TS; ++w) {
-        const float4 q = rb[w * 32];
-        mw[w] = q.x;
-        lw[w] = q.y;
-        iw[w] = __float_as_int(q.z);
+        mw[w] = rb[w * 128];
+        lw[w] = rb[w * 128 + 32];
+        iw[w] = want_assign ? __float_as_int(rb[w * 128 + 64]) : 0;
       }
       float M = mw[0];
 #pragma unroll
@@ -315,11 +338,18 @@ gma_write_team_kernel(BidirArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int ct = 0; ct < CTW; ++ct) {
-          const float gm = S[tt][ct][i] * fac[tt][i];
-          zacc[ct] += gm;
-          A[ct][4 * tt + i] = to_bf16(gm);
-        }
+        for (int ct = 0; ct < CTW; ++ct) A[ct][4 * tt + i] = to_bf16(S[tt][ct][i] * fac[tt][i]);
+#pragma unroll
+    for (int ct = 0; ct < CTW; ++ct) {
+      zacc[ct] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(A[ct], A[ct], 0, 1),
+                                                 ones2, zacc[ct], false);
+      zacc[ct] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(A[ct], A[ct], 2, 3),
+                                                 ones2, zacc[ct], false);
+      zacc[ct] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(A[ct], A[ct], 4, 5),
+                                                 ones2, zacc[ct], false);
+      zacc[ct] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(A[ct], A[ct], 6, 7),
+                                                 ones2, zacc[ct], false);
+    }
     if (want_assign && r == 0 && lane < 32) {
       const int64_t tok = grp * 32 + lane;
       if (tok < a.N) a.assign[(size_t)bh * a.N + tok] = __float_as_int(ftab[32 + lane]);

@@ -12,6 +12,8 @@ Workloads (names describe the shape; all use numpy ``default_rng(seed)``):
   (the long-context-classification shape of the paper's LRA experiments)
 * ``lm_causal_bf16``      B4 H12 N8192 d_r64 d_v64  K64   bf16, causal, chunk 64
   (the autoregressive language-modelling shape of the WikiText-103 runs)
+* ``lm_causal_k256_bf16`` the same shape with K256, the component count of the
+  WikiText-103 language model
 * ``long_bidir_bf16``     B1 H32 N32768 d_r64 d_v128 K128 bf16, bidirectional,
   skewed parameters: mu ~ N(0, 1.5), log sigma^2 ~ U(-1.5, 0.5),
   prior logits ~ N(0, 2)
@@ -78,6 +80,7 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("tiny_bidir_f32", 1, 1, 256, 16, 32, 8, "f32", False),
         Workload("lra_bidir_f32", 8, 8, 4096, 64, 64, 64, "f32", False),
         Workload("lm_causal_bf16", 4, 12, 8192, 64, 64, 64, "bf16", True),
+        Workload("lm_causal_k256_bf16", 4, 12, 8192, 64, 64, 256, "bf16", True),
         Workload("long_bidir_bf16", 1, 32, 32768, 64, 128, 128, "bf16", False,
                  mu_var=1.5, ls2_lo=-1.5, ls2_hi=0.5, logit_var=2.0),
         Workload("layer_causal_bf16", 2, 16, 16384, 64, 64, 32, "bf16", True,
