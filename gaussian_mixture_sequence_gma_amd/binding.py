@@ -14,7 +14,9 @@ import re
 from typing import List, Optional, Tuple
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgma.so")
+# GMA_LIBRARY names another build of the same library (e.g. one whose host
+# code is compiled with sanitizers); the default is the in-tree build
+LIB_PATH = os.environ.get("GMA_LIBRARY") or os.path.join(_HERE, "libgma.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "gma.h")
 
 GMA_F32, GMA_BF16 = 0, 1

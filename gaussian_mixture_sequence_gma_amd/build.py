@@ -58,6 +58,29 @@ def build(jobs: int | None = None, only: list | None = None) -> str:
     return LIB
 
 
+def build_host_sanitized() -> str:
+    """libgma_san.so: the library with the host code of gma_api.hip (argument
+    checks, planning, workspace sizing, the C ABI) compiled with AddressSanitizer
+    and UndefinedBehaviorSanitizer; device code and the other sources as built
+    by build().  Load it with clang's ASan runtime preloaded."""
+    objs = [os.path.join(OBJDIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    for o in objs[1:]:
+        if not os.path.exists(o):
+            raise RuntimeError("build() first: %s is missing" % o)
+    san_obj = os.path.join(OBJDIR, "gma_api_san.o")
+    san_flags = ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+    cmd = [HIPCC] + FLAGS + san_flags + ["-c", os.path.join(CSRC, SOURCES[0]), "-o", san_obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for the sanitized host build:\n" + r.stderr)
+    lib = os.path.join(OBJDIR, "libgma_san.so")
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", lib, san_obj] + objs[1:]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stderr)
+    return lib
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("-j", "--jobs", type=int, default=None)
