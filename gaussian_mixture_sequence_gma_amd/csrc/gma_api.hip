@@ -176,8 +176,9 @@ bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
 // Per calling thread: each thread that enables timing records and collects
 // only the launches it makes itself.
 struct Pending {
-  const char* tag;
-  hipEvent_t start, stop;
+  const char* tag = nullptr;
+  hipEvent_t start = nullptr, stop = nullptr;
+  hipError_t err = hipSuccess;      // the first failure creating or recording this pair
 };
 struct Total {
   std::string name;
@@ -193,12 +194,14 @@ thread_local TimingState t_timing;
 void timing_hook(const char* tag, hipStream_t s, int begin) {
   TimingState& ts = t_timing;
   if (begin) {
+    ts.open = Pending{};
     ts.open.tag = tag;
-    hipEventCreate(&ts.open.start);
-    hipEventCreate(&ts.open.stop);
-    hipEventRecord(ts.open.start, s);
+    hipError_t e = hipEventCreate(&ts.open.start);
+    if (e == hipSuccess) e = hipEventCreate(&ts.open.stop);
+    if (e == hipSuccess) e = hipEventRecord(ts.open.start, s);
+    ts.open.err = e;
   } else {
-    hipEventRecord(ts.open.stop, s);
+    if (ts.open.err == hipSuccess) ts.open.err = hipEventRecord(ts.open.stop, s);
     ts.pending.push_back(ts.open);
   }
 }
@@ -741,13 +744,19 @@ int gma_timing_collect(gma_kernel_time* out, int max, int* count) {
   std::vector<Pending> pend;
   pend.swap(t_timing.pending);
   std::vector<Total> totals;
+  hipError_t first_err = hipSuccess;
   for (auto& pe : pend) {
     float ms = 0.f;
-    hipError_t e = hipEventSynchronize(pe.stop);
+    hipError_t e = pe.err;
+    if (e == hipSuccess) e = hipEventSynchronize(pe.stop);
     if (e == hipSuccess) e = hipEventElapsedTime(&ms, pe.start, pe.stop);
-    hipEventDestroy(pe.start);
-    hipEventDestroy(pe.stop);
-    if (e != hipSuccess) return fail(GMA_ERR_HIP, std::string("timing: ") + hipGetErrorString(e));
+    // every event is released, also after a failure
+    if (pe.start) (void)hipEventDestroy(pe.start);
+    if (pe.stop) (void)hipEventDestroy(pe.stop);
+    if (e != hipSuccess) {
+      if (first_err == hipSuccess) first_err = e;
+      continue;
+    }
     bool found = false;
     for (auto& tt : totals)
       if (tt.name == pe.tag) {
@@ -764,6 +773,8 @@ int gma_timing_collect(gma_kernel_time* out, int max, int* count) {
     out[i].launches = totals[i].launches;
     out[i].total_ms = totals[i].ms;
   }
+  if (first_err != hipSuccess)
+    return fail(GMA_ERR_HIP, std::string("timing: ") + hipGetErrorString(first_err));
   return GMA_OK;
 }
 

@@ -284,7 +284,9 @@ const char* gma_last_error(void);
  * two hipEvents recorded on the launch stream.  gma_timing_collect synchronises
  * the calling thread's events, accumulates per-kernel totals, writes up to
  * `max` entries and the number of distinct kernels to *count, and resets them.
- * Other threads' calls are neither timed nor affected. */
+ * Other threads' calls are neither timed nor affected.  If creating, recording
+ * or reading an event pair failed, that launch is left out of the totals,
+ * every event is still released, and the call returns GMA_ERR_HIP. */
 typedef struct gma_kernel_time {
   char name[48];
   int64_t launches;
