@@ -185,9 +185,11 @@ def main():
     ap.add_argument("--workload", default="long_bidir_bf16")
     ap.add_argument("--causal", type=int, default=None, help="override the workload's variant")
     ap.add_argument("--reparam", action="store_true",
-                    help="each step first derives log sigma^2 and log pi on the device from "
-                         "unconstrained parameters (gma_reparameterize; the workload's log "
-                         "sigma^2 and log pi arrays stand in for omega and alpha)")
+                    help="each step derives log sigma^2 and log pi on the device from "
+                         "unconstrained parameters (the workload's log sigma^2 and log pi "
+                         "arrays stand in for omega and alpha): inside the forward's prologue "
+                         "(gma_forward_reparam) for gma_forward workloads, else by "
+                         "gma_reparameterize before the step")
     ap.add_argument("--usage-stats", action="store_true",
                     help="time gma_usage_stats (component-usage diagnostics) over the "
                          "workload's queries instead of the forward")
@@ -297,8 +299,12 @@ def main():
             binding.gma_usage_stats(Q, mu, ls2, lpi, dims, 0.1, u_counts, u_f[0], u_f[1], u_hs,
                                     ws, ws.numel())
             return
-        if args.reparam:
+        if args.reparam and (decode or w.d_model > 0):
             binding.gma_reparameterize(omega, alpha, 1e-4, w.H, w.K, w.d_r, ls2, lpi)
+        elif args.reparam:
+            binding.gma_forward_reparam(Q, K, V, mu, omega, alpha, 1e-4, w.eps, int(w.causal),
+                                        out, dims, None, None, ws, ws.numel())
+            return
         if decode:
             binding.gma_decode_step(Q, K, V, mu, ls2, lpi, w.eps, S_state, z_state, out, dims)
         elif w.d_model > 0:
@@ -413,7 +419,9 @@ def main():
     if args.backward:
         cfg["step"] = "gma_backward (all gradients, forward recomputed) in place of the forward"
     if args.reparam:
-        cfg["reparam"] = "gma_reparameterize (Eqs. 14-15, eps_sigma 1e-4) at the start of each step"
+        cfg["reparam"] = ("log sigma^2 and log pi from omega and alpha (Eqs. 14-15, eps_sigma 1e-4) "
+                          "in every step: " + ("gma_reparameterize before it" if (decode or w.d_model > 0)
+                                               else "inside gma_forward_reparam's prologue"))
     if decode:
         cfg["step"] = "one decode token per sequence against a carried fp32 state"
         cfg["state_len"] = w.state_len

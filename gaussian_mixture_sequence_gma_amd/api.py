@@ -33,7 +33,7 @@ def _check(tensors: dict, params: dict = None, io_dtype=None, H: int = None, Kc:
     """Validate one call's tensors.  tensors: name -> (tensor or None, shape);
     tensors of io_dtype (routing vectors, values, outputs) must share it, which
     must be bfloat16 or float32.  params: mu, log_sigma2, log_pi (fp32, [H,K,d_r],
-    [H,K,d_r], [H,K]).  extra: name -> (tensor or None, shape, dtype).  Shapes,
+    [H,K,d_r], [H,K]), or omega and alpha in place of the last two.  extra: name -> (tensor or None, shape, dtype).  Shapes,
     dtypes and contiguity are checked first, then that all tensors share one
     CUDA device."""
     allt = []
@@ -47,7 +47,8 @@ def _check(tensors: dict, params: dict = None, io_dtype=None, H: int = None, Kc:
         _req(t.dtype == io_dtype, "%s has dtype %s, expected %s" % (name, t.dtype, io_dtype))
         allt.append((name, t))
     if params is not None:
-        shapes = {"mu": (H, Kc, d_r), "log_sigma2": (H, Kc, d_r), "log_pi": (H, Kc)}
+        shapes = {"mu": (H, Kc, d_r), "log_sigma2": (H, Kc, d_r), "log_pi": (H, Kc),
+                  "omega": (H, Kc, d_r), "alpha": (H, Kc)}
         for name, t in params.items():
             _shape(t, shapes[name], name)
             _req(t.dtype == torch.float32, "%s must be float32, got %s" % (name, t.dtype))
@@ -119,6 +120,36 @@ def forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, mu: torch.Tensor,
         ak = torch.empty((Bb, H, N), dtype=torch.int32, device=Q.device)
     B.gma_forward(Q, K, V, mu, log_sigma2, log_pi, eps, int(causal), out, dims, aq, ak,
                   workspace, workspace.numel(), stream)
+    return (out, aq, ak) if assign else out
+
+
+def forward_reparam(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, mu: torch.Tensor,
+                    omega: torch.Tensor, alpha: torch.Tensor, eps_sigma: float = 1e-4,
+                    eps: float = 1e-6, causal: bool = False, assign: bool = False,
+                    chunk: int = 0, workspace: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, stream=None):
+    """forward() from the unconstrained parameters: omega [H,K,d_r] in place of
+    log sigma^2 and the prior logits alpha [H,K] in place of log pi (gma_forward_reparam)."""
+    _req(Q.dim() == 4 and V.dim() == 4 and mu.dim() == 3, "Q, V must be 4-D and mu 3-D")
+    Bb, H, N, d_r = Q.shape
+    d_v = V.shape[-1]
+    Kc = mu.shape[1]
+    _check({"Q": (Q, (Bb, H, N, d_r)), "K": (K, (Bb, H, N, d_r)), "V": (V, (Bb, H, N, d_v)),
+            "out": (out, (Bb, H, N, d_v))},
+           {"mu": mu, "omega": omega, "alpha": alpha}, Q.dtype, H, Kc, d_r,
+           _ws(workspace))
+    dims = B.make_dims(Bb, H, N, d_r, d_v, Kc, torch_dtype_code(Q), chunk)
+    need = B.gma_forward_workspace_bytes(dims, int(causal))
+    if workspace is None or workspace.numel() < need:
+        workspace = alloc_workspace(need, Q.device)
+    if out is None:
+        out = torch.empty((Bb, H, N, d_v), dtype=V.dtype, device=V.device)
+    aq = ak = None
+    if assign:
+        aq = torch.empty((Bb, H, N), dtype=torch.int32, device=Q.device)
+        ak = torch.empty((Bb, H, N), dtype=torch.int32, device=Q.device)
+    B.gma_forward_reparam(Q, K, V, mu, omega, alpha, eps_sigma, eps, int(causal), out, dims, aq,
+                          ak, workspace, workspace.numel(), stream)
     return (out, aq, ak) if assign else out
 
 

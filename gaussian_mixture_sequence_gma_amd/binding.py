@@ -60,6 +60,7 @@ def load():
     lib.gma_forward_workspace_bytes.argtypes = [D, i32, ctypes.POINTER(S)]
     lib.gma_forward.argtypes = [P, P, P, P, P, P, f32, i32, P, D, P, P, P, S, P]
     lib.gma_forward_noalloc.argtypes = [P, P, P, P, P, P, f32, i32, P, D, P, P, P]
+    lib.gma_forward_reparam.argtypes = [P, P, P, P, P, P, f32, f32, i32, P, D, P, P, P, S, P]
     lib.gma_layer_workspace_bytes.argtypes = [D, ctypes.c_int32, i32, ctypes.POINTER(S)]
     lib.gma_layer_forward.argtypes = [P, P, P, P, ctypes.c_int32, P, P, P, f32, i32, P, D, P, P,
                                       P, S, P]
@@ -83,6 +84,7 @@ def load():
     lib.gma_timing_collect.argtypes = [ctypes.POINTER(gma_kernel_time), i32,
                                        ctypes.POINTER(ctypes.c_int)]
     for fn in ("gma_validate", "gma_forward_workspace_bytes", "gma_forward", "gma_forward_noalloc",
+               "gma_forward_reparam",
                "gma_layer_workspace_bytes", "gma_layer_forward", "gma_layer_projection_layout",
                "gma_responsibilities", "gma_prefix_state", "gma_decode_step", "gma_reparameterize",
                "gma_usage_workspace_bytes", "gma_usage_stats",
@@ -152,6 +154,16 @@ def gma_forward(Q_X, K_X, V_X, mu, log_sigma2, log_pi, eps, causal, out, dims: g
                               _ptr(log_pi), float(eps), int(causal), _ptr(out),
                               ctypes.byref(dims), _ptr(assign_q), _ptr(assign_k),
                               _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def gma_forward_reparam(Q_X, K_X, V_X, mu, omega, alpha, eps_sigma, eps, causal, out,
+                        dims: gma_dims, assign_q=None, assign_k=None, workspace=None,
+                        workspace_bytes=0, stream=None):
+    _check(load().gma_forward_reparam(_ptr(Q_X), _ptr(K_X), _ptr(V_X), _ptr(mu), _ptr(omega),
+                                      _ptr(alpha), float(eps_sigma), float(eps), int(causal),
+                                      _ptr(out), ctypes.byref(dims), _ptr(assign_q),
+                                      _ptr(assign_k), _ptr(workspace), int(workspace_bytes),
+                                      _stream(stream)))
 
 
 def gma_forward_noalloc(Q_X, K_X, V_X, mu, log_sigma2, log_pi, eps, causal, out, dims: gma_dims,

@@ -45,6 +45,17 @@ def build(jobs: int | None = None, only: list | None = None) -> str:
     objects of an earlier build) and link libgma.so."""
     os.makedirs(OBJDIR, exist_ok=True)
     todo = SOURCES if not only else [s for s in SOURCES if s in only]
+    # a header newer than any object means every source is rebuilt: the
+    # sources share structures through the headers
+    objs0 = [os.path.join(OBJDIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    if only and all(os.path.exists(o) for o in objs0):
+        oldest = min(os.path.getmtime(o) for o in objs0)
+        hdrs = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")]
+        hdrs.append(os.path.join(INCLUDE, "gma.h"))
+        if any(os.path.getmtime(h) > oldest for h in hdrs):
+            todo = SOURCES
+    elif only:
+        todo = SOURCES
     jobs = jobs or min(len(todo), os.cpu_count() or 1)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         list(ex.map(_compile, todo))

@@ -300,6 +300,42 @@ int gma_forward(const void* Q_X, const void* K_X, const void* V_X, const float* 
   return forward_impl(p, t, causal, static_cast<hipStream_t>(stream), d, false);
 }
 
+int gma_forward_reparam(const void* Q_X, const void* K_X, const void* V_X, const float* mu,
+                        const float* omega, const float* alpha, float eps_sigma, float eps,
+                        int causal, void* out, const gma_dims* d, int32_t* assign_q,
+                        int32_t* assign_k, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  t_err.clear();
+  int st = check_dims(d, eps, causal);
+  if (st != GMA_OK) return st;
+  if (!(eps_sigma > 0.f) || !isfinite(eps_sigma))
+    return fail(GMA_ERR_INVALID_ARG, "eps_sigma must be finite and > 0");
+  if (!Q_X || !K_X || !V_X || !mu || !omega || !alpha || !out || !workspace)
+    return fail(GMA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(Q_X) || !aligned16(K_X) || !aligned16(V_X) || !aligned16(out) ||
+      !aligned16(workspace) || !aligned16(mu) || ((uintptr_t)omega & 3) ||
+      ((uintptr_t)alpha & 3) || ((uintptr_t)assign_q & 3) || ((uintptr_t)assign_k & 3))
+    return fail(GMA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned (omega, alpha: 4)");
+  Plan p;
+  st = make_plan(d, causal, false, p);
+  if (st != GMA_OK) return st;
+  if (workspace_bytes < p.total) return fail(GMA_ERR_WORKSPACE, "workspace too small");
+  Tensors t;
+  t.q = Q_X;
+  t.k = K_X;
+  t.v = V_X;
+  t.mu = mu;
+  t.omega = omega;
+  t.alpha = alpha;
+  t.eps_sigma = eps_sigma;
+  t.out = out;
+  t.assign_q = assign_q;
+  t.assign_k = assign_k;
+  t.eps = eps;
+  t.ws = static_cast<char*>(workspace);
+  return forward_impl(p, t, causal, static_cast<hipStream_t>(stream), d, false);
+}
+
 // ---- the workspace of gma_forward_noalloc ------------------------------------
 // A file-scope device array: each GPU the library runs on holds its own copy.
 // In host code `scratch` is only a host-side stand-in for the symbol; its

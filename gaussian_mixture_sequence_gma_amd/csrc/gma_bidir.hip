@@ -35,12 +35,16 @@ namespace gma {
 template <bool BF>
 __global__ void __launch_bounds__(256) gma_prologue_kernel(
     const float* __restrict__ mu, const float* __restrict__ ls2, const float* __restrict__ lpi,
-    int H, int K, int Kp, int DR, int DRP, char* __restrict__ params, size_t head_bytes) {
+    int H, int K, int Kp, int DR, int DRP, char* __restrict__ params, size_t head_bytes,
+    const float* __restrict__ omega, const float* __restrict__ alpha, float eps_sigma) {
   // one wave per (head, component) row; lanes stride the routing columns
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (row >= H * Kp) return;
   const int h = row / Kp, k = row - h * Kp;
+  // with omega: log sigma^2 and log pi from the unconstrained parameters, by
+  // the reparameterisation kernel's own arithmetic
+  const float lse = omega ? wave_log_norm(alpha + (size_t)h * K, K) : 0.f;
   const int n = Kp * DRP;
   char* base = params + (size_t)h * head_bytes;
   // fp32 path: the kernels contract A with (x^2 - 1) instead of x^2 (keeping the
@@ -51,8 +55,9 @@ __global__ void __launch_bounds__(256) gma_prologue_kernel(
     double a = 0.0, b = 0.0;
     if (k < K && d < DR) {
       const size_t off = ((size_t)h * K + k) * DR + d;
-      const double l = ls2[off], m = mu[off];
-      const double w = (double)expf(-ls2[off]);
+      const float lf = omega ? reparam_log_var(omega[off], eps_sigma) : ls2[off];
+      const double l = lf, m = mu[off];
+      const double w = (double)expf(-lf);
       a = -0.5 * w * kLog2eD;
       b = m * w * kLog2eD;
       acc += m * m * w + l;
@@ -89,7 +94,8 @@ __global__ void __launch_bounds__(256) gma_prologue_kernel(
     float* c = reinterpret_cast<float*>(base + (size_t)8 * n);
     float cv = -INFINITY;
     if (k < K) {
-      const double ck = (double)lpi[(size_t)h * K + k] - 0.5 * acc + (BF ? 0.0 : asum);
+      const float lp = omega ? alpha[(size_t)h * K + k] - lse : lpi[(size_t)h * K + k];
+      const double ck = (double)lp - 0.5 * acc + (BF ? 0.0 : asum);
       cv = (float)(kLog2eD * ck);
     }
     c[k] = cv;
@@ -1485,10 +1491,12 @@ hipError_t launch_prologue(const Plan& p, const Tensors& t, hipStream_t s) {
   const dim3 grid((unsigned)((rows + 3) / 4));
   if (p.bf)
     hipLaunchKernelGGL(gma_prologue_kernel<true>, grid, dim3(256), 0, s, t.mu, t.ls2, t.lpi,
-                       (int)p.H, p.K, p.Kp, p.DR, p.DRP, t.ws + p.off_params, p.head_bytes);
+                       (int)p.H, p.K, p.Kp, p.DR, p.DRP, t.ws + p.off_params, p.head_bytes,
+                       t.omega, t.alpha, t.eps_sigma);
   else
     hipLaunchKernelGGL(gma_prologue_kernel<false>, grid, dim3(256), 0, s, t.mu, t.ls2, t.lpi,
-                       (int)p.H, p.K, p.Kp, p.DR, p.DRP, t.ws + p.off_params, p.head_bytes);
+                       (int)p.H, p.K, p.Kp, p.DR, p.DRP, t.ws + p.off_params, p.head_bytes,
+                       t.omega, t.alpha, t.eps_sigma);
   if (g_launch_hook) g_launch_hook("gma_prologue", s, 0);
   return hipGetLastError();
 }

@@ -120,6 +120,30 @@ __device__ __forceinline__ int xor_lane_i(int v, int mask) {
   int src = (int)(threadIdx.x & 63) ^ mask;
   return __builtin_amdgcn_ds_bpermute(src << 2, v);
 }
+// The reparameterisations used for training ("Learning", Eqs. 14-15): the log
+// variance from its unconstrained parameter, log(log(1 + exp(w)) + eps_sigma)
+// with the softplus as max(w, 0) + log1p(exp(-|w|)), and the log-normaliser
+// of a head's K prior logits (one wave: lane-strided max and sum, then a
+// butterfly over the 64 lanes; every lane returns it).  Shared by the
+// reparameterisation kernel and the prologue, so both give the same bits.
+__device__ __forceinline__ float reparam_log_var(float w, float eps_sigma) {
+  const float sp = fmaxf(w, 0.f) + log1pf(expf(-fabsf(w)));
+  return logf(sp + eps_sigma);
+}
+__device__ __forceinline__ float xor_lane(float v, int mask);
+__device__ __forceinline__ float wave_log_norm(const float* __restrict__ a, int K) {
+  const int lane = threadIdx.x & 63;
+  float m = -INFINITY;
+  for (int k = lane; k < K; k += 64) m = fmaxf(m, a[k]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, xor_lane(m, o));
+  float s = 0.f;
+  for (int k = lane; k < K; k += 64) s += expf(a[k] - m);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += xor_lane(s, o);
+  return m + logf(s);
+}
+
 // Exchanges between the four lane groups g (16-lane rows) without the LDS
 // crossbar: v_permlane16_swap with both operands = v returns, in every lane,
 // the pair {v of the even row, v of the odd row} of its row pair (lanes l and

@@ -55,6 +55,12 @@ struct Tensors {
   // Z [BH,K] of all the keys, unpadded (the carried state of a prefix)
   float* state_v = nullptr;
   float* state_z = nullptr;
+  // forward from the unconstrained parameters (Eqs. 14-15): with omega set, the
+  // prologue takes log sigma^2 = log(softplus(omega) + eps_sigma) and
+  // log pi = alpha - logsumexp(alpha) in place of ls2 and lpi
+  const float* omega = nullptr;
+  const float* alpha = nullptr;
+  float eps_sigma = 0.f;
   // usage statistics: per-workgroup partials and the utilisation threshold
   float* diag = nullptr;
   float thr = 0.f;

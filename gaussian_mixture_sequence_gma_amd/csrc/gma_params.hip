@@ -24,27 +24,15 @@ __global__ void __launch_bounds__(256) gma_reparam_kernel(const float* __restric
                                                           float* __restrict__ lpi) {
   if ((int64_t)blockIdx.x < elem_blocks) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n) {
-      const float w = omega[i];
-      // log(1 + exp(w)) as max(w, 0) + log1p(exp(-|w|)): no overflow for large w
-      const float sp = fmaxf(w, 0.f) + log1pf(expf(-fabsf(w)));
-      ls2[i] = logf(sp + eps_sigma);
-    }
+    // log(1 + exp(w)) as max(w, 0) + log1p(exp(-|w|)): no overflow for large w
+    if (i < n) ls2[i] = reparam_log_var(omega[i], eps_sigma);
     return;
   }
   if (threadIdx.x >= 64) return;
   const int64_t h = (int64_t)blockIdx.x - elem_blocks;
   const int lane = threadIdx.x;
   const float* a = alpha + h * K;
-  float m = -INFINITY;
-  for (int k = lane; k < K; k += 64) m = fmaxf(m, a[k]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, xor_lane(m, o));
-  float s = 0.f;
-  for (int k = lane; k < K; k += 64) s += expf(a[k] - m);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) s += xor_lane(s, o);
-  const float lse = m + logf(s);
+  const float lse = wave_log_norm(a, K);
   for (int k = lane; k < K; k += 64) lpi[h * K + k] = a[k] - lse;
 }
 

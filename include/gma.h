@@ -98,6 +98,22 @@ int gma_forward(const void* Q_X, const void* K_X, const void* V_X,
                 int32_t* assign_q, int32_t* assign_k,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* gma_forward from the unconstrained mixture parameters the optimiser updates
+ * (the reparameterisations used for training, "Learning", Eqs. 14-15): the
+ * prologue derives log sigma^2 = log(log(1 + exp(omega)) + eps_sigma) and
+ * log pi = alpha - log sum exp(alpha) itself, with the arithmetic of
+ * gma_reparameterize, so the result is bit for bit gma_reparameterize followed
+ * by gma_forward, in one launch fewer and without the two derived arrays.
+ *  omega  [H,K,d_r] fp32, alpha [H,K] fp32 (4-byte aligned); eps_sigma > 0,
+ *         finite (else GMA_ERR_INVALID_ARG)
+ * Every other argument, the workspace (gma_forward_workspace_bytes) and the
+ * errors as gma_forward. */
+int gma_forward_reparam(const void* Q_X, const void* K_X, const void* V_X,
+                        const float* mu, const float* omega, const float* alpha,
+                        float eps_sigma, float eps, int causal, void* out,
+                        const gma_dims* d, int32_t* assign_q, int32_t* assign_k,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* gma_forward without a workspace argument, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc).  It runs the same kernels as gma_forward, with the

@@ -111,6 +111,26 @@ def test_forward_rejects_before_launch():
     assert _fwd(workspace_bytes=16) == B.GMA_ERR_WORKSPACE
 
 
+def _fwd_reparam(**over):
+    args = dict(Q_X=A16, K_X=A16, V_X=A16, mu=A16, omega=A16, alpha=A16, eps_sigma=1e-4,
+                eps=1e-6, causal=0, out=A16, dims=_dims(), assign_q=None, assign_k=None,
+                workspace=A16, workspace_bytes=0, stream=0)
+    args.update(over)
+    with pytest.raises(B.GmaError) as ei:
+        B.gma_forward_reparam(**args)
+    return ei.value.status
+
+
+def test_forward_reparam_rejects_before_launch():
+    assert _fwd_reparam(omega=None) == B.GMA_ERR_INVALID_ARG
+    assert _fwd_reparam(alpha=None) == B.GMA_ERR_INVALID_ARG
+    assert _fwd_reparam(eps_sigma=0.0) == B.GMA_ERR_INVALID_ARG
+    assert _fwd_reparam(eps_sigma=float("nan")) == B.GMA_ERR_INVALID_ARG
+    assert _fwd_reparam(omega=A16 + 2) == B.GMA_ERR_INVALID_ARG
+    assert _fwd_reparam(dims=_dims(K=300)) == B.GMA_ERR_UNSUPPORTED
+    assert _fwd_reparam(workspace_bytes=16) == B.GMA_ERR_WORKSPACE
+
+
 def test_layer_and_resp_reject_before_launch():
     d = _dims()
     with pytest.raises(B.GmaError) as ei:

@@ -96,3 +96,17 @@ def test_other_entries_reject():
         api.backward(X, X, t(B, H, N, DV, dtype=bf), *p, t(B, H, N, DV + 1, dtype=bf))
     with pytest.raises(ValueError, match="dO has dtype"):
         api.backward(X, X, t(B, H, N, DV, dtype=bf), *p, t(B, H, N, DV))
+
+
+@pytest.mark.parametrize("over,needle", [
+    (dict(omega=t(H, K + 1, DR)), "omega has shape"),
+    (dict(alpha=t(H, K, dtype=torch.float64)), "alpha must be float32"),
+    (dict(alpha=t(H + 1, K)), "alpha has shape"),
+])
+def test_forward_reparam_rejects(over, needle):
+    a = dict(Q=t(B, H, N, DR, dtype=bf), K=t(B, H, N, DR, dtype=bf), V=t(B, H, N, DV, dtype=bf),
+             mu=t(H, K, DR), omega=t(H, K, DR), alpha=t(H, K))
+    a.update(over)
+    with pytest.raises(ValueError) as e:
+        api.forward_reparam(a["Q"], a["K"], a["V"], a["mu"], a["omega"], a["alpha"], 1e-4)
+    assert needle in str(e.value)

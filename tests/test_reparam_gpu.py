@@ -58,3 +58,38 @@ def test_reparameterized_forward_matches_oracle(causal):
     e = rowwise_rel_err(out.cpu().numpy(), ref)
     print("reparam + forward causal=%d: %.2e" % (causal, e))
     assert e <= TOL["f32"]
+
+
+@pytest.mark.parametrize("dtype,causal,K,d_v", [
+    ("f32", False, 64, 64),
+    ("bf16", False, 128, 128),     # the long-context head shape's K and d_v
+    ("bf16", True, 64, 64),
+    ("f32", True, 100, 32),
+    ("bf16", True, 256, 128),      # K = 256, causal on the product path
+])
+def test_forward_reparam_fused(dtype, causal, K, d_v):
+    """gma_forward_reparam (the prologue derives log sigma^2 and log pi from
+    omega and alpha, Eqs. 14-15) equals gma_reparameterize followed by
+    gma_forward bit for bit, and the oracle forward on the oracle's
+    reparameterised parameters within the forward tolerance."""
+    w = inputs.Workload("reparam_fused", 2, 3, 333, 64, d_v, K, dtype, causal)
+    gen = inputs.generate(w, 4)
+    rng = np.random.default_rng(K + d_v)
+    om = rng.normal(0, 1.0, (w.H, w.K, w.d_r)).astype(np.float32)
+    al = rng.normal(0, 1.5, (w.H, w.K)).astype(np.float32)
+    dev = upload(gen)
+    omd, ald = torch.from_numpy(om).cuda(), torch.from_numpy(al).cuda()
+    fused, aq, ak = api.forward_reparam(dev["Q"], dev["K"], dev["V"], dev["mu"], omd, ald, 1e-4,
+                                        w.eps, causal, assign=True)
+    ls2, lpi = api.reparameterize(omd, ald, 1e-4)
+    two, aq2, ak2 = api.forward(dev["Q"], dev["K"], dev["V"], dev["mu"], ls2, lpi, w.eps, causal,
+                                assign=True)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, two), "fused reparameterisation differs from the two-step path"
+    assert torch.equal(aq, aq2) and torch.equal(ak, ak2)
+    r = oracle.reparameterize(om, al, 1e-4)
+    ref = oracle.forward(gen["Q"].f32, gen["K"].f32, gen["V"].f32, gen["mu"], r["log_sigma2"],
+                         r["log_pi"], w.eps, causal)["out"]
+    e = rowwise_rel_err(fused.float().cpu().numpy(), ref)
+    print("fused reparam + forward %s causal=%d K=%d: %.2e" % (dtype, causal, K, e))
+    assert e <= TOL[dtype]
