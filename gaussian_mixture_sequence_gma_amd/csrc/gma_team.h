@@ -44,16 +44,21 @@ struct WriteTeam {
   static constexpr int NW = 8;                            // waves per workgroup
   static constexpr int NT = NW / TS;                      // teams per workgroup
   static constexpr int COEF = (KP / 16) * NKS * 4;        // 1 KB operand chunks
-  // V tiles: [team][2 buffers] of VT bf16, their own array
-  static constexpr int VSH = NT * 2 * VT;
+  // V tiles: [team][NVB buffers] of VT bf16, their own array; two buffers
+  // where they fit, else one (the team then also waits for its waves' reads
+  // of a tile before the next tile's copies)
+  static constexpr int MAIN0 = COEF * 1024 + KP * 4 + NT * 2 * TS * 32 * 16 + NW * 64 * 4 + 2 * NW * 4;
+  static constexpr int NVB = MAIN0 + NT * 2 * VT * 2 <= 160 * 1024 ? 2 : 1;
+  static constexpr int VSH = NT * NVB * VT;
   // the other LDS: coefficient table, c, exchange records [team][round
   // parity][wave] of 128 floats (m of the 32 keys, then l, then the argmax,
-  // then unused), factor tables [wave][64], flags [wave]
+  // then unused), factor tables [wave][64], flags [wave] for the records and
+  // [wave] for the V tile reads
   static constexpr int OFF_C = COEF * 1024;
   static constexpr int OFF_X = OFF_C + KP * 4;
   static constexpr int OFF_FT = OFF_X + NT * 2 * TS * 32 * 16;
   static constexpr int OFF_F = OFF_FT + NW * 64 * 4;
-  static constexpr int MAIN = OFF_F + NW * 4;
+  static constexpr int MAIN = OFF_F + 2 * NW * 4;
   // epilogue: one wave's V~ slice and Z per slot; the main array holds
   // SLOTS_M slots, the V array SLOTS_V
   static constexpr int SLICE = (CTW * DVT * 4 + CTW) * 64;  // floats
@@ -105,13 +110,14 @@ gma_write_team_kernel(BidirArgs a) {
     for (int idx = threadIdx.x; idx < R::COEF * 64; idx += R::NW * 64) coef[idx] = src[idx];
     const float* cp = reinterpret_cast<const float*>(tb + (size_t)8 * C::Kp * C::DRP);
     for (int j = threadIdx.x; j < R::KP; j += R::NW * 64) cperm[j] = cp[j];
-    if (threadIdx.x < R::NW) flags[threadIdx.x] = 0;
+    if (threadIdx.x < 2 * R::NW) flags[threadIdx.x] = 0;
   }
   __syncthreads();
 
-  bf16* const vbuf = vsh + team * 2 * R::VT;
+  bf16* const vbuf = vsh + team * R::NVB * R::VT;
   float4* xch = reinterpret_cast<float4*>(lds + R::OFF_X) + team * 2 * TS * 32;
   int* tflags = flags + team * TS;
+  int* vflags = flags + R::NW + team * TS;            // one V buffer: reads done
   float* ftab = reinterpret_cast<float*>(lds + R::OFF_FT) + wave * 64;   // [32] factor, [32] argmax
 
   const int64_t G32 = (a.N + 31) / 32;
@@ -185,7 +191,8 @@ gma_write_team_kernel(BidirArgs a) {
     load_v(grp, 0);
   }
   for (; grp < ge; grp += NT, ++round) {
-    const int buf = round & 1;
+    const int buf = round & 1;                        // record parity
+    const int vbi = R::NVB == 2 ? buf : 0;            // V buffer
     asm volatile("" ::: "memory");      // keep the table reads inside the loop
     const bool more = grp + NT < ge;
     wait_vmcnt<R::NDW>();
@@ -356,7 +363,7 @@ gma_write_team_kernel(BidirArgs a) {
     }
 
     // ---- V~_slice += Gamma_slice^T V ---------------------------------------------
-    const bf16* vt = vbuf + buf * R::VT;
+    const bf16* vt = vbuf + vbi * R::VT;
 #pragma unroll
     for (int dt = 0; dt < R::DVT; ++dt) {
       const bf16x8 vb = tr_chunk_swz<R::ROWCH>(vt, 0, dt * 16);
@@ -365,8 +372,17 @@ gma_write_team_kernel(BidirArgs a) {
     }
     // every wave of the team has posted this round, so all have finished the
     // previous round's V~ update: its buffer takes the next group's tile (issued
-    // after this wave's reads of the current tile)
-    if (more) load_v(grp + NT, buf ^ 1);
+    // after this wave's reads of the current tile).  With one buffer the team
+    // first waits for all its waves' reads of this tile.
+    if constexpr (R::NVB == 2) {
+      if (more) load_v(grp + NT, buf ^ 1);
+    } else {
+      team_post(vflags + r, round + 1);
+#pragma unroll
+      for (int w = 0; w < TS; ++w)
+        if (w != r) team_wait(vflags + w, round + 1);
+      if (more) load_v(grp + NT, 0);
+    }
   }
 
   // ---- the teams' slices, added into team 0 in a fixed order (team 1, 2, ...),

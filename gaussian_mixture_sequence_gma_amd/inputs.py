@@ -17,6 +17,7 @@ Workloads (names describe the shape; all use numpy ``default_rng(seed)``):
 * ``long_bidir_bf16``     B1 H32 N32768 d_r64 d_v128 K128 bf16, bidirectional,
   skewed parameters: mu ~ N(0, 1.5), log sigma^2 ~ U(-1.5, 0.5),
   prior logits ~ N(0, 2)
+* ``long_bidir_k256_bf16`` the long-context shape at K256
 * ``layer_causal_bf16``   X[2,16384,1024] bf16, W_Q/W_K/W_V [1024, 16*64] with
   entries ~ N(0, 1/1024) rounded to bf16, H16 d_r64 d_v64 K32, causal
 * ``decode_bf16``         one causal decode step for a serving batch: B64 H32,
@@ -82,6 +83,8 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("lm_causal_bf16", 4, 12, 8192, 64, 64, 64, "bf16", True),
         Workload("lm_causal_k256_bf16", 4, 12, 8192, 64, 64, 256, "bf16", True),
         Workload("long_bidir_bf16", 1, 32, 32768, 64, 128, 128, "bf16", False,
+                 mu_var=1.5, ls2_lo=-1.5, ls2_hi=0.5, logit_var=2.0),
+        Workload("long_bidir_k256_bf16", 1, 32, 32768, 64, 128, 256, "bf16", False,
                  mu_var=1.5, ls2_lo=-1.5, ls2_hi=0.5, logit_var=2.0),
         Workload("layer_causal_bf16", 2, 16, 16384, 64, 64, 32, "bf16", True,
                  d_model=1024, w_var=1.0 / 1024.0),
