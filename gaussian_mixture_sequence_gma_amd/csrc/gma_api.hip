@@ -101,7 +101,8 @@ int make_plan(const gma_dims* d, int causal, bool fp32_compute, Plan& p) {
   const int cs = p.bf ? 32 : 16;
   p.DRP = p.DR < cs ? cs : p.DR;
   p.TG = 4 / p.NG;
-  if (causal && causal_lds_bytes(p.bf, p.DR, p.DV, p.Kp) > kMaxLds) {
+  p.khalf = causal && causal_khalf(p.bf, p.DRP, p.DV, p.Kp);
+  if (causal && !p.khalf && causal_lds_bytes(p.bf, p.DR, p.DV, p.Kp) > kMaxLds) {
     // the scan kernel's tiles do not fit in LDS: the causal forward runs as a
     // chain of products over stored responsibilities, on the bidirectional
     // plan at the length rounded up to the 64-token chunk
@@ -125,7 +126,7 @@ int make_plan(const gma_dims* d, int causal, bool fp32_compute, Plan& p) {
   // workgroup scans in the same round; otherwise about four per compute unit.
   {
     int64_t want_c = (1024 + p.BH - 1) / p.BH;
-    const int lds2 = causal2_lds_bytes(p.bf, p.DRP, p.DV, p.Kp);
+    const int lds2 = causal2_lds_bytes(p.bf, p.DRP, p.DV, p.khalf ? p.Kp / 2 : p.Kp);
     if (lds2 > 0) {
       const int64_t resident = 256 * (2 * lds2 <= kMaxLds ? 2 : 1);
       want_c = resident / p.BH;
@@ -165,6 +166,16 @@ int make_plan(const gma_dims* d, int causal, bool fp32_compute, Plan& p) {
     off += round256((size_t)p.BH * ns * p.Kp * p.DV * 4);
     p.off_carry_z = off;
     off += round256((size_t)p.BH * ns * p.Kp * 4);
+    if (p.khalf) {
+      // per key (maximum, 1 / sum); per query the first half's numerator
+      // [d_v] and (denominator, maximum, best score, its component)
+      p.off_kstat = off;
+      off += round256((size_t)p.BH * p.N * 8);
+      p.off_qpart = off;
+      off += round256((size_t)p.BH * p.N * p.DV * 4);
+      p.off_qpart2 = off;
+      off += round256((size_t)p.BH * p.N * 16);
+    }
   }
   p.total = off;
   return GMA_OK;

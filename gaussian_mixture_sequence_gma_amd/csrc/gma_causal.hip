@@ -43,6 +43,11 @@ struct CausalArgs {
   int out_bf;
   const void* q_lo;       // split routing vectors: low bf16 parts, or null
   const void* k_lo;
+  // scan over one half of the components (K_pad = 256):
+  const float2* kstat;    // per key (maximum, 1 / sum) over all components [BH][N]
+  float* qpart;           // the first half's numerators [BH][N][DV]
+  float4* qpart2;         // and (denominator, maximum, best score, its component) [BH][N]
+  int koff;               // first component of this half
 };
 
 // out[s] = sum_{s' < s} in[s'] over n terms at stride st, summed in order.
@@ -510,10 +515,16 @@ struct Causal2 {
                 "span sizing mirrors this LDS budget");
 };
 
-template <class C, bool XS>
+// HM = 0: all components.  HM = 1, 2: the components koff .. koff + C::Kp - 1
+// of the tables laid out for CF (K_pad = 2 C::Kp), the keys normalised by
+// kstat; the first half (HM = 1) leaves each query's numerator, denominator
+// and maximum in qpart / qpart2, the second (HM = 2) rescales both halves to
+// the larger maximum and writes O.
+template <class C, bool XS, int HM = 0, class CF = C>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 gma_causal2_kernel(CausalArgs a) {
   using R = Causal2<C>;
+  static_assert(HM == 0 || (!XS && CF::Kp == 2 * C::Kp && CF::DRP == C::DRP), "half scan");
   __shared__ __attribute__((aligned(16))) bf16x8 coef[R::COEF * 64];
   __shared__ __attribute__((aligned(16))) float cperm[R::KP];
   __shared__ __attribute__((aligned(16))) bf16 G[R::NB][kTile * R::GLD];
@@ -529,14 +540,17 @@ gma_causal2_kernel(CausalArgs a) {
   const int64_t t_end = a.N < t_begin + (int64_t)a.span_tiles * kTile
                             ? a.N : t_begin + (int64_t)a.span_tiles * kTile;
   const int nchunks = t_end > t_begin ? (int)((t_end - t_begin + kTile - 1) / kTile) : 0;
-  const bool want_aq = a.assign_q != nullptr, want_ak = a.assign_k != nullptr;
+  const bool want_aq = a.assign_q != nullptr;
+  // the half scans leave the keys' assignments to the span-totals pass
+  const bool want_ak = HM == 0 && a.assign_k != nullptr;
+  const int koff = HM ? a.koff : 0;
 
   // ---- tables, carried state -------------------------------------------------
   {
     const char* tb = a.params + (size_t)h * a.head_bytes + a.head_bytes / 2;
-    const bf16x8* src = reinterpret_cast<const bf16x8*>(tb);
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(tb) + (size_t)(koff / 16) * R::NKS * 4 * 64;
     for (int idx = threadIdx.x; idx < R::COEF * 64; idx += kThreads) coef[idx] = src[idx];
-    const float* cp = reinterpret_cast<const float*>(tb + (size_t)8 * C::Kp * C::DRP);
+    const float* cp = reinterpret_cast<const float*>(tb + (size_t)8 * CF::Kp * CF::DRP) + koff;
     for (int j = threadIdx.x; j < R::KP; j += kThreads) cperm[j] = cp[j];
     // the (Z_hi, Z_lo, 1) block: the ones row and the zero rows are constant
     // (rows 0 and 1 belong to write_st, which runs concurrently)
@@ -553,14 +567,14 @@ gma_causal2_kernel(CausalArgs a) {
   f32x4 sacc[R::CTW][R::DVT], zacc[R::CTW];
 #pragma unroll
   for (int j = 0; j < R::CTW; ++j) {
-    const int comp0 = (w * R::CTW + j) * 16;
+    const int comp0 = koff + (w * R::CTW + j) * 16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) zacc[j][i] = a.carry_z[sslot * C::Kp + comp0 + 4 * g + i];
+    for (int i = 0; i < 4; ++i) zacc[j][i] = a.carry_z[sslot * CF::Kp + comp0 + 4 * g + i];
 #pragma unroll
     for (int dt = 0; dt < R::DVT; ++dt)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        sacc[j][dt][i] = a.carry[(sslot * C::Kp + comp0 + 4 * g + i) * C::DV + dt * 16 + c];
+        sacc[j][dt][i] = a.carry[(sslot * CF::Kp + comp0 + 4 * g + i) * C::DV + dt * 16 + c];
   }
   // this wave's rows of the state table: S^T (d rows in pair_row order) and Z.
   // A lane's four components 4g .. 4g+3 of a tile are four consecutive
@@ -657,6 +671,30 @@ gma_causal2_kernel(CausalArgs a) {
     const int64_t rem = t_end - tile0;
     const int nvalid = (int)(rem < kTile ? rem : kTile);
     asm volatile("" ::: "memory");
+    // half scans: this lane's key normaliser over all components; the second
+    // half also the first half's partials of this lane's query (both arrive
+    // while the scores are formed)
+    const int qi = 16 * w + c;                      // this lane's query (and key) in the chunk
+    const size_t qtok = (size_t)bh * a.N + (size_t)(tile0 + qi);
+    float2 kst{3.0e38f, 0.f};
+    f32x4 pnum[HM == 2 ? R::DVT : 1];
+    f32x4 pq{1.f, 0.f, 0.f, 0.f};
+    if constexpr (HM != 0) {
+      if (qi < nvalid) kst = a.kstat[qtok];
+    }
+    if constexpr (HM == 2) {
+#pragma unroll
+      for (int dt = 0; dt < R::DVT; ++dt) pnum[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (qi < nvalid) {
+        const float* prow = a.qpart + qtok * C::DV + 8 * g;
+#pragma unroll
+        for (int qd = 0; qd < R::DVT / 2; ++qd) {
+          pnum[2 * qd] = *reinterpret_cast<const f32x4*>(prow + 32 * qd);
+          pnum[2 * qd + 1] = *reinterpret_cast<const f32x4*>(prow + 32 * qd + 4);
+        }
+        pq = *reinterpret_cast<const f32x4*>(a.qpart2 + qtok);
+      }
+    }
     // features of this wave's 16 queries and 16 keys
     bf16x8 fq[R::NKS][NFX<XS>], fk[R::NKS][NFX<XS>];
 #pragma unroll
@@ -699,8 +737,9 @@ gma_causal2_kernel(CausalArgs a) {
 
     // queries: e = exp2(s - max), packed as the B operand of the contractions
     // over components; keys: normalised responsibilities -> G
-    const int qi = 16 * w + c;                      // this lane's query (and key) in the chunk
     bf16x8 Eq[R::KS];
+    float mq, qbv = 0.f;
+    int qbi = 0;
     {
       float v = SQ[0][0];
 #pragma unroll
@@ -708,6 +747,7 @@ gma_causal2_kernel(CausalArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) v = fmaxf(v, SQ[ct][i]);
       const float m = groups_max(v);
+      mq = m;
 #pragma unroll
       for (int p = 0; p < R::KS; ++p)
 #pragma unroll
@@ -717,22 +757,29 @@ gma_causal2_kernel(CausalArgs a) {
         }
       if (want_aq) {
         float bv = SQ[0][0];
-        int bi = pair_row(0, 4 * g);
+        int bi = koff + pair_row(0, 4 * g);
 #pragma unroll
         for (int ct = 0; ct < R::CT; ++ct)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) argmax_merge(bv, bi, SQ[ct][i], pair_row(ct, 4 * g + i));
+          for (int i = 0; i < 4; ++i)
+            argmax_merge(bv, bi, SQ[ct][i], koff + pair_row(ct, 4 * g + i));
         groups_argmax(bv, bi);
-        if (g == 0 && qi < nvalid) a.assign_q[(size_t)bh * a.N + tile0 + qi] = bi;
+        qbv = bv;
+        qbi = bi;
+        if (HM == 0 && g == 0 && qi < nvalid) a.assign_q[qtok] = bi;
       }
     }
     {
-      float v = SK[0][0];
+      // the half scans take the maximum and the sum over all components from kstat
+      float m = kst.x;
+      if constexpr (HM == 0) {
+        float v = SK[0][0];
 #pragma unroll
-      for (int ct = 0; ct < R::CT; ++ct)
+        for (int ct = 0; ct < R::CT; ++ct)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v = fmaxf(v, SK[ct][i]);
-      const float m = groups_max(v);
+          for (int i = 0; i < 4; ++i) v = fmaxf(v, SK[ct][i]);
+        m = groups_max(v);
+      }
       float l = 0.f;
 #pragma unroll
       for (int ct = 0; ct < R::CT; ++ct)
@@ -742,8 +789,13 @@ gma_causal2_kernel(CausalArgs a) {
           SK[ct][i] = e;
           l += e;
         }
-      l = groups_sum(l);
-      const float inv = qi < nvalid ? fast_rcp(l) : 0.f;
+      float inv;
+      if constexpr (HM == 0) {
+        l = groups_sum(l);
+        inv = qi < nvalid ? fast_rcp(l) : 0.f;
+      } else {
+        inv = qi < nvalid ? kst.y : 0.f;
+      }
       bf16* grow_ = &G[buf][qi * R::GLD + 8 * g];
 #pragma unroll
       for (int p = 0; p < R::KS; ++p) {
@@ -817,22 +869,55 @@ gma_causal2_kernel(CausalArgs a) {
       acc[R::DVT] = mma(ones_r3, Pc, acc[R::DVT]);
     }
     {
+      // denominator: rows 0..3 of the last block (lane group 0), then every lane
+      // takes the value of lane group 0
       const f32x4 dz = acc[R::DVT];
-      float r = fast_rcp(dz[0] + dz[1] + dz[3] + a.eps * dz[2]);
+      float den = dz[0] + dz[1] + dz[3] + a.eps * dz[2];
       float r0, r1;
-      pair_xor16(r, r0, r1);
-      pair_xor32(r0, r, r1);
-      if (qi < nvalid) {
-        bf16* orow = reinterpret_cast<bf16*>(a.out) + ((size_t)bh * a.N + tile0 + qi) * C::DV;
+      pair_xor16(den, r0, r1);
+      pair_xor32(r0, den, r1);
+      if constexpr (HM == 1) {
+        if (qi < nvalid) {
+          float* prow = a.qpart + qtok * C::DV + 8 * g;
 #pragma unroll
-        for (int qd = 0; qd < R::DVT / 2; ++qd) {
-          bf16x8 o8;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            o8[i] = to_bf16(acc[2 * qd][i] * r);
-            o8[4 + i] = to_bf16(acc[2 * qd + 1][i] * r);
+          for (int qd = 0; qd < R::DVT / 2; ++qd) {
+            *reinterpret_cast<f32x4*>(prow + 32 * qd) = acc[2 * qd];
+            *reinterpret_cast<f32x4*>(prow + 32 * qd + 4) = acc[2 * qd + 1];
           }
-          st16(orow + 32 * qd + 8 * g, o8);
+          if (g == 0) a.qpart2[qtok] = float4{den, mq, qbv, __int_as_float(qbi)};
+        }
+      } else {
+        // second half: both halves rescaled to the larger maximum
+        float s0 = 0.f, s1 = 1.f;
+        if constexpr (HM == 2) {
+          const float M = fmaxf(mq, pq[1]);
+          s0 = exp2_fast(pq[1] - M);
+          s1 = exp2_fast(mq - M);
+          den = s0 * pq[0] + s1 * den;
+        }
+        const float r = fast_rcp(den);
+        s0 *= r;
+        s1 *= r;
+        if (qi < nvalid) {
+          bf16* orow = reinterpret_cast<bf16*>(a.out) + qtok * C::DV;
+#pragma unroll
+          for (int qd = 0; qd < R::DVT / 2; ++qd) {
+            bf16x8 o8;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if constexpr (HM == 2) {
+                o8[i] = to_bf16(acc[2 * qd][i] * s1 + pnum[2 * qd][i] * s0);
+                o8[4 + i] = to_bf16(acc[2 * qd + 1][i] * s1 + pnum[2 * qd + 1][i] * s0);
+              } else {
+                o8[i] = to_bf16(acc[2 * qd][i] * s1);
+                o8[4 + i] = to_bf16(acc[2 * qd + 1][i] * s1);
+              }
+            }
+            st16(orow + 32 * qd + 8 * g, o8);
+          }
+          // the lowest component at the overall maximum: the first half's on a tie
+          if (HM == 2 && want_aq && g == 0)
+            a.assign_q[qtok] = qbv > pq[2] ? qbi : __float_as_int(pq[3]);
         }
       }
     }
@@ -864,13 +949,20 @@ gma_causal2_kernel(CausalArgs a) {
 
 template <class C>
 static hipError_t run_causal(const Plan& p, const Tensors& t, hipStream_t s) {
-  if constexpr (causal_lds_bytes(C::kBF, C::DR, C::DV, C::Kp) > kMaxLds) {
+  // K_pad = 256 where the scan tables exceed LDS: the scan runs once per half
+  // of the components (CH), the keys normalised over all of them by the
+  // span-totals pass
+  constexpr bool KH = causal_khalf(C::kBF, C::DRP, C::DV, C::Kp);
+  using CH = Cfg<C::kBF, (C::CPW > 1 ? C::CPW / 2 : 1), 4, C::DR, C::DV>;
+  static_assert(!KH || (WriteTeam<C>::kOK && Causal2<CH>::kOK && CH::Kp * 2 == C::Kp),
+                "K-half scan");
+  if constexpr (!KH && causal_lds_bytes(C::kBF, C::DR, C::DV, C::Kp) > kMaxLds) {
     return hipErrorNotSupported;     // rejected earlier by validation
   } else {
   // 1. span totals through the latent-write kernel (one split per span)
   BidirArgs wa{};
   const bool split = t.k_lo != nullptr;
-  if (split && !(Causal2<C>::kOK && (WriteTeam<C>::kOK || Write2<C>::kOK)))
+  if (split && (KH || !(Causal2<C>::kOK && (WriteTeam<C>::kOK || Write2<C>::kOK))))
     return hipErrorNotSupported;
   wa.x = t.k;
   wa.x_lo = t.k_lo;
@@ -887,11 +979,19 @@ static hipError_t run_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   wa.assign = nullptr;
   const dim3 grid(p.nspan, (unsigned)p.BH);
   if (g_launch_hook) g_launch_hook("gma_span_state", s, 1);
-  // the token-owner write pays a per-workgroup set-up (its coefficient table):
-  // use it for spans of at least four 32-token steps per wave, or eight where
-  // it runs one wave per SIMD; one split per span
-  if (WriteTeam<C>::kOK && (split || p.span_tiles >= 4)) {
-    // team write: one split per span; a span is 2 span_tiles 32-key groups
+  if constexpr (KH) {
+    // also each key's maximum and 1 / sum over all components, and its
+    // assignment
+    wa.gpw = 2 * p.span_tiles;
+    wa.kstat = reinterpret_cast<float2*>(t.ws + p.off_kstat);
+    wa.assign = t.assign_k;
+    if (t.assign_k) hipLaunchKernelGGL((gma_write_team_kernel<C, false, true>), grid, dim3(512), 0, s, wa);
+    else hipLaunchKernelGGL((gma_write_team_kernel<C, false, false>), grid, dim3(512), 0, s, wa);
+  } else if (WriteTeam<C>::kOK && (split || p.span_tiles >= 4)) {
+    // the token-owner write pays a per-workgroup set-up (its coefficient
+    // table): use it for spans of at least four 32-token steps per wave, or
+    // eight where it runs one wave per SIMD; one split per span.  Team write:
+    // a span is 2 span_tiles 32-key groups.
     wa.gpw = 2 * p.span_tiles;
     if constexpr (WriteTeam<C>::kOK) {
       if (split) hipLaunchKernelGGL((gma_write_team_kernel<C, true, false>), grid, dim3(512), 0, s, wa);
@@ -944,7 +1044,16 @@ static hipError_t run_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   ca.q_lo = t.q_lo;
   ca.k_lo = t.k_lo;
   if (g_launch_hook) g_launch_hook("gma_causal", s, 1);
-  if constexpr (Causal2<C>::kOK) {
+  if constexpr (KH) {
+    // the first half leaves its partials, the second combines them
+    ca.kstat = reinterpret_cast<const float2*>(t.ws + p.off_kstat);
+    ca.qpart = reinterpret_cast<float*>(t.ws + p.off_qpart);
+    ca.qpart2 = reinterpret_cast<float4*>(t.ws + p.off_qpart2);
+    ca.koff = 0;
+    hipLaunchKernelGGL((gma_causal2_kernel<CH, false, 1, C>), grid, dim3(kThreads), 0, s, ca);
+    ca.koff = CH::Kp;
+    hipLaunchKernelGGL((gma_causal2_kernel<CH, false, 2, C>), grid, dim3(kThreads), 0, s, ca);
+  } else if constexpr (Causal2<C>::kOK) {
     if (split) hipLaunchKernelGGL((gma_causal2_kernel<C, true>), grid, dim3(kThreads), 0, s, ca);
     else hipLaunchKernelGGL((gma_causal2_kernel<C, false>), grid, dim3(kThreads), 0, s, ca);
   } else {

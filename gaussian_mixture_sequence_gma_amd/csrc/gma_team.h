@@ -324,8 +324,12 @@ gma_write_team_kernel(BidirArgs a) {
         if (mw[w] == M) best = iw[w];     // the lowest wave at the maximum wins
       }
       const int64_t tok = grp * 32 + key;
-      ftab[key] = tok < a.N ? own * fast_rcp(L) : 0.f;
+      const float invL = fast_rcp(L);
+      ftab[key] = tok < a.N ? own * invL : 0.f;
       if (want_assign) ftab[32 + key] = __int_as_float(best);
+      // the key's maximum and normaliser over all components, for a scan that
+      // forms its responsibilities one half of the components at a time
+      if (a.kstat != nullptr && r == 0 && tok < a.N) a.kstat[(size_t)bh * a.N + tok] = float2{M, invL};
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");

@@ -88,6 +88,14 @@ __host__ __device__ constexpr int causal2_lds_bytes(bool bf, int DRP, int DV, in
                            ? causal2_lds_bytes_nb(DRP, DV, Kp, 1)
                            : 0));
 }
+// bf16 causal forward at K_pad = 256 whose scan tables exceed LDS while those
+// of 128 components fit: the scan runs once per half of the components, with
+// the keys' normalisers over all K taken from the span-totals pass (the team
+// write, which needs d_v of 64 or 128 at this K)
+__host__ __device__ constexpr bool causal_khalf(bool bf, int DRP, int DV, int Kp) {
+  return bf && Kp == 256 && DRP <= 64 && (DV == 64 || DV == 128) &&
+         causal2_lds_bytes(true, DRP, DV, Kp) == 0 && causal2_lds_bytes(true, DRP, DV, Kp / 2) > 0;
+}
 
 struct BidirArgs {
   const void* x;          // K_X (write) or Q_X (read / resp), [BH][N][DR]
@@ -113,6 +121,9 @@ struct BidirArgs {
   int gpw;                // token-owner write: 32-token groups per split (0: derived)
   float eps;
   int out_bf;
+  float2* kstat;          // team write: per key, the maximum of its log2-domain scores
+                          // over all components and 1 / sum exp2(score - maximum),
+                          // [BH][N]; or null
 };
 
 template <class C>

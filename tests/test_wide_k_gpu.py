@@ -3,15 +3,15 @@
 Mistura Gaussiana (GMA)", section "Resultados e Desempenho", uses K = 256).
 
 Both variants and both input types.  Where the causal scan kernel's tiles do
-not fit in LDS (fp32 and bf16 at the larger K x d_v), the causal forward runs
-as a chain of fp32 products over stored responsibilities; the parity bar is
-the same.
+not fit in LDS, bf16 at d_r = 64 (or d_v = 128) runs the scan once per half of
+the components, and fp32 runs the causal forward as a chain of fp32 products
+over stored responsibilities; the parity bar is the same.
 """
 import pytest
 import torch
 
-from gaussian_mixture_sequence_gma_amd import binding as B, inputs
-from tests.parity import run_and_compare
+from gaussian_mixture_sequence_gma_amd import api, binding as B, inputs
+from tests.parity import run_and_compare, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -46,3 +46,52 @@ def test_long_head_k256(causal):
     """K = 256 with the long-context head's d_v = 128 and skewed parameters."""
     w = W["long_bidir_bf16"].with_(H=2, N=2000, K=256, causal=causal)
     run_and_compare(w)
+
+
+# bf16 causal at K_pad = 256 and d_r = 64, where the scan's tables exceed LDS:
+# the scan runs once per half of the components, the keys normalised over all
+# K by the span-totals pass and the halves' query terms rescaled to a common
+# maximum before O is formed.
+
+@pytest.mark.parametrize("d_v", [64, 128])
+@pytest.mark.parametrize("K", [129, 200, 256])
+def test_causal_khalf_several_chunks_per_span(K, d_v):
+    """64 sequences, so each span holds several 64-token chunks (the last span
+    fewer) and the final chunk is ragged; two heads compared in full."""
+    w = W["lm_causal_bf16"].with_(B=4, H=16, N=600, K=K, d_v=d_v)
+    run_and_compare(w, heads=2)
+
+
+def test_causal_khalf_full_lm_shape():
+    """The language-model shape at K = 256 (B4 H12 N8192, d_r = d_v = 64), as the
+    benchmark launches it; two heads compared in full."""
+    run_and_compare(W["lm_causal_k256_bf16"], heads=2)
+
+
+def test_causal_khalf_ignores_future_tokens_bitwise():
+    w = W["lm_causal_k256_bf16"].with_(B=1, H=2, N=3000)
+    gen = inputs.generate(w, 0)
+    dev = upload(gen)
+    base, aq0, ak0 = api.forward(dev["Q"], dev["K"], dev["V"], dev["mu"], dev["log_sigma2"],
+                                 dev["log_pi"], w.eps, True, assign=True)
+    for i in (0, 63, 64, 1000, 2999):
+        Q, K, V = dev["Q"].clone(), dev["K"].clone(), dev["V"].clone()
+        g = torch.Generator(device="cuda").manual_seed(i)
+        for t in (Q, K, V):
+            t[:, :, i + 1:] = torch.randn(t[:, :, i + 1:].shape, generator=g, device="cuda",
+                                          dtype=torch.float32).to(t.dtype)
+        out, aq, ak = api.forward(Q, K, V, dev["mu"], dev["log_sigma2"], dev["log_pi"], w.eps,
+                                  True, assign=True)
+        assert torch.equal(out[:, :, :i + 1].view(torch.int16), base[:, :, :i + 1].view(torch.int16))
+        assert torch.equal(aq[:, :, :i + 1], aq0[:, :, :i + 1])
+        assert torch.equal(ak[:, :, :i + 1], ak0[:, :, :i + 1])
+
+
+def test_causal_khalf_bitwise_deterministic():
+    w = W["lm_causal_k256_bf16"].with_(B=2, H=3, N=4000)
+    gen = inputs.generate(w, 0)
+    dev = upload(gen)
+    outs = [api.forward(dev["Q"], dev["K"], dev["V"], dev["mu"], dev["log_sigma2"],
+                        dev["log_pi"], w.eps, True).clone() for _ in range(3)]
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
