@@ -101,7 +101,7 @@ int make_plan(const gma_dims* d, int causal, bool fp32_compute, Plan& p) {
   const int cs = p.bf ? 32 : 16;
   p.DRP = p.DR < cs ? cs : p.DR;
   p.TG = 4 / p.NG;
-  p.khalf = causal && causal_khalf(p.bf, p.DRP, p.DV, p.Kp);
+  p.khalf = causal ? causal_khalf(p.bf, p.DRP, p.DV, p.Kp) : bidir_khalf(p.bf, p.DRP, p.DV, p.Kp);
   if (causal && !p.khalf && causal_lds_bytes(p.bf, p.DR, p.DV, p.Kp) > kMaxLds) {
     // the scan kernel's tiles do not fit in LDS: the causal forward runs as a
     // chain of products over stored responsibilities, on the bidirectional
@@ -156,6 +156,14 @@ int make_plan(const gma_dims* d, int causal, bool fp32_compute, Plan& p) {
     // steps x 1 KB per sequence
     p.off_vtab = off;
     off += round256((size_t)p.BH * (p.DV / 16 + 1) * ((p.Kp + 31) / 32) * 1024);
+    if (p.khalf) {
+      // the first half's numerators and (denominator, maximum, best score,
+      // its component) per query
+      p.off_qpart = off;
+      off += round256((size_t)p.BH * p.N * p.DV * 4);
+      p.off_qpart2 = off;
+      off += round256((size_t)p.BH * p.N * 16);
+    }
   } else {
     const size_t ns = (size_t)p.nspan;
     p.off_state = off;

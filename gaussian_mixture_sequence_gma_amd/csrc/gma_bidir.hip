@@ -565,19 +565,27 @@ struct Read2 {
   static constexpr int COEF = CT * NKS * 4;              // 1 KB operand chunks
   static constexpr int VCH = OT * KS;
   static constexpr int LDS = (COEF + VCH) * 1024 + KP * 4;
-  static constexpr bool kOK = C::kBF && C::Kp % 32 == 0 && C::DRP <= 64 && LDS <= 150 * 1024;
+  static_assert(LDS == read2_lds_bytes(C::DRP, C::DV, KP), "read-out LDS sizing");
+  static constexpr bool kOK = C::kBF && C::Kp % 32 == 0 && C::DRP <= 64 && LDS <= kRead2MaxLds;
 };
 // Waves per SIMD of the read-out (one workgroup of 4 * WPE waves per compute
 // unit): three where the registers allow (plain routing vectors), two for
-// split ones (their features take more registers).
-template <bool XS> constexpr int kRead2WPE = XS ? 2 : 3;
+// split ones (their features take more registers) and for the second half of
+// a split K (it also holds the first half's partials).
+template <bool XS, int HM = 0> constexpr int kRead2WPE = XS || HM == 2 ? 2 : 3;
 
-template <class C, bool XS>
-__global__ void __launch_bounds__(256 * kRead2WPE<XS>, 1)
-__attribute__((amdgpu_waves_per_eu(kRead2WPE<XS>, kRead2WPE<XS>)))
+// HM = 0: all components.  HM = 1, 2: the components koff .. koff + C::Kp - 1
+// of the tables laid out for CF (K_pad = 2 C::Kp); the first half (HM = 1)
+// leaves each query's numerator, denominator and maximum in qpart / qpart2,
+// the second (HM = 2) rescales both halves to the larger maximum and writes O.
+template <class C, bool XS, int HM = 0, class CF = C>
+__global__ void __launch_bounds__(256 * (kRead2WPE<XS, HM>), 1)
+__attribute__((amdgpu_waves_per_eu((kRead2WPE<XS, HM>), (kRead2WPE<XS, HM>))))
 gma_read2_kernel(BidirArgs a) {
   using R = Read2<C>;
-  constexpr int NW = 4 * kRead2WPE<XS>;
+  static_assert(HM == 0 || (!XS && CF::Kp == 2 * C::Kp && CF::DRP == C::DRP && R::DVT >= 2),
+                "half read-out");
+  constexpr int NW = 4 * kRead2WPE<XS, HM>;
   __shared__ __attribute__((aligned(16))) bf16x8 coef[R::COEF * 64];
   __shared__ __attribute__((aligned(16))) bf16x8 vtab[R::VCH * 64];
   __shared__ __attribute__((aligned(16))) float cperm[R::KP];
@@ -587,16 +595,23 @@ gma_read2_kernel(BidirArgs a) {
   const int64_t bh = blockIdx.y;
   const int h = (int)(bh % a.H);
   const bool want_assign = a.assign != nullptr;
+  const int koff = HM ? a.koff : 0;
 
-  // ---- tables: contiguous copies of what the prologue and the reduction wrote ----
+  // ---- tables: copies of what the prologue and the reduction wrote (a half:
+  // its component tiles of the coefficients, its contraction steps of each
+  // V~ block) ----
   {
+    constexpr int KSF = CF::Kp / 32;                 // contraction steps of the stored table
     const char* tb = a.params + (size_t)h * a.head_bytes + a.head_bytes / 2;
-    const bf16x8* src = reinterpret_cast<const bf16x8*>(tb);
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(tb) + (size_t)(koff / 16) * R::NKS * 4 * 64;
     for (int idx = threadIdx.x; idx < R::COEF * 64; idx += NW * 64) coef[idx] = src[idx];
-    const float* cp = reinterpret_cast<const float*>(tb + (size_t)8 * C::Kp * C::DRP);
+    const float* cp = reinterpret_cast<const float*>(tb + (size_t)8 * CF::Kp * CF::DRP) + koff;
     for (int j = threadIdx.x; j < R::KP; j += NW * 64) cperm[j] = cp[j];
-    const bf16x8* vsrc = a.vtab + (size_t)bh * R::VCH * 64;
-    for (int idx = threadIdx.x; idx < R::VCH * 64; idx += NW * 64) vtab[idx] = vsrc[idx];
+    const bf16x8* vsrc = a.vtab + (size_t)bh * R::OT * KSF * 64 + (koff / 32) * 64;
+    for (int idx = threadIdx.x; idx < R::VCH * 64; idx += NW * 64) {
+      const int blk = idx / (R::KS * 64), rem = idx - blk * (R::KS * 64);
+      vtab[idx] = vsrc[blk * KSF * 64 + rem];
+    }
   }
   __syncthreads();
 
@@ -649,7 +664,7 @@ gma_read2_kernel(BidirArgs a) {
     // operands of step j + 1 are read while the MFMAs of step j run.
     constexpr int NCP = R::CT / 2;
     constexpr int NSTEP = NCP * R::NKS;
-    constexpr int NBUF = kRead2WPE<XS> >= 3 ? 1 : 2;
+    constexpr int NBUF = kRead2WPE<XS, HM> >= 3 ? 1 : 2;
     auto load_w = [&](int j, bf16x8 (&w)[2][4]) {
       const int cp = 2 * (j % NCP), s = j / NCP;
 #pragma unroll
@@ -690,6 +705,7 @@ gma_read2_kernel(BidirArgs a) {
     // groups), e = exp2(s - m) packed as the read-out operand
     bf16x8 E[2][R::KS];
     int am[2] = {0, 0};
+    float mx[2], bvs[2] = {0.f, 0.f};
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       float v = S[tt][0][0];
@@ -698,15 +714,18 @@ gma_read2_kernel(BidirArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) v = fmaxf(v, S[tt][ct][i]);
       const float m = groups_max(v);
+      mx[tt] = m;
       if (want_assign) {
         float bv = S[tt][0][0];
-        int bi = pair_row(0, 4 * g);
+        int bi = koff + pair_row(0, 4 * g);
 #pragma unroll
         for (int ct = 0; ct < R::CT; ++ct)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) argmax_merge(bv, bi, S[tt][ct][i], pair_row(ct, 4 * g + i));
+          for (int i = 0; i < 4; ++i)
+            argmax_merge(bv, bi, S[tt][ct][i], koff + pair_row(ct, 4 * g + i));
         groups_argmax(bv, bi);
         am[tt] = bi;
+        bvs[tt] = bv;
       }
 #pragma unroll
       for (int p = 0; p < R::KS; ++p)
@@ -715,6 +734,29 @@ gma_read2_kernel(BidirArgs a) {
           E[tt][p][i] = to_bf16(exp2_fast(S[tt][2 * p][i] - m));
           E[tt][p][4 + i] = to_bf16(exp2_fast(S[tt][2 * p + 1][i] - m));
         }
+    }
+
+    // second half: the first half's partials of this lane's queries, in flight
+    // during the contraction below
+    f32x4 pnum[2][HM == 2 ? R::DVT : 1];
+    f32x4 pq[2] = {f32x4{1.f, 0.f, 0.f, 0.f}, f32x4{1.f, 0.f, 0.f, 0.f}};
+    if constexpr (HM == 2) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int64_t tok = grp * 32 + 16 * tt + c;
+#pragma unroll
+        for (int dt = 0; dt < R::DVT; ++dt) pnum[tt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (tok < a.N) {
+          const size_t qt = (size_t)bh * a.N + tok;
+          const float* prow = a.qpart + qt * C::DV + 8 * g;
+#pragma unroll
+          for (int qd = 0; qd < R::DVT / 2; ++qd) {
+            pnum[tt][2 * qd] = *reinterpret_cast<const f32x4*>(prow + 32 * qd);
+            pnum[tt][2 * qd + 1] = *reinterpret_cast<const f32x4*>(prow + 32 * qd + 4);
+          }
+          pq[tt] = *reinterpret_cast<const f32x4*>(a.qpart2 + qt);
+        }
+      }
     }
 
     // O^T (and the denominator block) = V~^T E^T
@@ -744,31 +786,63 @@ gma_read2_kernel(BidirArgs a) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const f32x4 dz = O[tt][R::DVT];
-      float r = fast_rcp(dz[0] + dz[1] + a.eps * dz[2]);
+      float den = dz[0] + dz[1] + a.eps * dz[2];
       float r0, r1;
-      pair_xor16(r, r0, r1);
-      pair_xor32(r0, r, r1);          // every lane: the value of lane group 0
+      pair_xor16(den, r0, r1);
+      pair_xor32(r0, den, r1);        // every lane: the value of lane group 0
       const int64_t tok = grp * 32 + 16 * tt + c;
-      if (tok < a.N) {
-        bf16* orow = out + (size_t)tok * C::DV;
-        if constexpr (R::DVT >= 2) {
+      if constexpr (HM == 1) {
+        if (tok < a.N) {
+          const size_t qt = (size_t)bh * a.N + tok;
+          float* prow = a.qpart + qt * C::DV + 8 * g;
 #pragma unroll
           for (int qd = 0; qd < R::DVT / 2; ++qd) {
-            bf16x8 o8;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              o8[i] = to_bf16(O[tt][2 * qd][i] * r);
-              o8[4 + i] = to_bf16(O[tt][2 * qd + 1][i] * r);
-            }
-            st16(orow + 32 * qd + 8 * g, o8);
+            *reinterpret_cast<f32x4*>(prow + 32 * qd) = O[tt][2 * qd];
+            *reinterpret_cast<f32x4*>(prow + 32 * qd + 4) = O[tt][2 * qd + 1];
           }
-        } else {
-          bf16x4 o4;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o4[i] = to_bf16(O[tt][0][i] * r);
-          *reinterpret_cast<bf16x4*>(orow + 4 * g) = o4;
+          if (g == 0) a.qpart2[qt] = float4{den, mx[tt], bvs[tt], __int_as_float(am[tt])};
         }
-        if (want_assign && g == 0) a.assign[(size_t)bh * a.N + tok] = am[tt];
+      } else {
+        // second half: both halves rescaled to the larger maximum
+        float s0 = 0.f, s1 = 1.f;
+        if constexpr (HM == 2) {
+          const float M = fmaxf(mx[tt], pq[tt][1]);
+          s0 = exp2_fast(pq[tt][1] - M);
+          s1 = exp2_fast(mx[tt] - M);
+          den = s0 * pq[tt][0] + s1 * den;
+        }
+        const float r = fast_rcp(den);
+        s0 *= r;
+        s1 *= r;
+        if (tok < a.N) {
+          bf16* orow = out + (size_t)tok * C::DV;
+          if constexpr (R::DVT >= 2) {
+#pragma unroll
+            for (int qd = 0; qd < R::DVT / 2; ++qd) {
+              bf16x8 o8;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                if constexpr (HM == 2) {
+                  o8[i] = to_bf16(O[tt][2 * qd][i] * s1 + pnum[tt][2 * qd][i] * s0);
+                  o8[4 + i] = to_bf16(O[tt][2 * qd + 1][i] * s1 + pnum[tt][2 * qd + 1][i] * s0);
+                } else {
+                  o8[i] = to_bf16(O[tt][2 * qd][i] * s1);
+                  o8[4 + i] = to_bf16(O[tt][2 * qd + 1][i] * s1);
+                }
+              }
+              st16(orow + 32 * qd + 8 * g, o8);
+            }
+          } else {
+            bf16x4 o4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o4[i] = to_bf16(O[tt][0][i] * s1);
+            *reinterpret_cast<bf16x4*>(orow + 4 * g) = o4;
+          }
+          // the lowest component at the overall maximum: the first half's on a tie
+          if (want_assign && g == 0)
+            a.assign[(size_t)bh * a.N + tok] =
+                HM == 2 && !(bvs[tt] > pq[tt][2]) ? __float_as_int(pq[tt][3]) : am[tt];
+        }
       }
     }
   }
@@ -1041,6 +1115,11 @@ static hipError_t run_bidir(const Plan& p, const Tensors& t, hipStream_t s) {
   // sequence).  Split routing vectors (the
   // layer's projections) run only on the token-owner kernels.
   int PS = C::kBF ? p.S : p.S * C::TG;          // partial slots per sequence
+  // K_pad = 256 where the read-out's tables exceed LDS: it runs once per half
+  // of the components (CH)
+  constexpr bool KHR = bidir_khalf(C::kBF, C::DRP, C::DV, C::Kp);
+  using CH = Cfg<C::kBF, (C::CPW > 1 ? C::CPW / 2 : 1), C::NG, C::DR, C::DV>;
+  static_assert(!KHR || (Read2<CH>::kOK && CH::Kp * 2 == C::Kp), "half read-out");
   if (split && !((WriteTeam<C>::kOK || Write2<C>::kOK) && Read2<C>::kOK))
     return hipErrorNotSupported;
   if (g_launch_hook) g_launch_hook("gma_write", s, 1);
@@ -1091,8 +1170,9 @@ static hipError_t run_bidir(const Plan& p, const Tensors& t, hipStream_t s) {
                      a.partial, a.partial_z, PS, C::Kp, C::DV,
                      reinterpret_cast<float*>(t.ws + p.off_vt),
                      reinterpret_cast<float*>(t.ws + p.off_z),
-                     Read2<C>::kOK && !t.state_v ? reinterpret_cast<bf16*>(t.ws + p.off_vtab)
-                                                 : nullptr,
+                     (Read2<C>::kOK || KHR) && !t.state_v
+                         ? reinterpret_cast<bf16*>(t.ws + p.off_vtab)
+                         : nullptr,
                      t.state_v, t.state_z, p.K);
   if (g_launch_hook) g_launch_hook("gma_reduce", s, 0);
   e = hipGetLastError();
@@ -1105,7 +1185,23 @@ static hipError_t run_bidir(const Plan& p, const Tensors& t, hipStream_t s) {
   a.out = t.out;
   a.assign = t.assign_q;
   if (g_launch_hook) g_launch_hook("gma_read", s, 1);
-  if constexpr (Read2<C>::kOK) {
+  if constexpr (KHR) {
+    // the first half leaves its partials, the second combines them; grids as
+    // below
+    const int64_t g32 = (p.N + 31) / 32;
+    int64_t s2 = (256 + p.BH - 1) / p.BH;
+    const int64_t cap = (g32 + 7) / 8;
+    if (s2 > cap) s2 = cap;
+    if (s2 < 1) s2 = 1;
+    a.qpart = reinterpret_cast<float*>(t.ws + p.off_qpart);
+    a.qpart2 = reinterpret_cast<float4*>(t.ws + p.off_qpart2);
+    a.koff = 0;
+    hipLaunchKernelGGL((gma_read2_kernel<CH, false, 1, C>), dim3((unsigned)s2, (unsigned)p.BH),
+                       dim3(256 * kRead2WPE<false, 1>), 0, s, a);
+    a.koff = CH::Kp;
+    hipLaunchKernelGGL((gma_read2_kernel<CH, false, 2, C>), dim3((unsigned)s2, (unsigned)p.BH),
+                       dim3(256 * kRead2WPE<false, 2>), 0, s, a);
+  } else if constexpr (Read2<C>::kOK) {
     // about one workgroup per compute unit, at least eight 32-query groups each
     const int64_t g32 = (p.N + 31) / 32;
     int64_t s2 = (256 + p.BH - 1) / p.BH;

@@ -27,12 +27,13 @@ struct Plan {
   int span_tiles = 0;       // 64-token chunks per causal span
   int nspan = 0;            // spans per sequence
   bool prod = false;        // causal on the product path (the scan kernel does not fit)
-  bool khalf = false;       // causal scan once per half of K_pad = 256 (causal_khalf)
+  bool khalf = false;       // causal scan or read-out once per half of K_pad = 256
+                            // (causal_khalf, bidir_khalf)
   // workspace layout (bytes)
   size_t head_bytes = 0;
   size_t off_params = 0, off_partial = 0, off_partial_z = 0, off_vt = 0, off_z = 0, off_vtab = 0;
   size_t off_state = 0, off_state_z = 0, off_carry = 0, off_carry_z = 0;
-  size_t off_kstat = 0, off_qpart = 0, off_qpart2 = 0;   // khalf: key normalisers, query partials
+  size_t off_kstat = 0, off_qpart = 0, off_qpart2 = 0;   // khalf: key normalisers (causal), query partials
   size_t total = 0;
 };
 

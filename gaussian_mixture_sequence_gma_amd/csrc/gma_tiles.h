@@ -88,6 +88,19 @@ __host__ __device__ constexpr int causal2_lds_bytes(bool bf, int DRP, int DV, in
                            ? causal2_lds_bytes_nb(DRP, DV, Kp, 1)
                            : 0));
 }
+// LDS bytes of the bf16 token-owner read-out (gma_read2_kernel): the
+// coefficient operand table, the V~ operand table with its (Z_hi, Z_lo, 1)
+// block, and the constants.  Mirrors Read2 in gma_bidir.hip.
+__host__ __device__ constexpr int read2_lds_bytes(int DRP, int DV, int Kp) {
+  return ((Kp / 16) * (DRP / 32) * 4 + (DV / 16 + 1) * (Kp / 32)) * 1024 + Kp * 4;
+}
+constexpr int kRead2MaxLds = 150 * 1024;
+// bf16 bidirectional read-out at K_pad = 256 whose tables exceed that bound
+// while those of 128 components fit: it runs once per half of the components
+__host__ __device__ constexpr bool bidir_khalf(bool bf, int DRP, int DV, int Kp) {
+  return bf && Kp == 256 && DRP <= 64 && DV >= 32 && read2_lds_bytes(DRP, DV, Kp) > kRead2MaxLds &&
+         read2_lds_bytes(DRP, DV, Kp / 2) <= kRead2MaxLds;
+}
 // bf16 causal forward at K_pad = 256 whose scan tables exceed LDS while those
 // of 128 components fit: the scan runs once per half of the components, with
 // the keys' normalisers over all K taken from the span-totals pass (the team
@@ -124,6 +137,10 @@ struct BidirArgs {
   float2* kstat;          // team write: per key, the maximum of its log2-domain scores
                           // over all components and 1 / sum exp2(score - maximum),
                           // [BH][N]; or null
+  // read-out over one half of the components (K_pad = 256):
+  float* qpart;           // the first half's numerators [BH][N][DV]
+  float4* qpart2;         // and (denominator, maximum, best score, its component) [BH][N]
+  int koff;               // first component of this half
 };
 
 template <class C>

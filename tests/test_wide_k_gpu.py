@@ -95,3 +95,21 @@ def test_causal_khalf_bitwise_deterministic():
                         dev["log_pi"], w.eps, True).clone() for _ in range(3)]
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+
+
+# bf16 bidirectional at d_r = 64 and K_pad = 256, where the read-out's tables
+# exceed LDS: it runs once per half of the components, the first half leaving
+# its numerators, denominators and maxima for the second.
+
+@pytest.mark.parametrize("d_v", [32, 64, 128])
+@pytest.mark.parametrize("K", [129, 200, 256])
+def test_bidir_khalf_read(K, d_v):
+    """A ragged length over several workgroups per sequence; assignments included."""
+    w = W["long_bidir_bf16"].with_(H=3, N=2333, K=K, d_v=d_v)
+    run_and_compare(w)
+
+
+def test_bidir_khalf_full_long_shape():
+    """The long-context shape at K = 256 (B1 H32 N32768, d_v = 128) as the
+    benchmark launches it; two heads compared in full."""
+    run_and_compare(W["long_bidir_k256_bf16"], heads=2)
