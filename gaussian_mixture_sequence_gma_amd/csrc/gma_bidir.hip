@@ -1263,7 +1263,9 @@ struct Usage2 {
   static constexpr int NKS = C::DRP / 32;
   static constexpr int COEF = CT * NKS * 4;
   static constexpr int LDS = COEF * 1024 + KP * 4 + KP * 4 + 4 * (3 * KP + 1) * 4;
-  static constexpr bool kOK = C::kBF && KP % 32 == 0 && C::DRP <= 64 && LDS <= 80 * 1024;
+  // two workgroups per compute unit where the tables allow, else one (K_pad 256
+  // with d_r = 64)
+  static constexpr bool kOK = C::kBF && KP % 32 == 0 && C::DRP <= 64 && LDS <= 150 * 1024;
 };
 
 template <class C, int MODE>
