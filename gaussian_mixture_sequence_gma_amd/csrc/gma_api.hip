@@ -174,11 +174,15 @@ int make_plan(const gma_dims* d, int causal, bool fp32_compute, Plan& p) {
     off += round256((size_t)p.BH * ns * p.Kp * p.DV * 4);
     p.off_carry_z = off;
     off += round256((size_t)p.BH * ns * p.Kp * 4);
+    if (p.bf && (causal2_lds_bytes(true, p.DRP, p.DV, p.Kp) > 0 || p.khalf)) {
+      // the keys' responsibilities from the span-totals pass for the
+      // token-owner scan: Gamma^K^T per 64-key chunk, [Kp][64] bf16
+      p.off_gt = off;
+      off += round256((size_t)p.BH * p.tiles * p.Kp * 64 * 2);
+    }
     if (p.khalf) {
-      // per key (maximum, 1 / sum); per query the first half's numerator
-      // [d_v] and (denominator, maximum, best score, its component)
-      p.off_kstat = off;
-      off += round256((size_t)p.BH * p.N * 8);
+      // per query the first half's numerator [d_v] and (denominator, maximum,
+      // best score, its component)
       p.off_qpart = off;
       off += round256((size_t)p.BH * p.N * p.DV * 4);
       p.off_qpart2 = off;

@@ -43,8 +43,9 @@ struct CausalArgs {
   int out_bf;
   const void* q_lo;       // split routing vectors: low bf16 parts, or null
   const void* k_lo;
+  const bf16* gt;         // token-owner scan: the keys' Gamma^K^T tiles from the
+                          // span-totals pass, [BH][ceil(N/64)][Kp][64] bf16
   // scan over one half of the components (K_pad = 256):
-  const float2* kstat;    // per key (maximum, 1 / sum) over all components [BH][N]
   float* qpart;           // the first half's numerators [BH][N][DV]
   float4* qpart2;         // and (denominator, maximum, best score, its component) [BH][N]
   int koff;               // first component of this half
@@ -473,12 +474,13 @@ __global__ void __launch_bounds__(kThreads) gma_causal_kernel(CausalArgs a) {
 }
 
 // ============================================================================
-// Causal scan, bf16 inputs, token-owner form.  Wave w owns tokens 16w .. 16w+15
-// of every 64-token chunk, as queries and as keys, with all K_pad components:
-// both score tiles (D[component][token], rows in the pair_row order) share each
-// coefficient operand read from LDS, and the softmaxes stay inside the wave.
-// Per chunk the wave writes its normalised Gamma^K rows to LDS; after one
-// barrier it forms, for its 16 queries,
+// Causal scan, bf16 inputs, token-owner form.  Wave w owns queries 16w ..
+// 16w+15 of every 64-token chunk, with all K_pad components, so the query
+// softmax stays inside the wave.  The keys' responsibilities are not formed
+// here: the span-totals pass, which scores every key anyway, stores them as
+// Gamma^K^T tiles (per 64-key chunk, [component][key] bf16), and the scan
+// copies each chunk's tile into LDS beside its values.  After one barrier
+// each wave forms, for its 16 queries,
 //   num = e^Q S + sum_{j <= i in chunk} (e^Q . Gamma^K_j) v_j,
 //   den = e^Q z + sum_{j <= i} (e^Q . Gamma^K_j) + eps * sum_k e^Q_k
 // (e^Q = exp2(s - max), unnormalised: the ratio is the same), all on MFMA: the
@@ -498,28 +500,29 @@ struct Causal2 {
   static constexpr int OT = DVT + 1;
   static constexpr int CTW = CT / 4;                       // state component tiles per wave
   static constexpr int COEF = CT * NKS * 4;
-  static constexpr int GLD = KP % 128 == 64 ? KP + 8 : KP + 16;   // Gamma^K row stride
   static constexpr int VROWCH = C::DV / 8;
   static constexpr int VROUNDS = kTile * VROWCH / 64;      // 1 KB wave copies per V tile
   static constexpr int VRPW = (VROUNDS + kWaves - 1) / kWaves;
+  static constexpr int GROUNDS = KP * kTile * 2 / 1024;    // 1 KB wave copies per Gamma^K^T tile
+  static constexpr int GRPW = GROUNDS / kWaves;
   static constexpr int STCH = OT * KS;
   static constexpr int lds_bytes(int nb) {
-    return COEF * 1024 + KP * 4 + nb * kTile * GLD * 2 + nb * kTile * C::DV * 2 + STCH * 1024;
+    return COEF * 1024 + KP * 4 + nb * KP * kTile * 2 + nb * kTile * C::DV * 2 + STCH * 1024;
   }
-  // Gamma^K and V tiles double-buffered when they fit (two barriers per chunk),
-  // else single-buffered with a third barrier after the state update
+  // Gamma^K^T and V tiles double-buffered when they fit (two barriers per
+  // chunk), else single-buffered with a third barrier after the state update
   static constexpr int NB = lds_bytes(2) <= 160 * 1024 ? 2 : 1;
   static constexpr bool kOK = C::kBF && KP % 64 == 0 && C::DRP <= 64 && C::DV >= 32 &&
                               lds_bytes(NB) <= 160 * 1024;
   static_assert(!kOK || causal2_lds_bytes(true, C::DRP, C::DV, KP) == lds_bytes(NB),
                 "span sizing mirrors this LDS budget");
+  static_assert(!kOK || GROUNDS % kWaves == 0, "Gamma^K^T copies divide among the waves");
 };
 
 // HM = 0: all components.  HM = 1, 2: the components koff .. koff + C::Kp - 1
-// of the tables laid out for CF (K_pad = 2 C::Kp), the keys normalised by
-// kstat; the first half (HM = 1) leaves each query's numerator, denominator
-// and maximum in qpart / qpart2, the second (HM = 2) rescales both halves to
-// the larger maximum and writes O.
+// of the tables laid out for CF (K_pad = 2 C::Kp); the first half (HM = 1)
+// leaves each query's numerator, denominator and maximum in qpart / qpart2,
+// the second (HM = 2) rescales both halves to the larger maximum and writes O.
 template <class C, bool XS, int HM = 0, class CF = C>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 gma_causal2_kernel(CausalArgs a) {
@@ -527,7 +530,9 @@ gma_causal2_kernel(CausalArgs a) {
   static_assert(HM == 0 || (!XS && CF::Kp == 2 * C::Kp && CF::DRP == C::DRP), "half scan");
   __shared__ __attribute__((aligned(16))) bf16x8 coef[R::COEF * 64];
   __shared__ __attribute__((aligned(16))) float cperm[R::KP];
-  __shared__ __attribute__((aligned(16))) bf16 G[R::NB][kTile * R::GLD];
+  // Gamma^K^T: KP rows of 64 keys, swizzled as swz_elem<8> (unpadded, filled
+  // by 1 KB direct copies)
+  __shared__ __attribute__((aligned(16))) bf16 G[R::NB][R::KP * kTile];
   __shared__ __attribute__((aligned(16))) bf16 Vb[R::NB][kTile * C::DV];
   __shared__ __attribute__((aligned(16))) bf16 ST[R::STCH * 512];
 
@@ -541,8 +546,6 @@ gma_causal2_kernel(CausalArgs a) {
                             ? a.N : t_begin + (int64_t)a.span_tiles * kTile;
   const int nchunks = t_end > t_begin ? (int)((t_end - t_begin + kTile - 1) / kTile) : 0;
   const bool want_aq = a.assign_q != nullptr;
-  // the half scans leave the keys' assignments to the span-totals pass
-  const bool want_ak = HM == 0 && a.assign_k != nullptr;
   const int koff = HM ? a.koff : 0;
 
   // ---- tables, carried state -------------------------------------------------
@@ -607,29 +610,27 @@ gma_causal2_kernel(CausalArgs a) {
   write_st();
 
   const bf16* qs = reinterpret_cast<const bf16*>(a.q) + (size_t)bh * a.N * C::DR;
-  const bf16* ks = reinterpret_cast<const bf16*>(a.k) + (size_t)bh * a.N * C::DR;
   const bf16* vs = reinterpret_cast<const bf16*>(a.v) + (size_t)bh * a.N * C::DV;
   const bf16* qls = XS ? reinterpret_cast<const bf16*>(a.q_lo) + (size_t)bh * a.N * C::DR : qs;
-  const bf16* kls = XS ? reinterpret_cast<const bf16*>(a.k_lo) + (size_t)bh * a.N * C::DR : ks;
-  // routing vectors of a chunk, loaded two chunks ahead: two register
+  // Gamma^K^T tiles of this sequence: [chunk][CF::Kp][64] bf16, this half's rows
+  const int64_t nch = (a.N + kTile - 1) / kTile;
+  const bf16* gts = a.gt + (size_t)bh * nch * CF::Kp * kTile + (size_t)koff * kTile;
+  // routing vectors of a chunk's queries, loaded two chunks ahead: two register
   // buffers, chunks alternating between them
-  bf16x8 xqA[R::NKS], xkA[R::NKS], xqlA[R::NKS], xklA[R::NKS];
-  bf16x8 xqB[R::NKS], xkB[R::NKS], xqlB[R::NKS], xklB[R::NKS];
-  auto load_x = [&](int k, bf16x8 (&xq)[R::NKS], bf16x8 (&xk)[R::NKS], bf16x8 (&xql)[R::NKS],
-                    bf16x8 (&xkl)[R::NKS]) {
+  bf16x8 xqA[R::NKS], xqlA[R::NKS];
+  bf16x8 xqB[R::NKS], xqlB[R::NKS];
+  auto load_x = [&](int k, bf16x8 (&xq)[R::NKS], bf16x8 (&xql)[R::NKS]) {
     const int64_t tok = t_begin + (int64_t)k * kTile + 16 * w + c;
 #pragma unroll
     for (int s = 0; s < R::NKS; ++s) {
       const int col = 32 * s + 8 * g;
       const bool ok = tok < t_end && col < C::DR;
       const size_t off = (size_t)(ok ? tok : t_begin) * C::DR + (ok ? col : 0);
-      const bf16x8 q = ld16_nt<bf16x8>(qs + off), kk = ld16_nt<bf16x8>(ks + off);
+      const bf16x8 q = ld16_nt<bf16x8>(qs + off);
       xq[s] = ok ? q : bf16x8{};
-      xk[s] = ok ? kk : bf16x8{};
       if constexpr (XS) {
-        const bf16x8 ql = ld16_nt<bf16x8>(qls + off), kl = ld16_nt<bf16x8>(kls + off);
+        const bf16x8 ql = ld16_nt<bf16x8>(qls + off);
         xql[s] = ok ? ql : bf16x8{};
-        xkl[s] = ok ? kl : bf16x8{};
       }
     }
   };
@@ -649,6 +650,18 @@ gma_causal2_kernel(CausalArgs a) {
       }
     }
   };
+  // Gamma^K^T tile of chunk k: lane l of copy j fills component row 8 j + l / 8,
+  // physical chunk l % 8 (logical chunk of keys (l % 8) ^ (2 row mod 8))
+  auto load_g = [&](int k, int buf) {
+    const bf16* src = gts + (size_t)(t_begin / kTile + k) * CF::Kp * kTile;
+#pragma unroll
+    for (int j = 0; j < R::GRPW; ++j) {
+      const int round = w * R::GRPW + j;
+      const int row = round * 8 + (lane >> 3), pc = lane & 7;
+      const int lc = pc ^ ((2 * row) & 6);
+      global_to_lds16_nt(src + (size_t)row * kTile + lc * 8, &G[buf][round * 512]);
+    }
+  };
   bf16x8 ones, ones_r3;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -656,32 +669,27 @@ gma_causal2_kernel(CausalArgs a) {
     ones_r3[e] = (bf16)(c == 3 ? 1.0f : 0.0f);          // A operand: row 3 = 1
   }
   if (nchunks > 0) {
-    load_x(0, xqA, xkA, xqlA, xklA);
+    load_x(0, xqA, xqlA);
     load_v(0, 0);
+    load_g(0, 0);
   }
-  if (nchunks > 1) load_x(1, xqB, xkB, xqlB, xklB);
+  if (nchunks > 1) load_x(1, xqB, xqlB);
   __syncthreads();                       // coefficient table and seeds visible to every wave
 
-  // one chunk; xq .. xkl hold its routing vectors and afterwards receive those
-  // of chunk k + 2
-  auto chunk = [&](int k, bf16x8 (&xq)[R::NKS], bf16x8 (&xk)[R::NKS], bf16x8 (&xql)[R::NKS],
-                   bf16x8 (&xkl)[R::NKS]) {
+  // one chunk; xq, xql hold its routing vectors and afterwards receive those of
+  // chunk k + 2
+  auto chunk = [&](int k, bf16x8 (&xq)[R::NKS], bf16x8 (&xql)[R::NKS]) {
     const int buf = R::NB == 2 ? (k & 1) : 0;
     const int64_t tile0 = t_begin + (int64_t)k * kTile;
     const int64_t rem = t_end - tile0;
     const int nvalid = (int)(rem < kTile ? rem : kTile);
     asm volatile("" ::: "memory");
-    // half scans: this lane's key normaliser over all components; the second
-    // half also the first half's partials of this lane's query (both arrive
-    // while the scores are formed)
-    const int qi = 16 * w + c;                      // this lane's query (and key) in the chunk
+    const int qi = 16 * w + c;                      // this lane's query in the chunk
     const size_t qtok = (size_t)bh * a.N + (size_t)(tile0 + qi);
-    float2 kst{3.0e38f, 0.f};
+    // second half: the first half's partials of this lane's query (they arrive
+    // while the scores are formed)
     f32x4 pnum[HM == 2 ? R::DVT : 1];
     f32x4 pq{1.f, 0.f, 0.f, 0.f};
-    if constexpr (HM != 0) {
-      if (qi < nvalid) kst = a.kstat[qtok];
-    }
     if constexpr (HM == 2) {
 #pragma unroll
       for (int dt = 0; dt < R::DVT; ++dt) pnum[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -695,21 +703,14 @@ gma_causal2_kernel(CausalArgs a) {
         pq = *reinterpret_cast<const f32x4*>(a.qpart2 + qtok);
       }
     }
-    // features of this wave's 16 queries and 16 keys
-    bf16x8 fq[R::NKS][NFX<XS>], fk[R::NKS][NFX<XS>];
+    // features of this wave's 16 queries
+    bf16x8 fq[R::NKS][NFX<XS>];
 #pragma unroll
-    for (int s = 0; s < R::NKS; ++s) {
-      make_features<XS>(xq[s], xql[s], fq[s]);
-      make_features<XS>(xk[s], xkl[s], fk[s]);
-    }
-    // scores: each coefficient operand serves the query and the key tile
-    f32x4 SQ[R::CT], SK[R::CT];
+    for (int s = 0; s < R::NKS; ++s) make_features<XS>(xq[s], xql[s], fq[s]);
+    // scores D[component][query]
+    f32x4 SQ[R::CT];
 #pragma unroll
-    for (int ct = 0; ct < R::CT; ++ct) {
-      const f32x4 cs = *reinterpret_cast<const f32x4*>(&cperm[ct * 16 + 4 * g]);
-      SQ[ct] = cs;
-      SK[ct] = cs;
-    }
+    for (int ct = 0; ct < R::CT; ++ct) SQ[ct] = *reinterpret_cast<const f32x4*>(&cperm[ct * 16 + 4 * g]);
     {
       // half-steps h = (component tile, routing chunk): the four operands of
       // half-step h + 1 are read from LDS while the MFMAs of h run
@@ -727,16 +728,13 @@ gma_causal2_kernel(CausalArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         const int ct = hs / R::NKS, s = hs % R::NKS;
 #pragma unroll
-        for (int q = 0; q < NQX<XS>; ++q) {
-          SQ[ct] = mma(wbuf[hs & 1][kWI[q]], fq[s][kFI[q]], SQ[ct]);
-          SK[ct] = mma(wbuf[hs & 1][kWI[q]], fk[s][kFI[q]], SK[ct]);
-        }
+        for (int q = 0; q < NQX<XS>; ++q) SQ[ct] = mma(wbuf[hs & 1][kWI[q]], fq[s][kFI[q]], SQ[ct]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 
-    // queries: e = exp2(s - max), packed as the B operand of the contractions
-    // over components; keys: normalised responsibilities -> G
+    // e = exp2(s - max), packed as the B operand of the contractions over
+    // components
     bf16x8 Eq[R::KS];
     float mq, qbv = 0.f;
     int qbi = 0;
@@ -769,61 +767,15 @@ gma_causal2_kernel(CausalArgs a) {
         if (HM == 0 && g == 0 && qi < nvalid) a.assign_q[qtok] = bi;
       }
     }
-    {
-      // the half scans take the maximum and the sum over all components from kstat
-      float m = kst.x;
-      if constexpr (HM == 0) {
-        float v = SK[0][0];
-#pragma unroll
-        for (int ct = 0; ct < R::CT; ++ct)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v = fmaxf(v, SK[ct][i]);
-        m = groups_max(v);
-      }
-      float l = 0.f;
-#pragma unroll
-      for (int ct = 0; ct < R::CT; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = exp2_fast(SK[ct][i] - m);
-          SK[ct][i] = e;
-          l += e;
-        }
-      float inv;
-      if constexpr (HM == 0) {
-        l = groups_sum(l);
-        inv = qi < nvalid ? fast_rcp(l) : 0.f;
-      } else {
-        inv = qi < nvalid ? kst.y : 0.f;
-      }
-      bf16* grow_ = &G[buf][qi * R::GLD + 8 * g];
-#pragma unroll
-      for (int p = 0; p < R::KS; ++p) {
-        bf16x8 v8;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v8[i] = to_bf16(SK[2 * p][i] * inv);
-          v8[4 + i] = to_bf16(SK[2 * p + 1][i] * inv);
-        }
-        st16(grow_ + 32 * p, v8);
-      }
-      if (want_ak) {
-        float bv = SK[0][0];
-        int bi = pair_row(0, 4 * g);
-#pragma unroll
-        for (int ct = 0; ct < R::CT; ++ct)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) argmax_merge(bv, bi, SK[ct][i], pair_row(ct, 4 * g + i));
-        groups_argmax(bv, bi);
-        if (g == 0 && qi < nvalid) a.assign_k[(size_t)bh * a.N + tile0 + qi] = bi;
-      }
-    }
-    wait_global_loads();                 // V(k) and this wave's loads
+    wait_global_loads();                 // V(k), Gamma^K^T(k) and this wave's loads
     lds_barrier();                                                    // B1
     if constexpr (R::NB == 2) {
-      if (k + 1 < nchunks) load_v(k + 1, buf ^ 1);
+      if (k + 1 < nchunks) {
+        load_v(k + 1, buf ^ 1);
+        load_g(k + 1, buf ^ 1);
+      }
     }
-    if (k + 2 < nchunks) load_x(k + 2, xq, xk, xql, xkl);
+    if (k + 2 < nchunks) load_x(k + 2, xq, xql);
 
     // ---- outputs of this wave's 16 queries ------------------------------------
     f32x4 acc[R::OT];
@@ -836,16 +788,18 @@ gma_causal2_kernel(CausalArgs a) {
         acc[dt] = mma(reinterpret_cast<const bf16x8*>(ST)[(dt * R::KS + p) * 64 + lane], Eq[p], acc[dt]);
     // intra-chunk: key pairs (32 keys; rows of key tile jt in tile_token order,
     // so a pair covers keys 32pp .. 32pp + 31) up to the one holding this wave's
-    // queries, which is masked to keys <= query
+    // queries, which is masked to keys <= query.  The A operand (key rows,
+    // components 32p + 8g ..) is a transpose read of Gamma^K^T: source lane s
+    // reads the four keys 8 (s % 4) + 4 jt .. of its component row.
     for (int pp = 0; pp <= (w >> 1); ++pp) {
       f32x4 P[2];
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         const int jt = 2 * pp + b;
         P[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const bf16* gr = &G[buf][tile_token(jt, c) * R::GLD + 8 * g];
+        const int blk = 32 * pp + 8 * (lane & 3) + 4 * b;
 #pragma unroll
-        for (int p = 0; p < R::KS; ++p) P[b] = mma(ld16<bf16x8>(gr + 32 * p), Eq[p], P[b]);
+        for (int p = 0; p < R::KS; ++p) P[b] = mma(tr_chunk_swz_blk<8>(G[buf], 32 * p, blk), Eq[p], P[b]);
         if (pp == (w >> 1)) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -924,11 +878,18 @@ gma_causal2_kernel(CausalArgs a) {
     lds_barrier();                                                    // B2
 
     // ---- state update on this wave's components: S += Gamma^K^T V, z += Gamma^K^T 1
+    // (keys past the end of the sequence, in its last chunk, are cleared)
 #pragma unroll
     for (int P2 = 0; P2 < 2; ++P2) {
 #pragma unroll
       for (int j = 0; j < R::CTW; ++j) {
-        const bf16x8 Ag = tr_chunk(G[buf], R::GLD, 32 * P2, (w * R::CTW + j) * 16);
+        const int comp = (w * R::CTW + j) * 16 + c;
+        bf16x8 Ag = *reinterpret_cast<const bf16x8*>(&G[buf][swz_elem<8>(comp, 32 * P2 + 8 * g)]);
+        if (nvalid < kTile) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (32 * P2 + 8 * g + e >= nvalid) Ag[e] = (bf16)0.f;
+        }
         zacc[j] = mma(Ag, ones, zacc[j]);
 #pragma unroll
         for (int dt = 0; dt < R::DVT; ++dt)
@@ -938,24 +899,30 @@ gma_causal2_kernel(CausalArgs a) {
     write_st();
     if constexpr (R::NB == 1) {
       lds_barrier();                                                  // B3: G, V free
-      if (k + 1 < nchunks) load_v(k + 1, 0);
+      if (k + 1 < nchunks) {
+        load_v(k + 1, 0);
+        load_g(k + 1, 0);
+      }
     }
   };
   for (int k = 0; k < nchunks; k += 2) {
-    chunk(k, xqA, xkA, xqlA, xklA);
-    if (k + 1 < nchunks) chunk(k + 1, xqB, xkB, xqlB, xklB);
+    chunk(k, xqA, xqlA);
+    if (k + 1 < nchunks) chunk(k + 1, xqB, xqlB);
   }
 }
 
 template <class C>
 static hipError_t run_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   // K_pad = 256 where the scan tables exceed LDS: the scan runs once per half
-  // of the components (CH), the keys normalised over all of them by the
-  // span-totals pass
+  // of the components (CH)
   constexpr bool KH = causal_khalf(C::kBF, C::DRP, C::DV, C::Kp);
   using CH = Cfg<C::kBF, (C::CPW > 1 ? C::CPW / 2 : 1), 4, C::DR, C::DV>;
   static_assert(!KH || (WriteTeam<C>::kOK && Causal2<CH>::kOK && CH::Kp * 2 == C::Kp),
                 "K-half scan");
+  // the token-owner scan takes the keys' responsibilities (and assignments)
+  // from the span-totals pass, which must then be a token-owner write
+  constexpr bool TOK = KH || Causal2<C>::kOK;
+  static_assert(!TOK || WriteTeam<C>::kOK || Write2<C>::kOK, "span pass storing Gamma^K^T");
   if constexpr (!KH && causal_lds_bytes(C::kBF, C::DR, C::DV, C::Kp) > kMaxLds) {
     return hipErrorNotSupported;     // rejected earlier by validation
   } else {
@@ -979,14 +946,24 @@ static hipError_t run_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   wa.assign = nullptr;
   const dim3 grid(p.nspan, (unsigned)p.BH);
   if (g_launch_hook) g_launch_hook("gma_span_state", s, 1);
-  if constexpr (KH) {
-    // also each key's maximum and 1 / sum over all components, and its
-    // assignment
+  if constexpr (TOK) {
+    // a token-owner write (one split per span of 2 span_tiles 32-key groups)
+    // that also stores the keys' Gamma^K^T tiles and assignments
     wa.gpw = 2 * p.span_tiles;
-    wa.kstat = reinterpret_cast<float2*>(t.ws + p.off_kstat);
+    wa.gt = reinterpret_cast<bf16*>(t.ws + p.off_gt);
     wa.assign = t.assign_k;
-    if (t.assign_k) hipLaunchKernelGGL((gma_write_team_kernel<C, false, true>), grid, dim3(512), 0, s, wa);
-    else hipLaunchKernelGGL((gma_write_team_kernel<C, false, false>), grid, dim3(512), 0, s, wa);
+    if constexpr (WriteTeam<C>::kOK) {
+      if (split) {
+        if (t.assign_k) hipLaunchKernelGGL((gma_write_team_kernel<C, true, true, true>), grid, dim3(512), 0, s, wa);
+        else hipLaunchKernelGGL((gma_write_team_kernel<C, true, false, true>), grid, dim3(512), 0, s, wa);
+      } else {
+        if (t.assign_k) hipLaunchKernelGGL((gma_write_team_kernel<C, false, true, true>), grid, dim3(512), 0, s, wa);
+        else hipLaunchKernelGGL((gma_write_team_kernel<C, false, false, true>), grid, dim3(512), 0, s, wa);
+      }
+    } else if constexpr (Write2<C>::kOK) {
+      if (split) hipLaunchKernelGGL((gma_write2_kernel<C, true, true>), grid, dim3(256), 0, s, wa);
+      else hipLaunchKernelGGL((gma_write2_kernel<C, false, true>), grid, dim3(256), 0, s, wa);
+    }
   } else if (WriteTeam<C>::kOK && (split || p.span_tiles >= 4)) {
     // the token-owner write pays a per-workgroup set-up (its coefficient
     // table): use it for spans of at least four 32-token steps per wave, or
@@ -1044,9 +1021,9 @@ static hipError_t run_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   ca.q_lo = t.q_lo;
   ca.k_lo = t.k_lo;
   if (g_launch_hook) g_launch_hook("gma_causal", s, 1);
+  ca.gt = TOK ? reinterpret_cast<const bf16*>(t.ws + p.off_gt) : nullptr;
   if constexpr (KH) {
     // the first half leaves its partials, the second combines them
-    ca.kstat = reinterpret_cast<const float2*>(t.ws + p.off_kstat);
     ca.qpart = reinterpret_cast<float*>(t.ws + p.off_qpart);
     ca.qpart2 = reinterpret_cast<float4*>(t.ws + p.off_qpart2);
     ca.koff = 0;

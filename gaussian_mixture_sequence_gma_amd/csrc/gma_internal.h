@@ -33,7 +33,8 @@ struct Plan {
   size_t head_bytes = 0;
   size_t off_params = 0, off_partial = 0, off_partial_z = 0, off_vt = 0, off_z = 0, off_vtab = 0;
   size_t off_state = 0, off_state_z = 0, off_carry = 0, off_carry_z = 0;
-  size_t off_kstat = 0, off_qpart = 0, off_qpart2 = 0;   // khalf: key normalisers (causal), query partials
+  size_t off_gt = 0;        // causal token-owner scan: the keys' Gamma^K^T tiles
+  size_t off_qpart = 0, off_qpart2 = 0;   // khalf: the first half's query partials
   size_t total = 0;
 };
 

@@ -123,7 +123,8 @@ struct Write2 {
   static constexpr int WPE = CT * DVT * 4 <= 64 ? 2 : 1;
 };
 
-template <class C, bool XS>
+// GT: the keys' Gamma^K^T tiles are stored to a.gt (the causal span-totals pass)
+template <class C, bool XS, bool GT = false>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Write2<C>::WPE, Write2<C>::WPE)))
 gma_write2_kernel(BidirArgs a) {
   using R = Write2<C>;
@@ -148,7 +149,9 @@ gma_write2_kernel(BidirArgs a) {
   }
   __syncthreads();
 
-  const int64_t G32 = (a.N + 31) / 32;
+  // with Gamma^K^T tiles requested, every 64-key chunk is covered whole (the
+  // keys past N get responsibilities 0)
+  const int64_t G32 = GT ? 2 * ((a.N + 63) / 64) : (a.N + 31) / 32;
   const int64_t gpw = a.gpw > 0 ? a.gpw : (G32 + gridDim.x - 1) / gridDim.x;
   const int64_t gb = (int64_t)blockIdx.x * gpw;
   const int64_t ge = gb + gpw < G32 ? gb + gpw : G32;
@@ -278,6 +281,14 @@ gma_write2_kernel(BidirArgs a) {
           A[ct][4 * tt + i] = to_bf16(gm);
         }
       }
+    // Gamma^K^T for the causal scan: lane (c, g) holds component pair_row(ct, c)
+    // of keys 8g .. 8g + 7, one 16-byte store each
+    if constexpr (GT) {
+      bf16* gdst = a.gt + ((size_t)bh * ((a.N + 63) / 64) + (size_t)(grp >> 1)) * C::Kp * 64 +
+                   (grp & 1) * 32 + 8 * g;
+#pragma unroll
+      for (int ct = 0; ct < R::CT; ++ct) st16(gdst + (size_t)pair_row(ct, c) * 64, A[ct]);
+    }
     if (want_assign) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)

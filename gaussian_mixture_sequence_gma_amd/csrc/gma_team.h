@@ -83,8 +83,9 @@ __device__ __forceinline__ void team_wait(const int* flag, int v) {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// AS: key assignments are written (a.assign non-null)
-template <class C, bool XS, bool AS>
+// AS: key assignments are written (a.assign non-null); GT: the keys'
+// Gamma^K^T tiles are stored to a.gt (the causal span-totals pass)
+template <class C, bool XS, bool AS, bool GT = false>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gma_write_team_kernel(BidirArgs a) {
   using R = WriteTeam<C>;
@@ -120,7 +121,9 @@ gma_write_team_kernel(BidirArgs a) {
   int* vflags = flags + R::NW + team * TS;            // one V buffer: reads done
   float* ftab = reinterpret_cast<float*>(lds + R::OFF_FT) + wave * 64;   // [32] factor, [32] argmax
 
-  const int64_t G32 = (a.N + 31) / 32;
+  // with Gamma^K^T tiles requested, every 64-key chunk is covered whole (the
+  // keys past N get responsibilities 0)
+  const int64_t G32 = GT ? 2 * ((a.N + 63) / 64) : (a.N + 31) / 32;
   const int64_t gpw = a.gpw > 0 ? a.gpw : (G32 + gridDim.x - 1) / gridDim.x;
   const int64_t gb = (int64_t)blockIdx.x * gpw;
   const int64_t ge = gb + gpw < G32 ? gb + gpw : G32;
@@ -324,12 +327,8 @@ gma_write_team_kernel(BidirArgs a) {
         if (mw[w] == M) best = iw[w];     // the lowest wave at the maximum wins
       }
       const int64_t tok = grp * 32 + key;
-      const float invL = fast_rcp(L);
-      ftab[key] = tok < a.N ? own * invL : 0.f;
+      ftab[key] = tok < a.N ? own * fast_rcp(L) : 0.f;
       if (want_assign) ftab[32 + key] = __int_as_float(best);
-      // the key's maximum and normaliser over all components, for a scan that
-      // forms its responsibilities one half of the components at a time
-      if (a.kstat != nullptr && r == 0 && tok < a.N) a.kstat[(size_t)bh * a.N + tok] = float2{M, invL};
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
@@ -364,6 +363,15 @@ gma_write_team_kernel(BidirArgs a) {
     if (want_assign && r == 0 && lane < 32) {
       const int64_t tok = grp * 32 + lane;
       if (tok < a.N) a.assign[(size_t)bh * a.N + tok] = __float_as_int(ftab[32 + lane]);
+    }
+    // Gamma^K^T for the causal scan: lane (c, g) holds component
+    // pair_row(r CTW + ct, c) of keys 8g .. 8g + 7, one 16-byte store each
+    if constexpr (GT) {
+      bf16* gdst = a.gt + ((size_t)bh * ((a.N + 63) / 64) + (size_t)(grp >> 1)) * C::Kp * 64 +
+                   (grp & 1) * 32 + 8 * g;
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct)
+        st16(gdst + (size_t)pair_row(r * CTW + ct, c) * 64, A[ct]);
     }
 
     // ---- V~_slice += Gamma_slice^T V ---------------------------------------------

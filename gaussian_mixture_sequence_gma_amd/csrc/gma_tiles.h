@@ -76,7 +76,7 @@ constexpr int kMaxLds = 160 * 1024;
 // table.  Mirrors Causal2 in gma_causal.hip.
 __host__ __device__ constexpr int causal2_lds_bytes_nb(int DRP, int DV, int Kp, int nb) {
   return (Kp / 16) * (DRP / 32) * 4 * 1024 + Kp * 4 +
-         nb * kTile * (Kp % 128 == 64 ? Kp + 8 : Kp + 16) * 2 + nb * kTile * DV * 2 +
+         nb * Kp * kTile * 2 + nb * kTile * DV * 2 +
          (DV / 16 + 1) * (Kp / 32) * 1024;
 }
 __host__ __device__ constexpr int causal2_lds_bytes(bool bf, int DRP, int DV, int Kp) {
@@ -102,8 +102,8 @@ __host__ __device__ constexpr bool bidir_khalf(bool bf, int DRP, int DV, int Kp)
          read2_lds_bytes(DRP, DV, Kp / 2) <= kRead2MaxLds;
 }
 // bf16 causal forward at K_pad = 256 whose scan tables exceed LDS while those
-// of 128 components fit: the scan runs once per half of the components, with
-// the keys' normalisers over all K taken from the span-totals pass (the team
+// of 128 components fit: the scan runs once per half of the components, each
+// on its rows of the keys' responsibilities from the span-totals pass (the team
 // write, which needs d_v of 64 or 128 at this K)
 __host__ __device__ constexpr bool causal_khalf(bool bf, int DRP, int DV, int Kp) {
   return bf && Kp == 256 && DRP <= 64 && (DV == 64 || DV == 128) &&
@@ -134,9 +134,10 @@ struct BidirArgs {
   int gpw;                // token-owner write: 32-token groups per split (0: derived)
   float eps;
   int out_bf;
-  float2* kstat;          // team write: per key, the maximum of its log2-domain scores
-                          // over all components and 1 / sum exp2(score - maximum),
-                          // [BH][N]; or null
+  bf16* gt;               // token-owner writes: the keys' responsibilities stored as
+                          // Gamma^K^T tiles [BH][ceil(N/64)][Kp][64] bf16 (every
+                          // 64-key chunk whole, zeros past N), for the causal scan;
+                          // or null
   // read-out over one half of the components (K_pad = 256):
   float* qpart;           // the first half's numerators [BH][N][DV]
   float4* qpart2;         // and (denominator, maximum, best score, its component) [BH][N]
