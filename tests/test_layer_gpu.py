@@ -135,3 +135,12 @@ def test_layer_large_mixture(causal):
     w = W["layer_causal_bf16"].with_(B=1, H=3, N=333, d_r=64, d_v=128, K=128, d_model=256,
                                      causal=causal)
     _run(w)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_layer_k_above_128(causal):
+    # K = 200 (K_pad 256) at d_r = d_v = 64: the layer runs its projections in
+    # fp32 and the fp32 forward (bidirectional kernels, causal product path)
+    w = W["layer_causal_bf16"].with_(B=1, H=3, N=300, d_r=64, d_v=64, K=200, d_model=128,
+                                     causal=causal)
+    _run(w)

@@ -65,7 +65,8 @@ def test_reparameterized_forward_matches_oracle(causal):
     ("bf16", False, 128, 128),     # the long-context head shape's K and d_v
     ("bf16", True, 64, 64),
     ("f32", True, 100, 32),
-    ("bf16", True, 256, 128),      # K = 256, causal on the product path
+    ("bf16", True, 256, 128),      # K = 256: the causal scan once per half of the components
+    ("bf16", False, 256, 64),      # K = 256: the read-out once per half of the components
 ])
 def test_forward_reparam_fused(dtype, causal, K, d_v):
     """gma_forward_reparam (the prologue derives log sigma^2 and log pi from
