@@ -113,3 +113,13 @@ def test_bidir_khalf_full_long_shape():
     """The long-context shape at K = 256 (B1 H32 N32768, d_v = 128) as the
     benchmark launches it; two heads compared in full."""
     run_and_compare(W["long_bidir_k256_bf16"], heads=2)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 31, 63, 65, 130])
+def test_k256_short_and_ragged_lengths(causal, N):
+    """K = 256 at d_r = 64: the half read-outs and half scans on lengths below,
+    at and just past one 32-key group and one 64-token chunk (the span pass then
+    covers a chunk whose second group lies wholly past N)."""
+    w = W["lm_causal_bf16"].with_(B=2, H=3, N=N, K=256, causal=causal)
+    run_and_compare(w)
