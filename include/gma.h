@@ -73,7 +73,12 @@ int gma_validate(const gma_dims* d, float eps, int causal, const void* const* pt
                  size_t workspace_bytes, size_t workspace_needed);
 
 /* Bytes of device workspace gma_forward needs for this shape and variant
- * (written to *bytes).  The same workspace also serves gma_responsibilities. */
+ * (written to *bytes).  The same workspace also serves gma_responsibilities.
+ * Bidirectional: a few tens of MB that do not grow with N (per-head tables
+ * and per-split partial sums).  Causal with bf16 inputs: in addition the
+ * keys' responsibilities as bf16 tiles, 2 * K_pad bytes per token-head
+ * (K_pad = K rounded up to a multiple of 64), and at K_pad = 256 with half
+ * scans 4 * d_v + 16 bytes per token-head of partial results. */
 int gma_forward_workspace_bytes(const gma_dims* d, int causal, size_t* bytes);
 
 /* GMA forward.
