@@ -77,7 +77,7 @@ int gma_validate(const gma_dims* d, float eps, int causal, const void* const* pt
  * Bidirectional: a few tens of MB that do not grow with N (per-head tables
  * and per-split partial sums).  Causal with bf16 inputs: in addition the
  * keys' responsibilities as bf16 tiles, 2 * K_pad bytes per token-head
- * (K_pad = K rounded up to a multiple of 64), and at K_pad = 256 with half
+ * (K_pad: the smallest of 64, 128, 256 not below K), and at K_pad = 256 with half
  * scans 4 * d_v + 16 bytes per token-head of partial results. */
 int gma_forward_workspace_bytes(const gma_dims* d, int causal, size_t* bytes);
 
