@@ -578,7 +578,9 @@ template <bool XS, int HM = 0> constexpr int kRead2WPE = XS || HM == 2 ? 2 : 3;
 // of the tables laid out for CF (K_pad = 2 C::Kp); the first half (HM = 1)
 // leaves each query's numerator, denominator and maximum in qpart / qpart2,
 // the second (HM = 2) rescales both halves to the larger maximum and writes O.
-template <class C, bool XS, int HM = 0, class CF = C>
+// AS: query assignments are written (a.assign non-null); a separate variant, so
+// that the plain read-out carries none of the argmax code.
+template <class C, bool XS, int HM = 0, class CF = C, bool AS = false>
 __global__ void __launch_bounds__(256 * (kRead2WPE<XS, HM>), 1)
 __attribute__((amdgpu_waves_per_eu((kRead2WPE<XS, HM>), (kRead2WPE<XS, HM>))))
 gma_read2_kernel(BidirArgs a) {
@@ -594,7 +596,7 @@ gma_read2_kernel(BidirArgs a) {
   const int c = lane & 15, g = lane >> 4;
   const int64_t bh = blockIdx.y;
   const int h = (int)(bh % a.H);
-  const bool want_assign = a.assign != nullptr;
+  constexpr bool want_assign = AS;
   const int koff = HM ? a.koff : 0;
 
   // ---- tables: copies of what the prologue and the reduction wrote (a half:
@@ -716,16 +718,16 @@ gma_read2_kernel(BidirArgs a) {
       const float m = groups_max(v);
       mx[tt] = m;
       if (want_assign) {
-        float bv = S[tt][0][0];
-        int bi = koff + pair_row(0, 4 * g);
+        // the lowest component index whose score equals the maximum m (m is
+        // one of the scores: the maxima select, they do not round)
+        int bi = 0x7fffffff;
 #pragma unroll
         for (int ct = 0; ct < R::CT; ++ct)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            argmax_merge(bv, bi, S[tt][ct][i], koff + pair_row(ct, 4 * g + i));
-        groups_argmax(bv, bi);
-        am[tt] = bi;
-        bvs[tt] = bv;
+            bi = min(bi, S[tt][ct][i] == m ? koff + pair_row(ct, 4 * g + i) : 0x7fffffff);
+        am[tt] = groups_min_i(bi);
+        bvs[tt] = m;
       }
 #pragma unroll
       for (int p = 0; p < R::KS; ++p)
@@ -1195,12 +1197,17 @@ static hipError_t run_bidir(const Plan& p, const Tensors& t, hipStream_t s) {
     if (s2 < 1) s2 = 1;
     a.qpart = reinterpret_cast<float*>(t.ws + p.off_qpart);
     a.qpart2 = reinterpret_cast<float4*>(t.ws + p.off_qpart2);
+    const dim3 gr((unsigned)s2, (unsigned)p.BH);
     a.koff = 0;
-    hipLaunchKernelGGL((gma_read2_kernel<CH, false, 1, C>), dim3((unsigned)s2, (unsigned)p.BH),
-                       dim3(256 * kRead2WPE<false, 1>), 0, s, a);
+    if (a.assign)
+      hipLaunchKernelGGL((gma_read2_kernel<CH, false, 1, C, true>), gr, dim3(256 * kRead2WPE<false, 1>), 0, s, a);
+    else
+      hipLaunchKernelGGL((gma_read2_kernel<CH, false, 1, C>), gr, dim3(256 * kRead2WPE<false, 1>), 0, s, a);
     a.koff = CH::Kp;
-    hipLaunchKernelGGL((gma_read2_kernel<CH, false, 2, C>), dim3((unsigned)s2, (unsigned)p.BH),
-                       dim3(256 * kRead2WPE<false, 2>), 0, s, a);
+    if (a.assign)
+      hipLaunchKernelGGL((gma_read2_kernel<CH, false, 2, C, true>), gr, dim3(256 * kRead2WPE<false, 2>), 0, s, a);
+    else
+      hipLaunchKernelGGL((gma_read2_kernel<CH, false, 2, C>), gr, dim3(256 * kRead2WPE<false, 2>), 0, s, a);
   } else if constexpr (Read2<C>::kOK) {
     // about one workgroup per compute unit, at least eight 32-query groups each
     const int64_t g32 = (p.N + 31) / 32;
@@ -1208,12 +1215,14 @@ static hipError_t run_bidir(const Plan& p, const Tensors& t, hipStream_t s) {
     const int64_t cap = (g32 + 7) / 8;
     if (s2 > cap) s2 = cap;
     if (s2 < 1) s2 = 1;
-    if (split)
-      hipLaunchKernelGGL((gma_read2_kernel<C, true>), dim3((unsigned)s2, (unsigned)p.BH),
-                         dim3(256 * kRead2WPE<true>), 0, s, a);
-    else
-      hipLaunchKernelGGL((gma_read2_kernel<C, false>), dim3((unsigned)s2, (unsigned)p.BH),
-                         dim3(256 * kRead2WPE<false>), 0, s, a);
+    const dim3 gr((unsigned)s2, (unsigned)p.BH);
+    if (split) {
+      if (a.assign) hipLaunchKernelGGL((gma_read2_kernel<C, true, 0, C, true>), gr, dim3(256 * kRead2WPE<true>), 0, s, a);
+      else hipLaunchKernelGGL((gma_read2_kernel<C, true>), gr, dim3(256 * kRead2WPE<true>), 0, s, a);
+    } else {
+      if (a.assign) hipLaunchKernelGGL((gma_read2_kernel<C, false, 0, C, true>), gr, dim3(256 * kRead2WPE<false>), 0, s, a);
+      else hipLaunchKernelGGL((gma_read2_kernel<C, false>), gr, dim3(256 * kRead2WPE<false>), 0, s, a);
+    }
   } else {
     hipLaunchKernelGGL((gma_read_kernel<C, 0>), grid, dim3(kThreads), 0, s, a);
   }

@@ -182,6 +182,12 @@ __device__ __forceinline__ float groups_sum(float v) {
   pair_xor32(a + b, a, b);
   return a + b;
 }
+__device__ __forceinline__ int groups_min_i(int v) {
+  int a, b;
+  pair_xor16_i(v, a, b);
+  pair_xor32_i(min(a, b), a, b);
+  return min(a, b);
+}
 
 // (value, index) argmax merge, ties to the lower index.
 __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {

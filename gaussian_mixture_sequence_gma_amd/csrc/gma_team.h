@@ -236,56 +236,52 @@ gma_write_team_kernel(BidirArgs a) {
     // ---- per key: local maximum and sum over this wave's components, posted as
     // the records m, l, argmax of keys 8 g + 4 tt + i by lane c = 0 of each
     // lane group ------------------------------------------------------------------
-    {
-      float mm[8], ll[8];
-      int bb[8];
+    // (each key tile's four records are posted as soon as they are formed, so
+    // that only four keys' values are live at a time)
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+    for (int tt = 0; tt < 2; ++tt) {
+      float mm[4], ll[4];
+      int bb[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float m = S[tt][0][i];
+      for (int i = 0; i < 4; ++i) {
+        float m = S[tt][0][i];
 #pragma unroll
-          for (int ct = 1; ct < CTW; ++ct) m = fmaxf(m, S[tt][ct][i]);
-          m = row16_max(m);
-          m = fmaxf(m, -3.0e38f);          // a slice of padded components only: e = 0
-          int bi = 0;
-          if (want_assign) {
-            // lowest component index of this slice at the maximum
-            bi = 1 << 30;
-#pragma unroll
-            for (int ct = 0; ct < CTW; ++ct) {
-              const int k = pair_row(r * CTW + ct, c);
-              bi = (S[tt][ct][i] == m && k < bi) ? k : bi;
-            }
-            bi = min(bi, dpp_i<0xB1>(bi));
-            bi = min(bi, dpp_i<0x4E>(bi));
-            bi = min(bi, dpp_i<0x141>(bi));
-            bi = min(bi, dpp_i<0x140>(bi));
-          }
-          float l = 0.f;
+        for (int ct = 1; ct < CTW; ++ct) m = fmaxf(m, S[tt][ct][i]);
+        m = row16_max(m);
+        m = fmaxf(m, -3.0e38f);          // a slice of padded components only: e = 0
+        int bi = 0;
+        if (want_assign) {
+          // lowest component index of this slice at the maximum
+          bi = 1 << 30;
 #pragma unroll
           for (int ct = 0; ct < CTW; ++ct) {
-            const float e = exp2_fast(S[tt][ct][i] - m);
-            S[tt][ct][i] = e;
-            l = ct == 0 ? e : l + e;
+            const int k = pair_row(r * CTW + ct, c);
+            bi = (S[tt][ct][i] == m && k < bi) ? k : bi;
           }
-          l = row16_sum(l);
-          mm[4 * tt + i] = m;
-          ll[4 * tt + i] = l;
-          bb[4 * tt + i] = bi;
+          bi = min(bi, dpp_i<0xB1>(bi));
+          bi = min(bi, dpp_i<0x4E>(bi));
+          bi = min(bi, dpp_i<0x141>(bi));
+          bi = min(bi, dpp_i<0x140>(bi));
         }
+        float l = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct) {
+          const float e = exp2_fast(S[tt][ct][i] - m);
+          S[tt][ct][i] = e;
+          l = ct == 0 ? e : l + e;
+        }
+        l = row16_sum(l);
+        mm[i] = m;
+        ll[i] = l;
+        bb[i] = bi;
+      }
       if (c == 0) {
-        float4* rec = xch + (buf * TS + r) * 32 + 2 * g;
+        float4* rec = xch + (buf * TS + r) * 32 + 2 * g + tt;
         rec[0] = float4{mm[0], mm[1], mm[2], mm[3]};
-        rec[1] = float4{mm[4], mm[5], mm[6], mm[7]};
         rec[8] = float4{ll[0], ll[1], ll[2], ll[3]};
-        rec[9] = float4{ll[4], ll[5], ll[6], ll[7]};
-        if (want_assign) {
+        if (want_assign)
           rec[16] = float4{__int_as_float(bb[0]), __int_as_float(bb[1]), __int_as_float(bb[2]),
                            __int_as_float(bb[3])};
-          rec[17] = float4{__int_as_float(bb[4]), __int_as_float(bb[5]), __int_as_float(bb[6]),
-                           __int_as_float(bb[7])};
-        }
       }
     }
     // this wave's copies of V(grp) have landed once at most the x loads of the
