@@ -43,6 +43,8 @@ struct CausalArgs {
   int out_bf;
   const void* q_lo;       // split routing vectors: low bf16 parts, or null
   const void* k_lo;
+  const float* state;     // token-owner scan: the spans' totals [BH][nspan][Kp][DV]
+  const float* state_z;   // and [BH][nspan][Kp] (the carried state is their prefix sum)
   const bf16* gt;         // token-owner scan: the keys' Gamma^K^T tiles from the
                           // span-totals pass, [BH][ceil(N/64)][Kp][64] bf16
   // scan over one half of the components (K_pad = 256):
@@ -566,18 +568,50 @@ gma_causal2_kernel(CausalArgs a) {
       reinterpret_cast<bf16x8*>(ST)[R::DVT * R::KS * 64 + idx] = v;
     }
   }
-  const size_t sslot = (size_t)bh * a.nspan + span;
+  // the state entering this span: the earlier spans' totals summed in span
+  // order (the order of an exclusive scan over spans), SB spans' loads issued
+  // before their adds; a slot past the earlier spans adds zeros
   f32x4 sacc[R::CTW][R::DVT], zacc[R::CTW];
 #pragma unroll
   for (int j = 0; j < R::CTW; ++j) {
-    const int comp0 = koff + (w * R::CTW + j) * 16;
+    zacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) zacc[j][i] = a.carry_z[sslot * CF::Kp + comp0 + 4 * g + i];
+    for (int dt = 0; dt < R::DVT; ++dt) sacc[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  {
+    constexpr int V1 = R::CTW * (R::DVT + 1) * 4;          // values per lane per span
+    constexpr int SB = V1 >= 48 ? 1 : 96 / V1;
+    for (int s0 = 0; s0 < span; s0 += SB) {
+      f32x4 ts[SB][R::CTW][R::DVT], tz[SB][R::CTW];
 #pragma unroll
-    for (int dt = 0; dt < R::DVT; ++dt)
+      for (int b = 0; b < SB; ++b) {
+        const bool in = s0 + b < span;
+        const size_t sl = (size_t)bh * a.nspan + (in ? s0 + b : 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sacc[j][dt][i] = a.carry[(sslot * CF::Kp + comp0 + 4 * g + i) * C::DV + dt * 16 + c];
+        for (int j = 0; j < R::CTW; ++j) {
+          const int comp0 = koff + (w * R::CTW + j) * 16;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            tz[b][j][i] = in ? a.state_z[sl * CF::Kp + comp0 + 4 * g + i] : 0.f;
+#pragma unroll
+          for (int dt = 0; dt < R::DVT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              ts[b][j][dt][i] = in ? a.state[(sl * CF::Kp + comp0 + 4 * g + i) * C::DV + dt * 16 + c] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < SB; ++b)
+#pragma unroll
+        for (int j = 0; j < R::CTW; ++j) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) zacc[j][i] += tz[b][j][i];
+#pragma unroll
+          for (int dt = 0; dt < R::DVT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sacc[j][dt][i] += ts[b][j][dt][i];
+        }
+    }
   }
   // this wave's rows of the state table: S^T (d rows in pair_row order) and Z.
   // A lane's four components 4g .. 4g+3 of a tile are four consecutive
@@ -989,7 +1023,9 @@ static hipError_t run_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  // 2. exclusive scan over spans
+  // 2. exclusive scan over spans (the token-owner scan sums the earlier spans'
+  // totals itself)
+  if constexpr (!TOK) {
   const int nred = C::Kp * C::DV + C::Kp;
   if (g_launch_hook) g_launch_hook("gma_span_scan", s, 1);
   hipLaunchKernelGGL(gma_span_scan_kernel, dim3((nred + 255) / 256, (unsigned)p.BH), dim3(256), 0,
@@ -999,6 +1035,7 @@ static hipError_t run_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   if (g_launch_hook) g_launch_hook("gma_span_scan", s, 0);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  }
 
   // 3. chunked scan
   CausalArgs ca{};
@@ -1022,6 +1059,8 @@ static hipError_t run_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   ca.k_lo = t.k_lo;
   if (g_launch_hook) g_launch_hook("gma_causal", s, 1);
   ca.gt = TOK ? reinterpret_cast<const bf16*>(t.ws + p.off_gt) : nullptr;
+  ca.state = reinterpret_cast<const float*>(t.ws + p.off_state);
+  ca.state_z = reinterpret_cast<const float*>(t.ws + p.off_state_z);
   if constexpr (KH) {
     // the first half leaves its partials, the second combines them
     ca.qpart = reinterpret_cast<float*>(t.ws + p.off_qpart);
