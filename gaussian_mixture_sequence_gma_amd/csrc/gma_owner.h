@@ -264,6 +264,20 @@ gma_write2_kernel(BidirArgs a) {
 #pragma unroll
         for (int ct = 1; ct < R::CT; ++ct) m = fmaxf(m, S[tt][ct][i]);
         m = row16_max(m);
+        const int64_t tok = grp * 32 + 8 * g + 4 * tt + i;
+        if (want_assign) {
+          // the lowest component index whose score equals the maximum m (one
+          // of the scores: the maxima select, they do not round)
+          int bi = 0x7fffffff;
+#pragma unroll
+          for (int ct = 0; ct < R::CT; ++ct)
+            bi = min(bi, S[tt][ct][i] == m ? pair_row(ct, c) : 0x7fffffff);
+          bi = min(bi, dpp_i<0xB1>(bi));
+          bi = min(bi, dpp_i<0x4E>(bi));
+          bi = min(bi, dpp_i<0x141>(bi));
+          bi = min(bi, dpp_i<0x140>(bi));
+          if (c == 0 && tok < a.N) a.assign[(size_t)bh * a.N + tok] = bi;
+        }
         float l = 0.f;
 #pragma unroll
         for (int ct = 0; ct < R::CT; ++ct) {
@@ -272,7 +286,6 @@ gma_write2_kernel(BidirArgs a) {
           l += e;
         }
         l = row16_sum(l);
-        const int64_t tok = grp * 32 + 8 * g + 4 * tt + i;
         const float inv = tok < a.N ? fast_rcp(l) : 0.f;
 #pragma unroll
         for (int ct = 0; ct < R::CT; ++ct) {
@@ -288,21 +301,6 @@ gma_write2_kernel(BidirArgs a) {
                    (grp & 1) * 32 + 8 * g;
 #pragma unroll
       for (int ct = 0; ct < R::CT; ++ct) st16(gdst + (size_t)pair_row(ct, c) * 64, A[ct]);
-    }
-    if (want_assign) {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // the largest responsibility is the largest score (ties: lowest index)
-          float bv = S[tt][0][i];
-          int bi = pair_row(0, c);
-#pragma unroll
-          for (int ct = 1; ct < R::CT; ++ct) argmax_merge(bv, bi, S[tt][ct][i], pair_row(ct, c));
-          row16_argmax(bv, bi);
-          const int64_t tok = grp * 32 + 8 * g + 4 * tt + i;
-          if (c == 0 && tok < a.N) a.assign[(size_t)bh * a.N + tok] = bi;
-        }
     }
 
     // V(grp) has arrived once at most the copies and loads of the next group
