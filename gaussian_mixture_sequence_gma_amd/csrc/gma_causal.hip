@@ -788,15 +788,16 @@ gma_causal2_kernel(CausalArgs a) {
           Eq[p][4 + i] = to_bf16(exp2_fast(SQ[2 * p + 1][i] - m));
         }
       if (want_aq) {
-        float bv = SQ[0][0];
-        int bi = koff + pair_row(0, 4 * g);
+        // the lowest component index whose score equals the maximum m (one of
+        // the scores: the maxima select, they do not round)
+        int bi = 0x7fffffff;
 #pragma unroll
         for (int ct = 0; ct < R::CT; ++ct)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            argmax_merge(bv, bi, SQ[ct][i], koff + pair_row(ct, 4 * g + i));
-        groups_argmax(bv, bi);
-        qbv = bv;
+            bi = min(bi, SQ[ct][i] == m ? koff + pair_row(ct, 4 * g + i) : 0x7fffffff);
+        bi = groups_min_i(bi);
+        qbv = m;
         qbi = bi;
         if (HM == 0 && g == 0 && qi < nvalid) a.assign_q[qtok] = bi;
       }
