@@ -20,7 +20,7 @@ LIB_PATH = os.environ.get("GMA_LIBRARY") or os.path.join(_HERE, "libgma.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "gma.h")
 
 GMA_F32, GMA_BF16 = 0, 1
-GMA_PROJ_F32, GMA_PROJ_SPLIT_BF16 = 0, 1
+GMA_PROJ_F32, GMA_PROJ_SPLIT_BF16, GMA_PROJ_FUSED_BF16 = 0, 1, 2
 GMA_OK, GMA_ERR_INVALID_ARG, GMA_ERR_UNSUPPORTED, GMA_ERR_WORKSPACE, GMA_ERR_HIP = range(5)
 
 

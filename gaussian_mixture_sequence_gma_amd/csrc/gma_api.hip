@@ -415,16 +415,22 @@ int gma_forward_noalloc(const void* Q_X, const void* K_X, const void* V_X, const
                      assign_k, ws, GMA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
-// The layer's plan and where its projections sit.  Where the bf16 kernels
-// take split routing vectors for this shape, the projection epilogue writes
-// Q_X and K_X as bf16 pairs (16 significant bits) and V_X in bf16, and the
-// bf16 GMA kernels run on them; otherwise the projections stay fp32 and feed
-// the fp32 GMA path.
+// The layer's plan and where its projections sit.  Fused (causal, bf16, d_r
+// = 64, at most 64 components, the scan kernel's shapes): the
+// projection epilogue forms the routing responsibilities and Q_X, K_X are
+// never stored; V_X is kept in bf16.  Otherwise, where the bf16 kernels take
+// split routing vectors for this shape, the projection epilogue writes Q_X and
+// K_X as bf16 pairs (16 significant bits) and V_X in bf16, and the bf16 GMA
+// kernels run on them; else the projections stay fp32 and feed the fp32 GMA
+// path.
 struct LayerPlan {
   Plan p;
   int split = 0;
+  int fused = 0;
+  int kc = 0;                        // fused: components formed (32 or 64)
   size_t gma_bytes = 0;
   size_t off[5] = {0, 0, 0, 0, 0};   // from the start of the workspace
+  size_t off_eq = 0;                 // fused: the queries' exponentials
   size_t total = 0;
 };
 
@@ -433,8 +439,11 @@ static int layer_plan(const gma_dims* d, int32_t d_model, int causal, LayerPlan&
   if (d_model < 64 || d_model > 8192 || d_model % 64)
     return fail(GMA_ERR_UNSUPPORTED, "d_model must be a multiple of 64 in 64..8192");
   int st = make_plan(d, causal, false, L.p);
-  L.split = st == GMA_OK && !L.p.prod && (causal ? causal_split_ok(L.p) : bidir_split_ok(L.p));
-  if (!L.split) {
+  L.fused = st == GMA_OK && causal && layer_fused_ok(L.p);
+  L.kc = L.p.K <= 32 ? 32 : 64;
+  L.split = !L.fused && st == GMA_OK && !L.p.prod &&
+            (causal ? causal_split_ok(L.p) : bidir_split_ok(L.p));
+  if (!L.split && !L.fused) {
     st = make_plan(d, causal, true, L.p);
     if (st != GMA_OK) return st;
   }
@@ -443,7 +452,12 @@ static int layer_plan(const gma_dims* d, int32_t d_model, int causal, LayerPlan&
   L.gma_bytes = round256(p.total);
   size_t off = L.gma_bytes;
   const size_t nr = (size_t)p.BH * p.N * p.DR, nv = (size_t)p.BH * p.N * p.DV;
-  if (L.split) {
+  if (L.fused) {
+    L.off[4] = off;
+    off += round256(2 * nv);
+    L.off_eq = off;
+    off += round256((size_t)p.BH * p.N * L.kc * 2);
+  } else if (L.split) {
     for (int m = 0; m < 4; ++m) {
       L.off[m] = off;
       off += round256(2 * nr);
@@ -481,7 +495,7 @@ int gma_layer_projection_layout(const gma_dims* d, int32_t d_model, int causal, 
   LayerPlan L;
   st = layer_plan(d, d_model, causal, L);
   if (st != GMA_OK) return st;
-  *format = L.split ? GMA_PROJ_SPLIT_BF16 : GMA_PROJ_F32;
+  *format = L.fused ? GMA_PROJ_FUSED_BF16 : (L.split ? GMA_PROJ_SPLIT_BF16 : GMA_PROJ_F32);
   for (int m = 0; m < 5; ++m) offsets[m] = L.off[m];
   return GMA_OK;
 }
@@ -510,6 +524,39 @@ int gma_layer_forward(const void* X, const void* W_Q, const void* W_K, const voi
   const void* const W[3] = {W_Q, W_K, W_V};
   void* P[3];
   void* lo[2] = {nullptr, nullptr};
+  if (L.fused) {
+    // prologue (the epilogue's coefficient tables), projections with the
+    // responsibilities formed in their epilogue, span totals, scan
+    Tensors t;
+    t.mu = mu;
+    t.ls2 = log_sigma2;
+    t.lpi = log_pi;
+    t.out = out;
+    t.eps = eps;
+    t.ws = ws;
+    hipError_t e = launch_prologue(p, t, s);
+    st = finish_launch(e, "prologue launch");
+    if (st != GMA_OK) return st;
+    P[0] = P[1] = nullptr;
+    P[2] = ws + L.off[4];
+    ProjFused fz;
+    fz.params = ws + p.off_params;
+    fz.head_bytes = p.head_bytes;
+    fz.Kp = p.Kp;
+    fz.DRP = p.DRP;
+    fz.kc = L.kc;
+    fz.eq = ws + L.off_eq;
+    fz.gt = ws + p.off_gt;
+    fz.assign_q = assign_q;
+    fz.assign_k = assign_k;
+    e = launch_proj(X, W, P, lo, 1, p.B, p.N, (int)p.H, d_model, p.DR, p.DV, s, &fz);
+    st = finish_launch(e, "projection launch");
+    if (st != GMA_OK) return st;
+    t.v = P[2];
+    t.eq = ws + L.off_eq;
+    t.kc = L.kc;
+    return finish_launch(launch_causal_fused(p, t, s), "causal launch");
+  }
   if (L.split) {
     P[0] = ws + L.off[0];
     lo[0] = ws + L.off[1];

@@ -51,6 +51,11 @@ struct CausalArgs {
   float* qpart;           // the first half's numerators [BH][N][DV]
   float4* qpart2;         // and (denominator, maximum, best score, its component) [BH][N]
   int koff;               // first component of this half
+  // the fused layer: queries' exponentials exp2(s - max s) [BH][N][kc] bf16 and
+  // the keys' Gamma^K^T [BH][ceil(N/64)][kc][64] from the projection epilogue,
+  // kc (32 or 64) components formed; the others are zero
+  const bf16* eq;
+  int kc;
 };
 
 // out[s] = sum_{s' < s} in[s'] over n terms at stride st, summed in order.
@@ -525,13 +530,16 @@ struct Causal2 {
 // of the tables laid out for CF (K_pad = 2 C::Kp); the first half (HM = 1)
 // leaves each query's numerator, denominator and maximum in qpart / qpart2,
 // the second (HM = 2) rescales both halves to the larger maximum and writes O.
-template <class C, bool XS, int HM = 0, class CF = C>
+// QG: the fused layer's scan, the queries' exponentials and the keys'
+// Gamma^K^T (a.kc rows) given; no routing scores are formed.
+template <class C, bool XS, int HM = 0, class CF = C, bool QG = false>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 gma_causal2_kernel(CausalArgs a) {
   using R = Causal2<C>;
   static_assert(HM == 0 || (!XS && CF::Kp == 2 * C::Kp && CF::DRP == C::DRP), "half scan");
-  __shared__ __attribute__((aligned(16))) bf16x8 coef[R::COEF * 64];
-  __shared__ __attribute__((aligned(16))) float cperm[R::KP];
+  static_assert(!QG || (HM == 0 && !XS), "given responsibilities: one pass");
+  __shared__ __attribute__((aligned(16))) bf16x8 coef[QG ? 1 : R::COEF * 64];
+  __shared__ __attribute__((aligned(16))) float cperm[QG ? 1 : R::KP];
   // Gamma^K^T: KP rows of 64 keys, swizzled as swz_elem<8> (unpadded, filled
   // by 1 KB direct copies)
   __shared__ __attribute__((aligned(16))) bf16 G[R::NB][R::KP * kTile];
@@ -552,11 +560,18 @@ gma_causal2_kernel(CausalArgs a) {
 
   // ---- tables, carried state -------------------------------------------------
   {
-    const char* tb = a.params + (size_t)h * a.head_bytes + a.head_bytes / 2;
-    const bf16x8* src = reinterpret_cast<const bf16x8*>(tb) + (size_t)(koff / 16) * R::NKS * 4 * 64;
-    for (int idx = threadIdx.x; idx < R::COEF * 64; idx += kThreads) coef[idx] = src[idx];
-    const float* cp = reinterpret_cast<const float*>(tb + (size_t)8 * CF::Kp * CF::DRP) + koff;
-    for (int j = threadIdx.x; j < R::KP; j += kThreads) cperm[j] = cp[j];
+    if constexpr (!QG) {
+      const char* tb = a.params + (size_t)h * a.head_bytes + a.head_bytes / 2;
+      const bf16x8* src = reinterpret_cast<const bf16x8*>(tb) + (size_t)(koff / 16) * R::NKS * 4 * 64;
+      for (int idx = threadIdx.x; idx < R::COEF * 64; idx += kThreads) coef[idx] = src[idx];
+      const float* cp = reinterpret_cast<const float*>(tb + (size_t)8 * CF::Kp * CF::DRP) + koff;
+      for (int j = threadIdx.x; j < R::KP; j += kThreads) cperm[j] = cp[j];
+    } else {
+      // the Gamma^K^T rows past kc are never copied: zero in both buffers
+      for (int idx = a.kc * kTile / 8 + threadIdx.x; idx < R::KP * kTile / 8; idx += kThreads)
+#pragma unroll
+        for (int bb = 0; bb < R::NB; ++bb) reinterpret_cast<bf16x8*>(G[bb])[idx] = bf16x8{};
+    }
     // the (Z_hi, Z_lo, 1) block: the ones row and the zero rows are constant
     // (rows 0 and 1 belong to write_st, which runs concurrently)
     for (int idx = threadIdx.x; idx < R::KS * 64; idx += kThreads) {
@@ -647,14 +662,29 @@ gma_causal2_kernel(CausalArgs a) {
   const bf16* vs = reinterpret_cast<const bf16*>(a.v) + (size_t)bh * a.N * C::DV;
   const bf16* qls = XS ? reinterpret_cast<const bf16*>(a.q_lo) + (size_t)bh * a.N * C::DR : qs;
   // Gamma^K^T tiles of this sequence: [chunk][CF::Kp][64] bf16, this half's rows
+  // (given responsibilities: [chunk][kc][64])
   const int64_t nch = (a.N + kTile - 1) / kTile;
-  const bf16* gts = a.gt + (size_t)bh * nch * CF::Kp * kTile + (size_t)koff * kTile;
-  // routing vectors of a chunk's queries, loaded two chunks ahead: two register
-  // buffers, chunks alternating between them
-  bf16x8 xqA[R::NKS], xqlA[R::NKS];
-  bf16x8 xqB[R::NKS], xqlB[R::NKS];
-  auto load_x = [&](int k, bf16x8 (&xq)[R::NKS], bf16x8 (&xql)[R::NKS]) {
+  const int grows = QG ? a.kc : CF::Kp;
+  const bf16* gts = a.gt + (size_t)bh * nch * grows * kTile + (size_t)koff * kTile;
+  // routing vectors of a chunk's queries (given responsibilities: their
+  // exponentials), loaded two chunks ahead: two register buffers, chunks
+  // alternating between them
+  constexpr int NX = QG ? R::KS : R::NKS;
+  bf16x8 xqA[NX], xqlA[NX];
+  bf16x8 xqB[NX], xqlB[NX];
+  auto load_x = [&](int k, bf16x8 (&xq)[NX], bf16x8 (&xql)[NX]) {
     const int64_t tok = t_begin + (int64_t)k * kTile + 16 * w + c;
+    if constexpr (QG) {
+      const bf16* es = a.eq + (size_t)bh * a.N * a.kc;
+#pragma unroll
+      for (int p = 0; p < R::KS; ++p) {
+        const bool ok = tok < t_end && 32 * p < a.kc;
+        const size_t off = ok ? (size_t)tok * a.kc + 32 * p + 8 * g : 0;
+        const bf16x8 e = ld16_nt<bf16x8>(es + off);
+        xq[p] = ok ? e : bf16x8{};
+      }
+      return;
+    }
 #pragma unroll
     for (int s = 0; s < R::NKS; ++s) {
       const int col = 32 * s + 8 * g;
@@ -687,10 +717,11 @@ gma_causal2_kernel(CausalArgs a) {
   // Gamma^K^T tile of chunk k: lane l of copy j fills component row 8 j + l / 8,
   // physical chunk l % 8 (logical chunk of keys (l % 8) ^ (2 row mod 8))
   auto load_g = [&](int k, int buf) {
-    const bf16* src = gts + (size_t)(t_begin / kTile + k) * CF::Kp * kTile;
+    const bf16* src = gts + (size_t)(t_begin / kTile + k) * grows * kTile;
 #pragma unroll
     for (int j = 0; j < R::GRPW; ++j) {
       const int round = w * R::GRPW + j;
+      if (QG && round * 8 >= a.kc) continue;
       const int row = round * 8 + (lane >> 3), pc = lane & 7;
       const int lc = pc ^ ((2 * row) & 6);
       global_to_lds16_nt(src + (size_t)row * kTile + lc * 8, &G[buf][round * 512]);
@@ -712,7 +743,7 @@ gma_causal2_kernel(CausalArgs a) {
 
   // one chunk; xq, xql hold its routing vectors and afterwards receive those of
   // chunk k + 2
-  auto chunk = [&](int k, bf16x8 (&xq)[R::NKS], bf16x8 (&xql)[R::NKS]) {
+  auto chunk = [&](int k, bf16x8 (&xq)[NX], bf16x8 (&xql)[NX]) {
     const int buf = R::NB == 2 ? (k & 1) : 0;
     const int64_t tile0 = t_begin + (int64_t)k * kTile;
     const int64_t rem = t_end - tile0;
@@ -737,6 +768,15 @@ gma_causal2_kernel(CausalArgs a) {
         pq = *reinterpret_cast<const f32x4*>(a.qpart2 + qtok);
       }
     }
+    // e = exp2(s - max), packed as the B operand of the contractions over
+    // components
+    bf16x8 Eq[R::KS];
+    float mq = 0.f, qbv = 0.f;
+    int qbi = 0;
+    if constexpr (QG) {
+#pragma unroll
+      for (int p = 0; p < R::KS; ++p) Eq[p] = xq[p];
+    } else {
     // features of this wave's 16 queries
     bf16x8 fq[R::NKS][NFX<XS>];
 #pragma unroll
@@ -767,11 +807,6 @@ gma_causal2_kernel(CausalArgs a) {
       }
     }
 
-    // e = exp2(s - max), packed as the B operand of the contractions over
-    // components
-    bf16x8 Eq[R::KS];
-    float mq, qbv = 0.f;
-    int qbi = 0;
     {
       float v = SQ[0][0];
 #pragma unroll
@@ -802,6 +837,7 @@ gma_causal2_kernel(CausalArgs a) {
         if (HM == 0 && g == 0 && qi < nvalid) a.assign_q[qtok] = bi;
       }
     }
+    }
     wait_global_loads();                 // V(k), Gamma^K^T(k) and this wave's loads
     lds_barrier();                                                    // B1
     if constexpr (R::NB == 2) {
@@ -816,11 +852,15 @@ gma_causal2_kernel(CausalArgs a) {
     f32x4 acc[R::OT];
 #pragma unroll
     for (int dt = 0; dt < R::OT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // given responsibilities: the 32-component steps past kc are zero
+    const int ksn = QG ? (a.kc + 31) / 32 : R::KS;
 #pragma unroll
-    for (int p = 0; p < R::KS; ++p)
+    for (int p = 0; p < R::KS; ++p) {
+      if (QG && p >= ksn) break;
 #pragma unroll
       for (int dt = 0; dt < R::OT; ++dt)
         acc[dt] = mma(reinterpret_cast<const bf16x8*>(ST)[(dt * R::KS + p) * 64 + lane], Eq[p], acc[dt]);
+    }
     // intra-chunk: key pairs (32 keys; rows of key tile jt in tile_token order,
     // so a pair covers keys 32pp .. 32pp + 31) up to the one holding this wave's
     // queries, which is masked to keys <= query.  The A operand (key rows,
@@ -834,7 +874,10 @@ gma_causal2_kernel(CausalArgs a) {
         P[b] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int blk = 32 * pp + 8 * (lane & 3) + 4 * b;
 #pragma unroll
-        for (int p = 0; p < R::KS; ++p) P[b] = mma(tr_chunk_swz_blk<8>(G[buf], 32 * p, blk), Eq[p], P[b]);
+        for (int p = 0; p < R::KS; ++p) {
+          if (QG && p >= ksn) break;
+          P[b] = mma(tr_chunk_swz_blk<8>(G[buf], 32 * p, blk), Eq[p], P[b]);
+        }
         if (pp == (w >> 1)) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -918,6 +961,7 @@ gma_causal2_kernel(CausalArgs a) {
     for (int P2 = 0; P2 < 2; ++P2) {
 #pragma unroll
       for (int j = 0; j < R::CTW; ++j) {
+        if (QG && (w * R::CTW + j) * 16 >= a.kc) continue;      // rows past kc: zero
         const int comp = (w * R::CTW + j) * 16 + c;
         bf16x8 Ag = *reinterpret_cast<const bf16x8*>(&G[buf][swz_elem<8>(comp, 32 * P2 + 8 * g)]);
         if (nvalid < kTile) {
@@ -943,6 +987,156 @@ gma_causal2_kernel(CausalArgs a) {
   for (int k = 0; k < nchunks; k += 2) {
     chunk(k, xqA, xqlA);
     if (k + 1 < nchunks) chunk(k + 1, xqB, xqlB);
+  }
+}
+
+// Span totals of the fused layer from the keys' given responsibilities:
+// S_span = sum over the span's chunks c of Gamma^K_c^T V_c and z_span =
+// Gamma^K_c^T 1 (the memories of "Causal GMA", Eq. 8b, summed over one span),
+// each wave on its component tiles as in the scan's state update.  A ring of
+// four tile buffers filled by direct global -> LDS copies keeps three chunks
+// in flight.
+template <class C, int KC>
+__global__ void __launch_bounds__(kThreads) gma_gt_totals_kernel(CausalArgs a, float* state,
+                                                                 float* state_z) {
+  using R = Causal2<C>;
+  constexpr int NBUF = 4;
+  constexpr int GRW = KC * kTile * 2 / 1024 / kWaves;      // 1 KB copies per wave and chunk
+  constexpr int VRW = R::VROUNDS / kWaves;
+  constexpr int L = GRW + VRW;
+  static_assert(KC * kTile * 2 / 1024 % kWaves == 0 && R::VROUNDS % kWaves == 0 && KC <= R::KP,
+                "copies divide among the waves");
+  __shared__ __attribute__((aligned(16))) bf16 G[NBUF][KC * kTile];
+  __shared__ __attribute__((aligned(16))) bf16 Vb[NBUF][kTile * C::DV];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int64_t bh = blockIdx.y;
+  const int span = blockIdx.x;
+  const int64_t t_begin = (int64_t)span * a.span_tiles * kTile;
+  const int64_t t_end = a.N < t_begin + (int64_t)a.span_tiles * kTile
+                            ? a.N : t_begin + (int64_t)a.span_tiles * kTile;
+  const int nchunks = t_end > t_begin ? (int)((t_end - t_begin + kTile - 1) / kTile) : 0;
+  const bf16* vs = reinterpret_cast<const bf16*>(a.v) + (size_t)bh * a.N * C::DV;
+  const int64_t nch = (a.N + kTile - 1) / kTile;
+  const bf16* gts = a.gt + (size_t)bh * nch * KC * kTile;
+
+  auto load = [&](int k, int buf) {
+    const int64_t t0 = t_begin + (int64_t)k * kTile;
+    const int64_t rem = t_end - t0;
+    const int nv = (int)(rem < kTile ? rem : kTile);
+#pragma unroll
+    for (int j = 0; j < VRW; ++j) {
+      const int round = w * VRW + j;
+      const int P = round * 64 + lane;
+      const int r = P / R::VROWCH, pc = P - r * R::VROWCH;
+      const int lc = pc ^ ((2 * r) & (R::VROWCH - 2));
+      const int rr = r < nv ? r : nv - 1;
+      global_to_lds16_nt(vs + (size_t)(t0 + rr) * C::DV + lc * 8, &Vb[buf][round * 512]);
+    }
+    const bf16* src = gts + (size_t)(t_begin / kTile + k) * KC * kTile;
+#pragma unroll
+    for (int j = 0; j < GRW; ++j) {
+      const int round = w * GRW + j;
+      const int row = round * 8 + (lane >> 3), pc = lane & 7;
+      const int lc = pc ^ ((2 * row) & 6);
+      global_to_lds16_nt(src + (size_t)row * kTile + lc * 8, &G[buf][round * 512]);
+    }
+  };
+
+  f32x4 sacc[R::CTW][R::DVT], zacc[R::CTW];
+#pragma unroll
+  for (int j = 0; j < R::CTW; ++j) {
+    zacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int dt = 0; dt < R::DVT; ++dt) sacc[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (bf16)1.0f;
+
+  for (int k = 0; k < NBUF - 1 && k < nchunks; ++k) load(k, k);
+  for (int k = 0; k < nchunks; ++k) {
+    const int buf = k % NBUF;
+    // chunk k's copies are complete once at most those of the chunks issued
+    // after it (k + 1 .. k + NBUF - 2) are outstanding
+    const int later = (nchunks - 1 < k + NBUF - 2 ? nchunks - 1 : k + NBUF - 2) - k;
+    if (later >= 2) wait_vmcnt<2 * L>();
+    else if (later == 1) wait_vmcnt<L>();
+    else wait_global_loads();
+    lds_barrier();                       // every wave's copies of chunk k; chunk k - 1 read
+    if (k + NBUF - 1 < nchunks) load(k + NBUF - 1, (k + NBUF - 1) % NBUF);
+    const int64_t rem = t_end - (t_begin + (int64_t)k * kTile);
+    const int nvalid = (int)(rem < kTile ? rem : kTile);
+#pragma unroll
+    for (int P2 = 0; P2 < 2; ++P2) {
+#pragma unroll
+      for (int j = 0; j < R::CTW; ++j) {
+        if ((w * R::CTW + j) * 16 >= KC) continue;
+        const int comp = (w * R::CTW + j) * 16 + c;
+        bf16x8 Ag = *reinterpret_cast<const bf16x8*>(&G[buf][swz_elem<8>(comp, 32 * P2 + 8 * g)]);
+        if (nvalid < kTile) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (32 * P2 + 8 * g + e >= nvalid) Ag[e] = (bf16)0.f;
+        }
+        zacc[j] = mma(Ag, ones, zacc[j]);
+#pragma unroll
+        for (int dt = 0; dt < R::DVT; ++dt)
+          sacc[j][dt] = mma(Ag, tr_chunk_swz<R::VROWCH>(Vb[buf], 32 * P2, dt * 16), sacc[j][dt]);
+      }
+    }
+  }
+  // this span's totals, [BH][nspan][K_pad][d_v] and [BH][nspan][K_pad]
+  const size_t sl = (size_t)bh * a.nspan + span;
+#pragma unroll
+  for (int j = 0; j < R::CTW; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int comp = (w * R::CTW + j) * 16 + 4 * g + i;
+      if (c == 0) state_z[sl * R::KP + comp] = zacc[j][i];
+#pragma unroll
+      for (int dt = 0; dt < R::DVT; ++dt) state[(sl * R::KP + comp) * C::DV + dt * 16 + c] = sacc[j][dt][i];
+    }
+}
+
+// The fused layer's causal forward after the projection epilogue: span totals
+// from the keys' responsibilities, then the scan on the given responsibilities.
+template <class C>
+static hipError_t run_causal_fused(const Plan& p, const Tensors& t, hipStream_t s) {
+  if constexpr (!(C::kBF && Causal2<C>::kOK)) {
+    return hipErrorNotSupported;
+  } else {
+    if (t.kc != 32 && t.kc != 64) return hipErrorInvalidValue;
+    CausalArgs ca{};
+    ca.v = t.v;
+    ca.out = t.out;
+    ca.N = p.N;
+    ca.H = (int)p.H;
+    ca.nspan = p.nspan;
+    ca.span_tiles = p.span_tiles;
+    ca.eps = t.eps;
+    ca.out_bf = p.out_bf ? 1 : 0;
+    ca.gt = reinterpret_cast<const bf16*>(t.ws + p.off_gt);
+    ca.eq = static_cast<const bf16*>(t.eq);
+    ca.kc = t.kc;
+    float* state = reinterpret_cast<float*>(t.ws + p.off_state);
+    float* state_z = reinterpret_cast<float*>(t.ws + p.off_state_z);
+    ca.state = state;
+    ca.state_z = state_z;
+    const dim3 grid(p.nspan, (unsigned)p.BH);
+    if (g_launch_hook) g_launch_hook("gma_span_state", s, 1);
+    if (t.kc == 32)
+      hipLaunchKernelGGL((gma_gt_totals_kernel<C, 32>), grid, dim3(kThreads), 0, s, ca, state, state_z);
+    else
+      hipLaunchKernelGGL((gma_gt_totals_kernel<C, 64>), grid, dim3(kThreads), 0, s, ca, state, state_z);
+    if (g_launch_hook) g_launch_hook("gma_span_state", s, 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (g_launch_hook) g_launch_hook("gma_causal", s, 1);
+    hipLaunchKernelGGL((gma_causal2_kernel<C, false, 0, C, true>), grid, dim3(kThreads), 0, s, ca);
+    if (g_launch_hook) g_launch_hook("gma_causal", s, 0);
+    return hipGetLastError();
   }
 }
 
@@ -1124,6 +1318,26 @@ static hipError_t causal_split_query_all(const Plan& p, const Tensors& t, hipStr
 
 bool causal_split_ok(const Plan& p) {
   return p.bf && causal_split_query_all(p, Tensors{}, nullptr) == hipSuccess;
+}
+
+bool layer_fused_ok(const Plan& p) {
+  return p.bf && !p.prod && !p.khalf && p.NG == 4 && p.Kp == 64 && p.DR == 64 &&
+         p.DV >= 32 && causal2_lds_bytes(true, p.DRP, p.DV, p.Kp) > 0;
+}
+
+#define GMA_FUSED_DV(DR)                                                      \
+  switch (p.DV) {                                                             \
+    case 32: return run_causal_fused<Cfg<true, 1, 4, DR, 32>>(p, t, s);       \
+    case 64: return run_causal_fused<Cfg<true, 1, 4, DR, 64>>(p, t, s);       \
+    case 128: return run_causal_fused<Cfg<true, 1, 4, DR, 128>>(p, t, s);     \
+  }                                                                           \
+  break;
+hipError_t launch_causal_fused(const Plan& p, const Tensors& t, hipStream_t s) {
+  if (!layer_fused_ok(p)) return hipErrorInvalidValue;
+  switch (0) {
+    default: GMA_FUSED_DV(64)
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s) {

@@ -68,6 +68,10 @@ struct Tensors {
   // usage statistics: per-workgroup partials and the utilisation threshold
   float* diag = nullptr;
   float thr = 0.f;
+  // fused layer: the queries' exponentials from the projection epilogue
+  // ([BH][N][kc] bf16; the keys' Gamma^K^T sit at off_gt) and kc
+  void* eq = nullptr;
+  int kc = 0;
 };
 
 // Launch helpers; each returns hipSuccess or the launch error.  `tag` names the
@@ -82,6 +86,11 @@ bool bidir_split_ok(const Plan& p);
 bool causal_split_ok(const Plan& p);
 hipError_t launch_bidir(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s);
+// The fused layer (causal, bf16, d_r = 64, K_pad 64, the scan kernel's
+// shapes): after launch_proj's fused epilogue, span totals from the keys'
+// Gamma^K^T at off_gt and the scan on the given responsibilities (t.eq, t.kc).
+bool layer_fused_ok(const Plan& p);
+hipError_t launch_causal_fused(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_resp(const Plan& p, const Tensors& t, hipStream_t s);
 // Usage statistics of the responsibilities of t.q (per head, over batches and
 // tokens); t.diag holds B*H*S*(3 K_pad + 4) floats of partials.
@@ -121,8 +130,23 @@ hipError_t launch_reparam(const float* omega, const float* alpha, float eps_sigm
 // Q_X, K_X, V_X = X W_Q, X W_K, X W_V (W[0..2]) into fp32 head-major out[0..2].
 // split = 0: out[0..2] are fp32.  split = 1: Q_X and K_X as bf16 pairs (out[m],
 // lo[m]: value = out + lo, 16 significant bits), V_X as bf16 in out[2].
+// fz (the fused form, d_r = 64): Q_X and K_X are not stored; the
+// epilogue writes per query the exponentials exp2(s - max s) of its routing
+// scores, bf16 [B,H,N][kc], and per 64-key chunk the keys' responsibilities
+// transposed, bf16 [B,H,ceil(N/64)][kc][64] (and the assignments when given),
+// from the prologue's tables; V_X as bf16 in out[2].
+struct ProjFused {
+  const char* params = nullptr;
+  size_t head_bytes = 0;
+  int Kp = 0, DRP = 0;
+  int kc = 0;              // components formed: 32 or 64
+  void* eq = nullptr;
+  void* gt = nullptr;
+  int32_t* assign_q = nullptr;
+  int32_t* assign_k = nullptr;
+};
 hipError_t launch_proj(const void* X, const void* const W[3], void* const out[3],
                        void* const lo[2], int split, int64_t B, int64_t N, int H, int d_model,
-                       int d_r, int d_v, hipStream_t s);
+                       int d_r, int d_v, hipStream_t s, const ProjFused* fz = nullptr);
 
 }  // namespace gma

@@ -162,8 +162,11 @@ int gma_layer_forward(const void* X, const void* W_Q, const void* W_K, const voi
 /* Storage of the projections gma_layer_forward leaves in its workspace. */
 typedef enum {
   GMA_PROJ_F32 = 0,        /* Q_X, K_X, V_X fp32 [B,H,N,d] at offsets[0..2] */
-  GMA_PROJ_SPLIT_BF16 = 1  /* bf16 [B,H,N,d]: Q_X hi, Q_X lo, K_X hi, K_X lo, V_X at
+  GMA_PROJ_SPLIT_BF16 = 1, /* bf16 [B,H,N,d]: Q_X hi, Q_X lo, K_X hi, K_X lo, V_X at
                               offsets[0..4]; Q_X = hi + lo */
+  GMA_PROJ_FUSED_BF16 = 2  /* Q_X and K_X are not stored (the projection's epilogue
+                              forms the routing responsibilities from them); V_X bf16
+                              [B,H,N,d_v] at offsets[4], offsets[0..3] = 0 */
 } gma_proj_format;
 
 /* Where gma_layer_forward leaves the projections for this shape and variant

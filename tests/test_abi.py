@@ -165,24 +165,36 @@ def test_timing_collect_empty():
 
 
 @pytest.mark.parametrize("causal", [0, 1])
-@pytest.mark.parametrize("kw,fmt", [
-    # bf16 token-owner kernels take split routing vectors: split bf16 projections
-    ({}, B.GMA_PROJ_SPLIT_BF16),
-    ({"K": 32, "N": 16384}, B.GMA_PROJ_SPLIT_BF16),
-    ({"K": 128, "d_v": 128}, B.GMA_PROJ_SPLIT_BF16),
+@pytest.mark.parametrize("kw,fmts", [
+    # bf16 token-owner kernels take split routing vectors: split bf16
+    # projections; causal with d_r = 64 and at most 64 components: the
+    # projection epilogue forms the responsibilities (only V_X is kept)
+    ({}, (B.GMA_PROJ_SPLIT_BF16, B.GMA_PROJ_FUSED_BF16)),
+    ({"K": 32, "N": 16384}, (B.GMA_PROJ_SPLIT_BF16, B.GMA_PROJ_FUSED_BF16)),
+    ({"K": 128, "d_v": 128}, (B.GMA_PROJ_SPLIT_BF16, B.GMA_PROJ_SPLIT_BF16)),
+    ({"d_r": 32, "K": 20}, (B.GMA_PROJ_SPLIT_BF16, B.GMA_PROJ_SPLIT_BF16)),
     # d_r = 128 exceeds the token-owner kernels: fp32 projections, fp32 path
-    ({"d_r": 128}, B.GMA_PROJ_F32),
+    ({"d_r": 128}, (B.GMA_PROJ_F32, B.GMA_PROJ_F32)),
 ])
-def test_layer_projection_layout(kw, fmt, causal):
+def test_layer_projection_layout(kw, fmts, causal):
     d = _dims(**kw)
     got, offs = B.gma_layer_projection_layout(d, 256, causal)
     total = B.gma_layer_workspace_bytes(d, 256, causal)
-    assert got == fmt
+    assert got == fmts[causal]
     T = d.B * d.H * d.N
     if got == B.GMA_PROJ_F32:
         sizes = [4 * T * d.d_r, 4 * T * d.d_r, 4 * T * d.d_v]
         used = offs[:3]
         assert offs[3] == offs[4] == 0
+    elif got == B.GMA_PROJ_FUSED_BF16:
+        # V_X, then the queries' exponentials (32 or 64 components) at the tail
+        sizes = [2 * T * d.d_v]
+        used = offs[4:]
+        assert offs[0] == offs[1] == offs[2] == offs[3] == 0
+        kc = 32 if d.K <= 32 else 64
+        assert used[0] > 0 and used[0] % 16 == 0
+        assert total - (used[0] + sizes[0]) >= 2 * T * kc
+        return
     else:
         sizes = [2 * T * d.d_r] * 4 + [2 * T * d.d_v]
         used = offs

@@ -11,9 +11,13 @@ The projections themselves are checked where gma_layer_forward leaves them
   split form: Q_X and K_X as hi + lo bf16 pairs keep 16 significant bits
     (relative error <= 2^-17 ~ 7.6e-6 per element, on top of the fp32 sum):
     3e-5 row-wise; V_X rounded to bf16 (<= 2^-9 ~ 2e-3 per element): 4e-3.
-In the split form the GMA part runs on the bf16 kernels, whose scores carry
-the bf16 path's error, so assignment near-ties are judged with that path's
-bound.
+  fused form (causal, d_r = 64, K <= 64): Q_X and K_X are never stored -- the
+    projection's epilogue forms the routing responsibilities from its fp32
+    accumulators -- so only V_X (bf16, 4e-3) is read back; the responsibilities
+    are checked through the output and the assignments.
+In the split and fused forms the GMA part runs on the bf16 kernels, whose
+scores carry the bf16 path's error, so assignment near-ties are judged with
+that path's bound.
 """
 import numpy as np
 import pytest
@@ -27,7 +31,8 @@ pytestmark = pytest.mark.gpu
 
 W = inputs.WORKLOADS
 PROJ_TOL = {binding.GMA_PROJ_F32: (1e-5, 1e-5, 1e-5),
-            binding.GMA_PROJ_SPLIT_BF16: (3e-5, 3e-5, 4e-3)}
+            binding.GMA_PROJ_SPLIT_BF16: (3e-5, 3e-5, 4e-3),
+            binding.GMA_PROJ_FUSED_BF16: (None, None, 4e-3)}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -38,8 +43,12 @@ def _gpu():
 
 
 def _projections(ws, fmt, offs, sizes):
-    """Q_X, K_X, V_X as float64 numpy arrays read back from the workspace."""
+    """Q_X, K_X, V_X as float64 numpy arrays read back from the workspace (None
+    for those the fused form never stores)."""
     out = []
+    if fmt == binding.GMA_PROJ_FUSED_BF16:
+        v = ws[offs[4]:offs[4] + 2 * sizes[2]].view(torch.bfloat16).float().cpu().numpy()
+        return [None, None, v.astype(np.float64)]
     if fmt == binding.GMA_PROJ_F32:
         for m, n in enumerate(sizes):
             out.append(ws[offs[m]:offs[m] + 4 * n].view(torch.float32).cpu().numpy()
@@ -70,6 +79,8 @@ def _run(w, seed=0, rows=None, check_proj=True):
         sizes = [w.B * w.H * w.N * d for d in (w.d_r, w.d_r, w.d_v)]
         got = _projections(ws, fmt, offs, sizes)
         for name, g, ref, tol in zip("QKV", got, P, PROJ_TOL[fmt]):
+            if g is None:
+                continue
             err = rowwise_rel_err(g.reshape(ref.shape), ref)
             print("[layer] %s projection (format %d) row-wise err %.3e" % (name, fmt, err),
                   flush=True)
@@ -144,3 +155,44 @@ def test_layer_k_above_128(causal):
     w = W["layer_causal_bf16"].with_(B=1, H=3, N=300, d_r=64, d_v=64, K=200, d_model=128,
                                      causal=causal)
     _run(w)
+
+
+# The fused form: causal, d_r = 64, K <= 64 (32 or 64 components formed by
+# the projection epilogue).  Lengths not a multiple of 4 take the epilogue's
+# per-key stores; H = 3 leaves the last 256-feature tile partly empty; B = 3
+# with short sequences puts several sequences in one 256-token tile.
+@pytest.mark.parametrize("N", [1, 3, 63, 65, 130, 301])
+@pytest.mark.parametrize("K", [32, 50])
+def test_layer_fused_ragged(N, K):
+    w = W["layer_causal_bf16"].with_(B=3, H=3, N=N, K=K, d_model=128)
+    fmt, _ = binding.gma_layer_projection_layout(
+        binding.make_dims(w.B, w.H, w.N, w.d_r, w.d_v, w.K, binding.GMA_BF16), w.d_model, 1)
+    assert fmt == binding.GMA_PROJ_FUSED_BF16
+    _run(w)
+
+
+@pytest.mark.parametrize("d_v", [32, 128])
+@pytest.mark.parametrize("K", [7, 64])
+def test_layer_fused_value_dims(d_v, K):
+    w = W["layer_causal_bf16"].with_(B=2, H=5, N=777, K=K, d_v=d_v, d_model=192)
+    _run(w)
+
+
+def test_layer_fused_several_chunks_per_span():
+    # 32 sequences of 2000 tokens: spans of several 64-token chunks, the last
+    # one ragged, through the span totals and the scan
+    w = W["layer_causal_bf16"].with_(B=2, H=16, N=2000, d_model=256)
+    _run(w, rows=inputs.sample_rows(w.N, 200, seed=5))
+
+
+def test_layer_fused_assignments_optional():
+    # without assignment outputs the epilogue takes its other branch: the
+    # output is bitwise the same
+    w = W["layer_causal_bf16"].with_(B=2, H=4, N=999, d_model=128)
+    gen = inputs.generate(w, 0)
+    dev = upload(gen)
+    args = (dev["X"], dev["W_Q"], dev["W_K"], dev["W_V"], w.H, dev["mu"], dev["log_sigma2"],
+            dev["log_pi"], w.eps, True)
+    o1, _, _ = api.layer_forward(*args, assign=True)
+    o2 = api.layer_forward(*args, assign=False)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
