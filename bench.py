@@ -51,12 +51,23 @@ def kernel_flops(name: str, w) -> int:
     return 0
 
 
-def kernel_bytes(name: str, w, s_r: int, s_v: int, s_out: int) -> int:
+def kernel_bytes(name: str, w, s_r: int, s_v: int, s_out: int, kc: int = 0) -> int:
     """Algorithmic HBM bytes of one launch of `name` on workload w: s_r, s_v are
     the bytes per element of the routing vectors and values the GMA kernels
     read (a split routing vector is a bf16 pair, 4 bytes), s_out of O.  The
-    layer's projection writes Q_X, K_X, V_X in the form the GMA kernels read."""
+    layer's projection writes Q_X, K_X, V_X in the form the GMA kernels read;
+    in the fused form (kc > 0) it writes V_X and, in place of Q_X and K_X, the
+    queries' exponentials and the keys' responsibilities (kc bf16 each per
+    token and head), which the span totals and the scan read."""
     T = w.B * w.H * w.N
+    if kc:
+        if name == "gma_proj":
+            return 2 * (w.B * w.N * w.d_model + w.d_model * w.H * (2 * w.d_r + w.d_v)) + \
+                T * (4 * kc + 2 * w.d_v)
+        if name == "gma_span_state":
+            return T * (2 * kc + 2 * w.d_v)
+        if name == "gma_causal":
+            return T * (4 * kc + 2 * w.d_v + w.d_v * s_out)
     if name == "gma_proj":
         return 2 * (w.B * w.N * w.d_model + w.d_model * w.H * (2 * w.d_r + w.d_v)) + \
             T * (2 * w.d_r * s_r + w.d_v * s_v)
@@ -236,6 +247,7 @@ def main():
     gen = inputs.generate(w, 0)
     s_out = 2 if w.dtype == "bf16" else 4
     s_r = s_v = s_out
+    kc = 0                                 # fused layer: components formed
 
     decode = w.state_len > 0
     if w.d_model > 0:
@@ -260,7 +272,10 @@ def main():
         # the projections reach the GMA kernels as bf16 pairs (Q_X, K_X) and
         # bf16 (V_X), or all in fp32
         fmt, _ = binding.gma_layer_projection_layout(dims, w.d_model, int(w.causal))
-        s_r, s_v = (4, 2) if fmt == binding.GMA_PROJ_SPLIT_BF16 else (4, 4)
+        s_r, s_v = (4, 2) if fmt in (binding.GMA_PROJ_SPLIT_BF16,
+                                     binding.GMA_PROJ_FUSED_BF16) else (4, 4)
+        if fmt == binding.GMA_PROJ_FUSED_BF16:
+            kc = 32 if w.K <= 32 else 64
     elif decode:
         nbytes = 0
         # the carried state, advanced in place by every step
@@ -377,7 +392,7 @@ def main():
         # roofline is taken for the whole step against its algorithmic bytes
         kernels["gma_backward"] = {"launches": args.steps, "avg_us": 1e3 * ms}
         dom = "gma_backward"
-    dom_bytes = kernel_bytes(dom, w, s_r, s_v, s_out)
+    dom_bytes = kernel_bytes(dom, w, s_r, s_v, s_out, kc)
     dom_flops = kernel_flops(dom, w)
     prof = profile_counters(dom, w.name, kernel_source_hash())
     traffic = prof.get("hbm_bytes_per_launch")
@@ -397,7 +412,7 @@ def main():
                     "alg_bytes_per_launch": dom_bytes}
     # the counters' HBM bytes over the same measured duration
     roofline["traffic_gbs"] = traffic / t_dom / 1e9 if traffic else None
-    step_bytes = sum(kernel_bytes(k, w, s_r, s_v, s_out) for k in kernels)
+    step_bytes = sum(kernel_bytes(k, w, s_r, s_v, s_out, kc) for k in kernels)
 
     cpu = None
     if not args.no_cpu_baseline and not args.usage_stats and not args.backward:

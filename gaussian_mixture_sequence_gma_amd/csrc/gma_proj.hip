@@ -263,38 +263,51 @@ __global__ void __launch_bounds__(64 * WAF * WAT) gma_proj_kernel(ProjArgs a) {
             seed[ct] = f32x4{cv, cv, cv, cv};
           }
         }
+        // token tiles in pairs: each coefficient operand read from LDS serves
+        // both
+        constexpr int TB = 2;
 #pragma unroll
-        for (int tn = 0; tn < WT; ++tn) {
-          f32x4 S[KE];
+        for (int tp = 0; tp < WT; tp += TB) {
+          f32x4 SS[TB][KE];
 #pragma unroll
-          for (int ct = 0; ct < KE; ++ct) S[ct] = seed[ct];
+          for (int bb = 0; bb < TB; ++bb)
+#pragma unroll
+            for (int ct = 0; ct < KE; ++ct) SS[bb][ct] = seed[ct];
 #pragma unroll
           for (int j = 0; j < NKH; ++j) {
-            // features of token 16 tn + s16 in routing chunk j, from the fp32
+            // features of tokens 16 tn + s16 in routing chunk j, from the fp32
             // accumulators
             const int jj = hh * NKH + j;
-            bf16x8 F[4];
+            bf16x8 F[TB][4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float x = acc[2 * jj + (e >> 2)][tn][e & 3];
-              bf16 h2, l2, h1, l1;
-              split_bf16(x * x, h2, l2);
-              split_bf16(x, h1, l1);
-              F[0][e] = h2;
-              F[1][e] = l2;
-              F[2][e] = h1;
-              F[3][e] = l1;
-            }
+            for (int bb = 0; bb < TB; ++bb)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const float x = acc[2 * jj + (e >> 2)][tp + bb][e & 3];
+                bf16 h2, l2, h1, l1;
+                split_bf16(x * x, h2, l2);
+                split_bf16(x, h1, l1);
+                F[bb][0][e] = h2;
+                F[bb][1][e] = l2;
+                F[bb][2][e] = h1;
+                F[bb][3][e] = l1;
+              }
 #pragma unroll
             for (int ct = 0; ct < KE; ++ct) {
               const bf16x8* tq = tab + ((jj * KE + ct) * 4) * 64 + lane;
               const bf16x8 Wv[4] = {tq[0], tq[64], tq[128], tq[192]};
 #pragma unroll
-              for (int u = 0; u < 6; ++u)
-                S[ct] = qside ? mma(Wv[kPW[u]], F[kPF[u]], S[ct])
-                              : mma(F[kPF[u]], Wv[kPW[u]], S[ct]);
+              for (int bb = 0; bb < TB; ++bb)
+#pragma unroll
+                for (int u = 0; u < 6; ++u)
+                  SS[bb][ct] = qside ? mma(Wv[kPW[u]], F[bb][kPF[u]], SS[bb][ct])
+                                     : mma(F[bb][kPF[u]], Wv[kPW[u]], SS[bb][ct]);
             }
           }
+#pragma unroll
+          for (int bb = 0; bb < TB; ++bb) {
+          const int tn = tp + bb;
+          f32x4 (&S)[KE] = SS[bb];
           if (qside) {
             // query 16 tn + s16: exponentials exp2(s - max) (the scan's
             // unnormalised responsibilities) and the lowest component at the
@@ -392,6 +405,7 @@ __global__ void __launch_bounds__(64 * WAF * WAT) gma_proj_kernel(ProjArgs a) {
                 if (a.assign_k && s16 == 0) a.assign_k[sq * a.N + n] = bk[i];
               }
             }
+          }
           }
         }
       }
