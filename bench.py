@@ -68,6 +68,8 @@ def kernel_bytes(name: str, w, s_r: int, s_v: int, s_out: int, kc: int = 0) -> i
             return T * (2 * kc + 2 * w.d_v)
         if name == "gma_causal":
             return T * (4 * kc + 2 * w.d_v + w.d_v * s_out)
+        if name == "gma_read":
+            return T * (2 * kc + w.d_v * s_out)
     if name == "gma_proj":
         return 2 * (w.B * w.N * w.d_model + w.d_model * w.H * (2 * w.d_r + w.d_v)) + \
             T * (2 * w.d_r * s_r + w.d_v * s_v)

@@ -415,8 +415,8 @@ int gma_forward_noalloc(const void* Q_X, const void* K_X, const void* V_X, const
                      assign_k, ws, GMA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
-// The layer's plan and where its projections sit.  Fused (causal, bf16, d_r
-// = 64, at most 64 components, the scan kernel's shapes): the
+// The layer's plan and where its projections sit.  Fused (bf16, d_r = 64, at
+// most 64 components, the scan kernel's shapes; either variant): the
 // projection epilogue forms the routing responsibilities and Q_X, K_X are
 // never stored; V_X is kept in bf16.  Otherwise, where the bf16 kernels take
 // split routing vectors for this shape, the projection epilogue writes Q_X and
@@ -438,9 +438,11 @@ static int layer_plan(const gma_dims* d, int32_t d_model, int causal, LayerPlan&
   if (d->dtype != GMA_BF16) return fail(GMA_ERR_UNSUPPORTED, "the projection layer takes bf16 X and W");
   if (d_model < 64 || d_model > 8192 || d_model % 64)
     return fail(GMA_ERR_UNSUPPORTED, "d_model must be a multiple of 64 in 64..8192");
-  int st = make_plan(d, causal, false, L.p);
-  L.fused = st == GMA_OK && causal && layer_fused_ok(L.p);
+  // the fused form runs on the causal plan (K_pad 64, spans) in both variants
+  int st = make_plan(d, 1, false, L.p);
+  L.fused = st == GMA_OK && layer_fused_ok(L.p);
   L.kc = L.p.K <= 32 ? 32 : 64;
+  if (!L.fused) st = make_plan(d, causal, false, L.p);
   L.split = !L.fused && st == GMA_OK && !L.p.prod &&
             (causal ? causal_split_ok(L.p) : bidir_split_ok(L.p));
   if (!L.split && !L.fused) {
@@ -555,7 +557,8 @@ int gma_layer_forward(const void* X, const void* W_Q, const void* W_K, const voi
     t.v = P[2];
     t.eq = ws + L.off_eq;
     t.kc = L.kc;
-    return finish_launch(launch_causal_fused(p, t, s), "causal launch");
+    return finish_launch(launch_layer_fused(p, t, causal != 0, s),
+                         causal ? "causal launch" : "bidirectional launch");
   }
   if (L.split) {
     P[0] = ws + L.off[0];

@@ -531,13 +531,17 @@ struct Causal2 {
 // leaves each query's numerator, denominator and maximum in qpart / qpart2,
 // the second (HM = 2) rescales both halves to the larger maximum and writes O.
 // QG: the fused layer's scan, the queries' exponentials and the keys'
-// Gamma^K^T (a.kc rows) given; no routing scores are formed.
-template <class C, bool XS, int HM = 0, class CF = C, bool QG = false>
+// Gamma^K^T (a.kc rows) given; no routing scores are formed.  BI (with QG):
+// the bidirectional read-out, O_i = gamma^Q_i V~ / (gamma^Q_i Z + eps) with
+// the memories of all keys ("Normalized broadcasting", Eq. 7): the state is
+// the sum of every span's totals and no chunk is scanned.
+template <class C, bool XS, int HM = 0, class CF = C, bool QG = false, bool BI = false>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 gma_causal2_kernel(CausalArgs a) {
   using R = Causal2<C>;
   static_assert(HM == 0 || (!XS && CF::Kp == 2 * C::Kp && CF::DRP == C::DRP), "half scan");
   static_assert(!QG || (HM == 0 && !XS), "given responsibilities: one pass");
+  static_assert(!BI || QG, "read-out on given responsibilities");
   __shared__ __attribute__((aligned(16))) bf16x8 coef[QG ? 1 : R::COEF * 64];
   __shared__ __attribute__((aligned(16))) float cperm[QG ? 1 : R::KP];
   // Gamma^K^T: KP rows of 64 keys, swizzled as swz_elem<8> (unpadded, filled
@@ -596,11 +600,12 @@ gma_causal2_kernel(CausalArgs a) {
   {
     constexpr int V1 = R::CTW * (R::DVT + 1) * 4;          // values per lane per span
     constexpr int SB = V1 >= 48 ? 1 : 96 / V1;
-    for (int s0 = 0; s0 < span; s0 += SB) {
+    const int nsum = BI ? a.nspan : span;      // read-out: every span's totals
+    for (int s0 = 0; s0 < nsum; s0 += SB) {
       f32x4 ts[SB][R::CTW][R::DVT], tz[SB][R::CTW];
 #pragma unroll
       for (int b = 0; b < SB; ++b) {
-        const bool in = s0 + b < span;
+        const bool in = s0 + b < nsum;
         const size_t sl = (size_t)bh * a.nspan + (in ? s0 + b : 0);
 #pragma unroll
         for (int j = 0; j < R::CTW; ++j) {
@@ -735,8 +740,10 @@ gma_causal2_kernel(CausalArgs a) {
   }
   if (nchunks > 0) {
     load_x(0, xqA, xqlA);
-    load_v(0, 0);
-    load_g(0, 0);
+    if constexpr (!BI) {
+      load_v(0, 0);
+      load_g(0, 0);
+    }
   }
   if (nchunks > 1) load_x(1, xqB, xqlB);
   __syncthreads();                       // coefficient table and seeds visible to every wave
@@ -838,9 +845,11 @@ gma_causal2_kernel(CausalArgs a) {
       }
     }
     }
-    wait_global_loads();                 // V(k), Gamma^K^T(k) and this wave's loads
-    lds_barrier();                                                    // B1
-    if constexpr (R::NB == 2) {
+    if constexpr (!BI) {
+      wait_global_loads();               // V(k), Gamma^K^T(k) and this wave's loads
+      lds_barrier();                                                  // B1
+    }
+    if constexpr (R::NB == 2 && !BI) {
       if (k + 1 < nchunks) {
         load_v(k + 1, buf ^ 1);
         load_g(k + 1, buf ^ 1);
@@ -866,7 +875,7 @@ gma_causal2_kernel(CausalArgs a) {
     // queries, which is masked to keys <= query.  The A operand (key rows,
     // components 32p + 8g ..) is a transpose read of Gamma^K^T: source lane s
     // reads the four keys 8 (s % 4) + 4 jt .. of its component row.
-    for (int pp = 0; pp <= (w >> 1); ++pp) {
+    for (int pp = 0; pp <= (BI ? -1 : (w >> 1)); ++pp) {
       f32x4 P[2];
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
@@ -953,6 +962,7 @@ gma_causal2_kernel(CausalArgs a) {
         }
       }
     }
+    if constexpr (BI) return;
     lds_barrier();                                                    // B2
 
     // ---- state update on this wave's components: S += Gamma^K^T V, z += Gamma^K^T 1
@@ -1100,10 +1110,11 @@ __global__ void __launch_bounds__(kThreads) gma_gt_totals_kernel(CausalArgs a, f
     }
 }
 
-// The fused layer's causal forward after the projection epilogue: span totals
-// from the keys' responsibilities, then the scan on the given responsibilities.
+// The fused layer's forward after the projection epilogue: span totals from
+// the keys' responsibilities, then the scan (causal) or the read-out over all
+// spans' totals (bidirectional) on the given responsibilities.
 template <class C>
-static hipError_t run_causal_fused(const Plan& p, const Tensors& t, hipStream_t s) {
+static hipError_t run_causal_fused(const Plan& p, const Tensors& t, bool causal, hipStream_t s) {
   if constexpr (!(C::kBF && Causal2<C>::kOK)) {
     return hipErrorNotSupported;
   } else {
@@ -1133,9 +1144,15 @@ static hipError_t run_causal_fused(const Plan& p, const Tensors& t, hipStream_t 
     if (g_launch_hook) g_launch_hook("gma_span_state", s, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (g_launch_hook) g_launch_hook("gma_causal", s, 1);
-    hipLaunchKernelGGL((gma_causal2_kernel<C, false, 0, C, true>), grid, dim3(kThreads), 0, s, ca);
-    if (g_launch_hook) g_launch_hook("gma_causal", s, 0);
+    if (causal) {
+      if (g_launch_hook) g_launch_hook("gma_causal", s, 1);
+      hipLaunchKernelGGL((gma_causal2_kernel<C, false, 0, C, true>), grid, dim3(kThreads), 0, s, ca);
+      if (g_launch_hook) g_launch_hook("gma_causal", s, 0);
+    } else {
+      if (g_launch_hook) g_launch_hook("gma_read", s, 1);
+      hipLaunchKernelGGL((gma_causal2_kernel<C, false, 0, C, true, true>), grid, dim3(kThreads), 0, s, ca);
+      if (g_launch_hook) g_launch_hook("gma_read", s, 0);
+    }
     return hipGetLastError();
   }
 }
@@ -1325,14 +1342,14 @@ bool layer_fused_ok(const Plan& p) {
          p.DV >= 32 && causal2_lds_bytes(true, p.DRP, p.DV, p.Kp) > 0;
 }
 
-#define GMA_FUSED_DV(DR)                                                      \
-  switch (p.DV) {                                                             \
-    case 32: return run_causal_fused<Cfg<true, 1, 4, DR, 32>>(p, t, s);       \
-    case 64: return run_causal_fused<Cfg<true, 1, 4, DR, 64>>(p, t, s);       \
-    case 128: return run_causal_fused<Cfg<true, 1, 4, DR, 128>>(p, t, s);     \
-  }                                                                           \
+#define GMA_FUSED_DV(DR)                                                            \
+  switch (p.DV) {                                                                   \
+    case 32: return run_causal_fused<Cfg<true, 1, 4, DR, 32>>(p, t, causal, s);     \
+    case 64: return run_causal_fused<Cfg<true, 1, 4, DR, 64>>(p, t, causal, s);     \
+    case 128: return run_causal_fused<Cfg<true, 1, 4, DR, 128>>(p, t, causal, s);   \
+  }                                                                                 \
   break;
-hipError_t launch_causal_fused(const Plan& p, const Tensors& t, hipStream_t s) {
+hipError_t launch_layer_fused(const Plan& p, const Tensors& t, bool causal, hipStream_t s) {
   if (!layer_fused_ok(p)) return hipErrorInvalidValue;
   switch (0) {
     default: GMA_FUSED_DV(64)

@@ -86,11 +86,13 @@ bool bidir_split_ok(const Plan& p);
 bool causal_split_ok(const Plan& p);
 hipError_t launch_bidir(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s);
-// The fused layer (causal, bf16, d_r = 64, K_pad 64, the scan kernel's
-// shapes): after launch_proj's fused epilogue, span totals from the keys'
-// Gamma^K^T at off_gt and the scan on the given responsibilities (t.eq, t.kc).
+// The fused layer (bf16, d_r = 64, K <= 64, the scan kernel's shapes; p is the
+// causal plan, K_pad 64, for either variant): after launch_proj's fused
+// epilogue, span totals from the keys' Gamma^K^T at off_gt, then the scan
+// (causal) or the read-out over every span's totals (bidirectional) on the
+// given responsibilities (t.eq, t.kc).
 bool layer_fused_ok(const Plan& p);
-hipError_t launch_causal_fused(const Plan& p, const Tensors& t, hipStream_t s);
+hipError_t launch_layer_fused(const Plan& p, const Tensors& t, bool causal, hipStream_t s);
 hipError_t launch_resp(const Plan& p, const Tensors& t, hipStream_t s);
 // Usage statistics of the responsibilities of t.q (per head, over batches and
 // tokens); t.diag holds B*H*S*(3 K_pad + 4) floats of partials.

@@ -146,13 +146,17 @@ int gma_layer_workspace_bytes(const gma_dims* d, int32_t d_model, int causal, si
  *  W_V        [d_model, H*d_v] of d->dtype; head h uses columns [h*d_v, (h+1)*d_v)
  *  d_model    multiple of 64, 64..8192
  * The projections are accumulated in fp32 (bf16 x bf16 products are exact in
- * fp32).  Where the bf16 GMA kernels support the shape (see
- * gma_layer_projection_layout) Q_X and K_X are then kept as bf16 pairs hi + lo
- * (16 significant bits), V_X is rounded to bf16, and the bf16 GMA path runs on
- * them; otherwise all three stay fp32 and feed the fp32 GMA path.  out is
- * [B,H,N,d_v] of d->dtype.  The projections stay in the workspace after the
- * call, at the offsets gma_layer_projection_layout reports.  Other arguments
- * as gma_forward. */
+ * fp32).  With d_r = 64 and K <= 64 (where the bf16 scan kernel takes the
+ * shape) the projection's epilogue forms the routing responsibilities of
+ * Section "Routing via mixture posteriors" (Eq. 3) from the fp32 accumulators
+ * and Q_X, K_X never reach memory; V_X is rounded to bf16.  Otherwise, where
+ * the bf16 GMA kernels support the shape, Q_X and K_X are kept as bf16 pairs
+ * hi + lo (16 significant bits), V_X is rounded to bf16, and the bf16 GMA
+ * path runs on them; else all three stay fp32 and feed the fp32 GMA path
+ * (gma_layer_projection_layout names the form).  out is [B,H,N,d_v] of
+ * d->dtype.  The projections kept stay in the workspace after the call, at
+ * the offsets gma_layer_projection_layout reports.  Other arguments as
+ * gma_forward. */
 int gma_layer_forward(const void* X, const void* W_Q, const void* W_K, const void* W_V,
                       int32_t d_model, const float* mu, const float* log_sigma2,
                       const float* log_pi, float eps, int causal, void* out,

@@ -167,10 +167,10 @@ def test_timing_collect_empty():
 @pytest.mark.parametrize("causal", [0, 1])
 @pytest.mark.parametrize("kw,fmts", [
     # bf16 token-owner kernels take split routing vectors: split bf16
-    # projections; causal with d_r = 64 and at most 64 components: the
-    # projection epilogue forms the responsibilities (only V_X is kept)
-    ({}, (B.GMA_PROJ_SPLIT_BF16, B.GMA_PROJ_FUSED_BF16)),
-    ({"K": 32, "N": 16384}, (B.GMA_PROJ_SPLIT_BF16, B.GMA_PROJ_FUSED_BF16)),
+    # projections; d_r = 64 and at most 64 components: the projection
+    # epilogue forms the responsibilities (only V_X is kept)
+    ({}, (B.GMA_PROJ_FUSED_BF16, B.GMA_PROJ_FUSED_BF16)),
+    ({"K": 32, "N": 16384}, (B.GMA_PROJ_FUSED_BF16, B.GMA_PROJ_FUSED_BF16)),
     ({"K": 128, "d_v": 128}, (B.GMA_PROJ_SPLIT_BF16, B.GMA_PROJ_SPLIT_BF16)),
     ({"d_r": 32, "K": 20}, (B.GMA_PROJ_SPLIT_BF16, B.GMA_PROJ_SPLIT_BF16)),
     # d_r = 128 exceeds the token-owner kernels: fp32 projections, fp32 path
@@ -211,7 +211,7 @@ def test_layer_projection_layout(kw, fmts, causal):
 
 def test_layer_projection_layout_errors():
     fmt, offs = B.gma_layer_projection_layout(_dims(), 256, 0)
-    assert fmt in (B.GMA_PROJ_F32, B.GMA_PROJ_SPLIT_BF16)
+    assert fmt in (B.GMA_PROJ_F32, B.GMA_PROJ_SPLIT_BF16, B.GMA_PROJ_FUSED_BF16)
     with pytest.raises(B.GmaError) as ei:
         B.gma_layer_projection_layout(_dims(), 100, 0)          # d_model not a multiple of 64
     assert ei.value.status == B.GMA_ERR_UNSUPPORTED

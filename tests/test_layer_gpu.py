@@ -133,8 +133,8 @@ def test_layer_full_size_sampled_rows():
 
 
 def test_layer_full_size_bidirectional_sampled_rows():
-    # the full layer shape, bidirectional: split projections into the bf16
-    # token-owner write and read-out
+    # the full layer shape, bidirectional: the fused form's read-out over every
+    # span's totals
     w = W["layer_causal_bf16"].with_(causal=False)
     _run(w, rows=inputs.sample_rows(w.N, 256, seed=4))
 
@@ -157,42 +157,48 @@ def test_layer_k_above_128(causal):
     _run(w)
 
 
-# The fused form: causal, d_r = 64, K <= 64 (32 or 64 components formed by
-# the projection epilogue).  Lengths not a multiple of 4 take the epilogue's
-# per-key stores; H = 3 leaves the last 256-feature tile partly empty; B = 3
-# with short sequences puts several sequences in one 256-token tile.
+# The fused form: d_r = 64, K <= 64 (32 or 64 components formed by the
+# projection epilogue), both variants.  Lengths not a multiple of 4 take the
+# epilogue's per-key stores; H = 3 leaves the last 256-feature tile partly
+# empty; B = 3 with short sequences puts several sequences in one 256-token
+# tile.
+@pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("N", [1, 3, 63, 65, 130, 301])
 @pytest.mark.parametrize("K", [32, 50])
-def test_layer_fused_ragged(N, K):
-    w = W["layer_causal_bf16"].with_(B=3, H=3, N=N, K=K, d_model=128)
+def test_layer_fused_ragged(N, K, causal):
+    w = W["layer_causal_bf16"].with_(B=3, H=3, N=N, K=K, d_model=128, causal=causal)
     fmt, _ = binding.gma_layer_projection_layout(
-        binding.make_dims(w.B, w.H, w.N, w.d_r, w.d_v, w.K, binding.GMA_BF16), w.d_model, 1)
+        binding.make_dims(w.B, w.H, w.N, w.d_r, w.d_v, w.K, binding.GMA_BF16), w.d_model,
+        int(causal))
     assert fmt == binding.GMA_PROJ_FUSED_BF16
     _run(w)
 
 
+@pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("d_v", [32, 128])
 @pytest.mark.parametrize("K", [7, 64])
-def test_layer_fused_value_dims(d_v, K):
-    w = W["layer_causal_bf16"].with_(B=2, H=5, N=777, K=K, d_v=d_v, d_model=192)
+def test_layer_fused_value_dims(d_v, K, causal):
+    w = W["layer_causal_bf16"].with_(B=2, H=5, N=777, K=K, d_v=d_v, d_model=192, causal=causal)
     _run(w)
 
 
-def test_layer_fused_several_chunks_per_span():
+@pytest.mark.parametrize("causal", [True, False])
+def test_layer_fused_several_chunks_per_span(causal):
     # 32 sequences of 2000 tokens: spans of several 64-token chunks, the last
-    # one ragged, through the span totals and the scan
-    w = W["layer_causal_bf16"].with_(B=2, H=16, N=2000, d_model=256)
+    # one ragged, through the span totals and the scan or read-out
+    w = W["layer_causal_bf16"].with_(B=2, H=16, N=2000, d_model=256, causal=causal)
     _run(w, rows=inputs.sample_rows(w.N, 200, seed=5))
 
 
-def test_layer_fused_assignments_optional():
+@pytest.mark.parametrize("causal", [True, False])
+def test_layer_fused_assignments_optional(causal):
     # without assignment outputs the epilogue takes its other branch: the
     # output is bitwise the same
     w = W["layer_causal_bf16"].with_(B=2, H=4, N=999, d_model=128)
     gen = inputs.generate(w, 0)
     dev = upload(gen)
     args = (dev["X"], dev["W_Q"], dev["W_K"], dev["W_V"], w.H, dev["mu"], dev["log_sigma2"],
-            dev["log_pi"], w.eps, True)
+            dev["log_pi"], w.eps, causal)
     o1, _, _ = api.layer_forward(*args, assign=True)
     o2 = api.layer_forward(*args, assign=False)
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
