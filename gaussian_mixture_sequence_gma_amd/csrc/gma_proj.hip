@@ -67,8 +67,9 @@ __device__ __forceinline__ int xswz(int r) { return (r ^ (r >> 3)) & 7; }
 // Large problems: 256 x 256 workgroup tiles of eight 64 x 128 wave tiles, two
 // waves per SIMD (128 accumulators each, so one wave's MFMAs run while the
 // other waits on LDS); per 64-deep step a wave reads 12 KB of LDS operands for
-// 64 MFMAs.  Small problems: 64 x 64 tiles of four 32 x 32 wave tiles, for
-// more workgroups.
+// 64 MFMAs.  (32-deep steps through four stage buffers, three steps' copies in
+// flight, measured slower: twice the barriers for the same bytes.)  Small
+// problems: 64 x 64 tiles of four 32 x 32 wave tiles, for more workgroups.
 template <int WF, int WT, int WAF, int WAT>
 struct ProjTile {
   static constexpr int NW = WAF * WAT;                // waves per workgroup

@@ -202,3 +202,13 @@ def test_layer_fused_assignments_optional(causal):
     o1, _, _ = api.layer_forward(*args, assign=True)
     o2 = api.layer_forward(*args, assign=False)
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_layer_split_large_tiles(causal):
+    # K = 128 (not the fused form) on a problem large enough for the
+    # projection's 256 x 256 workgroup tiles: split projections, d_model of
+    # 1024 in 32 steps through the four stage buffers
+    w = W["layer_causal_bf16"].with_(B=1, H=8, N=4500, K=128, d_v=128, d_model=1024,
+                                     causal=causal)
+    _run(w, rows=inputs.sample_rows(w.N, 200, seed=6))
