@@ -431,6 +431,7 @@ struct LayerPlan {
   size_t gma_bytes = 0;
   size_t off[5] = {0, 0, 0, 0, 0};   // from the start of the workspace
   size_t off_eq = 0;                 // fused: the queries' exponentials
+  size_t off_vtab = 0;               // fused, bidirectional: the state's operand table
   size_t total = 0;
 };
 
@@ -459,6 +460,8 @@ static int layer_plan(const gma_dims* d, int32_t d_model, int causal, LayerPlan&
     off += round256(2 * nv);
     L.off_eq = off;
     off += round256((size_t)p.BH * p.N * L.kc * 2);
+    L.off_vtab = off;
+    off += round256((size_t)p.BH * (p.DV / 16 + 1) * (p.Kp / 32) * 1024);
   } else if (L.split) {
     for (int m = 0; m < 4; ++m) {
       L.off[m] = off;
@@ -557,6 +560,7 @@ int gma_layer_forward(const void* X, const void* W_Q, const void* W_K, const voi
     t.v = P[2];
     t.eq = ws + L.off_eq;
     t.kc = L.kc;
+    t.vtab = ws + L.off_vtab;
     return finish_launch(launch_layer_fused(p, t, causal != 0, s),
                          causal ? "causal launch" : "bidirectional launch");
   }

@@ -1592,6 +1592,15 @@ __global__ void __launch_bounds__(256) gma_usage_reduce_kernel(
   }
 }
 
+hipError_t launch_reduce_table(const float* partial, const float* partial_z, int PS, int64_t BH,
+                               int Kp, int DV, float* vt, float* z, bf16* vtab, hipStream_t s) {
+  if (DV < 32 || Kp % 32) return hipErrorInvalidValue;
+  const int nred = Kp * DV / 8 + Kp;
+  hipLaunchKernelGGL(gma_reduce_kernel, dim3((nred + 255) / 256, (unsigned)BH), dim3(256), 0, s,
+                     partial, partial_z, PS, Kp, DV, vt, z, vtab, nullptr, nullptr, Kp);
+  return hipGetLastError();
+}
+
 hipError_t launch_prologue(const Plan& p, const Tensors& t, hipStream_t s) {
   if (g_launch_hook) g_launch_hook("gma_prologue", s, 1);
   const int64_t rows = p.H * (int64_t)p.Kp;          // one wave per (head, component)

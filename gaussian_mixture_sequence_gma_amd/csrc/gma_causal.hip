@@ -56,6 +56,7 @@ struct CausalArgs {
   // kc (32 or 64) components formed; the others are zero
   const bf16* eq;
   int kc;
+  const bf16* vtab;       // bidirectional read-out: the summed state as an operand table
 };
 
 // out[s] = sum_{s' < s} in[s'] over n terms at stride st, summed in order.
@@ -534,7 +535,8 @@ struct Causal2 {
 // Gamma^K^T (a.kc rows) given; no routing scores are formed.  BI (with QG):
 // the bidirectional read-out, O_i = gamma^Q_i V~ / (gamma^Q_i Z + eps) with
 // the memories of all keys ("Normalized broadcasting", Eq. 7): the state is
-// the sum of every span's totals and no chunk is scanned.
+// the operand table of every span's totals summed (a.vtab) and no chunk is
+// scanned, so a workgroup's span is any run of chunks.
 template <class C, bool XS, int HM = 0, class CF = C, bool QG = false, bool BI = false>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 gma_causal2_kernel(CausalArgs a) {
@@ -578,7 +580,7 @@ gma_causal2_kernel(CausalArgs a) {
     }
     // the (Z_hi, Z_lo, 1) block: the ones row and the zero rows are constant
     // (rows 0 and 1 belong to write_st, which runs concurrently)
-    for (int idx = threadIdx.x; idx < R::KS * 64; idx += kThreads) {
+    for (int idx = threadIdx.x; idx < (BI ? 0 : R::KS * 64); idx += kThreads) {
       const int r = idx & 15;
       if (r < 2) continue;
       bf16x8 v;
@@ -597,15 +599,14 @@ gma_causal2_kernel(CausalArgs a) {
 #pragma unroll
     for (int dt = 0; dt < R::DVT; ++dt) sacc[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  {
+  if constexpr (!BI) {
     constexpr int V1 = R::CTW * (R::DVT + 1) * 4;          // values per lane per span
     constexpr int SB = V1 >= 48 ? 1 : 96 / V1;
-    const int nsum = BI ? a.nspan : span;      // read-out: every span's totals
-    for (int s0 = 0; s0 < nsum; s0 += SB) {
+    for (int s0 = 0; s0 < span; s0 += SB) {
       f32x4 ts[SB][R::CTW][R::DVT], tz[SB][R::CTW];
 #pragma unroll
       for (int b = 0; b < SB; ++b) {
-        const bool in = s0 + b < nsum;
+        const bool in = s0 + b < span;
         const size_t sl = (size_t)bh * a.nspan + (in ? s0 + b : 0);
 #pragma unroll
         for (int j = 0; j < R::CTW; ++j) {
@@ -661,7 +662,13 @@ gma_causal2_kernel(CausalArgs a) {
       }
     }
   };
-  write_st();
+  if constexpr (BI) {
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(a.vtab) + (size_t)bh * R::STCH * 64;
+    for (int idx = threadIdx.x; idx < R::STCH * 64; idx += kThreads)
+      reinterpret_cast<bf16x8*>(ST)[idx] = src[idx];
+  } else {
+    write_st();
+  }
 
   const bf16* qs = reinterpret_cast<const bf16*>(a.q) + (size_t)bh * a.N * C::DR;
   const bf16* vs = reinterpret_cast<const bf16*>(a.v) + (size_t)bh * a.N * C::DV;
@@ -784,66 +791,66 @@ gma_causal2_kernel(CausalArgs a) {
 #pragma unroll
       for (int p = 0; p < R::KS; ++p) Eq[p] = xq[p];
     } else {
-    // features of this wave's 16 queries
-    bf16x8 fq[R::NKS][NFX<XS>];
+      // features of this wave's 16 queries
+      bf16x8 fq[R::NKS][NFX<XS>];
 #pragma unroll
-    for (int s = 0; s < R::NKS; ++s) make_features<XS>(xq[s], xql[s], fq[s]);
-    // scores D[component][query]
-    f32x4 SQ[R::CT];
+      for (int s = 0; s < R::NKS; ++s) make_features<XS>(xq[s], xql[s], fq[s]);
+      // scores D[component][query]
+      f32x4 SQ[R::CT];
 #pragma unroll
-    for (int ct = 0; ct < R::CT; ++ct) SQ[ct] = *reinterpret_cast<const f32x4*>(&cperm[ct * 16 + 4 * g]);
-    {
-      // half-steps h = (component tile, routing chunk): the four operands of
-      // half-step h + 1 are read from LDS while the MFMAs of h run
-      constexpr int NH = R::CT * R::NKS;
-      auto load_w = [&](int hs, bf16x8 (&wv)[4]) {
-        const int ct = hs / R::NKS, s = hs % R::NKS;
+      for (int ct = 0; ct < R::CT; ++ct) SQ[ct] = *reinterpret_cast<const f32x4*>(&cperm[ct * 16 + 4 * g]);
+      {
+        // half-steps h = (component tile, routing chunk): the four operands of
+        // half-step h + 1 are read from LDS while the MFMAs of h run
+        constexpr int NH = R::CT * R::NKS;
+        auto load_w = [&](int hs, bf16x8 (&wv)[4]) {
+          const int ct = hs / R::NKS, s = hs % R::NKS;
 #pragma unroll
-        for (int ar = 0; ar < 4; ++ar) wv[ar] = coef[((ct * R::NKS + s) * 4 + ar) * 64 + lane];
-      };
-      bf16x8 wbuf[2][4];
-      load_w(0, wbuf[0]);
+          for (int ar = 0; ar < 4; ++ar) wv[ar] = coef[((ct * R::NKS + s) * 4 + ar) * 64 + lane];
+        };
+        bf16x8 wbuf[2][4];
+        load_w(0, wbuf[0]);
 #pragma unroll
-      for (int hs = 0; hs < NH; ++hs) {
-        if (hs + 1 < NH) load_w(hs + 1, wbuf[(hs + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-        const int ct = hs / R::NKS, s = hs % R::NKS;
+        for (int hs = 0; hs < NH; ++hs) {
+          if (hs + 1 < NH) load_w(hs + 1, wbuf[(hs + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+          const int ct = hs / R::NKS, s = hs % R::NKS;
 #pragma unroll
-        for (int q = 0; q < NQX<XS>; ++q) SQ[ct] = mma(wbuf[hs & 1][kWI[q]], fq[s][kFI[q]], SQ[ct]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-
-    {
-      float v = SQ[0][0];
-#pragma unroll
-      for (int ct = 0; ct < R::CT; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v = fmaxf(v, SQ[ct][i]);
-      const float m = groups_max(v);
-      mq = m;
-#pragma unroll
-      for (int p = 0; p < R::KS; ++p)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          Eq[p][i] = to_bf16(exp2_fast(SQ[2 * p][i] - m));
-          Eq[p][4 + i] = to_bf16(exp2_fast(SQ[2 * p + 1][i] - m));
+          for (int q = 0; q < NQX<XS>; ++q) SQ[ct] = mma(wbuf[hs & 1][kWI[q]], fq[s][kFI[q]], SQ[ct]);
+          __builtin_amdgcn_sched_barrier(0);
         }
-      if (want_aq) {
-        // the lowest component index whose score equals the maximum m (one of
-        // the scores: the maxima select, they do not round)
-        int bi = 0x7fffffff;
+      }
+
+      {
+        float v = SQ[0][0];
 #pragma unroll
         for (int ct = 0; ct < R::CT; ++ct)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            bi = min(bi, SQ[ct][i] == m ? koff + pair_row(ct, 4 * g + i) : 0x7fffffff);
-        bi = groups_min_i(bi);
-        qbv = m;
-        qbi = bi;
-        if (HM == 0 && g == 0 && qi < nvalid) a.assign_q[qtok] = bi;
+          for (int i = 0; i < 4; ++i) v = fmaxf(v, SQ[ct][i]);
+        const float m = groups_max(v);
+        mq = m;
+#pragma unroll
+        for (int p = 0; p < R::KS; ++p)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            Eq[p][i] = to_bf16(exp2_fast(SQ[2 * p][i] - m));
+            Eq[p][4 + i] = to_bf16(exp2_fast(SQ[2 * p + 1][i] - m));
+          }
+        if (want_aq) {
+          // the lowest component index whose score equals the maximum m (one of
+          // the scores: the maxima select, they do not round)
+          int bi = 0x7fffffff;
+#pragma unroll
+          for (int ct = 0; ct < R::CT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              bi = min(bi, SQ[ct][i] == m ? koff + pair_row(ct, 4 * g + i) : 0x7fffffff);
+          bi = groups_min_i(bi);
+          qbv = m;
+          qbi = bi;
+          if (HM == 0 && g == 0 && qi < nvalid) a.assign_q[qtok] = bi;
+        }
       }
-    }
     }
     if constexpr (!BI) {
       wait_global_loads();               // V(k), Gamma^K^T(k) and this wave's loads
@@ -1149,8 +1156,21 @@ static hipError_t run_causal_fused(const Plan& p, const Tensors& t, bool causal,
       hipLaunchKernelGGL((gma_causal2_kernel<C, false, 0, C, true>), grid, dim3(kThreads), 0, s, ca);
       if (g_launch_hook) g_launch_hook("gma_causal", s, 0);
     } else {
+      // the spans' totals summed in span order into the read-out's operand
+      // table, then the read-out over runs of four chunks
+      if (!t.vtab) return hipErrorInvalidValue;
+      if (g_launch_hook) g_launch_hook("gma_reduce", s, 1);
+      e = launch_reduce_table(state, state_z, p.nspan, p.BH, C::Kp, C::DV,
+                              reinterpret_cast<float*>(t.ws + p.off_carry),
+                              reinterpret_cast<float*>(t.ws + p.off_carry_z),
+                              static_cast<bf16*>(t.vtab), s);
+      if (g_launch_hook) g_launch_hook("gma_reduce", s, 0);
+      if (e != hipSuccess) return e;
+      ca.vtab = static_cast<const bf16*>(t.vtab);
+      ca.span_tiles = p.tiles < 4 ? (int)p.tiles : 4;
+      const dim3 rgrid((unsigned)((p.tiles + ca.span_tiles - 1) / ca.span_tiles), (unsigned)p.BH);
       if (g_launch_hook) g_launch_hook("gma_read", s, 1);
-      hipLaunchKernelGGL((gma_causal2_kernel<C, false, 0, C, true, true>), grid, dim3(kThreads), 0, s, ca);
+      hipLaunchKernelGGL((gma_causal2_kernel<C, false, 0, C, true, true>), rgrid, dim3(kThreads), 0, s, ca);
       if (g_launch_hook) g_launch_hook("gma_read", s, 0);
     }
     return hipGetLastError();

@@ -72,6 +72,7 @@ struct Tensors {
   // ([BH][N][kc] bf16; the keys' Gamma^K^T sit at off_gt) and kc
   void* eq = nullptr;
   int kc = 0;
+  void* vtab = nullptr;   // bidirectional: the summed state as an operand table
 };
 
 // Launch helpers; each returns hipSuccess or the launch error.  `tag` names the
@@ -81,6 +82,12 @@ typedef void (*launch_hook_t)(const char* tag, hipStream_t s, int begin);
 extern thread_local launch_hook_t g_launch_hook;
 
 hipError_t launch_prologue(const Plan& p, const Tensors& t, hipStream_t s);
+// Sum PS partial states per sequence in slot order ([BH][PS][Kp][DV] and
+// [BH][PS][Kp] fp32) into vt, z and, as the read-out's bf16 MFMA operand table
+// ([BH][DV/16 + 1][Kp/32][64 lanes][8], the last block Z_hi, Z_lo, 1, zeros),
+// vtab.
+hipError_t launch_reduce_table(const float* partial, const float* partial_z, int PS, int64_t BH,
+                               int Kp, int DV, float* vt, float* z, __bf16* vtab, hipStream_t s);
 // Whether the bf16 kernels take split routing vectors (q_lo / k_lo) for this shape.
 bool bidir_split_ok(const Plan& p);
 bool causal_split_ok(const Plan& p);
