@@ -20,8 +20,8 @@
 //
 // Fused form (bf16 causal layer, d_r = 64, at most 64 components): a wave's
 // 64 features of Q_X or K_X are one whole head, so the epilogue forms the
-// routing scores of its 128 tokens from the fp32 accumulators ("Routing via
-// mixture posteriors", Eq. 3, on split-bf16 MFMA) and stores, instead of the
+// routing scores of its 128 tokens from the fp32 accumulators ("Gaussian
+// routing components", Eq. 3, on split-bf16 MFMA) and stores, instead of the
 // projections, what the scan consumes: per query the exponentials
 // exp2(s - max s) of its scores as bf16 [B,H,N,K_c], and per 64-key chunk the
 // keys' responsibilities transposed, bf16 [B,H,chunk][K_c][64], with K_c the

@@ -148,7 +148,7 @@ int gma_layer_workspace_bytes(const gma_dims* d, int32_t d_model, int causal, si
  * The projections are accumulated in fp32 (bf16 x bf16 products are exact in
  * fp32).  With d_r = 64 and K <= 64 (where the bf16 scan kernel takes the
  * shape) the projection's epilogue forms the routing responsibilities of
- * Section "Routing via mixture posteriors" (Eq. 3) from the fp32 accumulators
+ * "Gaussian routing components" (Eq. 3) from the fp32 accumulators
  * and Q_X, K_X never reach memory; V_X is rounded to bf16.  Otherwise, where
  * the bf16 GMA kernels support the shape, Q_X and K_X are kept as bf16 pairs
  * hi + lo (16 significant bits), V_X is rounded to bf16, and the bf16 GMA
