@@ -68,18 +68,21 @@ def test_forward_graph_replays_match_eager(causal, dtype, d_v, K):
             assert e <= TOL[dtype]
 
 
-def test_layer_graph_replays_match_eager():
+@pytest.mark.parametrize("causal", [True, False])
+def test_layer_graph_replays_match_eager(causal):
+    # the fused layer: projection with the responsibility epilogue, span
+    # totals, then the scan (causal) or the reduction and read-out
     w = inputs.WORKLOADS["layer_causal_bf16"].with_(name="graph_layer", B=1, N=1000)
     gen = inputs.generate(w, 4)
     dev = upload(gen)
 
     def run(out):
         return api.layer_forward(dev["X"], dev["W_Q"], dev["W_K"], dev["W_V"], w.H, dev["mu"],
-                                 dev["log_sigma2"], dev["log_pi"], w.eps, True, out=out,
+                                 dev["log_sigma2"], dev["log_pi"], w.eps, causal, out=out,
                                  workspace=ws)
 
     dims = B.make_dims(w.B, w.H, w.N, w.d_r, w.d_v, w.K, B.GMA_BF16)
-    ws = api.alloc_workspace(B.gma_layer_workspace_bytes(dims, w.d_model, 1), "cuda")
+    ws = api.alloc_workspace(B.gma_layer_workspace_bytes(dims, w.d_model, int(causal)), "cuda")
     eager = run(None)
     torch.cuda.synchronize()
     out = torch.empty_like(eager)
