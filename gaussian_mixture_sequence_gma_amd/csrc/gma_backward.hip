@@ -50,6 +50,11 @@ struct GemmArgs {
   int ksplit;
   int vec;           // bit 0: A rows 16-byte aligned; bit 1: B rows
   int accum;         // add to C instead of overwriting it (ksplit == 1 only)
+  // softmax Jacobian in the epilogue (wide kernel, one column tile, ksplit 1):
+  // C = G (C - rowsum(G C)) with G of unit u at G + u * sG, row stride ldg
+  const float* G;
+  int64_t sG;
+  int ldg;
 };
 
 constexpr int kGT = 64;                 // output tile
@@ -264,6 +269,19 @@ __global__ void __launch_bounds__(256) gma_bgemm_wide_kernel(GemmArgs g) {
   f32x4 acc[TN];
 #pragma unroll
   for (int j = 0; j < TN; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the softmax Jacobian's G entries of this lane, requested before the main
+  // loop so that they arrive while it runs
+  float gv[TN][4];
+  if (g.G) {
+    const float* Gu = g.G + (size_t)u * g.sG;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + 16 * wave + 4 * gq + e, n = 16 * j + r;
+        gv[j][e] = m < g.M && n < g.N ? Gu[(size_t)m * g.ldg + n] : 0.f;
+      }
+  }
 
   if (kb < ke) load(kb);
   for (int k0 = kb; k0 < ke; k0 += kGK) {
@@ -317,6 +335,34 @@ __global__ void __launch_bounds__(256) gma_bgemm_wide_kernel(GemmArgs g) {
   } else {
     C = g.C + (size_t)u * g.sC;
     ldc = g.ldc;
+  }
+  if (g.G) {
+    // dS = G (dG - sum_l G_l dG_l) ("Gradient structure", Eq. 18): a row's
+    // columns 16 j + r lie in this lane's TN tiles and the 16 lanes of its
+    // DPP row, so the row sum is an in-lane sum and a 16-lane butterfly
+    float dv[TN][4];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + 16 * wave + 4 * gq + e, n = 16 * j + r;
+        const bool ok = m < g.M && n < g.N;
+        const float prev = ok && g.accum ? C[(size_t)m * ldc + n] : 0.f;
+        dv[j][e] = ok ? prev + acc[j][e] : 0.f;
+      }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) sum += gv[j][e] * dv[j][e];
+      sum = row16_sum(sum);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int m = m0 + 16 * wave + 4 * gq + e, n = 16 * j + r;
+        if (m < g.M && n < g.N) C[(size_t)m * ldc + n] = gv[j][e] * (dv[j][e] - sum);
+      }
+    }
+    return;
   }
 #pragma unroll
   for (int j = 0; j < TN; ++j)
@@ -737,28 +783,37 @@ BwdLayout bwd_layout(const Plan& pp, bool causal, int64_t N) {
   return L;
 }
 
+// wide: 0 (64 x 64 tiles), 4, 8 or 9 (one column tile of 16 wide columns)
 template <bool TA, bool TB>
-void launch_gemm_kernel(bool wide9, bool wide, dim3 grid, const GemmArgs& g, hipStream_t s) {
+void launch_gemm_kernel(int wide, dim3 grid, const GemmArgs& g, hipStream_t s) {
   if (!wide) hipLaunchKernelGGL((gma_bgemm_kernel<TA, TB>), grid, dim3(256), 0, s, g);
-  else if (!wide9) hipLaunchKernelGGL((gma_bgemm_wide_kernel<TA, TB, 8>), grid, dim3(256), 0, s, g);
+  else if (wide == 4) hipLaunchKernelGGL((gma_bgemm_wide_kernel<TA, TB, 4>), grid, dim3(256), 0, s, g);
+  else if (wide == 8) hipLaunchKernelGGL((gma_bgemm_wide_kernel<TA, TB, 8>), grid, dim3(256), 0, s, g);
   else hipLaunchKernelGGL((gma_bgemm_wide_kernel<TA, TB, 9>), grid, dim3(256), 0, s, g);
 }
 
+// Whether gemm() can apply the softmax Jacobian of a result of width N in its
+// epilogue (one column tile).
+bool gemm_jacobian_ok(int N) { return N <= 144; }
+
 hipError_t gemm(bool ta, bool tb, const float* A, int lda, int64_t sA, const float* B, int ldb,
                 int64_t sB, int bmod, float* C, int ldc, int64_t sC, int M, int N, int K,
-                int64_t U, int ksplit, float* part, hipStream_t s, bool accum = false) {
+                int64_t U, int ksplit, float* part, hipStream_t s, bool accum = false,
+                const float* G = nullptr, int64_t sG = 0, int ldg = 0) {
+  if (G && (ksplit > 1 || !gemm_jacobian_ok(N))) return hipErrorInvalidValue;
   const int vec = ((lda % 4 == 0 && sA % 4 == 0 && ((uintptr_t)A & 15) == 0) ? 1 : 0) |
                   ((ldb % 4 == 0 && sB % 4 == 0 && ((uintptr_t)B & 15) == 0) ? 2 : 0);
   GemmArgs g{A, B, ksplit > 1 ? part : C, M, N, K, lda, ldb, ldc, sA, sB, sC, bmod, ksplit, vec,
-             accum ? 1 : 0};
-  // 64 < N <= 144: one column tile of 128 (8 MFMA tiles per wave) or 144 (9)
-  const bool wide = N > kGT && N <= 144, wide9 = N > 128;
+             accum ? 1 : 0, G, sG, ldg};
+  // 64 < N <= 144: one column tile of 128 (8 MFMA tiles per wave) or 144 (9);
+  // with the Jacobian epilogue also N <= 64 (4)
+  const int wide = N > 128 && N <= 144 ? 9 : (N > kGT && N <= 128 ? 8 : (G ? 4 : 0));
   const dim3 grid(wide ? 1u : (unsigned)((N + kGT - 1) / kGT), (unsigned)((M + kGT - 1) / kGT),
                   (unsigned)(U * ksplit));
-  if (!ta && !tb) launch_gemm_kernel<false, false>(wide9, wide, grid, g, s);
-  else if (!ta && tb) launch_gemm_kernel<false, true>(wide9, wide, grid, g, s);
-  else if (ta && !tb) launch_gemm_kernel<true, false>(wide9, wide, grid, g, s);
-  else launch_gemm_kernel<true, true>(wide9, wide, grid, g, s);
+  if (!ta && !tb) launch_gemm_kernel<false, false>(wide, grid, g, s);
+  else if (!ta && tb) launch_gemm_kernel<false, true>(wide, grid, g, s);
+  else if (ta && !tb) launch_gemm_kernel<true, false>(wide, grid, g, s);
+  else launch_gemm_kernel<true, true>(wide, grid, g, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ksplit <= 1) return e;
   hipLaunchKernelGGL(gma_split_sum_kernel, dim3((unsigned)((M * N + 255) / 256), (unsigned)U),
@@ -862,6 +917,9 @@ hipError_t run_backward(const Plan& pp, const Tensors& t0, const BwdTensors& gt,
 
   const int64_t Z = causal ? U * L.nc : U;      // product batch: units, or chunks
   const int C = kChunk;
+  // the softmax Jacobian in the epilogue of the products giving dGq and dGk
+  // where one column tile holds a row of K
+  const bool jac = gemm_jacobian_ok(K);
   if (!causal) {
     if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 1);
     // [V~ | Z] = Gk^T [V | 1]
@@ -909,18 +967,19 @@ hipError_t run_backward(const Plan& pp, const Tensors& t0, const BwdTensors& gt,
   if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 0);
   if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 1);
   if (!causal) {
-    // dGq = [a | b] [V~ | Z]^T
+    // dGq = [a | b] [V~ | Z]^T, then dSq = Gq (dGq - rowsum(Gq dGq)) in the
+    // product's epilogue where one column tile holds a row
     GMA_CHECK(gemm(false, true, nd, l1, Np * l1, vtz, l1, (int64_t)K * l1, 0, dGq, K, Np * K,
-                   (int)Np, K, w1, U, 1, part, s));
+                   (int)Np, K, w1, U, 1, part, s, false, jac ? Gq : nullptr, Np * K, K));
     // [dV~ | dZ] = Gq^T [a | b]
     GMA_CHECK(gemm(true, false, Gq, K, Np * K, nd, l1, Np * l1, 0, dvtz, l1, (int64_t)K * l1, K,
                    w1, (int)Np, U, ks, part, s));
     // dV = Gk dV~
     GMA_CHECK(gemm(false, false, Gk, K, Np * K, dvtz, l1, (int64_t)K * l1, 0, dvf, dv, Np * dv,
                    (int)Np, dv, K, U, 1, part, s));
-    // dGk = [V | 1] [dV~ | dZ]^T
+    // dGk = [V | 1] [dV~ | dZ]^T (and dSk)
     GMA_CHECK(gemm(false, true, v1, l1, Np * l1, dvtz, l1, (int64_t)K * l1, 0, dGk, K, Np * K,
-                   (int)Np, K, w1, U, 1, part, s));
+                   (int)Np, K, w1, U, 1, part, s, false, jac ? Gk : nullptr, Np * K, K));
   } else {
     // dGq_c = [a | b]_c [V~ | Z]_prefix^T + mask([a | b]_c [V | 1]_c^T) Gk_c
     GMA_CHECK(gemm(false, true, nd, l1, (int64_t)C * l1, vtz, l1, (int64_t)K * l1, 0, dGq, K,
@@ -931,7 +990,8 @@ hipError_t run_backward(const Plan& pp, const Tensors& t0, const BwdTensors& gt,
                        Z * C * C, 0);
     GMA_CHECK(hipGetLastError());
     GMA_CHECK(gemm(false, false, qc, C, (int64_t)C * C, Gk, K, (int64_t)C * K, 0, dGq, K,
-                   (int64_t)C * K, C, K, C, Z, 1, part, s, true));
+                   (int64_t)C * K, C, K, C, Z, 1, part, s, true, jac ? Gq : nullptr,
+                   (int64_t)C * K, K));
     // per chunk: Gq_c^T [a | b]_c, then the exclusive suffix over later chunks
     GMA_CHECK(gemm(true, false, Gq, K, (int64_t)C * K, nd, l1, (int64_t)C * l1, 0, dvtz, l1,
                    (int64_t)K * l1, K, w1, C, Z, 1, part, s));
@@ -947,7 +1007,8 @@ hipError_t run_backward(const Plan& pp, const Tensors& t0, const BwdTensors& gt,
                        Z * C * C, 1);
     GMA_CHECK(hipGetLastError());
     GMA_CHECK(gemm(false, false, qc, C, (int64_t)C * C, Gq, K, (int64_t)C * K, 0, dGk, K,
-                   (int64_t)C * K, C, K, C, Z, 1, part, s, true));
+                   (int64_t)C * K, C, K, C, Z, 1, part, s, true, jac ? Gk : nullptr,
+                   (int64_t)C * K, K));
     // dV_c = Gk_c dV~_suffix + mask(Gq_c Gk_c^T)^T a_c
     GMA_CHECK(gemm(false, false, Gk, K, (int64_t)C * K, dvtz, l1, (int64_t)K * l1, 0, dvf, dv,
                    (int64_t)C * dv, C, dv, K, Z, 1, part, s));
@@ -956,8 +1017,10 @@ hipError_t run_backward(const Plan& pp, const Tensors& t0, const BwdTensors& gt,
   }
   if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 0);
   if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 1);
-  launch_bwd_softmax(Gq, dGq, K, rows, s);
-  launch_bwd_softmax(Gk, dGk, K, rows, s);
+  if (!jac) {
+    launch_bwd_softmax(Gq, dGq, K, rows, s);
+    launch_bwd_softmax(Gk, dGk, K, rows, s);
+  }
   hipLaunchKernelGGL(gma_bwd_store_kernel<T>, dim3(sblocks(rows * dv / 4, 256)), dim3(256), 0, s,
                      dvf, dv, rows, Np, N0, gt.dV);
   GMA_CHECK(hipGetLastError());
