@@ -55,6 +55,16 @@ struct GemmArgs {
   const float* G;
   int64_t sG;
   int ldg;
+  // dX in the epilogue (wide kernel, ksplit 1, N = 2 d): the product is
+  // [P1 | P2] and dX = -x P1 + P2 is stored instead, x of unit u at
+  // X + u * sX (row stride ldx), dX row m of unit u at dx row u * dxN + m for
+  // m < dxN, as bf16 (dx_bf) or fp32
+  void* dx;
+  int dx_bf;
+  int64_t dxN;
+  const float* X;
+  int64_t sX;
+  int ldx;
 };
 
 constexpr int kGT = 64;                 // output tile
@@ -272,7 +282,17 @@ __global__ void __launch_bounds__(256) gma_bgemm_wide_kernel(GemmArgs g) {
   // the softmax Jacobian's G entries of this lane, requested before the main
   // loop so that they arrive while it runs
   float gv[TN][4];
-  if (g.G) {
+  if (g.dx) {
+    // x of this lane's P1 columns (tiles j < TN / 2)
+    const float* Xu = g.X + (size_t)u * g.sX;
+#pragma unroll
+    for (int j = 0; j < TN / 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + 16 * wave + 4 * gq + e, n = 16 * j + r;
+        gv[j][e] = m < g.M && n < g.N / 2 ? Xu[(size_t)m * g.ldx + n] : 0.f;
+      }
+  } else if (g.G) {
     const float* Gu = g.G + (size_t)u * g.sG;
 #pragma unroll
     for (int j = 0; j < TN; ++j)
@@ -335,6 +355,24 @@ __global__ void __launch_bounds__(256) gma_bgemm_wide_kernel(GemmArgs g) {
   } else {
     C = g.C + (size_t)u * g.sC;
     ldc = g.ldc;
+  }
+  if (g.dx) {
+    // dX = -x P1 + P2 ("Gradient structure": the score's routing-vector
+    // gradient): P1 in tiles j, P2 in tiles j + TN / 2 of the same lane
+    const int d = g.N / 2;
+#pragma unroll
+    for (int j = 0; j < TN / 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + 16 * wave + 4 * gq + e, n = 16 * j + r;
+        if (m < g.M && m < g.dxN && n < d) {
+          const float v = acc[j + TN / 2][e] - gv[j][e] * acc[j][e];
+          const size_t i = ((size_t)u * g.dxN + m) * d + n;
+          if (g.dx_bf) static_cast<bf16*>(g.dx)[i] = to_bf16(v);
+          else static_cast<float*>(g.dx)[i] = v;
+        }
+      }
+    return;
   }
   if (g.G) {
     // dS = G (dG - sum_l G_l dG_l) ("Gradient structure", Eq. 18): a row's
@@ -796,18 +834,41 @@ void launch_gemm_kernel(int wide, dim3 grid, const GemmArgs& g, hipStream_t s) {
 // epilogue (one column tile).
 bool gemm_jacobian_ok(int N) { return N <= 144; }
 
+// The dX epilogue: P = [P1 | P2] of width N = 2 d in one column tile whose
+// halves are whole MFMA tiles (d of 32 or 64).
+bool gemm_dx_ok(int N) { return N == 64 || N == 128; }
+
+struct DxOut {
+  void* dx = nullptr;
+  int bf = 0;
+  int64_t N = 0;
+  const float* X = nullptr;
+  int64_t sX = 0;
+  int ldx = 0;
+};
+
 hipError_t gemm(bool ta, bool tb, const float* A, int lda, int64_t sA, const float* B, int ldb,
                 int64_t sB, int bmod, float* C, int ldc, int64_t sC, int M, int N, int K,
                 int64_t U, int ksplit, float* part, hipStream_t s, bool accum = false,
-                const float* G = nullptr, int64_t sG = 0, int ldg = 0) {
+                const float* G = nullptr, int64_t sG = 0, int ldg = 0,
+                const DxOut* dxo = nullptr) {
   if (G && (ksplit > 1 || !gemm_jacobian_ok(N))) return hipErrorInvalidValue;
+  if (dxo && (ksplit > 1 || accum || G || !gemm_dx_ok(N))) return hipErrorInvalidValue;
   const int vec = ((lda % 4 == 0 && sA % 4 == 0 && ((uintptr_t)A & 15) == 0) ? 1 : 0) |
                   ((ldb % 4 == 0 && sB % 4 == 0 && ((uintptr_t)B & 15) == 0) ? 2 : 0);
   GemmArgs g{A, B, ksplit > 1 ? part : C, M, N, K, lda, ldb, ldc, sA, sB, sC, bmod, ksplit, vec,
              accum ? 1 : 0, G, sG, ldg};
+  if (dxo) {
+    g.dx = dxo->dx;
+    g.dx_bf = dxo->bf;
+    g.dxN = dxo->N;
+    g.X = dxo->X;
+    g.sX = dxo->sX;
+    g.ldx = dxo->ldx;
+  }
   // 64 < N <= 144: one column tile of 128 (8 MFMA tiles per wave) or 144 (9);
-  // with the Jacobian epilogue also N <= 64 (4)
-  const int wide = N > 128 && N <= 144 ? 9 : (N > kGT && N <= 128 ? 8 : (G ? 4 : 0));
+  // with an epilogue that needs whole rows also N <= 64 (4)
+  const int wide = N > 128 && N <= 144 ? 9 : (N > kGT && N <= 128 ? 8 : (G || dxo ? 4 : 0));
   const dim3 grid(wide ? 1u : (unsigned)((N + kGT - 1) / kGT), (unsigned)((M + kGT - 1) / kGT),
                   (unsigned)(U * ksplit));
   if (!ta && !tb) launch_gemm_kernel<false, false>(wide, grid, g, s);
@@ -1030,18 +1091,30 @@ hipError_t run_backward(const Plan& pp, const Tensors& t0, const BwdTensors& gt,
     float* dS = side ? dGk : dGq;
     float* x3 = side ? x3k : x3q;
     if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 1);
-    // [P1 | P2] = dS [w | mu w] (the head's table)
+    // [P1 | P2] = dS [w | mu w] (the head's table); where its halves are
+    // whole MFMA tiles the epilogue forms dX = -x P1 + P2 itself
+    const bool fdx = gemm_dx_ok(2 * dr);
+    DxOut dxo;
+    dxo.dx = side ? gt.dK : gt.dQ;
+    dxo.bf = sizeof(T) == 2;
+    dxo.N = N0;
+    dxo.X = x3;
+    dxo.sX = Np * l3;
+    dxo.ldx = l3;
     GMA_CHECK(gemm(false, false, dS, K, Np * K, WW, 2 * dr, (int64_t)K * 2 * dr, (int)pp.H, P,
-                   2 * dr, Np * 2 * dr, (int)Np, 2 * dr, K, U, 1, part, s));
+                   2 * dr, Np * 2 * dr, (int)Np, 2 * dr, K, U, 1, part, s, false, nullptr, 0, 0,
+                   fdx ? &dxo : nullptr));
     // [R1 | R2 | r0] = dS^T [x | x^2 | 1]
     GMA_CHECK(gemm(true, false, dS, K, Np * K, x3, l3, Np * l3, 0, side ? Rk : Rq, l3,
                    (int64_t)K * l3, K, w3, (int)Np, U, ks, part, s));
     if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 0);
-    if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 1);
-    hipLaunchKernelGGL(gma_bwd_dx_kernel<T>, dim3(sblocks(rows * dr / 4, 256)), dim3(256), 0, s,
-                       x3, l3, P, dr, rows, Np, N0, side ? gt.dK : gt.dQ);
-    GMA_CHECK(hipGetLastError());
-    if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 0);
+    if (!fdx) {
+      if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 1);
+      hipLaunchKernelGGL(gma_bwd_dx_kernel<T>, dim3(sblocks(rows * dr / 4, 256)), dim3(256), 0, s,
+                         x3, l3, P, dr, rows, Np, N0, side ? gt.dK : gt.dQ);
+      GMA_CHECK(hipGetLastError());
+      if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 0);
+    }
   }
   if (g_launch_hook) g_launch_hook("gma_bwd_params", s, 1);
   hipLaunchKernelGGL(gma_bwd_param_grad_kernel, dim3(blocks((int64_t)K * dr, 256), (unsigned)pp.H),
