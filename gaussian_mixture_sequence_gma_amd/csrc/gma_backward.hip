@@ -65,6 +65,12 @@ struct GemmArgs {
   const float* X;
   int64_t sX;
   int ldx;
+  // [a | b] in the epilogue (wide kernel, ksplit 1, N = d_v + 1): the product
+  // is [n | d - eps] and a = dO / d, b = -(dO . n) / d^2 are stored instead,
+  // dO row u * M + m (d_v wide, bf16 when dO_bf, else fp32)
+  const void* dO;
+  int dO_bf;
+  float eps;
 };
 
 constexpr int kGT = 64;                 // output tile
@@ -282,7 +288,21 @@ __global__ void __launch_bounds__(256) gma_bgemm_wide_kernel(GemmArgs g) {
   // the softmax Jacobian's G entries of this lane, requested before the main
   // loop so that they arrive while it runs
   float gv[TN][4];
-  if (g.dx) {
+  if (g.dO) {
+    // dO of this lane's columns below d_v
+    const int dvv = g.N - 1;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + 16 * wave + 4 * gq + e, n = 16 * j + r;
+        const size_t i = ((size_t)u * g.M + m) * dvv + n;
+        const bool ok = m < g.M && n < dvv;
+        gv[j][e] = !ok ? 0.f
+                       : (g.dO_bf ? (float)static_cast<const bf16*>(g.dO)[i]
+                                  : static_cast<const float*>(g.dO)[i]);
+      }
+  } else if (g.dx) {
     // x of this lane's P1 columns (tiles j < TN / 2)
     const float* Xu = g.X + (size_t)u * g.sX;
 #pragma unroll
@@ -355,6 +375,41 @@ __global__ void __launch_bounds__(256) gma_bgemm_wide_kernel(GemmArgs g) {
   } else {
     C = g.C + (size_t)u * g.sC;
     ldc = g.ldc;
+  }
+  if (g.dO) {
+    // [a | b] = [dO / d | -(dO . o) / d], o = n / d (the output's gradient
+    // through Eq. 7): d is column d_v of the row (lane r = d_v mod 16 of tile
+    // d_v / 16), dO . n a row sum, both over the 16-lane DPP row
+    const int dvv = g.N - 1;
+    float nv[TN][4];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + 16 * wave + 4 * gq + e, n = 16 * j + r;
+        const bool ok = m < g.M && n < g.N;
+        const float prev = ok && g.accum ? C[(size_t)m * ldc + n] : 0.f;
+        nv[j][e] = ok ? prev + acc[j][e] : 0.f;
+      }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float dp = 0.f, dt = 0.f;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = 16 * j + r;
+        dp += n == dvv ? nv[j][e] : 0.f;
+        dt += n < dvv ? gv[j][e] * nv[j][e] : 0.f;
+      }
+      const float den = row16_sum(dp) + g.eps;
+      const float dot = row16_sum(dt);
+      const float inv = 1.f / den;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int m = m0 + 16 * wave + 4 * gq + e, n = 16 * j + r;
+        if (m < g.M && n <= dvv) C[(size_t)m * ldc + n] = n < dvv ? gv[j][e] * inv : -dot * inv * inv;
+      }
+    }
+    return;
   }
   if (g.dx) {
     // dX = -x P1 + P2 ("Gradient structure": the score's routing-vector
@@ -484,65 +539,6 @@ __global__ void __launch_bounds__(256) gma_bwd_params_kernel(const float* __rest
   const float w = expf(-ls2[i]);
   ww[row * 2 * d + c] = w;
   ww[row * 2 * d + d + c] = mu[i] * w;
-}
-
-// One wave per token: from [n | d - eps] and dO, [a | b] in place.
-template <class T>
-__global__ void __launch_bounds__(256) gma_bwd_ab_kernel(float* __restrict__ nd,
-                                                         const void* __restrict__ dO, int dv,
-                                                         int ld, float eps, int64_t rows) {
-  const int lane = threadIdx.x & 63;
-  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows;
-       row += (int64_t)gridDim.x * 4) {
-  float* r = nd + (size_t)row * ld;
-  const float den = r[dv] + eps;
-  float dot = 0.f;
-  for (int c = lane; c < dv; c += 64) dot += ldx<T>(dO, (size_t)row * dv + c) * r[c];
-  dot = groups_sum(row16_sum(dot));
-  const float inv = 1.f / den;
-  for (int c = lane; c < dv; c += 64) r[c] = ldx<T>(dO, (size_t)row * dv + c) * inv;
-  if (lane == 0) r[dv] = -dot * inv * inv;     // o = n / d: (dO . n) / d^2
-  }
-}
-
-// The same with one 16-lane row per token (four tokens per wave, no loop) for
-// d_v <= 64 M: lane j holds elements 4 j + 64 m as 16-byte vectors.  Every
-// lane reads d - eps before lane 0 overwrites it (the row's lanes run in
-// lockstep and the store follows the read).
-template <class T, int M>
-__global__ void __launch_bounds__(256) gma_bwd_ab16_kernel(float* __restrict__ nd,
-                                                           const void* __restrict__ dO, int dv,
-                                                           int ld, float eps, int64_t rows) {
-  const int j = threadIdx.x & 15;
-  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  if (row >= rows) return;     // whole 16-lane rows leave together
-  float* r = nd + (size_t)row * ld;
-  const T* o = static_cast<const T*>(dO) + (size_t)row * dv;
-  const float den = r[dv] + eps;
-  f32x4 g[M], n[M];
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int c = 4 * j + 64 * m;
-    if (c < dv) {
-      g[m] = load4x(o + c);
-      n[m] = ld16<f32x4>(r + c);
-    } else {
-      g[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-      n[m] = g[m];
-    }
-  }
-  float dot = 0.f;
-#pragma unroll
-  for (int m = 0; m < M; ++m)
-    dot += g[m][0] * n[m][0] + g[m][1] * n[m][1] + g[m][2] * n[m][2] + g[m][3] * n[m][3];
-  dot = row16_sum(dot);
-  const float inv = 1.f / den;
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int c = 4 * j + 64 * m;
-    if (c < dv) st16(r + c, g[m] * inv);
-  }
-  if (j == 0) r[dv] = -dot * inv * inv;
 }
 
 // One wave per token: dS = G (dG - sum_l G_l dG_l), in place on dG.
@@ -851,13 +847,18 @@ hipError_t gemm(bool ta, bool tb, const float* A, int lda, int64_t sA, const flo
                 int64_t sB, int bmod, float* C, int ldc, int64_t sC, int M, int N, int K,
                 int64_t U, int ksplit, float* part, hipStream_t s, bool accum = false,
                 const float* G = nullptr, int64_t sG = 0, int ldg = 0,
-                const DxOut* dxo = nullptr) {
+                const DxOut* dxo = nullptr, const void* dO = nullptr, int dO_bf = 0,
+                float eps = 0.f) {
   if (G && (ksplit > 1 || !gemm_jacobian_ok(N))) return hipErrorInvalidValue;
   if (dxo && (ksplit > 1 || accum || G || !gemm_dx_ok(N))) return hipErrorInvalidValue;
+  if (dO && (ksplit > 1 || G || dxo || N > 144)) return hipErrorInvalidValue;
   const int vec = ((lda % 4 == 0 && sA % 4 == 0 && ((uintptr_t)A & 15) == 0) ? 1 : 0) |
                   ((ldb % 4 == 0 && sB % 4 == 0 && ((uintptr_t)B & 15) == 0) ? 2 : 0);
   GemmArgs g{A, B, ksplit > 1 ? part : C, M, N, K, lda, ldb, ldc, sA, sB, sC, bmod, ksplit, vec,
              accum ? 1 : 0, G, sG, ldg};
+  g.dO = dO;
+  g.dO_bf = dO_bf;
+  g.eps = eps;
   if (dxo) {
     g.dx = dxo->dx;
     g.dx_bf = dxo->bf;
@@ -868,7 +869,7 @@ hipError_t gemm(bool ta, bool tb, const float* A, int lda, int64_t sA, const flo
   }
   // 64 < N <= 144: one column tile of 128 (8 MFMA tiles per wave) or 144 (9);
   // with an epilogue that needs whole rows also N <= 64 (4)
-  const int wide = N > 128 && N <= 144 ? 9 : (N > kGT && N <= 128 ? 8 : (G || dxo ? 4 : 0));
+  const int wide = N > 128 && N <= 144 ? 9 : (N > kGT && N <= 128 ? 8 : (G || dxo || dO ? 4 : 0));
   const dim3 grid(wide ? 1u : (unsigned)((N + kGT - 1) / kGT), (unsigned)((M + kGT - 1) / kGT),
                   (unsigned)(U * ksplit));
   if (!ta && !tb) launch_gemm_kernel<false, false>(wide, grid, g, s);
@@ -986,9 +987,10 @@ hipError_t run_backward(const Plan& pp, const Tensors& t0, const BwdTensors& gt,
     // [V~ | Z] = Gk^T [V | 1]
     GMA_CHECK(gemm(true, false, Gk, K, Np * K, v1, l1, Np * l1, 0, vtz, l1, (int64_t)K * l1, K,
                    w1, (int)Np, U, ks, part, s));
-    // [n | d - eps] = Gq [V~ | Z]
+    // [n | d - eps] = Gq [V~ | Z], turned into [a | b] in the epilogue
     GMA_CHECK(gemm(false, false, Gq, K, Np * K, vtz, l1, (int64_t)K * l1, 0, nd, l1, Np * l1,
-                   (int)Np, w1, K, U, 1, part, s));
+                   (int)Np, w1, K, U, 1, part, s, false, nullptr, 0, 0, nullptr, dO,
+                   sizeof(T) == 2, t.eps));
     if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 0);
   } else {
     if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 1);
@@ -1008,24 +1010,12 @@ hipError_t run_backward(const Plan& pp, const Tensors& t0, const BwdTensors& gt,
     GMA_CHECK(gemm(false, false, Gq, K, (int64_t)C * K, vtz, l1, (int64_t)K * l1, 0, nd, l1,
                    (int64_t)C * l1, C, w1, K, Z, 1, part, s));
     GMA_CHECK(gemm(false, false, pc, C, (int64_t)C * C, v1, l1, (int64_t)C * l1, 0, nd, l1,
-                   (int64_t)C * l1, C, w1, C, Z, 1, part, s, true));
+                   (int64_t)C * l1, C, w1, C, Z, 1, part, s, true, nullptr, 0, 0, nullptr, dO,
+                   sizeof(T) == 2, t.eps));
     if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 0);
   }
-  if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 1);
-  if (dv % 4 == 0 && dv <= 128) {
-    const dim3 g16((unsigned)((rows + 15) / 16));
-    if (dv <= 64)
-      hipLaunchKernelGGL((gma_bwd_ab16_kernel<T, 1>), g16, dim3(256), 0, s, nd, dO, dv, l1, t.eps,
-                         rows);
-    else
-      hipLaunchKernelGGL((gma_bwd_ab16_kernel<T, 2>), g16, dim3(256), 0, s, nd, dO, dv, l1, t.eps,
-                         rows);
-  } else {
-    hipLaunchKernelGGL(gma_bwd_ab_kernel<T>, dim3(sblocks(rows, 4)), dim3(256), 0, s, nd, dO, dv,
-                       l1, t.eps, rows);
-  }
-  GMA_CHECK(hipGetLastError());
-  if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 0);
+  // [a | b] = [dO / d | -(dO . o) / d] was formed in the epilogue of the last
+  // product giving [n | d - eps] (d_v + 1 <= 129 columns: one column tile)
   if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 1);
   if (!causal) {
     // dGq = [a | b] [V~ | Z]^T, then dSq = Gq (dGq - rowsum(Gq dGq)) in the
