@@ -71,6 +71,13 @@ struct GemmArgs {
   const void* dO;
   int dO_bf;
   float eps;
+  // the result stored straight into the caller's tensor (wide kernel, ksplit
+  // 1, M dividing soNp): global row u * M + m is row r of unit q (soNp rows
+  // per unit), written to row q * soN + r when r < soN, N wide, bf16 when
+  // so_bf, else fp32
+  void* so;
+  int so_bf;
+  int64_t soN, soNp;
 };
 
 constexpr int kGT = 64;                 // output tile
@@ -376,6 +383,27 @@ __global__ void __launch_bounds__(256) gma_bgemm_wide_kernel(GemmArgs g) {
     C = g.C + (size_t)u * g.sC;
     ldc = g.ldc;
   }
+  if (g.so) {
+    // M divides Np (whole units, or 64-row chunks of them): the unit and the
+    // first row follow from u alone
+    const int64_t base = (int64_t)u * g.M, q = base / g.soNp, r0 = base - q * g.soNp;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + 16 * wave + 4 * gq + e, n = 16 * j + r;
+        if (m < g.M && n < g.N) {
+          const float v = (g.accum ? C[(size_t)m * ldc + n] : 0.f) + acc[j][e];
+          const int64_t rr = r0 + m;
+          if (rr < g.soN) {
+            const size_t i = (size_t)(q * g.soN + rr) * g.N + n;
+            if (g.so_bf) static_cast<bf16*>(g.so)[i] = to_bf16(v);
+            else static_cast<float*>(g.so)[i] = v;
+          }
+        }
+      }
+    return;
+  }
   if (g.dO) {
     // [a | b] = [dO / d | -(dO . o) / d], o = n / d (the output's gradient
     // through Eq. 7): d is column d_v of the row (lane r = d_v mod 16 of tile
@@ -622,20 +650,6 @@ __global__ void __launch_bounds__(256) gma_bwd_dx_kernel(const float* __restrict
   }
 }
 
-template <class T>
-__global__ void __launch_bounds__(256) gma_bwd_store_kernel(const float* __restrict__ src, int d,
-                                                            int64_t rows, int64_t Np, int64_t N,
-                                                            void* __restrict__ dst) {
-  const int q = d / 4;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < rows * q;
-       i += (int64_t)gridDim.x * 256) {
-    const int64_t row = i / q;
-    const int c = 4 * (int)(i - row * q);
-    const int64_t u = row / Np, r = row - u * Np;
-    if (r < N) store4x<T>(dst, (size_t)(u * N + r) * d + c, ld16<f32x4>(src + (size_t)row * d + c));
-  }
-}
-
 // [U][N][d] -> [U][Np][d], rows N..Np-1 zero.
 template <class T>
 __global__ void __launch_bounds__(256) gma_bwd_pad_kernel(const void* __restrict__ src, int d,
@@ -842,13 +856,21 @@ struct DxOut {
   int64_t sX = 0;
   int ldx = 0;
 };
+// A result stored straight into a caller's [units][N][width] tensor from
+// padded rows (Np per unit).
+struct StoreOut {
+  void* dst = nullptr;
+  int bf = 0;
+  int64_t N = 0, Np = 0;
+};
 
 hipError_t gemm(bool ta, bool tb, const float* A, int lda, int64_t sA, const float* B, int ldb,
                 int64_t sB, int bmod, float* C, int ldc, int64_t sC, int M, int N, int K,
                 int64_t U, int ksplit, float* part, hipStream_t s, bool accum = false,
                 const float* G = nullptr, int64_t sG = 0, int ldg = 0,
                 const DxOut* dxo = nullptr, const void* dO = nullptr, int dO_bf = 0,
-                float eps = 0.f) {
+                float eps = 0.f, const StoreOut* so = nullptr) {
+  if (so && (ksplit > 1 || G || dxo || dO || N > 144 || so->Np % M)) return hipErrorInvalidValue;
   if (G && (ksplit > 1 || !gemm_jacobian_ok(N))) return hipErrorInvalidValue;
   if (dxo && (ksplit > 1 || accum || G || !gemm_dx_ok(N))) return hipErrorInvalidValue;
   if (dO && (ksplit > 1 || G || dxo || N > 144)) return hipErrorInvalidValue;
@@ -859,6 +881,12 @@ hipError_t gemm(bool ta, bool tb, const float* A, int lda, int64_t sA, const flo
   g.dO = dO;
   g.dO_bf = dO_bf;
   g.eps = eps;
+  if (so) {
+    g.so = so->dst;
+    g.so_bf = so->bf;
+    g.soN = so->N;
+    g.soNp = so->Np;
+  }
   if (dxo) {
     g.dx = dxo->dx;
     g.dx_bf = dxo->bf;
@@ -869,7 +897,7 @@ hipError_t gemm(bool ta, bool tb, const float* A, int lda, int64_t sA, const flo
   }
   // 64 < N <= 144: one column tile of 128 (8 MFMA tiles per wave) or 144 (9);
   // with an epilogue that needs whole rows also N <= 64 (4)
-  const int wide = N > 128 && N <= 144 ? 9 : (N > kGT && N <= 128 ? 8 : (G || dxo || dO ? 4 : 0));
+  const int wide = N > 128 && N <= 144 ? 9 : (N > kGT && N <= 128 ? 8 : (G || dxo || dO || so ? 4 : 0));
   const dim3 grid(wide ? 1u : (unsigned)((N + kGT - 1) / kGT), (unsigned)((M + kGT - 1) / kGT),
                   (unsigned)(U * ksplit));
   if (!ta && !tb) launch_gemm_kernel<false, false>(wide, grid, g, s);
@@ -982,6 +1010,12 @@ hipError_t run_backward(const Plan& pp, const Tensors& t0, const BwdTensors& gt,
   // the softmax Jacobian in the epilogue of the products giving dGq and dGk
   // where one column tile holds a row of K
   const bool jac = gemm_jacobian_ok(K);
+  // dV goes to the caller's tensor from the epilogue of its (last) product
+  StoreOut dvo;
+  dvo.dst = gt.dV;
+  dvo.bf = sizeof(T) == 2;
+  dvo.N = N0;
+  dvo.Np = Np;
   if (!causal) {
     if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 1);
     // [V~ | Z] = Gk^T [V | 1]
@@ -1025,9 +1059,10 @@ hipError_t run_backward(const Plan& pp, const Tensors& t0, const BwdTensors& gt,
     // [dV~ | dZ] = Gq^T [a | b]
     GMA_CHECK(gemm(true, false, Gq, K, Np * K, nd, l1, Np * l1, 0, dvtz, l1, (int64_t)K * l1, K,
                    w1, (int)Np, U, ks, part, s));
-    // dV = Gk dV~
+    // dV = Gk dV~, stored into the caller's dV by the epilogue
     GMA_CHECK(gemm(false, false, Gk, K, Np * K, dvtz, l1, (int64_t)K * l1, 0, dvf, dv, Np * dv,
-                   (int)Np, dv, K, U, 1, part, s));
+                   (int)Np, dv, K, U, 1, part, s, false, nullptr, 0, 0, nullptr, nullptr, 0, 0.f,
+                   &dvo));
     // dGk = [V | 1] [dV~ | dZ]^T (and dSk)
     GMA_CHECK(gemm(false, true, v1, l1, Np * l1, dvtz, l1, (int64_t)K * l1, 0, dGk, K, Np * K,
                    (int)Np, K, w1, U, 1, part, s, false, jac ? Gk : nullptr, Np * K, K));
@@ -1064,18 +1099,17 @@ hipError_t run_backward(const Plan& pp, const Tensors& t0, const BwdTensors& gt,
     GMA_CHECK(gemm(false, false, Gk, K, (int64_t)C * K, dvtz, l1, (int64_t)K * l1, 0, dvf, dv,
                    (int64_t)C * dv, C, dv, K, Z, 1, part, s));
     GMA_CHECK(gemm(true, false, pc, C, (int64_t)C * C, nd, l1, (int64_t)C * l1, 0, dvf, dv,
-                   (int64_t)C * dv, C, dv, C, Z, 1, part, s, true));
+                   (int64_t)C * dv, C, dv, C, Z, 1, part, s, true, nullptr, 0, 0, nullptr,
+                   nullptr, 0, 0.f, &dvo));
   }
   if (g_launch_hook) g_launch_hook("gma_bwd_gemm", s, 0);
-  if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 1);
   if (!jac) {
+    if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 1);
     launch_bwd_softmax(Gq, dGq, K, rows, s);
     launch_bwd_softmax(Gk, dGk, K, rows, s);
+    GMA_CHECK(hipGetLastError());
+    if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 0);
   }
-  hipLaunchKernelGGL(gma_bwd_store_kernel<T>, dim3(sblocks(rows * dv / 4, 256)), dim3(256), 0, s,
-                     dvf, dv, rows, Np, N0, gt.dV);
-  GMA_CHECK(hipGetLastError());
-  if (g_launch_hook) g_launch_hook("gma_bwd_rows", s, 0);
 
   for (int side = 0; side < 2; ++side) {
     float* dS = side ? dGk : dGq;
