@@ -292,8 +292,9 @@ __global__ void __launch_bounds__(256) gma_bgemm_wide_kernel(GemmArgs g) {
   f32x4 acc[TN];
 #pragma unroll
   for (int j = 0; j < TN; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // the softmax Jacobian's G entries of this lane, requested before the main
-  // loop so that they arrive while it runs
+  // the epilogue's other input for this lane's elements (dO for [a | b], x
+  // for dX, G for the softmax Jacobian), requested before the main loop so
+  // that it arrives while the loop runs
   float gv[TN][4];
   if (g.dO) {
     // dO of this lane's columns below d_v
