@@ -34,7 +34,7 @@ namespace gma {
 namespace {
 
 constexpr int kPK = 64;    // d_model step
-constexpr int kBand = 8;   // token tiles per band of the tile order
+constexpr int kBand = 4;   // token tiles per band of the tile order
 
 struct ProjArgs {
   const bf16* X;
