@@ -122,9 +122,11 @@ def test_causal_backward_matches_oracle(B, H, N, d_r, d_v, K, dtype, skew):
 
 
 def test_causal_backward_single_token():
-    """N = 1: o = v up to eps, so the routing gradients are of order eps
-    (differences of equal terms) and are checked against the scale of the
-    terms; dV is checked as usual."""
+    """N = 1: o = v a / (a + eps), a = gamma^Q . gamma^K (Eqs. 5-7 with a
+    single key), so the routing gradients scale with eps / a; with the
+    responsibilities of this shape they are of order eps, a difference of
+    nearly equal terms, and are checked against the scale of the terms; dV is
+    checked as usual."""
     got, ref = _case(1, 2, 1, 16, 16, 4, "f32", False, causal=True)
     assert np.linalg.norm(got["dV"] - ref["dV"]) / np.linalg.norm(ref["dV"]) <= 1e-5
     for k in ("dQ", "dK", "dmu", "dlog_sigma2", "dlog_pi"):
