@@ -29,9 +29,7 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 bool supported_dim(int v) { return v == 16 || v == 32 || v == 64 || v == 128; }
 
-// scan: the call runs the causal forward's scan kernels (gma_forward,
-// gma_layer_forward, gma_validate), whose fp32 form has an LDS limit.
-int check_dims(const gma_dims* d, float eps, int causal, bool scan = true) {
+int check_dims(const gma_dims* d, float eps, int causal) {
   if (!d) return fail(GMA_ERR_INVALID_ARG, "dims is NULL");
   if (d->B < 1 || d->H < 1 || d->N < 1) return fail(GMA_ERR_INVALID_ARG, "B, H and N must be >= 1");
   if (d->d_r < 1 || d->d_v < 1 || d->K < 1)
@@ -49,7 +47,6 @@ int check_dims(const gma_dims* d, float eps, int causal, bool scan = true) {
   const int64_t BH = d->B * d->H;
   if (BH > 65535) return fail(GMA_ERR_UNSUPPORTED, "B*H above 65535 is not supported");
   if (d->N > lim / (BH * 128)) return fail(GMA_ERR_UNSUPPORTED, "B*H*N*d too large");
-  (void)scan;
   return GMA_OK;
 }
 
@@ -690,7 +687,7 @@ static int backward_plan(const gma_dims* d, int causal, Plan& p) {
 int gma_backward_workspace_bytes(const gma_dims* d, int causal, size_t* bytes) {
   t_err.clear();
   if (!bytes) return fail(GMA_ERR_INVALID_ARG, "bytes is NULL");
-  int st = check_dims(d, 0.f, causal, false);
+  int st = check_dims(d, 0.f, causal);
   if (st != GMA_OK) return st;
   Plan p;
   st = backward_plan(d, causal, p);
@@ -705,7 +702,7 @@ int gma_backward(const void* Q_X, const void* K_X, const void* V_X, const float*
                  float* dlog_sigma2, float* dlog_pi, void* workspace, size_t workspace_bytes,
                  void* stream) {
   t_err.clear();
-  int st = check_dims(d, eps, causal, false);
+  int st = check_dims(d, eps, causal);
   if (st != GMA_OK) return st;
   if (!Q_X || !K_X || !V_X || !mu || !log_sigma2 || !log_pi || !dO || !dQ || !dK || !dV ||
       !dmu || !dlog_sigma2 || !dlog_pi || !workspace)
@@ -783,7 +780,7 @@ int gma_decode_step(const void* q, const void* k, const void* v, const float* mu
   gma_dims dd = *d;
   dd.chunk = 0;           // a decode step has no chunk
   d = &dd;
-  int st = check_dims(d, eps, 1, false);
+  int st = check_dims(d, eps, 1);
   if (st != GMA_OK) return st;
   if (d->N != 1) return fail(GMA_ERR_INVALID_ARG, "a decode step takes N = 1 token per sequence");
   if (!q || !k || !v || !mu || !log_sigma2 || !log_pi || !state_v || !state_z || !out)
