@@ -133,6 +133,22 @@ def test_causal_backward_single_token():
         assert np.abs(got[k] - ref[k]).max() <= 1e-5, k
 
 
+@pytest.mark.parametrize("seed,skew", [(222, False), (222, True), (300, False), (301, False)])
+def test_causal_backward_single_token_bf16_wide(seed, skew):
+    """N = 1 at d_r = 128, K = 128 with bf16 inputs: the routing gradients
+    scale with eps / a (a = gamma^Q . gamma^K); seed 300 has a small overlap
+    (gradients of order 1), seed 222 a near-full one (rows of 1e-12 to 5e-5,
+    differences of terms of order 1).  Each element must lie within the bf16
+    bound relative to its tensor's largest element plus 1e-5 absolute, the
+    rounding of the cancelling terms; dV is checked as usual."""
+    got, ref = _case(1, 2, 1, 128, 16, 128, "bf16", skew, seed=seed, causal=True)
+    assert rowwise_rel_err(got["dV"], ref["dV"], floor=FLOOR) <= BWD_TOL["bf16"]
+    for k in ("dQ", "dK", "dmu", "dlog_sigma2", "dlog_pi"):
+        assert np.all(np.isfinite(got[k])), k
+        bound = ROUTE_TOL["bf16"] * np.abs(ref[k]).max() + 1e-5
+        assert np.abs(got[k] - ref[k]).max() <= bound, (k, np.abs(got[k] - ref[k]).max(), bound)
+
+
 @pytest.mark.parametrize("wname,heads", [("long_bidir_bf16", 1), ("lm_causal_bf16", 2)])
 def test_backward_full_shape_slice(wname, heads):
     """The benchmark workloads at their full length N, on a slice of units
