@@ -307,3 +307,19 @@ def test_generator_is_seeded_and_rounds_bf16():
     raw = rng.standard_normal(size=a["Q"].shape, dtype=np.float32)
     rel = np.abs(a["Q"].f32 - raw) / np.abs(raw)
     assert rel.max() <= 2.0 ** -8   # half an ulp of an 8-bit significand
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_single_token_closed_form(causal):
+    """One token: the latent memories hold gamma^K v and gamma^K (Eqs. 5-6), so
+    Eq. 7 reduces to o = v a / (a + eps) with a = gamma^Q . gamma^K, and the
+    value gradient to dV = dO a / (a + eps); the responsibilities come from
+    scikit-learn.  A large eps keeps the eps term visible."""
+    eps = 0.05
+    Q, Kx, V, mu, ls2, alpha = _rand_problem(23, B=2, H=3, N=1, d_r=6, d_v=5, K=7)
+    a = (_sklearn_gamma(Q, mu, ls2, alpha) * _sklearn_gamma(Kx, mu, ls2, alpha)).sum(-1)[..., None]
+    got = oracle.forward(Q, Kx, V, mu, ls2, alpha, eps, causal)
+    np.testing.assert_allclose(got["out"], V * a / (a + eps), rtol=1e-10, atol=1e-13)
+    dO = np.random.default_rng(24).standard_normal(V.shape)
+    g = oracle.backward(Q, Kx, V, mu, ls2, alpha, eps, dO, causal=causal)
+    np.testing.assert_allclose(g["dV"], dO * a / (a + eps), rtol=1e-10, atol=1e-13)
